@@ -1,0 +1,75 @@
+"""Reading tokens out of the paged caches, in float64.
+
+Test infrastructure only (see the package docstring).
+
+Pool layout read here (its own code; it shares nothing with the GPU path):
+
+* index cache - one page per 128-token block, page id = block id
+  (ROCm/ATOM PR 2962, the commit that declares the MXFP4 caches: "a single
+  8704 B field per block for the index key"):
+    bf16  [128 tok][128 dim] bf16;
+    fp8   [128 tok][128 dim] e4m3, times the per-tensor ``idx_scale``
+          (reading: the index cache takes one per-tensor scale, the same
+          convention as the fp8 K/V cache);
+    mxfp4 the 8704 B page of ``formats.decode_mxfp4_page``.
+* K/V cache, bf16 / fp8 - 16-token pages, 8 per 128-token block
+  (vLLM API page for ``sparse_attention_msa``: the page-16 rebase of the block
+  table and the stride check over the pages of a sparse block); K pages are
+  token-major [16 tok][128 dim], V pages dim-major [128 dim][16 tok], the
+  dim-major V page of the shapes in vLLM PR 61889, Validation.  fp8 values are
+  multiplied by the per-tensor ``k_scale`` / ``v_scale``.  One page id
+  addresses a K page and a V page (vLLM PR 61889, Details).
+* K/V cache, mxfp4 - one 8704 B page per block for K and one for V
+  (PR 2962, Summary: "K and V are MXFP4 pages of the same format").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import decode_bf16_bytes, decode_e4m3, decode_mxfp4_page
+
+BLOCK = 128
+PAGE16 = 16
+
+
+def index_block_keys(idx_pool: np.ndarray, dtype: str, idx_scale: float, block_ids) -> np.ndarray:
+    """Index keys of the given blocks -> float64 [n, 128 tok, 128 dim]."""
+    pages = np.asarray(idx_pool)[np.asarray(block_ids, dtype=np.int64)]
+    n = pages.shape[0]
+    if dtype == "bf16":
+        return decode_bf16_bytes(pages).reshape(n, BLOCK, 128)
+    if dtype == "fp8":
+        return decode_e4m3(pages).reshape(n, BLOCK, 128) * float(idx_scale)
+    if dtype == "mxfp4":
+        return decode_mxfp4_page(pages)
+    raise ValueError(dtype)
+
+
+def request_index_keys(idx_pool, dtype, idx_scale, block_table_row, length: int) -> np.ndarray:
+    """The first ``length`` index keys of one request, in position order -> [length, 128]."""
+    nb = -(-length // BLOCK)
+    if nb == 0:
+        return np.zeros((0, 128))
+    keys = index_block_keys(idx_pool, dtype, idx_scale, np.asarray(block_table_row)[:nb])
+    return keys.reshape(nb * BLOCK, 128)[:length]
+
+
+def kv_page_tokens(k_pool, v_pool, dtype: str, page_ids, k_scale: float, v_scale: float):
+    """Decode whole K/V pages -> (K, V), each float64 [n, page tokens, 128].
+
+    ``page_ids`` address both pools: the same id is the K page and the V page."""
+    ids = np.asarray(page_ids, dtype=np.int64)
+    kp = np.asarray(k_pool)[ids]
+    vp = np.asarray(v_pool)[ids]
+    n = ids.shape[0]
+    if dtype == "mxfp4":
+        return decode_mxfp4_page(kp), decode_mxfp4_page(vp)
+    if dtype == "bf16":
+        k = decode_bf16_bytes(kp).reshape(n, PAGE16, 128)
+        v = decode_bf16_bytes(vp).reshape(n, 128, PAGE16)
+    elif dtype == "fp8":
+        k = decode_e4m3(kp).reshape(n, PAGE16, 128) * float(k_scale)
+        v = decode_e4m3(vp).reshape(n, 128, PAGE16) * float(v_scale)
+    else:
+        raise ValueError(dtype)
+    return k, np.swapaxes(v, 1, 2)
