@@ -1,0 +1,204 @@
+/*
+ * isb.h - C ABI of libisb: one layer of indexed block-sparse paged-attention
+ * decode on an AMD Instinct MI355X (gfx950).
+ *
+ * The layer runs as four calls on one HIP stream, each taking plain device
+ * pointers and sizes:
+ *
+ *   isb_index_score              score every 128-token block of each request's
+ *                                paged index-key cache with the index query;
+ *   isb_topk_select              keep the top-k blocks of each (token, KV head);
+ *   isb_emit_sparse_block_table  turn the selection into a sparse page table;
+ *   isb_sparse_pa_decode         paged attention over the selected pages only
+ *                                (split-K flash decode plus a reduce launch).
+ *
+ * The calls follow the decode call of the vLLM API page for
+ * vllm.models.minimax_m3.amd.sparse_attention_msa (MiniMaxM3SparseAiterPAImpl
+ * .forward: query, K/V caches, top-k indices, block_table, seq_lens,
+ * num_kv_heads, scale, output, k_scale / v_scale, decode_query_len,
+ * sparse_block_table, sparse_context_lens), and the index caches and MXFP4
+ * pages of ROCm/ATOM PR 2962 ("[MiniMax-M3.1] MXFP4 index cache and MXFP4 KV
+ * cache", Summary).
+ *
+ * Common conventions
+ * ------------------
+ *  - Every pointer is device memory owned by the caller.  The library never
+ *    allocates, frees or synchronises; it only enqueues kernels on `stream`
+ *    (NULL = the default stream).  Calls may therefore be captured into a HIP
+ *    graph.  Inputs are read-only; outputs are fully written by every call, so
+ *    their prior contents never matter.
+ *  - R requests, q = decode_query_len, T = R q query tokens.  Token t = r q + i
+ *    of request r has causal length L_t = max(0, seq_lens[r] - (q - 1 - i)) and
+ *    n_t = ceil(L_t / 128) valid blocks.  Rows with n_t = 0 (pad requests of
+ *    length 0) select nothing and produce zeros.
+ *  - head_dim is 128.  H_kv KV heads; H_q query heads (G = H_q / H_kv <= 16);
+ *    H_idx index heads (a multiple of H_kv).
+ *  - Return value: ISB_OK (0) or a negative isb_status.  Nothing is enqueued
+ *    when an argument check fails.  ISB_E_LAUNCH reports hipGetLastError after
+ *    the launches.  Device-side data (page ids in range, seq_lens <= the table
+ *    width times 128) is the caller's contract; kernels treat an out-of-range
+ *    page id as poison (the affected scores / outputs become NaN) and never
+ *    dereference it.
+ *
+ * Pool layout (one page id addresses the K page and the V page alike)
+ * -------------------------------------------------------------------
+ *  index cache, one page per 128-token block (page id = block id):
+ *    ISB_BF16      [128 tok][128 dim] bf16                      32768 B
+ *    ISB_FP8_E4M3  [128 tok][128 dim] e4m3, x idx_scale         16384 B
+ *    ISB_MXFP4     128 x 64 B e2m1 (token j at 64 j, dim 2c in the low
+ *                  nibble of byte c, 2c+1 in the high nibble) then
+ *                  128 x 4 B e8m0 (token j at 8192 + 4 j, scale s for
+ *                  dims 32 s .. 32 s + 31)                       8704 B
+ *  K/V caches, bf16 / fp8: 16-token pages, 8 per block; block b of a request
+ *    is pages 8 block_table[r][b] + 0..7.  K page [16 tok][128 dim],
+ *    V page [128 dim][16 tok] (dim-major).  fp8 values times k_scale/v_scale.
+ *  K/V caches, MXFP4: one 8704 B page per block for K and one for V.
+ *  A K/V page id holds one page per KV head, [num_pages][H_kv][page bytes];
+ *  row (t, g) reads head g's page.  The index cache has one key per token,
+ *  shared by all index heads.
+ */
+#ifndef ISB_H
+#define ISB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layout-compatible with hipStream_t; NULL selects the default stream. */
+typedef struct ihipStream_t* isb_stream_t;
+
+typedef enum isb_dtype {
+  ISB_BF16 = 0,      /* bfloat16 */
+  ISB_FP8_E4M3 = 1,  /* OCP float8 e4m3fn (no infinities, 0x7F / 0xFF are NaN) */
+  ISB_MXFP4 = 2      /* OCP MX: e2m1 elements + one e8m0 scale per 32 */
+} isb_dtype;
+
+typedef enum isb_status {
+  ISB_OK = 0,
+  ISB_E_INVALID_ARG = -1,       /* null pointer or negative / zero size */
+  ISB_E_UNSUPPORTED_DTYPE = -2, /* dtype not valid for this argument */
+  ISB_E_SHAPE = -3,             /* shape relation violated (see each call) */
+  ISB_E_WORKSPACE = -4,         /* workspace smaller than required */
+  ISB_E_LAUNCH = -5             /* a kernel launch failed */
+} isb_status;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int isb_version(void);
+
+/* Static, human-readable text for an isb_status value. */
+const char* isb_strerror(int status);
+
+/*
+ * isb_index_score - block scores of every (KV head, token, block).
+ *
+ * Defines (ROCm/ATOM PR 2962, Known limits: one fp32 score per index head,
+ * row and 128-token block; Summary: e4m3 index query for the MXFP4 index):
+ *   scores[g][t][b] = sum over index heads h of group g of
+ *                     max over tokens j of block b with position < L_t of
+ *                     dot(q_idx[t][h][:], k_idx[j][:])          (fp32)
+ * for b < n_t, and -inf for n_t <= b < max_blocks.  The fp8 index cache
+ * multiplies by idx_scale (ignored otherwise).  A NaN among a block's causally
+ * valid keys makes that score NaN.
+ *
+ *   q_idx        [T][num_idx_heads][128], q_idx_dtype ISB_BF16 or ISB_FP8_E4M3
+ *   idx_pool     [idx_pool_blocks] pages of idx_dtype (layout above)
+ *   block_table  [num_reqs][block_table_stride] int32 block ids; entries past a
+ *                request's ceil(seq_len/128) blocks are never read
+ *   seq_lens     [num_reqs] int32, each <= 128 * min(max_blocks, stride)
+ *   scores       out, [num_kv_heads][T][max_blocks] fp32
+ * Shape errors: num_idx_heads % num_kv_heads != 0, max_blocks > stride.
+ */
+int isb_index_score(isb_stream_t stream,
+                    const void* q_idx, int q_idx_dtype, int num_idx_heads,
+                    const void* idx_pool, int idx_dtype, float idx_scale,
+                    int64_t idx_pool_blocks,
+                    const int32_t* block_table, int block_table_stride,
+                    const int32_t* seq_lens, int num_reqs, int decode_query_len,
+                    int num_kv_heads, int max_blocks, float* scores);
+
+/*
+ * isb_topk_select - the blocks each (KV head, token) row attends to.
+ *
+ * Per row (PR 2962: the tail block is always selected; pad rows compute
+ * nothing): the tail block n_t - 1, plus the top_k - 1 best of blocks
+ * [0, n_t - 1) by score, ties to the lower block index, NaN below every number
+ * and -0.0 equal to +0.0.  Written ascending, padded with -1; a row with
+ * n_t = 0 is all -1.  Bit-exact for given fp32 scores.
+ *
+ *   scores    [num_kv_heads][T][max_blocks] fp32 (as isb_index_score writes)
+ *   topk_idx  out, [num_kv_heads][T][top_k] int32
+ * Shape errors: top_k < 1, top_k > max_blocks, max_blocks > 1048576.
+ */
+int isb_topk_select(isb_stream_t stream, const float* scores,
+                    const int32_t* seq_lens, int num_reqs, int decode_query_len,
+                    int num_kv_heads, int max_blocks, int top_k, int32_t* topk_idx);
+
+/*
+ * isb_emit_sparse_block_table - selection -> sparse page table.
+ *
+ * Row (t, g) = t * num_kv_heads + g (token-major, as the vLLM page slices
+ * sparse_bt_buffer[: nd * kvh]).  The k-th selected block b of the row
+ * (entries >= 0 in order) becomes pages
+ *   sparse_bt[row][k * ppb + p] = block_table[r][b] * ppb + p,  p < ppb,
+ * unused slots are -1, and
+ *   sparse_ctx[row] = (m - 1) * 128 + (L_t - 128 (n_t - 1))
+ * for m >= 1 selected blocks (the tail block last), else 0.
+ * pages_per_block (ppb) is 8 for bf16 / fp8 K/V and 1 for MXFP4 K/V
+ * (PR 2962: pages_per_block is an emit parameter, 8 or 1).  Entries >= the
+ * table stride are treated as -1.
+ *
+ *   topk_idx    [num_kv_heads][T][top_k] int32
+ *   sparse_bt   out, [T * num_kv_heads][top_k * ppb] int32
+ *   sparse_ctx  out, [T * num_kv_heads] int32
+ * Shape errors: ppb not 1 or 8.
+ */
+int isb_emit_sparse_block_table(isb_stream_t stream, const int32_t* topk_idx,
+                                const int32_t* block_table, int block_table_stride,
+                                const int32_t* seq_lens, int num_reqs,
+                                int decode_query_len, int num_kv_heads, int top_k,
+                                int pages_per_block, int32_t* sparse_bt,
+                                int32_t* sparse_ctx);
+
+/*
+ * Bytes of workspace isb_sparse_pa_decode needs for these arguments (the
+ * split-K partial results).  Returns 0 for invalid arguments.
+ */
+size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv_heads,
+                                     int sparse_bt_stride, int kv_dtype);
+
+/*
+ * isb_sparse_pa_decode - attention over the selected pages.
+ *
+ * For row (t, g) and query head h of KV group g (vLLM API page, the decode
+ * call): z_u = sm_scale * dot(q[t][h], K_u) over sparse positions
+ * u < sparse_ctx[row]; out[t][h] = sum_u softmax(z)_u V_u, in fp32, written as
+ * bf16.  Position u is slot u mod P of page sparse_bt[row][u div P], with
+ * P = 16 tokens per page (bf16 / fp8 K/V) or 128 (MXFP4 K/V).  fp8 K/V are
+ * multiplied by k_scale / v_scale.  Rows with sparse_ctx = 0 output zeros.
+ *
+ *   q           [num_tokens][num_q_heads][128], q_dtype ISB_BF16 or ISB_FP8_E4M3
+ *   k_pool, v_pool  [num_pages][num_kv_heads] pages of kv_dtype (layout above)
+ *   sparse_bt   [num_tokens * num_kv_heads][sparse_bt_stride] int32 page ids
+ *   sparse_ctx  [num_tokens * num_kv_heads] int32, <= sparse_bt_stride * P
+ *   workspace   >= isb_sparse_pa_workspace_bytes(...) bytes, 16-byte aligned
+ *   out         out, [num_tokens][num_q_heads][128] bf16
+ * Shape errors: head_dim != 128, num_q_heads % num_kv_heads, G > 16.
+ */
+int isb_sparse_pa_decode(isb_stream_t stream,
+                         const void* q, int q_dtype,
+                         const void* k_pool, const void* v_pool, int kv_dtype,
+                         int64_t num_pages, float k_scale, float v_scale,
+                         const int32_t* sparse_bt, int sparse_bt_stride,
+                         const int32_t* sparse_ctx, int num_tokens,
+                         int num_q_heads, int num_kv_heads, int head_dim,
+                         float sm_scale, void* workspace, size_t workspace_bytes,
+                         void* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISB_H */

@@ -1,0 +1,18 @@
+"""Indexed block-sparse paged-attention decode for AMD Instinct MI355X (gfx950).
+
+The compute lives in libisb.so (hand-written HIP kernels behind a C ABI,
+declared in include/isb.h); ``binding`` marshals torch tensors into it and
+``workload`` builds seeded synthetic inputs.
+"""
+from .binding import (  # noqa: F401
+    DecodeLayer,
+    IsbError,
+    emit_sparse_block_table,
+    index_score,
+    load_library,
+    sparse_pa_decode,
+    sparse_pa_workspace_bytes,
+    strerror,
+    topk_select,
+    version,
+)

@@ -1,0 +1,227 @@
+"""Python binding of libisb (ctypes): argument marshalling only.
+
+Each function takes torch tensors that already live on a ROCm device, passes
+their device pointers and sizes to the C entry point of the same name
+(``isb_<name>``), enqueues on the tensor's current stream and returns the
+output tensors.  Every step of the decode runs in the HIP kernels of libisb;
+there is no fallback: if the library is not built, or no GPU is present, the
+functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+BF16, FP8_E4M3, MXFP4 = 0, 1, 2
+DTYPE_CODES = {"bf16": BF16, "fp8": FP8_E4M3, "e4m3": FP8_E4M3, "mxfp4": MXFP4}
+
+_STATUS = {
+    0: "ok",
+    -1: "invalid argument",
+    -2: "unsupported dtype",
+    -3: "shape mismatch",
+    -4: "workspace too small",
+    -5: "kernel launch failed",
+}
+
+_lib = None
+
+
+class IsbError(RuntimeError):
+    """A libisb call returned an error status."""
+
+    def __init__(self, name: str, status: int):
+        self.status = status
+        super().__init__(f"isb_{name}: {_STATUS.get(status, 'unknown error')} (status {status})")
+
+
+def _exc(name: str, status: int) -> Exception:
+    err = IsbError(name, status)
+    if status in (-1, -3, -4):
+        return ValueError(str(err))
+    if status == -2:
+        return NotImplementedError(str(err))
+    return err
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "isb_version": ([], _I),
+    "isb_strerror": ([_I], ctypes.c_char_p),
+    "isb_index_score": ([_P, _P, _I, _I, _P, _I, _F, _I64, _P, _I, _P, _I, _I, _I, _I, _P], _I),
+    "isb_topk_select": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "isb_emit_sparse_block_table": ([_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P], _I),
+    "isb_sparse_pa_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
+    "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I,
+                              _F, _P, _SZ, _P], _I),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Open libisb.so and declare its entry points (no GPU needed)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    status = getattr(load_library(), "isb_" + name)(*args)
+    if status != 0:
+        raise _exc(name, status)
+
+
+def _dev(*tensors: torch.Tensor) -> torch.device:
+    dev = tensors[0].device
+    if dev.type != "cuda":
+        raise RuntimeError("libisb runs on a ROCm GPU: tensors must be on a cuda device")
+    for t in tensors:
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _code(dtype) -> int:
+    return DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def version() -> int:
+    return int(load_library().isb_version())
+
+
+def strerror(status: int) -> str:
+    return load_library().isb_strerror(int(status)).decode()
+
+
+def index_score(q_idx, q_idx_dtype, idx_pool, idx_dtype, idx_scale, block_table, seq_lens,
+                decode_query_len, num_kv_heads, max_blocks, scores=None):
+    """Block scores [num_kv_heads, T, max_blocks] fp32 (see isb_index_score)."""
+    dev = _dev(q_idx, idx_pool, block_table, seq_lens)
+    T, H_idx = q_idx.shape[0], q_idx.shape[1]
+    if scores is None:
+        scores = torch.empty((num_kv_heads, T, max_blocks), dtype=torch.float32, device=dev)
+    _dev(scores)
+    _call("index_score", _stream(dev), q_idx.data_ptr(), _code(q_idx_dtype), H_idx,
+          idx_pool.data_ptr(), _code(idx_dtype), float(idx_scale), idx_pool.shape[0],
+          block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(), seq_lens.shape[0],
+          decode_query_len, num_kv_heads, max_blocks, scores.data_ptr())
+    return scores
+
+
+def topk_select(scores, seq_lens, decode_query_len, top_k, topk_idx=None):
+    """Selected blocks [num_kv_heads, T, top_k] int32 (see isb_topk_select)."""
+    dev = _dev(scores, seq_lens)
+    H_kv, T, MB = scores.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
+    _dev(topk_idx)
+    _call("topk_select", _stream(dev), scores.data_ptr(), seq_lens.data_ptr(), seq_lens.shape[0],
+          decode_query_len, H_kv, MB, top_k, topk_idx.data_ptr())
+    return topk_idx
+
+
+def emit_sparse_block_table(topk_idx, block_table, seq_lens, decode_query_len, pages_per_block,
+                            sparse_bt=None, sparse_ctx=None):
+    """(sparse_bt [T*H_kv, K*ppb], sparse_ctx [T*H_kv]) int32 (see isb_emit_sparse_block_table)."""
+    dev = _dev(topk_idx, block_table, seq_lens)
+    H_kv, T, K = topk_idx.shape
+    if sparse_bt is None:
+        sparse_bt = torch.empty((T * H_kv, K * pages_per_block), dtype=torch.int32, device=dev)
+    if sparse_ctx is None:
+        sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
+    _dev(sparse_bt, sparse_ctx)
+    _call("emit_sparse_block_table", _stream(dev), topk_idx.data_ptr(), block_table.data_ptr(),
+          block_table.shape[1], seq_lens.data_ptr(), seq_lens.shape[0], decode_query_len, H_kv, K,
+          pages_per_block, sparse_bt.data_ptr(), sparse_ctx.data_ptr())
+    return sparse_bt, sparse_ctx
+
+
+def sparse_pa_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, sparse_bt_stride, kv_dtype) -> int:
+    return int(load_library().isb_sparse_pa_workspace_bytes(
+        num_tokens, num_q_heads, num_kv_heads, sparse_bt_stride, _code(kv_dtype)))
+
+
+def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, sparse_bt, sparse_ctx,
+                     num_q_heads, num_kv_heads, sm_scale, out=None, workspace=None):
+    """Attention output [T, num_q_heads, 128] bf16 (see isb_sparse_pa_decode)."""
+    dev = _dev(q, k_pool, v_pool, sparse_bt, sparse_ctx)
+    T = q.shape[0]
+    stride = sparse_bt.shape[1]
+    need = sparse_pa_workspace_bytes(T, num_q_heads, num_kv_heads, stride, kv_dtype)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    _dev(out, workspace)
+    _call("sparse_pa_decode", _stream(dev), q.data_ptr(), _code(q_dtype), k_pool.data_ptr(),
+          v_pool.data_ptr(), _code(kv_dtype), k_pool.shape[0], float(k_scale), float(v_scale),
+          sparse_bt.data_ptr(), stride, sparse_ctx.data_ptr(), T, num_q_heads, num_kv_heads, 128,
+          float(sm_scale), workspace.data_ptr(), workspace.numel(), out.data_ptr())
+    return out
+
+
+class DecodeLayer:
+    """The four calls of one decode layer over a workload, with persistent outputs.
+
+    Buffers are allocated once at construction (torch, on the workload's
+    device); ``run()`` only enqueues the five kernels, so it can be timed or
+    captured."""
+
+    def __init__(self, w):
+        cfg = w.cfg
+        self.w = w
+        dev = w.q.device
+        T = cfg.num_tokens
+        self.scores = torch.empty((cfg.num_kv_heads, T, cfg.max_blocks), dtype=torch.float32, device=dev)
+        self.topk = torch.empty((cfg.num_kv_heads, T, cfg.top_k), dtype=torch.int32, device=dev)
+        ppb = cfg.pages_per_block
+        self.sparse_bt = torch.empty((T * cfg.num_kv_heads, cfg.top_k * ppb), dtype=torch.int32, device=dev)
+        self.sparse_ctx = torch.empty((T * cfg.num_kv_heads,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, cfg.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+        need = sparse_pa_workspace_bytes(T, cfg.num_q_heads, cfg.num_kv_heads, cfg.top_k * ppb, cfg.kv_dtype)
+        self.workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+
+    def run(self):
+        w, cfg = self.w, self.w.cfg
+        index_score(w.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale, w.block_table,
+                    w.seq_lens, cfg.query_len, cfg.num_kv_heads, cfg.max_blocks, scores=self.scores)
+        topk_select(self.scores, w.seq_lens, cfg.query_len, cfg.top_k, topk_idx=self.topk)
+        emit_sparse_block_table(self.topk, w.block_table, w.seq_lens, cfg.query_len,
+                                cfg.pages_per_block, sparse_bt=self.sparse_bt, sparse_ctx=self.sparse_ctx)
+        sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                         self.sparse_bt, self.sparse_ctx, cfg.num_q_heads, cfg.num_kv_heads,
+                         w.sm_scale, out=self.out, workspace=self.workspace)
+        return self.out
+
+
+# C names, for callers that prefer them.
+isb_index_score = index_score
+isb_topk_select = topk_select
+isb_emit_sparse_block_table = emit_sparse_block_table
+isb_sparse_pa_decode = sparse_pa_decode
+isb_sparse_pa_workspace_bytes = sparse_pa_workspace_bytes

@@ -1,0 +1,140 @@
+// Device helpers for the gfx950 kernels of libisb: vector types, exact element
+// conversions, MFMA wrappers and wave-level reductions.  CDNA4 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "isb.h"
+
+namespace isb {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kHeadDim = 128;
+constexpr int kBlockTokens = 128;
+constexpr int kPage16Tokens = 16;
+constexpr int kMxDataBytes = 128 * 64;
+constexpr int kMxPageBytes = kMxDataBytes + 128 * 4;  // 8704
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
+
+// ----------------------------------------------------------------- loads
+// 16-byte global loads; the pools are read once per step, so they bypass
+// nothing special: plain vector loads that the memory system coalesces.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ld8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+__device__ __forceinline__ uint32_t ld4(const void* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// ----------------------------------------------------------------- conversions
+// All exact: e4m3 and e2m1 * 2^k values are representable in bf16 (the
+// hardware conversions round only when a value does not fit, which e4m3 and
+// in-range e2m1 * scale never do).
+
+// Two e4m3 bytes (bytes 0,1 when hi = false, 2,3 when hi = true) -> two bf16.
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+
+// Four e4m3 bytes of one dword -> four bf16 (byte 0 first).
+__device__ __forceinline__ bf16x4 e4m3x4_to_bf16x4(uint32_t w) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return bf16x4{a[0], a[1], b[0], b[1]};
+}
+
+// Eight e2m1 nibbles of one dword (low nibble of byte 0 first) -> eight bf16,
+// each multiplied by `scale` (a power of two from an e8m0 byte).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t w, float scale) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// e8m0 byte -> float 2^(e - 127); 0xFF -> NaN; 0 -> 2^-127 (subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  e &= 0xFFu;
+  if (e == 0xFFu) return qnan();
+  if (e == 0u) return __uint_as_float(0x00400000u);
+  return __uint_as_float(e << 23);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ bf16x2 u32_as_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(bf16x2, w);
+}
+__device__ __forceinline__ bf16x8 u32x4_as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// ----------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x32_bf16: lane l = 16 g + r supplies A[r][8 g + i] and
+// B[8 g + i][r] (i < 8); the result lane l holds D[4 g + i][r] (i < 4).
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x16_bf16: lane l = 16 g + r supplies A[r][4 g + i] and
+// B[4 g + i][r] (i < 4); result as above.
+__device__ __forceinline__ f32x4 mfma_16x16x16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A in e2m1 and B in e4m3:
+//   A lane l = 16 g + r: row r, k = 32 g .. 32 g + 31 as 32 nibbles in the
+//     first four dwords (low nibble first); `scale_a` (e8m0 in bits 0..7)
+//     scales exactly those 32 elements;
+//   B lane l = 16 g + r: column r, bytes 0..15 are k = 16 g .. 16 g + 15 and
+//     bytes 16..31 are k = 64 + 16 g .. 64 + 16 g + 15; unit scale (127).
+// The empty asm keeps both sources live past the instruction: without it the
+// register allocator may place the destination over a source register, which
+// corrupts the product.
+__device__ __forceinline__ f32x4 mfma_scale_fp4_e4m3(i32x8 a, i32x8 b, f32x4 c, int scale_a) {
+  f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale_a, 0, 127);
+  asm volatile("" ::"v"(a), "v"(b));
+  return d;
+}
+
+// ----------------------------------------------------------------- cross-lane
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// DPP controls: quad_perm [1,0,3,2] (xor 1), [2,3,0,1] (xor 2), row_half_mirror,
+// row_mirror.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int m) { return __shfl_xor(x, m, kWave); }
+
+// Maximum over the four lanes {r, r+16, r+32, r+48} (the lane groups of an
+// MFMA result column).
+__device__ __forceinline__ float max_over_groups(float x) {
+  x = fmaxf(x, shfl_xor_f32(x, 16));
+  x = fmaxf(x, shfl_xor_f32(x, 32));
+  return x;
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += shfl_xor_f32(x, 16);
+  x += shfl_xor_f32(x, 32);
+  return x;
+}
+
+}  // namespace isb

@@ -1,0 +1,63 @@
+// Host-side helpers shared by the C-ABI entry points: status codes, argument
+// checks and launch-error mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "isb.h"
+
+namespace isb {
+
+inline hipStream_t as_hip(isb_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool is_pool_dtype(int d) { return d == ISB_BF16 || d == ISB_FP8_E4M3 || d == ISB_MXFP4; }
+inline bool is_query_dtype(int d) { return d == ISB_BF16 || d == ISB_FP8_E4M3; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? ISB_OK : ISB_E_LAUNCH;
+}
+
+inline int64_t idx_page_bytes(int dt) {
+  return dt == ISB_BF16 ? 32768 : dt == ISB_FP8_E4M3 ? 16384 : 8704;
+}
+
+// Split-K plan of isb_sparse_pa_decode; shared by the workspace query so the
+// two always agree.  A split is one workgroup of four waves.
+struct PaPlan {
+  int rows;             // num_tokens * num_kv_heads
+  int max_pages;        // sparse_bt_stride
+  int pages_per_split;  // pages one workgroup attends
+  int splits;           // workgroups per row
+};
+
+inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, int kv_dtype) {
+  PaPlan p;
+  p.rows = num_tokens * num_kv_heads;
+  p.max_pages = sparse_bt_stride;
+  // 16-token pages: at least 8 pages (2 a wave) per split; 128-token MXFP4
+  // pages: at least one page (8 tiles, 2 a wave).
+  const int min_pages = kv_dtype == ISB_MXFP4 ? 1 : 8;
+  const int target_wgs = 1024;
+  int want = (target_wgs + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
+  int most = (p.max_pages + min_pages - 1) / min_pages;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  p.pages_per_split = (p.max_pages + want - 1) / want;
+  if (p.pages_per_split < 1) p.pages_per_split = 1;
+  p.splits = (p.max_pages + p.pages_per_split - 1) / p.pages_per_split;
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+// Partial results per (row, split): 16 heads x 128 dims fp32, then 16 x (m, l).
+constexpr size_t kPartialO = 16 * 128;
+constexpr size_t kPartialML = 16 * 2;
+
+inline size_t pa_workspace_bytes(const PaPlan& p) {
+  return (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float);
+}
+
+}  // namespace isb

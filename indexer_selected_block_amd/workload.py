@@ -26,6 +26,9 @@ A request's token at absolute position ``p`` lives in the 128-token block
   ``v_scale``.  One page id addresses the K page and the V page alike.
 * K/V caches in MXFP4 use one 8704 B page per block (pages_per_block 1), the
   same page format as the MXFP4 index cache, for K and for V.
+* A K/V page id holds one page per KV head: the pools are
+  ``[num_pages][H_kv][page bytes]`` (the index cache has a single key per
+  token, shared by every index head, so it has no head dimension).
 
 Slots a request has not written (past its length) and every page no request
 uses hold poison (NaN in every format), and unused block-table entries point
@@ -157,8 +160,8 @@ class Workload:
     q: torch.Tensor             # uint8 [T, H_q, 128 * qbytes]
     q_idx: torch.Tensor         # uint8 [T, H_idx, 128 * qbytes]
     idx_pool: torch.Tensor      # uint8 [pool_blocks + 1, idx page bytes]
-    k_pool: torch.Tensor        # uint8 [num_pages, page bytes]
-    v_pool: torch.Tensor        # uint8 [num_pages, page bytes]
+    k_pool: torch.Tensor        # uint8 [num_pages, H_kv * page bytes]
+    v_pool: torch.Tensor        # uint8 [num_pages, H_kv * page bytes]
     idx_scale: float
     k_scale: float
     v_scale: float
@@ -307,7 +310,7 @@ def make_workload(cfg: Config, device="cpu", chunk_blocks: int = 2048) -> Worklo
 
     nb_pool = cfg.pool_blocks + 1
     idx_pool = torch.empty((nb_pool, idx_page_bytes(cfg.idx_dtype)), dtype=torch.uint8, device=dev)
-    kv_block_bytes = kv_page_bytes(cfg.kv_dtype) * ppb
+    kv_block_bytes = kv_page_bytes(cfg.kv_dtype) * ppb * cfg.num_kv_heads
     k_pool = torch.empty((nb_pool, kv_block_bytes), dtype=torch.uint8, device=dev)
     v_pool = torch.empty((nb_pool, kv_block_bytes), dtype=torch.uint8, device=dev)
     _fill_poison(idx_pool, cfg.idx_dtype)
@@ -321,11 +324,12 @@ def make_workload(cfg: Config, device="cpu", chunk_blocks: int = 2048) -> Worklo
     key_dist_kv = cfg.key_dist
     # fp8 per-tensor scales: amax / 448 over the values actually written.
     idx_scale = _write_cache(cfg, streams, _T_KEYS, idx_pool, cfg.idx_dtype, "idx", ids_d, valid_d,
-                             cfg.key_dist, chunk_blocks)
+                             cfg.key_dist, chunk_blocks, 1, 1)
     k_scale = _write_cache(cfg, streams, _T_K, k_pool, cfg.kv_dtype, "k", ids_d, valid_d,
-                           key_dist_kv, chunk_blocks)
+                           key_dist_kv, chunk_blocks, ppb, cfg.num_kv_heads)
     v_scale = _write_cache(cfg, streams, _T_V, v_pool, cfg.kv_dtype, "v", ids_d, valid_d,
-                           "normal" if cfg.key_dist != "mx_uniform" else "mx_uniform", chunk_blocks)
+                           "normal" if cfg.key_dist != "mx_uniform" else "mx_uniform", chunk_blocks,
+                           ppb, cfg.num_kv_heads)
 
     T = cfg.num_tokens
     q = _query(cfg, streams, _T_Q, (T, cfg.num_q_heads, cfg.head_dim), cfg.q_dtype)
@@ -337,8 +341,8 @@ def make_workload(cfg: Config, device="cpu", chunk_blocks: int = 2048) -> Worklo
         seq_lens=lens.to(torch.int32).to(dev),
         block_table=bt.to(torch.int32).to(dev),
         q=q, q_idx=q_idx, idx_pool=idx_pool,
-        k_pool=k_pool.view(nb_pool * ppb, page_bytes),
-        v_pool=v_pool.view(nb_pool * ppb, page_bytes),
+        k_pool=k_pool.view(nb_pool * ppb, cfg.num_kv_heads * page_bytes),
+        v_pool=v_pool.view(nb_pool * ppb, cfg.num_kv_heads * page_bytes),
         idx_scale=idx_scale, k_scale=k_scale, v_scale=v_scale,
         sm_scale=1.0 / math.sqrt(cfg.head_dim),
     )
@@ -365,50 +369,62 @@ def _chunks(n: int, size: int):
         yield s // size, s, min(n, s + size)
 
 
-def _write_cache(cfg, streams, tid, pool, dtype, which, ids, valid, dist, chunk_blocks) -> float:
-    """Fill the used blocks of one cache; returns the per-tensor scale (1.0 unless fp8)."""
+def _write_cache(cfg, streams, tid, pool, dtype, which, ids, valid, dist, chunk_blocks, ppb,
+                 heads) -> float:
+    """Fill the used blocks of one cache; returns the per-tensor scale (1.0 unless fp8).
+
+    ``pool`` is [blocks, ppb * heads * page bytes]: per block, ``ppb`` pages,
+    each holding one page per head."""
     n = ids.shape[0]
     dev = streams.device
     slot = torch.arange(BLOCK_TOKENS, device=dev)
+    pv = pool.view(pool.shape[0], ppb, heads, -1)
+
+    def put(s, e, h, page):
+        pv[ids[s:e], :, h, :] = page.reshape(e - s, ppb, -1)
+
     if dtype == "mxfp4" and dist == "mx_uniform":
         # e2m1 codes uniform over all 16 codes; e8m0 exponents uniform in [-4, 4].
-        for c, s, e in _chunks(n, chunk_blocks):
-            g = streams.gen(tid, c)
-            codes = torch.randint(0, 16, (e - s, BLOCK_TOKENS, HEAD_DIM), generator=g,
-                                  device=dev, dtype=torch.int64).to(torch.uint8)
-            sc = torch.randint(127 - 4, 127 + 5, (e - s, BLOCK_TOKENS, 4), generator=g,
-                               device=dev, dtype=torch.int64).to(torch.uint8)
-            page = _pack_mxfp4_page(codes, sc)
-            _poison_tail(page, valid[s:e], slot, dtype, which)
-            pool[ids[s:e]] = page
+        for h in range(heads):
+            for c, s, e in _chunks(n, chunk_blocks):
+                g = streams.gen(tid + 100 * h, c)
+                codes = torch.randint(0, 16, (e - s, BLOCK_TOKENS, HEAD_DIM), generator=g,
+                                      device=dev, dtype=torch.int64).to(torch.uint8)
+                sc = torch.randint(127 - 4, 127 + 5, (e - s, BLOCK_TOKENS, 4), generator=g,
+                                   device=dev, dtype=torch.int64).to(torch.uint8)
+                page = _pack_mxfp4_page(codes, sc)
+                _poison_tail(page, valid[s:e], slot, dtype, which)
+                put(s, e, h, page)
         return 1.0
 
     scale = 1.0
     if dtype == "fp8":
         amax = torch.zeros((), device=dev)
-        for c, s, e in _chunks(n, chunk_blocks):
-            x = _draw(cfg, streams, tid, c, (e - s, BLOCK_TOKENS, HEAD_DIM), dist)
-            m = (slot[None, :] < valid[s:e, None]).unsqueeze(-1)
-            amax = torch.maximum(amax, (x.abs() * m).amax())
+        for h in range(heads):
+            for c, s, e in _chunks(n, chunk_blocks):
+                x = _draw(cfg, streams, tid + 100 * h, c, (e - s, BLOCK_TOKENS, HEAD_DIM), dist)
+                m = (slot[None, :] < valid[s:e, None]).unsqueeze(-1)
+                amax = torch.maximum(amax, (x.abs() * m).amax())
         scale = float(amax) / E4M3_MAX if float(amax) > 0 else 1.0
-    for c, s, e in _chunks(n, chunk_blocks):
-        x = _draw(cfg, streams, tid, c, (e - s, BLOCK_TOKENS, HEAD_DIM), dist)
-        nb = e - s
-        if dtype == "bf16":
-            page = _to_bf16_bytes(x).reshape(nb, BLOCK_TOKENS, HEAD_DIM * 2)
-        elif dtype == "fp8":
-            page = _to_e4m3_bytes(x / scale).reshape(nb, BLOCK_TOKENS, HEAD_DIM)
-        else:
-            codes, sc = _mx_quantize(x)
-            page = _pack_mxfp4_page(codes, sc)
-        if dtype != "mxfp4" and which == "v":
-            # V pages are dim-major within each 16-token page.
-            esz = page.shape[-1] // HEAD_DIM
-            page = (page.reshape(nb, 8, PAGE16_TOKENS, HEAD_DIM, esz)
-                    .transpose(2, 3).contiguous())
-        page = page.reshape(nb, -1)
-        _poison_tail(page, valid[s:e], slot, dtype, which)
-        pool[ids[s:e]] = page
+    for h in range(heads):
+        for c, s, e in _chunks(n, chunk_blocks):
+            x = _draw(cfg, streams, tid + 100 * h, c, (e - s, BLOCK_TOKENS, HEAD_DIM), dist)
+            nb = e - s
+            if dtype == "bf16":
+                page = _to_bf16_bytes(x).reshape(nb, BLOCK_TOKENS, HEAD_DIM * 2)
+            elif dtype == "fp8":
+                page = _to_e4m3_bytes(x / scale).reshape(nb, BLOCK_TOKENS, HEAD_DIM)
+            else:
+                codes, sc = _mx_quantize(x)
+                page = _pack_mxfp4_page(codes, sc)
+            if dtype != "mxfp4" and which == "v":
+                # V pages are dim-major within each 16-token page.
+                esz = page.shape[-1] // HEAD_DIM
+                page = (page.reshape(nb, 8, PAGE16_TOKENS, HEAD_DIM, esz)
+                        .transpose(2, 3).contiguous())
+            page = page.reshape(nb, -1)
+            _poison_tail(page, valid[s:e], slot, dtype, which)
+            put(s, e, h, page)
     return scale
 
 

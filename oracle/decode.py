@@ -152,7 +152,8 @@ def sparse_pa_decode(q, k_pool, v_pool, kv_dtype, k_scale, v_scale, sparse_bt, s
     (t, g) and query head h of group g, z_u = scale q[t,h] . K_u over sparse
     positions u < sparse_ctx, softmax over u, output sum_u p_u V_u.  Position u
     is slot u mod P of page sparse_bt[row][u div P], P = 128 / ppb tokens a page.
-    Readings: a row of length 0 outputs zeros; fp8 K/V carry per-tensor scales.
+    Row (t, g) reads KV head g's page under each page id.  Readings: a row of
+    length 0 outputs zeros; fp8 K/V carry per-tensor scales.
     """
     q = np.asarray(q, dtype=np.float64)
     T, H_q, D = q.shape
@@ -166,7 +167,8 @@ def sparse_pa_decode(q, k_pool, v_pool, kv_dtype, k_scale, v_scale, sparse_bt, s
             if n == 0:
                 continue
             npages = -(-n // ptok)
-            K, V = kv_page_tokens(k_pool, v_pool, kv_dtype, sparse_bt[row, :npages], k_scale, v_scale)
+            K, V = kv_page_tokens(k_pool, v_pool, kv_dtype, sparse_bt[row, :npages], k_scale, v_scale,
+                                  head=g, num_kv_heads=num_kv_heads)
             K = K.reshape(npages * ptok, D)[:n]
             V = V.reshape(npages * ptok, D)[:n]
             qh = q[t, g * G:(g + 1) * G]

@@ -21,6 +21,10 @@ Pool layout read here (its own code; it shares nothing with the GPU path):
   addresses a K page and a V page (vLLM PR 61889, Details).
 * K/V cache, mxfp4 - one 8704 B page per block for K and one for V
   (PR 2962, Summary: "K and V are MXFP4 pages of the same format").
+* A K/V page id holds one page per KV head ([num_pages][H_kv][page]): the
+  MXFP4 cache declares one field per (page, KV head) for K and for V, and a
+  single field per block for the index key (PR 2962, the commit that
+  declares the MXFP4 caches).
 """
 from __future__ import annotations
 
@@ -54,13 +58,16 @@ def request_index_keys(idx_pool, dtype, idx_scale, block_table_row, length: int)
     return keys.reshape(nb * BLOCK, 128)[:length]
 
 
-def kv_page_tokens(k_pool, v_pool, dtype: str, page_ids, k_scale: float, v_scale: float):
-    """Decode whole K/V pages -> (K, V), each float64 [n, page tokens, 128].
+def kv_page_tokens(k_pool, v_pool, dtype: str, page_ids, k_scale: float, v_scale: float,
+                   head: int = 0, num_kv_heads: int = 1):
+    """Decode whole K/V pages of one KV head -> (K, V), each float64 [n, page tokens, 128].
 
     ``page_ids`` address both pools: the same id is the K page and the V page."""
     ids = np.asarray(page_ids, dtype=np.int64)
-    kp = np.asarray(k_pool)[ids]
-    vp = np.asarray(v_pool)[ids]
+    k_pool = np.asarray(k_pool)
+    v_pool = np.asarray(v_pool)
+    kp = k_pool.reshape(k_pool.shape[0], num_kv_heads, -1)[ids, head]
+    vp = v_pool.reshape(v_pool.shape[0], num_kv_heads, -1)[ids, head]
     n = ids.shape[0]
     if dtype == "mxfp4":
         return decode_mxfp4_page(kp), decode_mxfp4_page(vp)

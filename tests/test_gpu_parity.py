@@ -1,0 +1,300 @@
+"""GPU parity: every call of libisb against the CPU oracle (needs an MI355X).
+
+* Per call, on shrunk workloads of all five configurations (several tiles,
+  ragged tails, pad rows): scores within 1e-3 relative; top-k and block
+  tables bit-exact when both sides get the same fp32 scores / the same
+  selection; attention within 1e-2 max|V| + 1e-3 (fp8, MXFP4) or
+  4e-3 max|V| (bf16).
+* The chained layer: the GPU's own selection must be a valid top-k of the
+  oracle's fp64 scores (exactly the oracle's wherever no two candidates are
+  closer than the GPU's score error), and rows that agree must agree on the
+  table and the output.
+* Full-size workloads in the launch configuration the benchmark times, on
+  sampled requests the oracle recomputes from their own pages.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_block_amd as isb
+from indexer_selected_block_amd import workload as wl
+from oracle import decode as od
+
+from _util import (assert_scores_close, attn_tol, attended_vmax, host_inputs, oracle_attention,
+                   oracle_scores, sample_requests, selection_margin_ok, small_configs)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = small_configs()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a ROCm GPU")
+    isb.load_library()
+
+
+_cache = {}
+
+
+def _run_small(name):
+    if name not in _cache:
+        w = wl.make_workload(SMALL[name], device="cuda")
+        layer = isb.DecodeLayer(w)
+        layer.run()
+        torch.cuda.synchronize()
+        _cache[name] = (w, layer, host_inputs(w))
+    return _cache[name]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ index score
+@pytest.mark.parametrize("name", list(SMALL))
+def test_index_score_parity(name):
+    _say(f"[index_score] {name}")
+    w, layer, hi = _run_small(name)
+    assert_scores_close(layer.scores.cpu().numpy(), oracle_scores(hi))
+
+
+def test_index_score_output_contents_do_not_matter():
+    w, layer, hi = _run_small("spec_decode")
+    cfg = w.cfg
+    a = torch.full_like(layer.scores, float("nan"))
+    b = torch.zeros_like(layer.scores)
+    for buf in (a, b):
+        isb.index_score(w.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale, w.block_table,
+                        w.seq_lens, cfg.query_len, cfg.num_kv_heads, cfg.max_blocks, scores=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(a.view(torch.int32), layer.scores.view(torch.int32))
+
+
+def test_index_score_two_kv_heads_and_bf16_query_on_mxfp4():
+    # H_kv = 2 with 4 index heads (2 per group); MXFP4 keys with a bf16 index query
+    # take the bf16 tile path; e4m3 query on fp8 keys takes the converted tile path.
+    for base, kw in ((wl.CONFIGS["mxfp4"], dict(qidx_dtype="bf16")),
+                     (wl.CONFIGS["spec_decode"], dict(qidx_dtype="e4m3", num_idx_heads=2)),
+                     (wl.CONFIGS["mxfp4"], dict(num_kv_heads=2, num_q_heads=16))):
+        cfg = dataclasses.replace(wl.shrink(base, num_reqs=3, ctx_lo=200, ctx_hi=1400), **kw)
+        _say(f"[index_score variant] {cfg.name} {kw}")
+        w = wl.make_workload(cfg, device="cuda")
+        s = isb.index_score(w.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale,
+                            w.block_table, w.seq_lens, cfg.query_len, cfg.num_kv_heads, cfg.max_blocks)
+        torch.cuda.synchronize()
+        assert_scores_close(s.cpu().numpy(), oracle_scores(host_inputs(w)))
+
+
+# ------------------------------------------------------------------ top-k
+def _adversarial_scores(rng, H_kv, T, MB, K):
+    palette = np.array([0.5, -0.0, 0.0, 1.0, np.inf, -np.inf, np.nan, 3.0, -2.0, 1e-30, -1e30],
+                       dtype=np.float32)
+    s = rng.standard_normal((H_kv, T, MB)).astype(np.float32)
+    tie_rows = rng.random((H_kv, T)) < 0.5
+    pal = palette[rng.integers(0, len(palette), (H_kv, T, MB))]
+    s[tie_rows] = pal[tie_rows]
+    return s
+
+
+def _lengths_covering(rng, R, q_len, MB, K):
+    # causal block counts 0, 1, K-1, K, K+1 and MB all occur
+    special = [0, 1, 128 * (K - 1), 128 * K, 128 * K + 1, 128 * MB, 128 * (K + 1) + 5, 127]
+    lens = rng.integers(0, 128 * MB + 1, R)
+    lens[: min(R, len(special))] = [min(x, 128 * MB) for x in special[:R]]
+    return lens.astype(np.int32)
+
+
+@pytest.mark.parametrize("q_len,H_kv", [(1, 1), (4, 1), (2, 2)])
+@pytest.mark.parametrize("K", [1, 2, 7, 16, 32])
+def test_topk_bit_exact(K, q_len, H_kv):
+    rng = np.random.default_rng(1000 + K * 10 + q_len + H_kv)
+    MB, R = max(K + 3, 48), 24
+    lens = _lengths_covering(rng, R, q_len, MB, K)
+    s = _adversarial_scores(rng, H_kv, R * q_len, MB, K)
+    ref = od.topk_select(s, lens, q_len, K)
+    got = isb.topk_select(torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), q_len, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("MB,R,q_len,K", [(8192, 8, 2, 32), (256, 1075, 4, 16), (512, 128, 1, 16),
+                                          (1024, 64, 1, 16)])
+def test_topk_full_size_shapes(MB, R, q_len, K):
+    _say(f"[topk] MB={MB} rows={R * q_len}")
+    rng = np.random.default_rng(MB + R)
+    lens = rng.integers(0, 128 * MB + 1, R).astype(np.int32)
+    lens[0] = 128 * MB
+    lens[1] = 0
+    s = rng.standard_normal((1, R * q_len, MB)).astype(np.float32)
+    s[0, :, ::7] = np.round(s[0, :, ::7])          # plenty of exact ties
+    ref = od.topk_select(s, lens, q_len, K)
+    got = isb.topk_select(torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), q_len, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ emit
+@pytest.mark.parametrize("ppb", [8, 1])
+@pytest.mark.parametrize("H_kv,q_len", [(1, 1), (1, 4), (2, 3)])
+def test_emit_bit_exact(ppb, H_kv, q_len):
+    rng = np.random.default_rng(ppb * 7 + H_kv + q_len)
+    R, MB, K = 19, 40, 9
+    lens = _lengths_covering(rng, R, q_len, MB, K)
+    bt = rng.integers(0, 5000, (R, MB)).astype(np.int32)
+    topk = od.topk_select(rng.standard_normal((H_kv, R * q_len, MB)), lens, q_len, K)
+    sbt, sctx = od.emit_sparse_block_table(topk, bt, lens, q_len, H_kv, K, ppb)
+    g_sbt, g_sctx = isb.emit_sparse_block_table(torch.from_numpy(topk).cuda(), torch.from_numpy(bt).cuda(),
+                                                torch.from_numpy(lens).cuda(), q_len, ppb)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_sbt.cpu().numpy(), sbt)
+    assert np.array_equal(g_sctx.cpu().numpy(), sctx)
+
+
+# ------------------------------------------------------------------ attention
+def _synthetic_table(hi, seed):
+    cfg = hi["cfg"]
+    rng = np.random.default_rng(seed)
+    T = cfg.num_tokens
+    s = rng.standard_normal((cfg.num_kv_heads, T, cfg.max_blocks))
+    topk = od.topk_select(s, hi["seq_lens"], cfg.query_len, cfg.top_k)
+    return od.emit_sparse_block_table(topk, hi["block_table"], hi["seq_lens"], cfg.query_len,
+                                      cfg.num_kv_heads, cfg.top_k, cfg.pages_per_block)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_sparse_pa_parity(name):
+    _say(f"[sparse_pa] {name}")
+    w, layer, hi = _run_small(name)
+    cfg = w.cfg
+    sbt, sctx = _synthetic_table(hi, 5)
+    ref = oracle_attention(hi, sbt, sctx)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all(), "NaN in attention output (poison read?)"
+    tol = attn_tol(cfg.kv_dtype, attended_vmax(hi, sbt, sctx))
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"max |err| {err:.4g} > {tol:.4g}"
+    empty = np.nonzero(sctx.reshape(cfg.num_tokens, cfg.num_kv_heads).sum(axis=1) == 0)[0]
+    assert (got[empty] == 0).all()
+
+
+def test_sparse_pa_every_block_is_dense_attention():
+    # top-k >= every row's block count: the sparse decode is dense causal attention.
+    cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=4, ctx_lo=100, ctx_hi=2000, top_k=16)
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    topk = od.topk_select(np.zeros((1, cfg.num_tokens, cfg.max_blocks)), hi["seq_lens"], 1, 16)
+    assert (topk[0, :, :] >= 0).sum() == sum(-(-int(L) // 128) for L in hi["seq_lens"])
+    sbt, sctx = od.emit_sparse_block_table(topk, hi["block_table"], hi["seq_lens"], 1, 1, 16, 8)
+    assert list(sctx) == list(hi["seq_lens"])
+    ref = oracle_attention(hi, sbt, sctx)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(), 16, 1, w.sm_scale)
+    torch.cuda.synchronize()
+    tol = attn_tol("fp8", attended_vmax(hi, sbt, sctx))
+    assert np.abs(out.float().cpu().numpy() - ref).max() <= tol
+
+
+def test_sparse_pa_buffer_contents_do_not_matter():
+    w, layer, hi = _run_small("long_context")
+    cfg = w.cfg
+    outs = []
+    for fill in (float("nan"), 0.0):
+        out = torch.full((cfg.num_tokens, cfg.num_q_heads, 128), fill, dtype=torch.bfloat16, device="cuda")
+        ws = torch.full_like(layer.workspace, 0xFF)
+        if fill == 0.0:
+            ws.zero_()
+        isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                             layer.sparse_bt, layer.sparse_ctx, cfg.num_q_heads, cfg.num_kv_heads,
+                             w.sm_scale, out=out, workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), layer.out.view(torch.int16))
+
+
+# ------------------------------------------------------------------ chained layer
+def _check_chain(hi, scores_gpu, topk_gpu, sbt_gpu, sctx_gpu, out_gpu, ref, bt_global, toks=None):
+    cfg = hi["cfg"]
+    ql, H_kv, K = cfg.query_len, cfg.num_kv_heads, cfg.top_k
+    T = len(hi["seq_lens"]) * ql
+    assert_scores_close(scores_gpu, ref["scores"])
+    with np.errstate(invalid="ignore"):
+        err_row = np.where(np.isfinite(ref["scores"]), np.abs(scores_gpu - ref["scores"]), 0).max(axis=-1)
+    agree = np.zeros((H_kv, T), dtype=bool)
+    for g in range(H_kv):
+        for t in range(T):
+            r, i = divmod(t, ql)
+            nt = od.num_blocks(od.causal_length(hi["seq_lens"][r], ql, i))
+            if np.array_equal(topk_gpu[g, t], ref["topk"][g, t]):
+                agree[g, t] = True
+            else:
+                tol = 2 * err_row[g, t] + 1e-12
+                assert selection_margin_ok(ref["scores"][g, t], nt, K, list(topk_gpu[g, t]), tol), \
+                    f"row ({g},{t}): GPU selection is not a top-{K} of the oracle scores"
+    assert agree.mean() >= 0.9, f"only {agree.mean():.2%} of selections agree"
+    # the table the GPU emitted from its own selection, checked against the oracle's emit
+    sbt_ref, sctx_ref = od.emit_sparse_block_table(topk_gpu, bt_global, hi["seq_lens"], ql, H_kv, K,
+                                                   cfg.pages_per_block)
+    assert np.array_equal(sbt_gpu, sbt_ref) and np.array_equal(sctx_gpu, sctx_ref)
+    rows = [t for t in range(T) if agree[:, t].all()]
+    vmax = attended_vmax(hi, ref["sparse_bt"], ref["sparse_ctx"])
+    err = np.abs(out_gpu[rows] - ref["out"][rows]).max() if rows else 0.0
+    assert err <= attn_tol(cfg.kv_dtype, vmax), f"attention err {err:.4g}"
+
+
+def _oracle_layer(hi):
+    cfg = hi["cfg"]
+    return od.decode_layer(hi["q"], hi["q_idx"], hi["idx_pool"], cfg.idx_dtype, hi["idx_scale"],
+                           hi["k_pool"], hi["v_pool"], cfg.kv_dtype, hi["k_scale"], hi["v_scale"],
+                           hi["block_table"], hi["seq_lens"], cfg.query_len, cfg.num_kv_heads,
+                           cfg.max_blocks, cfg.top_k, cfg.pages_per_block, hi["sm_scale"])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_chain(name):
+    _say(f"[chain] {name}")
+    w, layer, hi = _run_small(name)
+    ref = _oracle_layer(hi)
+    _check_chain(hi, layer.scores.cpu().numpy().astype(np.float64), layer.topk.cpu().numpy(),
+                 layer.sparse_bt.cpu().numpy(), layer.sparse_ctx.cpu().numpy(),
+                 layer.out.float().cpu().numpy(), ref, hi["block_table"])
+
+
+# ------------------------------------------------------------------ full size, sampled
+FULL_SAMPLES = {"tiny_bf16": [0, 1, 2, 3], "fp8_decode": [3, 77], "spec_decode": None,
+                "mxfp4": [5, 60], "long_context": [6]}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_full_size_sampled(name):
+    cfg = wl.CONFIGS[name]
+    _say(f"[full] {name}: generating")
+    w = wl.make_workload(cfg, device="cuda")
+    layer = isb.DecodeLayer(w)
+    layer.run()
+    torch.cuda.synchronize()
+    reqs = FULL_SAMPLES[name]
+    if reqs is None:  # two live requests and one pad request
+        lens = w.seq_lens.cpu().numpy()
+        reqs = [int(np.nonzero(lens > 0)[0][0]), int(np.nonzero(lens > 0)[0][-1]), int(np.nonzero(lens == 0)[0][0])]
+    _say(f"[full] {name}: oracle on requests {reqs}")
+    hi, toks = sample_requests(w, reqs)
+    ref = _oracle_layer(hi)
+    H_kv = cfg.num_kv_heads
+    rows = [t * H_kv + g for t in toks for g in range(H_kv)]
+    bt_global = w.block_table[reqs].cpu().numpy()
+    _check_chain(hi, layer.scores[:, toks, :].cpu().numpy().astype(np.float64),
+                 layer.topk[:, toks, :].cpu().numpy(), layer.sparse_bt[rows].cpu().numpy(),
+                 layer.sparse_ctx[rows].cpu().numpy(), layer.out[toks].float().cpu().numpy(), ref,
+                 bt_global)
+    del w, layer
+    torch.cuda.empty_cache()

@@ -1,0 +1,96 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/isb.h
+declares, and rejects bad arguments before touching a GPU.  No kernel runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from indexer_selected_block_amd import binding
+from indexer_selected_block_amd.build import LIB_PATH, build_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isb.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        build_library()
+    return binding.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(isb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("isb_index_score", "isb_topk_select", "isb_emit_sparse_block_table",
+              "isb_sparse_pa_decode", "isb_sparse_pa_workspace_bytes", "isb_strerror", "isb_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) == set(binding.EXPORTED)
+
+
+def test_version_and_strerror(lib):
+    assert lib.isb_version() >= 100
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.isb_strerror(s)
+    assert b"unknown" in lib.isb_strerror(-99)
+
+
+NULL = None
+
+
+def test_argument_checks_return_before_any_launch(lib):
+    # null pointers
+    assert lib.isb_index_score(NULL, NULL, 0, 1, NULL, 0, 1.0, 1, NULL, 1, NULL, 1, 1, 1, 1, NULL) == -1
+    assert lib.isb_topk_select(NULL, NULL, NULL, 1, 1, 1, 1, 1, NULL) == -1
+    assert lib.isb_emit_sparse_block_table(NULL, NULL, NULL, 1, NULL, 1, 1, 1, 1, 8, NULL, NULL) == -1
+    assert lib.isb_sparse_pa_decode(NULL, NULL, 0, NULL, NULL, 1, 1, 1.0, 1.0, NULL, 1, NULL, 1, 16, 1,
+                                    128, 0.1, NULL, 0, NULL) == -1
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
+    # dtypes
+    assert lib.isb_index_score(NULL, p, 7, 1, p, 0, 1.0, 1, p, 1, p, 1, 1, 1, 1, p) == -2
+    assert lib.isb_index_score(NULL, p, 2, 1, p, 0, 1.0, 1, p, 1, p, 1, 1, 1, 1, p) == -2   # MXFP4 query
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 9, 1, 1.0, 1.0, p, 1, p, 1, 16, 1, 128, 0.1,
+                                    p, 1 << 20, p) == -2
+    # shapes
+    assert lib.isb_index_score(NULL, p, 0, 3, p, 0, 1.0, 1, p, 4, p, 1, 1, 2, 4, p) == -3       # 3 % 2
+    assert lib.isb_index_score(NULL, p, 0, 1, p, 0, 1.0, 1, p, 4, p, 1, 1, 1, 5, p) == -3       # MB > stride
+    assert lib.isb_topk_select(NULL, p, p, 1, 1, 1, 4, 5, p) == -3                              # K > MB
+    assert lib.isb_topk_select(NULL, p, p, 1, 1, 1, 4, 0, p) == -3
+    assert lib.isb_emit_sparse_block_table(NULL, p, p, 4, p, 1, 1, 1, 4, 4, p, p) == -3          # ppb 4
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 16, 1, 64, 0.1,
+                                    p, 1 << 20, p) == -3                                         # head_dim
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 32, 1, 128, 0.1,
+                                    p, 1 << 20, p) == -3                                         # G = 32
+    # workspace
+    need = lib.isb_sparse_pa_workspace_bytes(4, 16, 1, 128, 1)
+    assert need > 0
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 4, 16, 1, 128, 0.1,
+                                    p, need - 1, p) == -4
+
+
+def test_workspace_query(lib):
+    # split-K partials: rows x splits x 16 heads x (128 + 2) floats
+    for T, stride, dt in [(128, 128, 1), (4300, 128, 1), (64, 16, 2), (16, 256, 1), (4, 32, 0)]:
+        n = lib.isb_sparse_pa_workspace_bytes(T, 16, 1, stride, dt)
+        assert n > 0 and n % (16 * 130 * 4) == 0
+        splits = n // (16 * 130 * 4) // T
+        assert 1 <= splits <= stride
+    assert lib.isb_sparse_pa_workspace_bytes(0, 16, 1, 128, 1) == 0
+    assert lib.isb_sparse_pa_workspace_bytes(4, 16, 1, 128, 5) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    with pytest.raises(RuntimeError, match="ROCm GPU"):
+        binding.topk_select(torch.zeros(1, 1, 4), torch.ones(1, dtype=torch.int32), 1, 2)
