@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of one indexed block-sparse paged-attention decode layer on one MI355X.
+
+A step is one pass of the whole path over one batch: index_score ->
+topk_select -> emit_sparse_block_table -> sparse_pa_decode (+ its reduce), on
+the fp8 decode workload (128 requests x 1 token, contexts U{16384..65536},
+fp8 K/V and index cache, 16 query heads per KV head, top-k 16 blocks) unless
+--config names another.  Inputs are synthetic and resident in HBM before the
+timed region starts.
+
+Prints one JSON line: decode tokens/s of the whole step (value), the
+attended-KV HBM rate of the attention kernels, per-kernel durations measured
+with HIP events on the launch stream, a roofline entry for the dominant
+kernel (and one for the attention), and the CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode tokens/s + attended-KV HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+IDX_BYTES = {"bf16": 256, "fp8": 128, "mxfp4": 68}           # bytes per index key
+KV_BYTES = {"bf16": 256, "fp8": 128, "mxfp4": 68}            # bytes per token, one of K or V
+Q_BYTES = {"bf16": 2, "e4m3": 1}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="fp8_decode")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="independent copies of the layer's caches, used round-robin")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle baseline (0 skips it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 10 times (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 10}))
+
+
+def algorithmic_bytes(w, sparse_ctx):
+    """Bytes each kernel must move for this batch (Measurement)."""
+    cfg = w.cfg
+    lens = w.seq_lens.cpu().tolist()
+    ql, T = cfg.query_len, cfg.num_tokens
+    n_req_blocks = sum(-(-L // 128) for L in lens)
+    n_tok_blocks = 0
+    for r, L in enumerate(lens):
+        for i in range(ql):
+            n_tok_blocks += -(-max(0, L - (ql - 1 - i)) // 128)
+    qidx = T * cfg.num_idx_heads * 128 * Q_BYTES[cfg.qidx_dtype]
+    score = (sum(lens) * IDX_BYTES[cfg.idx_dtype] + qidx + 4 * n_req_blocks + 4 * len(lens)
+             + 4 * cfg.num_kv_heads * n_tok_blocks)
+    topk = 4 * cfg.num_kv_heads * n_tok_blocks + 4 * cfg.num_kv_heads * T * cfg.top_k
+    rows = T * cfg.num_kv_heads
+    slots = cfg.top_k * cfg.pages_per_block
+    # emit: the selection and the table entries it names in, the page table and lengths out
+    emit = 4 * cfg.num_kv_heads * T * cfg.top_k * 2 + 4 * rows * (slots + 1) + 4 * len(lens)
+    ctx = sparse_ctx.cpu().long()
+    attended = int(ctx.sum()) * 2 * KV_BYTES[cfg.kv_dtype]
+    ptok = 128 // cfg.pages_per_block
+    pages = int(((ctx + ptok - 1) // ptok).sum())
+    attn = (attended + T * cfg.num_q_heads * 128 * (Q_BYTES[cfg.q_dtype] + 2) + 4 * pages + 4 * rows)
+    return {"index_score": score, "topk_select": topk, "emit_sparse_block_table": emit,
+            "sparse_pa_decode": attn}, attended
+
+
+def kernel_sources_sha():
+    """Hash of each kernel's source file, to tell whether stored counters still apply."""
+    csrc = os.path.join(ROOT, "indexer_selected_block_amd", "csrc")
+    files = {"index_score": "index_score.hip", "topk_select": "topk_select.hip",
+             "emit_sparse_block_table": "emit.hip", "sparse_pa_decode": "sparse_pa.hip"}
+    common = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("isb_device.h", "isb_host.h"))
+    return {k: hashlib.sha256(common + open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
+            for k, f in files.items()}
+
+
+def stored_traffic(config, kernel, sha):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on this exact kernel source and workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(config, {}).get(kernel)
+    if not ent or ent.get("source_sha") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, as it is, on whole requests of the same workload until the
+    budget is spent; tokens/s over the requests it finished."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import decode as od
+    from oracle import formats
+
+    cfg = w.cfg
+    ppb = cfg.pages_per_block
+    done_tokens, elapsed, nreq = 0, 0.0, 0
+    order = list(range(cfg.total_reqs))
+    with threadpool_limits(limits=1):
+        for r in order:
+            if elapsed >= budget_s and nreq >= 2:
+                break
+            L = int(w.seq_lens[r])
+            nb = -(-L // 128)
+            if nb == 0:
+                continue
+            ids = w.block_table[r, :nb].long()
+            # copy this request's pages to the host (not timed), renumbered 0..nb-1
+            idx_pool = w.idx_pool[ids].cpu().numpy()
+            kv = lambda p: p.view(p.shape[0] // ppb, -1)[ids].cpu().reshape(nb * ppb, -1).numpy()  # noqa: E731
+            k_pool, v_pool = kv(w.k_pool), kv(w.v_pool)
+            toks = torch.arange(r * cfg.query_len, (r + 1) * cfg.query_len, device=w.q.device)
+            qb = w.q[toks].cpu().numpy()
+            qib = w.q_idx[toks].cpu().numpy()
+            bt = np.arange(nb, dtype=np.int64)[None, :]
+            t0 = time.perf_counter()
+            q = formats.decode_query(qb, cfg.q_dtype)
+            q_idx = formats.decode_query(qib, cfg.qidx_dtype)
+            od.decode_layer(q, q_idx, idx_pool, cfg.idx_dtype, w.idx_scale, k_pool, v_pool,
+                            cfg.kv_dtype, w.k_scale, w.v_scale, bt, [L], cfg.query_len,
+                            cfg.num_kv_heads, nb, cfg.top_k, ppb, w.sm_scale)
+            elapsed += time.perf_counter() - t0
+            done_tokens += cfg.query_len
+            nreq += 1
+    return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nreq} whole requests of the same workload ({done_tokens} query tokens), "
+                      f"{elapsed:.1f} s of CPU, numpy float64 with BLAS limited to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the path has no "
+                                   "multi-GPU part (see DESIGN.md for how it would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import indexer_selected_block_amd as isb
+    from indexer_selected_block_amd import workload as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = wl.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    print(f"[bench] building {args.config} x{args.layers} on {torch.cuda.get_device_name(0)}",
+          file=sys.stderr, flush=True)
+    layers = []
+    for li in range(args.layers):
+        c = cfg if li == 0 else dataclasses.replace(cfg, seed=cfg.seed + 1000 * li)
+        layers.append(isb.DecodeLayer(wl.make_workload(c, device=dev)))
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        layers[s % len(layers)].run()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, nothing else on the stream
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        layers[s % len(layers)].run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    T = cfg.num_tokens
+    ms_per_step = 1000.0 * elapsed / args.steps
+
+    # ---- per-kernel durations: HIP events on the launch stream around each call
+    stream = torch.cuda.current_stream(dev)
+    names = ["index_score", "topk_select", "emit_sparse_block_table", "sparse_pa_decode"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        L = layers[s % len(layers)]
+        w, c = L.w, L.w.cfg
+        e = ev[s]
+        e[0].record(stream)
+        isb.index_score(w.q_idx, c.qidx_dtype, w.idx_pool, c.idx_dtype, w.idx_scale, w.block_table,
+                        w.seq_lens, c.query_len, c.num_kv_heads, c.max_blocks, scores=L.scores)
+        e[1].record(stream)
+        isb.topk_select(L.scores, w.seq_lens, c.query_len, c.top_k, topk_idx=L.topk)
+        e[2].record(stream)
+        isb.emit_sparse_block_table(L.topk, w.block_table, w.seq_lens, c.query_len, c.pages_per_block,
+                                    sparse_bt=L.sparse_bt, sparse_ctx=L.sparse_ctx)
+        e[3].record(stream)
+        isb.sparse_pa_decode(w.q, c.q_dtype, w.k_pool, w.v_pool, c.kv_dtype, w.k_scale, w.v_scale,
+                             L.sparse_bt, L.sparse_ctx, c.num_q_heads, c.num_kv_heads, w.sm_scale,
+                             out=L.out, workspace=L.workspace)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    dur_ms = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+              for i, n in enumerate(names)}
+
+    w0 = layers[0].w
+    alg, attended = algorithmic_bytes(w0, layers[0].sparse_ctx)
+    shas = kernel_sources_sha()
+
+    def roof(kernel):
+        gbps = alg[kernel] / (dur_ms[kernel] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": stored_traffic(args.config, kernel, shas[kernel]),
+                "kernel": kernel, "avg_ms": round(dur_ms[kernel], 5),
+                "algorithmic_bytes": alg[kernel]}
+
+    dominant = max(names, key=lambda n: dur_ms[n])
+    attn_gbps = attended / (dur_ms["sparse_pa_decode"] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3->bf16 mfma, f32 accumulate" if cfg.kv_dtype == "fp8" else f"{cfg.kv_dtype} in, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "requests": cfg.total_reqs,
+                   "query_len": cfg.query_len, "tokens_per_step": T, "top_k": cfg.top_k,
+                   "q_heads_per_kv": cfg.num_q_heads // cfg.num_kv_heads,
+                   "index_heads": cfg.num_idx_heads, "kv_cache": cfg.kv_dtype,
+                   "index_cache": cfg.idx_dtype, "layers": args.layers},
+        "attended_kv_GBps": round(attn_gbps, 1),
+        "attended_kv_pct_hbm_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 2),
+        "kernel_ms": {k: round(v, 5) for k, v in dur_ms.items()},
+        "roofline": roof(dominant),
+        "roofline_sparse_pa_decode": roof("sparse_pa_decode"),
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

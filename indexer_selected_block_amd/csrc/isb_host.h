@@ -26,9 +26,15 @@ inline int64_t idx_page_bytes(int dt) {
 
 // Split-K plan of isb_sparse_pa_decode; shared by the workspace query so the
 // two always agree.  A split is one workgroup of four waves.
+//  16-token pages: each wave attends a run of `pages_per_wave` pages (at most
+//    8 fp8 / 4 bf16 pages, whose loads it issues at once); the run length is
+//    the smallest that covers the batch with ~2048 waves (8 per CU), so one
+//    round of waves has the whole batch in flight.
+//  128-token MXFP4 pages: the workgroup walks `pages_per_split` pages together.
 struct PaPlan {
   int rows;             // num_tokens * num_kv_heads
   int max_pages;        // sparse_bt_stride
+  int pages_per_wave;   // 16-token pages: run of one wave
   int pages_per_split;  // pages one workgroup attends
   int splits;           // workgroups per row
 };
@@ -37,22 +43,30 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   PaPlan p;
   p.rows = num_tokens * num_kv_heads;
   p.max_pages = sparse_bt_stride;
-  // 16-token pages: at least 8 pages (2 a wave) per split; 128-token MXFP4
-  // pages: at least one page (8 tiles, 2 a wave).
-  const int min_pages = kv_dtype == ISB_MXFP4 ? 1 : 8;
-  const int target_wgs = 1024;
-  int want = (target_wgs + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
-  int most = (p.max_pages + min_pages - 1) / min_pages;
-  if (want > most) want = most;
-  if (want < 1) want = 1;
-  p.pages_per_split = (p.max_pages + want - 1) / want;
-  if (p.pages_per_split < 1) p.pages_per_split = 1;
+  if (kv_dtype == ISB_MXFP4) {
+    const int target_wgs = 1024;
+    int want = (target_wgs + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
+    if (want > p.max_pages) want = p.max_pages;
+    if (want < 1) want = 1;
+    p.pages_per_wave = 0;
+    p.pages_per_split = (p.max_pages + want - 1) / want;
+  } else {
+    const int max_run = kv_dtype == ISB_BF16 ? 4 : 8;
+    const long long total = (long long)p.rows * p.max_pages;
+    const long long waves = 256LL * 8;
+    long long run = (total + waves - 1) / waves;
+    if (run > max_run) run = max_run;
+    if (run < 1) run = 1;
+    p.pages_per_wave = (int)run;
+    p.pages_per_split = 4 * p.pages_per_wave;
+  }
   p.splits = (p.max_pages + p.pages_per_split - 1) / p.pages_per_split;
   if (p.splits < 1) p.splits = 1;
   return p;
 }
 
-// Partial results per (row, split): 16 heads x 128 dims fp32, then 16 x (m, l).
+// Workspace: partial results per (row, split): 16 heads x 128 dims fp32, then
+// 16 x (m, l).
 constexpr size_t kPartialO = 16 * 128;
 constexpr size_t kPartialML = 16 * 2;
 

@@ -1,5 +1,5 @@
 // isb_sparse_pa_decode: split-K flash decode over the selected pages, then a
-// reduce launch that merges the splits.
+// reduce launch that merges the splits of rows that needed more than one.
 //
 // The decode call of the vLLM API page for sparse_attention_msa
 // (minimax_m3_sparse_attn_decode_aiter with the emitted sparse_block_table and
@@ -53,7 +53,7 @@ struct PaArgs {
   int64_t num_pages;
   float qk_scale;  // sm_scale * k_scale * log2(e)
   float v_scale;
-  int q_dt, sbt_stride, H_q, H_kv, G, splits, pps;
+  int q_dt, sbt_stride, H_q, H_kv, G, splits, pps, ppw;
 };
 
 constexpr int kPaWaves = 4;
@@ -107,6 +107,58 @@ __device__ __forceinline__ void attend_tile(Softmax& st, const bf16x8 (&qb)[4], 
   for (int dt = 0; dt < 8; ++dt) {
     st.o[dt] *= alpha;
     st.o[dt] = mfma_16x16x16_bf16(vt[dt], pb, st.o[dt]);
+  }
+}
+
+// Two 16-key tiles under one softmax update.  The PV product runs on
+// v_mfma_f32_16x16x32_bf16 with k = 8 g + e: e < 4 are keys 4 g + e of the
+// first tile and e >= 4 keys 4 g + e - 4 of the second, which is exactly what
+// the two S^T results leave in this lane; V^T is concatenated the same way.
+__device__ __forceinline__ void attend_pair(Softmax& st, const bf16x8 (&qb)[4],
+                                            const bf16x8 (&kb0)[4], const bf16x8 (&kb1)[4],
+                                            const bf16x4 (&vt0)[8], const bf16x4 (&vt1)[8],
+                                            int nvalid0, int nvalid1, bool bad0, bool bad1,
+                                            float qk_scale, int g) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s0 = mfma_16x16x32_bf16(kb0[j], qb[j], s0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s1 = mfma_16x16x32_bf16(kb1[j], qb[j], s1);
+  float z[8];
+  float tmax = neg_inf();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v0 = bad0 ? qnan() : s0[e] * qk_scale;
+    float v1 = bad1 ? qnan() : s1[e] * qk_scale;
+    z[e] = (4 * g + e < nvalid0) ? v0 : neg_inf();
+    z[4 + e] = (4 * g + e < nvalid1) ? v1 : neg_inf();
+    tmax = fmaxf(tmax, fmaxf(z[e], z[4 + e]));
+  }
+  tmax = max_over_groups(tmax);
+  const float m_new = fmaxf(st.m, tmax);
+  float psum = 0.f;
+  bf16x8 pb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = exp2f(z[e] - m_new);
+    psum += p;
+    pb[e] = (__bf16)p;
+  }
+  // Rescale the output only when some head's running max moved (a wave-uniform
+  // branch); after the first pages this is rare.
+  if (__ballot(m_new > st.m)) {
+    const float alpha = exp2f(st.m - m_new);  // 0 while m = -inf
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+  }
+  st.l += psum;
+  st.m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const bf16x8 va = {vt0[dt][0], vt0[dt][1], vt0[dt][2], vt0[dt][3],
+                       vt1[dt][0], vt1[dt][1], vt1[dt][2], vt1[dt][3]};
+    st.o[dt] = mfma_16x16x32_bf16(va, pb, st.o[dt]);
   }
 }
 
@@ -177,6 +229,7 @@ __device__ __forceinline__ bool page_ok(int64_t id, int64_t n) { return id >= 0 
 template <int KV_DT>
 __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   constexpr int P = KV_DT == ISB_MXFP4 ? 128 : 16;
+  constexpr int MAXP = KV_DT == ISB_BF16 ? 4 : 8;  // 16-token pages a wave keeps in flight
   __shared__ float s_m[kPaWaves][16];
   __shared__ float s_l[kPaWaves][16];
   __shared__ float s_o[kPaWaves][16][kHeadDim + 4];
@@ -185,15 +238,33 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   const int row = blockIdx.x, split = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int n_tok = a.sctx[row];
-  if (n_tok <= 0) return;
-  // a row never lists more pages than its table row holds
-  const int npages = min((n_tok + P - 1) / P, a.sbt_stride);
-  const int p0 = split * a.pps;
-  if (p0 >= npages) return;
-  const int p1 = min(npages, p0 + a.pps);
   const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
+  const int p0 = split * a.pps;
+  // The page ids of this wave's run are read together with the row length
+  // (not after it), so the K/V gathers start one memory round trip sooner.
+  const int wb = p0 + wave * a.ppw;
+  int my_id = -1;
+  if constexpr (KV_DT != ISB_MXFP4) {
+    if (lane < a.ppw && wb + lane < a.sbt_stride) my_id = pages[wb + lane];
+  }
+  const int n_tok = a.sctx[row];
+  const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);  // merge / output layout
+  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
+  if (n_tok <= 0) {  // an empty row attends nothing: split 0 writes its zeros
+    if (split == 0 && h < a.G) {
+      bf16x8 z;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) z[x] = (__bf16)0.f;
+      *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = z;
+    }
+    return;
+  }
+  // a row never lists more pages than its table row holds
+  const int npages = min((n_tok + P - 1) / P, a.sbt_stride);
+  if (p0 >= npages) return;
+  const int p1 = min(npages, p0 + a.pps);
+  const int live = (npages + a.pps - 1) / a.pps;  // splits of this row that have pages
 
   // Q^T operand: head kvh * G + c, dims 32 g .. 32 g + 31 (zero past G).
   bf16x8 qb[4];
@@ -216,35 +287,47 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (KV_DT != ISB_MXFP4) {
+    // Each wave owns a run of up to MAXP consecutive pages and issues every
+    // load of that run before any math, so a wave keeps its whole share of the
+    // row in flight (the split plan sizes runs so ~2048 waves cover a batch).
     constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
-    int p = p0 + wave;
-    PageRegs<KV_DT> cur, nxt;
-    int64_t id = p < p1 ? pages[p] : 0;
-    bool ok = page_ok(id, a.num_pages);
     const int64_t hstride = (int64_t)a.H_kv * PB;  // bytes per page id (all heads)
     const int64_t hoff = (int64_t)kvh * PB;
-    if (p < p1 && ok) load_page16<KV_DT>(cur, a.kp + id * hstride + hoff, a.vp + id * hstride + hoff, c, g);
-    while (p < p1) {
-      const int pn = p + kPaWaves;
-      const int64_t idn = pn < p1 ? pages[pn] : 0;
-      const bool okn = page_ok(idn, a.num_pages);
-      if (pn < p1 && okn)
-        load_page16<KV_DT>(nxt, a.kp + idn * hstride + hoff, a.vp + idn * hstride + hoff, c, g);
-      const int nvalid = min(16, n_tok - p * 16);
-      bf16x8 kb[4];
-      bf16x4 vt[8];
-      if (ok) {
-        page16_operands<KV_DT>(cur, nvalid, g, kb, vt);
-      } else {
+    const int cnt = max(0, min(a.ppw, p1 - wb));
+    PageRegs<KV_DT> pr[MAXP];
+    bool ok[MAXP];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kb[j] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < MAXP; ++j) {
+      const int64_t id = __builtin_amdgcn_readlane(my_id, j);
+      ok[j] = j < cnt && page_ok(id, a.num_pages);
+      if (ok[j]) load_page16<KV_DT>(pr[j], a.kp + id * hstride + hoff, a.vp + id * hstride + hoff, c, g);
+    }
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) vt[dt] = bf16x4{0, 0, 0, 0};
+    for (int j = 0; j < MAXP; j += 2) {
+      if (j < cnt) {
+        const int nv0 = min(16, n_tok - (wb + j) * 16);
+        const int nv1 = j + 1 < cnt ? min(16, n_tok - (wb + j + 1) * 16) : 0;
+        bf16x8 kb0[4], kb1[4];
+        bf16x4 vt0[8], vt1[8];
+        if (ok[j]) {
+          page16_operands<KV_DT>(pr[j], nv0, g, kb0, vt0);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) kb0[x] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) vt0[dt] = bf16x4{0, 0, 0, 0};
+        }
+        if (j + 1 < cnt && ok[j + 1]) {
+          page16_operands<KV_DT>(pr[j + 1], nv1, g, kb1, vt1);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) kb1[x] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) vt1[dt] = bf16x4{0, 0, 0, 0};
+        }
+        attend_pair(st, qb, kb0, kb1, vt0, vt1, nv0, nv1, !ok[j], j + 1 < cnt && !ok[j + 1],
+                    a.qk_scale, g);
       }
-      attend_tile(st, qb, kb, vt, nvalid, !ok, a.qk_scale, g);
-      cur = nxt;
-      ok = okn;
-      p = pn;
     }
   } else {
     // MXFP4: the workgroup walks its pages together; V is staged in LDS.
@@ -275,7 +358,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int vt_tok = tile * 16 + 4 * g + e;
-            const bool live = 4 * g + e < nvalid;
+            const bool on = 4 * g + e < nvalid;
             const uint32_t sw = *reinterpret_cast<const uint32_t*>(s_v + kMxDataBytes + 4 * vt_tok);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
@@ -283,8 +366,8 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
               const uint32_t byte = s_v[vt_tok * 64 + (d >> 1)];
               const uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 0xFu);
               const float sc_v = e8m0_to_f32(sw >> (8 * (d >> 5)));
-              const bf16x2 pr = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, sc_v, 0);
-              vt[dt][e] = live ? pr[0] : (__bf16)0.f;
+              const bf16x2 pr2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, sc_v, 0);
+              vt[dt][e] = on ? pr2[0] : (__bf16)0.f;
             }
           }
         } else {
@@ -298,7 +381,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
     }
   }
 
-  // Merge the four waves in LDS and write this split's partial result.
+  // Merge the four waves in LDS.
   const float l_tot = sum_over_groups(st.l);
   if (lane < 16) {
     s_m[wave][c] = st.m;
@@ -309,7 +392,6 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) s_o[wave][c][16 * dt + 4 * g + e] = st.o[dt][e];
   __syncthreads();
-  const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
   float M = neg_inf();
 #pragma unroll
   for (int w = 0; w < kPaWaves; ++w) M = fmaxf(M, s_m[w][h]);
@@ -322,53 +404,64 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) O[x] += s_o[w][h][d0 + x] * wt;
   }
-  const size_t base = (size_t)row * a.splits + split;
-  float* po = a.part_o + (base * 16 + h) * kHeadDim + d0;
-  *reinterpret_cast<f32x4*>(po) = f32x4{O[0], O[1], O[2], O[3]};
-  *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[4], O[5], O[6], O[7]};
-  if ((threadIdx.x & 15) == 0) {
-    a.part_ml[(base * 16 + h) * 2 + 0] = M;
-    a.part_ml[(base * 16 + h) * 2 + 1] = L;
+
+  if (live > 1) {
+    // Split-K: publish this split's partial; the reduce launch merges them.
+    const size_t base = (size_t)row * a.splits + split;
+    float* po = a.part_o + (base * 16 + h) * kHeadDim + d0;
+    *reinterpret_cast<f32x4*>(po) = f32x4{O[0], O[1], O[2], O[3]};
+    *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[4], O[5], O[6], O[7]};
+    if ((threadIdx.x & 15) == 0) {
+      a.part_ml[(base * 16 + h) * 2 + 0] = M;
+      a.part_ml[(base * 16 + h) * 2 + 1] = L;
+    }
+    return;
+  }
+  // A row that fits one split is finished here; the reduce launch skips it.
+  if (h < a.G) {
+    const float inv = a.v_scale / L;
+    bf16x8 ob;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(O[x] * inv);
+    *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = ob;
   }
 }
 
-// One workgroup per row: merge the row's live splits, normalise, write bf16.
+// One workgroup per row with more than one split: merge the row's partial
+// results with log-sum-exp weights, normalise and write bf16.  Rows of one
+// split (and empty rows) were written by the decode launch.
 template <int P>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(PaArgs a) {
   const int row = blockIdx.x;
   const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
   if (h >= a.G) return;
-  const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int n_tok = a.sctx[row];
   const int npages = n_tok > 0 ? min((n_tok + P - 1) / P, a.sbt_stride) : 0;
   const int live = (npages + a.pps - 1) / a.pps;
-  float O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live > 0) {
-    float M = neg_inf();
-    for (int s = 0; s < live; ++s)
-      M = fmaxf(M, a.part_ml[(((size_t)row * a.splits + s) * 16 + h) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < live; ++s) {
-      const size_t base = ((size_t)row * a.splits + s) * 16 + h;
-      const float ms = a.part_ml[base * 2];
-      const float wt = ms == neg_inf() ? 0.f : exp2f(ms - M);
-      L += a.part_ml[base * 2 + 1] * wt;
-      const float* po = a.part_o + base * kHeadDim + d0;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+  if (live <= 1) return;
+  const int t = row / a.H_kv, kvh = row % a.H_kv;
+  const size_t b0 = (size_t)row * a.splits * 16 + h;
+  float M = neg_inf();
+  for (int s = 0; s < live; ++s) M = fmaxf(M, a.part_ml[(b0 + (size_t)s * 16) * 2]);
+  float L = 0.f, O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < live; ++s) {
+    const size_t b = b0 + (size_t)s * 16;
+    const float ms = a.part_ml[b * 2];
+    const float wt = ms == neg_inf() ? 0.f : exp2f(ms - M);
+    L += a.part_ml[b * 2 + 1] * wt;
+    const float* po = a.part_o + b * kHeadDim + d0;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        O[x] += x0[x] * wt;
-        O[4 + x] += x1[x] * wt;
-      }
+    for (int x = 0; x < 4; ++x) {
+      O[x] += x0[x] * wt;
+      O[4 + x] += x1[x] * wt;
     }
-    const float inv = a.v_scale / L;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) O[x] *= inv;
   }
+  const float inv = a.v_scale / L;
   bf16x8 ob;
 #pragma unroll
-  for (int x = 0; x < 8; ++x) ob[x] = (__bf16)O[x];
+  for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(O[x] * inv);
   *reinterpret_cast<bf16x8*>(a.out + ((size_t)t * a.H_q + kvh * a.G + h) * kHeadDim + d0) = ob;
 }
 
@@ -427,17 +520,19 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   a.G = num_q_heads / num_kv_heads;
   a.splits = plan.splits;
   a.pps = plan.pages_per_split;
+  a.ppw = plan.pages_per_wave;
   hipStream_t st = as_hip(stream);
   dim3 grid((unsigned)rows, plan.splits);
+  dim3 rgrid((unsigned)rows);
   if (kv_dtype == ISB_BF16) {
     hipLaunchKernelGGL(pa_decode_kernel<ISB_BF16>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(pa_reduce_kernel<16>, dim3((unsigned)rows), dim3(256), 0, st, a);
+    if (plan.splits > 1) hipLaunchKernelGGL(pa_reduce_kernel<16>, rgrid, dim3(256), 0, st, a);
   } else if (kv_dtype == ISB_FP8_E4M3) {
     hipLaunchKernelGGL(pa_decode_kernel<ISB_FP8_E4M3>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(pa_reduce_kernel<16>, dim3((unsigned)rows), dim3(256), 0, st, a);
+    if (plan.splits > 1) hipLaunchKernelGGL(pa_reduce_kernel<16>, rgrid, dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(pa_decode_kernel<ISB_MXFP4>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(pa_reduce_kernel<128>, dim3((unsigned)rows), dim3(256), 0, st, a);
+    if (plan.splits > 1) hipLaunchKernelGGL(pa_reduce_kernel<128>, rgrid, dim3(256), 0, st, a);
   }
   return launch_status();
 }
