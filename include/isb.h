@@ -50,8 +50,13 @@
  *                  128 x 4 B e8m0 (token j at 8192 + 4 j, scale s for
  *                  dims 32 s .. 32 s + 31)                       8704 B
  *  K/V caches, bf16 / fp8: 16-token pages, 8 per block; block b of a request
- *    is pages 8 block_table[r][b] + 0..7.  K page [16 tok][128 dim],
- *    V page [128 dim][16 tok] (dim-major).  fp8 values times k_scale/v_scale.
+ *    is pages 8 block_table[r][b] + 0..7.  With e bytes per element (1 or 2),
+ *    a page is 2048 e bytes in the order the kernel's lanes read it:
+ *      K: key c, dim d at 1024 ((d mod 32) div (16/e)) + 256 (d div 32)
+ *         + 16 c + e (d mod (16/e));
+ *      V: key t, dim d = 16 dt + c at 1024 (dt div (4/e)) + 256 (t div 4)
+ *         + 16 c + 4 e (dt mod (4/e)) + e (t mod 4).
+ *    fp8 values times k_scale / v_scale.
  *  K/V caches, MXFP4: one 8704 B page per block for K and one for V.
  *  A K/V page id holds one page per KV head, [num_pages][H_kv][page bytes];
  *  row (t, g) reads head g's page.  The index cache has one key per token,

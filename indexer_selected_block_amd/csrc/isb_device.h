@@ -59,6 +59,16 @@ __device__ __forceinline__ bf16x4 e4m3x4_to_bf16x4(uint32_t w) {
   return bf16x4{a[0], a[1], b[0], b[1]};
 }
 
+// Eight e4m3 bytes (dword lo: bytes 0..3, then dword hi) -> eight bf16.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                          __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)});
+}
+
 // Eight e2m1 nibbles of one dword (low nibble of byte 0 first) -> eight bf16,
 // each multiplied by `scale` (a power of two from an e8m0 byte).
 __device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t w, float scale) {

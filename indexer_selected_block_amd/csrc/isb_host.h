@@ -26,10 +26,10 @@ inline int64_t idx_page_bytes(int dt) {
 
 // Split-K plan of isb_sparse_pa_decode; shared by the workspace query so the
 // two always agree.  A split is one workgroup of four waves.
-//  16-token pages: each wave attends a run of `pages_per_wave` pages (at most
-//    8 fp8 / 4 bf16 pages, whose loads it issues at once); the run length is
-//    the smallest that covers the batch with ~2048 waves (8 per CU), so one
-//    round of waves has the whole batch in flight.
+//  16-token pages: each wave attends a run of `pages_per_wave` pages (1, 2, 4
+//    or 8 fp8 / up to 4 bf16 pages, whose loads it issues at once); the run
+//    is the shortest power of two that covers the batch with ~2048 waves (8
+//    per CU), so one round of waves has the whole batch in flight.
 //  128-token MXFP4 pages: the workgroup walks `pages_per_split` pages together.
 struct PaPlan {
   int rows;             // num_tokens * num_kv_heads
@@ -54,10 +54,10 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
     const int max_run = kv_dtype == ISB_BF16 ? 4 : 8;
     const long long total = (long long)p.rows * p.max_pages;
     const long long waves = 256LL * 8;
-    long long run = (total + waves - 1) / waves;
-    if (run > max_run) run = max_run;
-    if (run < 1) run = 1;
-    p.pages_per_wave = (int)run;
+    const long long need = (total + waves - 1) / waves;
+    int run = 1;  // a power of two: the kernel is specialised on it
+    while (run < need && run < max_run) run *= 2;
+    p.pages_per_wave = run;
     p.pages_per_split = 4 * p.pages_per_wave;
   }
   p.splits = (p.max_pages + p.pages_per_split - 1) / p.pages_per_split;

@@ -10,32 +10,37 @@
 //
 // Work decomposition.  A row's pages are cut into `splits` runs of
 // `pages_per_split`; one workgroup of four waves attends one run.  A wave
-// takes one 16-token tile at a time:
+// takes 16-token tiles:
 //   S^T (16 keys x 16 heads) = K_tile . Q^T      4 x v_mfma_f32_16x16x32_bf16
 //   online softmax in fp32 (row max over lane groups by lane shuffles)
-//   O^T (128 dims x 16 heads) += V^T_tile . P^T   8 x v_mfma_f32_16x16x16_bf16
+//   O^T (128 dims x 16 heads) += V^T . P^T       v_mfma_f32_16x16x32_bf16 for two
+//                                                tiles, 16x16x16 for one
 // The G <= 16 query heads of a KV group fill the MFMA's 16 columns, so K and V
 // bytes are read once per row and reused by every head.  K and V are
 // dequantised to bf16 in registers (exact for e4m3 and for e2m1 x 2^k); the
 // per-tensor fp8 scales and the softmax scale are folded into one logit
 // multiplier (k_scale sm_scale log2 e) and the output (v_scale).
 //
-// Layout of the operands (lane = 16 g + c):
+// Operand layout (lane = 16 g + c):
 //   K tile, A of QK:  key c of the tile, dims 32 g .. 32 g + 31 (MFMA j takes
 //                     dims 32 g + 8 j .. + 7);  Q^T, B of QK: head c, same dims;
 //   S^T result:       lane holds keys 4 g + e (e < 4) of head c;
 //   P^T, B of PV:     exactly that: head c, keys 4 g + e;
-//   V^T, A of PV:     dim 16 dt + c, keys 4 g + e - one dword of an fp8 V page
-//                     ([128 dim][16 tok]) per dim tile dt;
+//   V^T, A of PV:     dim 16 dt + c, keys 4 g + e;
 //   O^T result:       lane holds dims 16 dt + 4 g + e of head c.
 // Every value a lane holds belongs to its head c, so the softmax rescale of
 // the output is lane-local.
 //
-// 16-token (bf16 / fp8) pages go straight from HBM to registers with 16-byte
-// (K) and 4-byte (V) loads, the next page's loads issued before the current
-// page's math.  128-token MXFP4 pages are token-major, which puts a V tile's
-// keys for one dim in four different rows; the workgroup stages each V page in
-// LDS and lanes read their nibbles from there.
+// 16-token (bf16 / fp8) pages are stored lane-native: the 16-byte chunk h of
+// lane l sits at byte 1024 h + 16 l of the K page and of the V page (K: dims
+// 32 g + 16 h .. of key c for fp8; V: dim tiles 4 h .. 4 h + 3, keys 4 g ..
+// 4 g + 3 of dim c for fp8), so every load instruction reads one contiguous
+// KiB and a page costs 4 (fp8) or 8 (bf16) loads a lane.  A wave issues every
+// load of its run of pages before any math, with no branch between them, so
+// its whole share of the row is in flight at once.
+// 128-token MXFP4 pages are token-major (the page format of the MXFP4 cache),
+// which puts a V tile's keys for one dim in four different rows; the
+// workgroup stages each V page in LDS and lanes read their nibbles from there.
 #include "isb_device.h"
 #include "isb_host.h"
 
@@ -53,17 +58,21 @@ struct PaArgs {
   int64_t num_pages;
   float qk_scale;  // sm_scale * k_scale * log2(e)
   float v_scale;
-  int q_dt, sbt_stride, H_q, H_kv, G, splits, pps, ppw;
+  int sbt_stride, H_q, H_kv, G, splits, pps, ppw;
 };
 
 constexpr int kPaWaves = 4;
 
-__device__ __forceinline__ bf16x8 load_q8_pa(const uint8_t* row, int q_dt, int dim0) {
-  if (q_dt == ISB_BF16) return u32x4_as_bf16x8(ld16(row + 2 * dim0));
-  u32x2 w = ld8(row + dim0);
-  bf16x4 a = e4m3x4_to_bf16x4(w[0]);
-  bf16x4 b = e4m3x4_to_bf16x4(w[1]);
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+template <int Q_DT>
+__device__ __forceinline__ bf16x8 load_q8_t(const uint8_t* row, int dim0) {
+  if constexpr (Q_DT == ISB_BF16) {
+    return u32x4_as_bf16x8(ld16(row + 2 * dim0));
+  } else {
+    u32x2 w = ld8(row + dim0);
+    bf16x4 a = e4m3x4_to_bf16x4(w[0]);
+    bf16x4 b = e4m3x4_to_bf16x4(w[1]);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
 }
 
 // Running state of one wave: per lane, head c = lane & 15.
@@ -73,79 +82,30 @@ struct Softmax {
   f32x4 o[8];   // O^T: dims 16 dt + 4 g + e of head c
 };
 
-// One 16-key tile: kb = K tile as the A operand (4 x bf16x8), vt = V^T tile
-// (8 x bf16x4), nvalid = keys of the tile that count (1..16), bad = NaN poison.
-__device__ __forceinline__ void attend_tile(Softmax& st, const bf16x8 (&qb)[4], const bf16x8 (&kb)[4],
-                                            const bf16x4 (&vt)[8], int nvalid, bool bad,
-                                            float qk_scale, int g) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void softmax_init(Softmax& st) {
+  st.m = neg_inf();
+  st.l = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) s = mfma_16x16x32_bf16(kb[j], qb[j], s);
-  float z[4];
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Folds the logits z (NZ per lane, -inf where masked) into the running state
+// and returns the probabilities to multiply into V.  The output is rescaled
+// only when some head's running max moved (a wave-uniform branch, rare after
+// the first pages).
+template <int NZ>
+__device__ __forceinline__ void softmax_update(Softmax& st, const float (&z)[NZ], float (&p)[NZ]) {
   float tmax = neg_inf();
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v = bad ? qnan() : s[e] * qk_scale;
-    v = (4 * g + e < nvalid) ? v : neg_inf();
-    z[e] = v;
-    tmax = fmaxf(tmax, v);
-  }
+  for (int e = 0; e < NZ; ++e) tmax = fmaxf(tmax, z[e]);
   tmax = max_over_groups(tmax);
   const float m_new = fmaxf(st.m, tmax);
-  const float alpha = exp2f(st.m - m_new);  // 0 on the first tile (m = -inf)
-  float p[4];
   float psum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < NZ; ++e) {
     p[e] = exp2f(z[e] - m_new);
     psum += p[e];
   }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    st.o[dt] *= alpha;
-    st.o[dt] = mfma_16x16x16_bf16(vt[dt], pb, st.o[dt]);
-  }
-}
-
-// Two 16-key tiles under one softmax update.  The PV product runs on
-// v_mfma_f32_16x16x32_bf16 with k = 8 g + e: e < 4 are keys 4 g + e of the
-// first tile and e >= 4 keys 4 g + e - 4 of the second, which is exactly what
-// the two S^T results leave in this lane; V^T is concatenated the same way.
-__device__ __forceinline__ void attend_pair(Softmax& st, const bf16x8 (&qb)[4],
-                                            const bf16x8 (&kb0)[4], const bf16x8 (&kb1)[4],
-                                            const bf16x4 (&vt0)[8], const bf16x4 (&vt1)[8],
-                                            int nvalid0, int nvalid1, bool bad0, bool bad1,
-                                            float qk_scale, int g) {
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) s0 = mfma_16x16x32_bf16(kb0[j], qb[j], s0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) s1 = mfma_16x16x32_bf16(kb1[j], qb[j], s1);
-  float z[8];
-  float tmax = neg_inf();
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v0 = bad0 ? qnan() : s0[e] * qk_scale;
-    float v1 = bad1 ? qnan() : s1[e] * qk_scale;
-    z[e] = (4 * g + e < nvalid0) ? v0 : neg_inf();
-    z[4 + e] = (4 * g + e < nvalid1) ? v1 : neg_inf();
-    tmax = fmaxf(tmax, fmaxf(z[e], z[4 + e]));
-  }
-  tmax = max_over_groups(tmax);
-  const float m_new = fmaxf(st.m, tmax);
-  float psum = 0.f;
-  bf16x8 pb;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p = exp2f(z[e] - m_new);
-    psum += p;
-    pb[e] = (__bf16)p;
-  }
-  // Rescale the output only when some head's running max moved (a wave-uniform
-  // branch); after the first pages this is rare.
   if (__ballot(m_new > st.m)) {
     const float alpha = exp2f(st.m - m_new);  // 0 while m = -inf
     st.l *= alpha;
@@ -154,82 +114,136 @@ __device__ __forceinline__ void attend_pair(Softmax& st, const bf16x8 (&qb)[4],
   }
   st.l += psum;
   st.m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const bf16x8 va = {vt0[dt][0], vt0[dt][1], vt0[dt][2], vt0[dt][3],
-                       vt1[dt][0], vt1[dt][1], vt1[dt][2], vt1[dt][3]};
-    st.o[dt] = mfma_16x16x32_bf16(va, pb, st.o[dt]);
-  }
 }
 
-// Raw bytes of one 16-token page for this lane.
+// One 16-key tile: kb = K tile as the A operand (4 x bf16x8), vt = V^T tile
+// (8 x bf16x4), nvalid = keys of the tile that count (1..16), bad = NaN poison.
+__device__ __forceinline__ void attend_tile(Softmax& st, const bf16x8 (&qb)[4], const bf16x8 (&kb)[4],
+                                            const bf16x4 (&vt)[8], int nvalid, bool bad,
+                                            float qk_scale, int g) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s = mfma_16x16x32_bf16(kb[j], qb[j], s);
+  float z[4], p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = bad ? qnan() : s[e] * qk_scale;
+    z[e] = (4 * g + e < nvalid) ? v : neg_inf();
+  }
+  softmax_update<4>(st, z, p);
+  const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16_bf16(vt[dt], pb, st.o[dt]);
+}
+
+// ----------------------------------------------------------------- 16-token pages
+// Raw bytes of one page for this lane: NC 16-byte chunks of K and of V.
 template <int KV_DT>
 struct PageRegs {
-  u32x4 k[KV_DT == ISB_BF16 ? 4 : 2];
-  uint32_t v[KV_DT == ISB_BF16 ? 16 : 8];
+  static constexpr int NC = KV_DT == ISB_BF16 ? 4 : 2;
+  u32x4 k[NC];
+  u32x4 v[NC];
 };
 
 template <int KV_DT>
-__device__ __forceinline__ void load_page16(PageRegs<KV_DT>& pr, const uint8_t* kpage,
-                                            const uint8_t* vpage, int c, int g) {
-  if constexpr (KV_DT == ISB_BF16) {
+__device__ __forceinline__ void load_k16(PageRegs<KV_DT>& pr, const uint8_t* kpage, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pr.k[j] = ld16(kpage + c * 256 + 64 * g + 16 * j);
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.k[h] = ld16(kpage + 1024 * h + 16 * lane);
+}
+template <int KV_DT>
+__device__ __forceinline__ void load_v16(PageRegs<KV_DT>& pr, const uint8_t* vpage, int lane) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      u32x2 w = ld8(vpage + (16 * dt + c) * 32 + 8 * g);
-      pr.v[2 * dt] = w[0];
-      pr.v[2 * dt + 1] = w[1];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) pr.k[j] = ld16(kpage + c * 128 + 32 * g + 16 * j);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) pr.v[dt] = ld4(vpage + (16 * dt + c) * 16 + 4 * g);
-  }
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] = ld16(vpage + 1024 * h + 16 * lane);
 }
 
 template <int KV_DT>
-__device__ __forceinline__ void page16_operands(const PageRegs<KV_DT>& pr, int nvalid, int g,
-                                                bf16x8 (&kb)[4], bf16x4 (&vt)[8]) {
+__device__ __forceinline__ void page16_operands_v(const PageRegs<KV_DT>& pr, bf16x4 (&vt)[8]) {
   if constexpr (KV_DT == ISB_BF16) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kb[j] = u32x4_as_bf16x8(pr.k[j]);
+    for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      bf16x2 a = u32_as_bf16x2(pr.v[2 * dt]);
-      bf16x2 b = u32_as_bf16x2(pr.v[2 * dt + 1]);
-      vt[dt] = bf16x4{a[0], a[1], b[0], b[1]};
-    }
+      for (int q = 0; q < 2; ++q)
+        vt[2 * h + q] = __builtin_bit_cast(bf16x4, u32x2{pr.v[h][2 * q], pr.v[h][2 * q + 1]});
   } else {
-    uint32_t w[8] = {pr.k[0][0], pr.k[0][1], pr.k[0][2], pr.k[0][3],
-                     pr.k[1][0], pr.k[1][1], pr.k[1][2], pr.k[1][3]};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x4 lo = e4m3x4_to_bf16x4(w[2 * j]);
-      bf16x4 hi = e4m3x4_to_bf16x4(w[2 * j + 1]);
-      kb[j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vt[dt] = e4m3x4_to_bf16x4(pr.v[dt]);
-  }
-  if (nvalid < 16) {  // keys past the row's length may hold anything: zero their V
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (4 * g + e >= nvalid) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) vt[dt][e] = (__bf16)0.f;
-      }
-    }
+      for (int q = 0; q < 4; ++q) vt[4 * h + q] = e4m3x4_to_bf16x4(pr.v[h][q]);
   }
 }
 
 __device__ __forceinline__ bool page_ok(int64_t id, int64_t n) { return id >= 0 && id < n; }
 
+// Keys at or past nvalid in a page may hold anything (0 x NaN would poison
+// the sum), so their raw V bytes are cleared before conversion.  Lane
+// (g, c) holds keys 4 g .. 4 g + 3: one byte each per fp8 dword, two keys per
+// bf16 dword (keys 4 g, 4 g + 1 in dword 2q, 4 g + 2, 4 g + 3 in dword 2q + 1).
 template <int KV_DT>
+__device__ __forceinline__ void clear_tail_keys(PageRegs<KV_DT>& pr, int nvalid, int g) {
+  const int keep = min(4, max(0, nvalid - 4 * g));  // keys of this lane that count
+  if constexpr (KV_DT == ISB_BF16) {
+    const uint64_t m64 = keep >= 4 ? ~0ull : ((1ull << (16 * keep)) - 1ull);
+    const uint32_t lo = (uint32_t)m64, hi = (uint32_t)(m64 >> 32);
+#pragma unroll
+    for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) {
+      pr.v[h][0] &= lo;
+      pr.v[h][1] &= hi;
+      pr.v[h][2] &= lo;
+      pr.v[h][3] &= hi;
+    }
+  } else {
+    const uint32_t m = keep >= 4 ? ~0u : ((1u << (8 * keep)) - 1u);
+#pragma unroll
+    for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] &= m;
+  }
+}
+
+// K operand of one page: fp8 chunk h holds dims 32 g + 16 h .. + 15 (kb[2h],
+// kb[2h+1]); bf16 chunk h holds dims 32 g + 8 h .. + 7 (kb[h]).
+template <int KV_DT>
+__device__ __forceinline__ void k_operand(const PageRegs<KV_DT>& pr, bf16x8 (&kb)[4]) {
+  if constexpr (KV_DT == ISB_BF16) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) kb[h] = u32x4_as_bf16x8(pr.k[h]);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) kb[2 * h + q] = e4m3x8_to_bf16x8(pr.k[h][2 * q], pr.k[h][2 * q + 1]);
+  }
+}
+
+// V^T operand of dim tile dt for a pair of pages (keys 4 g + e of the first
+// page, then of the second), as v_mfma_f32_16x16x32_bf16 wants it.
+template <int KV_DT>
+__device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const PageRegs<KV_DT>& b, int dt) {
+  if constexpr (KV_DT == ISB_BF16) {
+    const int h = dt >> 1, q = dt & 1;
+    return __builtin_bit_cast(bf16x8, u32x4{a.v[h][2 * q], a.v[h][2 * q + 1], b.v[h][2 * q], b.v[h][2 * q + 1]});
+  } else {
+    const int h = dt >> 2, q = dt & 3;
+    return e4m3x8_to_bf16x8(a.v[h][q], b.v[h][q]);
+  }
+}
+
+
+
+// Query columns past the group's G heads are zero (they were loaded from head
+// 0 so the load needs no branch).
+__device__ __forceinline__ void zero_missing_heads(bf16x8 (&qb)[4], int c, int G) {
+  if (c >= G) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+// ----------------------------------------------------------------- decode kernel
+// RUN: pages of one wave's run (16-token pages; a power of two).  Q_DT: query
+// dtype.  grid (rows, splits), four waves a workgroup.
+template <int KV_DT, int Q_DT, int RUN>
 __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   constexpr int P = KV_DT == ISB_MXFP4 ? 128 : 16;
-  constexpr int MAXP = KV_DT == ISB_BF16 ? 4 : 8;  // 16-token pages a wave keeps in flight
+  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   __shared__ float s_m[kPaWaves][16];
   __shared__ float s_l[kPaWaves][16];
   __shared__ float s_o[kPaWaves][16][kHeadDim + 4];
@@ -241,14 +255,22 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
   const int p0 = split * a.pps;
-  // The page ids of this wave's run are read together with the row length
-  // (not after it), so the K/V gathers start one memory round trip sooner.
-  const int wb = p0 + wave * a.ppw;
+  // Issued together before anything waits: this wave's page ids, the row
+  // length and the query, so the K/V gathers start after one round trip.
+  const int wb = p0 + wave * RUN;
   int my_id = -1;
   if constexpr (KV_DT != ISB_MXFP4) {
-    if (lane < a.ppw && wb + lane < a.sbt_stride) my_id = pages[wb + lane];
+    if (lane < RUN && wb + lane < a.sbt_stride) my_id = pages[wb + lane];
   }
   const int n_tok = a.sctx[row];
+  // Q^T operand: head kvh * G + c, dims 32 g .. 32 g + 31 (zero past G).
+  bf16x8 qb[4];
+  {
+    const int hc = c < a.G ? c : 0;
+    const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * QB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
+  }
   const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);  // merge / output layout
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
   if (n_tok <= 0) {  // an empty row attends nothing: split 0 writes its zeros
@@ -266,71 +288,110 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   const int p1 = min(npages, p0 + a.pps);
   const int live = (npages + a.pps - 1) / a.pps;  // splits of this row that have pages
 
-  // Q^T operand: head kvh * G + c, dims 32 g .. 32 g + 31 (zero past G).
-  bf16x8 qb[4];
-  {
-    const int qbytes = a.q_dt == ISB_BF16 ? 2 : 1;
-    if (c < a.G) {
-      const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + c) * kHeadDim * qbytes;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qb[j] = load_q8_pa(qrow, a.q_dt, 32 * g + 8 * j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qb[j] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
   Softmax st;
-  st.m = neg_inf();
-  st.l = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  softmax_init(st);
 
   if constexpr (KV_DT != ISB_MXFP4) {
-    // Each wave owns a run of up to MAXP consecutive pages and issues every
-    // load of that run before any math, so a wave keeps its whole share of the
-    // row in flight (the split plan sizes runs so ~2048 waves cover a batch).
     constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
     const int64_t hstride = (int64_t)a.H_kv * PB;  // bytes per page id (all heads)
     const int64_t hoff = (int64_t)kvh * PB;
-    const int cnt = max(0, min(a.ppw, p1 - wb));
-    PageRegs<KV_DT> pr[MAXP];
-    bool ok[MAXP];
+    const int cnt = max(0, min(RUN, p1 - wb));
+    if (cnt > 0) {
+      // Every load of the run, unconditionally: slots past the run re-read
+      // its first page, an out-of-range id reads page 0 and poisons its tile.
+      // All K chunks are issued before all V chunks, page by page, and kept in
+      // that order, so the logits of page j wait only for K of pages <= j and
+      // P.V of page j only for V of pages <= j.
+      PageRegs<KV_DT> pr[RUN];
+      bool ok[RUN];
+      int64_t use[RUN];
 #pragma unroll
-    for (int j = 0; j < MAXP; ++j) {
-      const int64_t id = __builtin_amdgcn_readlane(my_id, j);
-      ok[j] = j < cnt && page_ok(id, a.num_pages);
-      if (ok[j]) load_page16<KV_DT>(pr[j], a.kp + id * hstride + hoff, a.vp + id * hstride + hoff, c, g);
-    }
-#pragma unroll
-    for (int j = 0; j < MAXP; j += 2) {
-      if (j < cnt) {
-        const int nv0 = min(16, n_tok - (wb + j) * 16);
-        const int nv1 = j + 1 < cnt ? min(16, n_tok - (wb + j + 1) * 16) : 0;
-        bf16x8 kb0[4], kb1[4];
-        bf16x4 vt0[8], vt1[8];
-        if (ok[j]) {
-          page16_operands<KV_DT>(pr[j], nv0, g, kb0, vt0);
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) kb0[x] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) vt0[dt] = bf16x4{0, 0, 0, 0};
-        }
-        if (j + 1 < cnt && ok[j + 1]) {
-          page16_operands<KV_DT>(pr[j + 1], nv1, g, kb1, vt1);
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) kb1[x] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) vt1[dt] = bf16x4{0, 0, 0, 0};
-        }
-        attend_pair(st, qb, kb0, kb1, vt0, vt1, nv0, nv1, !ok[j], j + 1 < cnt && !ok[j + 1],
-                    a.qk_scale, g);
+      for (int j = 0; j < RUN; ++j) {
+        const int64_t id = __builtin_amdgcn_readlane(my_id, j < cnt ? j : 0);
+        ok[j] = page_ok(id, a.num_pages);
+        use[j] = (ok[j] ? id : 0) * hstride + hoff;
+        load_k16<KV_DT>(pr[j], a.kp + use[j], lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int j = 0; j < RUN; ++j) {
+        load_v16<KV_DT>(pr[j], a.vp + use[j], lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      zero_missing_heads(qb, c, a.G);
+      // Pass 1: every logit of the run, then one exact max per head for the
+      // whole run, so the output needs no online rescaling.
+      float z[RUN][4];
+      float mx = neg_inf();
+#pragma unroll
+      for (int j = 0; j < RUN; ++j) {
+        if (j < cnt) {
+          bf16x8 kb[4];
+          k_operand<KV_DT>(pr[j], kb);
+          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16(kb[x], qb[x], sacc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
+          const int nv = min(16, n_tok - (wb + j) * 16);
+          if (nv < 16) {  // the row's last page: keys past its length do not count
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
+            clear_tail_keys<KV_DT>(pr[j], nv, g);
+          }
+          if (!ok[j]) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[j][e] = qnan();
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, z[j][e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[j][e] = neg_inf();
+        }
+      }
+      mx = max_over_groups(mx);
+      // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
+      // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
+      float lsum = 0.f;
+      if constexpr (RUN == 1) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(z[0][e] - mx);
+          lsum += p[e];
+        }
+        const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+        bf16x4 vt[8];
+        page16_operands_v<KV_DT>(pr[0], vt);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16_bf16(vt[dt], pb, st.o[dt]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < RUN; j += 2) {
+          if (j < cnt) {
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = __builtin_amdgcn_exp2f(z[j][e] - mx);
+              const float p1 = __builtin_amdgcn_exp2f(z[j + 1][e] - mx);
+              lsum += p0 + p1;
+              pb[e] = (__bf16)p0;
+              pb[4 + e] = (__bf16)p1;
+            }
+            if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+              st.o[dt] = mfma_16x16x32_bf16(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, st.o[dt]);
+          }
+        }
+      }
+      st.m = mx;
+      st.l = lsum;
     }
   } else {
     // MXFP4: the workgroup walks its pages together; V is staged in LDS.
+    zero_missing_heads(qb, c, a.G);
     for (int p = p0; p < p1; ++p) {
       const int64_t id = pages[p];
       const bool ok = page_ok(id, a.num_pages);
@@ -465,6 +526,23 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(PaArgs a) {
   *reinterpret_cast<bf16x8*>(a.out + ((size_t)t * a.H_q + kvh * a.G + h) * kHeadDim + d0) = ob;
 }
 
+template <int KV_DT, int Q_DT>
+static void launch_decode(const PaArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (KV_DT == ISB_MXFP4) {
+    hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 1>), grid, dim3(256), 0, st, a);
+  } else {
+    switch (a.ppw) {
+      case 1: hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 1>), grid, dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 2>), grid, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 4>), grid, dim3(256), 0, st, a); break;
+      default:
+        if constexpr (KV_DT == ISB_FP8_E4M3)
+          hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 8>), grid, dim3(256), 0, st, a);
+        break;
+    }
+  }
+}
+
 }  // namespace isb
 
 extern "C" size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv_heads,
@@ -490,8 +568,7 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
       num_kv_heads <= 0)
     return ISB_E_INVALID_ARG;
   if (!is_query_dtype(q_dtype) || !is_pool_dtype(kv_dtype)) return ISB_E_UNSUPPORTED_DTYPE;
-  if (head_dim != kHeadDim || num_q_heads % num_kv_heads != 0 ||
-      num_q_heads / num_kv_heads > 16)
+  if (head_dim != kHeadDim || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16)
     return ISB_E_SHAPE;
   if (!(sm_scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f)) return ISB_E_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return ISB_E_INVALID_ARG;
@@ -513,7 +590,6 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   a.num_pages = num_pages;
   a.qk_scale = sm_scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
   a.v_scale = fp8 ? v_scale : 1.0f;
-  a.q_dt = q_dtype;
   a.sbt_stride = sparse_bt_stride;
   a.H_q = num_q_heads;
   a.H_kv = num_kv_heads;
@@ -522,17 +598,24 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   a.pps = plan.pages_per_split;
   a.ppw = plan.pages_per_wave;
   hipStream_t st = as_hip(stream);
-  dim3 grid((unsigned)rows, plan.splits);
-  dim3 rgrid((unsigned)rows);
+  const dim3 grid((unsigned)rows, plan.splits);
+  const bool qb = q_dtype == ISB_BF16;
   if (kv_dtype == ISB_BF16) {
-    hipLaunchKernelGGL(pa_decode_kernel<ISB_BF16>, grid, dim3(256), 0, st, a);
-    if (plan.splits > 1) hipLaunchKernelGGL(pa_reduce_kernel<16>, rgrid, dim3(256), 0, st, a);
+    if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, st);
+    else launch_decode<ISB_BF16, ISB_FP8_E4M3>(a, grid, st);
   } else if (kv_dtype == ISB_FP8_E4M3) {
-    hipLaunchKernelGGL(pa_decode_kernel<ISB_FP8_E4M3>, grid, dim3(256), 0, st, a);
-    if (plan.splits > 1) hipLaunchKernelGGL(pa_reduce_kernel<16>, rgrid, dim3(256), 0, st, a);
+    if (qb) launch_decode<ISB_FP8_E4M3, ISB_BF16>(a, grid, st);
+    else launch_decode<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, grid, st);
   } else {
-    hipLaunchKernelGGL(pa_decode_kernel<ISB_MXFP4>, grid, dim3(256), 0, st, a);
-    if (plan.splits > 1) hipLaunchKernelGGL(pa_reduce_kernel<128>, rgrid, dim3(256), 0, st, a);
+    if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, st);
+    else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, st);
+  }
+  if (plan.splits > 1) {
+    const dim3 rgrid((unsigned)rows);
+    if (kv_dtype == ISB_MXFP4)
+      hipLaunchKernelGGL(pa_reduce_kernel<128>, rgrid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(pa_reduce_kernel<16>, rgrid, dim3(256), 0, st, a);
   }
   return launch_status();
 }

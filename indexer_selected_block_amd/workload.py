@@ -21,8 +21,9 @@ A request's token at absolute position ``p`` lives in the 128-token block
            cache and MXFP4 KV cache", Summary and the layout commit message).
 * K/V caches in bf16 / fp8 use 16-token pages, 8 per block (pages_per_block 8):
   block ``b``'s pages are ``8 b .. 8 b + 7``; page ``8 b + s // 16`` holds
-  slot ``s``.  The K page is token-major ``[16 tok][128 dim]``; the V page is
-  dim-major ``[128 dim][16 tok]``.  fp8 values carry per-tensor ``k_scale`` /
+  slot ``s``.  Pages are laid out in 16-byte chunks in the order the
+  attention kernel's lanes read them (see ``k_page16_bytes`` /
+  ``v_page16_bytes``).  fp8 values carry per-tensor ``k_scale`` /
   ``v_scale``.  One page id addresses the K page and the V page alike.
 * K/V caches in MXFP4 use one 8704 B page per block (pages_per_block 1), the
   same page format as the MXFP4 index cache, for K and for V.
@@ -241,6 +242,33 @@ def _pack_mxfp4_page(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
     return torch.cat([data, scales.reshape(n, BLOCK_TOKENS * 4)], dim=1)
 
 
+# ---------------------------------------------------------------- 16-token page layout
+def k_page16_bytes(x: torch.Tensor) -> torch.Tensor:
+    """K values as bytes [n, 16 tok, 128 dim, esize] -> pages [n, 16 * 128 * esize].
+
+    Chunk h (16 bytes) of lane l = 16 g + c sits at byte 1024 h + 16 l and holds
+    key c's dims 32 g + (16 / esize) h .. (+ 16 / esize - 1): dim d of key c
+    lives at byte 1024 ((d mod 32) div dpc) + 256 (d div 32) + 16 c + esize (d mod dpc),
+    dpc = 16 / esize dims per chunk."""
+    n, esz = x.shape[0], x.shape[-1]
+    dpc = 16 // esz
+    y = x.reshape(n, PAGE16_TOKENS, 4, 32 // dpc, 16)      # [n, c, g, h, chunk bytes]
+    return y.permute(0, 3, 2, 1, 4).reshape(n, -1)
+
+
+def v_page16_bytes(x: torch.Tensor) -> torch.Tensor:
+    """V values as bytes [n, 16 tok, 128 dim, esize] -> pages [n, 16 * 128 * esize].
+
+    Chunk h of lane l = 16 g + c sits at byte 1024 h + 16 l and holds, for the
+    dim tiles dt = tpc h .. tpc h + tpc - 1 (tpc = 4 / esize), keys 4 g .. 4 g + 3
+    of dim 16 dt + c: key t = 4 g + e, dim 16 dt + c lives at byte
+    1024 (dt div tpc) + 16 (16 g + c) + 4 esize (dt mod tpc) + esize e."""
+    n, esz = x.shape[0], x.shape[-1]
+    tpc = 4 // esz
+    y = x.reshape(n, 4, 4, 8 // tpc, tpc, 16, esz)          # [n, g, e, h, q, c, byte]
+    return y.permute(0, 3, 1, 5, 4, 2, 6).reshape(n, -1)
+
+
 # ---------------------------------------------------------------- generation
 class _Streams:
     """Independent, reproducible torch generators keyed by (config seed, purpose, chunk)."""
@@ -410,26 +438,35 @@ def _write_cache(cfg, streams, tid, pool, dtype, which, ids, valid, dist, chunk_
         for c, s, e in _chunks(n, chunk_blocks):
             x = _draw(cfg, streams, tid + 100 * h, c, (e - s, BLOCK_TOKENS, HEAD_DIM), dist)
             nb = e - s
-            if dtype == "bf16":
-                page = _to_bf16_bytes(x).reshape(nb, BLOCK_TOKENS, HEAD_DIM * 2)
-            elif dtype == "fp8":
-                page = _to_e4m3_bytes(x / scale).reshape(nb, BLOCK_TOKENS, HEAD_DIM)
-            else:
+            if dtype == "mxfp4":
                 codes, sc = _mx_quantize(x)
                 page = _pack_mxfp4_page(codes, sc)
-            if dtype != "mxfp4" and which == "v":
-                # V pages are dim-major within each 16-token page.
-                esz = page.shape[-1] // HEAD_DIM
-                page = (page.reshape(nb, 8, PAGE16_TOKENS, HEAD_DIM, esz)
-                        .transpose(2, 3).contiguous())
-            page = page.reshape(nb, -1)
-            _poison_tail(page, valid[s:e], slot, dtype, which)
+                _poison_tail(page, valid[s:e], slot, dtype, which)
+                put(s, e, h, page)
+                continue
+            if dtype == "bf16":
+                vals = _to_bf16_bytes(x).reshape(nb, BLOCK_TOKENS, HEAD_DIM, 2)
+            else:
+                vals = _to_e4m3_bytes(x / scale).reshape(nb, BLOCK_TOKENS, HEAD_DIM, 1)
+            if which == "idx":
+                page = vals.reshape(nb, -1)
+                _poison_tail(page, valid[s:e], slot, dtype, which)
+            else:
+                # poison the unwritten slots in token order, then lay out the pages
+                bad = slot[None, :] >= valid[s:e, None]
+                pz = torch.tensor([0xC0, 0x7F] if dtype == "bf16" else [_E4M3_NAN],
+                                  dtype=torch.uint8, device=dev)
+                vals = torch.where(bad[:, :, None, None], pz, vals)
+                pages16 = vals.reshape(nb * 8, PAGE16_TOKENS, HEAD_DIM, vals.shape[-1])
+                lay = k_page16_bytes if which == "k" else v_page16_bytes
+                page = lay(pages16).reshape(nb, -1)
             put(s, e, h, page)
     return scale
 
 
 def _poison_tail(page: torch.Tensor, valid: torch.Tensor, slot: torch.Tensor, dtype: str, which: str) -> None:
-    """Overwrite the slots past each block's written length with poison."""
+    """Overwrite the slots past each block's written length with poison
+    (token-major pages: the index cache and MXFP4 pages)."""
     nb = page.shape[0]
     bad = slot[None, :] >= valid[:, None]            # [nb, 128]
     if not bool(bad.any()):
@@ -446,11 +483,6 @@ def _poison_tail(page: torch.Tensor, valid: torch.Tensor, slot: torch.Tensor, dt
     else:
         vals = page
         poison = _E4M3_NAN
-    if which == "v":
-        # [nb, 8 pages, 128 dim, 16 tok]
-        v = vals.view(nb, 8, HEAD_DIM, PAGE16_TOKENS)
-        m = bad.view(nb, 8, 1, PAGE16_TOKENS)
-        v.masked_fill_(m, poison)
-    else:
-        v = vals.view(nb, BLOCK_TOKENS, HEAD_DIM)
-        v.masked_fill_(bad.unsqueeze(-1), poison)
+    v = vals.view(nb, BLOCK_TOKENS, HEAD_DIM)
+    v.masked_fill_(bad.unsqueeze(-1), poison)
+

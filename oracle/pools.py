@@ -14,11 +14,16 @@ Pool layout read here (its own code; it shares nothing with the GPU path):
     mxfp4 the 8704 B page of ``formats.decode_mxfp4_page``.
 * K/V cache, bf16 / fp8 - 16-token pages, 8 per 128-token block
   (vLLM API page for ``sparse_attention_msa``: the page-16 rebase of the block
-  table and the stride check over the pages of a sparse block); K pages are
-  token-major [16 tok][128 dim], V pages dim-major [128 dim][16 tok], the
-  dim-major V page of the shapes in vLLM PR 61889, Validation.  fp8 values are
-  multiplied by the per-tensor ``k_scale`` / ``v_scale``.  One page id
-  addresses a K page and a V page (vLLM PR 61889, Details).
+  table and the stride check over the pages of a sparse block).  Within a
+  page the element order is this build's own (the sources show only that a
+  16-token page is sub-tiled for the kernel, vLLM PR 61889, Validation, the
+  K [.., 8, 16, 16] and V [.., 1, 128, 16] shapes).  With e = bytes per element:
+    K: key c, dim d at byte 1024 ((d mod 32) div (16/e)) + 256 (d div 32)
+       + 16 c + e (d mod (16/e));
+    V: key t, dim d = 16 dt + c at byte 1024 (dt div (4/e)) + 256 (t div 4)
+       + 16 c + 4 e (dt mod (4/e)) + e (t mod 4).
+  fp8 values are multiplied by the per-tensor ``k_scale`` / ``v_scale``.  One
+  page id addresses a K page and a V page (vLLM PR 61889, Details).
 * K/V cache, mxfp4 - one 8704 B page per block for K and one for V
   (PR 2962, Summary: "K and V are MXFP4 pages of the same format").
 * A K/V page id holds one page per KV head ([num_pages][H_kv][page]): the
@@ -34,6 +39,29 @@ from .formats import decode_bf16_bytes, decode_e4m3, decode_mxfp4_page
 
 BLOCK = 128
 PAGE16 = 16
+
+
+def _k_offsets(esize: int) -> np.ndarray:
+    """Byte offset of element (key c, dim d) of a 16-token K page -> [16, 128]."""
+    c = np.arange(PAGE16)[:, None]
+    d = np.arange(128)[None, :]
+    dpc = 16 // esize
+    return 1024 * ((d % 32) // dpc) + 256 * (d // 32) + 16 * c + esize * (d % dpc)
+
+
+def _v_offsets(esize: int) -> np.ndarray:
+    """Byte offset of element (key t, dim d) of a 16-token V page -> [16, 128]."""
+    t = np.arange(PAGE16)[:, None]
+    d = np.arange(128)[None, :]
+    dt, c = d // 16, d % 16
+    tpc = 4 // esize
+    return 1024 * (dt // tpc) + 256 * (t // 4) + 16 * c + 4 * esize * (dt % tpc) + esize * (t % 4)
+
+
+def _gather_elements(pages: np.ndarray, offsets: np.ndarray, esize: int) -> np.ndarray:
+    """pages [n, bytes] -> the raw element bytes in (key, dim) order [n, 16, 128 * esize]."""
+    idx = (offsets[..., None] + np.arange(esize)).reshape(PAGE16, 128 * esize)
+    return pages[:, idx]
 
 
 def index_block_keys(idx_pool: np.ndarray, dtype: str, idx_scale: float, block_ids) -> np.ndarray:
@@ -72,11 +100,11 @@ def kv_page_tokens(k_pool, v_pool, dtype: str, page_ids, k_scale: float, v_scale
     if dtype == "mxfp4":
         return decode_mxfp4_page(kp), decode_mxfp4_page(vp)
     if dtype == "bf16":
-        k = decode_bf16_bytes(kp).reshape(n, PAGE16, 128)
-        v = decode_bf16_bytes(vp).reshape(n, 128, PAGE16)
+        k = decode_bf16_bytes(_gather_elements(kp, _k_offsets(2), 2)).reshape(n, PAGE16, 128)
+        v = decode_bf16_bytes(_gather_elements(vp, _v_offsets(2), 2)).reshape(n, PAGE16, 128)
     elif dtype == "fp8":
-        k = decode_e4m3(kp).reshape(n, PAGE16, 128) * float(k_scale)
-        v = decode_e4m3(vp).reshape(n, 128, PAGE16) * float(v_scale)
+        k = decode_e4m3(_gather_elements(kp, _k_offsets(1), 1)).reshape(n, PAGE16, 128) * float(k_scale)
+        v = decode_e4m3(_gather_elements(vp, _v_offsets(1), 1)).reshape(n, PAGE16, 128) * float(v_scale)
     else:
         raise ValueError(dtype)
-    return k, np.swapaxes(v, 1, 2)
+    return k, v

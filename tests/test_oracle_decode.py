@@ -17,6 +17,8 @@ from indexer_selected_block_amd import workload as wl
 from oracle import decode as od
 from oracle import formats, pools
 
+import _pages
+
 
 # ------------------------------------------------------------------ helpers
 def _fp8_index_pool(rng, nblocks):
@@ -260,8 +262,8 @@ def test_emit_page_ids_address_k_and_v():
 def _kv_pools_fp8(rng, npages, kscale, vscale):
     k = torch.from_numpy(rng.standard_normal((npages, 16, 128)).astype(np.float32)).to(torch.float8_e4m3fn)
     v = torch.from_numpy(rng.standard_normal((npages, 16, 128)).astype(np.float32)).to(torch.float8_e4m3fn)
-    kp = k.view(torch.uint8).reshape(npages, -1).numpy()
-    vp = v.transpose(1, 2).contiguous().view(torch.uint8).reshape(npages, -1).numpy()
+    kp = _pages.k_pages(k.view(torch.uint8).numpy().reshape(npages, 16, 128, 1))
+    vp = _pages.v_pages(v.view(torch.uint8).numpy().reshape(npages, 16, 128, 1))
     return kp, vp, k.double().numpy() * kscale, v.double().numpy() * vscale
 
 
@@ -278,7 +280,9 @@ def test_attention_one_token_row_returns_v0():
 def test_attention_equal_keys_give_mean_v_and_empty_rows_zero():
     rng = np.random.default_rng(13)
     kp, vp, K, V = _kv_pools_fp8(rng, 3, 1.0, 1.0)
-    kp[:] = kp[0, :128][None, :].repeat(16 * 3, axis=0).reshape(3, -1)   # every token's key = token 0 of page 0
+    same = np.repeat(K[0, :1] / 1.0, 16, axis=0)                         # every key = key 0 of page 0
+    kp[:] = _pages.k_pages(torch.from_numpy(np.stack([same] * 3)).to(torch.float8_e4m3fn)
+                           .view(torch.uint8).numpy().reshape(3, 16, 128, 1))
     q = rng.standard_normal((2, 2, 128))
     sbt = np.array([[2, 0, -1], [1, 1, 1]])
     sctx = np.array([20, 0])
@@ -298,8 +302,13 @@ def _dense_reference(w):
     ppb = cfg.pages_per_block
     assert cfg.kv_dtype in ("fp8", "bf16")
     view = torch.float8_e4m3fn if cfg.kv_dtype == "fp8" else torch.bfloat16
-    kpages = w.k_pool.view(view).double().reshape(-1, 16, 128) * (w.k_scale if cfg.kv_dtype == "fp8" else 1)
-    vpages = w.v_pool.view(view).double().reshape(-1, 128, 16).transpose(1, 2) * (w.v_scale if cfg.kv_dtype == "fp8" else 1)
+    e = 1 if cfg.kv_dtype == "fp8" else 2
+    kb = _pages.read_back(w.k_pool.numpy(), e, "k")
+    vb = _pages.read_back(w.v_pool.numpy(), e, "v")
+    kpages = torch.from_numpy(kb.reshape(kb.shape[0], -1).copy()).view(view).double().reshape(-1, 16, 128)
+    vpages = torch.from_numpy(vb.reshape(vb.shape[0], -1).copy()).view(view).double().reshape(-1, 16, 128)
+    kpages = kpages * (w.k_scale if cfg.kv_dtype == "fp8" else 1)
+    vpages = vpages * (w.v_scale if cfg.kv_dtype == "fp8" else 1)
     for t in range(T):
         r, i = divmod(t, cfg.query_len)
         Lt = od.causal_length(int(w.seq_lens[r]), cfg.query_len, i)

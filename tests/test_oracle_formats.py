@@ -13,6 +13,8 @@ import torch
 
 from oracle import formats, pools
 
+import _pages
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_arithmetic.json")
 
 
@@ -89,12 +91,14 @@ def test_mxfp4_page_size_is_the_printed_one():
 
 
 def test_fp8_page16_bytes_match_the_printed_shapes():
-    # Our fp8 K page [16 tok][128 dim] and V page [128 dim][16 tok] hold the same
-    # 2048 B as one entry of the printed K [.., 8, 16, 16] and V [.., 1, 128, 16].
+    # Our fp8 K and V pages (16 tokens x 128 dims, 2048 B each, in our own
+    # element order) hold as many bytes as one entry of the printed
+    # K [.., 8, 16, 16] and V [.., 1, 128, 16], and the pool file holds them.
     g = _golden()["fp8_page16_shapes"]
     assert math.prod(g["k_cache"][1:]) == 16 * 128
     assert math.prod(g["v_cache"][1:]) == 128 * 16
-    assert g["v_cache"][3] == 128 and g["v_cache"][4] == 16          # V is dim-major
+    from indexer_selected_block_amd import workload as wl
+    assert wl.kv_page_bytes("fp8") == math.prod(g["k_cache"][1:])
 
 
 def test_mxfp4_page_hand_built():
@@ -119,8 +123,8 @@ def test_mxfp4_page_hand_built():
 
 def test_pool_readers_match_torch_views():
     # The pool readers against torch's own reinterpretation of the same bytes,
-    # laid out by hand here: index block = [128 tok][128 dim]; K page
-    # [16 tok][128 dim]; V page [128 dim][16 tok].
+    # laid out here: index block = [128 tok][128 dim]; K and V pages lane by
+    # lane (tests/_pages.py), for fp8 and bf16.
     rng = np.random.default_rng(0)
     vals = torch.from_numpy(rng.standard_normal((3, 128, 128)).astype(np.float32))
     idx_bf16 = vals.to(torch.bfloat16).view(torch.uint8).reshape(3, -1).numpy()
@@ -131,8 +135,34 @@ def test_pool_readers_match_torch_views():
     assert np.array_equal(got[0], idx_fp8.double().numpy()[1] * 0.5)
     k = (vals[:, :16] / 4).to(torch.float8_e4m3fn)            # [3 pages, 16 tok, 128 dim]
     v = (vals[:, 16:32] / 4).to(torch.float8_e4m3fn)
-    k_pool = k.view(torch.uint8).reshape(3, -1).numpy()
-    v_pool = v.transpose(1, 2).contiguous().view(torch.uint8).reshape(3, -1).numpy()
+    k_pool = _pages.k_pages(k.view(torch.uint8).numpy().reshape(3, 16, 128, 1))
+    v_pool = _pages.v_pages(v.view(torch.uint8).numpy().reshape(3, 16, 128, 1))
     K, V = pools.kv_page_tokens(k_pool, v_pool, "fp8", [2, 1], 2.0, 3.0)
     assert np.array_equal(K, k.double().numpy()[[2, 1]] * 2.0)
     assert np.array_equal(V, v.double().numpy()[[2, 1]] * 3.0)
+    kb = vals[:, 32:48].to(torch.bfloat16)
+    vb = vals[:, 48:64].to(torch.bfloat16)
+    k_pool = _pages.k_pages(kb.view(torch.uint8).numpy().reshape(3, 16, 128, 2))
+    v_pool = _pages.v_pages(vb.view(torch.uint8).numpy().reshape(3, 16, 128, 2))
+    K, V = pools.kv_page_tokens(k_pool, v_pool, "bf16", [0, 2], 1.0, 1.0)
+    assert np.array_equal(K, kb.double().numpy()[[0, 2]])
+    assert np.array_equal(V, vb.double().numpy()[[0, 2]])
+    # two KV heads under one page id: row g reads head g's page
+    k2 = np.concatenate([_pages.k_pages(k.view(torch.uint8).numpy().reshape(3, 16, 128, 1)),
+                         _pages.k_pages(v.view(torch.uint8).numpy().reshape(3, 16, 128, 1))], axis=1)
+    K0, _ = pools.kv_page_tokens(k2, k2, "fp8", [1], 1.0, 1.0, head=0, num_kv_heads=2)
+    K1, _ = pools.kv_page_tokens(k2, k2, "fp8", [1], 1.0, 1.0, head=1, num_kv_heads=2)
+    assert np.array_equal(K0[0], k.double().numpy()[1]) and np.array_equal(K1[0], v.double().numpy()[1])
+
+
+def test_generator_page_layout_matches_lane_builder():
+    # The generator's tensor permutes and the lane-by-lane builder agree.
+    from indexer_selected_block_amd import workload as wl
+    rng = np.random.default_rng(3)
+    for e in (1, 2):
+        vals = rng.integers(0, 256, (5, 16, 128, e), dtype=np.uint8)
+        t = torch.from_numpy(vals)
+        assert np.array_equal(wl.k_page16_bytes(t).numpy(), _pages.k_pages(vals))
+        assert np.array_equal(wl.v_page16_bytes(t).numpy(), _pages.v_pages(vals))
+        assert np.array_equal(_pages.read_back(_pages.k_pages(vals), e, "k"), vals)
+        assert np.array_equal(_pages.read_back(_pages.v_pages(vals), e, "v"), vals)
