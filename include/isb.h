@@ -43,8 +43,10 @@
  * Pool layout (one page id addresses the K page and the V page alike)
  * -------------------------------------------------------------------
  *  index cache, one page per 128-token block (page id = block id):
- *    ISB_BF16      [128 tok][128 dim] bf16                      32768 B
- *    ISB_FP8_E4M3  [128 tok][128 dim] e4m3, x idx_scale         16384 B
+ *    ISB_BF16      eight 16-token tiles, each laid out as a bf16 K page
+ *                  below (token 16 i + c of the block is key c of tile i,
+ *                  tile i at byte 4096 i)                        32768 B
+ *    ISB_FP8_E4M3  the same with e4m3 tiles of 2048 B, x idx_scale 16384 B
  *    ISB_MXFP4     128 x 64 B e2m1 (token j at 64 j, dim 2c in the low
  *                  nibble of byte c, 2c+1 in the high nibble) then
  *                  128 x 4 B e8m0 (token j at 8192 + 4 j, scale s for

@@ -9,15 +9,21 @@
 //
 // One wavefront scores one block of one request against every query row of
 // that request (q tokens x H_idx heads), so the block's keys cross HBM once
-// however many tokens the request decodes.  Three variants:
-//   * stream  - one query row (q = 1, H_idx = 1), bf16 / fp8 keys: a
-//               coalesced HBM stream with packed bf16 dot products on the VALU
-//               (2 flop per key byte leaves the VALU far from busy);
-//   * tile    - several query rows: keys converted to bf16 in registers and
-//               multiplied on v_mfma_f32_16x16x32_bf16, 16 keys x 16 rows a tile;
-//   * fp4     - MXFP4 keys with an e4m3 query: v_mfma_scale_f32_16x16x128_f8f6f4
-//               consumes the e2m1 data and its e8m0 scales directly, one
-//               instruction per 16 keys x 16 rows x 128 dims.
+// however many tokens the request decodes.  Every load of the block is issued
+// before any math.  Three variants:
+//   * stream - one query row (q = 1, H_idx = 1), bf16 / fp8 keys: packed bf16
+//              dot products on the VALU (2 flop per key byte leaves it far from
+//              busy), partial sums combined across the four lane groups;
+//   * tile   - several query rows: keys converted to bf16 in registers and
+//              multiplied on v_mfma_f32_16x16x32_bf16, 16 keys x 16 rows a tile;
+//   * fp4    - MXFP4 keys with an e4m3 query: v_mfma_scale_f32_16x16x128_f8f6f4
+//              consumes the e2m1 data and its e8m0 scales directly, one
+//              instruction per 16 keys x 16 rows x 128 dims.
+// bf16 / fp8 index pages are eight 16-key tiles in the lane order of the K
+// pages (chunk h of lane l = 16 g + m at byte 1024 h + 16 l of the tile holds
+// key m's dims 32 g + (16 / esize) h ...), so each load instruction reads one
+// contiguous KiB; MXFP4 pages keep their token-major format (64 B a key: one
+// 16-key tile is also one contiguous KiB a load).
 #include "isb_device.h"
 #include "isb_host.h"
 
@@ -31,29 +37,30 @@ struct ScoreArgs {
   float* scores;
   int64_t pool_blocks;
   float idx_scale;
-  int q_dt, idx_dt, H_idx, bt_stride, R, q_len, H_kv, MB;
+  int H_idx, bt_stride, R, q_len, H_kv, MB;
 };
 
 constexpr int kScoreWaves = 4;        // waves (blocks) per workgroup
 constexpr int kMaxQueryRows = 64;     // q_len * H_idx
 
-// Loads 8 consecutive dims of one query row as bf16 (exact for e4m3).
-__device__ __forceinline__ bf16x8 load_q8(const uint8_t* row, int q_dt, int dim0) {
-  if (q_dt == ISB_BF16) return u32x4_as_bf16x8(ld16(row + 2 * dim0));
-  u32x2 w = ld8(row + dim0);
-  bf16x4 a = e4m3x4_to_bf16x4(w[0]);
-  bf16x4 b = e4m3x4_to_bf16x4(w[1]);
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+template <int Q_DT>
+__device__ __forceinline__ bf16x8 load_q8(const uint8_t* row, int dim0) {
+  if constexpr (Q_DT == ISB_BF16) {
+    return u32x4_as_bf16x8(ld16(row + 2 * dim0));
+  } else {
+    const u32x2 w = ld8(row + dim0);
+    return e4m3x8_to_bf16x8(w[0], w[1]);
+  }
 }
 
 __device__ __forceinline__ int causal_len(int L, int q_len, int i) {
-  int v = L - (q_len - 1 - i);
+  const int v = L - (q_len - 1 - i);
   return v > 0 ? v : 0;
 }
 
-// Writes -inf (or `v`) for every (token, group) of request r at block b.
+// Writes vals[x] (or -inf) for every (token, group) x of request r at block b.
 __device__ __forceinline__ void write_scores(const ScoreArgs& a, int r, int b, int lane,
-                                             const float* vals /* per (i,g) or null */) {
+                                             const float* vals) {
   const int T = a.R * a.q_len;
   for (int x = lane; x < a.q_len * a.H_kv; x += kWave) {
     const int i = x / a.H_kv, g = x % a.H_kv;
@@ -63,142 +70,171 @@ __device__ __forceinline__ void write_scores(const ScoreArgs& a, int r, int b, i
 }
 
 // Group sums of per-row block maxima held in `rowmax[QR]` (wave-private LDS).
-__device__ __forceinline__ void finish(const ScoreArgs& a, int r, int b, int lane,
-                                       const float* rowmax, float* outv) {
+template <int KEY_DT>
+__device__ __forceinline__ void finish(const ScoreArgs& a, int lane, const float* rowmax, float* outv) {
   const int per = a.H_idx / a.H_kv;
   for (int x = lane; x < a.q_len * a.H_kv; x += kWave) {
     const int i = x / a.H_kv, g = x % a.H_kv;
     float s = 0.f;
     for (int h = 0; h < per; ++h) s += rowmax[i * a.H_idx + g * per + h];
-    outv[x] = s * (a.idx_dt == ISB_FP8_E4M3 ? a.idx_scale : 1.0f);
+    outv[x] = KEY_DT == ISB_FP8_E4M3 ? s * a.idx_scale : s;
+  }
+}
+
+// Raw chunks of one 16-key tile for this lane (bf16 / fp8 index pages).
+template <int KEY_DT>
+struct TileRegs {
+  static constexpr int NC = KEY_DT == ISB_BF16 ? 4 : 2;
+  u32x4 c[NC];
+};
+
+template <int KEY_DT>
+__device__ __forceinline__ void load_tile(TileRegs<KEY_DT>& t, const uint8_t* tile, int lane) {
+#pragma unroll
+  for (int h = 0; h < TileRegs<KEY_DT>::NC; ++h) t.c[h] = ld16(tile + 1024 * h + 16 * lane);
+}
+
+// MFMA A operand of a tile: dims 32 g + 8 j .. + 7 of key m in kb[j].
+template <int KEY_DT>
+__device__ __forceinline__ void tile_operand(const TileRegs<KEY_DT>& t, bf16x8 (&kb)[4]) {
+  if constexpr (KEY_DT == ISB_BF16) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) kb[h] = u32x4_as_bf16x8(t.c[h]);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) kb[2 * h + q] = e4m3x8_to_bf16x8(t.c[h][2 * q], t.c[h][2 * q + 1]);
   }
 }
 
 // ----------------------------------------------------------------- stream
-// One query row.  fp8: lane l reads 16 B of key (8 i + l/8) for i < 16 (one
-// coalesced KiB per instruction); bf16: 16 B of key (4 i + l/16) for i < 32.
-template <int KEY_DT>
-__device__ __forceinline__ float stream_block(const ScoreArgs& a, const uint8_t* page,
-                                              const uint8_t* qrow, int lane, int nvalid) {
+// One query row.  Lane (g, m) takes key m of every tile, dims 32 g .. 32 g + 31;
+// its partial dot products are summed over the four lane groups, the keys'
+// maximum over the sixteen lanes of a group.
+template <int KEY_DT, int Q_DT>
+__device__ __forceinline__ float stream_block(const uint8_t* page, const uint8_t* qrow, int lane,
+                                              int nvalid) {
+  constexpr int TB = KEY_DT == ISB_BF16 ? 4096 : 2048;  // bytes of a 16-key tile
+  constexpr int HALF = KEY_DT == ISB_BF16 ? 4 : 8;      // tiles whose loads are in flight together
+  const int m = lane & 15, g = lane >> 4;
+  bf16x2 qv[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x8 q8 = load_q8<Q_DT>(qrow, 32 * g + 8 * j);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) qv[4 * j + x] = bf16x2{q8[2 * x], q8[2 * x + 1]};
+  }
   float best = neg_inf();
   bool nan = false;
-  if constexpr (KEY_DT == ISB_FP8_E4M3) {
-    const int sub = lane & 7, tok0 = lane >> 3;
-    bf16x8 q0 = load_q8(qrow, a.q_dt, 16 * sub);
-    bf16x8 q1 = load_q8(qrow, a.q_dt, 16 * sub + 8);
-    bf16x2 qv[8] = {{q0[0], q0[1]}, {q0[2], q0[3]}, {q0[4], q0[5]}, {q0[6], q0[7]},
-                    {q1[0], q1[1]}, {q1[2], q1[3]}, {q1[4], q1[5]}, {q1[6], q1[7]}};
-    u32x4 raw[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) raw[i] = ld16(page + (8 * i + tok0) * 128 + 16 * sub);
+  for (int part = 0; part < 8 / HALF; ++part) {
+    TileRegs<KEY_DT> t[HALF];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int tt = 0; tt < HALF; ++tt) load_tile<KEY_DT>(t[tt], page + (part * HALF + tt) * TB, lane);
+#pragma unroll
+    for (int tt = 0; tt < HALF; ++tt) {
       float acc = 0.f;
+      if constexpr (KEY_DT == ISB_BF16) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(raw[i][w], false), qv[2 * w], acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(raw[i][w], true), qv[2 * w + 1], acc, false);
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(t[tt].c[h][w]), qv[4 * h + w], acc, false);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(t[tt].c[h][w], false), qv[8 * h + 2 * w],
+                                                  acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(t[tt].c[h][w], true), qv[8 * h + 2 * w + 1],
+                                                  acc, false);
+          }
       }
-      acc += dpp_f32<kDppXor1>(acc);
-      acc += dpp_f32<kDppXor2>(acc);
-      acc += dpp_f32<kDppHalfMirror>(acc);
-      if (8 * i + tok0 < nvalid) {
+      acc += shfl_xor_f32(acc, 16);
+      acc += shfl_xor_f32(acc, 32);
+      if (16 * (part * HALF + tt) + m < nvalid) {
         nan |= acc != acc;
         best = fmaxf(best, acc);
       }
     }
-    best = fmaxf(best, shfl_xor_f32(best, 8));
-  } else {  // bf16 keys
-    const int sub = lane & 15, tok0 = lane >> 4;
-    bf16x8 q0 = load_q8(qrow, a.q_dt, 8 * sub);
-    bf16x2 qv[4] = {{q0[0], q0[1]}, {q0[2], q0[3]}, {q0[4], q0[5]}, {q0[6], q0[7]}};
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 raw[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) raw[i] = ld16(page + (4 * (16 * half + i) + tok0) * 256 + 16 * sub);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(raw[i][w]), qv[w], acc, false);
-        acc += dpp_f32<kDppXor1>(acc);
-        acc += dpp_f32<kDppXor2>(acc);
-        acc += dpp_f32<kDppHalfMirror>(acc);
-        acc += dpp_f32<kDppMirror>(acc);
-        if (4 * (16 * half + i) + tok0 < nvalid) {
-          nan |= acc != acc;
-          best = fmaxf(best, acc);
-        }
-      }
-    }
   }
-  best = max_over_groups(best);
+  // maximum over the sixteen keys of a tile column (lanes of one row of 16)
+  best = fmaxf(best, dpp_f32<kDppXor1>(best));
+  best = fmaxf(best, dpp_f32<kDppXor2>(best));
+  best = fmaxf(best, dpp_f32<kDppHalfMirror>(best));
+  best = fmaxf(best, dpp_f32<kDppMirror>(best));
   if (__ballot(nan)) best = qnan();
   return best;
 }
 
 // ----------------------------------------------------------------- tiles
 // Block maxima for query rows [qt*16, qt*16+16) of request r, bf16 MFMA.
-// Lane (m = lane & 15, g = lane >> 4) supplies key m of a 16-key tile, dims
-// 32 g .. 32 g + 31, and query row m of the tile, the same dims; MFMA j
-// contracts dims 32 g + 8 j .. 32 g + 8 j + 7 of every lane group.
-template <int KEY_DT>
+// Lane (g, m) supplies key m of a tile and query row m, both at dims
+// 32 g .. 32 g + 31; the result lane holds keys 4 g + e of query row m.
+template <int KEY_DT, int Q_DT>
 __device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8_t* page, int r,
                                                  int qt, int QR, int lane, const int* nvalid_row) {
+  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   const int m = lane & 15, g = lane >> 4;
-  const int qbytes = a.q_dt == ISB_BF16 ? 2 : 1;
   const int n = qt * 16 + m;
+  const int nq = n < QR ? n : 0;
   bf16x8 qb[4];
-  if (n < QR) {
-    const int i = n / a.H_idx, h = n % a.H_idx;
-    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim * qbytes;
+  {
+    const int i = nq / a.H_idx, h = nq % a.H_idx;
+    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim * QB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = load_q8(qrow, a.q_dt, 32 * g + 8 * j);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) qb[j] = load_q8<Q_DT>(qrow, 32 * g + 8 * j);
   }
-  const int nv = n < QR ? nvalid_row[n / a.H_idx] : 0;
   float best = neg_inf();
   bool nan = false;
+  if constexpr (KEY_DT == ISB_MXFP4) {
+    u32x4 data[8];
+    uint32_t scl[8];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    bf16x8 kb[4][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = 16 * (4 * half + tt) + m;
-      if constexpr (KEY_DT == ISB_BF16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kb[tt][j] = u32x4_as_bf16x8(ld16(page + tok * 256 + 64 * g + 16 * j));
-      } else if constexpr (KEY_DT == ISB_FP8_E4M3) {
-        u32x4 w0 = ld16(page + tok * 128 + 32 * g);
-        u32x4 w1 = ld16(page + tok * 128 + 32 * g + 16);
-        uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 lo = e4m3x4_to_bf16x4(w[2 * j]);
-          bf16x4 hi = e4m3x4_to_bf16x4(w[2 * j + 1]);
-          kb[tt][j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      } else {  // MXFP4 keys, bf16 query
-        u32x4 w = ld16(page + tok * 64 + 16 * g);
-        const float sc = e8m0_to_f32(ld4(page + kMxDataBytes + 4 * tok) >> (8 * g));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kb[tt][j] = e2m1x8_to_bf16x8(w[j], sc);
-      }
+    for (int tt = 0; tt < 8; ++tt) {
+      const int tok = 16 * tt + m;
+      data[tt] = ld16(page + tok * 64 + 16 * g);
+      scl[tt] = ld4(page + kMxDataBytes + 4 * tok);
     }
+    const int nv = n < QR ? nvalid_row[n / a.H_idx] : 0;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 8; ++tt) {
+      const float sc = e8m0_to_f32(scl[tt] >> (8 * g));
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma_16x16x32_bf16(kb[tt][j], qb[j], acc);
-      // acc[e] = dot(key 16 tile + 4 g + e, query row n)
+      for (int j = 0; j < 4; ++j) acc = mfma_16x16x32_bf16(e2m1x8_to_bf16x8(data[tt][j], sc), qb[j], acc);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (16 * (4 * half + tt) + 4 * g + e < nv) {
+        if (16 * tt + 4 * g + e < nv) {
           nan |= acc[e] != acc[e];
           best = fmaxf(best, acc[e]);
+        }
+      }
+    }
+  } else {
+    constexpr int TB = KEY_DT == ISB_BF16 ? 4096 : 2048;
+    constexpr int HALF = KEY_DT == ISB_BF16 ? 4 : 8;
+    const int nv = n < QR ? nvalid_row[n / a.H_idx] : 0;
+#pragma unroll
+    for (int part = 0; part < 8 / HALF; ++part) {
+      TileRegs<KEY_DT> t[HALF];
+#pragma unroll
+      for (int tt = 0; tt < HALF; ++tt) load_tile<KEY_DT>(t[tt], page + (part * HALF + tt) * TB, lane);
+#pragma unroll
+      for (int tt = 0; tt < HALF; ++tt) {
+        bf16x8 kb[4];
+        tile_operand<KEY_DT>(t[tt], kb);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma_16x16x32_bf16(kb[j], qb[j], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (16 * (part * HALF + tt) + 4 * g + e < nv) {
+            nan |= acc[e] != acc[e];
+            best = fmaxf(best, acc[e]);
+          }
         }
       }
     }
@@ -213,15 +249,7 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, const uint8_
                                                 int qt, int QR, int lane, const int* nvalid_row) {
   const int m = lane & 15, g = lane >> 4;
   const int n = qt * 16 + m;
-  i32x8 qb = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (n < QR) {
-    const int i = n / a.H_idx, h = n % a.H_idx;
-    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim;
-    u32x4 lo = ld16(qrow + 16 * g);
-    u32x4 hi = ld16(qrow + 64 + 16 * g);
-    qb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  }
-  const int nv = n < QR ? nvalid_row[n / a.H_idx] : 0;
+  const int nq = n < QR ? n : 0;
   u32x4 data[8];
   uint32_t scl[8];
 #pragma unroll
@@ -230,11 +258,20 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, const uint8_
     data[tt] = ld16(page + tok * 64 + 16 * g);
     scl[tt] = ld4(page + kMxDataBytes + 4 * tok);
   }
+  i32x8 qb;
+  {
+    const int i = nq / a.H_idx, h = nq % a.H_idx;
+    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim;
+    const u32x4 lo = ld16(qrow + 16 * g);
+    const u32x4 hi = ld16(qrow + 64 + 16 * g);
+    qb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+  const int nv = n < QR ? nvalid_row[n / a.H_idx] : 0;
   float best = neg_inf();
   bool nan = false;
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    i32x8 ka = {(int)data[tt][0], (int)data[tt][1], (int)data[tt][2], (int)data[tt][3], 0, 0, 0, 0};
+    const i32x8 ka = {(int)data[tt][0], (int)data[tt][1], (int)data[tt][2], (int)data[tt][3], 0, 0, 0, 0};
     const int sa = (int)((scl[tt] >> (8 * g)) & 0xFFu);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mfma_scale_fp4_e4m3(ka, qb, acc, sa);
@@ -253,10 +290,12 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, const uint8_
 
 // ----------------------------------------------------------------- kernel
 // grid (ceil(MB / 4), R), 4 waves a workgroup, wave w scores block 4 x + w.
-template <int VARIANT, int KEY_DT>
+template <int VARIANT, int KEY_DT, int Q_DT>
 __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
   __shared__ float s_rowmax[kScoreWaves][kMaxQueryRows];
   __shared__ float s_out[kScoreWaves][kMaxQueryRows];
+  __shared__ int s_nvalid[kScoreWaves][16];
+  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.y;
   const int b = blockIdx.x * kScoreWaves + wave;
@@ -269,9 +308,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
   }
   const int QR = a.q_len * a.H_idx;
   // valid keys of this block for each query token (wave-private LDS)
-  __shared__ int s_nvalid[kScoreWaves][16];
   for (int i = lane; i < a.q_len; i += kWave) {
-    int v = causal_len(L, a.q_len, i) - b * kBlockTokens;
+    const int v = causal_len(L, a.q_len, i) - b * kBlockTokens;
     s_nvalid[wave][i] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
   }
   const int* nvalid_row = s_nvalid[wave];
@@ -284,28 +322,39 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
     write_scores(a, r, b, lane, s_out[wave]);
     return;
   }
-  const uint8_t* page = a.pool + blk * (KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes);
+  constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
+  const uint8_t* page = a.pool + blk * PB;
   if constexpr (VARIANT == 0) {
-    const int qbytes = a.q_dt == ISB_BF16 ? 2 : 1;
-    const uint8_t* qrow = a.q_idx + (size_t)r * kHeadDim * qbytes;  // q_len = H_idx = 1
-    float best = stream_block<KEY_DT>(a, page, qrow, lane, s_nvalid[wave][0]);
+    const uint8_t* qrow = a.q_idx + (size_t)r * kHeadDim * QB;  // q_len = H_idx = 1
+    const float best = stream_block<KEY_DT, Q_DT>(page, qrow, lane, s_nvalid[wave][0]);
     if (lane == 0) s_rowmax[wave][0] = best;
   } else {
     for (int qt = 0; qt * 16 < QR; ++qt) {
       float best;
-      if constexpr (VARIANT == 1) best = tile_block_bf16<KEY_DT>(a, page, r, qt, QR, lane, nvalid_row);
+      if constexpr (VARIANT == 1) best = tile_block_bf16<KEY_DT, Q_DT>(a, page, r, qt, QR, lane, nvalid_row);
       else best = tile_block_fp4(a, page, r, qt, QR, lane, nvalid_row);
       if (lane < 16 && qt * 16 + lane < QR) s_rowmax[wave][qt * 16 + lane] = best;
     }
   }
-  finish(a, r, b, lane, s_rowmax[wave], s_out[wave]);
+  finish<KEY_DT>(a, lane, s_rowmax[wave], s_out[wave]);
   write_scores(a, r, b, lane, s_out[wave]);
 }
 
-template <int VARIANT, int KEY_DT>
+template <int VARIANT, int KEY_DT, int Q_DT>
 static void launch(const ScoreArgs& a, hipStream_t st) {
-  dim3 grid((a.MB + kScoreWaves - 1) / kScoreWaves, a.R);
-  hipLaunchKernelGGL((index_score_kernel<VARIANT, KEY_DT>), grid, dim3(256), 0, st, a);
+  const dim3 grid((a.MB + kScoreWaves - 1) / kScoreWaves, a.R);
+  hipLaunchKernelGGL((index_score_kernel<VARIANT, KEY_DT, Q_DT>), grid, dim3(256), 0, st, a);
+}
+
+template <int KEY_DT, int Q_DT>
+static void launch_key(const ScoreArgs& a, bool one_row, hipStream_t st) {
+  if constexpr (KEY_DT == ISB_MXFP4) {
+    if constexpr (Q_DT == ISB_FP8_E4M3) launch<2, KEY_DT, Q_DT>(a, st);
+    else launch<1, KEY_DT, Q_DT>(a, st);
+  } else {
+    if (one_row) launch<0, KEY_DT, Q_DT>(a, st);
+    else launch<1, KEY_DT, Q_DT>(a, st);
+  }
 }
 
 }  // namespace isb
@@ -324,21 +373,23 @@ extern "C" int isb_index_score(isb_stream_t stream, const void* q_idx, int q_idx
   if (!is_query_dtype(q_idx_dtype) || !is_pool_dtype(idx_dtype)) return ISB_E_UNSUPPORTED_DTYPE;
   if (num_idx_heads % num_kv_heads != 0 || max_blocks > block_table_stride) return ISB_E_SHAPE;
   if (decode_query_len > 16 || decode_query_len * num_idx_heads > kMaxQueryRows) return ISB_E_SHAPE;
+  if (num_reqs > 65535) return ISB_E_SHAPE;
   if (!(idx_scale > 0.f) && idx_dtype == ISB_FP8_E4M3) return ISB_E_INVALID_ARG;
   ScoreArgs a{(const uint8_t*)q_idx, (const uint8_t*)idx_pool, block_table, seq_lens, scores,
-              idx_pool_blocks, idx_scale, q_idx_dtype, idx_dtype, num_idx_heads,
-              block_table_stride, num_reqs, decode_query_len, num_kv_heads, max_blocks};
+              idx_pool_blocks, idx_scale, num_idx_heads, block_table_stride, num_reqs,
+              decode_query_len, num_kv_heads, max_blocks};
   hipStream_t st = as_hip(stream);
   const bool one_row = decode_query_len * num_idx_heads == 1;
+  const bool qb = q_idx_dtype == ISB_BF16;
   if (idx_dtype == ISB_MXFP4) {
-    if (q_idx_dtype == ISB_FP8_E4M3) launch<2, ISB_MXFP4>(a, st);
-    else launch<1, ISB_MXFP4>(a, st);
+    if (qb) launch_key<ISB_MXFP4, ISB_BF16>(a, one_row, st);
+    else launch_key<ISB_MXFP4, ISB_FP8_E4M3>(a, one_row, st);
   } else if (idx_dtype == ISB_FP8_E4M3) {
-    if (one_row) launch<0, ISB_FP8_E4M3>(a, st);
-    else launch<1, ISB_FP8_E4M3>(a, st);
+    if (qb) launch_key<ISB_FP8_E4M3, ISB_BF16>(a, one_row, st);
+    else launch_key<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, one_row, st);
   } else {
-    if (one_row) launch<0, ISB_BF16>(a, st);
-    else launch<1, ISB_BF16>(a, st);
+    if (qb) launch_key<ISB_BF16, ISB_BF16>(a, one_row, st);
+    else launch_key<ISB_BF16, ISB_FP8_E4M3>(a, one_row, st);
   }
   return launch_status();
 }

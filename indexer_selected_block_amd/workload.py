@@ -11,9 +11,10 @@ A request's token at absolute position ``p`` lives in the 128-token block
 ``block_table[r][p // 128]`` at slot ``p % 128``.
 
 * Index cache, one page per 128-token block (page id == block id):
-  - bf16:  128 tokens x 128 dims, token-major, 32768 B;
-  - fp8:   128 tokens x 128 dims of e4m3, token-major, 16384 B, times one
-           per-tensor scale ``idx_scale``;
+  - bf16:  128 tokens x 128 dims, 32768 B: eight 16-token tiles, each laid out
+           like a 16-token K page (``k_page16_bytes``);
+  - fp8:   the same with e4m3 elements, 16384 B, times one per-tensor scale
+           ``idx_scale``;
   - MXFP4: 8704 B = 128 x 64 B of e2m1 data (token j at byte 64 j, dim d in
            byte d // 2, low nibble for even d) followed by 128 x 4 B of e8m0
            scales (token j at byte 8192 + 4 j, scale s covering dims 32 s ..
@@ -448,15 +449,15 @@ def _write_cache(cfg, streams, tid, pool, dtype, which, ids, valid, dist, chunk_
                 vals = _to_bf16_bytes(x).reshape(nb, BLOCK_TOKENS, HEAD_DIM, 2)
             else:
                 vals = _to_e4m3_bytes(x / scale).reshape(nb, BLOCK_TOKENS, HEAD_DIM, 1)
+            # poison the unwritten slots in token order, then lay out the pages
+            bad = slot[None, :] >= valid[s:e, None]
+            pz = torch.tensor([0xC0, 0x7F] if dtype == "bf16" else [_E4M3_NAN],
+                              dtype=torch.uint8, device=dev)
+            vals = torch.where(bad[:, :, None, None], pz, vals)
             if which == "idx":
-                page = vals.reshape(nb, -1)
-                _poison_tail(page, valid[s:e], slot, dtype, which)
+                tiles = vals.reshape(nb * 8, PAGE16_TOKENS, HEAD_DIM, vals.shape[-1])
+                page = k_page16_bytes(tiles).reshape(nb, -1)
             else:
-                # poison the unwritten slots in token order, then lay out the pages
-                bad = slot[None, :] >= valid[s:e, None]
-                pz = torch.tensor([0xC0, 0x7F] if dtype == "bf16" else [_E4M3_NAN],
-                                  dtype=torch.uint8, device=dev)
-                vals = torch.where(bad[:, :, None, None], pz, vals)
                 pages16 = vals.reshape(nb * 8, PAGE16_TOKENS, HEAD_DIM, vals.shape[-1])
                 lay = k_page16_bytes if which == "k" else v_page16_bytes
                 page = lay(pages16).reshape(nb, -1)
@@ -466,7 +467,7 @@ def _write_cache(cfg, streams, tid, pool, dtype, which, ids, valid, dist, chunk_
 
 def _poison_tail(page: torch.Tensor, valid: torch.Tensor, slot: torch.Tensor, dtype: str, which: str) -> None:
     """Overwrite the slots past each block's written length with poison
-    (token-major pages: the index cache and MXFP4 pages)."""
+    (MXFP4 pages, which are token-major)."""
     nb = page.shape[0]
     bad = slot[None, :] >= valid[:, None]            # [nb, 128]
     if not bool(bad.any()):
@@ -477,12 +478,4 @@ def _poison_tail(page: torch.Tensor, valid: torch.Tensor, slot: torch.Tensor, dt
         data.masked_fill_(bad.unsqueeze(-1), _MX_POISON)
         scl.masked_fill_(bad.unsqueeze(-1), _MX_POISON)
         return
-    if dtype == "bf16":
-        vals = page.view(torch.int16)
-        poison = _BF16_NAN_BITS
-    else:
-        vals = page
-        poison = _E4M3_NAN
-    v = vals.view(nb, BLOCK_TOKENS, HEAD_DIM)
-    v.masked_fill_(bad.unsqueeze(-1), poison)
-
+    raise ValueError(dtype)

@@ -7,8 +7,9 @@ Pool layout read here (its own code; it shares nothing with the GPU path):
 * index cache - one page per 128-token block, page id = block id
   (ROCm/ATOM PR 2962, the commit that declares the MXFP4 caches: "a single
   8704 B field per block for the index key"):
-    bf16  [128 tok][128 dim] bf16;
-    fp8   [128 tok][128 dim] e4m3, times the per-tensor ``idx_scale``
+    bf16  eight 16-token tiles, each in the element order of a 16-token K
+          page (below);
+    fp8   the same with e4m3 elements, times the per-tensor ``idx_scale``
           (reading: the index cache takes one per-tensor scale, the same
           convention as the fp8 K/V cache);
     mxfp4 the 8704 B page of ``formats.decode_mxfp4_page``.
@@ -68,10 +69,13 @@ def index_block_keys(idx_pool: np.ndarray, dtype: str, idx_scale: float, block_i
     """Index keys of the given blocks -> float64 [n, 128 tok, 128 dim]."""
     pages = np.asarray(idx_pool)[np.asarray(block_ids, dtype=np.int64)]
     n = pages.shape[0]
-    if dtype == "bf16":
-        return decode_bf16_bytes(pages).reshape(n, BLOCK, 128)
-    if dtype == "fp8":
-        return decode_e4m3(pages).reshape(n, BLOCK, 128) * float(idx_scale)
+    if dtype in ("bf16", "fp8"):
+        e = 2 if dtype == "bf16" else 1
+        tiles = pages.reshape(n * (BLOCK // PAGE16), -1)
+        raw = _gather_elements(tiles, _k_offsets(e), e)
+        if dtype == "bf16":
+            return decode_bf16_bytes(raw).reshape(n, BLOCK, 128)
+        return decode_e4m3(raw).reshape(n, BLOCK, 128) * float(idx_scale)
     if dtype == "mxfp4":
         return decode_mxfp4_page(pages)
     raise ValueError(dtype)

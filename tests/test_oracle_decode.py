@@ -21,16 +21,25 @@ import _pages
 
 
 # ------------------------------------------------------------------ helpers
+def _index_pages(t):
+    """[n, 128 tok, 128 dim] bf16/e4m3 tensor -> index pages: 8 tiles of 16 keys,
+    each laid out lane by lane like a K page."""
+    n = t.shape[0]
+    e = t.element_size()
+    raw = t.contiguous().view(torch.uint8).numpy().reshape(n * 8, 16, 128, e)
+    return _pages.k_pages(raw).reshape(n, -1)
+
+
 def _fp8_index_pool(rng, nblocks):
     vals = torch.from_numpy(rng.standard_normal((nblocks, 128, 128)).astype(np.float32) * 8)
     e4 = vals.to(torch.float8_e4m3fn)
-    return e4.view(torch.uint8).reshape(nblocks, -1).numpy(), e4.double().numpy()
+    return _index_pages(e4), e4.double().numpy()
 
 
 def _bf16_index_pool(rng, nblocks):
     vals = torch.from_numpy(rng.standard_normal((nblocks, 128, 128)).astype(np.float32))
     b = vals.to(torch.bfloat16)
-    return b.view(torch.uint8).reshape(nblocks, -1).numpy(), b.double().numpy()
+    return _index_pages(b), b.double().numpy()
 
 
 def _brute_scores(keys_by_block, q_idx, block_table, seq_lens, q_len, H_kv, MB, idx_scale=1.0):
@@ -99,11 +108,11 @@ def test_index_score_full_blocks_is_blockwise_max():
 
 def test_index_score_is_causal_per_query_token():
     rng = np.random.default_rng(5)
-    pool, _ = _bf16_index_pool(rng, 2)
+    vals = torch.from_numpy(rng.standard_normal((2, 128, 128)).astype(np.float32)).to(torch.bfloat16)
     L = 129                                     # token 0 of 2 sees 128 keys, token 1 sees 129
     # poison the key at position 128 (block 1, slot 0): only token 1 may read it
-    bad = pool.copy()
-    bad[1, :256] = np.frombuffer(np.full(128, 0x7FC0, dtype=np.uint16).tobytes(), dtype=np.uint8)
+    vals[1, 0, :] = float("nan")
+    bad = _index_pages(vals)
     q_idx = rng.standard_normal((2, 1, 128))
     s = od.index_score(q_idx, bad, "bf16", 1.0, np.array([[0, 1]]), np.array([L]), 2, 1, 2)
     assert np.isfinite(s[0, 0, 0]) and s[0, 0, 1] == -np.inf     # token 0: one block

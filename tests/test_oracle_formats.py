@@ -123,15 +123,16 @@ def test_mxfp4_page_hand_built():
 
 def test_pool_readers_match_torch_views():
     # The pool readers against torch's own reinterpretation of the same bytes,
-    # laid out here: index block = [128 tok][128 dim]; K and V pages lane by
-    # lane (tests/_pages.py), for fp8 and bf16.
+    # laid out lane by lane (tests/_pages.py): index blocks as eight K-page
+    # tiles, K and V pages, for fp8 and bf16.
     rng = np.random.default_rng(0)
     vals = torch.from_numpy(rng.standard_normal((3, 128, 128)).astype(np.float32))
-    idx_bf16 = vals.to(torch.bfloat16).view(torch.uint8).reshape(3, -1).numpy()
+    tiles = lambda t: _pages.k_pages(t.view(torch.uint8).numpy().reshape(24, 16, 128, t.element_size())).reshape(3, -1)  # noqa: E731
+    idx_bf16 = tiles(vals.to(torch.bfloat16))
     got = pools.index_block_keys(idx_bf16, "bf16", 1.0, [2, 0])
     assert np.array_equal(got, vals.to(torch.bfloat16).double().numpy()[[2, 0]])
     idx_fp8 = (vals / 4).to(torch.float8_e4m3fn)
-    got = pools.index_block_keys(idx_fp8.view(torch.uint8).reshape(3, -1).numpy(), "fp8", 0.5, [1])
+    got = pools.index_block_keys(tiles(idx_fp8), "fp8", 0.5, [1])
     assert np.array_equal(got[0], idx_fp8.double().numpy()[1] * 0.5)
     k = (vals[:, :16] / 4).to(torch.float8_e4m3fn)            # [3 pages, 16 tok, 128 dim]
     v = (vals[:, 16:32] / 4).to(torch.float8_e4m3fn)
