@@ -170,7 +170,8 @@ int isb_emit_sparse_block_table(isb_stream_t stream, const int32_t* topk_idx,
                                 int32_t* sparse_ctx);
 
 /*
- * Bytes of workspace isb_sparse_pa_decode needs for these arguments: the
+ * Bytes of workspace isb_sparse_pa_decode needs for these arguments: one
+ * arrival counter per row (the first 4 * rows bytes, padded to 256) and the
  * split-K partial results.  Returns 0 for invalid arguments.
  */
 size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv_heads,
@@ -182,9 +183,9 @@ size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv
  * For row (t, g) and query head h of KV group g (vLLM API page, the decode
  * call): z_u = sm_scale * dot(q[t][h], K_u) over sparse positions
  * u < sparse_ctx[row]; out[t][h] = sum_u softmax(z)_u V_u, in fp32, written as
- * bf16.  A row's pages are split across workgroups; a second launch merges
- * the partial results of rows with more than one split (log-sum-exp
- * weights).  Position u is slot u mod P of page sparse_bt[row][u div P], with
+ * bf16.  A row's pages are split across workgroups; the workgroup that
+ * finishes a row last merges its partial results (log-sum-exp weights, in
+ * split order, so results do not depend on timing).  One launch.  Position u is slot u mod P of page sparse_bt[row][u div P], with
  * P = 16 tokens per page (bf16 / fp8 K/V) or 128 (MXFP4 K/V).  fp8 K/V are
  * multiplied by k_scale / v_scale.  Rows with sparse_ctx = 0 output zeros.
  *
@@ -192,9 +193,12 @@ size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv
  *   k_pool, v_pool  [num_pages][num_kv_heads] pages of kv_dtype (layout above)
  *   sparse_bt   [num_tokens * num_kv_heads][sparse_bt_stride] int32 page ids
  *   sparse_ctx  [num_tokens * num_kv_heads] int32, <= sparse_bt_stride * P
- *   workspace   >= isb_sparse_pa_workspace_bytes(...) bytes, 16-byte aligned;
- *               its contents do not matter.  Calls that share a workspace
- *               must not overlap in time.
+ *   workspace   >= isb_sparse_pa_workspace_bytes(...) bytes, 16-byte aligned,
+ *               zero-filled before its first use (e.g. one hipMemsetAsync).
+ *               The arrival counters at its start must be zero when a call
+ *               begins, and every completed call leaves them zero; the rest
+ *               of it may hold anything.  Calls that share a workspace must
+ *               not overlap in time.
  *   out         out, [num_tokens][num_q_heads][128] bf16
  * Shape errors: head_dim != 128, num_q_heads % num_kv_heads, G > 16.
  */

@@ -173,8 +173,8 @@ def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, spa
     T = q.shape[0]
     stride = sparse_bt.shape[1]
     need = sparse_pa_workspace_bytes(T, num_q_heads, num_kv_heads, stride, kv_dtype)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    if workspace is None:  # zero-filled: the arrival counters start at zero
+        workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
     _dev(out, workspace)
@@ -189,7 +189,7 @@ class DecodeLayer:
     """The four calls of one decode layer over a workload, with persistent outputs.
 
     Buffers are allocated once at construction (torch, on the workload's
-    device); ``run()`` only enqueues the five kernels, so it can be timed or
+    device); ``run()`` only enqueues the four kernels, so it can be timed or
     captured."""
 
     def __init__(self, w):
@@ -204,7 +204,7 @@ class DecodeLayer:
         self.sparse_ctx = torch.empty((T * cfg.num_kv_heads,), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, cfg.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
         need = sparse_pa_workspace_bytes(T, cfg.num_q_heads, cfg.num_kv_heads, cfg.top_k * ppb, cfg.kv_dtype)
-        self.workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
 
     def run(self):
         w, cfg = self.w, self.w.cfg

@@ -65,13 +65,15 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   return p;
 }
 
-// Workspace: partial results per (row, split): 16 heads x 128 dims fp32, then
-// 16 x (m, l).
+// Workspace: one arrival counter per row (padded to 256 B), then the partial
+// results per (row, split): 16 heads x 128 dims fp32, then 16 x (m, l).
 constexpr size_t kPartialO = 16 * 128;
 constexpr size_t kPartialML = 16 * 2;
 
+inline size_t pa_arrival_bytes(const PaPlan& p) { return ((size_t)p.rows * 4 + 255) / 256 * 256; }
+
 inline size_t pa_workspace_bytes(const PaPlan& p) {
-  return (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float);
+  return pa_arrival_bytes(p) + (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float);
 }
 
 }  // namespace isb

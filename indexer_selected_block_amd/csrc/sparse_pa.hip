@@ -54,6 +54,7 @@ struct PaArgs {
   const int32_t* sctx;
   float* part_o;
   float* part_ml;
+  uint32_t* arrivals;  // per row: splits that have published (zero between calls)
   __bf16* out;
   int64_t num_pages;
   float qk_scale;  // sm_scale * k_scale * log2(e)
@@ -467,18 +468,77 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   }
 
   if (live > 1) {
-    // Split-K: publish this split's partial; the reduce launch merges them.
+    // Split-K: publish this split's partial with agent-coherent stores, wait
+    // until they are complete, then count the arrival.  The workgroup that
+    // arrives last merges the row (log-sum-exp weights) and clears the count
+    // for the next call.  Only coherent (agent-scope) accesses touch the
+    // partials and the counter, so no cache writeback or invalidation is
+    // needed between workgroups on different dies.
+    __shared__ int s_last;
+    // A split's 16 x 128 partial outputs are stored thread-interleaved
+    // (element x of thread i at 256 x + i), so each store and load
+    // instruction covers 256 contiguous bytes.
     const size_t base = (size_t)row * a.splits + split;
-    float* po = a.part_o + (base * 16 + h) * kHeadDim + d0;
-    *reinterpret_cast<f32x4*>(po) = f32x4{O[0], O[1], O[2], O[3]};
-    *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[4], O[5], O[6], O[7]};
+    float* po = a.part_o + base * kPartialO + threadIdx.x;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) __hip_atomic_store(po + 256 * x, O[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((threadIdx.x & 15) == 0) {
-      a.part_ml[(base * 16 + h) * 2 + 0] = M;
-      a.part_ml[(base * 16 + h) * 2 + 1] = L;
+      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    return;
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(a.arrivals + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(live - 1);
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (h >= a.G) return;
+    // Merge the splits in split order (so the result does not depend on
+    // which workgroup came last): this split's values are in registers, the
+    // others are read back four splits at a time, every load of a group
+    // issued before any use.
+    const float Mo = M, Lo = L;
+    float Oo[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) Oo[x] = O[x];
+    M = neg_inf();
+    L = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) O[x] = 0.f;
+    const size_t b0 = (size_t)row * a.splits * 16 + h;
+    for (int s0 = 0; s0 < live; s0 += 4) {
+      float ms[4], ls[4], os[4][8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int sp = s0 + k < live ? s0 + k : split;
+        const size_t b = b0 + (size_t)sp * 16;
+        ms[k] = __hip_atomic_load(a.part_ml + b * 2 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ls[k] = __hip_atomic_load(a.part_ml + b * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float* pk = a.part_o + ((size_t)row * a.splits + sp) * kPartialO + threadIdx.x;
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          os[k][x] = __hip_atomic_load(pk + 256 * x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int sp = s0 + k;
+        if (sp >= live) break;
+        const bool own = sp == split;
+        const float mk = own ? Mo : ms[k];
+        if (mk == neg_inf()) continue;
+        const float Mn = fmaxf(M, mk);
+        const float wa = M == neg_inf() ? 0.f : exp2f(M - Mn);
+        const float wb = exp2f(mk - Mn);
+        L = L * wa + (own ? Lo : ls[k]) * wb;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : os[k][x]) * wb;
+        M = Mn;
+      }
+    }
   }
-  // A row that fits one split is finished here; the reduce launch skips it.
+  // Finished row: normalise and write bf16.
   if (h < a.G) {
     const float inv = a.v_scale / L;
     bf16x8 ob;
@@ -486,44 +546,6 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
     for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(O[x] * inv);
     *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = ob;
   }
-}
-
-// One workgroup per row with more than one split: merge the row's partial
-// results with log-sum-exp weights, normalise and write bf16.  Rows of one
-// split (and empty rows) were written by the decode launch.
-template <int P>
-__global__ __launch_bounds__(256) void pa_reduce_kernel(PaArgs a) {
-  const int row = blockIdx.x;
-  const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
-  if (h >= a.G) return;
-  const int n_tok = a.sctx[row];
-  const int npages = n_tok > 0 ? min((n_tok + P - 1) / P, a.sbt_stride) : 0;
-  const int live = (npages + a.pps - 1) / a.pps;
-  if (live <= 1) return;
-  const int t = row / a.H_kv, kvh = row % a.H_kv;
-  const size_t b0 = (size_t)row * a.splits * 16 + h;
-  float M = neg_inf();
-  for (int s = 0; s < live; ++s) M = fmaxf(M, a.part_ml[(b0 + (size_t)s * 16) * 2]);
-  float L = 0.f, O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s = 0; s < live; ++s) {
-    const size_t b = b0 + (size_t)s * 16;
-    const float ms = a.part_ml[b * 2];
-    const float wt = ms == neg_inf() ? 0.f : exp2f(ms - M);
-    L += a.part_ml[b * 2 + 1] * wt;
-    const float* po = a.part_o + b * kHeadDim + d0;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      O[x] += x0[x] * wt;
-      O[4 + x] += x1[x] * wt;
-    }
-  }
-  const float inv = a.v_scale / L;
-  bf16x8 ob;
-#pragma unroll
-  for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(O[x] * inv);
-  *reinterpret_cast<bf16x8*>(a.out + ((size_t)t * a.H_q + kvh * a.G + h) * kHeadDim + d0) = ob;
 }
 
 template <int KV_DT, int Q_DT>
@@ -584,7 +606,8 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   a.vp = (const uint8_t*)v_pool;
   a.sbt = sparse_bt;
   a.sctx = sparse_ctx;
-  a.part_o = (float*)workspace;
+  a.arrivals = (uint32_t*)workspace;
+  a.part_o = (float*)((uint8_t*)workspace + pa_arrival_bytes(plan));
   a.part_ml = a.part_o + (size_t)plan.rows * plan.splits * kPartialO;
   a.out = (__bf16*)out;
   a.num_pages = num_pages;
@@ -609,13 +632,6 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   } else {
     if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, st);
     else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, st);
-  }
-  if (plan.splits > 1) {
-    const dim3 rgrid((unsigned)rows);
-    if (kv_dtype == ISB_MXFP4)
-      hipLaunchKernelGGL(pa_reduce_kernel<128>, rgrid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(pa_reduce_kernel<16>, rgrid, dim3(256), 0, st, a);
   }
   return launch_status();
 }

@@ -203,20 +203,28 @@ def test_sparse_pa_every_block_is_dense_attention():
     assert np.abs(out.float().cpu().numpy() - ref).max() <= tol
 
 
+def _arrival_bytes(rows):
+    return (4 * rows + 255) // 256 * 256
+
+
 def test_sparse_pa_repeat_calls_and_output_contents():
-    # Neither the output's nor the workspace's prior contents matter: three
-    # calls with differently filled buffers give bit-identical results.
+    # Neither the output's prior contents nor those of the workspace past its
+    # arrival counters matter: three calls with differently filled buffers give
+    # bit-identical results, and each call leaves the counters zero.
     for name in ("long_context", "fp8_decode", "mxfp4"):
         w, layer, hi = _run_small(name)
         cfg = w.cfg
         outs = []
         for fill, wfill in ((float("nan"), 0xFF), (0.0, 0), (float("inf"), 0x7F)):
             ws = torch.full_like(layer.workspace, wfill)
+            ws[:_arrival_bytes(cfg.num_tokens * cfg.num_kv_heads)] = 0
             out = torch.full((cfg.num_tokens, cfg.num_q_heads, 128), fill, dtype=torch.bfloat16, device="cuda")
             isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
                                  layer.sparse_bt, layer.sparse_ctx, cfg.num_q_heads, cfg.num_kv_heads,
                                  w.sm_scale, out=out, workspace=ws)
             outs.append(out)
+            torch.cuda.synchronize()
+            assert not ws[:_arrival_bytes(cfg.num_tokens * cfg.num_kv_heads)].any()
         torch.cuda.synchronize()
         for o in outs[1:]:
             assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))

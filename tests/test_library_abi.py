@@ -80,9 +80,11 @@ def test_argument_checks_return_before_any_launch(lib):
 
 
 def test_workspace_query(lib):
-    # split-K partials: rows x splits x 16 heads x (128 + 2) floats
+    # one u32 arrival counter per row (padded to 256 B), then the split-K
+    # partials: rows x splits x 16 heads x (128 + 2) floats
     for T, stride, dt in [(128, 128, 1), (4300, 128, 1), (64, 16, 2), (16, 256, 1), (4, 32, 0)]:
         n = lib.isb_sparse_pa_workspace_bytes(T, 16, 1, stride, dt)
+        n -= (4 * T + 255) // 256 * 256
         assert n > 0 and n % (16 * 130 * 4) == 0
         splits = n // (16 * 130 * 4) // T
         assert 1 <= splits <= stride
