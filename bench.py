@@ -2,7 +2,8 @@
 """Benchmark of one indexed block-sparse paged-attention decode layer on one MI355X.
 
 A step is one pass of the whole path over one batch: index_score ->
-topk_select -> emit_sparse_block_table -> sparse_pa_decode (+ its reduce), on
+topk_select_emit (top-k selection and the sparse page table, one launch) ->
+sparse_pa_decode (split-K attention and its merge, one launch), on
 the fp8 decode workload (128 requests x 1 token, contexts U{16384..65536},
 fp8 K/V and index cache, 16 query heads per KV head, top-k 16 blocks) unless
 --config names another.  Inputs are synthetic and resident in HBM before the
@@ -11,8 +12,9 @@ timed region starts.
 Prints one JSON line: decode tokens/s of the whole step (value), the
 attended-KV HBM rate of the attention kernels, per-kernel durations measured
 with HIP events on the launch stream, a roofline entry for the dominant
-kernel (and one for the attention), and the CPU oracle timed on a bounded
-sample of the same workload on this host.
+kernel (and one for the attention), a device copy's measured rate at the
+attention's transfer size and at 1 GiB next to the nominal peak, and the CPU
+oracle timed on a bounded sample of the same workload on this host.
 """
 from __future__ import annotations
 
@@ -65,6 +67,32 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 10}))
 
 
+def measured_copy(nbytes_moved):
+    """Device copy (torch's copy kernel) moving `nbytes_moved` bytes (half read,
+    half written) per launch, cycling over enough buffer pairs to exceed the
+    256 MB last-level cache; GB/s of the average launch, HIP events."""
+    import torch
+    half = max(1 << 20, nbytes_moved // 2)
+    pairs = max(2, -(-(600 << 20) // (2 * half)))
+    bufs = [(torch.ones(half, dtype=torch.uint8, device="cuda"),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(pairs)]
+    reps = max(2 * pairs, 20)
+    for i in range(pairs):
+        bufs[i][1].copy_(bufs[i][0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        src, dst = bufs[i % pairs]
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * half, "avg_us": round(us, 2), "GBps": round(2 * half / (us * 1e-6) / 1e9, 1)}
+
+
 def algorithmic_bytes(w, sparse_ctx):
     """Bytes each kernel must move for this batch (Measurement)."""
     cfg = w.cfg
@@ -78,25 +106,25 @@ def algorithmic_bytes(w, sparse_ctx):
     qidx = T * cfg.num_idx_heads * 128 * Q_BYTES[cfg.qidx_dtype]
     score = (sum(lens) * IDX_BYTES[cfg.idx_dtype] + qidx + 4 * n_req_blocks + 4 * len(lens)
              + 4 * cfg.num_kv_heads * n_tok_blocks)
-    topk = 4 * cfg.num_kv_heads * n_tok_blocks + 4 * cfg.num_kv_heads * T * cfg.top_k
     rows = T * cfg.num_kv_heads
     slots = cfg.top_k * cfg.pages_per_block
-    # emit: the selection and the table entries it names in, the page table and lengths out
-    emit = 4 * cfg.num_kv_heads * T * cfg.top_k * 2 + 4 * rows * (slots + 1) + 4 * len(lens)
+    # top-k + emit: scores and lengths in, the table entries the selection names
+    # in, the selection, the page table and the lengths out
+    topk_emit = (4 * cfg.num_kv_heads * n_tok_blocks + 4 * len(lens) + 4 * rows * cfg.top_k
+                 + 4 * rows * cfg.top_k + 4 * rows * (slots + 1))
     ctx = sparse_ctx.cpu().long()
     attended = int(ctx.sum()) * 2 * KV_BYTES[cfg.kv_dtype]
     ptok = 128 // cfg.pages_per_block
     pages = int(((ctx + ptok - 1) // ptok).sum())
     attn = (attended + T * cfg.num_q_heads * 128 * (Q_BYTES[cfg.q_dtype] + 2) + 4 * pages + 4 * rows)
-    return {"index_score": score, "topk_select": topk, "emit_sparse_block_table": emit,
-            "sparse_pa_decode": attn}, attended
+    return {"index_score": score, "topk_select_emit": topk_emit, "sparse_pa_decode": attn}, attended
 
 
 def kernel_sources_sha():
     """Hash of each kernel's source file, to tell whether stored counters still apply."""
     csrc = os.path.join(ROOT, "indexer_selected_block_amd", "csrc")
-    files = {"index_score": "index_score.hip", "topk_select": "topk_select.hip",
-             "emit_sparse_block_table": "emit.hip", "sparse_pa_decode": "sparse_pa.hip"}
+    files = {"index_score": "index_score.hip", "topk_select_emit": "topk_select.hip",
+             "sparse_pa_decode": "sparse_pa.hip"}
     common = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("isb_device.h", "isb_host.h"))
     return {k: hashlib.sha256(common + open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
             for k, f in files.items()}
@@ -213,8 +241,8 @@ def main():
 
     # ---- per-kernel durations: HIP events on the launch stream around each call
     stream = torch.cuda.current_stream(dev)
-    names = ["index_score", "topk_select", "emit_sparse_block_table", "sparse_pa_decode"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    names = ["index_score", "topk_select_emit", "sparse_pa_decode"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     for s in range(args.steps):
         L = layers[s % len(layers)]
         w, c = L.w, L.w.cfg
@@ -223,15 +251,13 @@ def main():
         isb.index_score(w.q_idx, c.qidx_dtype, w.idx_pool, c.idx_dtype, w.idx_scale, w.block_table,
                         w.seq_lens, c.query_len, c.num_kv_heads, c.max_blocks, scores=L.scores)
         e[1].record(stream)
-        isb.topk_select(L.scores, w.seq_lens, c.query_len, c.top_k, topk_idx=L.topk)
+        isb.topk_select_emit(L.scores, w.seq_lens, c.query_len, c.top_k, w.block_table, c.pages_per_block,
+                             topk_idx=L.topk, sparse_bt=L.sparse_bt, sparse_ctx=L.sparse_ctx)
         e[2].record(stream)
-        isb.emit_sparse_block_table(L.topk, w.block_table, w.seq_lens, c.query_len, c.pages_per_block,
-                                    sparse_bt=L.sparse_bt, sparse_ctx=L.sparse_ctx)
-        e[3].record(stream)
         isb.sparse_pa_decode(w.q, c.q_dtype, w.k_pool, w.v_pool, c.kv_dtype, w.k_scale, w.v_scale,
                              L.sparse_bt, L.sparse_ctx, c.num_q_heads, c.num_kv_heads, w.sm_scale,
                              out=L.out, workspace=L.workspace)
-        e[4].record(stream)
+        e[3].record(stream)
     torch.cuda.synchronize()
     dur_ms = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
               for i, n in enumerate(names)}
@@ -274,6 +300,8 @@ def main():
         "roofline": roof(dominant),
         "roofline_sparse_pa_decode": roof("sparse_pa_decode"),
     }
+    result["measured_copy"] = {"at_attention_size": measured_copy(alg["sparse_pa_decode"]),
+                               "at_1GiB": measured_copy(1 << 30)}
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)

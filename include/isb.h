@@ -9,8 +9,10 @@
  *                                paged index-key cache with the index query;
  *   isb_topk_select              keep the top-k blocks of each (token, KV head);
  *   isb_emit_sparse_block_table  turn the selection into a sparse page table;
+ *   isb_topk_select_emit         both of the above in one launch;
  *   isb_sparse_pa_decode         paged attention over the selected pages only
- *                                (split-K flash decode plus a reduce launch).
+ *                                (split-K flash decode; the last split of a
+ *                                row merges it, in the same launch).
  *
  * The calls follow the decode call of the vLLM API page for
  * vllm.models.minimax_m3.amd.sparse_attention_msa (MiniMaxM3SparseAiterPAImpl
@@ -70,6 +72,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Exported entry points; everything else in the library is hidden. */
+#define ISB_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -93,10 +98,10 @@ typedef enum isb_status {
 } isb_status;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
-int isb_version(void);
+ISB_API int isb_version(void);
 
 /* Static, human-readable text for an isb_status value. */
-const char* isb_strerror(int status);
+ISB_API const char* isb_strerror(int status);
 
 /*
  * isb_index_score - block scores of every (KV head, token, block).
@@ -118,7 +123,7 @@ const char* isb_strerror(int status);
  *   scores       out, [num_kv_heads][T][max_blocks] fp32
  * Shape errors: num_idx_heads % num_kv_heads != 0, max_blocks > stride.
  */
-int isb_index_score(isb_stream_t stream,
+ISB_API int isb_index_score(isb_stream_t stream,
                     const void* q_idx, int q_idx_dtype, int num_idx_heads,
                     const void* idx_pool, int idx_dtype, float idx_scale,
                     int64_t idx_pool_blocks,
@@ -139,7 +144,7 @@ int isb_index_score(isb_stream_t stream,
  *   topk_idx  out, [num_kv_heads][T][top_k] int32
  * Shape errors: top_k < 1, top_k > max_blocks, max_blocks > 1048576.
  */
-int isb_topk_select(isb_stream_t stream, const float* scores,
+ISB_API int isb_topk_select(isb_stream_t stream, const float* scores,
                     const int32_t* seq_lens, int num_reqs, int decode_query_len,
                     int num_kv_heads, int max_blocks, int top_k, int32_t* topk_idx);
 
@@ -162,7 +167,7 @@ int isb_topk_select(isb_stream_t stream, const float* scores,
  *   sparse_ctx  out, [T * num_kv_heads] int32
  * Shape errors: ppb not 1 or 8.
  */
-int isb_emit_sparse_block_table(isb_stream_t stream, const int32_t* topk_idx,
+ISB_API int isb_emit_sparse_block_table(isb_stream_t stream, const int32_t* topk_idx,
                                 const int32_t* block_table, int block_table_stride,
                                 const int32_t* seq_lens, int num_reqs,
                                 int decode_query_len, int num_kv_heads, int top_k,
@@ -170,11 +175,30 @@ int isb_emit_sparse_block_table(isb_stream_t stream, const int32_t* topk_idx,
                                 int32_t* sparse_ctx);
 
 /*
+ * isb_topk_select_emit - isb_topk_select followed by
+ * isb_emit_sparse_block_table, in one launch: each row's workgroup selects its
+ * blocks and writes their pages, so the selection never leaves the chip
+ * between the two steps.  Writes exactly what the two calls write (topk_idx,
+ * sparse_bt, sparse_ctx; same layouts, bit-identical).  Rows too wide for one
+ * workgroup's LDS run as the two separate launches.
+ *
+ * Arguments as in the two calls; max_blocks must not exceed
+ * block_table_stride.  Shape errors: those of both calls.
+ */
+ISB_API int isb_topk_select_emit(isb_stream_t stream, const float* scores,
+                                 const int32_t* seq_lens, int num_reqs,
+                                 int decode_query_len, int num_kv_heads, int max_blocks,
+                                 int top_k, const int32_t* block_table,
+                                 int block_table_stride, int pages_per_block,
+                                 int32_t* topk_idx, int32_t* sparse_bt,
+                                 int32_t* sparse_ctx);
+
+/*
  * Bytes of workspace isb_sparse_pa_decode needs for these arguments: one
  * arrival counter per row (the first 4 * rows bytes, padded to 256) and the
  * split-K partial results.  Returns 0 for invalid arguments.
  */
-size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv_heads,
+ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv_heads,
                                      int sparse_bt_stride, int kv_dtype);
 
 /*
@@ -202,7 +226,7 @@ size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv
  *   out         out, [num_tokens][num_q_heads][128] bf16
  * Shape errors: head_dim != 128, num_q_heads % num_kv_heads, G > 16.
  */
-int isb_sparse_pa_decode(isb_stream_t stream,
+ISB_API int isb_sparse_pa_decode(isb_stream_t stream,
                          const void* q, int q_dtype,
                          const void* k_pool, const void* v_pool, int kv_dtype,
                          int64_t num_pages, float k_scale, float v_scale,

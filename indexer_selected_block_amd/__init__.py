@@ -14,5 +14,6 @@ from .binding import (  # noqa: F401
     sparse_pa_workspace_bytes,
     strerror,
     topk_select,
+    topk_select_emit,
     version,
 )

@@ -60,6 +60,7 @@ _SIGNATURES = {
     "isb_index_score": ([_P, _P, _I, _I, _P, _I, _F, _I64, _P, _I, _P, _I, _I, _I, _I, _P], _I),
     "isb_topk_select": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "isb_emit_sparse_block_table": ([_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P], _I),
+    "isb_topk_select_emit": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P], _I),
     "isb_sparse_pa_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
     "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I,
                               _F, _P, _SZ, _P], _I),
@@ -161,6 +162,24 @@ def emit_sparse_block_table(topk_idx, block_table, seq_lens, decode_query_len, p
     return sparse_bt, sparse_ctx
 
 
+def topk_select_emit(scores, seq_lens, decode_query_len, top_k, block_table, pages_per_block,
+                     topk_idx=None, sparse_bt=None, sparse_ctx=None):
+    """(topk_idx, sparse_bt, sparse_ctx) in one launch (see isb_topk_select_emit)."""
+    dev = _dev(scores, seq_lens, block_table)
+    H_kv, T, MB = scores.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
+    if sparse_bt is None:
+        sparse_bt = torch.empty((T * H_kv, top_k * pages_per_block), dtype=torch.int32, device=dev)
+    if sparse_ctx is None:
+        sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
+    _dev(topk_idx, sparse_bt, sparse_ctx)
+    _call("topk_select_emit", _stream(dev), scores.data_ptr(), seq_lens.data_ptr(), seq_lens.shape[0],
+          decode_query_len, H_kv, MB, top_k, block_table.data_ptr(), block_table.shape[1],
+          pages_per_block, topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr())
+    return topk_idx, sparse_bt, sparse_ctx
+
+
 def sparse_pa_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, sparse_bt_stride, kv_dtype) -> int:
     return int(load_library().isb_sparse_pa_workspace_bytes(
         num_tokens, num_q_heads, num_kv_heads, sparse_bt_stride, _code(kv_dtype)))
@@ -186,11 +205,12 @@ def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, spa
 
 
 class DecodeLayer:
-    """The four calls of one decode layer over a workload, with persistent outputs.
+    """One decode layer over a workload, with persistent outputs: index_score,
+    topk_select_emit (top-k and the sparse table in one launch), sparse_pa_decode.
 
     Buffers are allocated once at construction (torch, on the workload's
-    device); ``run()`` only enqueues the four kernels, so it can be timed or
-    captured."""
+    device); ``run()`` only enqueues the three launches, so it can be timed
+    or captured."""
 
     def __init__(self, w):
         cfg = w.cfg
@@ -210,9 +230,9 @@ class DecodeLayer:
         w, cfg = self.w, self.w.cfg
         index_score(w.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale, w.block_table,
                     w.seq_lens, cfg.query_len, cfg.num_kv_heads, cfg.max_blocks, scores=self.scores)
-        topk_select(self.scores, w.seq_lens, cfg.query_len, cfg.top_k, topk_idx=self.topk)
-        emit_sparse_block_table(self.topk, w.block_table, w.seq_lens, cfg.query_len,
-                                cfg.pages_per_block, sparse_bt=self.sparse_bt, sparse_ctx=self.sparse_ctx)
+        topk_select_emit(self.scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table,
+                         cfg.pages_per_block, topk_idx=self.topk, sparse_bt=self.sparse_bt,
+                         sparse_ctx=self.sparse_ctx)
         sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
                          self.sparse_bt, self.sparse_ctx, cfg.num_q_heads, cfg.num_kv_heads,
                          w.sm_scale, out=self.out, workspace=self.workspace)
@@ -223,5 +243,6 @@ class DecodeLayer:
 isb_index_score = index_score
 isb_topk_select = topk_select
 isb_emit_sparse_block_table = emit_sparse_block_table
+isb_topk_select_emit = topk_select_emit
 isb_sparse_pa_decode = sparse_pa_decode
 isb_sparse_pa_workspace_bytes = sparse_pa_workspace_bytes

@@ -18,7 +18,7 @@ SOURCES = ["capi.hip", "index_score.hip", "topk_select.hip", "emit.hip", "sparse
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
 ]
 
 

@@ -47,6 +47,21 @@ __global__ __launch_bounds__(256) void emit_kernel(const int32_t* __restrict__ t
 
 }  // namespace isb
 
+int isb::emit_launch(hipStream_t st, const int32_t* topk_idx, const int32_t* block_table,
+                    int block_table_stride, const int32_t* seq_lens, int num_reqs,
+                    int decode_query_len, int num_kv_heads, int top_k, int pages_per_block,
+                    int32_t* sparse_bt, int32_t* sparse_ctx) {
+  using namespace isb;
+  const int T = num_reqs * decode_query_len;
+  const long long total = (long long)T * num_kv_heads * top_k * pages_per_block;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)blocks), dim3(256), 0, st, topk_idx, block_table,
+                     block_table_stride, seq_lens, decode_query_len, num_kv_heads, T, top_k,
+                     pages_per_block, sparse_bt, sparse_ctx);
+  return launch_status();
+}
+
 extern "C" int isb_emit_sparse_block_table(isb_stream_t stream, const int32_t* topk_idx,
                                            const int32_t* block_table, int block_table_stride,
                                            const int32_t* seq_lens, int num_reqs,
@@ -59,12 +74,6 @@ extern "C" int isb_emit_sparse_block_table(isb_stream_t stream, const int32_t* t
       block_table_stride <= 0)
     return ISB_E_INVALID_ARG;
   if (pages_per_block != 1 && pages_per_block != 8) return ISB_E_SHAPE;
-  const int T = num_reqs * decode_query_len;
-  const long long total = (long long)T * num_kv_heads * top_k * pages_per_block;
-  const long long blocks = (total + 255) / 256;
-  if (blocks > 0x7FFFFFFFLL) return ISB_E_SHAPE;
-  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)blocks), dim3(256), 0, as_hip(stream), topk_idx,
-                     block_table, block_table_stride, seq_lens, decode_query_len, num_kv_heads, T,
-                     top_k, pages_per_block, sparse_bt, sparse_ctx);
-  return launch_status();
+  return emit_launch(as_hip(stream), topk_idx, block_table, block_table_stride, seq_lens, num_reqs,
+                         decode_query_len, num_kv_heads, top_k, pages_per_block, sparse_bt, sparse_ctx);
 }

@@ -7,13 +7,15 @@
 // largest dot product over the block's causally valid keys, and the index
 // heads of a KV group are summed.
 //
-// One wavefront scores one block of one request against every query row of
+// One wavefront scores a block of one request against every query row of
 // that request (q tokens x H_idx heads), so the block's keys cross HBM once
-// however many tokens the request decodes.  Every load of the block is issued
-// before any math.  Three variants:
-//   * stream - one query row (q = 1, H_idx = 1), bf16 / fp8 keys: packed bf16
-//              dot products on the VALU (2 flop per key byte leaves it far from
-//              busy), partial sums combined across the four lane groups;
+// however many tokens the request decodes.  Every load of a wave is issued
+// before any math, and pages are read with nontemporal loads (they are read
+// once per launch).  Three variants:
+//   * stream - one query row (q = 1, H_idx = 1), bf16 / fp8 keys, two blocks
+//              a wave: packed bf16 dot products on the VALU (2 flop per key
+//              byte leaves it far from busy), partial sums combined across the
+//              four lane groups;
 //   * tile   - several query rows: keys converted to bf16 in registers and
 //              multiplied on v_mfma_f32_16x16x32_bf16, 16 keys x 16 rows a tile;
 //   * fp4    - MXFP4 keys with an e4m3 query: v_mfma_scale_f32_16x16x128_f8f6f4
@@ -91,7 +93,7 @@ struct TileRegs {
 template <int KEY_DT>
 __device__ __forceinline__ void load_tile(TileRegs<KEY_DT>& t, const uint8_t* tile, int lane) {
 #pragma unroll
-  for (int h = 0; h < TileRegs<KEY_DT>::NC; ++h) t.c[h] = ld16(tile + 1024 * h + 16 * lane);
+  for (int h = 0; h < TileRegs<KEY_DT>::NC; ++h) t.c[h] = ld16_nt(tile + 1024 * h + 16 * lane);
 }
 
 // MFMA A operand of a tile: dims 32 g + 8 j .. + 7 of key m in kb[j].
@@ -109,64 +111,99 @@ __device__ __forceinline__ void tile_operand(const TileRegs<KEY_DT>& t, bf16x8 (
 }
 
 // ----------------------------------------------------------------- stream
-// One query row.  Lane (g, m) takes key m of every tile, dims 32 g .. 32 g + 31;
-// its partial dot products are summed over the four lane groups, the keys'
-// maximum over the sixteen lanes of a group.
+// One query row (q = 1, H_idx = H_kv = 1): scores[r][b].  grid
+// (ceil(MB / (4 kStreamBlocks)), R); wave w of workgroup x scores blocks
+// kStreamBlocks (4 x + w) + n.  Lane (g, m) takes key m of every tile, dims
+// 32 g .. 32 g + 31; its partial dot products are summed over the four lane
+// groups, the keys' maximum over the sixteen lanes of a group.  Both blocks'
+// loads are issued before any math; a block past the request's end re-reads
+// the wave's first page (a cache hit) so that no load sits behind a branch.
+constexpr int kStreamBlocks = 2;
+
 template <int KEY_DT, int Q_DT>
-__device__ __forceinline__ float stream_block(const uint8_t* page, const uint8_t* qrow, int lane,
-                                              int nvalid) {
+__global__ __launch_bounds__(256) void index_stream_kernel(ScoreArgs a) {
   constexpr int TB = KEY_DT == ISB_BF16 ? 4096 : 2048;  // bytes of a 16-key tile
-  constexpr int HALF = KEY_DT == ISB_BF16 ? 4 : 8;      // tiles whose loads are in flight together
+  constexpr int64_t PB = 8 * TB;
+  constexpr int NB = kStreamBlocks;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
-  bf16x2 qv[16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bf16x8 q8 = load_q8<Q_DT>(qrow, 32 * g + 8 * j);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) qv[4 * j + x] = bf16x2{q8[2 * x], q8[2 * x + 1]};
+  const int r = blockIdx.y;
+  const int b0 = (blockIdx.x * kScoreWaves + wave) * NB;
+  if (b0 >= a.MB) return;
+  const int L = a.seq_lens[r];
+  const int nr = (L + kBlockTokens - 1) / kBlockTokens;
+  float* srow = a.scores + (size_t)r * a.MB;
+  if (b0 >= nr) {
+    if (lane < NB && b0 + lane < a.MB) srow[b0 + lane] = neg_inf();
+    return;
   }
-  float best = neg_inf();
-  bool nan = false;
+  int64_t blk[NB];
+  bool bad[NB];
 #pragma unroll
-  for (int part = 0; part < 8 / HALF; ++part) {
-    TileRegs<KEY_DT> t[HALF];
+  for (int n = 0; n < NB; ++n) {
+    const int b = b0 + n < nr ? b0 + n : b0;
+    blk[n] = a.bt[(size_t)r * a.bt_stride + b];
+    // an out-of-range block id is poison: its score is NaN, nothing is read through it
+    bad[n] = blk[n] < 0 || blk[n] >= a.pool_blocks;
+    if (bad[n]) blk[n] = 0;
+  }
+  TileRegs<KEY_DT> t[NB][8];
 #pragma unroll
-    for (int tt = 0; tt < HALF; ++tt) load_tile<KEY_DT>(t[tt], page + (part * HALF + tt) * TB, lane);
+  for (int n = 0; n < NB; ++n)
 #pragma unroll
-    for (int tt = 0; tt < HALF; ++tt) {
+    for (int tt = 0; tt < 8; ++tt) load_tile<KEY_DT>(t[n][tt], a.pool + blk[n] * PB + tt * TB, lane);
+  bf16x2 qv[16];
+  {
+    const uint8_t* qrow = a.q_idx + (size_t)r * kHeadDim * (Q_DT == ISB_BF16 ? 2 : 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 q8 = load_q8<Q_DT>(qrow, 32 * g + 8 * j);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qv[4 * j + x] = bf16x2{q8[2 * x], q8[2 * x + 1]};
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int b = b0 + n;
+    const int nvalid = min(L - b * kBlockTokens, kBlockTokens);  // <= 0 past the end
+    float best = neg_inf();
+    bool nan = false;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
       float acc = 0.f;
       if constexpr (KEY_DT == ISB_BF16) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
           for (int w = 0; w < 4; ++w)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(t[tt].c[h][w]), qv[4 * h + w], acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(t[n][tt].c[h][w]), qv[4 * h + w], acc, false);
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(t[tt].c[h][w], false), qv[8 * h + 2 * w],
+            acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(t[n][tt].c[h][w], false), qv[8 * h + 2 * w],
                                                   acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(t[tt].c[h][w], true), qv[8 * h + 2 * w + 1],
-                                                  acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16x2(t[n][tt].c[h][w], true),
+                                                  qv[8 * h + 2 * w + 1], acc, false);
           }
       }
       acc += shfl_xor_f32(acc, 16);
       acc += shfl_xor_f32(acc, 32);
-      if (16 * (part * HALF + tt) + m < nvalid) {
+      if (16 * tt + m < nvalid) {
         nan |= acc != acc;
         best = fmaxf(best, acc);
       }
     }
+    // maximum over the sixteen keys of a tile column (lanes of one row of 16)
+    best = fmaxf(best, dpp_f32<kDppXor1>(best));
+    best = fmaxf(best, dpp_f32<kDppXor2>(best));
+    best = fmaxf(best, dpp_f32<kDppHalfMirror>(best));
+    best = fmaxf(best, dpp_f32<kDppMirror>(best));
+    if (__ballot(nan) || bad[n]) best = qnan();
+    if (KEY_DT == ISB_FP8_E4M3) best *= a.idx_scale;
+    if (lane == 0 && b < a.MB) srow[b] = nvalid > 0 ? best : neg_inf();
   }
-  // maximum over the sixteen keys of a tile column (lanes of one row of 16)
-  best = fmaxf(best, dpp_f32<kDppXor1>(best));
-  best = fmaxf(best, dpp_f32<kDppXor2>(best));
-  best = fmaxf(best, dpp_f32<kDppHalfMirror>(best));
-  best = fmaxf(best, dpp_f32<kDppMirror>(best));
-  if (__ballot(nan)) best = qnan();
-  return best;
 }
 
 // ----------------------------------------------------------------- tiles
@@ -195,8 +232,8 @@ __device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int tok = 16 * tt + m;
-      data[tt] = ld16(page + tok * 64 + 16 * g);
-      scl[tt] = ld4(page + kMxDataBytes + 4 * tok);
+      data[tt] = ld16_nt(page + tok * 64 + 16 * g);
+      scl[tt] = ld4_nt(page + kMxDataBytes + 4 * tok);
     }
     const int nv = n < QR ? nvalid_row[n / a.H_idx] : 0;
 #pragma unroll
@@ -255,8 +292,8 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, const uint8_
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
     const int tok = 16 * tt + m;
-    data[tt] = ld16(page + tok * 64 + 16 * g);
-    scl[tt] = ld4(page + kMxDataBytes + 4 * tok);
+    data[tt] = ld16_nt(page + tok * 64 + 16 * g);
+    scl[tt] = ld4_nt(page + kMxDataBytes + 4 * tok);
   }
   i32x8 qb;
   {
@@ -295,7 +332,6 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
   __shared__ float s_rowmax[kScoreWaves][kMaxQueryRows];
   __shared__ float s_out[kScoreWaves][kMaxQueryRows];
   __shared__ int s_nvalid[kScoreWaves][16];
-  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.y;
   const int b = blockIdx.x * kScoreWaves + wave;
@@ -324,17 +360,11 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
   }
   constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
   const uint8_t* page = a.pool + blk * PB;
-  if constexpr (VARIANT == 0) {
-    const uint8_t* qrow = a.q_idx + (size_t)r * kHeadDim * QB;  // q_len = H_idx = 1
-    const float best = stream_block<KEY_DT, Q_DT>(page, qrow, lane, s_nvalid[wave][0]);
-    if (lane == 0) s_rowmax[wave][0] = best;
-  } else {
-    for (int qt = 0; qt * 16 < QR; ++qt) {
-      float best;
-      if constexpr (VARIANT == 1) best = tile_block_bf16<KEY_DT, Q_DT>(a, page, r, qt, QR, lane, nvalid_row);
-      else best = tile_block_fp4(a, page, r, qt, QR, lane, nvalid_row);
-      if (lane < 16 && qt * 16 + lane < QR) s_rowmax[wave][qt * 16 + lane] = best;
-    }
+  for (int qt = 0; qt * 16 < QR; ++qt) {
+    float best;
+    if constexpr (VARIANT == 1) best = tile_block_bf16<KEY_DT, Q_DT>(a, page, r, qt, QR, lane, nvalid_row);
+    else best = tile_block_fp4(a, page, r, qt, QR, lane, nvalid_row);
+    if (lane < 16 && qt * 16 + lane < QR) s_rowmax[wave][qt * 16 + lane] = best;
   }
   finish<KEY_DT>(a, lane, s_rowmax[wave], s_out[wave]);
   write_scores(a, r, b, lane, s_out[wave]);
@@ -342,8 +372,14 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
 
 template <int VARIANT, int KEY_DT, int Q_DT>
 static void launch(const ScoreArgs& a, hipStream_t st) {
-  const dim3 grid((a.MB + kScoreWaves - 1) / kScoreWaves, a.R);
-  hipLaunchKernelGGL((index_score_kernel<VARIANT, KEY_DT, Q_DT>), grid, dim3(256), 0, st, a);
+  if constexpr (VARIANT == 0) {
+    const int per = kScoreWaves * kStreamBlocks;
+    hipLaunchKernelGGL((index_stream_kernel<KEY_DT, Q_DT>), dim3((a.MB + per - 1) / per, a.R), dim3(256), 0,
+                       st, a);
+  } else {
+    const dim3 grid((a.MB + kScoreWaves - 1) / kScoreWaves, a.R);
+    hipLaunchKernelGGL((index_score_kernel<VARIANT, KEY_DT, Q_DT>), grid, dim3(256), 0, st, a);
+  }
 }
 
 template <int KEY_DT, int Q_DT>

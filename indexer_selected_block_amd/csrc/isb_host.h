@@ -76,4 +76,11 @@ inline size_t pa_workspace_bytes(const PaPlan& p) {
   return pa_arrival_bytes(p) + (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float);
 }
 
+// The standalone emit launch (emit.hip); the fused top-k entry point falls
+// back to it for rows too wide for LDS.
+int emit_launch(hipStream_t st, const int32_t* topk_idx, const int32_t* block_table,
+                int block_table_stride, const int32_t* seq_lens, int num_reqs, int decode_query_len,
+                int num_kv_heads, int top_k, int pages_per_block, int32_t* sparse_bt,
+                int32_t* sparse_ctx);
+
 }  // namespace isb

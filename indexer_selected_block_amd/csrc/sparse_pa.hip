@@ -149,12 +149,12 @@ struct PageRegs {
 template <int KV_DT>
 __device__ __forceinline__ void load_k16(PageRegs<KV_DT>& pr, const uint8_t* kpage, int lane) {
 #pragma unroll
-  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.k[h] = ld16(kpage + 1024 * h + 16 * lane);
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.k[h] = ld16_nt(kpage + 1024 * h + 16 * lane);
 }
 template <int KV_DT>
 __device__ __forceinline__ void load_v16(PageRegs<KV_DT>& pr, const uint8_t* vpage, int lane) {
 #pragma unroll
-  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] = ld16(vpage + 1024 * h + 16 * lane);
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] = ld16_nt(vpage + 1024 * h + 16 * lane);
 }
 
 template <int KV_DT>
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
       if (ok) {
         const uint8_t* vsrc = a.vp + (id * a.H_kv + kvh) * kMxPageBytes;
         for (int x = threadIdx.x; x < kMxPageBytes / 16; x += 256)
-          *reinterpret_cast<u32x4*>(s_v + 16 * x) = ld16(vsrc + 16 * x);
+          *reinterpret_cast<u32x4*>(s_v + 16 * x) = ld16_nt(vsrc + 16 * x);
       }
       __syncthreads();
       const uint8_t* kpage = a.kp + ((ok ? id : 0) * a.H_kv + kvh) * kMxPageBytes;
@@ -412,8 +412,8 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
         bf16x4 vt[8];
         if (ok) {
           const int tok = tile * 16 + c;
-          const u32x4 w = ld16(kpage + tok * 64 + 16 * g);
-          const float sc = e8m0_to_f32(ld4(kpage + kMxDataBytes + 4 * tok) >> (8 * g));
+          const u32x4 w = ld16_nt(kpage + tok * 64 + 16 * g);
+          const float sc = e8m0_to_f32(ld4_nt(kpage + kMxDataBytes + 4 * tok) >> (8 * g));
 #pragma unroll
           for (int j = 0; j < 4; ++j) kb[j] = e2m1x8_to_bf16x8(w[j], sc);
           // V^T: dim 16 dt + c, keys tile*16 + 4 g + e, from the LDS copy.

@@ -1,24 +1,39 @@
 // isb_topk_select: per (KV head, token) row, the tail block plus the top_k - 1
-// best earlier blocks, written ascending.
+// best earlier blocks, written ascending.  isb_topk_select_emit does the same
+// and also writes the sparse page table of the selection (the work of
+// isb_emit_sparse_block_table) from the same workgroup.
 //
 // ROCm/ATOM PR 2962 (decode commit: the tail page is always selected; Pad-row
 // fix: a row of causal length 0 computes nothing) fixes the tail rule and the
 // clamp; ties go to the lower block index.
 //
 // One workgroup selects one row by radix select on order-preserving 32-bit
-// keys: four 8-bit passes build a 256-bin LDS histogram of the keys that match
-// the prefix found so far, and one wave-scanned pass over the bins finds the
-// digit where the count of larger keys reaches top_k - 1.  The threshold key
-// is then exact; keys above it are taken, and keys equal to it are taken in
+// keys: four 8-bit passes build a 256-bin histogram of the keys that match
+// the prefix found so far, and one scan over the bins finds the digit where
+// the count of larger keys reaches top_k - 1.  The threshold key is then
+// exact; keys above it are taken, and keys equal to it are taken in
 // block-index order until the count is met (a block-wide prefix count).  The
 // selected indices are compacted in index order, which gives the ascending
 // output without a sort.
+//
+// Rows of up to 8192 blocks are read from HBM once, into LDS, together with
+// the row's length (and, for the fused emit, its block-table row), so every
+// pass after that is an LDS pass.  Wider rows use the same algorithm over
+// global memory.
 #include "isb_device.h"
 #include "isb_host.h"
 
 namespace isb {
 
-constexpr int kTopkThreads = 256;
+struct TopkArgs {
+  const float* scores;
+  const int32_t* seq_lens;
+  const int32_t* bt;  // fused emit only
+  int32_t* topk;
+  int32_t* sbt;       // fused emit only
+  int32_t* sctx;      // fused emit only
+  int q_len, T, MB, K, H_kv, bt_stride, ppb;
+};
 
 // Order-preserving key: larger score -> larger key; -0.0 == +0.0; every NaN
 // maps to 0, below -inf (0x007FFFFF).
@@ -29,8 +44,9 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum over the 256 threads of the workgroup.
-__device__ __forceinline__ int block_incl_scan(int v, int* s_wave, int* total) {
+// Inclusive prefix sum over the NT threads of the workgroup.
+template <int NT>
+__device__ __forceinline__ int block_incl_scan(int v, int* s_wave) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -40,54 +56,50 @@ __device__ __forceinline__ int block_incl_scan(int v, int* s_wave, int* total) {
   }
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
-  int before = 0, all = 0;
+  int before = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
-    const int c = s_wave[w];
-    before += w < wave ? c : 0;
-    all += c;
-  }
+  for (int w = 0; w < NT / 64; ++w) before += w < wave ? s_wave[w] : 0;
   __syncthreads();
-  if (total) *total = all;
   return x + before;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
-                                                            const int32_t* __restrict__ seq_lens,
-                                                            int q_len, int T, int MB, int K,
-                                                            int32_t* __restrict__ out) {
-  __shared__ int s_hist[256];
-  __shared__ int s_wave[kTopkThreads / 64];
-  __shared__ int s_pick[2];
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x;          // g * T + t
-  const int t = row % T;
-  const int r = t / q_len, i = t % q_len;
-  int Lt = seq_lens[r] - (q_len - 1 - i);
-  Lt = Lt > 0 ? Lt : 0;
+// Causal geometry of topk row `row` (= g * T + t).
+struct RowGeom {
+  int g, t, r, Lt, nt;
+};
+__device__ __forceinline__ RowGeom row_geom(const TopkArgs& a, int row, int Lr) {
+  RowGeom q;
+  q.g = row / a.T;
+  q.t = row % a.T;
+  q.r = q.t / a.q_len;
+  const int i = q.t % a.q_len;
+  const int Lt = Lr - (a.q_len - 1 - i);
+  q.Lt = Lt > 0 ? Lt : 0;
   // n_t never exceeds the score row (callers keep seq_lens <= 128 max_blocks)
-  const int nt = min((Lt + kBlockTokens - 1) / kBlockTokens, MB);
-  int32_t* o = out + (size_t)row * K;
-  const float* s = scores + (size_t)row * MB;
-  const int W = nt - 1;                 // candidates [0, W); block W is the tail
-  if (nt == 0 || W <= K - 1) {
-    for (int j = tid; j < K; j += kTopkThreads) o[j] = j < nt ? j : -1;
-    return;
-  }
-  int need = K - 1;
+  q.nt = min((q.Lt + kBlockTokens - 1) / kBlockTokens, a.MB);
+  return q;
+}
+
+// Selects the row whose keys KEY(j), j < W, are given; writes the K - 1
+// chosen candidates ascending through put(pos, j).  need = K - 1 < W.
+template <int NT, typename KeyFn, typename PutFn>
+__device__ __forceinline__ void radix_select(int W, int need, KeyFn key, PutFn put, int* s_hist,
+                                             int* s_wave, int* s_pick) {
+  const int tid = threadIdx.x;
+  const int keep = need;
   uint32_t prefix = 0u, pmask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    s_hist[tid] = 0;
+    for (int x = tid; x < 256; x += NT) s_hist[x] = 0;
     __syncthreads();
-    for (int j = tid; j < W; j += kTopkThreads) {
-      const uint32_t k = order_key(s[j]);
+    for (int j = tid; j < W; j += NT) {
+      const uint32_t k = key(j);
       if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> shift) & 0xFF], 1);
     }
     __syncthreads();
-    // thread x holds bin 255 - x, so the inclusive scan counts keys >= that bin.
-    const int c = s_hist[255 - tid];
-    const int incl = block_incl_scan(c, s_wave, nullptr);
-    if (incl - c < need && need <= incl) {
+    // thread x < 256 holds bin 255 - x, so the inclusive scan counts keys >= that bin.
+    const int c = tid < 256 ? s_hist[255 - tid] : 0;
+    const int incl = block_incl_scan<NT>(c, s_wave);
+    if (tid < 256 && incl - c < need && need <= incl) {
       s_pick[0] = 255 - tid;
       s_pick[1] = incl - c;
     }
@@ -99,27 +111,138 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
   // prefix is the exact threshold key; `need` keys equal to it are taken, the
   // lowest block indices first.
-  const int chunk = (W + kTopkThreads - 1) / kTopkThreads;
+  const int chunk = (W + NT - 1) / NT;
   const int j0 = tid * chunk;
   const int j1 = min(W, j0 + chunk);
   int eq = 0;
-  for (int j = j0; j < j1; ++j) eq += order_key(s[j]) == prefix;
-  const int eq_before = block_incl_scan(eq, s_wave, nullptr) - eq;
+  for (int j = j0; j < j1; ++j) eq += key(j) == prefix;
+  const int eq_before = block_incl_scan<NT>(eq, s_wave) - eq;
   int take = 0, seen = eq_before;
   for (int j = j0; j < j1; ++j) {
-    const uint32_t k = order_key(s[j]);
+    const uint32_t k = key(j);
     if (k > prefix) ++take;
     else if (k == prefix) take += (seen++ < need);
   }
-  int pos = block_incl_scan(take, s_wave, nullptr) - take;
+  int pos = block_incl_scan<NT>(take, s_wave) - take;
   seen = eq_before;
   for (int j = j0; j < j1; ++j) {
-    const uint32_t k = order_key(s[j]);
+    const uint32_t k = key(j);
     bool sel = k > prefix;
     if (k == prefix) sel = seen++ < need;
-    if (sel && pos < K - 1) o[pos++] = j;
+    if (sel && pos < keep) put(pos++, j);
   }
-  if (tid == 0) o[K - 1] = W;           // the tail block, larger than every candidate
+}
+
+// LDS-resident rows (MB <= 8192).  Dynamic LDS: keys[MB], then (BT_LDS) the
+// block-table row [MB], then (EMIT) the selection [K].
+template <int NT, bool EMIT, bool BT_LDS>
+__global__ __launch_bounds__(NT) void topk_lds_kernel(TopkArgs a) {
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ int s_hist[256];
+  __shared__ int s_wave[NT / 64];
+  __shared__ int s_pick[2];
+  uint32_t* s_key = s_dyn;
+  int32_t* s_bt = reinterpret_cast<int32_t*>(s_dyn + a.MB);
+  int32_t* s_sel = reinterpret_cast<int32_t*>(s_dyn + a.MB * (BT_LDS ? 2 : 1));
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  // Every global load first: length, scores and (fused, narrow rows) the
+  // block-table row, so the workgroup waits for one round trip.
+  const int Lr = a.seq_lens[(row % a.T) / a.q_len];
+  const float* s = a.scores + (size_t)row * a.MB;
+  for (int j = tid; j < a.MB; j += NT) s_key[j] = order_key(s[j]);
+  const RowGeom q = row_geom(a, row, Lr);
+  if constexpr (BT_LDS)
+    for (int j = tid; j < a.MB; j += NT) s_bt[j] = a.bt[(size_t)q.r * a.bt_stride + j];
+  __syncthreads();
+  int32_t* o = a.topk + (size_t)row * a.K;
+  const int W = q.nt - 1;  // candidates [0, W); block W is the tail
+  int m;                   // blocks selected
+  if (q.nt == 0 || W <= a.K - 1) {
+    for (int j = tid; j < a.K; j += NT) {
+      const int v = j < q.nt ? j : -1;
+      o[j] = v;
+      if constexpr (EMIT) s_sel[j] = v;
+    }
+    m = q.nt;
+  } else {
+    radix_select<NT>(
+        W, a.K - 1, [&](int j) { return s_key[j]; },
+        [&](int pos, int j) {
+          o[pos] = j;
+          if constexpr (EMIT) s_sel[pos] = j;
+        },
+        s_hist, s_wave, s_pick);
+    if (tid == 0) {
+      o[a.K - 1] = W;  // the tail block, larger than every candidate
+      if constexpr (EMIT) s_sel[a.K - 1] = W;
+    }
+    m = a.K;
+  }
+  if constexpr (EMIT) {
+    __syncthreads();
+    const int slots = a.K * a.ppb;
+    const int erow = q.t * a.H_kv + q.g;
+    int32_t* so = a.sbt + (size_t)erow * slots;
+    for (int x = tid; x < slots; x += NT) {
+      const int kk = x / a.ppb, p = x % a.ppb;
+      int32_t page = -1;
+      if (kk < m) {
+        const int b = s_sel[kk];
+        const int32_t blk = BT_LDS ? s_bt[b] : a.bt[(size_t)q.r * a.bt_stride + b];
+        page = blk * a.ppb + p;
+      }
+      so[x] = page;
+    }
+    if (tid == 0) a.sctx[erow] = m > 0 ? (m - 1) * kBlockTokens + (q.Lt - kBlockTokens * (q.nt - 1)) : 0;
+  }
+}
+
+// Rows wider than LDS holds: the same selection over global memory.
+__global__ __launch_bounds__(256) void topk_global_kernel(TopkArgs a) {
+  __shared__ int s_hist[256];
+  __shared__ int s_wave[4];
+  __shared__ int s_pick[2];
+  const int row = blockIdx.x;
+  const RowGeom q = row_geom(a, row, a.seq_lens[(row % a.T) / a.q_len]);
+  int32_t* o = a.topk + (size_t)row * a.K;
+  const float* s = a.scores + (size_t)row * a.MB;
+  const int W = q.nt - 1;
+  if (q.nt == 0 || W <= a.K - 1) {
+    for (int j = threadIdx.x; j < a.K; j += 256) o[j] = j < q.nt ? j : -1;
+    return;
+  }
+  radix_select<256>(
+      W, a.K - 1, [&](int j) { return order_key(s[j]); }, [&](int pos, int j) { o[pos] = j; }, s_hist,
+      s_wave, s_pick);
+  if (threadIdx.x == 0) o[a.K - 1] = W;
+}
+
+// Dynamic LDS of topk_lds_kernel, or 0 when the row does not fit.
+inline size_t topk_lds_bytes(int MB, int K, bool emit, bool bt_lds) {
+  if (MB > 8192) return 0;
+  const size_t b = 4 * ((size_t)MB * (bt_lds ? 2 : 1) + (emit ? (size_t)K : 0));
+  return b <= 48 * 1024 ? b : 0;
+}
+
+template <bool EMIT, bool BT_LDS>
+static void launch_lds(const TopkArgs& a, unsigned rows, size_t lds, hipStream_t st) {
+  if (a.MB <= 2048)
+    hipLaunchKernelGGL((topk_lds_kernel<256, EMIT, BT_LDS>), dim3(rows), dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL((topk_lds_kernel<1024, EMIT, BT_LDS>), dim3(rows), dim3(1024), lds, st, a);
+}
+
+// Shared argument checks of the two entry points; 0 or an ISB_E_* code.
+static int check_topk(const float* scores, const int32_t* seq_lens, int32_t* topk_idx, int num_reqs,
+                      int decode_query_len, int num_kv_heads, int max_blocks, int top_k) {
+  if (!scores || !seq_lens || !topk_idx) return ISB_E_INVALID_ARG;
+  if (num_reqs <= 0 || decode_query_len <= 0 || num_kv_heads <= 0 || max_blocks <= 0)
+    return ISB_E_INVALID_ARG;
+  if (top_k < 1 || top_k > max_blocks || max_blocks > (1 << 20)) return ISB_E_SHAPE;
+  const long long rows = (long long)num_reqs * decode_query_len * num_kv_heads;
+  if (rows > 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  return ISB_OK;
 }
 
 }  // namespace isb
@@ -128,14 +251,54 @@ extern "C" int isb_topk_select(isb_stream_t stream, const float* scores, const i
                                int num_reqs, int decode_query_len, int num_kv_heads,
                                int max_blocks, int top_k, int32_t* topk_idx) {
   using namespace isb;
-  if (!scores || !seq_lens || !topk_idx) return ISB_E_INVALID_ARG;
-  if (num_reqs <= 0 || decode_query_len <= 0 || num_kv_heads <= 0 || max_blocks <= 0)
-    return ISB_E_INVALID_ARG;
-  if (top_k < 1 || top_k > max_blocks || max_blocks > (1 << 20)) return ISB_E_SHAPE;
-  const int T = num_reqs * decode_query_len;
-  const long long rows = (long long)T * num_kv_heads;
-  if (rows > 0x7FFFFFFFLL) return ISB_E_SHAPE;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTopkThreads), 0, as_hip(stream),
-                     scores, seq_lens, decode_query_len, T, max_blocks, top_k, topk_idx);
+  const int err = check_topk(scores, seq_lens, topk_idx, num_reqs, decode_query_len, num_kv_heads,
+                             max_blocks, top_k);
+  if (err) return err;
+  TopkArgs a{scores, seq_lens, nullptr, topk_idx, nullptr, nullptr, decode_query_len,
+             num_reqs * decode_query_len, max_blocks, top_k, num_kv_heads, 0, 0};
+  const unsigned rows = (unsigned)((long long)a.T * num_kv_heads);
+  hipStream_t st = as_hip(stream);
+  const size_t lds = topk_lds_bytes(max_blocks, top_k, false, false);
+  if (lds)
+    launch_lds<false, false>(a, rows, lds, st);
+  else
+    hipLaunchKernelGGL(topk_global_kernel, dim3(rows), dim3(256), 0, st, a);
+  return launch_status();
+}
+
+extern "C" int isb_topk_select_emit(isb_stream_t stream, const float* scores,
+                                    const int32_t* seq_lens, int num_reqs, int decode_query_len,
+                                    int num_kv_heads, int max_blocks, int top_k,
+                                    const int32_t* block_table, int block_table_stride,
+                                    int pages_per_block, int32_t* topk_idx, int32_t* sparse_bt,
+                                    int32_t* sparse_ctx) {
+  using namespace isb;
+  const int err = check_topk(scores, seq_lens, topk_idx, num_reqs, decode_query_len, num_kv_heads,
+                             max_blocks, top_k);
+  if (err) return err;
+  if (!block_table || !sparse_bt || !sparse_ctx) return ISB_E_INVALID_ARG;
+  if (block_table_stride <= 0) return ISB_E_INVALID_ARG;
+  if (pages_per_block != 1 && pages_per_block != 8) return ISB_E_SHAPE;
+  if (max_blocks > block_table_stride) return ISB_E_SHAPE;
+  const long long slots = (long long)num_reqs * decode_query_len * num_kv_heads * top_k * pages_per_block;
+  if (slots > 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  TopkArgs a{scores, seq_lens, block_table, topk_idx, sparse_bt, sparse_ctx, decode_query_len,
+             num_reqs * decode_query_len, max_blocks, top_k, num_kv_heads, block_table_stride,
+             pages_per_block};
+  const unsigned rows = (unsigned)((long long)a.T * num_kv_heads);
+  hipStream_t st = as_hip(stream);
+  size_t lds = topk_lds_bytes(max_blocks, top_k, true, true);
+  if (lds) {
+    launch_lds<true, true>(a, rows, lds, st);
+  } else if ((lds = topk_lds_bytes(max_blocks, top_k, true, false)) != 0) {
+    launch_lds<true, false>(a, rows, lds, st);
+  } else {
+    hipLaunchKernelGGL(topk_global_kernel, dim3(rows), dim3(256), 0, st, a);
+    const int e = launch_status();
+    if (e) return e;
+    return emit_launch(st, topk_idx, block_table, block_table_stride, seq_lens, num_reqs,
+                           decode_query_len, num_kv_heads, top_k, pages_per_block, sparse_bt,
+                           sparse_ctx);
+  }
   return launch_status();
 }

@@ -123,7 +123,7 @@ def test_topk_bit_exact(K, q_len, H_kv):
 
 
 @pytest.mark.parametrize("MB,R,q_len,K", [(8192, 8, 2, 32), (256, 1075, 4, 16), (512, 128, 1, 16),
-                                          (1024, 64, 1, 16)])
+                                          (1024, 64, 1, 16), (10000, 4, 1, 32), (3000, 6, 1, 5)])
 def test_topk_full_size_shapes(MB, R, q_len, K):
     _say(f"[topk] MB={MB} rows={R * q_len}")
     rng = np.random.default_rng(MB + R)
@@ -151,6 +151,35 @@ def test_emit_bit_exact(ppb, H_kv, q_len):
     g_sbt, g_sctx = isb.emit_sparse_block_table(torch.from_numpy(topk).cuda(), torch.from_numpy(bt).cuda(),
                                                 torch.from_numpy(lens).cuda(), q_len, ppb)
     torch.cuda.synchronize()
+    assert np.array_equal(g_sbt.cpu().numpy(), sbt)
+    assert np.array_equal(g_sctx.cpu().numpy(), sctx)
+
+
+# ------------------------------------------------------------------ fused top-k + emit
+# Widths cover each launch shape of the fused call: 256-thread rows with the
+# block-table row in LDS, 1024-thread rows with and without it, and rows too
+# wide for LDS (two launches).
+@pytest.mark.parametrize("MB,R,q_len,H_kv,K,ppb", [(48, 24, 1, 1, 7, 8), (40, 19, 3, 2, 9, 1),
+                                                   (512, 40, 1, 1, 16, 8), (3000, 6, 2, 1, 32, 8),
+                                                   (8192, 4, 2, 1, 32, 8), (10000, 3, 1, 2, 16, 1),
+                                                   (300, 5, 4, 1, 300, 8)])
+def test_topk_select_emit_matches_oracle(MB, R, q_len, H_kv, K, ppb):
+    _say(f"[topk+emit] MB={MB} R={R} q={q_len} H_kv={H_kv} K={K} ppb={ppb}")
+    rng = np.random.default_rng(MB * 3 + K)
+    lens = _lengths_covering(rng, R, q_len, MB, K)
+    s = _adversarial_scores(rng, H_kv, R * q_len, MB, K).astype(np.float32)
+    bt = rng.integers(0, 5000, (R, MB + 3)).astype(np.int32)   # table stride wider than MB
+    topk = od.topk_select(s, lens, q_len, K)
+    sbt, sctx = od.emit_sparse_block_table(topk, bt, lens, q_len, H_kv, K, ppb)
+    # prior contents of the outputs do not matter
+    g_topk = torch.full((H_kv, R * q_len, K), 12345, dtype=torch.int32, device="cuda")
+    g_sbt = torch.full((R * q_len * H_kv, K * ppb), -7, dtype=torch.int32, device="cuda")
+    g_sctx = torch.full((R * q_len * H_kv,), 99, dtype=torch.int32, device="cuda")
+    isb.topk_select_emit(torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), q_len, K,
+                         torch.from_numpy(bt).cuda(), ppb, topk_idx=g_topk, sparse_bt=g_sbt,
+                         sparse_ctx=g_sctx)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_topk.cpu().numpy(), topk)
     assert np.array_equal(g_sbt.cpu().numpy(), sbt)
     assert np.array_equal(g_sctx.cpu().numpy(), sctx)
 
