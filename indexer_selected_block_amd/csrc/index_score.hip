@@ -91,9 +91,10 @@ struct TileRegs {
 };
 
 template <int KEY_DT>
-__device__ __forceinline__ void load_tile(TileRegs<KEY_DT>& t, const uint8_t* tile, int lane) {
+__device__ __forceinline__ void load_tile(TileRegs<KEY_DT>& t, __amdgpu_buffer_rsrc_t page, int tile_off,
+                                          int lane) {
 #pragma unroll
-  for (int h = 0; h < TileRegs<KEY_DT>::NC; ++h) t.c[h] = ld16_nt(tile + 1024 * h + 16 * lane);
+  for (int h = 0; h < TileRegs<KEY_DT>::NC; ++h) t.c[h] = bl16_nt(page, 1024 * h + 16 * lane, tile_off);
 }
 
 // MFMA A operand of a tile: dims 32 g + 8 j .. + 7 of key m in kb[j].
@@ -112,20 +113,21 @@ __device__ __forceinline__ void tile_operand(const TileRegs<KEY_DT>& t, bf16x8 (
 
 // ----------------------------------------------------------------- stream
 // One query row (q = 1, H_idx = H_kv = 1): scores[r][b].  grid
-// (ceil(MB / (4 kStreamBlocks)), R); wave w of workgroup x scores blocks
-// kStreamBlocks (4 x + w) + n.  Lane (g, m) takes key m of every tile, dims
+// (ceil(MB / (4 NB)), R); wave w of workgroup x scores blocks NB (4 x + w) + n,
+// NB = 2 for fp8 keys, 1 for bf16 keys.  Lane (g, m) takes key m of every tile, dims
 // 32 g .. 32 g + 31; its partial dot products are summed over the four lane
 // groups, the keys' maximum over the sixteen lanes of a group.  Both blocks'
 // loads are issued before any math; a block past the request's end re-reads
 // the wave's first page (a cache hit) so that no load sits behind a branch.
-constexpr int kStreamBlocks = 2;
+template <int KEY_DT>
+constexpr int stream_blocks() { return KEY_DT == ISB_BF16 ? 1 : 2; }  // 32 KiB of keys a wave
 
 template <int KEY_DT, int Q_DT>
 __global__ __launch_bounds__(256) void index_stream_kernel(ScoreArgs a) {
   constexpr int TB = KEY_DT == ISB_BF16 ? 4096 : 2048;  // bytes of a 16-key tile
   constexpr int64_t PB = 8 * TB;
-  constexpr int NB = kStreamBlocks;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int NB = stream_blocks<KEY_DT>();
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const int r = blockIdx.y;
   const int b0 = (blockIdx.x * kScoreWaves + wave) * NB;
@@ -142,16 +144,13 @@ __global__ __launch_bounds__(256) void index_stream_kernel(ScoreArgs a) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const int b = b0 + n < nr ? b0 + n : b0;
-    blk[n] = a.bt[(size_t)r * a.bt_stride + b];
+    blk[n] = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r * a.bt_stride + b]);
     // an out-of-range block id is poison: its score is NaN, nothing is read through it
     bad[n] = blk[n] < 0 || blk[n] >= a.pool_blocks;
     if (bad[n]) blk[n] = 0;
   }
-  TileRegs<KEY_DT> t[NB][8];
-#pragma unroll
-  for (int n = 0; n < NB; ++n)
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) load_tile<KEY_DT>(t[n][tt], a.pool + blk[n] * PB + tt * TB, lane);
+  // the query first: the load counter is in order, so what is used first is
+  // loaded first
   bf16x2 qv[16];
   {
     const uint8_t* qrow = a.q_idx + (size_t)r * kHeadDim * (Q_DT == ISB_BF16 ? 2 : 1);
@@ -162,6 +161,13 @@ __global__ __launch_bounds__(256) void index_stream_kernel(ScoreArgs a) {
       for (int x = 0; x < 4; ++x) qv[4 * j + x] = bf16x2{q8[2 * x], q8[2 * x + 1]};
     }
   }
+  TileRegs<KEY_DT> t[NB][8];
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) load_tile<KEY_DT>(t[n][tt], page_rsrc(a.pool + blk[n] * PB, PB), tt * TB, lane);
+  // every page load of the wave is in flight before the first use
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const int b = b0 + n;
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(256) void index_stream_kernel(ScoreArgs a) {
 // Lane (g, m) supplies key m of a tile and query row m, both at dims
 // 32 g .. 32 g + 31; the result lane holds keys 4 g + e of query row m.
 template <int KEY_DT, int Q_DT>
-__device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8_t* page, int r,
+__device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, __amdgpu_buffer_rsrc_t page, int r,
                                                  int qt, int QR, int lane, const int* nvalid_row) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   const int m = lane & 15, g = lane >> 4;
@@ -231,9 +237,8 @@ __device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8
     uint32_t scl[8];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const int tok = 16 * tt + m;
-      data[tt] = ld16_nt(page + tok * 64 + 16 * g);
-      scl[tt] = ld4_nt(page + kMxDataBytes + 4 * tok);
+      data[tt] = bl16_nt(page, 64 * m + 16 * g, 1024 * tt);
+      scl[tt] = bl4_nt(page, 4 * m, kMxDataBytes + 64 * tt);
     }
     const int nv = n < QR ? nvalid_row[n / a.H_idx] : 0;
 #pragma unroll
@@ -249,6 +254,7 @@ __device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8
           best = fmaxf(best, acc[e]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     constexpr int TB = KEY_DT == ISB_BF16 ? 4096 : 2048;
@@ -258,7 +264,7 @@ __device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8
     for (int part = 0; part < 8 / HALF; ++part) {
       TileRegs<KEY_DT> t[HALF];
 #pragma unroll
-      for (int tt = 0; tt < HALF; ++tt) load_tile<KEY_DT>(t[tt], page + (part * HALF + tt) * TB, lane);
+      for (int tt = 0; tt < HALF; ++tt) load_tile<KEY_DT>(t[tt], page, (part * HALF + tt) * TB, lane);
 #pragma unroll
       for (int tt = 0; tt < HALF; ++tt) {
         bf16x8 kb[4];
@@ -273,6 +279,9 @@ __device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8
             best = fmaxf(best, acc[e]);
           }
         }
+        // one tile's operands at a time: converting every tile up front would
+        // hold 128 more registers and halve the waves in flight
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -282,7 +291,7 @@ __device__ __forceinline__ float tile_block_bf16(const ScoreArgs& a, const uint8
 }
 
 // MXFP4 keys and an e4m3 query on the scaled MFMA: one instruction a tile.
-__device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, const uint8_t* page, int r,
+__device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, __amdgpu_buffer_rsrc_t page, int r,
                                                 int qt, int QR, int lane, const int* nvalid_row) {
   const int m = lane & 15, g = lane >> 4;
   const int n = qt * 16 + m;
@@ -291,9 +300,8 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, const uint8_
   uint32_t scl[8];
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    const int tok = 16 * tt + m;
-    data[tt] = ld16_nt(page + tok * 64 + 16 * g);
-    scl[tt] = ld4_nt(page + kMxDataBytes + 4 * tok);
+    data[tt] = bl16_nt(page, 64 * m + 16 * g, 1024 * tt);
+    scl[tt] = bl4_nt(page, 4 * m, kMxDataBytes + 64 * tt);
   }
   i32x8 qb;
   {
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
   __shared__ float s_rowmax[kScoreWaves][kMaxQueryRows];
   __shared__ float s_out[kScoreWaves][kMaxQueryRows];
   __shared__ int s_nvalid[kScoreWaves][16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int r = blockIdx.y;
   const int b = blockIdx.x * kScoreWaves + wave;
   if (b >= a.MB) return;
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
     s_nvalid[wave][i] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
   }
   const int* nvalid_row = s_nvalid[wave];
-  const int64_t blk = a.bt[(size_t)r * a.bt_stride + b];
+  const int64_t blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r * a.bt_stride + b]);
   if (blk < 0 || blk >= a.pool_blocks) {
     // An out-of-range block id is poison: NaN where the block is causally
     // visible, -inf elsewhere.  Nothing is read through it.
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
     return;
   }
   constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
-  const uint8_t* page = a.pool + blk * PB;
+  const __amdgpu_buffer_rsrc_t page = page_rsrc(a.pool + blk * PB, (int)PB);
   for (int qt = 0; qt * 16 < QR; ++qt) {
     float best;
     if constexpr (VARIANT == 1) best = tile_block_bf16<KEY_DT, Q_DT>(a, page, r, qt, QR, lane, nvalid_row);
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
 template <int VARIANT, int KEY_DT, int Q_DT>
 static void launch(const ScoreArgs& a, hipStream_t st) {
   if constexpr (VARIANT == 0) {
-    const int per = kScoreWaves * kStreamBlocks;
+    const int per = kScoreWaves * stream_blocks<KEY_DT>();
     hipLaunchKernelGGL((index_stream_kernel<KEY_DT, Q_DT>), dim3((a.MB + per - 1) / per, a.R), dim3(256), 0,
                        st, a);
   } else {

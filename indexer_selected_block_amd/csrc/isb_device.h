@@ -25,6 +25,10 @@ constexpr int kMxPageBytes = kMxDataBytes + 128 * 4;  // 8704
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWave = 64;
 
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar)
+// value, so that addresses derived from it live in scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
 
@@ -47,6 +51,23 @@ __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
 }
 __device__ __forceinline__ uint32_t ld4_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// Raw buffer loads from one cache page.  The page's base address sits in a
+// wave-uniform buffer descriptor (scalar registers), so a wave's loads share
+// one per-lane offset register and add the rest as scalar and immediate
+// offsets, instead of holding a 64-bit address pair per load.  Descriptor
+// word 3 is the raw-buffer format of the gfx9 family; `bytes` bounds the page
+// (loads past it return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 / 4 bytes at voff + soff, nontemporal (cache policy nt: read once).
+__device__ __forceinline__ u32x4 bl16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+__device__ __forceinline__ uint32_t bl4_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 2);
 }
 
 // ----------------------------------------------------------------- conversions

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_v[KV_DT == ISB_MXFP4 ? kMxPageBytes : 16];
 
   const int row = blockIdx.x, split = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
