@@ -25,16 +25,15 @@ inline int64_t idx_page_bytes(int dt) {
 }
 
 // Split-K plan of isb_sparse_pa_decode; shared by the workspace query so the
-// two always agree.  A split is one workgroup of four waves.
-//  16-token pages: each wave attends a run of `pages_per_wave` pages (1, 2, 4
-//    or 8 fp8 / up to 4 bf16 pages, whose loads it issues at once); the run
-//    is the shortest power of two that covers the batch with ~2048 waves (8
-//    per CU), so one round of waves has the whole batch in flight.
-//  128-token MXFP4 pages: the workgroup walks `pages_per_split` pages together.
+// two always agree.  A split is one workgroup of four waves; a wave attends a
+// run of `pages_per_wave` consecutive pages whose loads it issues at once:
+// 8 fp8 / 4 bf16 16-token pages (32 KiB of K and V), or one 128-token MXFP4
+// page.  Decode launches are latency-bound, so a wave takes the largest run
+// its registers hold: fewer, fuller waves and fewer partials to merge.
 struct PaPlan {
   int rows;             // num_tokens * num_kv_heads
   int max_pages;        // sparse_bt_stride
-  int pages_per_wave;   // 16-token pages: run of one wave
+  int pages_per_wave;   // run of one wave
   int pages_per_split;  // pages one workgroup attends
   int splits;           // workgroups per row
 };
@@ -43,23 +42,8 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   PaPlan p;
   p.rows = num_tokens * num_kv_heads;
   p.max_pages = sparse_bt_stride;
-  if (kv_dtype == ISB_MXFP4) {
-    const int target_wgs = 1024;
-    int want = (target_wgs + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
-    if (want > p.max_pages) want = p.max_pages;
-    if (want < 1) want = 1;
-    p.pages_per_wave = 0;
-    p.pages_per_split = (p.max_pages + want - 1) / want;
-  } else {
-    const int max_run = kv_dtype == ISB_BF16 ? 4 : 8;
-    const long long total = (long long)p.rows * p.max_pages;
-    const long long waves = 256LL * 8;
-    const long long need = (total + waves - 1) / waves;
-    int run = 1;  // a power of two: the kernel is specialised on it
-    while (run < need && run < max_run) run *= 2;
-    p.pages_per_wave = run;
-    p.pages_per_split = 4 * p.pages_per_wave;
-  }
+  p.pages_per_wave = kv_dtype == ISB_MXFP4 ? 1 : kv_dtype == ISB_BF16 ? 4 : 8;
+  p.pages_per_split = 4 * p.pages_per_wave;
   p.splits = (p.max_pages + p.pages_per_split - 1) / p.pages_per_split;
   if (p.splits < 1) p.splits = 1;
   return p;

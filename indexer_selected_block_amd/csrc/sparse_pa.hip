@@ -1,5 +1,5 @@
-// isb_sparse_pa_decode: split-K flash decode over the selected pages, then a
-// reduce launch that merges the splits of rows that needed more than one.
+// isb_sparse_pa_decode: split-K flash decode over the selected pages; the
+// last workgroup to finish a row merges the row's splits, in the same launch.
 //
 // The decode call of the vLLM API page for sparse_attention_msa
 // (minimax_m3_sparse_attn_decode_aiter with the emitted sparse_block_table and
@@ -8,13 +8,15 @@
 // ROCm/ATOM PR 2962 (Summary: MXFP4 K and V pages, one row per token and KV
 // head).
 //
-// Work decomposition.  A row's pages are cut into `splits` runs of
-// `pages_per_split`; one workgroup of four waves attends one run.  A wave
-// takes 16-token tiles:
-//   S^T (16 keys x 16 heads) = K_tile . Q^T      4 x v_mfma_f32_16x16x32_bf16
-//   online softmax in fp32 (row max over lane groups by lane shuffles)
-//   O^T (128 dims x 16 heads) += V^T . P^T       v_mfma_f32_16x16x32_bf16 for two
-//                                                tiles, 16x16x16 for one
+// Work decomposition.  A row's pages are cut into splits of four waves' runs;
+// one workgroup attends one split.  A wave issues every load of its run (up
+// to 8 fp8 / 4 bf16 16-token pages, or one 128-token MXFP4 page) before any
+// math, computes every logit of the run, takes one exact maximum per head,
+// then the probabilities and P.V, so its output needs no online rescaling.
+// The four waves merge in LDS, the splits of a row through the workspace.
+//   S^T (16 keys x 16 heads) = K_tile . Q^T      v_mfma_f32_16x16x32_bf16, or
+//                                                one scaled fp4 x fp8 MFMA
+//   O^T (128 dims x 16 heads) += V^T . P^T       v_mfma_f32_16x16x{32,16}_bf16
 // The G <= 16 query heads of a KV group fill the MFMA's 16 columns, so K and V
 // bytes are read once per row and reused by every head.  K and V are
 // dequantised to bf16 in registers (exact for e4m3 and for e2m1 x 2^k); the
@@ -26,21 +28,25 @@
 //                     dims 32 g + 8 j .. + 7);  Q^T, B of QK: head c, same dims;
 //   S^T result:       lane holds keys 4 g + e (e < 4) of head c;
 //   P^T, B of PV:     exactly that: head c, keys 4 g + e;
-//   V^T, A of PV:     dim 16 dt + c, keys 4 g + e;
-//   O^T result:       lane holds dims 16 dt + 4 g + e of head c.
-// Every value a lane holds belongs to its head c, so the softmax rescale of
-// the output is lane-local.
+//   V^T, A of PV:     row r of MFMA dt is one dim, keys 4 g + e;
+//   O^T result:       lane holds rows 4 g + e of each dt, head c.
+// Every value a lane holds belongs to its head c, so the softmax needs only
+// lane-group reductions.
 //
 // 16-token (bf16 / fp8) pages are stored lane-native: the 16-byte chunk h of
 // lane l sits at byte 1024 h + 16 l of the K page and of the V page (K: dims
 // 32 g + 16 h .. of key c for fp8; V: dim tiles 4 h .. 4 h + 3, keys 4 g ..
 // 4 g + 3 of dim c for fp8), so every load instruction reads one contiguous
-// KiB and a page costs 4 (fp8) or 8 (bf16) loads a lane.  A wave issues every
-// load of its run of pages before any math, with no branch between them, so
-// its whole share of the row is in flight at once.
-// 128-token MXFP4 pages are token-major (the page format of the MXFP4 cache),
-// which puts a V tile's keys for one dim in four different rows; the
-// workgroup stages each V page in LDS and lanes read their nibbles from there.
+// KiB and row r of V^T tile dt is dim 16 dt + r.
+// 128-token MXFP4 pages are token-major (the page format of the MXFP4 cache).
+// K: lane (g, c) of tile t loads the 16 bytes of token 16 t + c that hold dims
+// 32 g .., and their e8m0 scale; with an e4m3 query the scaled MFMA multiplies
+// them as stored.  V: the wave copies its page to a wave-private LDS buffer;
+// lane (g, c) reads one 4-byte word per key, dims 8 c .. 8 c + 7, so row r of
+// V^T tile dt is dim 8 r + dt.
+//
+// Page loads are raw buffer loads from a wave-uniform descriptor of the page
+// (one offset register a wave, nontemporal: every page is read once).
 #include "isb_device.h"
 #include "isb_host.h"
 
@@ -59,82 +65,168 @@ struct PaArgs {
   int64_t num_pages;
   float qk_scale;  // sm_scale * k_scale * log2(e)
   float v_scale;
-  int sbt_stride, H_q, H_kv, G, splits, pps, ppw;
+  int sbt_stride, H_q, H_kv, G, splits, pps;
 };
 
 constexpr int kPaWaves = 4;
+constexpr int kMergeGroup = 8;  // splits whose partials the merging workgroup loads at once
 
 template <int Q_DT>
 __device__ __forceinline__ bf16x8 load_q8_t(const uint8_t* row, int dim0) {
   if constexpr (Q_DT == ISB_BF16) {
     return u32x4_as_bf16x8(ld16(row + 2 * dim0));
   } else {
-    u32x2 w = ld8(row + dim0);
-    bf16x4 a = e4m3x4_to_bf16x4(w[0]);
-    bf16x4 b = e4m3x4_to_bf16x4(w[1]);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const u32x2 w = ld8(row + dim0);
+    return e4m3x8_to_bf16x8(w[0], w[1]);
   }
 }
 
-// Running state of one wave: per lane, head c = lane & 15.
-struct Softmax {
-  float m;      // running max of scaled logits (log2 domain), same in the 4 lane groups
-  float l;      // this lane's share of the running sum
-  f32x4 o[8];   // O^T: dims 16 dt + 4 g + e of head c
+__device__ __forceinline__ bool page_ok(int64_t id, int64_t n) { return id >= 0 && id < n; }
+
+// Per-workgroup LDS of the merge: each wave's per-head max and sum, and its
+// unnormalised output O[head][dim].
+struct WaveParts {
+  float m[kPaWaves][16];
+  float l[kPaWaves][16];
+  float o[kPaWaves][16][kHeadDim + 4];
 };
 
-__device__ __forceinline__ void softmax_init(Softmax& st) {
-  st.m = neg_inf();
-  st.l = 0.f;
+// The workgroup's share of a row, once every wave has written its part: merge
+// the waves; a row of one split is finished here, otherwise the split is
+// published and the last split to arrive merges the row (log-sum-exp weights,
+// in split order) and writes it.  Thread (h, d0) = (tid / 16, 8 (tid % 16))
+// owns dims d0 .. d0 + 7 of head h.
+__device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts& wp, int row, int split, int live,
+                                             __bf16* out_row) {
+  __shared__ int s_last;
+  const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
+  __syncthreads();
+  float M = neg_inf();
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < kPaWaves; ++w) M = fmaxf(M, wp.m[w][h]);
+  float L = 0.f, O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < kPaWaves; ++w) {
+    const float mw = wp.m[w][h];
+    const float wt = mw == neg_inf() ? 0.f : exp2f(mw - M);
+    L += wp.l[w][h] * wt;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) O[x] += wp.o[w][h][d0 + x] * wt;
+  }
+
+  if (live > 1) {
+    // Publish this split's partial with agent-coherent stores, wait until
+    // they are complete, then count the arrival.  The workgroup that arrives
+    // last merges the row and clears the count for the next call.  Only
+    // coherent (agent-scope) accesses touch the partials and the counter, so
+    // no cache writeback or invalidation is needed between workgroups on
+    // different dies.  A split's 16 x 128 outputs are stored
+    // thread-interleaved (element x of thread i at 256 x + i), so each store
+    // and load instruction covers 256 contiguous bytes.
+    const size_t base = (size_t)row * a.splits + split;
+    float* po = a.part_o + base * kPartialO + threadIdx.x;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) __hip_atomic_store(po + 256 * x, O[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((threadIdx.x & 15) == 0) {
+      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(a.arrivals + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(live - 1);
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (h >= a.G) return;
+    // Merge in split order, so the result does not depend on which workgroup
+    // came last: this split's values are in registers, the others are read
+    // back kMergeGroup splits at a time, every load of a group issued first.
+    const float Mo = M, Lo = L;
+    float Oo[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) Oo[x] = O[x];
+    M = neg_inf();
+    L = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) O[x] = 0.f;
+    for (int s0 = 0; s0 < live; s0 += kMergeGroup) {
+      float ms[kMergeGroup], ls[kMergeGroup], os[kMergeGroup][8];
+#pragma unroll
+      for (int k = 0; k < kMergeGroup; ++k) {
+        const int sp = s0 + k;
+        if (sp < live && sp != split) {  // a wave-uniform branch
+          const size_t b = ((size_t)row * a.splits + sp) * 16 + h;
+          ms[k] = __hip_atomic_load(a.part_ml + b * 2 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ls[k] = __hip_atomic_load(a.part_ml + b * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float* pk = a.part_o + ((size_t)row * a.splits + sp) * kPartialO + threadIdx.x;
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            os[k][x] = __hip_atomic_load(pk + 256 * x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeGroup; ++k) {
+        const int sp = s0 + k;
+        if (sp >= live) break;
+        const bool own = sp == split;
+        const float mk = own ? Mo : ms[k];
+        if (mk == neg_inf()) continue;
+        const float Mn = fmaxf(M, mk);
+        const float wa = M == neg_inf() ? 0.f : exp2f(M - Mn);
+        const float wb = exp2f(mk - Mn);
+        L = L * wa + (own ? Lo : ls[k]) * wb;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : os[k][x]) * wb;
+        M = Mn;
+      }
+    }
+  }
+  // Finished row: normalise and write bf16.
+  if (h < a.G) {
+    const float inv = a.v_scale / L;
+    bf16x8 ob;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(O[x] * inv);
+    *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = ob;
+  }
 }
 
-// Folds the logits z (NZ per lane, -inf where masked) into the running state
-// and returns the probabilities to multiply into V.  The output is rescaled
-// only when some head's running max moved (a wave-uniform branch, rare after
-// the first pages).
-template <int NZ>
-__device__ __forceinline__ void softmax_update(Softmax& st, const float (&z)[NZ], float (&p)[NZ]) {
-  float tmax = neg_inf();
+// A row with nothing to attend outputs zeros (split 0 writes them).
+__device__ __forceinline__ void write_empty_row(const PaArgs& a, int split, __bf16* out_row) {
+  const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
+  if (split == 0 && h < a.G) {
+    bf16x8 z;
 #pragma unroll
-  for (int e = 0; e < NZ; ++e) tmax = fmaxf(tmax, z[e]);
-  tmax = max_over_groups(tmax);
-  const float m_new = fmaxf(st.m, tmax);
-  float psum = 0.f;
-#pragma unroll
-  for (int e = 0; e < NZ; ++e) {
-    p[e] = exp2f(z[e] - m_new);
-    psum += p[e];
+    for (int x = 0; x < 8; ++x) z[x] = (__bf16)0.f;
+    *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = z;
   }
-  if (__ballot(m_new > st.m)) {
-    const float alpha = exp2f(st.m - m_new);  // 0 while m = -inf
-    st.l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
-  }
-  st.l += psum;
-  st.m = m_new;
 }
 
-// One 16-key tile: kb = K tile as the A operand (4 x bf16x8), vt = V^T tile
-// (8 x bf16x4), nvalid = keys of the tile that count (1..16), bad = NaN poison.
-__device__ __forceinline__ void attend_tile(Softmax& st, const bf16x8 (&qb)[4], const bf16x8 (&kb)[4],
-                                            const bf16x4 (&vt)[8], int nvalid, bool bad,
-                                            float qk_scale, int g) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) s = mfma_16x16x32_bf16(kb[j], qb[j], s);
-  float z[4], p[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float v = bad ? qnan() : s[e] * qk_scale;
-    z[e] = (4 * g + e < nvalid) ? v : neg_inf();
+// A wave's result in LDS; row r of V^T tile dt is dim DIM_MUL r + DT_MUL dt.
+template <int DIM_MUL, int DT_MUL>
+__device__ __forceinline__ void wave_to_lds(WaveParts& wp, int wave, int lane, float m, float l,
+                                            const f32x4 (&o)[8]) {
+  const int c = lane & 15, g = lane >> 4;
+  const float l_tot = sum_over_groups(l);
+  if (lane < 16) {
+    wp.m[wave][c] = m;
+    wp.l[wave][c] = l_tot;
   }
-  softmax_update<4>(st, z, p);
-  const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16_bf16(vt[dt], pb, st.o[dt]);
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wp.o[wave][c][DIM_MUL * (4 * g + e) + DT_MUL * dt] = o[dt][e];
+}
+
+// Query columns past the group's G heads are zero (they were loaded from head
+// 0 so the load needs no branch).
+__device__ __forceinline__ void zero_missing_heads(bf16x8 (&qb)[4], int c, int G) {
+  if (c >= G) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
 }
 
 // ----------------------------------------------------------------- 16-token pages
@@ -147,14 +239,14 @@ struct PageRegs {
 };
 
 template <int KV_DT>
-__device__ __forceinline__ void load_k16(PageRegs<KV_DT>& pr, const uint8_t* kpage, int lane) {
+__device__ __forceinline__ void load_k16(PageRegs<KV_DT>& pr, __amdgpu_buffer_rsrc_t kpage, int lane) {
 #pragma unroll
-  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.k[h] = ld16_nt(kpage + 1024 * h + 16 * lane);
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.k[h] = bl16_nt(kpage, 1024 * h + 16 * lane, 0);
 }
 template <int KV_DT>
-__device__ __forceinline__ void load_v16(PageRegs<KV_DT>& pr, const uint8_t* vpage, int lane) {
+__device__ __forceinline__ void load_v16(PageRegs<KV_DT>& pr, __amdgpu_buffer_rsrc_t vpage, int lane) {
 #pragma unroll
-  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] = ld16_nt(vpage + 1024 * h + 16 * lane);
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] = bl16_nt(vpage, 1024 * h + 16 * lane, 0);
 }
 
 template <int KV_DT>
@@ -172,8 +264,6 @@ __device__ __forceinline__ void page16_operands_v(const PageRegs<KV_DT>& pr, bf1
       for (int q = 0; q < 4; ++q) vt[4 * h + q] = e4m3x4_to_bf16x4(pr.v[h][q]);
   }
 }
-
-__device__ __forceinline__ bool page_ok(int64_t id, int64_t n) { return id >= 0 && id < n; }
 
 // Keys at or past nvalid in a page may hold anything (0 x NaN would poison
 // the sum), so their raw V bytes are cleared before conversion.  Lane
@@ -227,29 +317,13 @@ __device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const
   }
 }
 
-
-
-// Query columns past the group's G heads are zero (they were loaded from head
-// 0 so the load needs no branch).
-__device__ __forceinline__ void zero_missing_heads(bf16x8 (&qb)[4], int c, int G) {
-  if (c >= G) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-}
-
-// ----------------------------------------------------------------- decode kernel
-// RUN: pages of one wave's run (16-token pages; a power of two).  Q_DT: query
-// dtype.  grid (rows, splits), four waves a workgroup.
+// RUN: pages of one wave's run (a power of two).  grid (rows, splits), four
+// waves a workgroup.
 template <int KV_DT, int Q_DT, int RUN>
-__global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
-  constexpr int P = KV_DT == ISB_MXFP4 ? 128 : 16;
+__global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
-  __shared__ float s_m[kPaWaves][16];
-  __shared__ float s_l[kPaWaves][16];
-  __shared__ float s_o[kPaWaves][16][kHeadDim + 4];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[KV_DT == ISB_MXFP4 ? kMxPageBytes : 16];
-
+  constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
+  __shared__ WaveParts wp;
   const int row = blockIdx.x, split = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -260,9 +334,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
   // length and the query, so the K/V gathers start after one round trip.
   const int wb = p0 + wave * RUN;
   int my_id = -1;
-  if constexpr (KV_DT != ISB_MXFP4) {
-    if (lane < RUN && wb + lane < a.sbt_stride) my_id = pages[wb + lane];
-  }
+  if (lane < RUN && wb + lane < a.sbt_stride) my_id = pages[wb + lane];
   const int n_tok = a.sctx[row];
   // Q^T operand: head kvh * G + c, dims 32 g .. 32 g + 31 (zero past G).
   bf16x8 qb[4];
@@ -272,297 +344,247 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
   }
-  const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);  // merge / output layout
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  if (n_tok <= 0) {  // an empty row attends nothing: split 0 writes its zeros
-    if (split == 0 && h < a.G) {
-      bf16x8 z;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) z[x] = (__bf16)0.f;
-      *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = z;
-    }
+  if (n_tok <= 0) {
+    write_empty_row(a, split, out_row);
     return;
   }
   // a row never lists more pages than its table row holds
-  const int npages = min((n_tok + P - 1) / P, a.sbt_stride);
+  const int npages = min((n_tok + 15) / 16, a.sbt_stride);
   if (p0 >= npages) return;
   const int p1 = min(npages, p0 + a.pps);
   const int live = (npages + a.pps - 1) / a.pps;  // splits of this row that have pages
 
-  Softmax st;
-  softmax_init(st);
-
-  if constexpr (KV_DT != ISB_MXFP4) {
-    constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
-    const int64_t hstride = (int64_t)a.H_kv * PB;  // bytes per page id (all heads)
-    const int64_t hoff = (int64_t)kvh * PB;
-    const int cnt = max(0, min(RUN, p1 - wb));
-    if (cnt > 0) {
-      // Every load of the run, unconditionally: slots past the run re-read
-      // its first page, an out-of-range id reads page 0 and poisons its tile.
-      // All K chunks are issued before all V chunks, page by page, and kept in
-      // that order, so the logits of page j wait only for K of pages <= j and
-      // P.V of page j only for V of pages <= j.
-      PageRegs<KV_DT> pr[RUN];
-      bool ok[RUN];
-      int64_t use[RUN];
+  float mx = neg_inf(), lsum = 0.f;
+  f32x4 o[8];
 #pragma unroll
-      for (int j = 0; j < RUN; ++j) {
-        const int64_t id = __builtin_amdgcn_readlane(my_id, j < cnt ? j : 0);
-        ok[j] = page_ok(id, a.num_pages);
-        use[j] = (ok[j] ? id : 0) * hstride + hoff;
-        load_k16<KV_DT>(pr[j], a.kp + use[j], lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t hstride = (int64_t)a.H_kv * PB;  // bytes per page id (all heads)
+  const int64_t hoff = (int64_t)kvh * PB;
+  const int cnt = max(0, min(RUN, p1 - wb));
+  if (cnt > 0) {
+    // Every load of the run, unconditionally: slots past the run re-read its
+    // first page, an out-of-range id reads page 0 and poisons its tile.  All
+    // K chunks are issued before all V chunks, page by page, and kept in that
+    // order, so the logits of page j wait only for K of pages <= j and P.V of
+    // page j only for V of pages <= j.
+    PageRegs<KV_DT> pr[RUN];
+    bool ok[RUN];
+    int64_t use[RUN];
 #pragma unroll
-      for (int j = 0; j < RUN; ++j) {
-        load_v16<KV_DT>(pr[j], a.vp + use[j], lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      zero_missing_heads(qb, c, a.G);
-      // Pass 1: every logit of the run, then one exact max per head for the
-      // whole run, so the output needs no online rescaling.
-      float z[RUN][4];
-      float mx = neg_inf();
+    for (int j = 0; j < RUN; ++j) {
+      const int64_t id = __builtin_amdgcn_readlane(my_id, j < cnt ? j : 0);
+      ok[j] = page_ok(id, a.num_pages);
+      use[j] = (ok[j] ? id : 0) * hstride + hoff;
+      load_k16<KV_DT>(pr[j], page_rsrc(a.kp + use[j], PB), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-      for (int j = 0; j < RUN; ++j) {
-        if (j < cnt) {
-          bf16x8 kb[4];
-          k_operand<KV_DT>(pr[j], kb);
-          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RUN; ++j) {
+      load_v16<KV_DT>(pr[j], page_rsrc(a.vp + use[j], PB), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    zero_missing_heads(qb, c, a.G);
+    // Pass 1: every logit of the run, then one exact max per head.
+    float z[RUN][4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16(kb[x], qb[x], sacc);
+    for (int j = 0; j < RUN; ++j) {
+      if (j < cnt) {
+        bf16x8 kb[4];
+        k_operand<KV_DT>(pr[j], kb);
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
-          const int nv = min(16, n_tok - (wb + j) * 16);
-          if (nv < 16) {  // the row's last page: keys past its length do not count
+        for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16(kb[x], qb[x], sacc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
-            clear_tail_keys<KV_DT>(pr[j], nv, g);
-          }
-          if (!ok[j]) {
+        for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
+        const int nv = min(16, n_tok - (wb + j) * 16);
+        if (nv < 16) {  // the row's last page: keys past its length do not count
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[j][e] = qnan();
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, z[j][e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[j][e] = neg_inf();
+          for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
+          clear_tail_keys<KV_DT>(pr[j], nv, g);
         }
-      }
-      mx = max_over_groups(mx);
-      // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
-      // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
-      float lsum = 0.f;
-      if constexpr (RUN == 1) {
-        float p[4];
+        if (!ok[j]) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(z[0][e] - mx);
-          lsum += p[e];
+          for (int e = 0; e < 4; ++e) z[j][e] = qnan();
         }
-        const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-        bf16x4 vt[8];
-        page16_operands_v<KV_DT>(pr[0], vt);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16_bf16(vt[dt], pb, st.o[dt]);
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, z[j][e]);
       } else {
 #pragma unroll
-        for (int j = 0; j < RUN; j += 2) {
-          if (j < cnt) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 = __builtin_amdgcn_exp2f(z[j][e] - mx);
-              const float p1 = __builtin_amdgcn_exp2f(z[j + 1][e] - mx);
-              lsum += p0 + p1;
-              pb[e] = (__bf16)p0;
-              pb[4 + e] = (__bf16)p1;
-            }
-            if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-              st.o[dt] = mfma_16x16x32_bf16(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, st.o[dt]);
-          }
-        }
+        for (int e = 0; e < 4; ++e) z[j][e] = neg_inf();
       }
-      st.m = mx;
-      st.l = lsum;
     }
-  } else {
-    // MXFP4: the workgroup walks its pages together; V is staged in LDS.
-    zero_missing_heads(qb, c, a.G);
-    for (int p = p0; p < p1; ++p) {
-      const int64_t id = pages[p];
-      const bool ok = page_ok(id, a.num_pages);
-      __syncthreads();  // previous page's LDS reads are done
-      if (ok) {
-        const uint8_t* vsrc = a.vp + (id * a.H_kv + kvh) * kMxPageBytes;
-        for (int x = threadIdx.x; x < kMxPageBytes / 16; x += 256)
-          *reinterpret_cast<u32x4*>(s_v + 16 * x) = ld16_nt(vsrc + 16 * x);
-      }
-      __syncthreads();
-      const uint8_t* kpage = a.kp + ((ok ? id : 0) * a.H_kv + kvh) * kMxPageBytes;
-      for (int tile = wave; tile < 8; tile += kPaWaves) {
-        const int base = p * P + tile * 16;
-        const int nvalid = min(16, n_tok - base);
-        if (nvalid <= 0) break;
-        bf16x8 kb[4];
-        bf16x4 vt[8];
-        if (ok) {
-          const int tok = tile * 16 + c;
-          const u32x4 w = ld16_nt(kpage + tok * 64 + 16 * g);
-          const float sc = e8m0_to_f32(ld4_nt(kpage + kMxDataBytes + 4 * tok) >> (8 * g));
+    mx = max_over_groups(mx);
+    // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
+    // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
+    if constexpr (RUN == 1) {
+      float p[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) kb[j] = e2m1x8_to_bf16x8(w[j], sc);
-          // V^T: dim 16 dt + c, keys tile*16 + 4 g + e, from the LDS copy.
+      for (int e = 0; e < 4; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(z[0][e] - mx);
+        lsum += p[e];
+      }
+      const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+      bf16x4 vt[8];
+      page16_operands_v<KV_DT>(pr[0], vt);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] = mfma_16x16x16_bf16(vt[dt], pb, o[dt]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < RUN; j += 2) {
+        if (j < cnt) {
+          bf16x8 pb;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int vt_tok = tile * 16 + 4 * g + e;
-            const bool on = 4 * g + e < nvalid;
-            const uint32_t sw = *reinterpret_cast<const uint32_t*>(s_v + kMxDataBytes + 4 * vt_tok);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-              const int d = 16 * dt + c;
-              const uint32_t byte = s_v[vt_tok * 64 + (d >> 1)];
-              const uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 0xFu);
-              const float sc_v = e8m0_to_f32(sw >> (8 * (d >> 5)));
-              const bf16x2 pr2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, sc_v, 0);
-              vt[dt][e] = on ? pr2[0] : (__bf16)0.f;
-            }
+            const float p0 = __builtin_amdgcn_exp2f(z[j][e] - mx);
+            const float p1 = __builtin_amdgcn_exp2f(z[j + 1][e] - mx);
+            lsum += p0 + p1;
+            pb[e] = (__bf16)p0;
+            pb[4 + e] = (__bf16)p1;
           }
-        } else {
+          if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
 #pragma unroll
-          for (int j = 0; j < 4; ++j) kb[j] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) vt[dt] = bf16x4{0, 0, 0, 0};
+          for (int dt = 0; dt < 8; ++dt)
+            o[dt] = mfma_16x16x32_bf16(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
         }
-        attend_tile(st, qb, kb, vt, nvalid, !ok, a.qk_scale, g);
       }
     }
   }
+  wave_to_lds<1, 16>(wp, wave, lane, mx, lsum, o);  // row r of tile dt: dim 16 dt + r
+  finish_split(a, wp, row, split, live, out_row);
+}
 
-  // Merge the four waves in LDS.
-  const float l_tot = sum_over_groups(st.l);
-  if (lane < 16) {
-    s_m[wave][c] = st.m;
-    s_l[wave][c] = l_tot;
+// ----------------------------------------------------------------- MXFP4 pages
+// One 128-token page a wave (eight 16-key tiles); grid (rows, splits).
+template <int Q_DT>
+__global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
+  __shared__ WaveParts wp;
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kPaWaves][kMxPageBytes];
+  const int row = blockIdx.x, split = blockIdx.y;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int t = row / a.H_kv, kvh = row % a.H_kv;
+  const int p0 = split * a.pps;
+  const int p = p0 + wave;
+  const int n_tok = a.sctx[row];
+  const int32_t id_raw = p < a.sbt_stride ? a.sbt[(size_t)row * a.sbt_stride + p] : -1;
+  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
+  if (n_tok <= 0) {
+    write_empty_row(a, split, out_row);
+    return;
   }
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[wave][c][16 * dt + 4 * g + e] = st.o[dt][e];
-  __syncthreads();
-  float M = neg_inf();
-#pragma unroll
-  for (int w = 0; w < kPaWaves; ++w) M = fmaxf(M, s_m[w][h]);
-  float L = 0.f, O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int w = 0; w < kPaWaves; ++w) {
-    const float mw = s_m[w][h];
-    const float wt = mw == neg_inf() ? 0.f : exp2f(mw - M);
-    L += s_l[w][h] * wt;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) O[x] += s_o[w][h][d0 + x] * wt;
-  }
+  const int npages = min((n_tok + kBlockTokens - 1) / kBlockTokens, a.sbt_stride);
+  if (p0 >= npages) return;
+  const int live = (npages + a.pps - 1) / a.pps;
 
-  if (live > 1) {
-    // Split-K: publish this split's partial with agent-coherent stores, wait
-    // until they are complete, then count the arrival.  The workgroup that
-    // arrives last merges the row (log-sum-exp weights) and clears the count
-    // for the next call.  Only coherent (agent-scope) accesses touch the
-    // partials and the counter, so no cache writeback or invalidation is
-    // needed between workgroups on different dies.
-    __shared__ int s_last;
-    // A split's 16 x 128 partial outputs are stored thread-interleaved
-    // (element x of thread i at 256 x + i), so each store and load
-    // instruction covers 256 contiguous bytes.
-    const size_t base = (size_t)row * a.splits + split;
-    float* po = a.part_o + base * kPartialO + threadIdx.x;
+  float mx = neg_inf(), lsum = 0.f;
+  f32x4 o[8];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) __hip_atomic_store(po + 256 * x, O[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((threadIdx.x & 15) == 0) {
-      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p < npages) {
+    const int hc = c < a.G ? c : 0;
+    const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * (Q_DT == ISB_BF16 ? 2 : 1);
+    // query first (the load counter is in order): e4m3 bytes as the scaled
+    // MFMA's B operand (dims 16 g .. and 64 + 16 g ..), or bf16 operands
+    i32x8 q8;
+    bf16x8 qb[4];
+    if constexpr (Q_DT == ISB_FP8_E4M3) {
+      const u32x4 lo = ld16(qrow + 16 * g), hi = ld16(qrow + 64 + 16 * g);
+      q8 = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
-    __syncthreads();
-    if (threadIdx.x == 0)
-      s_last = __hip_atomic_fetch_add(a.arrivals + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(live - 1);
-    __syncthreads();
-    if (!s_last) return;
-    if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (h >= a.G) return;
-    // Merge the splits in split order (so the result does not depend on
-    // which workgroup came last): this split's values are in registers, the
-    // others are read back four splits at a time, every load of a group
-    // issued before any use.
-    const float Mo = M, Lo = L;
-    float Oo[8];
+    const int64_t id = __builtin_amdgcn_readfirstlane(id_raw);
+    const bool ok = page_ok(id, a.num_pages);
+    const int64_t pg = ((ok ? id : 0) * a.H_kv + kvh) * kMxPageBytes;
+    const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kp + pg, kMxPageBytes);
+    const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vp + pg, kMxPageBytes);
+    u32x4 kd[8];
+    uint32_t ks[8];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) Oo[x] = O[x];
-    M = neg_inf();
-    L = 0.f;
+    for (int tt = 0; tt < 8; ++tt) {
+      kd[tt] = bl16_nt(rk, 64 * c + 16 * g, 1024 * tt);
+      ks[tt] = bl4_nt(rk, 4 * c, kMxDataBytes + 64 * tt);
+    }
+    u32x4 vd[9];  // the V page: 8 KiB of data, then 512 B of scales (upper lanes read past it: zero)
 #pragma unroll
-    for (int x = 0; x < 8; ++x) O[x] = 0.f;
-    const size_t b0 = (size_t)row * a.splits * 16 + h;
-    for (int s0 = 0; s0 < live; s0 += 4) {
-      float ms[4], ls[4], os[4][8];
+    for (int i = 0; i < 9; ++i) vd[i] = bl16_nt(rv, 16 * lane, 1024 * i);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (Q_DT == ISB_FP8_E4M3) {
+      if (c >= a.G) q8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    } else {
+      zero_missing_heads(qb, c, a.G);
+    }
+    const int nvp = min(kBlockTokens, n_tok - p * kBlockTokens);  // keys of the page that count
+    // Pass 1: the page's logits and one exact max per head.
+    float z[8][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int sp = s0 + k < live ? s0 + k : split;
-        const size_t b = b0 + (size_t)sp * 16;
-        ms[k] = __hip_atomic_load(a.part_ml + b * 2 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ls[k] = __hip_atomic_load(a.part_ml + b * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float* pk = a.part_o + ((size_t)row * a.splits + sp) * kPartialO + threadIdx.x;
+    for (int tt = 0; tt < 8; ++tt) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      const uint32_t sbyte = (ks[tt] >> (8 * g)) & 0xFFu;
+      if constexpr (Q_DT == ISB_FP8_E4M3) {
+        const i32x8 ka = {(int)kd[tt][0], (int)kd[tt][1], (int)kd[tt][2], (int)kd[tt][3], 0, 0, 0, 0};
+        s = mfma_scale_fp4_e4m3(ka, q8, s, (int)sbyte);
+      } else {
+        const float sc = e8m0_to_f32(sbyte);
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          os[k][x] = __hip_atomic_load(pk + 256 * x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int j = 0; j < 4; ++j) s = mfma_16x16x32_bf16(e2m1x8_to_bf16x8(kd[tt][j], sc), qb[j], s);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int sp = s0 + k;
-        if (sp >= live) break;
-        const bool own = sp == split;
-        const float mk = own ? Mo : ms[k];
-        if (mk == neg_inf()) continue;
-        const float Mn = fmaxf(M, mk);
-        const float wa = M == neg_inf() ? 0.f : exp2f(M - Mn);
-        const float wb = exp2f(mk - Mn);
-        L = L * wa + (own ? Lo : ls[k]) * wb;
+      for (int e = 0; e < 4; ++e) {
+        const float v = ok ? s[e] * a.qk_scale : qnan();
+        z[tt][e] = 16 * tt + 4 * g + e < nvp ? v : neg_inf();
+        mx = fmaxf(mx, z[tt][e]);
+      }
+    }
+    mx = max_over_groups(mx);
+    // The V page into this wave's LDS buffer (read back only by this wave,
+    // whose LDS operations complete in order).
+    uint8_t* sv = s_v[wave];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : os[k][x]) * wb;
-        M = Mn;
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sv + 1024 * i + 16 * lane) = vd[i];
+    if (lane < 32) *reinterpret_cast<u32x4*>(sv + kMxDataBytes + 16 * lane) = vd[8];
+    // Pass 2: probabilities and P.V.  Lane (g, c) takes keys 4 g + e of the
+    // tile and dims 8 c .. 8 c + 7 (one data word, one scale byte per key);
+    // MFMA dt gets dim 8 c + dt.
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pr[e] = __builtin_amdgcn_exp2f(z[tt][e] - mx);
+        lsum += pr[e];
+      }
+      const bf16x4 pb = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
+      bf16x8 vv[4];  // key e: dims 8 c .. 8 c + 7
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = 16 * tt + 4 * g + e;
+        const bool on = tok < nvp;  // keys past the length may be poison: zero, unit scale
+        const uint32_t w = on ? *reinterpret_cast<const uint32_t*>(sv + 64 * tok + 4 * c) : 0u;
+        const float sc = on ? e8m0_to_f32(sv[kMxDataBytes + 4 * tok + (c >> 2)]) : 1.f;
+        vv[e] = e2m1x8_to_bf16x8(w, sc);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x4 vt = {vv[0][dt], vv[1][dt], vv[2][dt], vv[3][dt]};
+        o[dt] = mfma_16x16x16_bf16(vt, pb, o[dt]);
       }
     }
   }
-  // Finished row: normalise and write bf16.
-  if (h < a.G) {
-    const float inv = a.v_scale / L;
-    bf16x8 ob;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(O[x] * inv);
-    *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = ob;
-  }
+  wave_to_lds<8, 1>(wp, wave, lane, mx, lsum, o);  // row r of tile dt: dim 8 r + dt
+  finish_split(a, wp, row, split, live, out_row);
 }
 
 template <int KV_DT, int Q_DT>
 static void launch_decode(const PaArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (KV_DT == ISB_MXFP4) {
-    hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 1>), grid, dim3(256), 0, st, a);
-  } else {
-    switch (a.ppw) {
-      case 1: hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 1>), grid, dim3(256), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 2>), grid, dim3(256), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 4>), grid, dim3(256), 0, st, a); break;
-      default:
-        if constexpr (KV_DT == ISB_FP8_E4M3)
-          hipLaunchKernelGGL((pa_decode_kernel<KV_DT, Q_DT, 8>), grid, dim3(256), 0, st, a);
-        break;
-    }
-  }
+  if constexpr (KV_DT == ISB_MXFP4)
+    hipLaunchKernelGGL((pamx_kernel<Q_DT>), grid, dim3(256), 0, st, a);
+  else if constexpr (KV_DT == ISB_BF16)
+    hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, 4>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, 8>), grid, dim3(256), 0, st, a);
 }
 
 }  // namespace isb
@@ -619,7 +641,6 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   a.G = num_q_heads / num_kv_heads;
   a.splits = plan.splits;
   a.pps = plan.pages_per_split;
-  a.ppw = plan.pages_per_wave;
   hipStream_t st = as_hip(stream);
   const dim3 grid((unsigned)rows, plan.splits);
   const bool qb = q_dtype == ISB_BF16;
