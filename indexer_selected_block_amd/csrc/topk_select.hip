@@ -16,10 +16,9 @@
 // selected indices are compacted in index order, which gives the ascending
 // output without a sort.
 //
-// Rows of up to 8192 blocks are read from HBM once, into LDS, together with
-// the row's length (and, for the fused emit, its block-table row), so every
-// pass after that is an LDS pass.  Wider rows use the same algorithm over
-// global memory.
+// Rows of up to 8192 blocks are read from HBM once, into registers, together
+// with the row's length (and, for the fused emit, its block-table row, into
+// LDS).  Wider rows use the same algorithm over global memory.
 #include "isb_device.h"
 #include "isb_host.h"
 
@@ -133,28 +132,41 @@ __device__ __forceinline__ void radix_select(int W, int need, KeyFn key, PutFn p
   }
 }
 
-// LDS-resident rows (MB <= 8192).  Dynamic LDS: keys[MB], then (BT_LDS) the
-// block-table row [MB], then (EMIT) the selection [K].
-template <int NT, bool EMIT, bool BT_LDS>
-__global__ __launch_bounds__(NT) void topk_lds_kernel(TopkArgs a) {
-  extern __shared__ uint32_t s_dyn[];
-  __shared__ int s_hist[256];
-  __shared__ int s_wave[NT / 64];
+// Rows of up to 8192 blocks: NT threads, E keys each in registers (thread t
+// owns blocks E t .. E t + E - 1, so the compaction is in block order).  Each
+// radix pass: every wave builds its own 256-bin histogram (no contention
+// between waves), wave 0 sums the waves' bins and finds the digit, two
+// barriers a pass.  Dynamic LDS: (BT_LDS) the block-table row [MB], then
+// (EMIT) the selection [K].
+template <int NT, int E, bool EMIT, bool BT_LDS>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
+  constexpr int NW = NT / 64;
+  extern __shared__ int32_t s_dyn[];
+  __shared__ int s_hist[NW][256];
+  __shared__ int s_wave[NW];
   __shared__ int s_pick[2];
-  uint32_t* s_key = s_dyn;
-  int32_t* s_bt = reinterpret_cast<int32_t*>(s_dyn + a.MB);
-  int32_t* s_sel = reinterpret_cast<int32_t*>(s_dyn + a.MB * (BT_LDS ? 2 : 1));
-  const int tid = threadIdx.x;
+  int32_t* s_bt = s_dyn;
+  int32_t* s_sel = s_dyn + (BT_LDS ? a.MB : 0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int row = blockIdx.x;
   // Every global load first: length, scores and (fused, narrow rows) the
   // block-table row, so the workgroup waits for one round trip.
   const int Lr = a.seq_lens[(row % a.T) / a.q_len];
   const float* s = a.scores + (size_t)row * a.MB;
-  for (int j = tid; j < a.MB; j += NT) s_key[j] = order_key(s[j]);
   const RowGeom q = row_geom(a, row, Lr);
-  if constexpr (BT_LDS)
-    for (int j = tid; j < a.MB; j += NT) s_bt[j] = a.bt[(size_t)q.r * a.bt_stride + j];
-  __syncthreads();
+  float sc[E];
+  int32_t btv[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int j = E * tid + i;
+    sc[i] = j < a.MB ? s[j] : 0.f;
+    if constexpr (BT_LDS) btv[i] = j < a.MB ? a.bt[(size_t)q.r * a.bt_stride + j] : 0;
+  }
+  if constexpr (BT_LDS) {
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (E * tid + i < a.MB) s_bt[E * tid + i] = btv[i];
+  }
   int32_t* o = a.topk + (size_t)row * a.K;
   const int W = q.nt - 1;  // candidates [0, W); block W is the tail
   int m;                   // blocks selected
@@ -166,13 +178,84 @@ __global__ __launch_bounds__(NT) void topk_lds_kernel(TopkArgs a) {
     }
     m = q.nt;
   } else {
-    radix_select<NT>(
-        W, a.K - 1, [&](int j) { return s_key[j]; },
-        [&](int pos, int j) {
-          o[pos] = j;
-          if constexpr (EMIT) s_sel[pos] = j;
-        },
-        s_hist, s_wave, s_pick);
+    uint32_t key[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) key[i] = E * tid + i < W ? order_key(sc[i]) : 0u;
+    const int jlim = W - E * tid;  // my keys i < jlim are candidates
+    const int keep = a.K - 1;      // candidates to select (0 when top_k = 1)
+    int need = keep;
+    uint32_t prefix = 0u, pmask = 0u;
+    // With need >= 1 every pass finds its digit (need never exceeds the keys
+    // that match the prefix); with top_k = 1 only the tail is selected.
+    for (int shift = 24; shift >= 0 && keep > 0; shift -= 8) {
+      // this wave's histogram: cleared, then filled (LDS operations of a wave
+      // complete in order; wave 0 finished reading the previous pass's bins
+      // before the barrier that ended it)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) s_hist[wave][lane + 64 * x] = 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&s_hist[wave][(key[i] >> shift) & 0xFF], 1);
+      __syncthreads();
+      if (wave == 0) {
+        // lane l takes digits 255 - 4 l - x (x < 4): descending digit order
+        int cnt[4], tot = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          int c = 0;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) c += s_hist[w][255 - 4 * lane - x];
+          cnt[x] = c;
+          tot += c;
+        }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        int run = incl - tot;  // keys in higher digits
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (run < need && need <= run + cnt[x]) {
+            s_pick[0] = 255 - 4 * lane - x;
+            s_pick[1] = run;
+          }
+          run += cnt[x];
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_pick[0] << shift;
+      pmask |= 0xFFu << shift;
+      need -= s_pick[1];
+    }
+    // prefix is the exact threshold key; keys above it are taken, and `need`
+    // keys equal to it, the lowest block indices first.  One scan of packed
+    // (greater, equal) counts gives each thread its output position.
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if (i < jlim) {
+        gt += key[i] > prefix;
+        eq += key[i] == prefix;
+      }
+    }
+    const int packed = gt | (eq << 16);
+    const int before = block_incl_scan<NT>(packed, s_wave) - packed;
+    int seen = before >> 16;
+    int pos = (before & 0xFFFF) + min(seen, need);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if (i < jlim && keep > 0) {
+        bool sel = key[i] > prefix;
+        if (key[i] == prefix) sel = seen++ < need;
+        if (sel && pos < keep) {
+          o[pos] = E * tid + i;
+          if constexpr (EMIT) s_sel[pos] = E * tid + i;
+          ++pos;
+        }
+      }
+    }
     if (tid == 0) {
       o[a.K - 1] = W;  // the tail block, larger than every candidate
       if constexpr (EMIT) s_sel[a.K - 1] = W;
@@ -218,19 +301,28 @@ __global__ __launch_bounds__(256) void topk_global_kernel(TopkArgs a) {
   if (threadIdx.x == 0) o[a.K - 1] = W;
 }
 
-// Dynamic LDS of topk_lds_kernel, or 0 when the row does not fit.
+// Dynamic LDS of topk_reg_kernel, or 0 when the row does not fit.
 inline size_t topk_lds_bytes(int MB, int K, bool emit, bool bt_lds) {
   if (MB > 8192) return 0;
-  const size_t b = 4 * ((size_t)MB * (bt_lds ? 2 : 1) + (emit ? (size_t)K : 0));
-  return b <= 48 * 1024 ? b : 0;
+  const size_t b = 4 * ((bt_lds ? (size_t)MB : 0) + (emit ? (size_t)K : 0));
+  return b <= 40 * 1024 ? (b ? b : 4) : 0;
 }
 
 template <bool EMIT, bool BT_LDS>
-static void launch_lds(const TopkArgs& a, unsigned rows, size_t lds, hipStream_t st) {
-  if (a.MB <= 2048)
-    hipLaunchKernelGGL((topk_lds_kernel<256, EMIT, BT_LDS>), dim3(rows), dim3(256), lds, st, a);
+static void launch_reg(const TopkArgs& a, unsigned rows, size_t lds, hipStream_t st) {
+  const dim3 g(rows);
+  if (a.MB <= 256)
+    hipLaunchKernelGGL((topk_reg_kernel<256, 1, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+  else if (a.MB <= 512)
+    hipLaunchKernelGGL((topk_reg_kernel<256, 2, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+  else if (a.MB <= 1024)
+    hipLaunchKernelGGL((topk_reg_kernel<256, 4, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+  else if (a.MB <= 2048)
+    hipLaunchKernelGGL((topk_reg_kernel<256, 8, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+  else if (a.MB <= 4096)
+    hipLaunchKernelGGL((topk_reg_kernel<1024, 4, EMIT, BT_LDS>), g, dim3(1024), lds, st, a);
   else
-    hipLaunchKernelGGL((topk_lds_kernel<1024, EMIT, BT_LDS>), dim3(rows), dim3(1024), lds, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<1024, 8, EMIT, BT_LDS>), g, dim3(1024), lds, st, a);
 }
 
 // Shared argument checks of the two entry points; 0 or an ISB_E_* code.
@@ -260,7 +352,7 @@ extern "C" int isb_topk_select(isb_stream_t stream, const float* scores, const i
   hipStream_t st = as_hip(stream);
   const size_t lds = topk_lds_bytes(max_blocks, top_k, false, false);
   if (lds)
-    launch_lds<false, false>(a, rows, lds, st);
+    launch_reg<false, false>(a, rows, lds, st);
   else
     hipLaunchKernelGGL(topk_global_kernel, dim3(rows), dim3(256), 0, st, a);
   return launch_status();
@@ -289,9 +381,9 @@ extern "C" int isb_topk_select_emit(isb_stream_t stream, const float* scores,
   hipStream_t st = as_hip(stream);
   size_t lds = topk_lds_bytes(max_blocks, top_k, true, true);
   if (lds) {
-    launch_lds<true, true>(a, rows, lds, st);
+    launch_reg<true, true>(a, rows, lds, st);
   } else if ((lds = topk_lds_bytes(max_blocks, top_k, true, false)) != 0) {
-    launch_lds<true, false>(a, rows, lds, st);
+    launch_reg<true, false>(a, rows, lds, st);
   } else {
     hipLaunchKernelGGL(topk_global_kernel, dim3(rows), dim3(256), 0, st, a);
     const int e = launch_status();
