@@ -215,6 +215,42 @@ def test_sparse_pa_parity(name):
     assert (got[empty] == 0).all()
 
 
+# Query / cache dtype pairs and head groupings the five workloads do not use,
+# and rows with more splits than the merging workgroup loads at once.
+_PA_VARIANTS = {
+    "mxfp4_kv_bf16_q": ("mxfp4", dict(q_dtype="bf16")),
+    "bf16_kv_e4m3_q": ("tiny_bf16", dict(q_dtype="e4m3")),
+    "fp8_kv_e4m3_q": ("fp8_decode", dict(q_dtype="e4m3")),
+    "fp8_two_kv_heads": ("fp8_decode", dict(num_kv_heads=2, num_q_heads=16)),
+    "mxfp4_two_kv_heads": ("mxfp4", dict(num_kv_heads=2, num_q_heads=16)),
+    "fp8_group_of_4": ("fp8_decode", dict(num_q_heads=4)),
+    "fp8_18_splits": ("fp8_decode", dict(top_k=72)),
+    "mxfp4_10_splits": ("mxfp4", dict(top_k=40)),
+}
+
+
+@pytest.mark.parametrize("variant", list(_PA_VARIANTS))
+def test_sparse_pa_variants(variant):
+    base, kw = _PA_VARIANTS[variant]
+    cfg = dataclasses.replace(SMALL[base], **kw)
+    if "splits" in variant:
+        cfg = dataclasses.replace(wl.shrink(SMALL[base], num_reqs=3, ctx_lo=9000, ctx_hi=12000), **kw)
+    _say(f"[sparse_pa variant] {variant}: {cfg}")
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    sbt, sctx = _synthetic_table(hi, 11)
+    ref = oracle_attention(hi, sbt, sctx)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all(), "NaN in attention output (poison read?)"
+    tol = attn_tol(cfg.kv_dtype, attended_vmax(hi, sbt, sctx))
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"max |err| {err:.4g} > {tol:.4g}"
+
+
 def test_sparse_pa_every_block_is_dense_attention():
     # top-k >= every row's block count: the sparse decode is dense causal attention.
     cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=4, ctx_lo=100, ctx_hi=2000, top_k=16)
