@@ -25,16 +25,23 @@ inline int64_t idx_page_bytes(int dt) {
 }
 
 // Split-K plan of isb_sparse_pa_decode; shared by the workspace query so the
-// two always agree.  A split is one workgroup of four waves; a wave attends a
-// run of `pages_per_wave` consecutive pages whose loads it issues at once:
-// 8 fp8 / 4 bf16 16-token pages (32 KiB of K and V), or one 128-token MXFP4
-// page.  Decode launches are latency-bound, so a wave takes the largest run
-// its registers hold: fewer, fuller waves and fewer partials to merge.
+// two always agree.  A wave attends a run of `pages_per_wave` consecutive
+// pages whose loads it issues at once: 8 fp8 / 4 bf16 16-token pages (32 KiB
+// of K and V), or one 128-token MXFP4 page; a workgroup (four waves) covers
+// four runs a round.  Rows are cut into just enough splits to give the chip
+// about kPaResidentWorkgroups workgroups (two per CU of an MI355X); a split
+// longer than one round is walked round by round.  Batches that fill the chip
+// by themselves thus take one split per row, with nothing to merge between
+// workgroups, and small batches spread a row over several workgroups that
+// each read everything they attend in one round.
+constexpr int kPaResidentWorkgroups = 512;
+
 struct PaPlan {
   int rows;             // num_tokens * num_kv_heads
   int max_pages;        // sparse_bt_stride
   int pages_per_wave;   // run of one wave
-  int pages_per_split;  // pages one workgroup attends
+  int pages_per_round;  // 4 runs: what a workgroup reads at once
+  int pages_per_split;  // a whole number of rounds
   int splits;           // workgroups per row
 };
 
@@ -43,7 +50,14 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   p.rows = num_tokens * num_kv_heads;
   p.max_pages = sparse_bt_stride;
   p.pages_per_wave = kv_dtype == ISB_MXFP4 ? 1 : kv_dtype == ISB_BF16 ? 4 : 8;
-  p.pages_per_split = 4 * p.pages_per_wave;
+  p.pages_per_round = 4 * p.pages_per_wave;
+  const int rounds = (p.max_pages + p.pages_per_round - 1) / p.pages_per_round;  // of a whole row
+  int want = (kPaResidentWorkgroups + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
+  if (kv_dtype == ISB_MXFP4) want = rounds;  // MXFP4 rows are short: one round a split
+  if (want > rounds) want = rounds;
+  if (want < 1) want = 1;
+  const int rounds_per_split = (rounds + want - 1) / want;
+  p.pages_per_split = rounds_per_split * p.pages_per_round;
   p.splits = (p.max_pages + p.pages_per_split - 1) / p.pages_per_split;
   if (p.splits < 1) p.splits = 1;
   return p;

@@ -8,12 +8,16 @@
 // ROCm/ATOM PR 2962 (Summary: MXFP4 K and V pages, one row per token and KV
 // head).
 //
-// Work decomposition.  A row's pages are cut into splits of four waves' runs;
-// one workgroup attends one split.  A wave issues every load of its run (up
-// to 8 fp8 / 4 bf16 16-token pages, or one 128-token MXFP4 page) before any
-// math, computes every logit of the run, takes one exact maximum per head,
-// then the probabilities and P.V, so its output needs no online rescaling.
-// The four waves merge in LDS, the splits of a row through the workspace.
+// Work decomposition.  A row's pages are cut into splits; one workgroup of
+// four waves attends one split, a round (four runs, one a wave) at a time.  A
+// wave issues every load of its run (8 fp8 / 4 bf16 16-token pages, or one
+// 128-token MXFP4 page) before any math, computes every logit of the run,
+// takes one exact maximum per head, rescales what earlier rounds accumulated
+// if that maximum grew, then adds the probabilities' P.V.  The four waves
+// merge in LDS, the splits of a row through the workspace.  Small batches
+// take several splits a row (every page of the batch in flight in one round);
+// batches that fill the chip take one split a row and nothing is merged
+// between workgroups.
 //   S^T (16 keys x 16 heads) = K_tile . Q^T      v_mfma_f32_16x16x32_bf16, or
 //                                                one scaled fp4 x fp8 MFMA
 //   O^T (128 dims x 16 heads) += V^T . P^T       v_mfma_f32_16x16x{32,16}_bf16
@@ -318,11 +322,15 @@ __device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const
 }
 
 // RUN: pages of one wave's run (a power of two).  grid (rows, splits), four
-// waves a workgroup.
+// waves a workgroup.  A split is walked one round (four runs, one per wave)
+// at a time; each round's loads are issued together and its logits give one
+// exact max per head, folded into the wave's running max between rounds.
 template <int KV_DT, int Q_DT, int RUN>
 __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
+  constexpr int ROUND = 4 * RUN;    // pages of a round
+  constexpr int IDS = 64 / RUN;     // rounds whose page ids one load of the wave holds
   __shared__ WaveParts wp;
   const int row = blockIdx.x, split = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -330,11 +338,16 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
   const int p0 = split * a.pps;
-  // Issued together before anything waits: this wave's page ids, the row
-  // length and the query, so the K/V gathers start after one round trip.
-  const int wb = p0 + wave * RUN;
-  int my_id = -1;
-  if (lane < RUN && wb + lane < a.sbt_stride) my_id = pages[wb + lane];
+  const int pend = min(a.sbt_stride, p0 + a.pps);
+  // Lane L holds the page id of slot L % RUN of this wave's run in round
+  // r0 + L / RUN (-1 past the split).
+  auto load_ids = [&](int r0) {
+    const int pidx = p0 + (r0 + lane / RUN) * ROUND + wave * RUN + lane % RUN;
+    return pidx < pend ? pages[pidx] : -1;
+  };
+  // Issued together before anything waits: the first rounds' page ids, the
+  // row length and the query, so the K/V gathers start after one round trip.
+  int my_ids = load_ids(0);
   const int n_tok = a.sctx[row];
   // Q^T operand: head kvh * G + c, dims 32 g .. 32 g + 31 (zero past G).
   bf16x8 qb[4];
@@ -354,15 +367,21 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   if (p0 >= npages) return;
   const int p1 = min(npages, p0 + a.pps);
   const int live = (npages + a.pps - 1) / a.pps;  // splits of this row that have pages
+  const int nrounds = (p1 - p0 + ROUND - 1) / ROUND;
+  zero_missing_heads(qb, c, a.G);
 
-  float mx = neg_inf(), lsum = 0.f;
+  float M = neg_inf(), lsum = 0.f;  // running max (per head) and this lane's share of the sum
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t hstride = (int64_t)a.H_kv * PB;  // bytes per page id (all heads)
   const int64_t hoff = (int64_t)kvh * PB;
-  const int cnt = max(0, min(RUN, p1 - wb));
-  if (cnt > 0) {
+  for (int r = 0; r < nrounds; ++r) {
+    if (r > 0 && r % IDS == 0) my_ids = load_ids(r);
+    const int wb = p0 + r * ROUND + wave * RUN;
+    const int cnt = max(0, min(RUN, p1 - wb));
+    if (cnt == 0) continue;  // wave-uniform: this wave has nothing left in the split
+    const int ibase = (r % IDS) * RUN;
     // Every load of the run, unconditionally: slots past the run re-read its
     // first page, an out-of-range id reads page 0 and poisons its tile.  All
     // K chunks are issued before all V chunks, page by page, and kept in that
@@ -373,7 +392,7 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
     int64_t use[RUN];
 #pragma unroll
     for (int j = 0; j < RUN; ++j) {
-      const int64_t id = __builtin_amdgcn_readlane(my_id, j < cnt ? j : 0);
+      const int64_t id = __builtin_amdgcn_readlane(my_ids, ibase + (j < cnt ? j : 0));
       ok[j] = page_ok(id, a.num_pages);
       use[j] = (ok[j] ? id : 0) * hstride + hoff;
       load_k16<KV_DT>(pr[j], page_rsrc(a.kp + use[j], PB), lane);
@@ -384,9 +403,9 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
       load_v16<KV_DT>(pr[j], page_rsrc(a.vp + use[j], PB), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    zero_missing_heads(qb, c, a.G);
     // Pass 1: every logit of the run, then one exact max per head.
     float z[RUN][4];
+    float mx = neg_inf();
 #pragma unroll
     for (int j = 0; j < RUN; ++j) {
       if (j < cnt) {
@@ -415,13 +434,23 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
       }
     }
     mx = max_over_groups(mx);
+    // Fold the round's max into the running one (rescaling what earlier
+    // rounds accumulated).
+    const float m_new = fmaxf(M, mx);
+    if (r > 0) {
+      const float alpha = M == m_new ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+    M = m_new;
     // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
     // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
     if constexpr (RUN == 1) {
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(z[0][e] - mx);
+        p[e] = __builtin_amdgcn_exp2f(z[0][e] - M);
         lsum += p[e];
       }
       const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
@@ -436,11 +465,11 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
           bf16x8 pb;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(z[j][e] - mx);
-            const float p1 = __builtin_amdgcn_exp2f(z[j + 1][e] - mx);
-            lsum += p0 + p1;
-            pb[e] = (__bf16)p0;
-            pb[4 + e] = (__bf16)p1;
+            const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
+            const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
+            lsum += p0v + p1v;
+            pb[e] = (__bf16)p0v;
+            pb[4 + e] = (__bf16)p1v;
           }
           if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
 #pragma unroll
@@ -450,7 +479,7 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
       }
     }
   }
-  wave_to_lds<1, 16>(wp, wave, lane, mx, lsum, o);  // row r of tile dt: dim 16 dt + r
+  wave_to_lds<1, 16>(wp, wave, lane, M, lsum, o);  // row r of tile dt: dim 16 dt + r
   finish_split(a, wp, row, split, live, out_row);
 }
 

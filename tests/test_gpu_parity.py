@@ -229,6 +229,31 @@ _PA_VARIANTS = {
 }
 
 
+@pytest.mark.parametrize("base", ["spec_decode", "tiny_bf16"])
+def test_sparse_pa_one_split_several_rounds(base):
+    # Enough rows to fill the chip: one split a row, walked in several rounds
+    # with the running max carried between them (fp8 runs of 8 pages, bf16 of 4).
+    reqs = 150 if base == "spec_decode" else 520   # >= 512 rows either way
+    cfg = wl.shrink(wl.CONFIGS[base], num_reqs=reqs, ctx_lo=1500, ctx_hi=3000, num_pad_reqs=3,
+                    pool_blocks=reqs * 24 + 64, top_k=12)
+    _say(f"[sparse_pa rounds] {base}: {cfg.num_tokens} rows")
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    sbt, sctx = _synthetic_table(hi, 21)
+    rows = cfg.num_tokens * cfg.num_kv_heads
+    assert rows >= 512 and sbt.shape[1] > 4 * (8 if cfg.kv_dtype == "fp8" else 4)
+    ref = oracle_attention(hi, sbt, sctx)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    tol = attn_tol(cfg.kv_dtype, attended_vmax(hi, sbt, sctx))
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"max |err| {err:.4g} > {tol:.4g}"
+
+
 @pytest.mark.parametrize("variant", list(_PA_VARIANTS))
 def test_sparse_pa_variants(variant):
     base, kw = _PA_VARIANTS[variant]
