@@ -40,19 +40,6 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 __device__ __forceinline__ u32x2 ld8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
-__device__ __forceinline__ uint32_t ld4(const void* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
-}
-// Nontemporal 16-byte load (global_load_dwordx4 ... nt), for cache pages that
-// a launch reads once: streaming them past the caches instead of keeping
-// them raises the achieved HBM rate by about a tenth on the index scan.
-__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ uint32_t ld4_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
-
 // Raw buffer loads from one cache page.  The page's base address sits in a
 // wave-uniform buffer descriptor (scalar registers), so a wave's loads share
 // one per-lane offset register and add the rest as scalar and immediate
@@ -62,7 +49,9 @@ __device__ __forceinline__ uint32_t ld4_nt(const void* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-// 16 / 4 bytes at voff + soff, nontemporal (cache policy nt: read once).
+// 16 / 4 bytes at voff + soff, nontemporal (cache policy nt): cache pages
+// are read once per launch, and streaming them past the caches raises the
+// achieved HBM rate of the index scan by about a tenth.
 __device__ __forceinline__ u32x4 bl16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
 }
@@ -115,8 +104,6 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   if (e == 0u) return __uint_as_float(0x00400000u);
   return __uint_as_float(e << 23);
 }
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 __device__ __forceinline__ bf16x2 u32_as_bf16x2(uint32_t w) {
   return __builtin_bit_cast(bf16x2, w);
