@@ -2,8 +2,9 @@
  * isb.h - C ABI of libisb: one layer of indexed block-sparse paged-attention
  * decode on an AMD Instinct MI355X (gfx950).
  *
- * The layer runs as four calls on one HIP stream, each taking plain device
- * pointers and sizes:
+ * The layer's steps are separate calls on one HIP stream, each taking plain
+ * device pointers and sizes (a layer step can run as three launches:
+ * isb_index_score, isb_topk_select_emit, isb_sparse_pa_decode):
  *
  *   isb_index_score              score every 128-token block of each request's
  *                                paged index-key cache with the index query;
@@ -28,7 +29,8 @@
  *    allocates, frees or synchronises; it only enqueues kernels on `stream`
  *    (NULL = the default stream).  Calls may therefore be captured into a HIP
  *    graph.  Inputs are read-only; outputs are fully written by every call, so
- *    their prior contents never matter.
+ *    their prior contents never matter.  (The attention workspace is the one
+ *    buffer with a contract on its contents: see isb_sparse_pa_decode.)
  *  - R requests, q = decode_query_len, T = R q query tokens.  Token t = r q + i
  *    of request r has causal length L_t = max(0, seq_lens[r] - (q - 1 - i)) and
  *    n_t = ceil(L_t / 128) valid blocks.  Rows with n_t = 0 (pad requests of
@@ -121,7 +123,9 @@ ISB_API const char* isb_strerror(int status);
  *                request's ceil(seq_len/128) blocks are never read
  *   seq_lens     [num_reqs] int32, each <= 128 * min(max_blocks, stride)
  *   scores       out, [num_kv_heads][T][max_blocks] fp32
- * Shape errors: num_idx_heads % num_kv_heads != 0, max_blocks > stride.
+ * Shape errors: num_idx_heads % num_kv_heads != 0, max_blocks > stride,
+ * decode_query_len > 16, decode_query_len * num_idx_heads > 64,
+ * num_reqs > 65535.
  */
 ISB_API int isb_index_score(isb_stream_t stream,
                     const void* q_idx, int q_idx_dtype, int num_idx_heads,
