@@ -138,7 +138,43 @@ __device__ __forceinline__ void radix_select(int W, int need, KeyFn key, PutFn p
 // between waves), wave 0 sums the waves' bins and finds the digit, two
 // barriers a pass.  Dynamic LDS: (BT_LDS) the block-table row [MB], then
 // (EMIT) the selection [K].
-template <int NT, int E, bool EMIT, bool BT_LDS>
+// VEC: rows start 16-byte aligned and hold a multiple of 4 entries (score
+// rows and, with BT_LDS, block-table rows), so a thread's E consecutive
+// entries arrive in 16-byte (or, for E = 2, 8-byte) loads; per-entry 4-byte
+// loads at a stride of E entries would touch E times as many cache lines.
+template <int E, bool VEC, typename T>
+__device__ __forceinline__ void load_run(const T* row, int j0, int n, T (&v)[E]) {
+  if constexpr (VEC && E >= 4) {
+#pragma unroll
+    for (int x = 0; x < E / 4; ++x) {
+      if (j0 + 4 * x < n) {
+        const u32x4 w = ld16(row + j0 + 4 * x);
+        // each element copied to a scalar first: a bit cast taken straight
+        // from a vector element reads element 0 here
+        const uint32_t e[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int y = 0; y < 4; ++y) v[4 * x + y] = __builtin_bit_cast(T, e[y]);
+      } else {
+#pragma unroll
+        for (int y = 0; y < 4; ++y) v[4 * x + y] = T(0);
+      }
+    }
+  } else if constexpr (VEC && E == 2) {
+    if (j0 < n) {
+      const u32x2 w = ld8(row + j0);
+      const uint32_t e0 = w[0], e1 = w[1];
+      v[0] = __builtin_bit_cast(T, e0);
+      v[1] = __builtin_bit_cast(T, e1);
+    } else {
+      v[0] = v[1] = T(0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = j0 + i < n ? row[j0 + i] : T(0);
+  }
+}
+
+template <int NT, int E, bool EMIT, bool BT_LDS, bool VEC>
 __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
   constexpr int NW = NT / 64;
   extern __shared__ int32_t s_dyn[];
@@ -156,12 +192,8 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
   const RowGeom q = row_geom(a, row, Lr);
   float sc[E];
   int32_t btv[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int j = E * tid + i;
-    sc[i] = j < a.MB ? s[j] : 0.f;
-    if constexpr (BT_LDS) btv[i] = j < a.MB ? a.bt[(size_t)q.r * a.bt_stride + j] : 0;
-  }
+  load_run<E, VEC>(s, E * tid, a.MB, sc);
+  if constexpr (BT_LDS) load_run<E, VEC>(a.bt + (size_t)q.r * a.bt_stride, E * tid, a.MB, btv);
   if constexpr (BT_LDS) {
 #pragma unroll
     for (int i = 0; i < E; ++i)
@@ -308,21 +340,31 @@ inline size_t topk_lds_bytes(int MB, int K, bool emit, bool bt_lds) {
   return b <= 40 * 1024 ? (b ? b : 4) : 0;
 }
 
-template <bool EMIT, bool BT_LDS>
-static void launch_reg(const TopkArgs& a, unsigned rows, size_t lds, hipStream_t st) {
+template <bool EMIT, bool BT_LDS, bool VEC>
+static void launch_reg_v(const TopkArgs& a, unsigned rows, size_t lds, hipStream_t st) {
   const dim3 g(rows);
   if (a.MB <= 256)
-    hipLaunchKernelGGL((topk_reg_kernel<256, 1, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<256, 1, EMIT, BT_LDS, VEC>), g, dim3(256), lds, st, a);
   else if (a.MB <= 512)
-    hipLaunchKernelGGL((topk_reg_kernel<256, 2, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<256, 2, EMIT, BT_LDS, VEC>), g, dim3(256), lds, st, a);
   else if (a.MB <= 1024)
-    hipLaunchKernelGGL((topk_reg_kernel<256, 4, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<256, 4, EMIT, BT_LDS, VEC>), g, dim3(256), lds, st, a);
   else if (a.MB <= 2048)
-    hipLaunchKernelGGL((topk_reg_kernel<256, 8, EMIT, BT_LDS>), g, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<256, 8, EMIT, BT_LDS, VEC>), g, dim3(256), lds, st, a);
   else if (a.MB <= 4096)
-    hipLaunchKernelGGL((topk_reg_kernel<1024, 4, EMIT, BT_LDS>), g, dim3(1024), lds, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<1024, 4, EMIT, BT_LDS, VEC>), g, dim3(1024), lds, st, a);
   else
-    hipLaunchKernelGGL((topk_reg_kernel<1024, 8, EMIT, BT_LDS>), g, dim3(1024), lds, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<1024, 8, EMIT, BT_LDS, VEC>), g, dim3(1024), lds, st, a);
+}
+
+template <bool EMIT, bool BT_LDS>
+static void launch_reg(const TopkArgs& a, unsigned rows, size_t lds, hipStream_t st) {
+  const bool vec = a.MB % 4 == 0 && reinterpret_cast<uintptr_t>(a.scores) % 16 == 0 &&
+                   (!BT_LDS || (a.bt_stride % 4 == 0 && reinterpret_cast<uintptr_t>(a.bt) % 16 == 0));
+  if (vec)
+    launch_reg_v<EMIT, BT_LDS, true>(a, rows, lds, st);
+  else
+    launch_reg_v<EMIT, BT_LDS, false>(a, rows, lds, st);
 }
 
 // Shared argument checks of the two entry points; 0 or an ISB_E_* code.

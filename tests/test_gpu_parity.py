@@ -123,7 +123,8 @@ def test_topk_bit_exact(K, q_len, H_kv):
 
 
 @pytest.mark.parametrize("MB,R,q_len,K", [(8192, 8, 2, 32), (256, 1075, 4, 16), (512, 128, 1, 16),
-                                          (1024, 64, 1, 16), (10000, 4, 1, 32), (3000, 6, 1, 5)])
+                                          (1024, 64, 1, 16), (10000, 4, 1, 32), (3000, 6, 1, 5),
+                                          (1027, 5, 1, 16), (4095, 3, 2, 32)])
 def test_topk_full_size_shapes(MB, R, q_len, K):
     _say(f"[topk] MB={MB} rows={R * q_len}")
     rng = np.random.default_rng(MB + R)
@@ -162,7 +163,8 @@ def test_emit_bit_exact(ppb, H_kv, q_len):
 @pytest.mark.parametrize("MB,R,q_len,H_kv,K,ppb", [(48, 24, 1, 1, 7, 8), (40, 19, 3, 2, 9, 1),
                                                    (512, 40, 1, 1, 16, 8), (3000, 6, 2, 1, 32, 8),
                                                    (8192, 4, 2, 1, 32, 8), (10000, 3, 1, 2, 16, 1),
-                                                   (300, 5, 4, 1, 300, 8)])
+                                                   (300, 5, 4, 1, 300, 8), (45, 7, 1, 1, 5, 8),
+                                                   (1027, 4, 1, 1, 16, 1)])
 def test_topk_select_emit_matches_oracle(MB, R, q_len, H_kv, K, ppb):
     _say(f"[topk+emit] MB={MB} R={R} q={q_len} H_kv={H_kv} K={K} ppb={ppb}")
     rng = np.random.default_rng(MB * 3 + K)
