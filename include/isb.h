@@ -138,7 +138,7 @@ ISB_API int isb_index_score(isb_stream_t stream,
 /*
  * isb_topk_select - the blocks each (KV head, token) row attends to.
  *
- * Per row (PR 2962: the tail block is always selected; pad rows compute
+ * Per row (PR 2962: the tail block is part of every selection; pad rows compute
  * nothing): the tail block n_t - 1, plus the top_k - 1 best of blocks
  * [0, n_t - 1) by score, ties to the lower block index, NaN below every number
  * and -0.0 equal to +0.0.  Written ascending, padded with -1; a row with

@@ -1,0 +1,185 @@
+// Device code of the top-k block selection, shared by the selection kernels
+// (topk_select.hip) and the attention launch that selects its own rows
+// (sparse_pa.hip).
+//
+// Rule (ROCm/ATOM PR 2962: the decode commit keeps the tail page in every
+// selection; the pad-row fix makes a row of causal length 0 compute nothing): a row with n_t
+// valid blocks keeps its tail block n_t - 1 and the top_k - 1 best of blocks
+// [0, n_t - 1), ties to the lower block index; NaN ranks below every number
+// and -0.0 equals +0.0.  The selection is written ascending and padded with -1.
+//
+// Method: radix select on order-preserving 32-bit keys.  Four 8-bit passes
+// each count, per wave, the keys that match the prefix found so far into a
+// 256-bin LDS histogram (no contention between waves); wave 0 sums the waves'
+// bins and finds the digit where the count of larger keys reaches top_k - 1
+// (two barriers a pass).  The threshold key is then exact; keys above it are
+// taken, and keys equal to it are taken in block order until the count is
+// met.  One scan of packed (greater, equal) counts gives each thread its
+// output position, so the output is ascending without a sort.
+#pragma once
+
+#include "isb_device.h"
+
+namespace isb {
+
+// Order-preserving key: larger score -> larger key; -0.0 == +0.0; every NaN
+// maps to 0, below -inf (0x007FFFFF).
+__device__ __forceinline__ uint32_t order_key(float s) {
+  if (s != s) return 0u;
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over the NT threads of the workgroup.
+template <int NT>
+__device__ __forceinline__ int block_incl_scan(int v, int* s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) before += w < wave ? s_wave[w] : 0;
+  __syncthreads();
+  return x + before;
+}
+
+// Entries j0 .. j0 + E - 1 of a row of n entries (0 past the end).  VEC: the
+// row starts 16-byte aligned and n is a multiple of 4, so the entries arrive
+// in 16-byte (E >= 4) or 8-byte (E = 2) loads; per-entry 4-byte loads at a
+// stride of E entries would touch E times as many cache lines.
+template <int E, bool VEC, typename T>
+__device__ __forceinline__ void load_run(const T* row, int j0, int n, T (&v)[E]) {
+  if constexpr (VEC && E >= 4) {
+#pragma unroll
+    for (int x = 0; x < E / 4; ++x) {
+      if (j0 + 4 * x < n) {
+        const u32x4 w = ld16(row + j0 + 4 * x);
+        // each element copied to a scalar first: a bit cast taken straight
+        // from a vector element reads element 0 here
+        const uint32_t e[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int y = 0; y < 4; ++y) v[4 * x + y] = __builtin_bit_cast(T, e[y]);
+      } else {
+#pragma unroll
+        for (int y = 0; y < 4; ++y) v[4 * x + y] = T(0);
+      }
+    }
+  } else if constexpr (VEC && E == 2) {
+    if (j0 < n) {
+      const u32x2 w = ld8(row + j0);
+      const uint32_t e0 = w[0], e1 = w[1];
+      v[0] = __builtin_bit_cast(T, e0);
+      v[1] = __builtin_bit_cast(T, e1);
+    } else {
+      v[0] = v[1] = T(0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = j0 + i < n ? row[j0 + i] : T(0);
+  }
+}
+
+// LDS of select_row: one histogram per wave, wave totals, the digit found.
+template <int NT>
+struct SelectLds {
+  int hist[NT / 64][256];
+  int wave_tot[NT / 64];
+  int pick[2];
+};
+
+// The selection of one row whose scores for blocks E t .. E t + E - 1 are in
+// thread t's sc[] (NT threads, all of the workgroup).  put(k, b) receives
+// selection slot k < K and its block b (ascending; -1 past the m selected
+// blocks).  Returns m = min(K, n_t).  Every thread must call it.
+template <int NT, int E, typename PutFn>
+__device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, SelectLds<NT>& sl, PutFn put) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int W = nt - 1;  // candidates [0, W); block W is the tail
+  if (nt == 0 || W <= K - 1) {
+    for (int j = tid; j < K; j += NT) put(j, j < nt ? j : -1);
+    return nt;
+  }
+  uint32_t key[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) key[i] = E * tid + i < W ? order_key(sc[i]) : 0u;
+  const int jlim = W - E * tid;  // my keys i < jlim are candidates
+  const int keep = K - 1;        // candidates to select (0 when top_k = 1)
+  int need = keep;
+  uint32_t prefix = 0u, pmask = 0u;
+  // With need >= 1 every pass finds its digit (need never exceeds the keys
+  // that match the prefix); with top_k = 1 only the tail is selected.
+  for (int shift = 24; shift >= 0 && keep > 0; shift -= 8) {
+    // this wave's histogram: cleared, then filled (LDS operations of a wave
+    // complete in order; wave 0 finished reading the previous pass's bins
+    // before the barrier that ended it)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) sl.hist[wave][lane + 64 * x] = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&sl.hist[wave][(key[i] >> shift) & 0xFF], 1);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l takes digits 255 - 4 l - x (x < 4): descending digit order
+      int cnt[4], tot = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) c += sl.hist[w][255 - 4 * lane - x];
+        cnt[x] = c;
+        tot += c;
+      }
+      int incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      int run = incl - tot;  // keys in higher digits
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (run < need && need <= run + cnt[x]) {
+          sl.pick[0] = 255 - 4 * lane - x;
+          sl.pick[1] = run;
+        }
+        run += cnt[x];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sl.pick[0] << shift;
+    pmask |= 0xFFu << shift;
+    need -= sl.pick[1];
+  }
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    if (i < jlim) {
+      gt += key[i] > prefix;
+      eq += key[i] == prefix;
+    }
+  }
+  const int packed = gt | (eq << 16);
+  const int before = block_incl_scan<NT>(packed, sl.wave_tot) - packed;
+  int seen = before >> 16;
+  int pos = (before & 0xFFFF) + min(seen, need);
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    if (i < jlim && keep > 0) {
+      bool sel = key[i] > prefix;
+      if (key[i] == prefix) sel = seen++ < need;
+      if (sel && pos < keep) put(pos++, E * tid + i);
+    }
+  }
+  if (tid == 0) put(K - 1, W);  // the tail block, larger than every candidate
+  return K;
+}
+
+}  // namespace isb

@@ -3,9 +3,9 @@
 // and also writes the sparse page table of the selection (the work of
 // isb_emit_sparse_block_table) from the same workgroup.
 //
-// ROCm/ATOM PR 2962 (decode commit: the tail page is always selected; Pad-row
-// fix: a row of causal length 0 computes nothing) fixes the tail rule and the
-// clamp; ties go to the lower block index.
+// ROCm/ATOM PR 2962 fixes the tail rule (the decode commit keeps the tail page
+// in every selection) and the clamp (the pad-row fix: a row of causal length 0
+// computes nothing); ties go to the lower block index.
 //
 // One workgroup selects one row by radix select on order-preserving 32-bit
 // keys: four 8-bit passes build a 256-bin histogram of the keys that match
@@ -21,6 +21,7 @@
 // LDS).  Wider rows use the same algorithm over global memory.
 #include "isb_device.h"
 #include "isb_host.h"
+#include "select_device.h"
 
 namespace isb {
 
@@ -33,34 +34,6 @@ struct TopkArgs {
   int32_t* sctx;      // fused emit only
   int q_len, T, MB, K, H_kv, bt_stride, ppb;
 };
-
-// Order-preserving key: larger score -> larger key; -0.0 == +0.0; every NaN
-// maps to 0, below -inf (0x007FFFFF).
-__device__ __forceinline__ uint32_t order_key(float s) {
-  if (s != s) return 0u;
-  uint32_t u = __float_as_uint(s);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Inclusive prefix sum over the NT threads of the workgroup.
-template <int NT>
-__device__ __forceinline__ int block_incl_scan(int v, int* s_wave) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) before += w < wave ? s_wave[w] : 0;
-  __syncthreads();
-  return x + before;
-}
 
 // Causal geometry of topk row `row` (= g * T + t).
 struct RowGeom {
@@ -138,52 +111,13 @@ __device__ __forceinline__ void radix_select(int W, int need, KeyFn key, PutFn p
 // between waves), wave 0 sums the waves' bins and finds the digit, two
 // barriers a pass.  Dynamic LDS: (BT_LDS) the block-table row [MB], then
 // (EMIT) the selection [K].
-// VEC: rows start 16-byte aligned and hold a multiple of 4 entries (score
-// rows and, with BT_LDS, block-table rows), so a thread's E consecutive
-// entries arrive in 16-byte (or, for E = 2, 8-byte) loads; per-entry 4-byte
-// loads at a stride of E entries would touch E times as many cache lines.
-template <int E, bool VEC, typename T>
-__device__ __forceinline__ void load_run(const T* row, int j0, int n, T (&v)[E]) {
-  if constexpr (VEC && E >= 4) {
-#pragma unroll
-    for (int x = 0; x < E / 4; ++x) {
-      if (j0 + 4 * x < n) {
-        const u32x4 w = ld16(row + j0 + 4 * x);
-        // each element copied to a scalar first: a bit cast taken straight
-        // from a vector element reads element 0 here
-        const uint32_t e[4] = {w[0], w[1], w[2], w[3]};
-#pragma unroll
-        for (int y = 0; y < 4; ++y) v[4 * x + y] = __builtin_bit_cast(T, e[y]);
-      } else {
-#pragma unroll
-        for (int y = 0; y < 4; ++y) v[4 * x + y] = T(0);
-      }
-    }
-  } else if constexpr (VEC && E == 2) {
-    if (j0 < n) {
-      const u32x2 w = ld8(row + j0);
-      const uint32_t e0 = w[0], e1 = w[1];
-      v[0] = __builtin_bit_cast(T, e0);
-      v[1] = __builtin_bit_cast(T, e1);
-    } else {
-      v[0] = v[1] = T(0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = j0 + i < n ? row[j0 + i] : T(0);
-  }
-}
-
 template <int NT, int E, bool EMIT, bool BT_LDS, bool VEC>
 __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
-  constexpr int NW = NT / 64;
   extern __shared__ int32_t s_dyn[];
-  __shared__ int s_hist[NW][256];
-  __shared__ int s_wave[NW];
-  __shared__ int s_pick[2];
+  __shared__ SelectLds<NT> sl;
   int32_t* s_bt = s_dyn;
   int32_t* s_sel = s_dyn + (BT_LDS ? a.MB : 0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int tid = threadIdx.x;
   const int row = blockIdx.x;
   // Every global load first: length, scores and (fused, narrow rows) the
   // block-table row, so the workgroup waits for one round trip.
@@ -200,100 +134,10 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
       if (E * tid + i < a.MB) s_bt[E * tid + i] = btv[i];
   }
   int32_t* o = a.topk + (size_t)row * a.K;
-  const int W = q.nt - 1;  // candidates [0, W); block W is the tail
-  int m;                   // blocks selected
-  if (q.nt == 0 || W <= a.K - 1) {
-    for (int j = tid; j < a.K; j += NT) {
-      const int v = j < q.nt ? j : -1;
-      o[j] = v;
-      if constexpr (EMIT) s_sel[j] = v;
-    }
-    m = q.nt;
-  } else {
-    uint32_t key[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) key[i] = E * tid + i < W ? order_key(sc[i]) : 0u;
-    const int jlim = W - E * tid;  // my keys i < jlim are candidates
-    const int keep = a.K - 1;      // candidates to select (0 when top_k = 1)
-    int need = keep;
-    uint32_t prefix = 0u, pmask = 0u;
-    // With need >= 1 every pass finds its digit (need never exceeds the keys
-    // that match the prefix); with top_k = 1 only the tail is selected.
-    for (int shift = 24; shift >= 0 && keep > 0; shift -= 8) {
-      // this wave's histogram: cleared, then filled (LDS operations of a wave
-      // complete in order; wave 0 finished reading the previous pass's bins
-      // before the barrier that ended it)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) s_hist[wave][lane + 64 * x] = 0;
-#pragma unroll
-      for (int i = 0; i < E; ++i)
-        if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&s_hist[wave][(key[i] >> shift) & 0xFF], 1);
-      __syncthreads();
-      if (wave == 0) {
-        // lane l takes digits 255 - 4 l - x (x < 4): descending digit order
-        int cnt[4], tot = 0;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          int c = 0;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) c += s_hist[w][255 - 4 * lane - x];
-          cnt[x] = c;
-          tot += c;
-        }
-        int incl = tot;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += y;
-        }
-        int run = incl - tot;  // keys in higher digits
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          if (run < need && need <= run + cnt[x]) {
-            s_pick[0] = 255 - 4 * lane - x;
-            s_pick[1] = run;
-          }
-          run += cnt[x];
-        }
-      }
-      __syncthreads();
-      prefix |= (uint32_t)s_pick[0] << shift;
-      pmask |= 0xFFu << shift;
-      need -= s_pick[1];
-    }
-    // prefix is the exact threshold key; keys above it are taken, and `need`
-    // keys equal to it, the lowest block indices first.  One scan of packed
-    // (greater, equal) counts gives each thread its output position.
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      if (i < jlim) {
-        gt += key[i] > prefix;
-        eq += key[i] == prefix;
-      }
-    }
-    const int packed = gt | (eq << 16);
-    const int before = block_incl_scan<NT>(packed, s_wave) - packed;
-    int seen = before >> 16;
-    int pos = (before & 0xFFFF) + min(seen, need);
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      if (i < jlim && keep > 0) {
-        bool sel = key[i] > prefix;
-        if (key[i] == prefix) sel = seen++ < need;
-        if (sel && pos < keep) {
-          o[pos] = E * tid + i;
-          if constexpr (EMIT) s_sel[pos] = E * tid + i;
-          ++pos;
-        }
-      }
-    }
-    if (tid == 0) {
-      o[a.K - 1] = W;  // the tail block, larger than every candidate
-      if constexpr (EMIT) s_sel[a.K - 1] = W;
-    }
-    m = a.K;
-  }
+  const int m = select_row<NT, E>(sc, q.nt, a.K, sl, [&](int k, int b) {
+    o[k] = b;
+    if constexpr (EMIT) s_sel[k] = b;
+  });
   if constexpr (EMIT) {
     __syncthreads();
     const int slots = a.K * a.ppb;

@@ -23,7 +23,7 @@ def causal_length(seq_len: int, q_len: int, i: int) -> int:
     """L_t for query token i of a request of length seq_len.
 
     Clamped at 0, so a pad request (length 0) with q > 1 computes nothing
-    (PR 2962, "Pad-row fix": the emit clamps a row's causal length where it
+    (PR 2962, the pad-row fix: the emit clamps a row's causal length where it
     enters)."""
     return max(0, int(seq_len) - (q_len - 1 - i))
 
@@ -76,9 +76,9 @@ def index_score(q_idx, idx_pool, idx_dtype, idx_scale, block_table, seq_lens, q_
 def topk_select(scores, seq_lens, q_len, top_k):
     """Selected block indices, int32 [H_kv, T, top_k], ascending, padded with -1.
 
-    Per row: the tail block n_t - 1 is always selected (PR 2962, the decode
-    commit: "the tail page is always selected"; ``sparse_local_block`` checked
-    at startup); the other top_k - 1 are the best of blocks [0, n_t - 1) by
+    Per row: the tail block n_t - 1 is part of every selection (PR 2962, the
+    decode commit keeps the tail page; ``sparse_local_block`` is checked at
+    startup); the other top_k - 1 are the best of blocks [0, n_t - 1) by
     score, ties to the lower block index.  A row with n_t = 0 selects nothing
     (Pad-row fix).  Readings: NaN ranks below every number, -0.0 equals +0.0,
     the output is ascending by block index (so the tail is last) and unused

@@ -4,12 +4,13 @@ Test infrastructure only (see the package docstring).
 
 Formats, as the sources name them:
 * e4m3fn - ``float8_e4m3fn`` K/V and index values and the e4m3 query
-  (ROCm/ATOM PR 2962, Summary: "an fp8 index query, e4m3"; the fused-writer
-  commit message: a ``float8_e4m3fn`` q with a unit-scale saturating cast).
+  (ROCm/ATOM PR 2962, Summary: the MXFP4 index is scored with an e4m3 index
+  query; the fused-writer commit message: a ``float8_e4m3fn`` q with a
+  unit-scale saturating cast).
   Definition (OCP 8-bit floating point, E4M3): sign s, 4 exponent bits E
   (bias 7), 3 mantissa bits m; E = 0 is subnormal 2^-6 * m/8; all other codes
   are 2^(E-7) * (1 + m/8) except E = 15, m = 7, which is NaN; no infinities.
-* e2m1 - the MXFP4 element (PR 2962, Summary: "e2m1 data").  OCP MX v1.0:
+* e2m1 - the MXFP4 element (PR 2962, Summary: the data part of a page).  OCP MX v1.0:
   sign, 2 exponent bits (bias 1), 1 mantissa bit; magnitudes
   0, 0.5, 1, 1.5, 2, 3, 4, 6.
 * e8m0 - the MXFP4 block scale, one per 32 elements (PR 2962, Summary).

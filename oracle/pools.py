@@ -26,7 +26,7 @@ Pool layout read here (its own code; it shares nothing with the GPU path):
   fp8 values are multiplied by the per-tensor ``k_scale`` / ``v_scale``.  One
   page id addresses a K page and a V page (vLLM PR 61889, Details).
 * K/V cache, mxfp4 - one 8704 B page per block for K and one for V
-  (PR 2962, Summary: "K and V are MXFP4 pages of the same format").
+  (PR 2962, Summary: K and V use the same MXFP4 page format).
 * A K/V page id holds one page per KV head ([num_pages][H_kv][page]): the
   MXFP4 cache declares one field per (page, KV head) for K and for V, and a
   single field per block for the index key (PR 2962, the commit that
