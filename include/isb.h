@@ -3,8 +3,8 @@
  * decode on an AMD Instinct MI355X (gfx950).
  *
  * The layer's steps are separate calls on one HIP stream, each taking plain
- * device pointers and sizes (a layer step can run as three launches:
- * isb_index_score, isb_topk_select_emit, isb_sparse_pa_decode):
+ * device pointers and sizes (a whole layer step can run as two launches:
+ * isb_index_score, then isb_select_attend):
  *
  *   isb_index_score              score every 128-token block of each request's
  *                                paged index-key cache with the index query;
@@ -13,7 +13,8 @@
  *   isb_topk_select_emit         both of the above in one launch;
  *   isb_sparse_pa_decode         paged attention over the selected pages only
  *                                (split-K flash decode; the last split of a
- *                                row merges it, in the same launch).
+ *                                row merges it, in the same launch);
+ *   isb_select_attend            top-k, emit and attention in one launch.
  *
  * The calls follow the decode call of the vLLM API page for
  * vllm.models.minimax_m3.amd.sparse_attention_msa (MiniMaxM3SparseAiterPAImpl
@@ -239,6 +240,33 @@ ISB_API int isb_sparse_pa_decode(isb_stream_t stream,
                          int num_q_heads, int num_kv_heads, int head_dim,
                          float sm_scale, void* workspace, size_t workspace_bytes,
                          void* out);
+
+/*
+ * isb_select_attend - isb_topk_select_emit followed by isb_sparse_pa_decode,
+ * in one launch where it can: each attention workgroup selects its row's
+ * blocks itself (from the row's scores and block-table row) and takes its
+ * page ids from there; the first split of each row also writes topk_idx,
+ * sparse_bt and sparse_ctx.  Writes exactly what the two calls write (the
+ * selection, table and lengths bit-identical; the output as
+ * isb_sparse_pa_decode computes it).  One launch for bf16 / fp8 K/V with
+ * max_blocks <= 2048, max_blocks and block_table_stride multiples of 4 and
+ * 16-byte aligned scores and block table; otherwise the two calls in turn.
+ *
+ * Arguments as in isb_topk_select_emit and isb_sparse_pa_decode (the sparse
+ * table stride is top_k * pages_per_block, 8 or 1 by kv_dtype; head_dim 128).
+ * The workspace is the one isb_sparse_pa_workspace_bytes gives for
+ * sparse_bt_stride = top_k * pages_per_block, with the same contract.
+ */
+ISB_API int isb_select_attend(isb_stream_t stream, const float* scores,
+                              const int32_t* seq_lens, int num_reqs,
+                              int decode_query_len, int num_kv_heads, int max_blocks,
+                              int top_k, const int32_t* block_table,
+                              int block_table_stride, const void* q, int q_dtype,
+                              const void* k_pool, const void* v_pool, int kv_dtype,
+                              int64_t num_pages, float k_scale, float v_scale,
+                              int num_q_heads, float sm_scale, void* workspace,
+                              size_t workspace_bytes, int32_t* topk_idx,
+                              int32_t* sparse_bt, int32_t* sparse_ctx, void* out);
 
 #ifdef __cplusplus
 }

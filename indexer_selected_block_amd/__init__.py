@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     emit_sparse_block_table,
     index_score,
     load_library,
+    select_attend,
     sparse_pa_decode,
     sparse_pa_workspace_bytes,
     strerror,

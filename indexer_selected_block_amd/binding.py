@@ -61,6 +61,8 @@ _SIGNATURES = {
     "isb_topk_select": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "isb_emit_sparse_block_table": ([_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P], _I),
     "isb_topk_select_emit": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P], _I),
+    "isb_select_attend": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _I, _I64, _F, _F, _I, _F,
+                           _P, _SZ, _P, _P, _P, _P], _I),
     "isb_sparse_pa_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
     "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I,
                               _F, _P, _SZ, _P], _I),
@@ -204,13 +206,41 @@ def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, spa
     return out
 
 
+def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_dtype, k_pool, v_pool,
+                  kv_dtype, k_scale, v_scale, num_q_heads, sm_scale, topk_idx=None, sparse_bt=None,
+                  sparse_ctx=None, out=None, workspace=None):
+    """(topk_idx, sparse_bt, sparse_ctx, out): top-k, emit and attention (see isb_select_attend)."""
+    dev = _dev(scores, seq_lens, block_table, q, k_pool, v_pool)
+    H_kv, T, MB = scores.shape
+    ppb = 1 if _code(kv_dtype) == DTYPE_CODES["mxfp4"] else 8
+    if topk_idx is None:
+        topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
+    if sparse_bt is None:
+        sparse_bt = torch.empty((T * H_kv, top_k * ppb), dtype=torch.int32, device=dev)
+    if sparse_ctx is None:
+        sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    need = sparse_pa_workspace_bytes(T, num_q_heads, H_kv, top_k * ppb, kv_dtype)
+    if workspace is None:  # zero-filled: the arrival counters start at zero
+        workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
+    _dev(topk_idx, sparse_bt, sparse_ctx, out, workspace)
+    _call("select_attend", _stream(dev), scores.data_ptr(), seq_lens.data_ptr(), seq_lens.shape[0],
+          decode_query_len, H_kv, MB, top_k, block_table.data_ptr(), block_table.shape[1], q.data_ptr(),
+          _code(q_dtype), k_pool.data_ptr(), v_pool.data_ptr(), _code(kv_dtype), k_pool.shape[0],
+          float(k_scale), float(v_scale), num_q_heads, float(sm_scale), workspace.data_ptr(),
+          workspace.numel(), topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr(), out.data_ptr())
+    return topk_idx, sparse_bt, sparse_ctx, out
+
+
 class DecodeLayer:
     """One decode layer over a workload, with persistent outputs: index_score,
-    topk_select_emit (top-k and the sparse table in one launch), sparse_pa_decode.
+    then select_attend (top-k, the sparse table and the attention, in one launch
+    where the shapes allow it).
 
     Buffers are allocated once at construction (torch, on the workload's
-    device); ``run()`` only enqueues the three launches, so it can be timed
-    or captured."""
+    device); ``run()`` only enqueues the launches, so it can be timed or
+    captured."""
 
     def __init__(self, w):
         cfg = w.cfg
@@ -230,12 +260,10 @@ class DecodeLayer:
         w, cfg = self.w, self.w.cfg
         index_score(w.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale, w.block_table,
                     w.seq_lens, cfg.query_len, cfg.num_kv_heads, cfg.max_blocks, scores=self.scores)
-        topk_select_emit(self.scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table,
-                         cfg.pages_per_block, topk_idx=self.topk, sparse_bt=self.sparse_bt,
-                         sparse_ctx=self.sparse_ctx)
-        sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
-                         self.sparse_bt, self.sparse_ctx, cfg.num_q_heads, cfg.num_kv_heads,
-                         w.sm_scale, out=self.out, workspace=self.workspace)
+        select_attend(self.scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table, w.q, cfg.q_dtype,
+                      w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale, cfg.num_q_heads, w.sm_scale,
+                      topk_idx=self.topk, sparse_bt=self.sparse_bt, sparse_ctx=self.sparse_ctx, out=self.out,
+                      workspace=self.workspace)
         return self.out
 
 
@@ -244,5 +272,6 @@ isb_index_score = index_score
 isb_topk_select = topk_select
 isb_emit_sparse_block_table = emit_sparse_block_table
 isb_topk_select_emit = topk_select_emit
+isb_select_attend = select_attend
 isb_sparse_pa_decode = sparse_pa_decode
 isb_sparse_pa_workspace_bytes = sparse_pa_workspace_bytes

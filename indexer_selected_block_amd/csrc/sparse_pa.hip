@@ -53,6 +53,7 @@
 // (one offset register a wave, nontemporal: every page is read once).
 #include "isb_device.h"
 #include "isb_host.h"
+#include "select_device.h"
 
 namespace isb {
 
@@ -321,43 +322,23 @@ __device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const
   }
 }
 
-// RUN: pages of one wave's run (a power of two).  grid (rows, splits), four
-// waves a workgroup.  A split is walked one round (four runs, one per wave)
-// at a time; each round's loads are issued together and its logits give one
-// exact max per head, folded into the wave's running max between rounds.
-template <int KV_DT, int Q_DT, int RUN>
-__global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
-  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
+// The attention of one split of row `row` (token t = row / H_kv, KV head kvh),
+// given its sparse length, its query operand qb, this lane's page id for the
+// first rounds (my_ids = ids(0)) and `ids(r0)`: this lane's page id for round
+// r0 + lane / RUN, slot lane % RUN of this wave's run (-1 past the split).
+// A split is walked one round (four runs, one per wave) at a time; each
+// round's loads are issued together and its logits give one exact max per
+// head, folded into the wave's running max between rounds.
+template <int KV_DT, int Q_DT, int RUN, typename IdFn>
+__device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, int row, int split, int kvh,
+                                               int n_tok, bf16x8 (&qb)[4], int my_ids, IdFn ids,
+                                               __bf16* out_row) {
   constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
   constexpr int ROUND = 4 * RUN;    // pages of a round
-  constexpr int IDS = 64 / RUN;     // rounds whose page ids one load of the wave holds
-  __shared__ WaveParts wp;
-  const int row = blockIdx.x, split = blockIdx.y;
+  constexpr int IDS = 64 / RUN;     // rounds whose page ids one id fetch holds
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int t = row / a.H_kv, kvh = row % a.H_kv;
-  const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
   const int p0 = split * a.pps;
-  const int pend = min(a.sbt_stride, p0 + a.pps);
-  // Lane L holds the page id of slot L % RUN of this wave's run in round
-  // r0 + L / RUN (-1 past the split).
-  auto load_ids = [&](int r0) {
-    const int pidx = p0 + (r0 + lane / RUN) * ROUND + wave * RUN + lane % RUN;
-    return pidx < pend ? pages[pidx] : -1;
-  };
-  // Issued together before anything waits: the first rounds' page ids, the
-  // row length and the query, so the K/V gathers start after one round trip.
-  int my_ids = load_ids(0);
-  const int n_tok = a.sctx[row];
-  // Q^T operand: head kvh * G + c, dims 32 g .. 32 g + 31 (zero past G).
-  bf16x8 qb[4];
-  {
-    const int hc = c < a.G ? c : 0;
-    const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * QB;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
-  }
-  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
   if (n_tok <= 0) {
     write_empty_row(a, split, out_row);
     return;
@@ -377,7 +358,7 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   const int64_t hstride = (int64_t)a.H_kv * PB;  // bytes per page id (all heads)
   const int64_t hoff = (int64_t)kvh * PB;
   for (int r = 0; r < nrounds; ++r) {
-    if (r > 0 && r % IDS == 0) my_ids = load_ids(r);
+    if (r > 0 && r % IDS == 0) my_ids = ids(r);
     const int wb = p0 + r * ROUND + wave * RUN;
     const int cnt = max(0, min(RUN, p1 - wb));
     if (cnt == 0) continue;  // wave-uniform: this wave has nothing left in the split
@@ -481,6 +462,118 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   }
   wave_to_lds<1, 16>(wp, wave, lane, M, lsum, o);  // row r of tile dt: dim 16 dt + r
   finish_split(a, wp, row, split, live, out_row);
+}
+
+// RUN: pages of one wave's run (a power of two).  grid (rows, splits), four
+// waves a workgroup; page ids come from the sparse page table.
+template <int KV_DT, int Q_DT, int RUN>
+__global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
+  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
+  constexpr int ROUND = 4 * RUN;
+  __shared__ WaveParts wp;
+  const int row = blockIdx.x, split = blockIdx.y;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int t = row / a.H_kv, kvh = row % a.H_kv;
+  const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
+  const int p0 = split * a.pps;
+  const int pend = min(a.sbt_stride, p0 + a.pps);
+  auto load_ids = [&](int r0) {
+    const int pidx = p0 + (r0 + lane / RUN) * ROUND + wave * RUN + lane % RUN;
+    return pidx < pend ? pages[pidx] : -1;
+  };
+  // Issued together before anything waits: the first rounds' page ids, the
+  // row length and the query, so the K/V gathers start after one round trip.
+  const int my_ids = load_ids(0);
+  const int n_tok = a.sctx[row];
+  // Q^T operand: head kvh * G + c, dims 32 g .. 32 g + 31 (zero past G).
+  bf16x8 qb[4];
+  {
+    const int hc = c < a.G ? c : 0;
+    const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * QB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
+  }
+  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
+  attend_split16<KV_DT, Q_DT, RUN>(a, wp, row, split, kvh, n_tok, qb, my_ids, load_ids, out_row);
+}
+
+// ----------------------------------------------------------------- select + attend
+// Top-k selection and the attention of a row in one launch, for 16-token
+// pages and rows of up to kSelMaxBlocks blocks.  Every workgroup of a row
+// selects the row's blocks itself (the same result in each: the selection is
+// a function of the scores) from the scores and the block-table row, both
+// read into registers / LDS in one round trip, and takes its page ids from
+// LDS; split 0 also writes the selection, the sparse page table and the
+// sparse length, as isb_topk_select_emit would.
+struct SelArgs {
+  const float* scores;      // [H_kv][T][MB]
+  const int32_t* seq_lens;  // [R]
+  const int32_t* bt;        // [R][bt_stride]
+  int32_t* topk;            // out [H_kv][T][K]
+  int32_t* sbt;             // out [T * H_kv][K * 8]
+  int32_t* sctx;            // out [T * H_kv]
+  int q_len, T, MB, K, bt_stride;
+};
+
+constexpr int kSelMaxBlocks = 2048;
+
+template <int KV_DT, int Q_DT, int RUN, int E>
+__global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
+  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
+  constexpr int ROUND = 4 * RUN;
+  __shared__ WaveParts wp;
+  __shared__ SelectLds<256> sl;
+  __shared__ int32_t s_bt[kSelMaxBlocks];
+  __shared__ int32_t s_sel[kSelMaxBlocks];
+  const int row = blockIdx.x, split = blockIdx.y;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int t = row / a.H_kv, kvh = row % a.H_kv;
+  const int r = t / sa.q_len, i = t % sa.q_len;
+  const int trow = kvh * sa.T + t;  // the row's index in the score and selection buffers
+  // Every global load first: the request's length, the row's scores, the
+  // request's block-table row and the query.
+  const int Lr = sa.seq_lens[r];
+  float sc[E];
+  int32_t btv[E];
+  load_run<E, true>(sa.scores + (size_t)trow * sa.MB, E * tid, sa.MB, sc);
+  load_run<E, true>(sa.bt + (size_t)r * sa.bt_stride, E * tid, sa.MB, btv);
+  bf16x8 qb[4];
+  {
+    const int hc = c < a.G ? c : 0;
+    const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * QB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
+  }
+  const int Lt = max(0, Lr - (sa.q_len - 1 - i));
+  const int nt = min((Lt + kBlockTokens - 1) / kBlockTokens, sa.MB);
+#pragma unroll
+  for (int x = 0; x < E; ++x)
+    if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
+  int32_t* o = sa.topk + (size_t)trow * sa.K;
+  const int m = select_row<256, E>(sc, nt, sa.K, sl, [&](int k, int b) {
+    s_sel[k] = b;
+    if (split == 0) o[k] = b;
+  });
+  __syncthreads();  // the selection and the block-table row are in LDS
+  const int n_tok = m > 0 ? (m - 1) * kBlockTokens + (Lt - kBlockTokens * (nt - 1)) : 0;
+  if (split == 0) {
+    const int slots = sa.K * 8;
+    int32_t* so = sa.sbt + (size_t)row * slots;
+    for (int x = tid; x < slots; x += 256) so[x] = (x >> 3) < m ? s_bt[s_sel[x >> 3]] * 8 + (x & 7) : -1;
+    if (tid == 0) sa.sctx[row] = n_tok;
+  }
+  const int p0 = split * a.pps;
+  const int pend = min(a.sbt_stride, p0 + a.pps);
+  const int mpages = 8 * m;
+  auto ids = [&](int r0) {
+    const int pidx = p0 + (r0 + lane / RUN) * ROUND + wave * RUN + lane % RUN;
+    return pidx < pend && pidx < mpages ? s_bt[s_sel[pidx >> 3]] * 8 + (pidx & 7) : -1;
+  };
+  const int my_ids = ids(0);
+  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
+  attend_split16<KV_DT, Q_DT, RUN>(a, wp, row, split, kvh, n_tok, qb, my_ids, ids, out_row);
 }
 
 // ----------------------------------------------------------------- MXFP4 pages
@@ -627,16 +720,15 @@ extern "C" size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads,
   return pa_workspace_bytes(pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype));
 }
 
-extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dtype,
-                                    const void* k_pool, const void* v_pool, int kv_dtype,
-                                    int64_t num_pages, float k_scale, float v_scale,
-                                    const int32_t* sparse_bt, int sparse_bt_stride,
-                                    const int32_t* sparse_ctx, int num_tokens, int num_q_heads,
-                                    int num_kv_heads, int head_dim, float sm_scale,
-                                    void* workspace, size_t workspace_bytes, void* out) {
-  using namespace isb;
-  if (!q || !k_pool || !v_pool || !sparse_bt || !sparse_ctx || !workspace || !out)
-    return ISB_E_INVALID_ARG;
+namespace isb {
+
+// Argument checks and kernel arguments shared by isb_sparse_pa_decode and
+// isb_select_attend; 0 or an ISB_E_* code.
+static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                    int64_t num_pages, float k_scale, float v_scale, int sparse_bt_stride,
+                    int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, float sm_scale,
+                    void* workspace, size_t workspace_bytes, void* out, PaArgs& a, PaPlan& plan) {
+  if (!q || !k_pool || !v_pool || !workspace || !out) return ISB_E_INVALID_ARG;
   if (num_pages <= 0 || sparse_bt_stride <= 0 || num_tokens <= 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0)
     return ISB_E_INVALID_ARG;
@@ -647,16 +739,15 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return ISB_E_INVALID_ARG;
   const long long rows = (long long)num_tokens * num_kv_heads;
   if (rows > 0x7FFFFFFFLL) return ISB_E_SHAPE;
-  const PaPlan plan = pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype);
+  plan = pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype);
   if (plan.splits > 65535) return ISB_E_SHAPE;
   if (workspace_bytes < pa_workspace_bytes(plan)) return ISB_E_WORKSPACE;
   const bool fp8 = kv_dtype == ISB_FP8_E4M3;
-  PaArgs a;
   a.q = (const uint8_t*)q;
   a.kp = (const uint8_t*)k_pool;
   a.vp = (const uint8_t*)v_pool;
-  a.sbt = sparse_bt;
-  a.sctx = sparse_ctx;
+  a.sbt = nullptr;
+  a.sctx = nullptr;
   a.arrivals = (uint32_t*)workspace;
   a.part_o = (float*)((uint8_t*)workspace + pa_arrival_bytes(plan));
   a.part_ml = a.part_o + (size_t)plan.rows * plan.splits * kPartialO;
@@ -670,8 +761,44 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   a.G = num_q_heads / num_kv_heads;
   a.splits = plan.splits;
   a.pps = plan.pages_per_split;
+  return ISB_OK;
+}
+
+template <int KV_DT, int Q_DT, int E>
+static void launch_select_attend_e(const PaArgs& a, const SelArgs& sa, dim3 grid, hipStream_t st) {
+  constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
+  hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, E>), grid, dim3(256), 0, st, a, sa);
+}
+
+template <int KV_DT, int Q_DT>
+static void launch_select_attend(const PaArgs& a, const SelArgs& sa, dim3 grid, hipStream_t st) {
+  if (sa.MB <= 256) launch_select_attend_e<KV_DT, Q_DT, 1>(a, sa, grid, st);
+  else if (sa.MB <= 512) launch_select_attend_e<KV_DT, Q_DT, 2>(a, sa, grid, st);
+  else if (sa.MB <= 1024) launch_select_attend_e<KV_DT, Q_DT, 4>(a, sa, grid, st);
+  else launch_select_attend_e<KV_DT, Q_DT, 8>(a, sa, grid, st);
+}
+
+}  // namespace isb
+
+extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dtype,
+                                    const void* k_pool, const void* v_pool, int kv_dtype,
+                                    int64_t num_pages, float k_scale, float v_scale,
+                                    const int32_t* sparse_bt, int sparse_bt_stride,
+                                    const int32_t* sparse_ctx, int num_tokens, int num_q_heads,
+                                    int num_kv_heads, int head_dim, float sm_scale,
+                                    void* workspace, size_t workspace_bytes, void* out) {
+  using namespace isb;
+  if (!sparse_bt || !sparse_ctx) return ISB_E_INVALID_ARG;
+  PaArgs a;
+  PaPlan plan;
+  const int err = pa_setup(q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale,
+                           sparse_bt_stride, num_tokens, num_q_heads, num_kv_heads, head_dim, sm_scale,
+                           workspace, workspace_bytes, out, a, plan);
+  if (err) return err;
+  a.sbt = sparse_bt;
+  a.sctx = sparse_ctx;
   hipStream_t st = as_hip(stream);
-  const dim3 grid((unsigned)rows, plan.splits);
+  const dim3 grid((unsigned)plan.rows, plan.splits);
   const bool qb = q_dtype == ISB_BF16;
   if (kv_dtype == ISB_BF16) {
     if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, st);
@@ -682,6 +809,59 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   } else {
     if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, st);
     else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, st);
+  }
+  return launch_status();
+}
+
+extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const int32_t* seq_lens,
+                                 int num_reqs, int decode_query_len, int num_kv_heads, int max_blocks,
+                                 int top_k, const int32_t* block_table, int block_table_stride,
+                                 const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                                 int kv_dtype, int64_t num_pages, float k_scale, float v_scale,
+                                 int num_q_heads, float sm_scale, void* workspace,
+                                 size_t workspace_bytes, int32_t* topk_idx, int32_t* sparse_bt,
+                                 int32_t* sparse_ctx, void* out) {
+  using namespace isb;
+  if (!scores || !seq_lens || !block_table || !topk_idx || !sparse_bt || !sparse_ctx)
+    return ISB_E_INVALID_ARG;
+  if (num_reqs <= 0 || decode_query_len <= 0 || num_kv_heads <= 0 || max_blocks <= 0 ||
+      block_table_stride <= 0)
+    return ISB_E_INVALID_ARG;
+  if (top_k < 1 || top_k > max_blocks || max_blocks > (1 << 20) || max_blocks > block_table_stride)
+    return ISB_E_SHAPE;
+  const int ppb = kv_dtype == ISB_MXFP4 ? 1 : 8;
+  const long long T = (long long)num_reqs * decode_query_len;
+  if (T * num_kv_heads * top_k * ppb > 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  PaArgs a;
+  PaPlan plan;
+  const int err = pa_setup(q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale, top_k * ppb,
+                           (int)T, num_q_heads, num_kv_heads, kHeadDim, sm_scale, workspace, workspace_bytes,
+                           out, a, plan);
+  if (err) return err;
+  hipStream_t st = as_hip(stream);
+  const bool one_launch = kv_dtype != ISB_MXFP4 && max_blocks <= kSelMaxBlocks && max_blocks % 4 == 0 &&
+                          block_table_stride % 4 == 0 && reinterpret_cast<uintptr_t>(scores) % 16 == 0 &&
+                          reinterpret_cast<uintptr_t>(block_table) % 16 == 0;
+  if (!one_launch) {
+    // MXFP4 pages and wide or unaligned rows: the two steps as two launches.
+    int e = isb_topk_select_emit(stream, scores, seq_lens, num_reqs, decode_query_len, num_kv_heads,
+                                 max_blocks, top_k, block_table, block_table_stride, ppb, topk_idx,
+                                 sparse_bt, sparse_ctx);
+    if (e) return e;
+    return isb_sparse_pa_decode(stream, q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale,
+                                sparse_bt, top_k * ppb, sparse_ctx, (int)T, num_q_heads, num_kv_heads,
+                                kHeadDim, sm_scale, workspace, workspace_bytes, out);
+  }
+  SelArgs sa{scores, seq_lens, block_table, topk_idx, sparse_bt, sparse_ctx, decode_query_len, (int)T,
+             max_blocks, top_k, block_table_stride};
+  const dim3 grid((unsigned)plan.rows, plan.splits);
+  const bool qb = q_dtype == ISB_BF16;
+  if (kv_dtype == ISB_BF16) {
+    if (qb) launch_select_attend<ISB_BF16, ISB_BF16>(a, sa, grid, st);
+    else launch_select_attend<ISB_BF16, ISB_FP8_E4M3>(a, sa, grid, st);
+  } else {
+    if (qb) launch_select_attend<ISB_FP8_E4M3, ISB_BF16>(a, sa, grid, st);
+    else launch_select_attend<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, sa, grid, st);
   }
   return launch_status();
 }

@@ -186,6 +186,45 @@ def test_topk_select_emit_matches_oracle(MB, R, q_len, H_kv, K, ppb):
     assert np.array_equal(g_sctx.cpu().numpy(), sctx)
 
 
+# ------------------------------------------------------------------ select + attend
+_SEL_CASES = {
+    "fp8_decode": ("fp8_decode", {}),
+    "spec_decode": ("spec_decode", {}),
+    "tiny_bf16": ("tiny_bf16", {}),
+    "fp8_two_kv_heads": ("fp8_decode", dict(num_kv_heads=2, num_q_heads=16, num_idx_heads=2)),
+    "long_context_rows_not_x4": ("long_context", {}),     # two launches: rows not a multiple of 4
+    "mxfp4": ("mxfp4", {}),                               # two launches: 128-token pages
+}
+
+
+@pytest.mark.parametrize("case", list(_SEL_CASES))
+def test_select_attend_matches_the_two_calls(case):
+    # The one-launch selection + attention writes exactly what
+    # topk_select_emit followed by sparse_pa_decode writes.
+    base, kw = _SEL_CASES[case]
+    cfg = dataclasses.replace(SMALL[base], **kw)
+    _say(f"[select_attend] {case}: MB={cfg.max_blocks}")
+    w = wl.make_workload(cfg, device="cuda")
+    scores = isb.index_score(w.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale, w.block_table,
+                             w.seq_lens, cfg.query_len, cfg.num_kv_heads, cfg.max_blocks)
+    topk, sbt, sctx = isb.topk_select_emit(scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table,
+                                           cfg.pages_per_block)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               sbt, sctx, cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+    T, H_kv = cfg.num_tokens, cfg.num_kv_heads
+    f_topk = torch.full_like(topk, 777)
+    f_sbt = torch.full_like(sbt, -5)
+    f_sctx = torch.full_like(sctx, 3)
+    f_out = torch.full_like(out, float("nan"))
+    isb.select_attend(scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table, w.q, cfg.q_dtype, w.k_pool,
+                      w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale, cfg.num_q_heads, w.sm_scale,
+                      topk_idx=f_topk, sparse_bt=f_sbt, sparse_ctx=f_sctx, out=f_out)
+    torch.cuda.synchronize()
+    assert torch.equal(f_topk, topk) and torch.equal(f_sbt, sbt) and torch.equal(f_sctx, sctx)
+    assert torch.equal(f_out.view(torch.int16), out.view(torch.int16))
+    assert f_out.shape == (T, cfg.num_q_heads, 128) and sbt.shape[0] == T * H_kv
+
+
 # ------------------------------------------------------------------ attention
 def _synthetic_table(hi, seed):
     cfg = hi["cfg"]

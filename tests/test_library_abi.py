@@ -55,6 +55,8 @@ def test_argument_checks_return_before_any_launch(lib):
     assert lib.isb_topk_select(NULL, NULL, NULL, 1, 1, 1, 1, 1, NULL) == -1
     assert lib.isb_emit_sparse_block_table(NULL, NULL, NULL, 1, NULL, 1, 1, 1, 1, 8, NULL, NULL) == -1
     assert lib.isb_topk_select_emit(NULL, NULL, NULL, 1, 1, 1, 4, 2, NULL, 4, 8, NULL, NULL, NULL) == -1
+    assert lib.isb_select_attend(NULL, NULL, NULL, 1, 1, 1, 4, 2, NULL, 4, NULL, 0, NULL, NULL, 1, 8, 1.0, 1.0,
+                                 16, 0.1, NULL, 0, NULL, NULL, NULL, NULL) == -1
     assert lib.isb_sparse_pa_decode(NULL, NULL, 0, NULL, NULL, 1, 1, 1.0, 1.0, NULL, 1, NULL, 1, 16, 1,
                                     128, 0.1, NULL, 0, NULL) == -1
     p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
@@ -73,6 +75,12 @@ def test_argument_checks_return_before_any_launch(lib):
     assert lib.isb_topk_select_emit(NULL, p, p, 1, 1, 1, 8, 2, p, 4, 8, p, p, p) == -3            # MB > stride
     assert lib.isb_topk_select_emit(NULL, p, p, 1, 1, 1, 4, 5, p, 4, 8, p, p, p) == -3            # K > MB
     assert lib.isb_index_score(NULL, p, 0, 1, p, 0, 1.0, 1, p, 4, p, 1, 17, 1, 4, p) == -3      # q > 16
+    assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 8, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,
+                                 16, 0.1, p, 1 << 20, p, p, p, p) == -3                          # MB > stride
+    assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 4, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,
+                                 32, 0.1, p, 1 << 20, p, p, p, p) == -3                          # G = 32
+    assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 4, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,
+                                 16, 0.1, p, 16, p, p, p, p) == -4                               # workspace
     assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 16, 1, 64, 0.1,
                                     p, 1 << 20, p) == -3                                         # head_dim
     assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 32, 1, 128, 0.1,
