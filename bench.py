@@ -125,8 +125,9 @@ def kernel_sources_sha():
     """Hash of each kernel's source file, to tell whether stored counters still apply."""
     csrc = os.path.join(ROOT, "indexer_selected_block_amd", "csrc")
     files = {"index_score": "index_score.hip", "topk_select_emit": "topk_select.hip",
-             "sparse_pa_decode": "sparse_pa.hip"}
-    common = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("isb_device.h", "isb_host.h"))
+             "sparse_pa_decode": "sparse_pa.hip", "select_attend": "sparse_pa.hip"}
+    common = b"".join(open(os.path.join(csrc, f), "rb").read()
+                      for f in ("isb_device.h", "isb_host.h", "select_device.h"))
     return {k: hashlib.sha256(common + open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
             for k, f in files.items()}
 
