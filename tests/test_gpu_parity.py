@@ -410,6 +410,43 @@ def test_layer_chain(name):
                  layer.out.float().cpu().numpy(), ref, hi["block_table"])
 
 
+# ------------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("name", ["fp8_decode", "spec_decode", "mxfp4"])
+def test_layer_replays_from_a_hip_graph(name):
+    # The calls allocate nothing and never synchronise, so a layer step can be
+    # captured; every replay (with eager work and syncs in between) must give
+    # the eager step's outputs bit for bit, and leave the workspace counters
+    # zero for the next call.
+    _say(f"[graph] {name}")
+    w = wl.make_workload(SMALL[name], device="cuda")
+    layer = isb.DecodeLayer(w)
+    layer.run()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (layer.scores, layer.topk, layer.sparse_bt, layer.sparse_ctx, layer.out)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # warm-up on the capturing stream
+        layer.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.run()
+    rows = w.cfg.num_tokens * w.cfg.num_kv_heads
+    for rep in range(4):
+        for t in (layer.scores, layer.out):
+            t.fill_(float("nan"))            # eager work between replays
+        layer.topk.fill_(-9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (layer.scores, layer.topk, layer.sparse_bt, layer.sparse_ctx, layer.out)
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                               b.view(torch.uint8) if b.dtype != torch.int32 else b), f"replay {rep}"
+        assert not layer.workspace[:(4 * rows + 255) // 256 * 256].any()
+
+
 # ------------------------------------------------------------------ full size, sampled
 FULL_SAMPLES = {"tiny_bf16": [0, 1, 2, 3], "fp8_decode": [3, 77], "spec_decode": None,
                 "mxfp4": [5, 60], "long_context": [6]}
