@@ -9,11 +9,15 @@ fp8 K/V and index cache, 16 query heads per KV head, top-k 16 blocks) unless
 --config names another.  Inputs are synthetic and resident in HBM before the
 timed region starts.
 
+Each step uses the next of --layers independent copies of the inputs, so the
+pages a step reads were not read by the step before it.
+
 Prints one JSON line: decode tokens/s of the whole step (value), the
-attended-KV HBM rate of the attention, per-call durations measured with HIP
-events on the launch stream (the step's two calls, and the path's separate
-calls index_score, topk_select_emit and sparse_pa_decode), a roofline entry
-for the dominant kernel (and one for the attention alone), a device copy's measured rate at the
+attended-KV HBM rate of the attention, per-call durations (the step's two
+calls, and the path's separate calls index_score, topk_select_emit and
+sparse_pa_decode) taken as differences between back-to-back passes of K steps
+timed with HIP events on the launch stream, a roofline entry for the dominant
+kernel (and one for the attention alone), a device copy's measured rate at the
 attention's transfer size and at 1 GiB next to the nominal peak, and the CPU
 oracle timed on a bounded sample of the same workload on this host.
 """
@@ -45,8 +49,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="fp8_decode")
-    ap.add_argument("--layers", type=int, default=1,
-                    help="independent copies of the layer's caches, used round-robin")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="independent copies of the layer's inputs, used round-robin, so a "
+                         "step does not find the previous step's pages in the 256 MB "
+                         "last-level cache")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -241,40 +247,56 @@ def main():
     T = cfg.num_tokens
     ms_per_step = 1000.0 * elapsed / args.steps
 
-    # ---- per-kernel durations: HIP events on the launch stream around each call
+    # ---- per-kernel durations, each in its place in the step: passes of K
+    # steps that stop after a given call, run back to back and timed with HIP
+    # events on the launch stream; a call's duration is the difference between
+    # the pass that ends with it and the pass that ends just before it (an
+    # event between two kernels would add its own idle gap, these do not).
     stream = torch.cuda.current_stream(dev)
-    names = ["index_score", "topk_select_emit", "sparse_pa_decode"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        L = layers[s % len(layers)]
+
+    def call_index(L):
         w, c = L.w, L.w.cfg
-        e = ev[s]
-        e[0].record(stream)
         isb.index_score(w.q_idx, c.qidx_dtype, w.idx_pool, c.idx_dtype, w.idx_scale, w.block_table,
                         w.seq_lens, c.query_len, c.num_kv_heads, c.max_blocks, scores=L.scores)
-        e[1].record(stream)
+
+    def call_topk(L):
+        w, c = L.w, L.w.cfg
         isb.topk_select_emit(L.scores, w.seq_lens, c.query_len, c.top_k, w.block_table, c.pages_per_block,
                              topk_idx=L.topk, sparse_bt=L.sparse_bt, sparse_ctx=L.sparse_ctx)
-        e[2].record(stream)
+
+    def call_attend(L):
+        w, c = L.w, L.w.cfg
         isb.sparse_pa_decode(w.q, c.q_dtype, w.k_pool, w.v_pool, c.kv_dtype, w.k_scale, w.v_scale,
                              L.sparse_bt, L.sparse_ctx, c.num_q_heads, c.num_kv_heads, w.sm_scale,
                              out=L.out, workspace=L.workspace)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    dur_ms = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-              for i, n in enumerate(names)}
-    # the fused call the step runs after index_score: top-k, emit and attention
-    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for s in range(args.steps):
-        L = layers[s % len(layers)]
+
+    def call_select_attend(L):
         w, c = L.w, L.w.cfg
-        sev[s][0].record(stream)
         isb.select_attend(L.scores, w.seq_lens, c.query_len, c.top_k, w.block_table, w.q, c.q_dtype, w.k_pool,
                           w.v_pool, c.kv_dtype, w.k_scale, w.v_scale, c.num_q_heads, w.sm_scale, topk_idx=L.topk,
                           sparse_bt=L.sparse_bt, sparse_ctx=L.sparse_ctx, out=L.out, workspace=L.workspace)
-        sev[s][1].record(stream)
-    torch.cuda.synchronize()
-    dur_ms["select_attend"] = sum(a.elapsed_time(b) for a, b in sev) / args.steps
+
+    def pass_ms(calls):
+        """Average ms of one step made of `calls`, over K steps (HIP events)."""
+        for s in range(min(args.warmup, 4)):
+            for f in calls:
+                f(layers[s % len(layers)])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(args.steps):
+            for f in calls:
+                f(layers[s % len(layers)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t_i = pass_ms([call_index])
+    t_it = pass_ms([call_index, call_topk])
+    t_ita = pass_ms([call_index, call_topk, call_attend])
+    t_step = pass_ms([call_index, call_select_attend])
+    dur_ms = {"index_score": t_i, "topk_select_emit": t_it - t_i, "sparse_pa_decode": t_ita - t_it,
+              "select_attend": t_step - t_i}
+    names = ["index_score", "topk_select_emit", "sparse_pa_decode"]
 
     w0 = layers[0].w
     alg, attended = algorithmic_bytes(w0, layers[0].sparse_ctx)
@@ -312,6 +334,7 @@ def main():
         "attended_kv_pct_hbm_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 2),
         "step_launches": ["index_score", "select_attend"],
         "kernel_ms": {k: round(v, 5) for k, v in dur_ms.items()},
+        "kernel_ms_method": "differences of back-to-back passes of K steps ending after each call (HIP events)",
         "roofline": roof(dominant),
         "roofline_sparse_pa_decode": roof("sparse_pa_decode"),
     }

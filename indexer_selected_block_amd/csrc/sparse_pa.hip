@@ -90,7 +90,7 @@ __device__ __forceinline__ bool page_ok(int64_t id, int64_t n) { return id >= 0 
 
 // Per-workgroup LDS of the merge: each wave's per-head max and sum, and its
 // unnormalised output O[head][dim].
-struct WaveParts {
+struct alignas(16) WaveParts {
   float m[kPaWaves][16];
   float l[kPaWaves][16];
   float o[kPaWaves][16][kHeadDim + 4];
@@ -113,10 +113,15 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts& wp, int
 #pragma unroll
   for (int w = 0; w < kPaWaves; ++w) {
     const float mw = wp.m[w][h];
-    const float wt = mw == neg_inf() ? 0.f : exp2f(mw - M);
+    const float wt = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
     L += wp.l[w][h] * wt;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&wp.o[w][h][d0]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&wp.o[w][h][d0 + 4]);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) O[x] += wp.o[w][h][d0 + x] * wt;
+    for (int x = 0; x < 4; ++x) {
+      O[x] += lo[x] * wt;
+      O[4 + x] += hi[x] * wt;
+    }
   }
 
   if (live > 1) {
@@ -179,8 +184,8 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts& wp, int
         const float mk = own ? Mo : ms[k];
         if (mk == neg_inf()) continue;
         const float Mn = fmaxf(M, mk);
-        const float wa = M == neg_inf() ? 0.f : exp2f(M - Mn);
-        const float wb = exp2f(mk - Mn);
+        const float wa = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        const float wb = __builtin_amdgcn_exp2f(mk - Mn);
         L = L * wa + (own ? Lo : ls[k]) * wb;
 #pragma unroll
         for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : os[k][x]) * wb;
@@ -188,13 +193,15 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts& wp, int
       }
     }
   }
-  // Finished row: normalise and write bf16.
+  // Finished row: normalise and write bf16 (nontemporal: nothing here reads
+  // it back).
   if (h < a.G) {
     const float inv = a.v_scale / L;
     bf16x8 ob;
 #pragma unroll
     for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(O[x] * inv);
-    *reinterpret_cast<bf16x8*>(out_row + h * kHeadDim + d0) = ob;
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ob),
+                                reinterpret_cast<u32x4*>(out_row + h * kHeadDim + d0));
   }
 }
 
@@ -219,10 +226,15 @@ __device__ __forceinline__ void wave_to_lds(WaveParts& wp, int wave, int lane, f
     wp.m[wave][c] = m;
     wp.l[wave][c] = l_tot;
   }
+  if constexpr (DIM_MUL == 1) {  // dims 4 g .. 4 g + 3 of tile dt are adjacent: one 16-byte store
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(&wp.o[wave][c][4 * g + DT_MUL * dt]) = o[dt];
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wp.o[wave][c][DIM_MUL * (4 * g + e) + DT_MUL * dt] = o[dt][e];
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wp.o[wave][c][DIM_MUL * (4 * g + e) + DT_MUL * dt] = o[dt][e];
+  }
 }
 
 // Query columns past the group's G heads are zero (they were loaded from head
