@@ -10,12 +10,15 @@
 //
 // Method: radix select on order-preserving 32-bit keys.  Four 8-bit passes
 // each count, per wave, the keys that match the prefix found so far into a
-// 256-bin LDS histogram (no contention between waves); wave 0 sums the waves'
-// bins and finds the digit where the count of larger keys reaches top_k - 1
-// (two barriers a pass).  The threshold key is then exact; keys above it are
-// taken, and keys equal to it are taken in block order until the count is
-// met.  One scan of packed (greater, equal) counts gives each thread its
-// output position, so the output is ascending without a sort.
+// 256-bin LDS histogram (no contention between waves); the waves' bins are
+// summed and the digit where the count of larger keys reaches top_k - 1 is
+// found with a wave-wide prefix sum.  With four waves every wave finds the
+// digit itself from histograms that alternate between two buffers, so a pass
+// has one barrier; with more waves wave 0 finds it and hands it over in LDS
+// (two barriers).  The threshold key is then exact; keys above it are taken,
+// and keys equal to it are taken in block order until the count is met.  One
+// scan of packed (greater, equal) counts gives each thread its output
+// position, so the output is ascending without a sort.
 #pragma once
 
 #include "isb_device.h"
@@ -31,16 +34,24 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16
+// lanes, then the totals of rows 0 / 2 broadcast into rows 1 / 3 and the
+// total of lanes 0..31 into rows 2 and 3 (DPP; lanes with no source add 0).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // Inclusive prefix sum over the NT threads of the workgroup.
 template <int NT>
 __device__ __forceinline__ int block_incl_scan(int v, int* s_wave) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   int before = 0;
@@ -86,10 +97,12 @@ __device__ __forceinline__ void load_run(const T* row, int j0, int n, T (&v)[E])
   }
 }
 
-// LDS of select_row: one histogram per wave, wave totals, the digit found.
+// LDS of select_row: one histogram per wave (two with four waves, used by
+// alternate passes), wave totals, the digit found.
 template <int NT>
-struct SelectLds {
-  int hist[NT / 64][256];
+struct alignas(16) SelectLds {
+  static constexpr int NB = NT <= 256 ? 2 : 1;
+  int hist[NB][NT / 64][256];
   int wave_tot[NT / 64];
   int pick[2];
 };
@@ -116,47 +129,59 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
   uint32_t prefix = 0u, pmask = 0u;
   // With need >= 1 every pass finds its digit (need never exceeds the keys
   // that match the prefix); with top_k = 1 only the tail is selected.
-  for (int shift = 24; shift >= 0 && keep > 0; shift -= 8) {
+  constexpr int NB = SelectLds<NT>::NB;
+  for (int shift = 24, pass = 0; shift >= 0 && keep > 0; shift -= 8, ++pass) {
+    int(&hist)[NW][256] = sl.hist[NB == 2 ? (pass & 1) : 0];
     // this wave's histogram: cleared, then filled (LDS operations of a wave
-    // complete in order; wave 0 finished reading the previous pass's bins
-    // before the barrier that ended it)
+    // complete in order; no wave still reads it: with two buffers its last
+    // reader finished before the previous pass's barrier, with one buffer
+    // wave 0 finished before the barrier that ended the previous pass)
 #pragma unroll
-    for (int x = 0; x < 4; ++x) sl.hist[wave][lane + 64 * x] = 0;
+    for (int x = 0; x < 4; ++x) hist[wave][lane + 64 * x] = 0;
 #pragma unroll
     for (int i = 0; i < E; ++i)
-      if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&sl.hist[wave][(key[i] >> shift) & 0xFF], 1);
+      if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&hist[wave][(key[i] >> shift) & 0xFF], 1);
     __syncthreads();
-    if (wave == 0) {
+    int digit = 0, above = 0;
+    if (NB == 2 || wave == 0) {
       // lane l takes digits 255 - 4 l - x (x < 4): descending digit order
-      int cnt[4], tot = 0;
+      int cnt[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        int c = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) c += sl.hist[w][255 - 4 * lane - x];
-        cnt[x] = c;
-        tot += c;
+      for (int w = 0; w < NW; ++w) {
+        const int4 v = *reinterpret_cast<const int4*>(&hist[w][252 - 4 * lane]);
+        cnt[0] += v.w;
+        cnt[1] += v.z;
+        cnt[2] += v.y;
+        cnt[3] += v.x;
       }
-      int incl = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      int run = incl - tot;  // keys in higher digits
+      const int tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+      int run = wave_incl_scan(tot) - tot;  // keys in higher digits
+      int fd = -1, fr = 0;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         if (run < need && need <= run + cnt[x]) {
-          sl.pick[0] = 255 - 4 * lane - x;
-          sl.pick[1] = run;
+          fd = 255 - 4 * lane - x;
+          fr = run;
         }
         run += cnt[x];
       }
+      // exactly one lane found the digit
+      const int src = __builtin_ctzll(__ballot(fd >= 0));
+      digit = __builtin_amdgcn_readlane(fd, src);
+      above = __builtin_amdgcn_readlane(fr, src);
     }
-    __syncthreads();
-    prefix |= (uint32_t)sl.pick[0] << shift;
+    if constexpr (NB == 1) {
+      if (tid == 0) {
+        sl.pick[0] = digit;
+        sl.pick[1] = above;
+      }
+      __syncthreads();
+      digit = sl.pick[0];
+      above = sl.pick[1];
+    }
+    prefix |= (uint32_t)digit << shift;
     pmask |= 0xFFu << shift;
-    need -= sl.pick[1];
+    need -= above;
   }
   int gt = 0, eq = 0;
 #pragma unroll
