@@ -15,10 +15,12 @@
 // found with a wave-wide prefix sum.  With four waves every wave finds the
 // digit itself from histograms that alternate between two buffers, so a pass
 // has one barrier; with more waves wave 0 finds it and hands it over in LDS
-// (two barriers).  The threshold key is then exact; keys above it are taken,
-// and keys equal to it are taken in block order until the count is met.  One
-// scan of packed (greater, equal) counts gives each thread its output
-// position, so the output is ascending without a sort.
+// (two barriers).  The passes stop early once the keys under the prefix
+// found so far are exactly the ones still needed.  Keys above the threshold
+// (compared under the prefix's mask) are taken, and keys equal to it are taken
+// in block order until the count is met.  One scan of packed (greater, equal)
+// counts gives each thread its output position, so the output is ascending
+// without a sort.
 #pragma once
 
 #include "isb_device.h"
@@ -104,7 +106,7 @@ struct alignas(16) SelectLds {
   static constexpr int NB = NT <= 256 ? 2 : 1;
   int hist[NB][NT / 64][256];
   int wave_tot[NT / 64];
-  int pick[2];
+  int pick[3];
 };
 
 // The selection of one row whose scores for blocks E t .. E t + E - 1 are in
@@ -142,7 +144,7 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
     for (int i = 0; i < E; ++i)
       if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&hist[wave][(key[i] >> shift) & 0xFF], 1);
     __syncthreads();
-    int digit = 0, above = 0;
+    int digit = 0, above = 0, inside = 0;
     if (NB == 2 || wave == 0) {
       // lane l takes digits 255 - 4 l - x (x < 4): descending digit order
       int cnt[4] = {0, 0, 0, 0};
@@ -156,12 +158,13 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
       }
       const int tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
       int run = wave_incl_scan(tot) - tot;  // keys in higher digits
-      int fd = -1, fr = 0;
+      int fd = -1, fr = 0, fc = 0;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         if (run < need && need <= run + cnt[x]) {
           fd = 255 - 4 * lane - x;
           fr = run;
+          fc = cnt[x];
         }
         run += cnt[x];
       }
@@ -169,26 +172,32 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
       const int src = __builtin_ctzll(__ballot(fd >= 0));
       digit = __builtin_amdgcn_readlane(fd, src);
       above = __builtin_amdgcn_readlane(fr, src);
+      inside = __builtin_amdgcn_readlane(fc, src);
     }
     if constexpr (NB == 1) {
       if (tid == 0) {
         sl.pick[0] = digit;
         sl.pick[1] = above;
+        sl.pick[2] = inside;
       }
       __syncthreads();
       digit = sl.pick[0];
       above = sl.pick[1];
+      inside = sl.pick[2];
     }
     prefix |= (uint32_t)digit << shift;
     pmask |= 0xFFu << shift;
     need -= above;
+    // Every key under the prefix is taken: the lower digits cannot change
+    // the selection, so the passes stop (the keys compare under the mask).
+    if (inside == need) break;
   }
   int gt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     if (i < jlim) {
-      gt += key[i] > prefix;
-      eq += key[i] == prefix;
+      gt += (key[i] & pmask) > prefix;
+      eq += (key[i] & pmask) == prefix;
     }
   }
   const int packed = gt | (eq << 16);
@@ -198,8 +207,9 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     if (i < jlim && keep > 0) {
-      bool sel = key[i] > prefix;
-      if (key[i] == prefix) sel = seen++ < need;
+      const uint32_t mk = key[i] & pmask;
+      bool sel = mk > prefix;
+      if (mk == prefix) sel = seen++ < need;
       if (sel && pos < keep) put(pos++, E * tid + i);
     }
   }
