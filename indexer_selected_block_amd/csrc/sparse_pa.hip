@@ -45,9 +45,10 @@
 // 128-token MXFP4 pages are token-major (the page format of the MXFP4 cache).
 // K: lane (g, c) of tile t loads the 16 bytes of token 16 t + c that hold dims
 // 32 g .., and their e8m0 scale; with an e4m3 query the scaled MFMA multiplies
-// them as stored.  V: the wave copies its page to a wave-private LDS buffer;
-// lane (g, c) reads one 4-byte word per key, dims 8 c .. 8 c + 7, so row r of
-// V^T tile dt is dim 8 r + dt.
+// them as stored.  V: lane (g, c) loads, for each of its keys, the 4-byte
+// word that holds dims 8 c .. 8 c + 7, and for each tile the 16 bytes of
+// scales of its four keys, straight from the page, so row r of V^T tile dt is
+// dim 8 r + dt.
 //
 // Page loads are raw buffer loads from a wave-uniform descriptor of the page
 // (one offset register a wave, nontemporal: every page is read once).
@@ -593,7 +594,6 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
 template <int Q_DT>
 __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
   __shared__ WaveParts wp;
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[kPaWaves][kMxPageBytes];
   const int row = blockIdx.x, split = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -641,9 +641,16 @@ __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
       kd[tt] = bl16_nt(rk, 64 * c + 16 * g, 1024 * tt);
       ks[tt] = bl4_nt(rk, 4 * c, kMxDataBytes + 64 * tt);
     }
-    u32x4 vd[9];  // the V page: 8 KiB of data, then 512 B of scales (upper lanes read past it: zero)
+    // V: keys 16 tt + 4 g + e of tile tt, the word of dims 8 c .. 8 c + 7,
+    // and the four keys' scale words (one 16-byte load a tile)
+    uint32_t vw[8][4];
+    u32x4 vs[8];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) vd[i] = bl16_nt(rv, 16 * lane, 1024 * i);
+    for (int tt = 0; tt < 8; ++tt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vw[tt][e] = bl4_nt(rv, 64 * (4 * g + e) + 4 * c, 1024 * tt);
+      vs[tt] = bl16_nt(rv, 16 * g, kMxDataBytes + 64 * tt);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (Q_DT == ISB_FP8_E4M3) {
       if (c >= a.G) q8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -673,12 +680,6 @@ __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
       }
     }
     mx = max_over_groups(mx);
-    // The V page into this wave's LDS buffer (read back only by this wave,
-    // whose LDS operations complete in order).
-    uint8_t* sv = s_v[wave];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sv + 1024 * i + 16 * lane) = vd[i];
-    if (lane < 32) *reinterpret_cast<u32x4*>(sv + kMxDataBytes + 16 * lane) = vd[8];
     // Pass 2: probabilities and P.V.  Lane (g, c) takes keys 4 g + e of the
     // tile and dims 8 c .. 8 c + 7 (one data word, one scale byte per key);
     // MFMA dt gets dim 8 c + dt.
@@ -696,8 +697,9 @@ __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * tt + 4 * g + e;
         const bool on = tok < nvp;  // keys past the length may be poison: zero, unit scale
-        const uint32_t w = on ? *reinterpret_cast<const uint32_t*>(sv + 64 * tok + 4 * c) : 0u;
-        const float sc = on ? e8m0_to_f32(sv[kMxDataBytes + 4 * tok + (c >> 2)]) : 1.f;
+        const uint32_t w = on ? vw[tt][e] : 0u;
+        const uint32_t sw = vs[tt][e];
+        const float sc = on ? e8m0_to_f32((sw >> (8 * (c >> 2))) & 0xFFu) : 1.f;
         vv[e] = e2m1x8_to_bf16x8(w, sc);
       }
 #pragma unroll
