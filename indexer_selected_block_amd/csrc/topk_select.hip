@@ -177,6 +177,9 @@ __global__ __launch_bounds__(256) void topk_global_kernel(TopkArgs a) {
   if (threadIdx.x == 0) o[a.K - 1] = W;
 }
 
+// Widest rows whose block-table row the fused top-k + emit reads up front.
+constexpr int kBtLdsMaxBlocks = 2048;
+
 // Dynamic LDS of topk_reg_kernel, or 0 when the row does not fit.
 inline size_t topk_lds_bytes(int MB, int K, bool emit, bool bt_lds) {
   if (MB > 8192) return 0;
@@ -265,7 +268,10 @@ extern "C" int isb_topk_select_emit(isb_stream_t stream, const float* scores,
              pages_per_block};
   const unsigned rows = (unsigned)((long long)a.T * num_kv_heads);
   hipStream_t st = as_hip(stream);
-  size_t lds = topk_lds_bytes(max_blocks, top_k, true, true);
+  // The block-table row rides along with the scores when it is small; a wide
+  // row's table would double what each workgroup reads before it can select,
+  // so there only the selected blocks' entries are read, after the selection.
+  size_t lds = max_blocks <= kBtLdsMaxBlocks ? topk_lds_bytes(max_blocks, top_k, true, true) : 0;
   if (lds) {
     launch_reg<true, true>(a, rows, lds, st);
   } else if ((lds = topk_lds_bytes(max_blocks, top_k, true, false)) != 0) {

@@ -158,8 +158,8 @@ def test_emit_bit_exact(ppb, H_kv, q_len):
 
 # ------------------------------------------------------------------ fused top-k + emit
 # Widths cover each launch shape of the fused call: 256-thread rows with the
-# block-table row in LDS, 1024-thread rows with and without it, and rows too
-# wide for LDS (two launches).
+# block-table row in LDS, 1024-thread rows that read only the selected
+# entries of it, and rows too wide for LDS (two launches).
 @pytest.mark.parametrize("MB,R,q_len,H_kv,K,ppb", [(48, 24, 1, 1, 7, 8), (40, 19, 3, 2, 9, 1),
                                                    (512, 40, 1, 1, 16, 8), (3000, 6, 2, 1, 32, 8),
                                                    (8192, 4, 2, 1, 32, 8), (10000, 3, 1, 2, 16, 1),
