@@ -306,7 +306,11 @@ def main():
     names = ["index_score", "topk_select_emit", "sparse_pa_decode"]
 
     w0 = layers[0].w
-    alg, attended = algorithmic_bytes(w0, layers[0].sparse_ctx)
+    # the copies differ in lengths and selections: bytes are averaged over the
+    # copies the timed steps cycle through, like the durations
+    per_copy = [algorithmic_bytes(L.w, L.sparse_ctx) for L in layers]
+    alg = {k: sum(a[k] for a, _ in per_copy) / len(per_copy) for k in per_copy[0][0]}
+    attended = sum(x for _, x in per_copy) / len(per_copy)
     shas = kernel_sources_sha()
 
     def roof(kernel):
@@ -315,7 +319,7 @@ def main():
                 "frac": round(gbps / HBM_PEAK_GBPS, 4),
                 "traffic": stored_traffic(args.config, kernel, shas[kernel]),
                 "kernel": kernel, "avg_ms": round(dur_ms[kernel], 5),
-                "algorithmic_bytes": alg[kernel]}
+                "algorithmic_bytes": int(round(alg[kernel]))}
 
     dominant = max(names, key=lambda n: dur_ms[n])  # among the separate calls
     attn_gbps = attended / (dur_ms["sparse_pa_decode"] * 1e-3) / 1e9
@@ -347,7 +351,7 @@ def main():
         "roofline": roof(dominant),
         "roofline_sparse_pa_decode": roof("sparse_pa_decode"),
     }
-    result["measured_copy"] = {"at_attention_size": measured_copy(alg["sparse_pa_decode"]),
+    result["measured_copy"] = {"at_attention_size": measured_copy(int(alg["sparse_pa_decode"])),
                                "at_1GiB": measured_copy(1 << 30)}
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
