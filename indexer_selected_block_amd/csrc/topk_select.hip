@@ -17,8 +17,10 @@
 // output without a sort.
 //
 // Rows of up to 8192 blocks are read from HBM once, into registers, together
-// with the row's length (and, for the fused emit, its block-table row, into
-// LDS).  Wider rows use the same algorithm over global memory.
+// with the row's length (and, for the fused emit on rows of up to 2048
+// blocks, its block-table row, into LDS; wider rows read only the selected
+// entries of it, after the selection).  Wider rows use the same algorithm
+// over global memory.
 #include "isb_device.h"
 #include "isb_host.h"
 #include "select_device.h"
