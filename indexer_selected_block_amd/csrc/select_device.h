@@ -49,8 +49,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Inclusive prefix sum over the NT threads of the workgroup.
-template <int NT>
+// Inclusive prefix sum over the NT threads of the workgroup.  REUSE: s_wave
+// may be written again (by a later scan) before the caller's next barrier, so
+// the scan ends with one.
+template <int NT, bool REUSE = true>
 __device__ __forceinline__ int block_incl_scan(int v, int* s_wave) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int x = wave_incl_scan(v);
@@ -59,7 +61,7 @@ __device__ __forceinline__ int block_incl_scan(int v, int* s_wave) {
   int before = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) before += w < wave ? s_wave[w] : 0;
-  __syncthreads();
+  if constexpr (REUSE) __syncthreads();
   return x + before;
 }
 
@@ -201,7 +203,8 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
     }
   }
   const int packed = gt | (eq << 16);
-  const int before = block_incl_scan<NT>(packed, sl.wave_tot) - packed;
+  // one scan a call: its totals are not written again
+  const int before = block_incl_scan<NT, false>(packed, sl.wave_tot) - packed;
   int seen = before >> 16;
   int pos = (before & 0xFFFF) + min(seen, need);
 #pragma unroll
