@@ -291,17 +291,23 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    t_i = pass_ms([call_index])
-    t_it = pass_ms([call_index, call_topk])
-    t_ita = pass_ms([call_index, call_topk, call_attend])
-    t_step = pass_ms([call_index, call_select_attend])
+    # the four passes in turn, three times; each pass's median, so that one
+    # noisy pass does not move a difference
+    reps = {"i": [], "it": [], "ita": [], "step": []}
+    for _ in range(3):
+        reps["i"].append(pass_ms([call_index]))
+        reps["it"].append(pass_ms([call_index, call_topk]))
+        reps["ita"].append(pass_ms([call_index, call_topk, call_attend]))
+        reps["step"].append(pass_ms([call_index, call_select_attend]))
+    t_i, t_it, t_ita, t_step = (sorted(reps[k])[1] for k in ("i", "it", "ita", "step"))
     dur_ms = {"index_score": t_i, "topk_select_emit": t_it - t_i, "sparse_pa_decode": t_ita - t_it,
               "select_attend": t_step - t_i}
     # the same with one input copy: the attention's pages can stay in the
     # last-level cache from the step before (reported apart, never as value)
     all_layers = layers
     layers = layers[:1]
-    warm_attend = pass_ms([call_index, call_topk, call_attend]) - pass_ms([call_index, call_topk])
+    warm = [pass_ms([call_index, call_topk, call_attend]) - pass_ms([call_index, call_topk]) for _ in range(3)]
+    warm_attend = sorted(warm)[1]
     layers = all_layers
     names = ["index_score", "topk_select_emit", "sparse_pa_decode"]
 
@@ -346,7 +352,7 @@ def main():
         "attended_kv_pct_hbm_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 2),
         "step_launches": ["index_score", "select_attend"],
         "kernel_ms": {k: round(v, 5) for k, v in dur_ms.items()},
-        "kernel_ms_method": "differences of back-to-back passes of K steps ending after each call (HIP events)",
+        "kernel_ms_method": "differences of back-to-back passes of K steps ending after each call (HIP events; median of 3 rounds)",
         "sparse_pa_decode_ms_one_input_copy": round(warm_attend, 5),
         "roofline": roof(dominant),
         "roofline_sparse_pa_decode": roof("sparse_pa_decode"),
