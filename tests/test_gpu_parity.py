@@ -317,6 +317,29 @@ def test_sparse_pa_variants(variant):
     assert err <= tol, f"max |err| {err:.4g} > {tol:.4g}"
 
 
+# Any row count: the split plan gives small batches many splits a row (every
+# page in flight at once) and large ones a single split; the counts cross the
+# plan's steps (512 resident workgroups) and leave ragged final rounds.
+@pytest.mark.parametrize("reqs", [1, 2, 5, 33, 129, 257, 511, 700])
+def test_sparse_pa_row_counts(reqs):
+    cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=reqs, ctx_lo=200, ctx_hi=5000,
+                    pool_blocks=reqs * 40 + 64, top_k=8)
+    _say(f"[sparse_pa rows] {reqs} rows")
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    sbt, sctx = _synthetic_table(hi, 31 + reqs)
+    ref = oracle_attention(hi, sbt, sctx)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all(), "NaN in attention output (poison read?)"
+    tol = attn_tol(cfg.kv_dtype, attended_vmax(hi, sbt, sctx))
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"max |err| {err:.4g} > {tol:.4g}"
+
+
 def test_sparse_pa_every_block_is_dense_attention():
     # top-k >= every row's block count: the sparse decode is dense causal attention.
     cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=4, ctx_lo=100, ctx_hi=2000, top_k=16)
