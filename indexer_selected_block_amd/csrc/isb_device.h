@@ -70,13 +70,6 @@ __device__ __forceinline__ bf16x2 e4m3x2_to_bf16x2(uint32_t w, bool hi) {
             : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
 }
 
-// Four e4m3 bytes of one dword -> four bf16 (byte 0 first).
-__device__ __forceinline__ bf16x4 e4m3x4_to_bf16x4(uint32_t w) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-  return bf16x4{a[0], a[1], b[0], b[1]};
-}
-
 // Eight e4m3 bytes (dword lo: bytes 0..3, then dword hi) -> eight bf16.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);

@@ -267,22 +267,6 @@ __device__ __forceinline__ void load_v16(PageRegs<KV_DT>& pr, __amdgpu_buffer_rs
   for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] = bl16_nt(vpage, 1024 * h + 16 * lane, 0);
 }
 
-template <int KV_DT>
-__device__ __forceinline__ void page16_operands_v(const PageRegs<KV_DT>& pr, bf16x4 (&vt)[8]) {
-  if constexpr (KV_DT == ISB_BF16) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        vt[2 * h + q] = __builtin_bit_cast(bf16x4, u32x2{pr.v[h][2 * q], pr.v[h][2 * q + 1]});
-  } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) vt[4 * h + q] = e4m3x4_to_bf16x4(pr.v[h][q]);
-  }
-}
-
 // Keys at or past nvalid in a page may hold anything (0 x NaN would poison
 // the sum), so their raw V bytes are cleared before conversion.  Lane
 // (g, c) holds keys 4 g .. 4 g + 3: one byte each per fp8 dword, two keys per
@@ -346,6 +330,7 @@ template <int KV_DT, int Q_DT, int RUN, typename IdFn>
 __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, int row, int split, int kvh,
                                                int n_tok, bf16x8 (&qb)[4], int my_ids, IdFn ids,
                                                __bf16* out_row) {
+  static_assert(RUN % 2 == 0, "P.V takes the pages of a run in pairs");
   constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
   constexpr int ROUND = 4 * RUN;    // pages of a round
   constexpr int IDS = 64 / RUN;     // rounds whose page ids one id fetch holds
@@ -440,36 +425,22 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, i
     M = m_new;
     // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
     // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
-    if constexpr (RUN == 1) {
-      float p[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(z[0][e] - M);
-        lsum += p[e];
-      }
-      const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-      bf16x4 vt[8];
-      page16_operands_v<KV_DT>(pr[0], vt);
+    for (int j = 0; j < RUN; j += 2) {
+      if (j < cnt) {
+        bf16x8 pb;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] = mfma_16x16x16_bf16(vt[dt], pb, o[dt]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < RUN; j += 2) {
-        if (j < cnt) {
-          bf16x8 pb;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
-            const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
-            lsum += p0v + p1v;
-            pb[e] = (__bf16)p0v;
-            pb[4 + e] = (__bf16)p1v;
-          }
-          if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            o[dt] = mfma_16x16x32_bf16(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
+        for (int e = 0; e < 4; ++e) {
+          const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
+          const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
+          lsum += p0v + p1v;
+          pb[e] = (__bf16)p0v;
+          pb[4 + e] = (__bf16)p1v;
         }
+        if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          o[dt] = mfma_16x16x32_bf16(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
       }
     }
   }
