@@ -2,8 +2,10 @@
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -45,5 +47,61 @@ def build_library(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+_MFMA = re.compile(r"^\s*(v_mfma\S*)\s+(.*)$")
+
+
+def _reg_range(tok: str):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return m.group(1), int(m.group(2)), int(m.group(3))
+    m = re.match(r"([va])(\d+)$", tok)
+    if m:
+        return m.group(1), int(m.group(2)), int(m.group(2))
+    return None
+
+
+def mfma_operand_overlaps(asm: str) -> list:
+    """MFMA instructions of gfx950 assembly whose destination registers overlap
+    a source operand other than an identical accumulator (the register
+    allocator has placed the scaled fp4 MFMA's destination over a source,
+    which corrupts the product)."""
+    bad = []
+    for line in asm.splitlines():
+        m = _MFMA.match(line)
+        if not m:
+            continue
+        ops = [o.strip() for o in m.group(2).split(",")]
+        d = _reg_range(ops[0])
+        for k, src in enumerate(_reg_range(o) for o in ops[1:4]):
+            if not d or not src or src[0] != d[0]:
+                continue
+            overlap = not (src[2] < d[1] or src[1] > d[2])
+            if overlap and not (k == 2 and src[1:] == d[1:]):
+                bad.append(line.strip())
+    return bad
+
+
+def check_mfma_operands() -> int:
+    """Compiles every source to gfx950 assembly and raises if any MFMA
+    destination overlaps a source; returns the number of MFMAs checked."""
+    total = 0
+    with tempfile.TemporaryDirectory() as tmp:
+        for src in SOURCES:
+            out = os.path.join(tmp, src + ".s")
+            flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+            cmd = [hipcc(), *flags, "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC,
+                   os.path.join(CSRC, src), "-o", out]
+            proc = subprocess.run(cmd, capture_output=True, text=True)
+            if proc.returncode != 0:
+                raise RuntimeError(f"hipcc -S {src} failed ({proc.returncode}):\n{proc.stderr}")
+            asm = open(out).read()
+            total += sum(1 for line in asm.splitlines() if _MFMA.match(line))
+            bad = mfma_operand_overlaps(asm)
+            if bad:
+                raise RuntimeError(f"{src}: MFMA destination overlaps a source:\n" + "\n".join(bad[:10]))
+    return total
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(f"checked {check_mfma_operands()} MFMA instructions: no operand overlap")

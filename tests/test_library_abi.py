@@ -109,3 +109,16 @@ def test_binding_refuses_cpu_tensors(lib):
     import torch
     with pytest.raises(RuntimeError, match="ROCm GPU"):
         binding.topk_select(torch.zeros(1, 1, 4), torch.ones(1, dtype=torch.int32), 1, 2)
+
+
+def test_mfma_overlap_check_reads_register_ranges():
+    # The build's assembly check: a destination over a source is caught, an
+    # accumulator identical to the destination is not.
+    from indexer_selected_block_amd.build import mfma_operand_overlaps
+    ok = "  v_mfma_f32_16x16x32_bf16 v[4:7], v[8:11], v[12:15], v[4:7]"
+    clash = "  v_mfma_scale_f32_16x16x128_f8f6f4 v[0:3], v[2:9], v[12:19], v[0:3], v20, v21"
+    clash_b = "  v_mfma_f32_16x16x16_bf16 a[0:3], v[0:1], a[2:3], a[0:3]"
+    assert mfma_operand_overlaps(ok) == []
+    assert mfma_operand_overlaps(clash) == [clash.strip()]
+    assert mfma_operand_overlaps(clash_b) == [clash_b.strip()]
+    assert mfma_operand_overlaps("\n".join([ok, clash])) == [clash.strip()]
