@@ -43,6 +43,26 @@ struct ScoreArgs {
 };
 
 constexpr int kScoreWaves = 4;        // waves (blocks) per workgroup
+
+// Column group of request r taken by workgroup column p of gx, for workgroups
+// of BPW blocks.  Workgroups are dealt round-robin to the eight dies (XCDs),
+// each with its own L2.  This mapping hands each die whole 32-block spans (one
+// 128-byte line of a score row), so the workgroups that write a line share an
+// L2, which merges their 4- and 8-byte writes before the line goes to HBM
+// (spread over eight L2s, each partial line was written back on its own).
+// The spans rotate over the dies from request to request: the spans past a
+// short request's end hold no keys, and a fixed span-to-die map would leave
+// the dies that own the last spans idle.  Any mapping is correct; this one
+// only places the work.
+template <int BPW>
+__device__ __forceinline__ int score_column(int p, int gx, int r) {
+  constexpr int LW = 32 / BPW;  // workgroups per span
+  const int full = gx / (8 * LW) * (8 * LW);
+  if (p >= full) return p;
+  const int k = p & 7, q = p >> 3;
+  const int j = q / LW, w = q % LW;
+  return LW * (8 * j + ((k + r) & 7)) + w;
+}
 constexpr int kMaxQueryRows = 64;     // q_len * H_idx
 
 template <int Q_DT>
@@ -130,7 +150,7 @@ __global__ __launch_bounds__(256) void index_stream_kernel(ScoreArgs a) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const int r = blockIdx.y;
-  const int b0 = (blockIdx.x * kScoreWaves + wave) * NB;
+  const int b0 = (score_column<kScoreWaves * NB>(blockIdx.x, gridDim.x, blockIdx.y) * kScoreWaves + wave) * NB;
   if (b0 >= a.MB) return;
   const int L = a.seq_lens[r];
   const int nr = (L + kBlockTokens - 1) / kBlockTokens;
@@ -342,7 +362,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a) {
   __shared__ int s_nvalid[kScoreWaves][16];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int r = blockIdx.y;
-  const int b = blockIdx.x * kScoreWaves + wave;
+  const int b = score_column<kScoreWaves>(blockIdx.x, gridDim.x, blockIdx.y) * kScoreWaves + wave;
   if (b >= a.MB) return;
   const int L = a.seq_lens[r];
   const int nr = (L + kBlockTokens - 1) / kBlockTokens;
