@@ -122,3 +122,17 @@ def test_mfma_overlap_check_reads_register_ranges():
     assert mfma_operand_overlaps(clash) == [clash.strip()]
     assert mfma_operand_overlaps(clash_b) == [clash_b.strip()]
     assert mfma_operand_overlaps("\n".join([ok, clash])) == [clash.strip()]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # The path has no multi-GPU part: bench.py --gpus N > 1 says so and exits
+    # before touching a device.
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    proc = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    msg = json.loads(proc.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
