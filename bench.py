@@ -101,7 +101,11 @@ def measured_copy(nbytes_moved):
 
 
 def algorithmic_bytes(w, sparse_ctx):
-    """Bytes each kernel must move for this batch (Measurement)."""
+    """Bytes each kernel must move for this batch: the index keys of every
+    request once, the queries, the table entries and lengths read, the scores,
+    selection, page table and outputs written; for the attention the K and V
+    bytes of the attended positions.  Split partials and re-reads are not
+    counted."""
     cfg = w.cfg
     lens = w.seq_lens.cpu().tolist()
     ql, T = cfg.query_len, cfg.num_tokens
@@ -213,7 +217,8 @@ def main():
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the path has no "
-                                   "multi-GPU part (see DESIGN.md for how it would shard)",
+                                   "multi-GPU part (rows are independent; each GPU would run "
+                                   "it on its own requests)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

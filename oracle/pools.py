@@ -16,7 +16,7 @@ Pool layout read here (its own code; it shares nothing with the GPU path):
 * K/V cache, bf16 / fp8 - 16-token pages, 8 per 128-token block
   (vLLM API page for ``sparse_attention_msa``: the page-16 rebase of the block
   table and the stride check over the pages of a sparse block).  Within a
-  page the element order is this build's own (the sources show only that a
+  page the element order is this library's own (the sources show only that a
   16-token page is sub-tiled for the kernel, vLLM PR 61889, Validation, the
   K [.., 8, 16, 16] and V [.., 1, 128, 16] shapes).  With e = bytes per element:
     K: key c, dim d at byte 1024 ((d mod 32) div (16/e)) + 256 (d div 32)
