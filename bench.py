@@ -131,6 +131,29 @@ def algorithmic_bytes(w, sparse_ctx):
     return {"index_score": score, "topk_select_emit": topk_emit, "sparse_pa_decode": attn}, attended
 
 
+def index_flops(w):
+    """Multiply-adds (x2) the scorer must do: each index query row against each
+    of its token's causally valid keys, 128 dims."""
+    cfg = w.cfg
+    ql = cfg.query_len
+    tok_keys = sum(max(0, L - (ql - 1 - i)) for L in w.seq_lens.cpu().tolist() for i in range(ql))
+    return 2 * 128 * cfg.num_idx_heads * tok_keys
+
+
+def scorer_is_wide(cfg):
+    """More than 16 tokens or 64 index query rows a request: the scorer that
+    holds a block's keys in registers and runs them against 16-row query tiles
+    on MFMA (prefill chunks); its bound is the MFMA rate, not HBM."""
+    return cfg.query_len > 16 or cfg.query_len * cfg.num_idx_heads > 64
+
+
+# dense MFMA peaks of MI355X (TFLOP/s) for the scorer's operand types: bf16
+# operands (bf16 / fp8 keys converted to bf16, or MXFP4 keys with a bf16 query),
+# or MXFP4 keys with an e4m3 query on the scaled fp8/fp4 instruction (fp8 rate)
+def mfma_peak_tflops(cfg):
+    return 5000.0 if (cfg.idx_dtype == "mxfp4" and cfg.qidx_dtype == "e4m3") else 2500.0
+
+
 def kernel_sources_sha():
     """Hash of each kernel's source file, to tell whether stored counters still apply."""
     csrc = os.path.join(ROOT, "indexer_selected_block_amd", "csrc")
@@ -324,7 +347,17 @@ def main():
     attended = sum(x for _, x in per_copy) / len(per_copy)
     shas = kernel_sources_sha()
 
+    flops = sum(index_flops(L.w) for L in layers) / len(layers)
+
     def roof(kernel):
+        if kernel == "index_score" and scorer_is_wide(cfg):
+            tflops = flops / (dur_ms[kernel] * 1e-3) / 1e12
+            peak = mfma_peak_tflops(cfg)
+            return {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4),
+                    "traffic": stored_traffic(args.config, kernel, shas[kernel]),
+                    "kernel": kernel, "avg_ms": round(dur_ms[kernel], 5),
+                    "algorithmic_flops": int(round(flops)), "algorithmic_bytes": int(round(alg[kernel]))}
         gbps = alg[kernel] / (dur_ms[kernel] * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4),
@@ -362,6 +395,8 @@ def main():
         "roofline": roof(dominant),
         "roofline_sparse_pa_decode": roof("sparse_pa_decode"),
     }
+    if dominant != "index_score":
+        result["roofline_index_score"] = roof("index_score")
     result["measured_copy"] = {"at_attention_size": measured_copy(int(alg["sparse_pa_decode"])),
                                "at_1GiB": measured_copy(1 << 30)}
     if args.cpu_seconds > 0:

@@ -124,9 +124,14 @@ ISB_API const char* isb_strerror(int status);
  *                request's ceil(seq_len/128) blocks are never read
  *   seq_lens     [num_reqs] int32, each <= 128 * min(max_blocks, stride)
  *   scores       out, [num_kv_heads][T][max_blocks] fp32
+ * decode_query_len may be a prefill chunk: up to 16 tokens and 64 query rows
+ * (decode_query_len * num_idx_heads) a request take the decode kernels; more
+ * take a kernel that holds a block's keys in registers and runs them against
+ * up to 128 query rows a wave, which needs num_idx_heads to divide 16.
  * Shape errors: num_idx_heads % num_kv_heads != 0, max_blocks > stride,
- * decode_query_len > 16, decode_query_len * num_idx_heads > 64,
- * num_reqs > 65535.
+ * more than 16 tokens or 64 rows with 16 % num_idx_heads != 0,
+ * decode_query_len * num_idx_heads > 2^20, num_reqs * decode_query_len
+ * > 2^31 - 1, num_reqs > 65535.
  */
 ISB_API int isb_index_score(isb_stream_t stream,
                     const void* q_idx, int q_idx_dtype, int num_idx_heads,

@@ -20,7 +20,14 @@
 //              multiplied on v_mfma_f32_16x16x32_bf16, 16 keys x 16 rows a tile;
 //   * fp4    - MXFP4 keys with an e4m3 query: v_mfma_scale_f32_16x16x128_f8f6f4
 //              consumes the e2m1 data and its e8m0 scales directly, one
-//              instruction per 16 keys x 16 rows x 128 dims.
+//              instruction per 16 keys x 16 rows x 128 dims;
+//   * wide   - many query rows (a chunk of prefill tokens, more than 16 tokens
+//              or 64 rows): a wave loads its block's keys once, keeps them in
+//              registers and runs them against up to kWideTiles 16-row query
+//              tiles (the grid's third dimension takes the rest), with the
+//              MFMA of the key type above; each row's causal length is
+//              computed in the loop, and the index heads of a KV group are
+//              summed across the lanes that hold them.
 // bf16 / fp8 index pages are eight 16-key tiles in the lane order of the K
 // pages (chunk h of lane l = 16 g + m at byte 1024 h + 16 l of the tile holds
 // key m's dims 32 g + (16 / esize) h ...), so each load instruction reads one
@@ -63,7 +70,8 @@ __device__ __forceinline__ int score_column(int p, int gx, int r) {
   const int j = q / LW, w = q % LW;
   return LW * (8 * j + ((k + r) & 7)) + w;
 }
-constexpr int kMaxQueryRows = 64;     // q_len * H_idx
+constexpr int kMaxQueryRows = 64;     // q_len * H_idx of the tile / stream variants
+constexpr long long kMaxWideRows = 1 << 20;  // q_len * H_idx of the wide variant
 
 template <int Q_DT>
 __device__ __forceinline__ bf16x8 load_q8(const uint8_t* row, int dim0) {
@@ -353,6 +361,184 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, __amdgpu_buf
   return nan ? qnan() : best;
 }
 
+// ----------------------------------------------------------------- wide
+// Query tiles (16 rows each) a wave of the wide variant runs its block against.
+constexpr int kWideTiles = 8;
+
+// Key tiles of a block held in registers at once by the wide variant: four
+// of the eight for fp8 keys (one tile's operand is converted at a time), two
+// for bf16 keys (with four the compiler copies them through scratch), the
+// whole block for MXFP4 (40 registers).
+template <int KEY_DT>
+constexpr int wide_part_tiles() { return KEY_DT == ISB_MXFP4 ? 8 : KEY_DT == ISB_FP8_E4M3 ? 4 : 2; }
+
+template <int KEY_DT>
+struct PartKeys {
+  TileRegs<KEY_DT> t[wide_part_tiles<KEY_DT>()];
+};
+template <>
+struct PartKeys<ISB_MXFP4> {
+  u32x4 data[8];    // key m of tile tt, dims 32 g .. 32 g + 31 (e2m1)
+  uint32_t scl[8];  // key m's four e8m0 scales
+};
+
+template <int KEY_DT>
+__device__ __forceinline__ void load_part_keys(PartKeys<KEY_DT>& k, __amdgpu_buffer_rsrc_t page, int part,
+                                               int lane) {
+  if constexpr (KEY_DT == ISB_MXFP4) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      k.data[tt] = bl16_nt(page, 64 * m + 16 * g, 1024 * tt);
+      k.scl[tt] = bl4_nt(page, 4 * m, kMxDataBytes + 64 * tt);
+    }
+  } else {
+    constexpr int TB = KEY_DT == ISB_BF16 ? 4096 : 2048;
+    constexpr int NT = wide_part_tiles<KEY_DT>();
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) load_tile<KEY_DT>(k.t[tt], page, (part * NT + tt) * TB, lane);
+  }
+}
+
+// Folds the keys of one part into the running maximum `best` of query row n
+// (lane (g, m) of a 16-row tile holds keys 4 g + e of row m); keys at or past
+// nv (the row's causally valid keys in this block) do not count, a NaN
+// product among the valid ones sets `nan`.
+template <int KEY_DT, int Q_DT>
+__device__ __forceinline__ void wide_part_max(const ScoreArgs& a, const PartKeys<KEY_DT>& k, int part, int r,
+                                              int nq, int nv, int lane, float& best, bool& nan) {
+  constexpr int NT = wide_part_tiles<KEY_DT>();
+  const int g = lane >> 4;
+  const int i = nq / a.H_idx, h = nq % a.H_idx;
+  if constexpr (KEY_DT == ISB_MXFP4 && Q_DT == ISB_FP8_E4M3) {
+    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim;
+    const u32x4 lo = ld16(qrow + 16 * g);
+    const u32x4 hi = ld16(qrow + 64 + 16 * g);
+    const i32x8 qb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const i32x8 ka = {(int)k.data[tt][0], (int)k.data[tt][1], (int)k.data[tt][2], (int)k.data[tt][3], 0, 0, 0, 0};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_scale_fp4_e4m3(ka, qb, acc, (int)((k.scl[tt] >> (8 * g)) & 0xFFu));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (16 * tt + 4 * g + e < nv) {
+          nan |= acc[e] != acc[e];
+          best = fmaxf(best, acc[e]);
+        }
+      }
+    }
+  } else {
+    constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
+    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim * QB;
+    bf16x8 qb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = load_q8<Q_DT>(qrow, 32 * g + 8 * j);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (KEY_DT == ISB_MXFP4) {
+        const float sc = e8m0_to_f32(k.scl[tt] >> (8 * g));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma_16x16x32_bf16(e2m1x8_to_bf16x8(k.data[tt][j], sc), qb[j], acc);
+      } else {
+        bf16x8 kb[4];
+        tile_operand<KEY_DT>(k.t[tt], kb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma_16x16x32_bf16(kb[j], qb[j], acc);
+      }
+      const int key0 = 16 * (part * NT + tt) + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (key0 + e < nv) {
+          nan |= acc[e] != acc[e];
+          best = fmaxf(best, acc[e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// grid (ceil(MB / 4), R, ceil(QR / (16 kWideTiles))), 4 waves a workgroup:
+// wave w scores block 4 x + w of request y for query rows
+// [16 kWideTiles z, 16 kWideTiles (z + 1)).  Needs 16 % H_idx == 0, so a
+// 16-row tile holds whole tokens (row n = token n / H_idx, head n % H_idx)
+// and each KV group's index heads sit on adjacent lanes.
+template <int KEY_DT, int Q_DT>
+__global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
+  constexpr int NT = wide_part_tiles<KEY_DT>();
+  constexpr int PARTS = 8 / NT;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int m = lane & 15;
+  const int r = blockIdx.y;
+  const int b = score_column<kScoreWaves>(blockIdx.x, gridDim.x, blockIdx.y) * kScoreWaves + wave;
+  if (b >= a.MB) return;
+  const int QR = a.q_len * a.H_idx;
+  const int n0 = 16 * kWideTiles * blockIdx.z;   // first query row of this wave
+  const int n1 = min(QR, n0 + 16 * kWideTiles);  // one past the last
+  const int per = a.H_idx / a.H_kv;               // index heads of a KV group
+  const int T = a.R * a.q_len;
+  const int L = a.seq_lens[r];
+  const int nr = (L + kBlockTokens - 1) / kBlockTokens;
+  if (b >= nr) {  // no token of the request reaches this block
+    const int i0 = n0 / a.H_idx, i1 = n1 / a.H_idx;
+    for (int x = lane; x < (i1 - i0) * a.H_kv; x += kWave) {
+      const int i = i0 + x / a.H_kv, gg = x % a.H_kv;
+      a.scores[((size_t)gg * T + (size_t)r * a.q_len + i) * a.MB + b] = neg_inf();
+    }
+    return;
+  }
+  const int64_t blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r * a.bt_stride + b]);
+  // an out-of-range block id is poison: NaN where the block is causally
+  // visible, -inf elsewhere; nothing is read through it
+  const bool bad = blk < 0 || blk >= a.pool_blocks;
+  constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
+  const __amdgpu_buffer_rsrc_t page = page_rsrc(a.pool + (bad ? 0 : blk) * PB, (int)PB);
+  // row n = n0 + 16 q + m of each tile q: its causally valid keys in this block
+  float best[kWideTiles];
+  bool nan[kWideTiles];
+  int nv[kWideTiles];
+#pragma unroll
+  for (int q = 0; q < kWideTiles; ++q) {
+    const int n = n0 + 16 * q + m;
+    const int v = n < n1 ? causal_len(L, a.q_len, n / a.H_idx) - b * kBlockTokens : 0;
+    nv[q] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
+    best[q] = neg_inf();
+    nan[q] = false;
+  }
+#pragma unroll
+  for (int part = 0; part < PARTS; ++part) {
+    PartKeys<KEY_DT> keys;
+    load_part_keys<KEY_DT>(keys, page, part, lane);
+#pragma unroll
+    for (int q = 0; q < kWideTiles; ++q) {
+      const int n = n0 + 16 * q + m;
+      if (n0 + 16 * q < n1)  // wave-uniform: the tile has rows
+        wide_part_max<KEY_DT, Q_DT>(a, keys, part, r, n < n1 ? n : n0, nv[q], lane, best[q], nan[q]);
+      // one query tile's operands at a time (hoisting the next tiles' query
+      // loads would push the keys out of registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kWideTiles; ++q) {
+    const int n = n0 + 16 * q + m;
+    if (n0 + 16 * q >= n1) continue;  // wave-uniform
+    float s = max_over_groups(best[q]);
+    if ((__ballot(nan[q]) >> m & 0x0001000100010001ull) != 0) s = qnan();
+    if (bad) s = nv[q] > 0 ? qnan() : neg_inf();
+    // sum the group's heads: rows n .. n + per - 1 sit on adjacent lanes
+    for (int off = 1; off < per; off <<= 1) s += shfl_xor_f32(s, off);
+    if (KEY_DT == ISB_FP8_E4M3) s *= a.idx_scale;
+    const int h = n % a.H_idx;
+    if (lane < 16 && n < n1 && h % per == 0) {
+      const int i = n / a.H_idx, gg = h / per;
+      a.scores[((size_t)gg * T + (size_t)r * a.q_len + i) * a.MB + b] = s;
+    }
+  }
+}
+
 // ----------------------------------------------------------------- kernel
 // grid (ceil(MB / 4), R), 4 waves a workgroup, wave w scores block 4 x + w.
 template <int VARIANT, int KEY_DT, int Q_DT>
@@ -411,7 +597,18 @@ static void launch(const ScoreArgs& a, hipStream_t st) {
 }
 
 template <int KEY_DT, int Q_DT>
-static void launch_key(const ScoreArgs& a, bool one_row, hipStream_t st) {
+static void launch_wide(const ScoreArgs& a, hipStream_t st) {
+  const int QR = a.q_len * a.H_idx;
+  const dim3 grid((a.MB + kScoreWaves - 1) / kScoreWaves, a.R, (QR + 16 * kWideTiles - 1) / (16 * kWideTiles));
+  hipLaunchKernelGGL((index_wide_kernel<KEY_DT, Q_DT>), grid, dim3(256), 0, st, a);
+}
+
+template <int KEY_DT, int Q_DT>
+static void launch_key(const ScoreArgs& a, bool one_row, bool wide, hipStream_t st) {
+  if (wide) {
+    launch_wide<KEY_DT, Q_DT>(a, st);
+    return;
+  }
   if constexpr (KEY_DT == ISB_MXFP4) {
     if constexpr (Q_DT == ISB_FP8_E4M3) launch<2, KEY_DT, Q_DT>(a, st);
     else launch<1, KEY_DT, Q_DT>(a, st);
@@ -436,7 +633,13 @@ extern "C" int isb_index_score(isb_stream_t stream, const void* q_idx, int q_idx
     return ISB_E_INVALID_ARG;
   if (!is_query_dtype(q_idx_dtype) || !is_pool_dtype(idx_dtype)) return ISB_E_UNSUPPORTED_DTYPE;
   if (num_idx_heads % num_kv_heads != 0 || max_blocks > block_table_stride) return ISB_E_SHAPE;
-  if (decode_query_len > 16 || decode_query_len * num_idx_heads > kMaxQueryRows) return ISB_E_SHAPE;
+  // up to 16 tokens and 64 query rows a request: the tile / stream variants;
+  // more (a prefill chunk): the wide variant, whose 16-row tiles must hold
+  // whole tokens
+  const long long QR = (long long)decode_query_len * num_idx_heads;
+  const bool wide = decode_query_len > 16 || QR > kMaxQueryRows;
+  if (wide && (16 % num_idx_heads != 0 || QR > kMaxWideRows)) return ISB_E_SHAPE;
+  if ((long long)num_reqs * decode_query_len > 0x7FFFFFFFLL) return ISB_E_SHAPE;
   if (num_reqs > 65535) return ISB_E_SHAPE;
   if (!(idx_scale > 0.f) && idx_dtype == ISB_FP8_E4M3) return ISB_E_INVALID_ARG;
   ScoreArgs a{(const uint8_t*)q_idx, (const uint8_t*)idx_pool, block_table, seq_lens, scores,
@@ -446,14 +649,14 @@ extern "C" int isb_index_score(isb_stream_t stream, const void* q_idx, int q_idx
   const bool one_row = decode_query_len * num_idx_heads == 1;
   const bool qb = q_idx_dtype == ISB_BF16;
   if (idx_dtype == ISB_MXFP4) {
-    if (qb) launch_key<ISB_MXFP4, ISB_BF16>(a, one_row, st);
-    else launch_key<ISB_MXFP4, ISB_FP8_E4M3>(a, one_row, st);
+    if (qb) launch_key<ISB_MXFP4, ISB_BF16>(a, one_row, wide, st);
+    else launch_key<ISB_MXFP4, ISB_FP8_E4M3>(a, one_row, wide, st);
   } else if (idx_dtype == ISB_FP8_E4M3) {
-    if (qb) launch_key<ISB_FP8_E4M3, ISB_BF16>(a, one_row, st);
-    else launch_key<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, one_row, st);
+    if (qb) launch_key<ISB_FP8_E4M3, ISB_BF16>(a, one_row, wide, st);
+    else launch_key<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, one_row, wide, st);
   } else {
-    if (qb) launch_key<ISB_BF16, ISB_BF16>(a, one_row, st);
-    else launch_key<ISB_BF16, ISB_FP8_E4M3>(a, one_row, st);
+    if (qb) launch_key<ISB_BF16, ISB_BF16>(a, one_row, wide, st);
+    else launch_key<ISB_BF16, ISB_FP8_E4M3>(a, one_row, wide, st);
   }
   return launch_status();
 }

@@ -139,6 +139,16 @@ CONFIGS: dict[str, Config] = {
         idx_dtype="mxfp4", kv_dtype="fp8", q_dtype="bf16", qidx_dtype="e4m3",
         pool_blocks=890768 // 8, key_dist="student_t3", seed=5,
         description="8 requests x 2 tokens, 1048576-token contexts, fp8 K/V, MXFP4 index, top-k 32"),
+    # Chunked prefill: the last 512 tokens of each request are the query chunk,
+    # each token with its own causal top-k (the decode formulas with
+    # decode_query_len = 512); otherwise the fp8 decode workload's setup.
+    "prefill": Config(
+        "prefill", num_reqs=4, query_len=512, ctx_lo=16384, ctx_hi=65536, num_pad_reqs=0,
+        num_kv_heads=1, num_q_heads=16, num_idx_heads=1, top_k=16,
+        idx_dtype="fp8", kv_dtype="fp8", q_dtype="bf16", qidx_dtype="bf16",
+        pool_blocks=4 * 512 + 64, key_dist="normal", seed=6,
+        description="4 requests x 512-token prefill chunks, contexts U{16384..65536}, fp8 K/V and index, "
+                    "top-k 16 per token"),
 }
 
 

@@ -2,6 +2,8 @@
 tolerances, and per-request sampling of full-size workloads."""
 from __future__ import annotations
 
+from dataclasses import replace
+
 import numpy as np
 import torch
 
@@ -26,6 +28,11 @@ def small_configs():
         "spec_decode": wl.shrink(c["spec_decode"], num_reqs=6, ctx_lo=300, ctx_hi=3000, num_pad_reqs=2),
         "mxfp4": wl.shrink(c["mxfp4"], num_reqs=3, ctx_lo=900, ctx_hi=3000),
         "long_context": wl.shrink(c["long_context"], num_reqs=2, ctx_lo=5000, ctx_hi=9000),
+        # prefill chunks (more than 16 tokens or 64 index rows: the wide scorer),
+        # each with a ragged last query tile, for every index key type
+        "prefill": replace(wl.shrink(c["prefill"], num_reqs=2, ctx_lo=600, ctx_hi=3000), query_len=150),
+        "prefill_mxfp4": replace(wl.shrink(c["mxfp4"], num_reqs=2, ctx_lo=900, ctx_hi=2500), query_len=37),
+        "prefill_bf16": replace(c["tiny_bf16"], name="prefill_bf16", query_len=70, ctx_lo=700, ctx_hi=1024),
     }
 
 

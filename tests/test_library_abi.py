@@ -74,7 +74,12 @@ def test_argument_checks_return_before_any_launch(lib):
     assert lib.isb_topk_select_emit(NULL, p, p, 1, 1, 1, 4, 2, p, 4, 4, p, p, p) == -3            # ppb 4
     assert lib.isb_topk_select_emit(NULL, p, p, 1, 1, 1, 8, 2, p, 4, 8, p, p, p) == -3            # MB > stride
     assert lib.isb_topk_select_emit(NULL, p, p, 1, 1, 1, 4, 5, p, 4, 8, p, p, p) == -3            # K > MB
-    assert lib.isb_index_score(NULL, p, 0, 1, p, 0, 1.0, 1, p, 4, p, 1, 17, 1, 4, p) == -3      # q > 16
+    # more than 16 tokens or 64 query rows take the wide scorer, whose 16-row
+    # tiles must hold whole tokens: 16 % H_idx == 0
+    assert lib.isb_index_score(NULL, p, 0, 3, p, 0, 1.0, 1, p, 4, p, 1, 17, 1, 4, p) == -3      # q 17, H_idx 3
+    assert lib.isb_index_score(NULL, p, 0, 3, p, 0, 1.0, 1, p, 4, p, 1, 22, 3, 4, p) == -3      # 66 rows, H_idx 3
+    assert lib.isb_index_score(NULL, p, 0, 16, p, 0, 1.0, 1, p, 4, p, 1, 65537, 1, 4, p) == -3  # rows > 2^20
+    assert lib.isb_index_score(NULL, p, 0, 1, p, 0, 1.0, 1, p, 4, p, 65535, 40000, 1, 4, p) == -3  # T > 2^31-1
     assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 8, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,
                                  16, 0.1, p, 1 << 20, p, p, p, p) == -3                          # MB > stride
     assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 4, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,

@@ -87,6 +87,24 @@ def test_index_score_brute_force_tiny(H_idx, H_kv, q_len):
     np.testing.assert_allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-12)
 
 
+def test_index_score_brute_force_prefill_chunk():
+    # A 20-token chunk at the end of a 140-token request: token i's causal
+    # length is 121 + i, so tokens 0..7 see block 0 only (block 1 is -inf for
+    # them) and tokens 8..19 see 1..12 keys of block 1; two index heads summed.
+    rng = np.random.default_rng(21)
+    pool, keys = _fp8_index_pool(rng, 3)
+    seq_lens = np.array([140])
+    bt = np.array([[2, 0]])
+    q_len, H_idx, H_kv = 20, 2, 1
+    q_idx = rng.standard_normal((q_len, H_idx, 128))
+    got = od.index_score(q_idx, pool, "fp8", 0.5, bt, seq_lens, q_len, H_kv, 2)
+    ref = _brute_scores(keys, q_idx, bt, seq_lens, q_len, H_kv, 2, idx_scale=0.5)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    assert np.isneginf(got[0, :8, 1]).all() and np.isfinite(got[0, 8:, 1]).all()
+    fin = np.isfinite(ref)
+    np.testing.assert_allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
 def test_index_score_one_token_equals_dot():
     rng = np.random.default_rng(3)
     pool, keys = _bf16_index_pool(rng, 2)
