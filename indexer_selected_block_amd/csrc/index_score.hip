@@ -365,139 +365,197 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, __amdgpu_buf
 // Query tiles (16 rows each) a wave of the wide variant runs its block against.
 constexpr int kWideTiles = 8;
 
-// Key tiles of a block held in registers at once by the wide variant: four
-// of the eight for fp8 keys (one tile's operand is converted at a time), two
-// for bf16 keys (with four the compiler copies them through scratch), the
-// whole block for MXFP4 (40 registers).
+// Key tiles of a block the wide variant converts to MFMA operands at once
+// (a part): four (64 registers of bf16 operands); the raw bytes of the next
+// part are loaded while this part's tiles run against the query tiles.
 template <int KEY_DT>
-constexpr int wide_part_tiles() { return KEY_DT == ISB_MXFP4 ? 8 : KEY_DT == ISB_FP8_E4M3 ? 4 : 2; }
+constexpr int wide_part_tiles() { return KEY_DT == ISB_MXFP4 ? 4 : 2; }
 
+// Raw bytes of one part of a block, as loaded.
 template <int KEY_DT>
-struct PartKeys {
+struct PartRaw {
   TileRegs<KEY_DT> t[wide_part_tiles<KEY_DT>()];
 };
 template <>
-struct PartKeys<ISB_MXFP4> {
-  u32x4 data[8];    // key m of tile tt, dims 32 g .. 32 g + 31 (e2m1)
-  uint32_t scl[8];  // key m's four e8m0 scales
+struct PartRaw<ISB_MXFP4> {
+  u32x4 data[4];    // key m of tile tt, dims 32 g .. 32 g + 31 (e2m1)
+  uint32_t scl[4];  // key m's four e8m0 scales
 };
 
 template <int KEY_DT>
-__device__ __forceinline__ void load_part_keys(PartKeys<KEY_DT>& k, __amdgpu_buffer_rsrc_t page, int part,
-                                               int lane) {
+__device__ __forceinline__ void load_part_raw(PartRaw<KEY_DT>& k, __amdgpu_buffer_rsrc_t page, int part, int lane) {
+  constexpr int NT = wide_part_tiles<KEY_DT>();
   if constexpr (KEY_DT == ISB_MXFP4) {
     const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      k.data[tt] = bl16_nt(page, 64 * m + 16 * g, 1024 * tt);
-      k.scl[tt] = bl4_nt(page, 4 * m, kMxDataBytes + 64 * tt);
+    for (int tt = 0; tt < NT; ++tt) {
+      k.data[tt] = bl16_nt(page, 64 * m + 16 * g, 1024 * (part * NT + tt));
+      k.scl[tt] = bl4_nt(page, 4 * m, kMxDataBytes + 64 * (part * NT + tt));
     }
   } else {
     constexpr int TB = KEY_DT == ISB_BF16 ? 4096 : 2048;
-    constexpr int NT = wide_part_tiles<KEY_DT>();
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) load_tile<KEY_DT>(k.t[tt], page, (part * NT + tt) * TB, lane);
   }
 }
 
-// Folds the keys of one part into the running maximum `best` of query row n
-// (lane (g, m) of a 16-row tile holds keys 4 g + e of row m); keys at or past
-// nv (the row's causally valid keys in this block) do not count, a NaN
-// product among the valid ones sets `nan`.
+// MFMA operands of one part: bf16 for the bf16 MFMA (keys converted once,
+// whatever the number of query tiles), or the raw e2m1 data and scales for
+// the scaled fp4 x e4m3 MFMA.
 template <int KEY_DT, int Q_DT>
-__device__ __forceinline__ void wide_part_max(const ScoreArgs& a, const PartKeys<KEY_DT>& k, int part, int r,
-                                              int nq, int nv, int lane, float& best, bool& nan) {
+struct PartOps {
+  bf16x8 kb[wide_part_tiles<KEY_DT>()][4];  // tile tt: dims 32 g + 8 j .. of key m in kb[tt][j]
+};
+template <>
+struct PartOps<ISB_MXFP4, ISB_FP8_E4M3> {
+  u32x4 data[4];  // e2m1, as loaded
+  int sa[4];      // this lane's e8m0 scale byte of each tile
+};
+
+template <int KEY_DT, int Q_DT>
+__device__ __forceinline__ void part_operands(const PartRaw<KEY_DT>& k, int lane, PartOps<KEY_DT, Q_DT>& o) {
   constexpr int NT = wide_part_tiles<KEY_DT>();
   const int g = lane >> 4;
-  const int i = nq / a.H_idx, h = nq % a.H_idx;
   if constexpr (KEY_DT == ISB_MXFP4 && Q_DT == ISB_FP8_E4M3) {
-    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      o.data[tt] = k.data[tt];
+      o.sa[tt] = (int)((k.scl[tt] >> (8 * g)) & 0xFFu);
+    }
+  } else if constexpr (KEY_DT == ISB_MXFP4) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const float sc = e8m0_to_f32(k.scl[tt] >> (8 * g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o.kb[tt][j] = e2m1x8_to_bf16x8(k.data[tt][j], sc);
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) tile_operand<KEY_DT>(k.t[tt], o.kb[tt]);
+  }
+}
+
+// IEEE maximum that propagates NaN (v_maximum3_f32 on gfx950): a NaN
+// product among a row's valid keys makes its block maximum NaN with no
+// separate test.
+__device__ __forceinline__ float nan_max(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+__device__ __forceinline__ float nan_max3(float x, float y, float z) { return nan_max(x, nan_max(y, z)); }
+
+// Folds one part's keys into the running maximum `best` of query row n
+// (lane (g, m) of a 16-row tile holds keys 4 g + e of row m).  full: every
+// row of the tile sees the whole block (wave-uniform); otherwise keys at or
+// past nv (the row's causally valid keys in this block) count as -inf.
+// qrow: the row as stored.
+template <int KEY_DT, int Q_DT>
+__device__ __forceinline__ void wide_part_max(const PartOps<KEY_DT, Q_DT>& k, int part, const uint8_t* qrow,
+                                              bool full, int nv, int lane, float& best) {
+  constexpr int NT = wide_part_tiles<KEY_DT>();
+  const int g = lane >> 4;
+  f32x4 acc[NT];
+  if constexpr (KEY_DT == ISB_MXFP4 && Q_DT == ISB_FP8_E4M3) {
     const u32x4 lo = ld16(qrow + 16 * g);
     const u32x4 hi = ld16(qrow + 64 + 16 * g);
     const i32x8 qb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       const i32x8 ka = {(int)k.data[tt][0], (int)k.data[tt][1], (int)k.data[tt][2], (int)k.data[tt][3], 0, 0, 0, 0};
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_scale_fp4_e4m3(ka, qb, acc, (int)((k.scl[tt] >> (8 * g)) & 0xFFu));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (16 * tt + 4 * g + e < nv) {
-          nan |= acc[e] != acc[e];
-          best = fmaxf(best, acc[e]);
-        }
-      }
+      acc[tt] = mfma_scale_fp4_e4m3(ka, qb, f32x4{0.f, 0.f, 0.f, 0.f}, k.sa[tt]);
     }
   } else {
-    constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
-    const uint8_t* qrow = a.q_idx + ((size_t)(r * a.q_len + i) * a.H_idx + h) * kHeadDim * QB;
     bf16x8 qb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) qb[j] = load_q8<Q_DT>(qrow, 32 * g + 8 * j);
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KEY_DT == ISB_MXFP4) {
-        const float sc = e8m0_to_f32(k.scl[tt] >> (8 * g));
+      acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma_16x16x32_bf16(e2m1x8_to_bf16x8(k.data[tt][j], sc), qb[j], acc);
-      } else {
-        bf16x8 kb[4];
-        tile_operand<KEY_DT>(k.t[tt], kb);
+      for (int j = 0; j < 4; ++j) acc[tt] = mfma_16x16x32_bf16(k.kb[tt][j], qb[j], acc[tt]);
+    }
+  }
+  if (full) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma_16x16x32_bf16(kb[j], qb[j], acc);
-      }
+    for (int tt = 0; tt < NT; ++tt) {
+      best = nan_max3(best, acc[tt][0], acc[tt][1]);
+      best = nan_max3(best, acc[tt][2], acc[tt][3]);
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
       const int key0 = 16 * (part * NT + tt) + 4 * g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (key0 + e < nv) {
-          nan |= acc[e] != acc[e];
-          best = fmaxf(best, acc[e]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 4; ++e) best = nan_max(best, key0 + e < nv ? acc[tt][e] : neg_inf());
     }
   }
 }
 
 // grid (ceil(MB / 4), R, ceil(QR / (16 kWideTiles))), 4 waves a workgroup:
 // wave w scores block 4 x + w of request y for query rows
-// [16 kWideTiles z, 16 kWideTiles (z + 1)).  Needs 16 % H_idx == 0, so a
+// [16 kWideTiles z, 16 kWideTiles (z + 1)), which the workgroup stages in LDS.  Needs 16 % H_idx == 0, so a
 // 16-row tile holds whole tokens (row n = token n / H_idx, head n % H_idx)
 // and each KV group's index heads sit on adjacent lanes.
 template <int KEY_DT, int Q_DT>
 __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   constexpr int NT = wide_part_tiles<KEY_DT>();
   constexpr int PARTS = 8 / NT;
+  constexpr int QROW = Q_DT == ISB_BF16 ? 2 * kHeadDim : kHeadDim;  // bytes of a query row
+  // LDS pitch of a staged row: 16 bytes past a multiple of 256 puts the 16
+  // rows a 16-byte read of a tile touches on distinct banks
+  constexpr int QPITCH = QROW + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[16 * kWideTiles * QPITCH];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int m = lane & 15;
   const int r = blockIdx.y;
-  const int b = score_column<kScoreWaves>(blockIdx.x, gridDim.x, blockIdx.y) * kScoreWaves + wave;
-  if (b >= a.MB) return;
   const int QR = a.q_len * a.H_idx;
-  const int n0 = 16 * kWideTiles * blockIdx.z;   // first query row of this wave
+  const int n0 = 16 * kWideTiles * blockIdx.z;   // first query row of this workgroup
   const int n1 = min(QR, n0 + 16 * kWideTiles);  // one past the last
-  const int per = a.H_idx / a.H_kv;               // index heads of a KV group
+  const int per = a.H_idx / a.H_kv;  // index heads of a KV group
   const int T = a.R * a.q_len;
   const int L = a.seq_lens[r];
   const int nr = (L + kBlockTokens - 1) / kBlockTokens;
-  if (b >= nr) {  // no token of the request reaches this block
+  const int col = score_column<kScoreWaves>(blockIdx.x, gridDim.x, blockIdx.y);
+  const int b = col * kScoreWaves + wave;
+  // -inf for every token of this workgroup's rows at block b (no token of the
+  // request reaches it)
+  auto write_unreached = [&]() {
     const int i0 = n0 / a.H_idx, i1 = n1 / a.H_idx;
     for (int x = lane; x < (i1 - i0) * a.H_kv; x += kWave) {
       const int i = i0 + x / a.H_kv, gg = x % a.H_kv;
       a.scores[((size_t)gg * T + (size_t)r * a.q_len + i) * a.MB + b] = neg_inf();
     }
+  };
+  if (col * kScoreWaves >= nr) {  // all four blocks past the request's end (uniform over the workgroup)
+    if (b < a.MB) write_unreached();
     return;
   }
-  const int64_t blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r * a.bt_stride + b]);
+  const bool live = b < nr && b < a.MB;
+  int64_t blk = 0;
+  if (live) blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r * a.bt_stride + b]);
   // an out-of-range block id is poison: NaN where the block is causally
   // visible, -inf elsewhere; nothing is read through it
   const bool bad = blk < 0 || blk >= a.pool_blocks;
   constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
   const __amdgpu_buffer_rsrc_t page = page_rsrc(a.pool + (bad ? 0 : blk) * PB, (int)PB);
+  // the first part of the keys is requested before the query rows, so one
+  // round trip covers both
+  PartRaw<KEY_DT> raw;
+  if (live) load_part_raw<KEY_DT>(raw, page, 0, lane);
+  // The four waves score four blocks against the same query rows: the rows
+  // (contiguous in q_idx: row n of request r is row r QR + n) are staged in
+  // LDS once, as stored.
+  {
+    const uint8_t* src = a.q_idx + ((size_t)r * QR + n0) * QROW;
+    constexpr int CPR = QROW / 16;  // 16-byte chunks a row
+    for (int c = threadIdx.x; c < (n1 - n0) * CPR; c += 256)
+      *reinterpret_cast<u32x4*>(s_q + (c / CPR) * QPITCH + (c % CPR) * 16) = ld16(src + (size_t)c * 16);
+  }
+  __syncthreads();
+  if (b >= a.MB) return;
+  if (b >= nr) {
+    write_unreached();
+    return;
+  }
   // row n = n0 + 16 q + m of each tile q: its causally valid keys in this block
   float best[kWideTiles];
-  bool nan[kWideTiles];
   int nv[kWideTiles];
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
@@ -505,28 +563,30 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
     const int v = n < n1 ? causal_len(L, a.q_len, n / a.H_idx) - b * kBlockTokens : 0;
     nv[q] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
     best[q] = neg_inf();
-    nan[q] = false;
   }
 #pragma unroll
   for (int part = 0; part < PARTS; ++part) {
-    PartKeys<KEY_DT> keys;
-    load_part_keys<KEY_DT>(keys, page, part, lane);
+    PartOps<KEY_DT, Q_DT> ops;
+    part_operands<KEY_DT, Q_DT>(raw, lane, ops);
+    if (part + 1 < PARTS) load_part_raw<KEY_DT>(raw, page, part + 1, lane);  // in flight during this part
 #pragma unroll
     for (int q = 0; q < kWideTiles; ++q) {
       const int n = n0 + 16 * q + m;
-      if (n0 + 16 * q < n1)  // wave-uniform: the tile has rows
-        wide_part_max<KEY_DT, Q_DT>(a, keys, part, r, n < n1 ? n : n0, nv[q], lane, best[q], nan[q]);
-      // one query tile's operands at a time (hoisting the next tiles' query
-      // loads would push the keys out of registers)
-      __builtin_amdgcn_sched_barrier(0);
+      if (n0 + 16 * q < n1) {  // wave-uniform: the tile has rows
+        // rows grow in causal length down the tile: its first row (lane 0)
+        // sees the fewest keys
+        const bool full = __builtin_amdgcn_readfirstlane(nv[q]) == kBlockTokens;
+        wide_part_max<KEY_DT, Q_DT>(ops, part, s_q + ((n < n1 ? n : n0) - n0) * QPITCH, full, nv[q], lane,
+                                    best[q]);
+      }
     }
   }
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
     const int n = n0 + 16 * q + m;
     if (n0 + 16 * q >= n1) continue;  // wave-uniform
-    float s = max_over_groups(best[q]);
-    if ((__ballot(nan[q]) >> m & 0x0001000100010001ull) != 0) s = qnan();
+    float s = nan_max(best[q], shfl_xor_f32(best[q], 16));  // over the four lane groups
+    s = nan_max(s, shfl_xor_f32(s, 32));
     if (bad) s = nv[q] > 0 ? qnan() : neg_inf();
     // sum the group's heads: rows n .. n + per - 1 sit on adjacent lanes
     for (int off = 1; off < per; off <<= 1) s += shfl_xor_f32(s, off);
