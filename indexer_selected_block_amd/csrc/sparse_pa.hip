@@ -77,6 +77,17 @@ struct PaArgs {
 constexpr int kPaWaves = 4;
 constexpr int kMergeGroup = 8;  // splits whose partials the merging workgroup loads at once
 
+// Row of grid column x.  Workgroups are dealt round-robin to the eight dies
+// (XCDs), each with its own L2; consecutive rows (the tokens of one request,
+// whose selections share blocks) are given to one die, die d taking rows
+// [d R / 8, (d + 1) R / 8), so a block several of them attend is fetched into
+// that die's L2 once.  A permutation of the rows: any mapping gives the same
+// results.  Rows past the last multiple of eight keep their column.
+__device__ __forceinline__ int grid_row(int x, int rows) {
+  const int per = rows >> 3;
+  return x < 8 * per ? (x & 7) * per + (x >> 3) : x;
+}
+
 template <int Q_DT>
 __device__ __forceinline__ bf16x8 load_q8_t(const uint8_t* row, int dim0) {
   if constexpr (Q_DT == ISB_BF16) {
@@ -455,7 +466,7 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   constexpr int ROUND = 4 * RUN;
   __shared__ WaveParts wp;
-  const int row = blockIdx.x, split = blockIdx.y;
+  const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
@@ -510,7 +521,7 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   __shared__ SelectLds<256> sl;
   __shared__ int32_t s_bt[kSelMaxBlocks];
   __shared__ int32_t s_sel[kSelMaxBlocks];
-  const int row = blockIdx.x, split = blockIdx.y;
+  const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
@@ -565,7 +576,7 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
 template <int Q_DT>
 __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
   __shared__ WaveParts wp;
-  const int row = blockIdx.x, split = blockIdx.y;
+  const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
