@@ -100,12 +100,35 @@ def measured_copy(nbytes_moved):
     return {"bytes_moved": 2 * half, "avg_us": round(us, 2), "GBps": round(2 * half / (us * 1e-6) / 1e9, 1)}
 
 
-def algorithmic_bytes(w, sparse_ctx):
+def distinct_attended_tokens(w, topk):
+    """K/V positions the attention must read at least once: per request and KV
+    head, the union over the request's query tokens of their selected blocks,
+    each block up to the longest causal reach of a token that selects it (the
+    tokens of one request can select the same blocks)."""
+    cfg = w.cfg
+    ql = cfg.query_len
+    lens = w.seq_lens.cpu().tolist()
+    tk = topk.cpu().tolist()  # [H_kv][T][K]
+    total = 0
+    for g in range(cfg.num_kv_heads):
+        for r, L in enumerate(lens):
+            reach = {}
+            for i in range(ql):
+                Lt = max(0, L - (ql - 1 - i))
+                for b in tk[g][r * ql + i]:
+                    if b >= 0:
+                        reach[b] = max(reach.get(b, 0), min(128, Lt - 128 * b))
+            total += sum(reach.values())
+    return total
+
+
+def algorithmic_bytes(w, sparse_ctx, topk):
     """Bytes each kernel must move for this batch: the index keys of every
     request once, the queries, the table entries and lengths read, the scores,
     selection, page table and outputs written; for the attention the K and V
-    bytes of the attended positions.  Split partials and re-reads are not
-    counted."""
+    bytes of the positions attended, each distinct position once (rows of one
+    request that select the same block need its bytes once).  Split partials
+    and re-reads are not counted."""
     cfg = w.cfg
     lens = w.seq_lens.cpu().tolist()
     ql, T = cfg.query_len, cfg.num_tokens
@@ -124,11 +147,12 @@ def algorithmic_bytes(w, sparse_ctx):
     topk_emit = (4 * cfg.num_kv_heads * n_tok_blocks + 4 * len(lens) + 4 * rows * cfg.top_k
                  + 4 * rows * cfg.top_k + 4 * rows * (slots + 1))
     ctx = sparse_ctx.cpu().long()
-    attended = int(ctx.sum()) * 2 * KV_BYTES[cfg.kv_dtype]
+    attended = distinct_attended_tokens(w, topk) * 2 * KV_BYTES[cfg.kv_dtype]
     ptok = 128 // cfg.pages_per_block
     pages = int(((ctx + ptok - 1) // ptok).sum())
     attn = (attended + T * cfg.num_q_heads * 128 * (Q_BYTES[cfg.q_dtype] + 2) + 4 * pages + 4 * rows)
-    return {"index_score": score, "topk_select_emit": topk_emit, "sparse_pa_decode": attn}, attended
+    per_row = int(ctx.sum()) * 2 * KV_BYTES[cfg.kv_dtype]
+    return {"index_score": score, "topk_select_emit": topk_emit, "sparse_pa_decode": attn}, attended, per_row
 
 
 def index_flops(w):
@@ -342,9 +366,10 @@ def main():
     w0 = layers[0].w
     # the copies differ in lengths and selections: bytes are averaged over the
     # copies the timed steps cycle through, like the durations
-    per_copy = [algorithmic_bytes(L.w, L.sparse_ctx) for L in layers]
-    alg = {k: sum(a[k] for a, _ in per_copy) / len(per_copy) for k in per_copy[0][0]}
-    attended = sum(x for _, x in per_copy) / len(per_copy)
+    per_copy = [algorithmic_bytes(L.w, L.sparse_ctx, L.topk) for L in layers]
+    alg = {k: sum(a[k] for a, _, _ in per_copy) / len(per_copy) for k in per_copy[0][0]}
+    attended = sum(x for _, x, _ in per_copy) / len(per_copy)
+    attended_rows = sum(x for _, _, x in per_copy) / len(per_copy)
     shas = kernel_sources_sha()
 
     flops = sum(index_flops(L.w) for L in layers) / len(layers)
@@ -388,6 +413,7 @@ def main():
                    "index_cache": cfg.idx_dtype, "layers": args.layers},
         "attended_kv_GBps": round(attn_gbps, 1),
         "attended_kv_pct_hbm_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 2),
+        "attended_kv_bytes": {"distinct": int(round(attended)), "summed_over_rows": int(round(attended_rows))},
         "step_launches": ["index_score", "select_attend"],
         "kernel_ms": {k: round(v, 5) for k, v in dur_ms.items()},
         "kernel_ms_method": "differences of back-to-back passes of K steps ending after each call (HIP events; median of 3 rounds)",
