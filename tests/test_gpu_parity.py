@@ -90,6 +90,33 @@ def test_index_score_two_kv_heads_and_bf16_query_on_mxfp4():
         assert_scores_close(s.cpu().numpy(), oracle_scores(host_inputs(w)))
 
 
+WIDE_CASES = {
+    # more than 16 tokens or 64 index rows a request: the wide scorer, for every
+    # key / index-query type pair and head layout (index heads per KV group 1..4,
+    # 16-row tiles holding 1..16 tokens), each with a ragged last query tile
+    "fp8_bf16q_8heads_2kv": ("spec_decode", dict(query_len=24, num_idx_heads=8, num_kv_heads=2)),
+    "fp8_e4m3q": ("spec_decode", dict(query_len=33, qidx_dtype="e4m3")),
+    "mxfp4_e4m3q_16heads_4kv": ("mxfp4", dict(query_len=9, num_idx_heads=16, num_kv_heads=4)),
+    "mxfp4_bf16q": ("mxfp4", dict(query_len=20, qidx_dtype="bf16")),
+    "bf16_e4m3q_2heads_2kv": ("tiny_bf16", dict(query_len=40, num_idx_heads=2, num_kv_heads=2,
+                                                qidx_dtype="e4m3")),
+}
+
+
+@pytest.mark.parametrize("case", list(WIDE_CASES))
+def test_index_score_wide_variants(case):
+    base, kw = WIDE_CASES[case]
+    cfg = dataclasses.replace(wl.shrink(wl.CONFIGS[base], num_reqs=3, ctx_lo=300, ctx_hi=1400, num_pad_reqs=0),
+                              **kw)
+    assert cfg.query_len > 16 or cfg.query_len * cfg.num_idx_heads > 64
+    _say(f"[index_score wide] {case}")
+    w = wl.make_workload(cfg, device="cuda")
+    s = isb.index_score(w.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale,
+                        w.block_table, w.seq_lens, cfg.query_len, cfg.num_kv_heads, cfg.max_blocks)
+    torch.cuda.synchronize()
+    assert_scores_close(s.cpu().numpy(), oracle_scores(host_inputs(w)))
+
+
 # ------------------------------------------------------------------ top-k
 def _adversarial_scores(rng, H_kv, T, MB, K):
     palette = np.array([0.5, -0.0, 0.0, 1.0, np.inf, -np.inf, np.nan, 3.0, -2.0, 1e-30, -1e30],
