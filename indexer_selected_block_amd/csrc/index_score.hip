@@ -509,6 +509,9 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   const int n0 = 16 * kWideTiles * blockIdx.z;   // first query row of this workgroup
   const int n1 = min(QR, n0 + 16 * kWideTiles);  // one past the last
   const int per = a.H_idx / a.H_kv;  // index heads of a KV group
+  // H_idx divides 16 and per divides H_idx: both are powers of two, so the
+  // row -> (token, head) and head -> group splits are shifts and masks
+  const int hsh = __builtin_ctz(a.H_idx), psh = __builtin_ctz(per);
   const int T = a.R * a.q_len;
   const int L = a.seq_lens[r];
   const int nr = (L + kBlockTokens - 1) / kBlockTokens;
@@ -517,7 +520,7 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   // -inf for every token of this workgroup's rows at block b (no token of the
   // request reaches it)
   auto write_unreached = [&]() {
-    const int i0 = n0 / a.H_idx, i1 = n1 / a.H_idx;
+    const int i0 = n0 >> hsh, i1 = n1 >> hsh;
     for (int x = lane; x < (i1 - i0) * a.H_kv; x += kWave) {
       const int i = i0 + x / a.H_kv, gg = x % a.H_kv;
       a.scores[((size_t)gg * T + (size_t)r * a.q_len + i) * a.MB + b] = neg_inf();
@@ -560,7 +563,7 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
     const int n = n0 + 16 * q + m;
-    const int v = n < n1 ? causal_len(L, a.q_len, n / a.H_idx) - b * kBlockTokens : 0;
+    const int v = n < n1 ? causal_len(L, a.q_len, n >> hsh) - b * kBlockTokens : 0;
     nv[q] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
     best[q] = neg_inf();
   }
@@ -591,9 +594,9 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
     // sum the group's heads: rows n .. n + per - 1 sit on adjacent lanes
     for (int off = 1; off < per; off <<= 1) s += shfl_xor_f32(s, off);
     if (KEY_DT == ISB_FP8_E4M3) s *= a.idx_scale;
-    const int h = n % a.H_idx;
-    if (lane < 16 && n < n1 && h % per == 0) {
-      const int i = n / a.H_idx, gg = h / per;
+    const int h = n & (a.H_idx - 1);
+    if (lane < 16 && n < n1 && (h & (per - 1)) == 0) {
+      const int i = n >> hsh, gg = h >> psh;
       a.scores[((size_t)gg * T + (size_t)r * a.q_len + i) * a.MB + b] = s;
     }
   }
