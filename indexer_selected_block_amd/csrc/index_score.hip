@@ -560,12 +560,18 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   // row n = n0 + 16 q + m of each tile q: its causally valid keys in this block
   float best[kWideTiles];
   int nv[kWideTiles];
+  const uint8_t* qrow[kWideTiles];  // this lane's staged query row of tile q
+  uint32_t full = 0;                // bit q: every row of tile q sees the whole block
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
     const int n = n0 + 16 * q + m;
     const int v = n < n1 ? causal_len(L, a.q_len, n >> hsh) - b * kBlockTokens : 0;
     nv[q] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
     best[q] = neg_inf();
+    qrow[q] = s_q + ((n < n1 ? n : n0) - n0) * QPITCH;
+    // rows grow in causal length down the tile: its first row (lane 0) sees
+    // the fewest keys
+    if (__builtin_amdgcn_readfirstlane(nv[q]) == kBlockTokens) full |= 1u << q;
   }
 #pragma unroll
   for (int part = 0; part < PARTS; ++part) {
@@ -573,16 +579,9 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
     part_operands<KEY_DT, Q_DT>(raw, lane, ops);
     if (part + 1 < PARTS) load_part_raw<KEY_DT>(raw, page, part + 1, lane);  // in flight during this part
 #pragma unroll
-    for (int q = 0; q < kWideTiles; ++q) {
-      const int n = n0 + 16 * q + m;
-      if (n0 + 16 * q < n1) {  // wave-uniform: the tile has rows
-        // rows grow in causal length down the tile: its first row (lane 0)
-        // sees the fewest keys
-        const bool full = __builtin_amdgcn_readfirstlane(nv[q]) == kBlockTokens;
-        wide_part_max<KEY_DT, Q_DT>(ops, part, s_q + ((n < n1 ? n : n0) - n0) * QPITCH, full, nv[q], lane,
-                                    best[q]);
-      }
-    }
+    for (int q = 0; q < kWideTiles; ++q)
+      if (n0 + 16 * q < n1)  // wave-uniform: the tile has rows
+        wide_part_max<KEY_DT, Q_DT>(ops, part, qrow[q], (full >> q) & 1u, nv[q], lane, best[q]);
   }
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
