@@ -366,7 +366,8 @@ __device__ __forceinline__ float tile_block_fp4(const ScoreArgs& a, __amdgpu_buf
 constexpr int kWideTiles = 8;
 
 // Key tiles of a block the wide variant converts to MFMA operands at once
-// (a part): four (64 registers of bf16 operands); the raw bytes of the next
+// (a part): two for bf16 and fp8 keys (32 registers of bf16 operands, which
+// keeps four waves a SIMD), four for MXFP4 keys; the raw bytes of the next
 // part are loaded while this part's tiles run against the query tiles.
 template <int KEY_DT>
 constexpr int wide_part_tiles() { return KEY_DT == ISB_MXFP4 ? 4 : 2; }
@@ -490,9 +491,10 @@ __device__ __forceinline__ void wide_part_max(const PartOps<KEY_DT, Q_DT>& k, in
 
 // grid (ceil(MB / 4), R, ceil(QR / (16 kWideTiles))), 4 waves a workgroup:
 // wave w scores block 4 x + w of request y for query rows
-// [16 kWideTiles z, 16 kWideTiles (z + 1)), which the workgroup stages in LDS.  Needs 16 % H_idx == 0, so a
-// 16-row tile holds whole tokens (row n = token n / H_idx, head n % H_idx)
-// and each KV group's index heads sit on adjacent lanes.
+// [16 kWideTiles z, 16 kWideTiles (z + 1)), which the workgroup stages in
+// LDS.  Needs 16 % H_idx == 0, so a 16-row tile holds whole tokens (row n =
+// token n / H_idx, head n % H_idx) and each KV group's index heads sit on
+// adjacent lanes.
 template <int KEY_DT, int Q_DT>
 __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   constexpr int NT = wide_part_tiles<KEY_DT>();
