@@ -253,7 +253,7 @@ ISB_API int isb_sparse_pa_decode(isb_stream_t stream,
  * page ids from there; the first split of each row also writes topk_idx,
  * sparse_bt and sparse_ctx.  Writes exactly what the two calls write (the
  * selection, table and lengths bit-identical; the output as
- * isb_sparse_pa_decode computes it).  One launch for bf16 / fp8 K/V with
+ * isb_sparse_pa_decode computes it).  One launch (any K/V dtype) with
  * max_blocks <= 2048, max_blocks and block_table_stride multiples of 4 and
  * 16-byte aligned scores and block table; otherwise the two calls in turn.
  *

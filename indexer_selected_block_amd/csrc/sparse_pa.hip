@@ -506,7 +506,7 @@ struct SelArgs {
   const int32_t* seq_lens;  // [R]
   const int32_t* bt;        // [R][bt_stride]
   int32_t* topk;            // out [H_kv][T][K]
-  int32_t* sbt;             // out [T * H_kv][K * 8]
+  int32_t* sbt;             // out [T * H_kv][K * ppb]
   int32_t* sctx;            // out [T * H_kv]
   int q_len, T, MB, K, bt_stride;
 };
@@ -572,19 +572,15 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
 }
 
 // ----------------------------------------------------------------- MXFP4 pages
-// One 128-token page a wave (eight 16-key tiles); grid (rows, splits).
+// One 128-token page a wave (eight 16-key tiles): page p0 + wave of the
+// row's split, whose id is id_raw (-1 past the row's pages).
 template <int Q_DT>
-__global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
-  __shared__ WaveParts wp;
-  const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
+__device__ __forceinline__ void attend_split_mx(const PaArgs& a, WaveParts& wp, int row, int split, int t,
+                                                int kvh, int n_tok, int32_t id_raw, __bf16* out_row) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int p0 = split * a.pps;
   const int p = p0 + wave;
-  const int n_tok = a.sctx[row];
-  const int32_t id_raw = p < a.sbt_stride ? a.sbt[(size_t)row * a.sbt_stride + p] : -1;
-  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
   if (n_tok <= 0) {
     write_empty_row(a, split, out_row);
     return;
@@ -695,6 +691,63 @@ __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
   finish_split(a, wp, row, split, live, out_row);
 }
 
+// grid (rows, splits); page ids come from the sparse page table.
+template <int Q_DT>
+__global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
+  __shared__ WaveParts wp;
+  const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
+  const int t = row / a.H_kv, kvh = row % a.H_kv;
+  const int p = split * a.pps + wave_id();
+  const int n_tok = a.sctx[row];
+  const int32_t id_raw = p < a.sbt_stride ? a.sbt[(size_t)row * a.sbt_stride + p] : -1;
+  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
+  attend_split_mx<Q_DT>(a, wp, row, split, t, kvh, n_tok, id_raw, out_row);
+}
+
+// Selection and attention of a row in one launch for MXFP4 pages (one page a
+// block) and rows of up to kSelMaxBlocks blocks, as pa16sel_kernel does for
+// 16-token pages: every workgroup of a row selects the row's blocks from its
+// scores and block-table row, split 0 also writes the selection, the page
+// table and the sparse length.
+template <int Q_DT, int E>
+__global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
+  __shared__ WaveParts wp;
+  __shared__ SelectLds<256> sl;
+  __shared__ int32_t s_bt[kSelMaxBlocks];
+  __shared__ int32_t s_sel[kSelMaxBlocks];
+  const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int t = row / a.H_kv, kvh = row % a.H_kv;
+  const int r = t / sa.q_len, i = t % sa.q_len;
+  const int trow = kvh * sa.T + t;  // the row's index in the score and selection buffers
+  const int Lr = sa.seq_lens[r];
+  float sc[E];
+  int32_t btv[E];
+  load_run<E, true>(sa.scores + (size_t)trow * sa.MB, E * tid, sa.MB, sc);
+  load_run<E, true>(sa.bt + (size_t)r * sa.bt_stride, E * tid, sa.MB, btv);
+  const int Lt = max(0, Lr - (sa.q_len - 1 - i));
+  const int nt = min((Lt + kBlockTokens - 1) / kBlockTokens, sa.MB);
+#pragma unroll
+  for (int x = 0; x < E; ++x)
+    if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
+  int32_t* o = sa.topk + (size_t)trow * sa.K;
+  const int m = select_row<256, E>(sc, nt, sa.K, sl, [&](int k, int b) {
+    s_sel[k] = b;
+    if (split == 0) o[k] = b;
+  });
+  __syncthreads();  // the selection and the block-table row are in LDS
+  const int n_tok = m > 0 ? (m - 1) * kBlockTokens + (Lt - kBlockTokens * (nt - 1)) : 0;
+  if (split == 0) {  // one page a block: the row's k-th page is its k-th selected block
+    int32_t* so = sa.sbt + (size_t)row * sa.K;
+    for (int x = tid; x < sa.K; x += 256) so[x] = x < m ? s_bt[s_sel[x]] : -1;
+    if (tid == 0) sa.sctx[row] = n_tok;
+  }
+  const int p = split * a.pps + wave_id();
+  const int32_t id_raw = p < m ? s_bt[s_sel[p]] : -1;
+  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
+  attend_split_mx<Q_DT>(a, wp, row, split, t, kvh, n_tok, id_raw, out_row);
+}
+
 template <int KV_DT, int Q_DT>
 static void launch_decode(const PaArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (KV_DT == ISB_MXFP4)
@@ -762,8 +815,12 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
 
 template <int KV_DT, int Q_DT, int E>
 static void launch_select_attend_e(const PaArgs& a, const SelArgs& sa, dim3 grid, hipStream_t st) {
-  constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
-  hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, E>), grid, dim3(256), 0, st, a, sa);
+  if constexpr (KV_DT == ISB_MXFP4) {
+    hipLaunchKernelGGL((pamxsel_kernel<Q_DT, E>), grid, dim3(256), 0, st, a, sa);
+  } else {
+    constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
+    hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, E>), grid, dim3(256), 0, st, a, sa);
+  }
 }
 
 template <int KV_DT, int Q_DT>
@@ -835,11 +892,11 @@ extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const
                            out, a, plan);
   if (err) return err;
   hipStream_t st = as_hip(stream);
-  const bool one_launch = kv_dtype != ISB_MXFP4 && max_blocks <= kSelMaxBlocks && max_blocks % 4 == 0 &&
-                          block_table_stride % 4 == 0 && reinterpret_cast<uintptr_t>(scores) % 16 == 0 &&
+  const bool one_launch = max_blocks <= kSelMaxBlocks && max_blocks % 4 == 0 && block_table_stride % 4 == 0 &&
+                          reinterpret_cast<uintptr_t>(scores) % 16 == 0 &&
                           reinterpret_cast<uintptr_t>(block_table) % 16 == 0;
   if (!one_launch) {
-    // MXFP4 pages and wide or unaligned rows: the two steps as two launches.
+    // wide or unaligned rows: the two steps as two launches.
     int e = isb_topk_select_emit(stream, scores, seq_lens, num_reqs, decode_query_len, num_kv_heads,
                                  max_blocks, top_k, block_table, block_table_stride, ppb, topk_idx,
                                  sparse_bt, sparse_ctx);
@@ -855,9 +912,12 @@ extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const
   if (kv_dtype == ISB_BF16) {
     if (qb) launch_select_attend<ISB_BF16, ISB_BF16>(a, sa, grid, st);
     else launch_select_attend<ISB_BF16, ISB_FP8_E4M3>(a, sa, grid, st);
-  } else {
+  } else if (kv_dtype == ISB_FP8_E4M3) {
     if (qb) launch_select_attend<ISB_FP8_E4M3, ISB_BF16>(a, sa, grid, st);
     else launch_select_attend<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, sa, grid, st);
+  } else {
+    if (qb) launch_select_attend<ISB_MXFP4, ISB_BF16>(a, sa, grid, st);
+    else launch_select_attend<ISB_MXFP4, ISB_FP8_E4M3>(a, sa, grid, st);
   }
   return launch_status();
 }

@@ -220,7 +220,10 @@ _SEL_CASES = {
     "tiny_bf16": ("tiny_bf16", {}),
     "fp8_two_kv_heads": ("fp8_decode", dict(num_kv_heads=2, num_q_heads=16, num_idx_heads=2)),
     "long_context_rows_not_x4": ("long_context", {}),     # two launches: rows not a multiple of 4
-    "mxfp4": ("mxfp4", {}),                               # two launches: 128-token pages
+    "mxfp4": ("mxfp4", {}),                               # one launch, 128-token pages
+    "mxfp4_two_kv_heads": ("mxfp4", dict(num_kv_heads=2, num_q_heads=16)),
+    "mxfp4_bf16_query": ("mxfp4", dict(q_dtype="bf16")),
+    "prefill_mxfp4": ("prefill_mxfp4", {}),              # 37 tokens a request, 74 rows
 }
 
 
