@@ -141,3 +141,40 @@ def test_bench_refuses_more_than_one_gpu():
     assert proc.returncode == 2
     msg = json.loads(proc.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_bench_counts_each_attended_position_once():
+    # The attention's algorithmic bytes: per request and KV head, the union over
+    # its query tokens of the positions they attend (a block several tokens
+    # select counts once, up to the longest causal reach among them), checked
+    # against a set of (head, request, position) built token by token.
+    import sys
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    from indexer_selected_block_amd import workload as wl
+
+    cfg = wl.shrink(wl.CONFIGS["spec_decode"], num_reqs=4, ctx_lo=130, ctx_hi=700, num_pad_reqs=1)
+    cfg = wl.replace(cfg, num_kv_heads=2, num_q_heads=16, num_idx_heads=2)
+    w = wl.make_workload(cfg, device="cpu")
+    rng = np.random.default_rng(3)
+    T, ql, K = cfg.num_tokens, cfg.query_len, cfg.top_k
+    lens = w.seq_lens.tolist()
+    topk = np.full((cfg.num_kv_heads, T, K), -1, dtype=np.int32)
+    seen = set()
+    for g in range(cfg.num_kv_heads):
+        for t in range(T):
+            r, i = divmod(t, ql)
+            Lt = max(0, lens[r] - (ql - 1 - i))
+            nt = -(-Lt // 128)
+            if nt == 0:
+                continue
+            blocks = sorted(set(rng.choice(nt, size=min(K, nt), replace=False).tolist()) | {nt - 1})[:K]
+            topk[g, t, :len(blocks)] = blocks
+            for b in blocks:
+                for pos in range(128 * b, min(128 * b + 128, Lt)):
+                    seen.add((g, r, pos))
+    assert bench.distinct_attended_tokens(w, torch.from_numpy(topk)) == len(seen)
