@@ -1,0 +1,158 @@
+"""Writing new tokens into the paged caches, and the e4m3 query cast.
+
+Test infrastructure only (see the package docstring).
+
+This is the step in front of the decode path (ROCm/ATOM PR 2962, the commit
+messages under Follow-ups: the fused writer quantises the new tokens' keys and
+values into the MXFP4 / fp8 cache pages and casts the query to float8_e4m3fn
+with a unit scale, saturating).  Readings where the sources are silent:
+
+* placement - token i of request r's q new tokens sits at absolute position
+  seq_lens[r] - q + i (the lengths include the new tokens); a position below
+  zero (a pad request) is not written;
+* e4m3fn encoding - round to nearest, ties to the even code, magnitudes above
+  448 saturate to 448, NaN becomes 0x7F; the sign is kept (a negative value
+  that rounds to zero is -0), as in every encoding here;
+* MXFP4 encoding (OCP MX v1.0) - per 32 consecutive dims the shared exponent
+  is floor(log2 amax) - 2 (2 is the largest e2m1 exponent), clamped to the
+  e8m0 range [-127, 127] (-127 for an all-zero group); each element's e2m1
+  code rounds x / 2^exponent to nearest, ties to the even code, and magnitudes
+  above 6 saturate to 6;
+* bf16 values are stored as given;
+* QK-norm and rope are not part of this writer: it stores the vectors it is
+  given.
+
+Every code below is chosen from the decoded value tables of ``formats`` (the
+nearest representable value, ties to the even code), and bytes are placed with
+the page offset formulas of ``pools``, so the writer is the exact inverse of the
+readers the oracle's decode path uses.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats, pools
+
+E4M3_MAX = 448.0
+E2M1_MAX = 6.0
+
+
+def _nearest_code(a: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Index of the nearest entry of the increasing table to each a >= 0 (a
+    within the table's range), ties to the even index."""
+    hi = np.clip(np.searchsorted(table, a, side="left"), 1, len(table) - 1)
+    lo = hi - 1
+    dlo = a - table[lo]
+    dhi = table[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    return np.where(pick_hi, hi, lo)
+
+
+_E4M3_TABLE = np.array([formats.e4m3_value(c) for c in range(0x7F)])   # codes 0x00..0x7E, increasing
+_E2M1_TABLE = np.array([formats.e2m1_value(c) for c in range(8)])      # 0, .5, 1, 1.5, 2, 3, 4, 6
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """e4m3fn bytes of x (any shape), rounding and saturating as above."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    code = _nearest_code(np.where(np.isnan(a), 0.0, a), _E4M3_TABLE).astype(np.uint8)
+    code = code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def encode_e2m1(x) -> np.ndarray:
+    """4-bit e2m1 codes of x (finite), rounding and saturating as above."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E2M1_MAX)
+    code = _nearest_code(a, _E2M1_TABLE).astype(np.uint8)
+    return code | np.where(np.signbit(x), 8, 0).astype(np.uint8)
+
+
+def mx_quantize(x) -> tuple[np.ndarray, np.ndarray]:
+    """x [..., 128] -> (e2m1 codes [..., 128], e8m0 scale bytes [..., 4])."""
+    x = np.asarray(x, dtype=np.float64)
+    g = x.reshape(*x.shape[:-1], 4, 32)
+    amax = np.abs(g).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127.0)
+    e = np.clip(e, -127, 127)
+    codes = encode_e2m1(g / np.exp2(e)[..., None]).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def _mxfp4_put(flat: np.ndarray, base: int, slot: int, codes: np.ndarray, scales: np.ndarray) -> None:
+    """Token `slot` of the 8704 B MXFP4 page at byte `base` of a flat pool
+    (formats.decode_mxfp4_page's layout)."""
+    flat[base + 64 * slot:base + 64 * slot + 64] = codes[0::2] | (codes[1::2] << 4)
+    s0 = base + formats.MXFP4_DATA_BYTES + 4 * slot
+    flat[s0:s0 + 4] = scales
+
+
+def _bf16_bytes(x: np.ndarray) -> np.ndarray:
+    """bf16 values given as float (exactly representable) -> their two bytes each."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16).view(np.uint8).reshape(*np.shape(x), 2)
+
+
+def _element_bytes(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
+    """[..., 128] values -> [..., 128, e] stored bytes for bf16 / fp8."""
+    if dtype == "bf16":
+        return _bf16_bytes(x)
+    return encode_e4m3(np.asarray(x, dtype=np.float64) / scale)[..., None]
+
+
+def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,
+                k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str, k_scale: float, v_scale: float,
+                idx_pool: np.ndarray, idx_dtype: str, idx_scale: float) -> None:
+    """Writes the new tokens into the pools, in place.
+
+    k_new, v_new [T, H_kv, 128] and idx_new [T, 128] hold the values (floats;
+    bf16 caches take values that bf16 represents exactly); the pools are the
+    contiguous byte arrays the readers of ``pools`` take (K/V: pages of
+    H_kv heads each, head g of page id n at (n H_kv + g) page bytes; index
+    cache: one page per block)."""
+    T, H_kv, _ = np.shape(k_new)
+    k_new, v_new, idx_new = (np.asarray(a, dtype=np.float64) for a in (k_new, v_new, idx_new))
+    kf, vf, xf = (np.asarray(a).reshape(-1) for a in (k_pool, v_pool, idx_pool))  # flat byte views
+    assert all(np.shares_memory(a, b) for a, b in ((kf, k_pool), (vf, v_pool), (xf, idx_pool)))
+    for t in range(T):
+        r, i = divmod(t, q_len)
+        p = int(seq_lens[r]) - q_len + i
+        if p < 0:
+            continue
+        blk, slot = int(block_table[r][p // pools.BLOCK]), p % pools.BLOCK
+        # index key: one per token, no head dimension; page id = block id
+        if idx_dtype == "mxfp4":
+            codes, scales = mx_quantize(idx_new[t])
+            _mxfp4_put(xf, blk * formats.MXFP4_PAGE_BYTES, slot, codes, scales)
+        else:
+            e = 2 if idx_dtype == "bf16" else 1
+            off = blk * 16384 * e + 2048 * e * (slot // pools.PAGE16) + _k_offsets_row(e, slot % pools.PAGE16)
+            xf[off] = _element_bytes(idx_new[t], idx_dtype, idx_scale).reshape(-1)
+        for g in range(H_kv):
+            if kv_dtype == "mxfp4":
+                for flat, x in ((kf, k_new[t, g]), (vf, v_new[t, g])):
+                    codes, scales = mx_quantize(x)
+                    _mxfp4_put(flat, (blk * H_kv + g) * formats.MXFP4_PAGE_BYTES, slot, codes, scales)
+            else:
+                e = 2 if kv_dtype == "bf16" else 1
+                base = ((8 * blk + slot // pools.PAGE16) * H_kv + g) * 2048 * e
+                c = slot % pools.PAGE16
+                kf[base + _k_offsets_row(e, c)] = _element_bytes(k_new[t, g], kv_dtype, k_scale).reshape(-1)
+                vf[base + _v_offsets_row(e, c)] = _element_bytes(v_new[t, g], kv_dtype, v_scale).reshape(-1)
+
+
+def _k_offsets_row(esize: int, c: int) -> np.ndarray:
+    """Byte offsets of the 128 dims of key c of a 16-token K page, each element's bytes in order."""
+    return (pools._k_offsets(esize)[c][:, None] + np.arange(esize)).reshape(-1)
+
+
+def _v_offsets_row(esize: int, t: int) -> np.ndarray:
+    """Byte offsets of the 128 dims of key t of a 16-token V page, each element's bytes in order."""
+    return (pools._v_offsets(esize)[t][:, None] + np.arange(esize)).reshape(-1)
+
+
+def quantize_query_e4m3(q) -> np.ndarray:
+    """The query cast of the fused writer: e4m3fn bytes with a unit scale, saturating."""
+    return encode_e4m3(q)
