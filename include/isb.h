@@ -16,6 +16,12 @@
  *                                row merges it, in the same launch);
  *   isb_select_attend            top-k, emit and attention in one launch.
  *
+ * In front of them, the cache writer of the same decode step:
+ *
+ *   isb_write_cache              quantise the step's new keys, values and
+ *                                index keys into the pools;
+ *   isb_quantize_e4m3            the unit-scale e4m3 cast of a query.
+ *
  * The calls follow the decode call of the vLLM API page for
  * vllm.models.minimax_m3.amd.sparse_attention_msa (MiniMaxM3SparseAiterPAImpl
  * .forward: query, K/V caches, top-k indices, block_table, seq_lens,
@@ -272,6 +278,60 @@ ISB_API int isb_select_attend(isb_stream_t stream, const float* scores,
                               int num_q_heads, float sm_scale, void* workspace,
                               size_t workspace_bytes, int32_t* topk_idx,
                               int32_t* sparse_bt, int32_t* sparse_ctx, void* out);
+
+/*
+ * isb_write_cache - store the new tokens of a step into the paged caches.
+ *
+ * The cache write in front of the decode (ROCm/ATOM PR 2962, the commit
+ * messages under Follow-ups: the fused writer quantises K, V and the index key
+ * straight into the MXFP4 / fp8 pages; a layer that reuses another layer's
+ * top-k writes K and V only).  Token t = r q + i is stored at position
+ * p = seq_lens[r] - q + i of request r (seq_lens count the new tokens), in
+ * block block_table[r][p div 128], slot p mod 128; tokens with p < 0 (pad
+ * requests) are skipped.  Encodings:
+ *   ISB_FP8_E4M3  the e4m3fn code of x / scale (the quotient formed in fp32),
+ *                 rounded to nearest with ties to the even code, magnitudes
+ *                 above 448 saturated, NaN stored as 0x7F, the sign kept;
+ *   ISB_MXFP4     per 32 dims an e8m0 exponent floor(log2 amax) - 2, clamped to
+ *                 [-127, 127] (-127 for an all-zero group), and each element's
+ *                 e2m1 code of x / 2^exponent, rounded to nearest with ties to
+ *                 the even code, saturated at 6 (OCP MX v1.0);
+ *   ISB_BF16      the value as given.
+ * Only the bytes of the written tokens change; QK-norm and rope are not
+ * applied (the vectors are stored as given).
+ *
+ *   k_new, v_new  [T][num_kv_heads][128] bf16, 4-byte aligned
+ *   idx_new       [T][128] bf16, or NULL (then idx_pool must be NULL too and
+ *                 the index arguments are ignored)
+ *   block_table   [num_reqs][block_table_stride] int32 block ids
+ *   seq_lens      [num_reqs] int32
+ *   k_pool, v_pool  in/out, [num_pages][num_kv_heads] pages of kv_dtype
+ *                 (layout above: a bf16 / fp8 block is pages 8 b .. 8 b + 7);
+ *                 k_scale / v_scale > 0 for fp8
+ *   idx_pool      in/out, [idx_pool_blocks] index pages of idx_dtype;
+ *                 idx_scale > 0 for fp8
+ * Positions past the table (p div 128 >= block_table_stride) and block ids
+ * whose pages fall outside the pools are skipped, never written.  Calls that
+ * write the same slot must not overlap in time.  Shape errors: num_kv_heads >
+ * 65535, num_reqs * decode_query_len > 2^31 - 1.
+ */
+ISB_API int isb_write_cache(isb_stream_t stream, const void* k_new, const void* v_new,
+                            const void* idx_new, const int32_t* block_table,
+                            int block_table_stride, const int32_t* seq_lens, int num_reqs,
+                            int decode_query_len, int num_kv_heads, void* k_pool, void* v_pool,
+                            int kv_dtype, float k_scale, float v_scale, int64_t num_pages,
+                            void* idx_pool, int idx_dtype, float idx_scale,
+                            int64_t idx_pool_blocks);
+
+/*
+ * isb_quantize_e4m3 - out[i] = the e4m3fn code of x[i] with a unit scale
+ * (rounding and saturation as ISB_FP8_E4M3 of isb_write_cache), for n bf16
+ * elements.  The query cast of the same fused writer (ROCm/ATOM PR 2962,
+ * Follow-ups: the main query, and optionally the index query, come back as
+ * float8_e4m3fn with a unit, saturating scale); its output is a valid
+ * ISB_FP8_E4M3 query for isb_index_score and isb_sparse_pa_decode.
+ */
+ISB_API int isb_quantize_e4m3(isb_stream_t stream, const void* x, int64_t n, void* out);
 
 #ifdef __cplusplus
 }

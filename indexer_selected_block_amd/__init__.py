@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     emit_sparse_block_table,
     index_score,
     load_library,
+    quantize_e4m3,
     select_attend,
     sparse_pa_decode,
     sparse_pa_workspace_bytes,
@@ -17,4 +18,5 @@ from .binding import (  # noqa: F401
     topk_select,
     topk_select_emit,
     version,
+    write_cache,
 )

@@ -66,6 +66,9 @@ _SIGNATURES = {
     "isb_sparse_pa_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
     "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I,
                               _F, _P, _SZ, _P], _I),
+    "isb_write_cache": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _F, _F, _I64, _P, _I, _F, _I64],
+                        _I),
+    "isb_quantize_e4m3": ([_P, _P, _I64, _P], _I),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -231,6 +234,53 @@ def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_d
           float(k_scale), float(v_scale), num_q_heads, float(sm_scale), workspace.data_ptr(),
           workspace.numel(), topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr(), out.data_ptr())
     return topk_idx, sparse_bt, sparse_ctx, out
+
+
+def write_cache(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len, k_pool, v_pool, kv_dtype,
+                k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0):
+    """Stores the step's new K, V (and index keys, unless idx_new is None) into
+    the pools, in place (see isb_write_cache)."""
+    if (idx_new is None) != (idx_pool is None):
+        raise ValueError("idx_new and idx_pool go together")
+    dev = _dev(k_new, v_new, block_table, seq_lens, k_pool, v_pool,
+               *(() if idx_new is None else (idx_new, idx_pool)))
+    R, H_kv = seq_lens.shape[0], k_new.shape[1]
+    T = R * decode_query_len
+    if k_new.shape != (T, H_kv, 128) or v_new.shape != (T, H_kv, 128) or \
+            (idx_new is not None and idx_new.shape != (T, 128)):
+        raise ValueError("k_new, v_new [T, H_kv, 128] and idx_new [T, 128] with T = num_reqs * query_len")
+    for t in (k_new, v_new) + (() if idx_new is None else (idx_new,)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("new keys and values are bf16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_table.shape[0] != R:
+        raise ValueError("block_table [num_reqs, stride] and seq_lens [num_reqs] are int32")
+    kv_page = {BF16: 4096, FP8_E4M3: 2048, MXFP4: 8704}.get(_code(kv_dtype))
+    idx_page = {BF16: 32768, FP8_E4M3: 16384, MXFP4: 8704}.get(_code(idx_dtype))
+    for pool, row in ((k_pool, kv_page and H_kv * kv_page), (v_pool, kv_page and H_kv * kv_page)) + \
+            (() if idx_pool is None else ((idx_pool, idx_page),)):
+        if row and (pool.dtype != torch.uint8 or pool.numel() != pool.shape[0] * row):
+            raise ValueError("pools are uint8 [pages, page bytes (times H_kv for K / V)]")
+    _call("write_cache", _stream(dev), k_new.data_ptr(), v_new.data_ptr(),
+          None if idx_new is None else idx_new.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+          seq_lens.data_ptr(), R, decode_query_len, H_kv, k_pool.data_ptr(),
+          v_pool.data_ptr(), _code(kv_dtype), float(k_scale), float(v_scale), k_pool.shape[0],
+          None if idx_pool is None else idx_pool.data_ptr(), _code(idx_dtype), float(idx_scale),
+          0 if idx_pool is None else idx_pool.shape[0])
+
+
+def quantize_e4m3(x, out=None):
+    """uint8 e4m3fn codes of a bf16 tensor, unit scale (see isb_quantize_e4m3)."""
+    dev = _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    _dev(out)
+    if out.numel() != x.numel():
+        raise ValueError("out must have x's size")
+    if x.numel():
+        _call("quantize_e4m3", _stream(dev), x.data_ptr(), x.numel(), out.data_ptr())
+    return out
 
 
 class DecodeLayer:

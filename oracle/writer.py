@@ -10,15 +10,18 @@ with a unit scale, saturating).  Readings where the sources are silent:
 * placement - token i of request r's q new tokens sits at absolute position
   seq_lens[r] - q + i (the lengths include the new tokens); a position below
   zero (a pad request) is not written;
-* e4m3fn encoding - round to nearest, ties to the even code, magnitudes above
-  448 saturate to 448, NaN becomes 0x7F; the sign is kept (a negative value
-  that rounds to zero is -0), as in every encoding here;
+* e4m3fn encoding - of x / scale formed in fp32 (the precision the kernel
+  decides in): round to nearest, ties to the even code, magnitudes above 448
+  saturate to 448, NaN becomes 0x7F; the sign is kept (a negative value that
+  rounds to zero is -0), as in every encoding here;
 * MXFP4 encoding (OCP MX v1.0) - per 32 consecutive dims the shared exponent
   is floor(log2 amax) - 2 (2 is the largest e2m1 exponent), clamped to the
   e8m0 range [-127, 127] (-127 for an all-zero group); each element's e2m1
   code rounds x / 2^exponent to nearest, ties to the even code, and magnitudes
   above 6 saturate to 6;
 * bf16 values are stored as given;
+* a layer that reuses another layer's top-k has no index key to write: the
+  writer then takes no index vector and leaves the index pool alone;
 * QK-norm and rope are not part of this writer: it stores the vectors it is
   given.
 
@@ -99,7 +102,10 @@ def _element_bytes(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
     """[..., 128] values -> [..., 128, e] stored bytes for bf16 / fp8."""
     if dtype == "bf16":
         return _bf16_bytes(x)
-    return encode_e4m3(np.asarray(x, dtype=np.float64) / scale)[..., None]
+    # the quotient is rounded to fp32 before the e4m3 rounding, as the kernel
+    # forms it: both sides take the rounding decision on the same number
+    y = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    return encode_e4m3(y.astype(np.float64))[..., None]
 
 
 def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,
@@ -107,15 +113,21 @@ def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,
                 idx_pool: np.ndarray, idx_dtype: str, idx_scale: float) -> None:
     """Writes the new tokens into the pools, in place.
 
-    k_new, v_new [T, H_kv, 128] and idx_new [T, 128] hold the values (floats;
-    bf16 caches take values that bf16 represents exactly); the pools are the
+    k_new, v_new [T, H_kv, 128] and idx_new [T, 128] (or None: no index key)
+    hold the values (floats; bf16 caches take values that bf16 represents
+    exactly); the pools are the
     contiguous byte arrays the readers of ``pools`` take (K/V: pages of
     H_kv heads each, head g of page id n at (n H_kv + g) page bytes; index
     cache: one page per block)."""
     T, H_kv, _ = np.shape(k_new)
-    k_new, v_new, idx_new = (np.asarray(a, dtype=np.float64) for a in (k_new, v_new, idx_new))
-    kf, vf, xf = (np.asarray(a).reshape(-1) for a in (k_pool, v_pool, idx_pool))  # flat byte views
-    assert all(np.shares_memory(a, b) for a, b in ((kf, k_pool), (vf, v_pool), (xf, idx_pool)))
+    with_idx = idx_new is not None
+    k_new, v_new = (np.asarray(a, dtype=np.float64) for a in (k_new, v_new))
+    kf, vf = (np.asarray(a).reshape(-1) for a in (k_pool, v_pool))  # flat byte views
+    assert np.shares_memory(kf, k_pool) and np.shares_memory(vf, v_pool)
+    if with_idx:
+        idx_new = np.asarray(idx_new, dtype=np.float64)
+        xf = np.asarray(idx_pool).reshape(-1)
+        assert np.shares_memory(xf, idx_pool)
     for t in range(T):
         r, i = divmod(t, q_len)
         p = int(seq_lens[r]) - q_len + i
@@ -123,7 +135,9 @@ def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,
             continue
         blk, slot = int(block_table[r][p // pools.BLOCK]), p % pools.BLOCK
         # index key: one per token, no head dimension; page id = block id
-        if idx_dtype == "mxfp4":
+        if not with_idx:
+            pass
+        elif idx_dtype == "mxfp4":
             codes, scales = mx_quantize(idx_new[t])
             _mxfp4_put(xf, blk * formats.MXFP4_PAGE_BYTES, slot, codes, scales)
         else:

@@ -1,0 +1,226 @@
+"""GPU parity of the cache writer and the e4m3 query cast against the oracle.
+
+Both sides start from the same pool bytes and the same bf16 new tokens; the
+pools the GPU writes must equal the oracle's byte for byte (integer work:
+bit-exact), including the pages no token touches.  The inputs mix normal
+values with the encodings' edge cases: ties between adjacent codes, values
+past the saturation points, subnormal e4m3 values, signed zeros, all-zero MX
+groups and NaN (fp8 only).  Full-size cases write one step of new tokens into
+the decode workloads' own pools and compare the touched pages against the
+oracle run on those pages alone, then check that no other byte changed.
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_block_amd as isb
+from indexer_selected_block_amd import workload as wl
+from oracle import formats, writer
+
+pytestmark = pytest.mark.gpu
+
+KV_PAGE = {"bf16": 4096, "fp8": 2048, "mxfp4": formats.MXFP4_PAGE_BYTES}
+IDX_PAGE = {"bf16": 32768, "fp8": 16384, "mxfp4": formats.MXFP4_PAGE_BYTES}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a ROCm GPU")
+    isb.load_library()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _edge_values(rng, n, dtype):
+    """n bf16 values: normals at mixed magnitudes plus the encodings' edge cases."""
+    x = rng.standard_normal(n) * np.exp2(rng.integers(-6, 6, n))
+    e4m3 = np.array([formats.e4m3_value(c) for c in range(0x7F)])
+    specials = np.concatenate([
+        (e4m3[:-1] + e4m3[1:]) / 2,                  # e4m3 ties (exact in bf16)
+        [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0],     # e2m1 ties at a group scale of 1
+        [448.0, 464.0, 1e4, 2.0 ** -10, 2.0 ** -9 * 3, -0.0, 0.0]])
+    k = min(len(specials), n // 2)
+    pos = rng.choice(n, size=k, replace=False)
+    x[pos] = rng.permutation(specials)[:k] * rng.choice([-1, 1], k)
+    if dtype == "fp8" and n >= 8:
+        x[rng.choice(n, size=2, replace=False)] = np.nan
+    return x
+
+
+# An MX group whose maximum 4 gives it the exponent 0, holding every e2m1 tie
+# (then scaled by 2^s: the same ties at the exponent s).
+_MX_TIES = np.array([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 4) * np.tile([1, 1, 1, 1, -1, -1, -1, -1], 4)
+
+
+def _new_tokens(rng, T, H_kv, kv_dtype, idx_dtype):
+    def bf16(a):
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+
+    k = bf16(_edge_values(rng, T * H_kv * 128, kv_dtype).reshape(T, H_kv, 128))
+    v = bf16(_edge_values(rng, T * H_kv * 128, kv_dtype).reshape(T, H_kv, 128))
+    i = bf16(_edge_values(rng, T * 128, idx_dtype).reshape(T, 128))
+    if kv_dtype == "mxfp4" and T:
+        k[0, 0, :32] = 0                                     # an all-zero MX group
+        k[0, 0, 32:64] = torch.from_numpy(_MX_TIES).to(torch.bfloat16)
+        v[-1, -1, 96:] = torch.from_numpy(_MX_TIES * 2.0 ** -20).to(torch.bfloat16)
+    if idx_dtype == "mxfp4" and T:
+        i[0, 64:96] = torch.from_numpy(_MX_TIES * 2.0 ** -3).to(torch.bfloat16)
+    return k, v, i
+
+
+def _host(t):
+    return t.float().double().numpy()
+
+
+CASES = {
+    # name: (kv dtype, index dtype, H_kv, query_len, seq_lens, table width, pool blocks)
+    "fp8_fp8_decode": ("fp8", "fp8", 1, 1, [300, 1, 0, 4097, 128], 40, 64),
+    "fp8_fp8_spec_h2": ("fp8", "fp8", 2, 4, [300, 2, 0, 4097, 129, 3], 40, 64),
+    "bf16_bf16": ("bf16", "bf16", 2, 3, [300, 2, 0, 1000], 10, 48),
+    "mxfp4_mxfp4": ("mxfp4", "mxfp4", 1, 4, [300, 2, 0, 4097, 129], 40, 64),
+    "mxfp4_mxfp4_h2": ("mxfp4", "mxfp4", 2, 3, [260, 2, 0, 900], 10, 48),
+    "fp8_kv_mxfp4_idx": ("fp8", "mxfp4", 1, 2, [300, 1, 0, 513], 8, 40),
+    "bf16_kv_fp8_idx": ("bf16", "fp8", 1, 5, [640, 4, 0, 700], 8, 40),
+    "mxfp4_kv_bf16_idx": ("mxfp4", "bf16", 2, 2, [130, 1, 0, 257], 8, 40),
+    "prefill_chunk": ("fp8", "fp8", 1, 150, [600, 149, 0, 2000], 16, 48),
+}
+
+
+def _case_inputs(name):
+    kv, idt, H, q, lens, width, nblk = CASES[name]
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    R = len(lens)
+    # each request's blocks distinct from every other's (no two tokens share a
+    # slot); table entries past a request's blocks hold arbitrary ids
+    bt = rng.integers(0, nblk, (R, width)).astype(np.int32)
+    need = [-(-L // 128) for L in lens]
+    assert sum(need) <= nblk and max(need) <= width
+    ids = rng.permutation(nblk)
+    for r in range(R):
+        bt[r, :need[r]] = ids[sum(need[:r]):sum(need[:r + 1])]
+    npages = nblk * (8 if kv != "mxfp4" else 1)
+    pools = dict(k=rng.integers(0, 256, (npages, H * KV_PAGE[kv]), dtype=np.uint8),
+                 v=rng.integers(0, 256, (npages, H * KV_PAGE[kv]), dtype=np.uint8),
+                 i=rng.integers(0, 256, (nblk, IDX_PAGE[idt]), dtype=np.uint8))
+    k_new, v_new, i_new = _new_tokens(rng, R * q, H, kv, idt)
+    return kv, idt, H, q, np.array(lens, np.int32), bt, pools, (k_new, v_new, i_new)
+
+
+def _gpu_write(kv, idt, q, lens, bt, pools, news, ks, vs, xs, with_idx=True):
+    dev = "cuda"
+    d = {n: torch.from_numpy(a).to(dev) for n, a in pools.items()}
+    k_new, v_new, i_new = (t.to(dev) for t in news)
+    isb.write_cache(k_new, v_new, i_new if with_idx else None, torch.from_numpy(bt).to(dev),
+                    torch.from_numpy(lens).to(dev), q, d["k"], d["v"], kv, ks, vs,
+                    d["i"] if with_idx else None, idt, xs)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy() for n, t in d.items()}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_write_cache_bit_exact(name):
+    kv, idt, H, q, lens, bt, pools, news = _case_inputs(name)
+    # unit scales in the decode case: the e4m3 ties among the inputs stay ties
+    ks, vs, xs = (1.0, 1.0, 1.0) if name.endswith("decode") else (0.013, 0.021, 0.037)
+    _say(f"write_cache {name}: kv {kv} idx {idt} H_kv {H} q {q} lens {lens.tolist()}")
+    got = _gpu_write(kv, idt, q, lens, bt, pools, news, ks, vs, xs)
+    ref = {n: a.copy() for n, a in pools.items()}
+    writer.write_cache(_host(news[0]), _host(news[1]), _host(news[2]), bt, lens, q, ref["k"], ref["v"], kv,
+                       ks, vs, ref["i"], idt, xs)
+    for n in ("k", "v", "i"):
+        bad = np.argwhere(got[n] != ref[n])
+        assert bad.size == 0, f"pool {n}: {len(bad)} bytes differ, first at {bad[:4].tolist()}"
+    assert any(not np.array_equal(got[n], pools[n]) for n in ("k", "v", "i"))
+
+
+@pytest.mark.parametrize("name", ["fp8_fp8_spec_h2", "mxfp4_mxfp4"])
+def test_write_cache_without_index_key(name):
+    kv, idt, H, q, lens, bt, pools, news = _case_inputs(name)
+    _say(f"write_cache (no index key) {name}")
+    got = _gpu_write(kv, idt, q, lens, bt, pools, news, 0.02, 0.03, 0.05, with_idx=False)
+    ref = {n: a.copy() for n, a in pools.items()}
+    writer.write_cache(_host(news[0]), _host(news[1]), None, bt, lens, q, ref["k"], ref["v"], kv, 0.02, 0.03,
+                       ref["i"], idt, 0.05)
+    for n in ("k", "v", "i"):
+        assert np.array_equal(got[n], ref[n]), n
+    assert np.array_equal(got["i"], pools["i"])
+
+
+def test_write_cache_skips_blocks_outside_the_pools():
+    # a table row whose ids fall outside the pools writes nothing; the rest is
+    # written as if that request were a pad request
+    kv, idt, H, q, lens, bt, pools, news = _case_inputs("fp8_fp8_spec_h2")
+    bt_bad = bt.copy()
+    bt_bad[3] = 64 + np.arange(bt.shape[1])                  # 64 blocks in the pools
+    bt_bad[0, 2] = -1                                        # request 0 writes at positions 296..299
+    _say("write_cache out-of-pool ids")
+    got = _gpu_write(kv, idt, q, lens, bt_bad, pools, news, 0.02, 0.03, 0.05)
+    lens_ref = lens.copy()
+    lens_ref[[0, 3]] = 0
+    ref = {n: a.copy() for n, a in pools.items()}
+    writer.write_cache(_host(news[0]), _host(news[1]), _host(news[2]), bt, lens_ref, q, ref["k"], ref["v"], kv,
+                       0.02, 0.03, ref["i"], idt, 0.05)
+    for n in ("k", "v", "i"):
+        assert np.array_equal(got[n], ref[n]), n
+
+
+# The writer of the decode workloads at their full sizes: one step of new
+# tokens, every request's tokens written into the workload's own pools.
+FULL = ["fp8_decode", "spec_decode", "mxfp4"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_write_cache_full_size(name):
+    cfg = wl.CONFIGS[name]
+    w = wl.make_workload(cfg, device="cuda")
+    rng = np.random.default_rng(11)
+    T, H, q = cfg.num_tokens, cfg.num_kv_heads, cfg.query_len
+    news = _new_tokens(rng, T, H, cfg.kv_dtype, cfg.idx_dtype)
+    lens = w.seq_lens.cpu().numpy()
+    bt = w.block_table.cpu().numpy()
+    blocks = sorted({int(bt[r, p // 128]) for r in range(len(lens))
+                     for p in range(max(0, int(lens[r]) - q), int(lens[r]))})
+    _say(f"write_cache full {name}: T {T} blocks touched {len(blocks)}")
+    ppb = 1 if cfg.kv_dtype == "mxfp4" else 8
+    kv_rows = torch.tensor([ppb * b + j for b in blocks for j in range(ppb)], device="cuda")
+    ix_rows = torch.tensor(blocks, device="cuda")
+    before = dict(k=w.k_pool.clone(), v=w.v_pool.clone(), i=w.idx_pool.clone())
+    isb.write_cache(*(t.cuda() for t in news), w.block_table, w.seq_lens, q, w.k_pool, w.v_pool, cfg.kv_dtype,
+                    w.k_scale, w.v_scale, w.idx_pool, cfg.idx_dtype, w.idx_scale)
+    torch.cuda.synchronize()
+    # the oracle on the touched pages alone, block ids renumbered 0..n-1
+    remap = np.full(int(bt.max()) + 1, -1, np.int64)
+    remap[blocks] = np.arange(len(blocks))
+    bt_c = np.where(bt >= 0, remap[np.clip(bt, 0, None)], -1)
+    ref = dict(k=before["k"][kv_rows].cpu().numpy(), v=before["v"][kv_rows].cpu().numpy(),
+               i=before["i"][ix_rows].cpu().numpy())
+    writer.write_cache(_host(news[0]), _host(news[1]), _host(news[2]), bt_c, lens, q, ref["k"], ref["v"],
+                       cfg.kv_dtype, w.k_scale, w.v_scale, ref["i"], cfg.idx_dtype, w.idx_scale)
+    got = dict(k=w.k_pool[kv_rows].cpu().numpy(), v=w.v_pool[kv_rows].cpu().numpy(),
+               i=w.idx_pool[ix_rows].cpu().numpy())
+    for n in ("k", "v", "i"):
+        assert np.array_equal(got[n], ref[n]), n
+    # every other byte of the pools is unchanged
+    before["k"][kv_rows] = w.k_pool[kv_rows]
+    before["v"][kv_rows] = w.v_pool[kv_rows]
+    before["i"][ix_rows] = w.idx_pool[ix_rows]
+    assert torch.equal(before["k"], w.k_pool) and torch.equal(before["v"], w.v_pool)
+    assert torch.equal(before["i"], w.idx_pool)
+
+
+@pytest.mark.parametrize("n", [1, 255, 1024, 1025, 128 * 1024 * 16 + 3])
+def test_quantize_e4m3_bit_exact(n):
+    rng = np.random.default_rng(n)
+    x = torch.from_numpy(_edge_values(rng, n, "fp8").astype(np.float32)).to(torch.bfloat16)
+    x[:1] = float("inf") if n > 4 else x[:1]
+    _say(f"quantize_e4m3 n {n}")
+    got = isb.quantize_e4m3(x.cuda()).cpu().numpy()
+    ref = writer.quantize_query_e4m3(_host(x))
+    assert np.array_equal(got, ref)

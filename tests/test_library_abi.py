@@ -29,7 +29,8 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("isb_index_score", "isb_topk_select", "isb_emit_sparse_block_table",
-              "isb_sparse_pa_decode", "isb_sparse_pa_workspace_bytes", "isb_strerror", "isb_version"):
+              "isb_sparse_pa_decode", "isb_sparse_pa_workspace_bytes", "isb_strerror", "isb_version",
+              "isb_write_cache", "isb_quantize_e4m3"):
         assert n in names
 
 
@@ -90,6 +91,18 @@ def test_argument_checks_return_before_any_launch(lib):
                                     p, 1 << 20, p) == -3                                         # head_dim
     assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 32, 1, 128, 0.1,
                                     p, 1 << 20, p) == -3                                         # G = 32
+    # the cache writer and the query cast
+    w = lambda k=p, idx=p, ipool=p, H=1, kvdt=1, ks=1.0, idt=1, xs=1.0, q=1: lib.isb_write_cache(  # noqa: E731
+        NULL, k, p, idx, p, 4, p, 2, q, H, p, p, kvdt, ks, 1.0, 64, ipool, idt, xs, 8)
+    assert w(k=NULL) == -1
+    assert w(idx=NULL) == -1 and w(ipool=NULL) == -1            # index vector and pool go together
+    assert w(q=0) == -1
+    assert w(kvdt=5) == -2 and w(idt=3) == -2
+    assert w(ks=0.0) == -1 and w(xs=-1.0) == -1                 # fp8 scales must be positive
+    assert w(H=70000) == -3
+    assert w(k=ctypes.c_void_p(18)) == -1                       # bf16 pairs are read 4 bytes at a time
+    assert lib.isb_quantize_e4m3(NULL, NULL, 4, p) == -1
+    assert lib.isb_quantize_e4m3(NULL, p, 0, p) == -1
     # workspace
     need = lib.isb_sparse_pa_workspace_bytes(4, 16, 1, 128, 1)
     assert need > 0

@@ -96,7 +96,8 @@ def test_writer_reads_back_through_the_page_readers(kv_dtype, idx_dtype):
         if dtype == "bf16":
             return x
         if dtype == "fp8":
-            return formats.decode_e4m3(writer.encode_e4m3(x / scale)) * scale
+            y = (x.astype(np.float32) / np.float32(scale)).astype(np.float64)
+            return formats.decode_e4m3(writer.encode_e4m3(y)) * scale
         c, sc = writer.mx_quantize(x)
         return formats.decode_e2m1(c) * np.repeat(formats.decode_e8m0(sc), 32, axis=-1)
 
@@ -124,6 +125,21 @@ def test_writer_reads_back_through_the_page_readers(kv_dtype, idx_dtype):
     for n in range(nblk):
         if n not in touched_i:
             assert np.array_equal(idx_pool[n], i0[n])
+
+
+def test_writer_without_index_key_leaves_the_index_pool_and_writes_the_same_kv():
+    rng = np.random.default_rng(4)
+    bt, seq_lens = np.array([[1, 0]]), np.array([200])
+    k_new, v_new = rng.standard_normal((2, 2, 1, 128))          # two tokens, one KV head each
+    idx_new = rng.standard_normal((2, 128))
+    pools_a = [np.zeros((16, 2048), np.uint8), np.zeros((16, 2048), np.uint8), np.zeros((2, 16384), np.uint8)]
+    pools_b = [a.copy() for a in pools_a]
+    writer.write_cache(k_new, v_new, idx_new, bt, seq_lens, 2, pools_a[0], pools_a[1], "fp8", 0.1, 0.1,
+                       pools_a[2], "fp8", 0.1)
+    writer.write_cache(k_new, v_new, None, bt, seq_lens, 2, pools_b[0], pools_b[1], "fp8", 0.1, 0.1,
+                       pools_b[2], "fp8", 0.1)
+    assert np.array_equal(pools_a[0], pools_b[0]) and np.array_equal(pools_a[1], pools_b[1])
+    assert pools_a[2].any() and not pools_b[2].any()
 
 
 def test_query_cast_is_unit_scale_saturating_e4m3():
