@@ -19,4 +19,5 @@ from .binding import (  # noqa: F401
     topk_select_emit,
     version,
     write_cache,
+    write_cache_launcher,
 )

@@ -240,6 +240,20 @@ def write_cache(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len, 
                 k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0):
     """Stores the step's new K, V (and index keys, unless idx_new is None) into
     the pools, in place (see isb_write_cache)."""
+    _call("write_cache", *_write_cache_args(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len,
+                                            k_pool, v_pool, kv_dtype, k_scale, v_scale, idx_pool, idx_dtype,
+                                            idx_scale))
+
+
+def write_cache_launcher(*args, **kwargs):
+    """write_cache's arguments checked once: returns a callable that enqueues
+    the same write again (same tensors, same stream) with no further checks."""
+    a = _write_cache_args(*args, **kwargs)
+    return lambda: _call("write_cache", *a)
+
+
+def _write_cache_args(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len, k_pool, v_pool, kv_dtype,
+                      k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0):
     if (idx_new is None) != (idx_pool is None):
         raise ValueError("idx_new and idx_pool go together")
     dev = _dev(k_new, v_new, block_table, seq_lens, k_pool, v_pool,
@@ -260,12 +274,12 @@ def write_cache(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len, 
             (() if idx_pool is None else ((idx_pool, idx_page),)):
         if row and (pool.dtype != torch.uint8 or pool.numel() != pool.shape[0] * row):
             raise ValueError("pools are uint8 [pages, page bytes (times H_kv for K / V)]")
-    _call("write_cache", _stream(dev), k_new.data_ptr(), v_new.data_ptr(),
-          None if idx_new is None else idx_new.data_ptr(), block_table.data_ptr(), block_table.shape[1],
-          seq_lens.data_ptr(), R, decode_query_len, H_kv, k_pool.data_ptr(),
-          v_pool.data_ptr(), _code(kv_dtype), float(k_scale), float(v_scale), k_pool.shape[0],
-          None if idx_pool is None else idx_pool.data_ptr(), _code(idx_dtype), float(idx_scale),
-          0 if idx_pool is None else idx_pool.shape[0])
+    return (_stream(dev), k_new.data_ptr(), v_new.data_ptr(),
+            None if idx_new is None else idx_new.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+            seq_lens.data_ptr(), R, decode_query_len, H_kv, k_pool.data_ptr(),
+            v_pool.data_ptr(), _code(kv_dtype), float(k_scale), float(v_scale), k_pool.shape[0],
+            None if idx_pool is None else idx_pool.data_ptr(), _code(idx_dtype), float(idx_scale),
+            0 if idx_pool is None else idx_pool.shape[0])
 
 
 def quantize_e4m3(x, out=None):

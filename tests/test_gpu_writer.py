@@ -224,3 +224,73 @@ def test_quantize_e4m3_bit_exact(n):
     got = isb.quantize_e4m3(x.cuda()).cpu().numpy()
     ref = writer.quantize_query_e4m3(_host(x))
     assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ top-k reuse and the e4m3 index query
+def test_reusing_layer_writes_kv_only_and_attends_with_the_source_selection():
+    # A layer that reuses another layer's top-k: it writes its new K and V (no
+    # index key) into caches of its own and attends with the source layer's
+    # sparse table, with no scorer or selector of its own.  The source
+    # selection comes from seeded scores, selected on both sides (the GPU's
+    # bit-exact), the reusing layer's caches from the two writers.
+    from _util import attended_vmax, attn_tol, host_inputs, oracle_attention, small_configs
+    from oracle import decode as od
+
+    cfg = small_configs()["spec_decode"]
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    T, H, q = cfg.num_tokens, cfg.num_kv_heads, cfg.query_len
+    rng = np.random.default_rng(31)
+    scores = rng.standard_normal((H, T, cfg.max_blocks)).astype(np.float32)
+    _say(f"top-k reuse: {cfg.name} T {T}")
+    # source layer's selection
+    topk_ref = od.topk_select(scores, hi["seq_lens"], q, cfg.top_k)
+    sbt_ref, sctx_ref = od.emit_sparse_block_table(topk_ref, hi["block_table"], hi["seq_lens"], q, H, cfg.top_k,
+                                                   cfg.pages_per_block)
+    _, sbt, sctx = isb.topk_select_emit(torch.from_numpy(scores).cuda(), w.seq_lens, q, cfg.top_k, w.block_table,
+                                        cfg.pages_per_block)
+    torch.cuda.synchronize()
+    assert np.array_equal(sbt.cpu().numpy(), sbt_ref) and np.array_equal(sctx.cpu().numpy(), sctx_ref)
+    # reusing layer: its own caches (a copy of the source's), its new tokens, its query
+    k_pool, v_pool = w.k_pool.clone(), w.v_pool.clone()
+    news = [torch.from_numpy(rng.standard_normal((T, H, 128)).astype(np.float32)).to(torch.bfloat16)
+            for _ in range(2)]                               # finite values: the attention is compared
+    isb.write_cache(news[0].cuda(), news[1].cuda(), None, w.block_table, w.seq_lens, q, k_pool, v_pool,
+                    cfg.kv_dtype, w.k_scale, w.v_scale)
+    qB = torch.from_numpy(rng.standard_normal((T, cfg.num_q_heads, 128)).astype(np.float32)).to(torch.bfloat16)
+    out = isb.sparse_pa_decode(qB.cuda(), "bf16", k_pool, v_pool, cfg.kv_dtype, w.k_scale, w.v_scale, sbt, sctx,
+                               cfg.num_q_heads, H, w.sm_scale)
+    torch.cuda.synchronize()
+    hB = dict(hi, q=_host(qB), k_pool=hi["k_pool"].copy(), v_pool=hi["v_pool"].copy())
+    writer.write_cache(_host(news[0]), _host(news[1]), None, hi["block_table"], hi["seq_lens"], q, hB["k_pool"],
+                       hB["v_pool"], cfg.kv_dtype, hi["k_scale"], hi["v_scale"], None, "bf16", 1.0)
+    assert np.array_equal(k_pool.cpu().numpy(), hB["k_pool"]) and np.array_equal(v_pool.cpu().numpy(), hB["v_pool"])
+    ref = oracle_attention(hB, sbt_ref, sctx_ref)
+    got = out.float().cpu().numpy()
+    tol = attn_tol(cfg.kv_dtype, attended_vmax(hB, sbt_ref, sctx_ref))
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"max |err| {err:.4g} > {tol:.4g}"
+
+
+def test_e4m3_index_query_from_the_cast_scores_like_the_oracle():
+    # The e4m3 index query: a bf16 query cast by isb_quantize_e4m3, then scored
+    # against the MXFP4 index cache; the oracle casts with its own encoder.
+    from _util import assert_scores_close, host_inputs, small_configs
+    from oracle import decode as od
+
+    cfg = small_configs()["mxfp4"]
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    rng = np.random.default_rng(32)
+    q_bf16 = torch.from_numpy((rng.standard_normal((cfg.num_tokens, cfg.num_idx_heads, 128)) * 4)
+                              .astype(np.float32)).to(torch.bfloat16)
+    _say(f"e4m3 index query: {cfg.name}")
+    q8 = isb.quantize_e4m3(q_bf16.cuda())
+    scores = isb.index_score(q8, "e4m3", w.idx_pool, cfg.idx_dtype, w.idx_scale, w.block_table, w.seq_lens,
+                             cfg.query_len, cfg.num_kv_heads, cfg.max_blocks)
+    torch.cuda.synchronize()
+    codes = writer.quantize_query_e4m3(_host(q_bf16))
+    assert np.array_equal(q8.cpu().numpy(), codes)
+    ref = od.index_score(formats.decode_e4m3(codes), hi["idx_pool"], cfg.idx_dtype, hi["idx_scale"],
+                         hi["block_table"], hi["seq_lens"], cfg.query_len, cfg.num_kv_heads, cfg.max_blocks)
+    assert_scores_close(scores.cpu().numpy(), ref)
