@@ -149,3 +149,42 @@ def sample_requests(w, reqs):
         idx_pool=idx_pool, k_pool=k_pool, v_pool=v_pool, idx_scale=w.idx_scale,
         k_scale=w.k_scale, v_scale=w.v_scale, sm_scale=w.sm_scale)
     return hi, toks
+
+
+def check_chain(hi, scores_gpu, topk_gpu, sbt_gpu, sctx_gpu, out_gpu, ref, bt_global, toks=None):
+    """A GPU layer's scores, selection, table and output against the oracle layer's:
+    selections may differ only where the scores are within their tolerance."""
+    cfg = hi["cfg"]
+    ql, H_kv, K = cfg.query_len, cfg.num_kv_heads, cfg.top_k
+    T = len(hi["seq_lens"]) * ql
+    assert_scores_close(scores_gpu, ref["scores"])
+    with np.errstate(invalid="ignore"):
+        err_row = np.where(np.isfinite(ref["scores"]), np.abs(scores_gpu - ref["scores"]), 0).max(axis=-1)
+    agree = np.zeros((H_kv, T), dtype=bool)
+    for g in range(H_kv):
+        for t in range(T):
+            r, i = divmod(t, ql)
+            nt = od.num_blocks(od.causal_length(hi["seq_lens"][r], ql, i))
+            if np.array_equal(topk_gpu[g, t], ref["topk"][g, t]):
+                agree[g, t] = True
+            else:
+                tol = 2 * err_row[g, t] + 1e-12
+                assert selection_margin_ok(ref["scores"][g, t], nt, K, list(topk_gpu[g, t]), tol), \
+                    f"row ({g},{t}): GPU selection is not a top-{K} of the oracle scores"
+    assert agree.mean() >= 0.9, f"only {agree.mean():.2%} of selections agree"
+    # the table the GPU emitted from its own selection, checked against the oracle's emit
+    sbt_ref, sctx_ref = od.emit_sparse_block_table(topk_gpu, bt_global, hi["seq_lens"], ql, H_kv, K,
+                                                   cfg.pages_per_block)
+    assert np.array_equal(sbt_gpu, sbt_ref) and np.array_equal(sctx_gpu, sctx_ref)
+    rows = [t for t in range(T) if agree[:, t].all()]
+    vmax = attended_vmax(hi, ref["sparse_bt"], ref["sparse_ctx"])
+    err = np.abs(out_gpu[rows] - ref["out"][rows]).max() if rows else 0.0
+    assert err <= attn_tol(cfg.kv_dtype, vmax), f"attention err {err:.4g}"
+
+
+def oracle_layer(hi):
+    cfg = hi["cfg"]
+    return od.decode_layer(hi["q"], hi["q_idx"], hi["idx_pool"], cfg.idx_dtype, hi["idx_scale"],
+                           hi["k_pool"], hi["v_pool"], cfg.kv_dtype, hi["k_scale"], hi["v_scale"],
+                           hi["block_table"], hi["seq_lens"], cfg.query_len, cfg.num_kv_heads,
+                           cfg.max_blocks, cfg.top_k, cfg.pages_per_block, hi["sm_scale"])

@@ -22,8 +22,8 @@ import indexer_selected_block_amd as isb
 from indexer_selected_block_amd import workload as wl
 from oracle import decode as od
 
-from _util import (assert_scores_close, attn_tol, attended_vmax, host_inputs, oracle_attention,
-                   oracle_scores, sample_requests, selection_margin_ok, small_configs)
+from _util import (assert_scores_close, attn_tol, attended_vmax, check_chain, host_inputs, oracle_attention,
+                   oracle_layer, oracle_scores, sample_requests, small_configs)
 
 pytestmark = pytest.mark.gpu
 
@@ -416,49 +416,12 @@ def test_sparse_pa_repeat_calls_and_output_contents():
 
 
 # ------------------------------------------------------------------ chained layer
-def _check_chain(hi, scores_gpu, topk_gpu, sbt_gpu, sctx_gpu, out_gpu, ref, bt_global, toks=None):
-    cfg = hi["cfg"]
-    ql, H_kv, K = cfg.query_len, cfg.num_kv_heads, cfg.top_k
-    T = len(hi["seq_lens"]) * ql
-    assert_scores_close(scores_gpu, ref["scores"])
-    with np.errstate(invalid="ignore"):
-        err_row = np.where(np.isfinite(ref["scores"]), np.abs(scores_gpu - ref["scores"]), 0).max(axis=-1)
-    agree = np.zeros((H_kv, T), dtype=bool)
-    for g in range(H_kv):
-        for t in range(T):
-            r, i = divmod(t, ql)
-            nt = od.num_blocks(od.causal_length(hi["seq_lens"][r], ql, i))
-            if np.array_equal(topk_gpu[g, t], ref["topk"][g, t]):
-                agree[g, t] = True
-            else:
-                tol = 2 * err_row[g, t] + 1e-12
-                assert selection_margin_ok(ref["scores"][g, t], nt, K, list(topk_gpu[g, t]), tol), \
-                    f"row ({g},{t}): GPU selection is not a top-{K} of the oracle scores"
-    assert agree.mean() >= 0.9, f"only {agree.mean():.2%} of selections agree"
-    # the table the GPU emitted from its own selection, checked against the oracle's emit
-    sbt_ref, sctx_ref = od.emit_sparse_block_table(topk_gpu, bt_global, hi["seq_lens"], ql, H_kv, K,
-                                                   cfg.pages_per_block)
-    assert np.array_equal(sbt_gpu, sbt_ref) and np.array_equal(sctx_gpu, sctx_ref)
-    rows = [t for t in range(T) if agree[:, t].all()]
-    vmax = attended_vmax(hi, ref["sparse_bt"], ref["sparse_ctx"])
-    err = np.abs(out_gpu[rows] - ref["out"][rows]).max() if rows else 0.0
-    assert err <= attn_tol(cfg.kv_dtype, vmax), f"attention err {err:.4g}"
-
-
-def _oracle_layer(hi):
-    cfg = hi["cfg"]
-    return od.decode_layer(hi["q"], hi["q_idx"], hi["idx_pool"], cfg.idx_dtype, hi["idx_scale"],
-                           hi["k_pool"], hi["v_pool"], cfg.kv_dtype, hi["k_scale"], hi["v_scale"],
-                           hi["block_table"], hi["seq_lens"], cfg.query_len, cfg.num_kv_heads,
-                           cfg.max_blocks, cfg.top_k, cfg.pages_per_block, hi["sm_scale"])
-
-
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_chain(name):
     _say(f"[chain] {name}")
     w, layer, hi = _run_small(name)
-    ref = _oracle_layer(hi)
-    _check_chain(hi, layer.scores.cpu().numpy().astype(np.float64), layer.topk.cpu().numpy(),
+    ref = oracle_layer(hi)
+    check_chain(hi, layer.scores.cpu().numpy().astype(np.float64), layer.topk.cpu().numpy(),
                  layer.sparse_bt.cpu().numpy(), layer.sparse_ctx.cpu().numpy(),
                  layer.out.float().cpu().numpy(), ref, hi["block_table"])
 
@@ -519,11 +482,11 @@ def test_full_size_sampled(name):
         reqs = [int(np.nonzero(lens > 0)[0][0]), int(np.nonzero(lens > 0)[0][-1]), int(np.nonzero(lens == 0)[0][0])]
     _say(f"[full] {name}: oracle on requests {reqs}")
     hi, toks = sample_requests(w, reqs)
-    ref = _oracle_layer(hi)
+    ref = oracle_layer(hi)
     H_kv = cfg.num_kv_heads
     rows = [t * H_kv + g for t in toks for g in range(H_kv)]
     bt_global = w.block_table[reqs].cpu().numpy()
-    _check_chain(hi, layer.scores[:, toks, :].cpu().numpy().astype(np.float64),
+    check_chain(hi, layer.scores[:, toks, :].cpu().numpy().astype(np.float64),
                  layer.topk[:, toks, :].cpu().numpy(), layer.sparse_bt[rows].cpu().numpy(),
                  layer.sparse_ctx[rows].cpu().numpy(), layer.out[toks].float().cpu().numpy(), ref,
                  bt_global)

@@ -294,3 +294,40 @@ def test_e4m3_index_query_from_the_cast_scores_like_the_oracle():
     ref = od.index_score(formats.decode_e4m3(codes), hi["idx_pool"], cfg.idx_dtype, hi["idx_scale"],
                          hi["block_table"], hi["seq_lens"], cfg.query_len, cfg.num_kv_heads, cfg.max_blocks)
     assert_scores_close(scores.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ a whole decode step
+@pytest.mark.parametrize("name", ["fp8_decode", "spec_decode", "mxfp4", "tiny_bf16"])
+def test_decode_step_after_the_cache_write(name):
+    # A decode step as a server runs it: the step's new tokens written by
+    # isb_write_cache (they are each request's last tokens, so every row's tail
+    # block holds them), then the layer (index score, select + attend) over the
+    # updated caches.  The oracle writes with its own writer into the same
+    # starting caches and runs its own layer.
+    from _util import check_chain, host_inputs, oracle_layer, small_configs
+
+    cfg = small_configs()[name]
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    T, H, q = cfg.num_tokens, cfg.num_kv_heads, cfg.query_len
+
+    def bf16(*shape):
+        return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+
+    k_new, v_new, i_new = bf16(T, H, 128), bf16(T, H, 128), bf16(T, 128)
+    _say(f"decode step after the write: {name}")
+    isb.write_cache(k_new.cuda(), v_new.cuda(), i_new.cuda(), w.block_table, w.seq_lens, q, w.k_pool, w.v_pool,
+                    cfg.kv_dtype, w.k_scale, w.v_scale, w.idx_pool, cfg.idx_dtype, w.idx_scale)
+    layer = isb.DecodeLayer(w)
+    layer.run()
+    torch.cuda.synchronize()
+    writer.write_cache(_host(k_new), _host(v_new), _host(i_new), hi["block_table"], hi["seq_lens"], q,
+                       hi["k_pool"], hi["v_pool"], cfg.kv_dtype, hi["k_scale"], hi["v_scale"], hi["idx_pool"],
+                       cfg.idx_dtype, hi["idx_scale"])
+    assert np.array_equal(w.k_pool.cpu().numpy(), hi["k_pool"]) and np.array_equal(w.idx_pool.cpu().numpy(),
+                                                                                      hi["idx_pool"])
+    ref = oracle_layer(hi)
+    check_chain(hi, layer.scores.cpu().numpy().astype(np.float64), layer.topk.cpu().numpy(),
+                layer.sparse_bt.cpu().numpy(), layer.sparse_ctx.cpu().numpy(), layer.out.float().cpu().numpy(),
+                ref, hi["block_table"])
