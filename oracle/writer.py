@@ -22,8 +22,16 @@ with a unit scale, saturating).  Readings where the sources are silent:
 * bf16 values are stored as given;
 * a layer that reuses another layer's top-k has no index key to write: the
   writer then takes no index vector and leaves the index pool alone;
-* QK-norm and rope are not part of this writer: it stores the vectors it is
-  given.
+* QK-norm and rope (optional, per vector kind: K, index key, query) - the
+  pages name the fused QK-norm / rope step but none of its parameters, so the
+  caller supplies them: RMS normalisation of each 128-dim head vector,
+  y_d = w_d x_d / sqrt(mean(x^2) + eps), then the rotation of dim pairs
+  (a, b) -> (a cos - b sin, b cos + a sin) at the token's position p, with
+  cos / sin read from the caller's tables [positions][rot_dim / 2]; pairs are
+  (i, i + rot_dim / 2) (NeoX) or (2i, 2i + 1) (interleaved), dims past rot_dim
+  are left alone.  V is stored as given.  The transformed value is rounded to
+  fp32 (the kernel's precision) before it is encoded; bf16 storage rounds to
+  nearest, ties to even.
 
 Every code below is chosen from the decoded value tables of ``formats`` (the
 nearest representable value, ties to the even code), and bytes are placed with
@@ -92,10 +100,54 @@ def _mxfp4_put(flat: np.ndarray, base: int, slot: int, codes: np.ndarray, scales
     flat[s0:s0 + 4] = scales
 
 
+def bf16_bits(x) -> np.ndarray:
+    """bf16 codes of x (rounded to fp32 first): round to nearest, ties to even;
+    NaN becomes a quiet NaN with its sign."""
+    u = np.asarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32).astype(np.uint64)
+    rne = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = ((u & 0x7FFFFFFF) > 0x7F800000)
+    return np.where(nan, (u >> 16) | 0x40, rne).astype(np.uint16)
+
+
 def _bf16_bytes(x: np.ndarray) -> np.ndarray:
-    """bf16 values given as float (exactly representable) -> their two bytes each."""
-    u = np.asarray(x, dtype=np.float32).view(np.uint32)
-    return (u >> 16).astype(np.uint16).view(np.uint8).reshape(*np.shape(x), 2)
+    """values -> the two bytes of each one's bf16 code (the identity on bf16 values)."""
+    return bf16_bits(x).view(np.uint8).reshape(*np.shape(x), 2)
+
+
+def rms_norm(x, weight, eps: float) -> np.ndarray:
+    """x [..., 128] -> w * x / sqrt(mean(x^2) + eps), per vector."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(weight, dtype=np.float64) * x / np.sqrt(ms + eps)
+
+
+def rope(x, pos: int, cos, sin, rot_dim: int, neox: bool) -> np.ndarray:
+    """One 128-dim vector rotated at position pos: pair i of the first rot_dim
+    dims turns by the angle whose cosine / sine are cos[pos][i] / sin[pos][i]."""
+    y = np.array(x, dtype=np.float64)
+    half = rot_dim // 2
+    c = np.asarray(cos, dtype=np.float64)[pos, :half]
+    s_ = np.asarray(sin, dtype=np.float64)[pos, :half]
+    if neox:
+        a, b = y[:half].copy(), y[half:rot_dim].copy()
+        y[:half], y[half:rot_dim] = a * c - b * s_, b * c + a * s_
+    else:
+        a, b = y[0:rot_dim:2].copy(), y[1:rot_dim:2].copy()
+        y[0:rot_dim:2], y[1:rot_dim:2] = a * c - b * s_, b * c + a * s_
+    return y
+
+
+def transform(x, pos: int, tf) -> np.ndarray:
+    """The optional QK-norm then rope of one vector; tf is None or a dict with
+    norm_weight (None: no norm), eps, cos / sin (None: no rope), rot_dim, neox.
+    Rounded to fp32, the precision the stored value is decided in."""
+    y = np.asarray(x, dtype=np.float64)
+    if tf is not None:
+        if tf.get("norm_weight") is not None:
+            y = rms_norm(y, tf["norm_weight"], tf["eps"])
+        if tf.get("cos") is not None:
+            y = rope(y, pos, tf["cos"], tf["sin"], tf["rot_dim"], tf["neox"])
+    return y.astype(np.float32).astype(np.float64)
 
 
 def _element_bytes(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
@@ -110,7 +162,7 @@ def _element_bytes(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
 
 def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,
                 k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str, k_scale: float, v_scale: float,
-                idx_pool: np.ndarray, idx_dtype: str, idx_scale: float) -> None:
+                idx_pool: np.ndarray, idx_dtype: str, idx_scale: float, k_tf=None, idx_tf=None) -> None:
     """Writes the new tokens into the pools, in place.
 
     k_new, v_new [T, H_kv, 128] and idx_new [T, 128] (or None: no index key)
@@ -118,7 +170,8 @@ def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,
     exactly); the pools are the
     contiguous byte arrays the readers of ``pools`` take (K/V: pages of
     H_kv heads each, head g of page id n at (n H_kv + g) page bytes; index
-    cache: one page per block)."""
+    cache: one page per block).  k_tf / idx_tf: the optional QK-norm and rope
+    of the keys and of the index keys (see ``transform``)."""
     T, H_kv, _ = np.shape(k_new)
     with_idx = idx_new is not None
     k_new, v_new = (np.asarray(a, dtype=np.float64) for a in (k_new, v_new))
@@ -134,26 +187,28 @@ def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,
         if p < 0:
             continue
         blk, slot = int(block_table[r][p // pools.BLOCK]), p % pools.BLOCK
+        kt = [transform(k_new[t, g], p, k_tf) for g in range(H_kv)]
+        it = transform(idx_new[t], p, idx_tf) if with_idx else None
         # index key: one per token, no head dimension; page id = block id
         if not with_idx:
             pass
         elif idx_dtype == "mxfp4":
-            codes, scales = mx_quantize(idx_new[t])
+            codes, scales = mx_quantize(it)
             _mxfp4_put(xf, blk * formats.MXFP4_PAGE_BYTES, slot, codes, scales)
         else:
             e = 2 if idx_dtype == "bf16" else 1
             off = blk * 16384 * e + 2048 * e * (slot // pools.PAGE16) + _k_offsets_row(e, slot % pools.PAGE16)
-            xf[off] = _element_bytes(idx_new[t], idx_dtype, idx_scale).reshape(-1)
+            xf[off] = _element_bytes(it, idx_dtype, idx_scale).reshape(-1)
         for g in range(H_kv):
             if kv_dtype == "mxfp4":
-                for flat, x in ((kf, k_new[t, g]), (vf, v_new[t, g])):
+                for flat, x in ((kf, kt[g]), (vf, v_new[t, g])):
                     codes, scales = mx_quantize(x)
                     _mxfp4_put(flat, (blk * H_kv + g) * formats.MXFP4_PAGE_BYTES, slot, codes, scales)
             else:
                 e = 2 if kv_dtype == "bf16" else 1
                 base = ((8 * blk + slot // pools.PAGE16) * H_kv + g) * 2048 * e
                 c = slot % pools.PAGE16
-                kf[base + _k_offsets_row(e, c)] = _element_bytes(k_new[t, g], kv_dtype, k_scale).reshape(-1)
+                kf[base + _k_offsets_row(e, c)] = _element_bytes(kt[g], kv_dtype, k_scale).reshape(-1)
                 vf[base + _v_offsets_row(e, c)] = _element_bytes(v_new[t, g], kv_dtype, v_scale).reshape(-1)
 
 
@@ -170,3 +225,21 @@ def _v_offsets_row(esize: int, t: int) -> np.ndarray:
 def quantize_query_e4m3(q) -> np.ndarray:
     """The query cast of the fused writer: e4m3fn bytes with a unit scale, saturating."""
     return encode_e4m3(q)
+
+
+def prepare_query(q, seq_lens, q_len: int, tf, out_dtype: str) -> np.ndarray:
+    """Queries [T, H, 128] of the step's tokens: the optional QK-norm and rope
+    at each token's position, then stored as bf16 codes (uint16) or unit-scale
+    e4m3 codes (uint8).  Rows of pad tokens (position < 0) are zero."""
+    q = np.asarray(q, dtype=np.float64)
+    T, H, _ = q.shape
+    out = np.zeros((T, H, 128), dtype=np.uint16 if out_dtype == "bf16" else np.uint8)
+    for t in range(T):
+        r, i = divmod(t, q_len)
+        p = int(seq_lens[r]) - q_len + i
+        if p < 0:
+            continue
+        for h in range(H):
+            y = transform(q[t, h], p, tf)
+            out[t, h] = bf16_bits(y) if out_dtype == "bf16" else encode_e4m3(y)
+    return out

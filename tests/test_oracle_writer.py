@@ -145,3 +145,108 @@ def test_writer_without_index_key_leaves_the_index_pool_and_writes_the_same_kv()
 def test_query_cast_is_unit_scale_saturating_e4m3():
     q = np.array([1.0, -2.5, 500.0, 0.0])
     assert list(writer.quantize_query_e4m3(q)) == [0x38, 0xC2, 0x7E, 0x00]
+
+
+# ------------------------------------------------------------------ QK-norm and rope
+def _tables(positions, rot_dim, base=10000.0):
+    inv = base ** (-np.arange(0, rot_dim, 2) / rot_dim)
+    ang = np.arange(positions)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32), ang
+
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 128)) * 3
+    w = rng.standard_normal(128)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w), eps=1e-6).numpy()
+    assert np.allclose(writer.rms_norm(x, w, 1e-6), ref, rtol=1e-13, atol=1e-13)
+    # unit weight, no epsilon: unit root mean square, and a scaled input gives the same output
+    y = writer.rms_norm(x, np.ones(128), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-14)
+    assert np.allclose(writer.rms_norm(5 * x, np.ones(128), 0.0), y, rtol=1e-13)
+
+
+@pytest.mark.parametrize("rot_dim", [128, 64, 32])
+def test_rope_neox_is_a_complex_rotation_and_interleaved_its_permutation(rot_dim):
+    rng = np.random.default_rng(rot_dim)
+    cos, sin, _ = _tables(40, rot_dim)
+    half = rot_dim // 2
+    for pos in (0, 1, 17, 39):
+        x = rng.standard_normal(128)
+        z = (x[:half] + 1j * x[half:rot_dim]) * (cos[pos].astype(np.float64) + 1j * sin[pos].astype(np.float64))
+        y = writer.rope(x, pos, cos, sin, rot_dim, neox=True)
+        assert np.allclose(y[:half], z.real, rtol=0, atol=1e-14) and np.allclose(y[half:rot_dim], z.imag, atol=1e-14)
+        assert np.array_equal(y[rot_dim:], x[rot_dim:])
+        # interleaved pairs (2i, 2i+1) are NeoX pairs after moving even dims first
+        perm = np.concatenate([np.arange(0, rot_dim, 2), np.arange(1, rot_dim, 2), np.arange(rot_dim, 128)])
+        yi = writer.rope(x, pos, cos, sin, rot_dim, neox=False)
+        assert np.allclose(yi[perm], writer.rope(x[perm], pos, cos, sin, rot_dim, neox=True), atol=1e-14)
+    # position 0 turns nothing; turning by p then by q is turning by p + q
+    x = rng.standard_normal(128)
+    assert np.allclose(writer.rope(x, 0, cos, sin, rot_dim, True), x, atol=1e-15)
+    c64, s64 = np.cos(_tables(40, rot_dim)[2]), np.sin(_tables(40, rot_dim)[2])
+    two = writer.rope(writer.rope(x, 5, c64, s64, rot_dim, True), 7, c64, s64, rot_dim, True)
+    assert np.allclose(two, writer.rope(x, 12, c64, s64, rot_dim, True), atol=1e-12)
+
+
+def test_bf16_bits_round_to_nearest_even_like_torch():
+    rng = np.random.default_rng(6)
+    b = torch.from_numpy(rng.standard_normal(4000).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    step = np.abs(b) * 2.0 ** -8                          # half a bf16 step at each value
+    x = np.concatenate([rng.standard_normal(20000) * 50, b + step, b - step, [np.inf, -np.inf, 0.0, -0.0]])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(writer.bf16_bits(x), ref)
+
+
+@pytest.mark.parametrize("kv_dtype,idx_dtype,neox", [("fp8", "mxfp4", True), ("bf16", "fp8", False),
+                                                     ("mxfp4", "bf16", True)])
+def test_writer_with_norm_and_rope_stores_the_transformed_keys(kv_dtype, idx_dtype, neox):
+    rng = np.random.default_rng(7)
+    H_kv, q_len = 2, 2
+    seq_lens = np.array([300, 1])
+    bt = np.array([[2, 0, 3], [1, 3, 3]])
+    nblk = 4
+    kpb = {"bf16": 4096, "fp8": 2048}.get(kv_dtype, formats.MXFP4_PAGE_BYTES)
+    ipb = {"bf16": 32768, "fp8": 16384, "mxfp4": formats.MXFP4_PAGE_BYTES}[idx_dtype]
+    npages = nblk * (8 if kv_dtype != "mxfp4" else 1)
+    k_pool = np.zeros((npages, H_kv * kpb), np.uint8)
+    v_pool = np.zeros_like(k_pool)
+    idx_pool = np.zeros((nblk, ipb), np.uint8)
+    T = 2 * q_len
+    k_new, v_new, idx_new = rng.standard_normal((T, H_kv, 128)), rng.standard_normal((T, H_kv, 128)), \
+        rng.standard_normal((T, 128))
+    cos, sin, _ = _tables(512, 64)
+    k_tf = dict(norm_weight=rng.standard_normal(128), eps=1e-6, cos=cos, sin=sin, rot_dim=64, neox=neox)
+    i_tf = dict(norm_weight=None, eps=0.0, cos=cos, sin=sin, rot_dim=64, neox=neox)
+    ks, vs, xs = 0.02, 0.03, 0.05
+    writer.write_cache(k_new, v_new, idx_new, bt, seq_lens, q_len, k_pool, v_pool, kv_dtype, ks, vs,
+                       idx_pool, idx_dtype, xs, k_tf=k_tf, idx_tf=i_tf)
+    plain_k, plain_v, plain_i = k_pool.copy(), v_pool.copy(), idx_pool.copy()
+    # the same pools written without the transform from the transformed vectors
+    kt = np.array([[writer.transform(k_new[t, g], seq_lens[t // q_len] - q_len + t % q_len, k_tf)
+                    for g in range(H_kv)] for t in range(T)])
+    it = np.array([writer.transform(idx_new[t], max(0, seq_lens[t // q_len] - q_len + t % q_len), i_tf)
+                   for t in range(T)])
+    k2, v2, i2 = np.zeros_like(k_pool), np.zeros_like(v_pool), np.zeros_like(idx_pool)
+    writer.write_cache(kt, v_new, it, bt, seq_lens, q_len, k2, v2, kv_dtype, ks, vs, i2, idx_dtype, xs)
+    assert np.array_equal(plain_k, k2) and np.array_equal(plain_v, v2) and np.array_equal(plain_i, i2)
+    # and rope moved the keys: without it the pools differ
+    k3, v3, i3 = np.zeros_like(k_pool), np.zeros_like(v_pool), np.zeros_like(idx_pool)
+    writer.write_cache(k_new, v_new, idx_new, bt, seq_lens, q_len, k3, v3, kv_dtype, ks, vs, i3, idx_dtype, xs)
+    assert not np.array_equal(k3, plain_k) and not np.array_equal(i3, plain_i) and np.array_equal(v3, plain_v)
+
+
+def test_prepare_query_pads_zero_and_casts_the_transformed_rows():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((4, 3, 128)) * 2
+    seq_lens = np.array([50, 1])
+    cos, sin, _ = _tables(64, 128)
+    tf = dict(norm_weight=np.full(128, 0.5), eps=1e-5, cos=cos, sin=sin, rot_dim=128, neox=True)
+    out8 = writer.prepare_query(q, seq_lens, 2, tf, "e4m3")
+    out16 = writer.prepare_query(q, seq_lens, 2, tf, "bf16")
+    assert not out8[2].any() and not out16[2].any()                 # request 1, token 0: position -1
+    for t, p in ((0, 48), (1, 49), (3, 0)):
+        y = np.array([writer.transform(q[t, h], p, tf) for h in range(3)])
+        assert np.array_equal(out8[t], writer.encode_e4m3(y)) and np.array_equal(out16[t], writer.bf16_bits(y))
+    # without a transform the e4m3 output is the plain cast
+    assert np.array_equal(writer.prepare_query(q, np.array([2, 2]), 2, None, "e4m3"), writer.quantize_query_e4m3(q))
