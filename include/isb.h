@@ -20,7 +20,9 @@
  *
  *   isb_write_cache              quantise the step's new keys, values and
  *                                index keys into the pools;
- *   isb_quantize_e4m3            the unit-scale e4m3 cast of a query.
+ *   isb_quantize_e4m3            the unit-scale e4m3 cast of a query;
+ *   isb_prepare_query            a query's QK-norm and rope, then its bf16 or
+ *                                e4m3 form.
  *
  * The calls follow the decode call of the vLLM API page for
  * vllm.models.minimax_m3.amd.sparse_attention_msa (MiniMaxM3SparseAiterPAImpl
@@ -280,6 +282,31 @@ ISB_API int isb_select_attend(isb_stream_t stream, const float* scores,
                               int32_t* sparse_bt, int32_t* sparse_ctx, void* out);
 
 /*
+ * The optional QK-norm and rope of the fused cache writer (ROCm/ATOM PR 2962,
+ * Follow-ups: the fused QK-norm / rope / cache writer; the pages give none of
+ * the step's parameters, so the caller does).  For one 128-dim head vector x
+ * at position p, in fp32:
+ *   norm  (norm_weight != NULL)  y_d = norm_weight[d] x_d / sqrt(mean(x^2) + eps)
+ *   rope  (rope_cos != NULL)     dim pairs (a, b) -> (a c - b s, b c + a s) with
+ *         c = rope_cos[p][i], s = rope_sin[p][i] for pair i < rot_dim / 2:
+ *         pairs (i, i + rot_dim / 2) when neox, else (2i, 2i + 1); dims past
+ *         rot_dim unchanged.
+ * norm_weight [128], rope_cos and rope_sin [rope_positions][rot_dim / 2]: fp32
+ * device arrays owned by the caller; eps >= 0; rot_dim a multiple of 4 in
+ * 4..128 (ISB_E_SHAPE otherwise).  A NULL isb_norm_rope, or one with both
+ * norm_weight and rope_cos NULL, applies nothing.
+ */
+typedef struct isb_norm_rope {
+  const float* norm_weight;
+  float eps;
+  const float* rope_cos;
+  const float* rope_sin;
+  int64_t rope_positions;
+  int rot_dim;
+  int neox;
+} isb_norm_rope;
+
+/*
  * isb_write_cache - store the new tokens of a step into the paged caches.
  *
  * The cache write in front of the decode (ROCm/ATOM PR 2962, the commit
@@ -297,8 +324,11 @@ ISB_API int isb_select_attend(isb_stream_t stream, const float* scores,
  *                 e2m1 code of x / 2^exponent, rounded to nearest with ties to
  *                 the even code, saturated at 6 (OCP MX v1.0);
  *   ISB_BF16      the value as given.
- * Only the bytes of the written tokens change; QK-norm and rope are not
- * applied (the vectors are stored as given).
+ * Only the bytes of the written tokens change.  K (every KV head) and the
+ * index key first take the QK-norm and rope of k_norm_rope / idx_norm_rope at
+ * the token's position (see isb_norm_rope; NULL = stored as given); V is
+ * stored as given.  With a transform, a bf16 pool takes the fp32 result
+ * rounded to nearest even.
  *
  *   k_new, v_new  [T][num_kv_heads][128] bf16, 4-byte aligned
  *   idx_new       [T][128] bf16, or NULL (then idx_pool must be NULL too and
@@ -310,8 +340,9 @@ ISB_API int isb_select_attend(isb_stream_t stream, const float* scores,
  *                 k_scale / v_scale > 0 for fp8
  *   idx_pool      in/out, [idx_pool_blocks] index pages of idx_dtype;
  *                 idx_scale > 0 for fp8
- * Positions past the table (p div 128 >= block_table_stride) and block ids
- * whose pages fall outside the pools are skipped, never written.  Calls that
+ * Positions past the table (p div 128 >= block_table_stride), positions at
+ * or past a given rope table's rope_positions, and block ids whose pages fall
+ * outside the pools are skipped, never written.  Calls that
  * write the same slot must not overlap in time.  Shape errors: num_kv_heads >
  * 65535, num_reqs * decode_query_len > 2^31 - 1.
  */
@@ -321,7 +352,8 @@ ISB_API int isb_write_cache(isb_stream_t stream, const void* k_new, const void* 
                             int decode_query_len, int num_kv_heads, void* k_pool, void* v_pool,
                             int kv_dtype, float k_scale, float v_scale, int64_t num_pages,
                             void* idx_pool, int idx_dtype, float idx_scale,
-                            int64_t idx_pool_blocks);
+                            int64_t idx_pool_blocks, const isb_norm_rope* k_norm_rope,
+                            const isb_norm_rope* idx_norm_rope);
 
 /*
  * isb_quantize_e4m3 - out[i] = the e4m3fn code of x[i] with a unit scale
@@ -332,6 +364,22 @@ ISB_API int isb_write_cache(isb_stream_t stream, const void* k_new, const void* 
  * ISB_FP8_E4M3 query for isb_index_score and isb_sparse_pa_decode.
  */
 ISB_API int isb_quantize_e4m3(isb_stream_t stream, const void* x, int64_t n, void* out);
+
+/*
+ * isb_prepare_query - the query side of the fused writer: each head vector of
+ * q [T][num_heads][128] bf16 (T = num_reqs * decode_query_len, token t = r q + i
+ * at position seq_lens[r] - q + i) takes the QK-norm and rope of norm_rope
+ * (NULL: none) and is written to out [T][num_heads][128] as bf16 (rounded to
+ * nearest even) or, with out_dtype ISB_FP8_E4M3, as the unit-scale e4m3 cast
+ * of isb_quantize_e4m3 (ROCm/ATOM PR 2962, Follow-ups: the main query comes
+ * back as e4m3; the index query too when asked for).  Rows of pad tokens
+ * (position < 0) are written as zeros, rows at or past rope_positions as NaN.
+ * q and out 4-byte aligned.  Shape errors: num_heads > 65535,
+ * num_reqs * decode_query_len > 2^31 - 1.
+ */
+ISB_API int isb_prepare_query(isb_stream_t stream, const void* q, int num_heads,
+                              const int32_t* seq_lens, int num_reqs, int decode_query_len,
+                              const isb_norm_rope* norm_rope, int out_dtype, void* out);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,10 @@ from .binding import (  # noqa: F401
     IsbError,
     emit_sparse_block_table,
     index_score,
+    NormRope,
     load_library,
+    norm_rope,
+    prepare_query,
     quantize_e4m3,
     select_attend,
     sparse_pa_decode,

@@ -54,6 +54,36 @@ _I64 = ctypes.c_int64
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 
+class NormRope(ctypes.Structure):
+    """isb_norm_rope: the optional QK-norm and rope of the fused writer."""
+    _fields_ = [("norm_weight", ctypes.c_void_p), ("eps", ctypes.c_float), ("rope_cos", ctypes.c_void_p),
+                ("rope_sin", ctypes.c_void_p), ("rope_positions", ctypes.c_int64), ("rot_dim", ctypes.c_int),
+                ("neox", ctypes.c_int)]
+
+
+def norm_rope(norm_weight=None, eps=0.0, rope_cos=None, rope_sin=None, rot_dim=0, neox=True):
+    """An isb_norm_rope from fp32 device tensors: norm_weight [128], rope_cos /
+    rope_sin [positions, rot_dim / 2] (None: that part is not applied).  The
+    tensors must outlive the calls that use it."""
+    nr = NormRope()
+    if norm_weight is not None:
+        if norm_weight.dtype != torch.float32 or norm_weight.shape != (128,) or not norm_weight.is_contiguous():
+            raise ValueError("norm_weight is fp32 [128]")
+        nr.norm_weight, nr.eps = norm_weight.data_ptr(), float(eps)
+    if rope_cos is not None or rope_sin is not None:
+        for t in (rope_cos, rope_sin):
+            if t is None or t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != rot_dim // 2 or \
+                    not t.is_contiguous():
+                raise ValueError("rope_cos / rope_sin are fp32 [positions, rot_dim / 2]")
+        if rope_cos.shape != rope_sin.shape:
+            raise ValueError("rope_cos and rope_sin differ in shape")
+        nr.rope_cos, nr.rope_sin = rope_cos.data_ptr(), rope_sin.data_ptr()
+        nr.rope_positions, nr.rot_dim, nr.neox = rope_cos.shape[0], int(rot_dim), int(bool(neox))
+    return nr
+
+
+_NR = ctypes.POINTER(NormRope)
+
 _SIGNATURES = {
     "isb_version": ([], _I),
     "isb_strerror": ([_I], ctypes.c_char_p),
@@ -66,8 +96,9 @@ _SIGNATURES = {
     "isb_sparse_pa_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
     "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I,
                               _F, _P, _SZ, _P], _I),
-    "isb_write_cache": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _F, _F, _I64, _P, _I, _F, _I64],
-                        _I),
+    "isb_write_cache": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _F, _F, _I64, _P, _I, _F, _I64,
+                         _NR, _NR], _I),
+    "isb_prepare_query": ([_P, _P, _I, _P, _I, _I, _NR, _I, _P], _I),
     "isb_quantize_e4m3": ([_P, _P, _I64, _P], _I),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -237,12 +268,14 @@ def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_d
 
 
 def write_cache(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len, k_pool, v_pool, kv_dtype,
-                k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0):
+                k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0, k_norm_rope=None,
+                idx_norm_rope=None):
     """Stores the step's new K, V (and index keys, unless idx_new is None) into
-    the pools, in place (see isb_write_cache)."""
+    the pools, in place, K and index keys after their optional QK-norm / rope
+    (``norm_rope(...)`` structures; see isb_write_cache)."""
     _call("write_cache", *_write_cache_args(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len,
                                             k_pool, v_pool, kv_dtype, k_scale, v_scale, idx_pool, idx_dtype,
-                                            idx_scale))
+                                            idx_scale, k_norm_rope, idx_norm_rope))
 
 
 def write_cache_launcher(*args, **kwargs):
@@ -252,8 +285,13 @@ def write_cache_launcher(*args, **kwargs):
     return lambda: _call("write_cache", *a)
 
 
+def _ref(nr):
+    return None if nr is None else ctypes.byref(nr)
+
+
 def _write_cache_args(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len, k_pool, v_pool, kv_dtype,
-                      k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0):
+                      k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0, k_norm_rope=None,
+                      idx_norm_rope=None):
     if (idx_new is None) != (idx_pool is None):
         raise ValueError("idx_new and idx_pool go together")
     dev = _dev(k_new, v_new, block_table, seq_lens, k_pool, v_pool,
@@ -279,7 +317,7 @@ def _write_cache_args(k_new, v_new, idx_new, block_table, seq_lens, decode_query
             seq_lens.data_ptr(), R, decode_query_len, H_kv, k_pool.data_ptr(),
             v_pool.data_ptr(), _code(kv_dtype), float(k_scale), float(v_scale), k_pool.shape[0],
             None if idx_pool is None else idx_pool.data_ptr(), _code(idx_dtype), float(idx_scale),
-            0 if idx_pool is None else idx_pool.shape[0])
+            0 if idx_pool is None else idx_pool.shape[0], _ref(k_norm_rope), _ref(idx_norm_rope))
 
 
 def quantize_e4m3(x, out=None):
@@ -294,6 +332,26 @@ def quantize_e4m3(x, out=None):
         raise ValueError("out must have x's size")
     if x.numel():
         _call("quantize_e4m3", _stream(dev), x.data_ptr(), x.numel(), out.data_ptr())
+    return out
+
+
+def prepare_query(q, seq_lens, decode_query_len, norm_rope=None, out_dtype="e4m3", out=None):
+    """q [T, H, 128] bf16 after its optional QK-norm / rope, as e4m3 codes
+    (uint8) or bf16 (see isb_prepare_query)."""
+    dev = _dev(q, seq_lens)
+    T, H = q.shape[0], q.shape[1]
+    if q.dtype != torch.bfloat16 or q.shape[2] != 128 or T != seq_lens.shape[0] * decode_query_len:
+        raise ValueError("q is bf16 [num_reqs * query_len, H, 128]")
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens is int32")
+    code = _code(out_dtype)
+    if out is None:
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16 if code == BF16 else torch.uint8, device=dev)
+    _dev(out)
+    if out.numel() != q.numel() or out.element_size() != (2 if code == BF16 else 1):
+        raise ValueError("out must match q's shape in the output dtype")
+    _call("prepare_query", _stream(dev), q.data_ptr(), H, seq_lens.data_ptr(), seq_lens.shape[0],
+          decode_query_len, _ref(norm_rope), code, out.data_ptr())
     return out
 
 

@@ -13,6 +13,10 @@
 //           [-127, 127]), each element's e2m1 code rounded to nearest, ties
 //           to the even code, saturating at +-6 (OCP MX v1.0);
 //   bf16  - stored as given.
+// Before the encoding, K and the index key (and, in isb_prepare_query, the
+// query) may take the fused step's QK-norm and rope, with parameters the
+// caller gives (isb_norm_rope): y = w x / sqrt(mean(x^2) + eps), then dim
+// pairs turned by the table angle of the token's position; computed in fp32.
 // Bytes go where the decode kernels read them (the page layouts of isb.h).
 // This is not a bandwidth kernel: a decode step writes a few hundred bytes a
 // token.
@@ -48,6 +52,61 @@ __device__ __forceinline__ uint32_t e2m1_code(float y) {
   return ((__float_as_uint(y) >> 28) & 8u) | m;
 }
 
+// The device copy of an isb_norm_rope (all zero: nothing to apply).
+struct NormRope {
+  const float* w;   // [128] or null
+  const float* cs;  // [npos][rot / 2] or null
+  const float* sn;
+  int64_t npos;
+  float eps;
+  int rot, neox;
+};
+
+__device__ __forceinline__ bool applies(const NormRope& f) { return f.w != nullptr || f.cs != nullptr; }
+
+// The QK-norm, then the rope, of one 128-dim vector held two dims a lane
+// (x0, x1 = dims 2 lane, 2 lane + 1) at position p < npos.  Wave-uniform.
+__device__ __forceinline__ void norm_rope(const NormRope& f, int p, int lane, float& x0, float& x1) {
+  if (f.w) {
+    float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    const float r = 1.f / sqrtf(ss * (1.f / 128.f) + f.eps);
+    x0 = x0 * r * f.w[2 * lane];
+    x1 = x1 * r * f.w[2 * lane + 1];
+  }
+  if (f.cs) {
+    const int half = f.rot >> 1, d = 2 * lane;
+    const float* c = f.cs + (int64_t)p * half;
+    const float* s = f.sn + (int64_t)p * half;
+    if (f.neox) {
+      // dims d < half pair with d + half, held by the lane half / 2 further on
+      const int q = half >> 1;
+      const int src = lane < q ? lane + q : lane - q;
+      const float y0 = __shfl(x0, src, kWave), y1 = __shfl(x1, src, kWave);
+      if (d < half) {
+        x0 = x0 * c[d] - y0 * s[d];
+        x1 = x1 * c[d + 1] - y1 * s[d + 1];
+      } else if (d < f.rot) {
+        const int j = d - half;
+        x0 = x0 * c[j] + y0 * s[j];
+        x1 = x1 * c[j + 1] + y1 * s[j + 1];
+      }
+    } else if (d < f.rot) {  // the pair (d, d + 1) is this lane's
+      const float a = x0, b = x1, cj = c[lane], sj = s[lane];
+      x0 = a * cj - b * sj;
+      x1 = b * cj + a * sj;
+    }
+  }
+}
+
+// bf16 code of x: round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 struct WriteArgs {
   const uint16_t* k_new;    // bf16 [T][H_kv][128]
   const uint16_t* v_new;
@@ -60,6 +119,7 @@ struct WriteArgs {
   int64_t num_pages, idx_blocks;
   float k_scale, v_scale, idx_scale;
   int bt_stride, q_len, H_kv, T;
+  NormRope ktf, itf;  // the keys' and the index keys' QK-norm / rope
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -125,6 +185,8 @@ __global__ __launch_bounds__(256) void write_cache_kernel(WriteArgs a) {
   const int r = t / a.q_len, i = t % a.q_len;
   const int p = a.seq_lens[r] - a.q_len + i;
   if (p < 0 || p / kBlockTokens >= a.bt_stride) return;  // a pad row, or past the table
+  // a position past a rope table: the whole token is skipped
+  if ((a.ktf.cs && p >= a.ktf.npos) || (a.idx_new && a.itf.cs && p >= a.itf.npos)) return;
   const int64_t blk = a.bt[(size_t)r * a.bt_stride + p / kBlockTokens];
   const int slot = p % kBlockTokens;
   const int d = 2 * lane;  // this lane's dims d, d + 1
@@ -132,8 +194,15 @@ __global__ __launch_bounds__(256) void write_cache_kernel(WriteArgs a) {
   const int g = is_idx ? 0 : v % a.H_kv;
   const uint16_t* src = is_idx ? a.idx_new + (size_t)t * kHeadDim
                                : (is_v ? a.v_new : a.k_new) + ((size_t)t * a.H_kv + g) * kHeadDim;
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(src + d);
-  const float x0 = bf16_bits_to_f32(w & 0xFFFFu), x1 = bf16_bits_to_f32(w >> 16);
+  uint32_t w = *reinterpret_cast<const uint32_t*>(src + d);
+  float x0 = bf16_bits_to_f32(w & 0xFFFFu), x1 = bf16_bits_to_f32(w >> 16);
+  if (!is_v) {
+    const NormRope& f = is_idx ? a.itf : a.ktf;
+    if (applies(f)) {
+      norm_rope(f, p, lane, x0, x1);
+      w = bf16_rne(x0) | (bf16_rne(x1) << 16);  // the bf16 pool's bits
+    }
+  }
   if (is_idx) {  // page id = block id, no head dimension
     if (blk < 0 || blk >= a.idx_blocks) return;
     if constexpr (IDX_DT == ISB_MXFP4) {
@@ -167,6 +236,66 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const uint16_t* x, i
     if (i0 + k < n) out[i0 + k] = (uint8_t)e4m3_code(bf16_bits_to_f32(x[i0 + k]));
 }
 
+// isb_prepare_query: one wave a (token, head) vector of q [T][H][128] bf16;
+// out [T][H][128] as bf16 codes (OUT_E = 2) or unit-scale e4m3 (OUT_E = 1).
+struct QueryArgs {
+  const uint16_t* q;
+  const int32_t* seq_lens;
+  uint8_t* out;
+  NormRope tf;
+  int H, q_len, T;
+};
+
+template <int OUT_E>
+__global__ __launch_bounds__(256) void prepare_query_kernel(QueryArgs a) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const long long item = (long long)blockIdx.x * 4 + wave;
+  if (item >= (long long)a.T * a.H) return;
+  const int t = (int)(item / a.H);
+  const int r = t / a.q_len, i = t % a.q_len;
+  const int p = a.seq_lens[r] - a.q_len + i;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(a.q + (size_t)item * kHeadDim + 2 * lane);
+  float x0 = bf16_bits_to_f32(w & 0xFFFFu), x1 = bf16_bits_to_f32(w >> 16);
+  uint32_t c0, c1;
+  if (p < 0) {  // a pad row: zeros
+    c0 = c1 = 0u;
+  } else if (a.tf.cs && p >= a.tf.npos) {  // past the rope table: NaN
+    c0 = c1 = OUT_E == 2 ? 0x7FC0u : 0x7Fu;
+  } else {
+    norm_rope(a.tf, p, lane, x0, x1);
+    c0 = OUT_E == 2 ? bf16_rne(x0) : e4m3_code(x0);
+    c1 = OUT_E == 2 ? bf16_rne(x1) : e4m3_code(x1);
+  }
+  if constexpr (OUT_E == 2)
+    *reinterpret_cast<uint32_t*>(a.out + ((size_t)item * kHeadDim + 2 * lane) * 2) = c0 | (c1 << 16);
+  else
+    *reinterpret_cast<uint16_t*>(a.out + (size_t)item * kHeadDim + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+}
+
+// isb_norm_rope -> NormRope after the host checks; 0 or an ISB_E_* code.
+static int read_norm_rope(const isb_norm_rope* h, NormRope& f) {
+  f = NormRope{nullptr, nullptr, nullptr, 0, 0.f, 0, 0};
+  if (!h) return ISB_OK;
+  if (h->norm_weight) {
+    if (!(h->eps >= 0.f) || !(h->eps < INFINITY) || reinterpret_cast<uintptr_t>(h->norm_weight) % 4)
+      return ISB_E_INVALID_ARG;
+    f.w = h->norm_weight;
+    f.eps = h->eps;
+  }
+  if (h->rope_cos || h->rope_sin) {
+    if (!h->rope_cos || !h->rope_sin || h->rope_positions <= 0) return ISB_E_INVALID_ARG;
+    if (h->rot_dim < 4 || h->rot_dim > kHeadDim || h->rot_dim % 4) return ISB_E_SHAPE;
+    if (reinterpret_cast<uintptr_t>(h->rope_cos) % 4 || reinterpret_cast<uintptr_t>(h->rope_sin) % 4)
+      return ISB_E_INVALID_ARG;
+    f.cs = h->rope_cos;
+    f.sn = h->rope_sin;
+    f.npos = h->rope_positions;
+    f.rot = h->rot_dim;
+    f.neox = h->neox != 0;
+  }
+  return ISB_OK;
+}
+
 template <int KV_DT, int IDX_DT>
 static void launch_write(const WriteArgs& a, hipStream_t st) {
   const long long items = (long long)a.T * (2 * a.H_kv + (a.idx_new != nullptr));
@@ -187,7 +316,8 @@ extern "C" int isb_write_cache(isb_stream_t stream, const void* k_new, const voi
                                const int32_t* seq_lens, int num_reqs, int decode_query_len,
                                int num_kv_heads, void* k_pool, void* v_pool, int kv_dtype, float k_scale,
                                float v_scale, int64_t num_pages, void* idx_pool, int idx_dtype,
-                               float idx_scale, int64_t idx_pool_blocks) {
+                               float idx_scale, int64_t idx_pool_blocks, const isb_norm_rope* k_norm_rope,
+                               const isb_norm_rope* idx_norm_rope) {
   using namespace isb;
   if (!k_new || !v_new || !block_table || !seq_lens || !k_pool || !v_pool) return ISB_E_INVALID_ARG;
   const bool with_idx = idx_new != nullptr;
@@ -206,9 +336,15 @@ extern "C" int isb_write_cache(isb_stream_t stream, const void* k_new, const voi
       reinterpret_cast<uintptr_t>(idx_new) % 4 || reinterpret_cast<uintptr_t>(k_pool) % 4 ||
       reinterpret_cast<uintptr_t>(v_pool) % 4 || reinterpret_cast<uintptr_t>(idx_pool) % 4)
     return ISB_E_INVALID_ARG;
+  NormRope ktf, itf;
+  int e = read_norm_rope(k_norm_rope, ktf);
+  if (!e && with_idx) e = read_norm_rope(idx_norm_rope, itf);
+  if (e) return e;
+  if (!with_idx) itf = NormRope{nullptr, nullptr, nullptr, 0, 0.f, 0, 0};
   WriteArgs a{(const uint16_t*)k_new, (const uint16_t*)v_new, (const uint16_t*)idx_new, block_table, seq_lens,
               (uint8_t*)k_pool, (uint8_t*)v_pool, (uint8_t*)idx_pool, num_pages, idx_pool_blocks,
-              k_scale, v_scale, idx_scale, block_table_stride, decode_query_len, num_kv_heads, (int)T};
+              k_scale, v_scale, idx_scale, block_table_stride, decode_query_len, num_kv_heads, (int)T,
+              ktf, itf};
   if (!with_idx) idx_dtype = ISB_BF16;  // no index vector: any instantiation will do
   hipStream_t st = as_hip(stream);
   if (kv_dtype == ISB_BF16) launch_write_kv<ISB_BF16>(a, idx_dtype, st);
@@ -223,5 +359,26 @@ extern "C" int isb_quantize_e4m3(isb_stream_t stream, const void* x, int64_t n, 
   if ((n + 1023) / 1024 > 0x7FFFFFFFLL) return ISB_E_SHAPE;
   hipLaunchKernelGGL(quantize_e4m3_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, as_hip(stream),
                      (const uint16_t*)x, n, (uint8_t*)out);
+  return launch_status();
+}
+
+extern "C" int isb_prepare_query(isb_stream_t stream, const void* q, int num_heads, const int32_t* seq_lens,
+                                 int num_reqs, int decode_query_len, const isb_norm_rope* norm_rope,
+                                 int out_dtype, void* out) {
+  using namespace isb;
+  if (!q || !seq_lens || !out || num_heads <= 0 || num_reqs <= 0 || decode_query_len <= 0)
+    return ISB_E_INVALID_ARG;
+  if (out_dtype != ISB_BF16 && out_dtype != ISB_FP8_E4M3) return ISB_E_UNSUPPORTED_DTYPE;
+  const long long T = (long long)num_reqs * decode_query_len;
+  if (T > 0x7FFFFFFFLL || num_heads > 65535 || T * num_heads > 4LL * 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(out) % 4) return ISB_E_INVALID_ARG;
+  QueryArgs a{(const uint16_t*)q, seq_lens, (uint8_t*)out, {}, num_heads, decode_query_len, (int)T};
+  const int e = read_norm_rope(norm_rope, a.tf);
+  if (e) return e;
+  const dim3 grid((unsigned)((T * num_heads + 3) / 4));
+  if (out_dtype == ISB_BF16)
+    hipLaunchKernelGGL(prepare_query_kernel<2>, grid, dim3(256), 0, as_hip(stream), a);
+  else
+    hipLaunchKernelGGL(prepare_query_kernel<1>, grid, dim3(256), 0, as_hip(stream), a);
   return launch_status();
 }

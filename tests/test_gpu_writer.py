@@ -331,3 +331,167 @@ def test_decode_step_after_the_cache_write(name):
     check_chain(hi, layer.scores.cpu().numpy().astype(np.float64), layer.topk.cpu().numpy(),
                 layer.sparse_bt.cpu().numpy(), layer.sparse_ctx.cpu().numpy(), layer.out.float().cpu().numpy(),
                 ref, hi["block_table"])
+
+
+# ------------------------------------------------------------------ QK-norm and rope
+def _rope_tables(positions, rot_dim, base=10000.0):
+    inv = base ** (-np.arange(0, rot_dim, 2) / rot_dim)
+    ang = np.arange(positions)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _exact(x, p, tf):
+    """The transform in fp64, not rounded to fp32: the value both sides round."""
+    y = np.asarray(x, dtype=np.float64)
+    if tf.get("norm_weight") is not None:
+        y = writer.rms_norm(y, tf["norm_weight"], tf["eps"])
+    if tf.get("cos") is not None:
+        y = writer.rope(y, p, tf["cos"], tf["sin"], tf["rot_dim"], tf["neox"])
+    return y
+
+
+def _near_ties_only(got, ref, exact, what):
+    """got and ref decoded values agree, except where the exact value sits at a
+    tie between them (fp32 arithmetic in a different order may break it either
+    way): at most 0.1% of the elements."""
+    bad = got != ref
+    if bad.any():
+        mid = (got[bad] + ref[bad]) / 2
+        slack = 2.0 ** -16 * np.maximum(np.abs(exact[bad]), 1e-30)
+        assert np.all(np.abs(exact[bad] - mid) <= slack), f"{what}: a mismatch that is not a near tie"
+        assert bad.mean() <= 1e-3, f"{what}: {bad.sum()} near ties of {bad.size}"
+
+
+def _slot_mask(shape, dtype, page_kind, H_kv, slots):
+    """Bytes of the written (page, head, slot) triples of a pool, as a mask."""
+    m = np.zeros(int(np.prod(shape)), dtype=bool)
+    for page, g, slot in slots:
+        if dtype == "mxfp4":
+            base = (page * (H_kv if page_kind == "kv" else 1) + g) * formats.MXFP4_PAGE_BYTES
+            m[base + 64 * slot: base + 64 * slot + 64] = True
+            m[base + formats.MXFP4_DATA_BYTES + 4 * slot: base + formats.MXFP4_DATA_BYTES + 4 * slot + 4] = True
+        else:
+            e = 2 if dtype == "bf16" else 1
+            if page_kind == "kv":
+                base, c = ((8 * page + slot // 16) * H_kv + g) * 2048 * e, slot % 16
+            else:
+                base, c = page * 16384 * e + 2048 * e * (slot // 16), slot % 16
+            m[base + writer._k_offsets_row(e, c)] = True
+    return m.reshape(shape)
+
+
+NR_CASES = {
+    # kv dtype, index dtype, H_kv, query_len, neox, rotated dims, norm on the index key
+    "fp8_neox_full": ("fp8", "fp8", 1, 1, True, 128, True),
+    "fp8_h2_interleaved_64": ("fp8", "mxfp4", 2, 4, False, 64, False),
+    "bf16_neox_32": ("bf16", "bf16", 2, 3, True, 32, True),
+    "mxfp4_neox_64": ("mxfp4", "mxfp4", 1, 4, True, 64, True),
+}
+
+
+@pytest.mark.parametrize("name", list(NR_CASES))
+def test_write_cache_with_norm_and_rope(name):
+    kv, idt, H, q, neox, rot, idx_norm = NR_CASES[name]
+    lens = np.array([300, 2, 0, 4097, 129][: 5 if q > 1 else 4], np.int32)
+    R = len(lens)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    nblk = 64
+    need = [-(-int(L) // 128) for L in lens]
+    ids = rng.permutation(nblk)
+    bt = rng.integers(0, nblk, (R, 40)).astype(np.int32)
+    for r in range(R):
+        bt[r, :need[r]] = ids[sum(need[:r]):sum(need[:r + 1])]
+    npages = nblk * (8 if kv != "mxfp4" else 1)
+    pools = dict(k=rng.integers(0, 256, (npages, H * KV_PAGE[kv]), dtype=np.uint8),
+                 v=rng.integers(0, 256, (npages, H * KV_PAGE[kv]), dtype=np.uint8),
+                 i=rng.integers(0, 256, (nblk, IDX_PAGE[idt]), dtype=np.uint8))
+    T = R * q
+    bf = lambda *s: torch.from_numpy((rng.standard_normal(s) * 3).astype(np.float32)).to(torch.bfloat16)  # noqa
+    k_new, v_new, i_new = bf(T, H, 128), bf(T, H, 128), bf(T, 128)
+    cos, sin = _rope_tables(4200, rot)
+    kw = (rng.standard_normal(128) * 0.5 + 1).astype(np.float32)
+    iw = (rng.standard_normal(128) * 0.5 + 1).astype(np.float32)
+    k_tf = dict(norm_weight=kw, eps=1e-6, cos=cos, sin=sin, rot_dim=rot, neox=neox)
+    i_tf = dict(norm_weight=iw if idx_norm else None, eps=1e-6, cos=cos, sin=sin, rot_dim=rot, neox=neox)
+    ks, vs, xs = 0.05, 0.021, 0.04
+    _say(f"write_cache norm+rope {name}")
+    d = {n: torch.from_numpy(a).cuda() for n, a in pools.items()}
+    dev_t = {n: torch.from_numpy(a).cuda() for n, a in (("kw", kw), ("iw", iw), ("cos", cos), ("sin", sin))}
+    knr = isb.norm_rope(dev_t["kw"], 1e-6, dev_t["cos"], dev_t["sin"], rot, neox)
+    inr = isb.norm_rope(dev_t["iw"] if idx_norm else None, 1e-6, dev_t["cos"], dev_t["sin"], rot, neox)
+    isb.write_cache(k_new.cuda(), v_new.cuda(), i_new.cuda(), torch.from_numpy(bt).cuda(),
+                    torch.from_numpy(lens).cuda(), q, d["k"], d["v"], kv, ks, vs, d["i"], idt, xs,
+                    k_norm_rope=knr, idx_norm_rope=inr)
+    torch.cuda.synchronize()
+    got = {n: t.cpu().numpy() for n, t in d.items()}
+    ref = {n: a.copy() for n, a in pools.items()}
+    writer.write_cache(_host(k_new), _host(v_new), _host(i_new), bt, lens, q, ref["k"], ref["v"], kv, ks, vs,
+                       ref["i"], idt, xs, k_tf=k_tf, idx_tf=i_tf)
+    assert np.array_equal(got["v"], ref["v"])                        # V is stored as given
+    kslots, islots, toks = [], [], []
+    for t in range(T):
+        r, i = divmod(t, q)
+        p = int(lens[r]) - q + i
+        if p < 0:
+            continue
+        blk = int(bt[r, p // 128])
+        toks.append((t, p, blk))
+        islots.append((blk, 0, p % 128))
+        kslots += [(blk, g, p % 128) for g in range(H)]
+    for n, dt, kind, slots in (("k", kv, "kv", kslots), ("i", idt, "idx", islots)):
+        outside = ~_slot_mask(got[n].shape, dt, kind, H, slots)
+        assert np.array_equal(got[n][outside], ref[n][outside]), f"pool {n} changed outside the written slots"
+    for t, p, blk in toks:
+        kg = pools_read(got, kv, idt, H, blk, p, ks, xs)
+        kr = pools_read(ref, kv, idt, H, blk, p, ks, xs)
+        for g in range(H):
+            _near_ties_only(kg[0][g], kr[0][g], _exact(_host(k_new)[t, g], p, k_tf), f"K t{t} g{g}")
+        _near_ties_only(kg[1], kr[1], _exact(_host(i_new)[t], p, i_tf), f"index key t{t}")
+
+
+def pools_read(pl, kv, idt, H, blk, p, ks, xs):
+    """Decoded K of every head and the index key of position p in block blk."""
+    from oracle import pools as op
+    if kv == "mxfp4":
+        ks_ = [op.kv_page_tokens(pl["k"], pl["v"], kv, [blk], ks, 1.0, head=g, num_kv_heads=H)[0][0, p % 128]
+               for g in range(H)]
+    else:
+        page = 8 * blk + (p % 128) // 16
+        ks_ = [op.kv_page_tokens(pl["k"], pl["v"], kv, [page], ks, 1.0, head=g, num_kv_heads=H)[0][0, p % 16]
+               for g in range(H)]
+    key = op.index_block_keys(pl["i"], idt, xs, [blk])[0][p % 128]
+    return ks_, key
+
+
+@pytest.mark.parametrize("out_dtype", ["e4m3", "bf16"])
+@pytest.mark.parametrize("neox,rot", [(True, 128), (False, 64)])
+def test_prepare_query_matches_the_oracle(out_dtype, neox, rot):
+    rng = np.random.default_rng(rot + neox)
+    lens = np.array([70, 1, 0, 40], np.int32)                  # positions 68..69, -1..0, pads, 38..39
+    q_len, H = 2, 16
+    T = len(lens) * q_len
+    qb = torch.from_numpy((rng.standard_normal((T, H, 128)) * 2).astype(np.float32)).to(torch.bfloat16)
+    cos, sin = _rope_tables(69, rot)                           # position 69 lies past the table
+    w = (rng.standard_normal(128) * 0.3 + 1).astype(np.float32)
+    tf = dict(norm_weight=w, eps=1e-5, cos=cos, sin=sin, rot_dim=rot, neox=neox)
+    dev = {n: torch.from_numpy(a).cuda() for n, a in (("w", w), ("cos", cos), ("sin", sin))}
+    nr = isb.norm_rope(dev["w"], 1e-5, dev["cos"], dev["sin"], rot, neox)
+    _say(f"prepare_query {out_dtype} neox {neox} rot {rot}")
+    out = isb.prepare_query(qb.cuda(), torch.from_numpy(lens).cuda(), q_len, nr, out_dtype)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16) if out_dtype == "bf16" else out.cpu().numpy()
+    dec = (lambda c: torch.from_numpy(c.view(np.int16)).view(torch.bfloat16).double().numpy()) \
+        if out_dtype == "bf16" else formats.decode_e4m3
+    qh = _host(qb)
+    for t in range(T):
+        r, i = divmod(t, q_len)
+        p = int(lens[r]) - q_len + i
+        if p < 0:
+            assert not got[t].any()
+            continue
+        if p >= 69:
+            assert np.isnan(dec(got[t])).all()
+            continue
+        ref = writer.prepare_query(qh[t:t + 1], np.array([p + 1]), 1, tf, "bf16" if out_dtype == "bf16" else "e4m3")
+        for h in range(H):
+            _near_ties_only(dec(got[t, h]), dec(ref[0, h]), _exact(qh[t, h], p, tf), f"q t{t} h{h}")

@@ -30,7 +30,7 @@ def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("isb_index_score", "isb_topk_select", "isb_emit_sparse_block_table",
               "isb_sparse_pa_decode", "isb_sparse_pa_workspace_bytes", "isb_strerror", "isb_version",
-              "isb_write_cache", "isb_quantize_e4m3"):
+              "isb_write_cache", "isb_quantize_e4m3", "isb_prepare_query"):
         assert n in names
 
 
@@ -92,8 +92,9 @@ def test_argument_checks_return_before_any_launch(lib):
     assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 32, 1, 128, 0.1,
                                     p, 1 << 20, p) == -3                                         # G = 32
     # the cache writer and the query cast
-    w = lambda k=p, idx=p, ipool=p, H=1, kvdt=1, ks=1.0, idt=1, xs=1.0, q=1: lib.isb_write_cache(  # noqa: E731
-        NULL, k, p, idx, p, 4, p, 2, q, H, p, p, kvdt, ks, 1.0, 64, ipool, idt, xs, 8)
+    w = lambda k=p, idx=p, ipool=p, H=1, kvdt=1, ks=1.0, idt=1, xs=1.0, q=1, ktf=None: lib.isb_write_cache(  # noqa
+        NULL, k, p, idx, p, 4, p, 2, q, H, p, p, kvdt, ks, 1.0, 64, ipool, idt, xs, 8,
+        None if ktf is None else ctypes.byref(ktf), None)
     assert w(k=NULL) == -1
     assert w(idx=NULL) == -1 and w(ipool=NULL) == -1            # index vector and pool go together
     assert w(q=0) == -1
@@ -101,6 +102,18 @@ def test_argument_checks_return_before_any_launch(lib):
     assert w(ks=0.0) == -1 and w(xs=-1.0) == -1                 # fp8 scales must be positive
     assert w(H=70000) == -3
     assert w(k=ctypes.c_void_p(18)) == -1                       # bf16 pairs are read 4 bytes at a time
+    # QK-norm / rope parameters: cos without sin, a rotated width not a multiple of 4, a negative eps
+    assert w(ktf=binding.NormRope(rope_cos=16, rope_positions=8, rot_dim=64)) == -1
+    assert w(ktf=binding.NormRope(rope_cos=16, rope_sin=32, rope_positions=8, rot_dim=66)) == -3
+    assert w(ktf=binding.NormRope(rope_cos=16, rope_sin=32, rope_positions=8, rot_dim=132)) == -3
+    assert w(ktf=binding.NormRope(norm_weight=16, eps=-1.0)) == -1
+    assert w(ktf=binding.NormRope(rope_cos=16, rope_sin=32, rope_positions=0, rot_dim=64)) == -1
+    pq = lambda q=p, H=4, dt=1, nr=None: lib.isb_prepare_query(  # noqa: E731
+        NULL, q, H, p, 2, 1, None if nr is None else ctypes.byref(nr), dt, p)
+    assert pq(q=NULL) == -1 and pq(H=0) == -1
+    assert pq(dt=2) == -2
+    assert pq(H=70000) == -3
+    assert pq(nr=binding.NormRope(rope_cos=16, rope_sin=32, rope_positions=8, rot_dim=2)) == -3
     assert lib.isb_quantize_e4m3(NULL, NULL, 4, p) == -1
     assert lib.isb_quantize_e4m3(NULL, p, 0, p) == -1
     # workspace
