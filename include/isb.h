@@ -310,9 +310,9 @@ typedef struct isb_norm_rope {
  * isb_write_cache - store the new tokens of a step into the paged caches.
  *
  * The cache write in front of the decode (ROCm/ATOM PR 2962, the commit
- * messages under Follow-ups: the fused writer quantises K, V and the index key
- * straight into the MXFP4 / fp8 pages; a layer that reuses another layer's
- * top-k writes K and V only).  Token t = r q + i is stored at position
+ * messages under Follow-ups: one fused kernel encodes K, V and the index key
+ * directly in the MXFP4 / fp8 page format; a layer whose selection comes from
+ * an earlier layer keeps no index keys of its own).  Token t = r q + i is stored at position
  * p = seq_lens[r] - q + i of request r (seq_lens count the new tokens), in
  * block block_table[r][p div 128], slot p mod 128; tokens with p < 0 (pad
  * requests) are skipped.  Encodings:
@@ -359,8 +359,8 @@ ISB_API int isb_write_cache(isb_stream_t stream, const void* k_new, const void* 
  * isb_quantize_e4m3 - out[i] = the e4m3fn code of x[i] with a unit scale
  * (rounding and saturation as ISB_FP8_E4M3 of isb_write_cache), for n bf16
  * elements.  The query cast of the same fused writer (ROCm/ATOM PR 2962,
- * Follow-ups: the main query, and optionally the index query, come back as
- * float8_e4m3fn with a unit, saturating scale); its output is a valid
+ * Follow-ups: it emits the attention query, and on request the index query,
+ * in float8_e4m3fn, scale 1, clamped at the format's maximum); its output is a valid
  * ISB_FP8_E4M3 query for isb_index_score and isb_sparse_pa_decode.
  */
 ISB_API int isb_quantize_e4m3(isb_stream_t stream, const void* x, int64_t n, void* out);
@@ -371,8 +371,8 @@ ISB_API int isb_quantize_e4m3(isb_stream_t stream, const void* x, int64_t n, voi
  * at position seq_lens[r] - q + i) takes the QK-norm and rope of norm_rope
  * (NULL: none) and is written to out [T][num_heads][128] as bf16 (rounded to
  * nearest even) or, with out_dtype ISB_FP8_E4M3, as the unit-scale e4m3 cast
- * of isb_quantize_e4m3 (ROCm/ATOM PR 2962, Follow-ups: the main query comes
- * back as e4m3; the index query too when asked for).  Rows of pad tokens
+ * of isb_quantize_e4m3 (ROCm/ATOM PR 2962, Follow-ups: the fused writer emits
+ * the attention query in e4m3, and the index query on request).  Rows of pad tokens
  * (position < 0) are written as zeros, rows at or past rope_positions as NaN.
  * q and out 4-byte aligned.  Shape errors: num_heads > 65535,
  * num_reqs * decode_query_len > 2^31 - 1.

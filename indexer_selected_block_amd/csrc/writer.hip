@@ -2,9 +2,9 @@
 // the paged caches; isb_quantize_e4m3: the unit-scale e4m3 query cast.
 //
 // The step in front of the decode path (ROCm/ATOM PR 2962, the commit
-// messages under Follow-ups: the fused writer quantises the new tokens' K and
-// V into the MXFP4 / fp8 pages and casts the query to float8_e4m3fn with a unit
-// scale, saturating).  Token i of request r's q new tokens sits at position
+// messages under Follow-ups: one fused kernel encodes the new tokens' K and V
+// in the MXFP4 / fp8 page format and emits the query in float8_e4m3fn, scale
+// 1, clamped at the format's maximum).  Token i of request r's q new tokens sits at position
 // seq_lens[r] - q + i; one wave writes one (token, vector) pair, two dims a
 // lane: the K and V of every KV head and the token's index key.
 //   fp8   - e4m3 of x / scale (formed in fp32): round to nearest, ties to the

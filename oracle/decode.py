@@ -22,9 +22,9 @@ from .pools import BLOCK, kv_page_tokens, request_index_keys
 def causal_length(seq_len: int, q_len: int, i: int) -> int:
     """L_t for query token i of a request of length seq_len.
 
-    Clamped at 0, so a pad request (length 0) with q > 1 computes nothing
-    (PR 2962, the pad-row fix: the emit clamps a row's causal length where it
-    enters)."""
+    Floored at 0, so the rows of a pad request (length 0) with q > 1 select
+    and attend nothing (PR 2962, the pad-row fix: the emit step floors a row's
+    causal length at zero on entry)."""
     return max(0, int(seq_len) - (q_len - 1 - i))
 
 

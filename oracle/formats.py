@@ -5,8 +5,8 @@ Test infrastructure only (see the package docstring).
 Formats, as the sources name them:
 * e4m3fn - ``float8_e4m3fn`` K/V and index values and the e4m3 query
   (ROCm/ATOM PR 2962, Summary: the MXFP4 index is scored with an e4m3 index
-  query; the fused-writer commit message: a ``float8_e4m3fn`` q with a
-  unit-scale saturating cast).
+  query; the fused-writer commit message: the query emitted in
+  ``float8_e4m3fn`` with scale 1, clamped at the format's maximum).
   Definition (OCP 8-bit floating point, E4M3): sign s, 4 exponent bits E
   (bias 7), 3 mantissa bits m; E = 0 is subnormal 2^-6 * m/8; all other codes
   are 2^(E-7) * (1 + m/8) except E = 15, m = 7, which is NaN; no infinities.

@@ -3,9 +3,9 @@
 Test infrastructure only (see the package docstring).
 
 This is the step in front of the decode path (ROCm/ATOM PR 2962, the commit
-messages under Follow-ups: the fused writer quantises the new tokens' keys and
-values into the MXFP4 / fp8 cache pages and casts the query to float8_e4m3fn
-with a unit scale, saturating).  Readings where the sources are silent:
+messages under Follow-ups: one fused kernel encodes the new tokens' keys and
+values in the MXFP4 / fp8 page format and emits the query in float8_e4m3fn,
+scale 1, clamped at the format's maximum).  Readings where the sources are silent:
 
 * placement - token i of request r's q new tokens sits at absolute position
   seq_lens[r] - q + i (the lengths include the new tokens); a position below
