@@ -495,3 +495,63 @@ def test_prepare_query_matches_the_oracle(out_dtype, neox, rot):
         ref = writer.prepare_query(qh[t:t + 1], np.array([p + 1]), 1, tf, "bf16" if out_dtype == "bf16" else "e4m3")
         for h in range(H):
             _near_ties_only(dec(got[t, h]), dec(ref[0, h]), _exact(qh[t, h], p, tf), f"q t{t} h{h}")
+
+
+@pytest.mark.parametrize("name", ["fp8_decode", "mxfp4"])
+def test_fused_decode_step_with_norm_and_rope(name):
+    # The whole step with the fused writer's transform: new K and index keys
+    # written after QK-norm and rope, the query and the index query prepared
+    # with the same (bf16 or e4m3, as the workload's queries are stored), then
+    # the layer.  The oracle runs its own writer, query step and layer from the
+    # same inputs.  These seeds hit no fp32 near-tie (both sides' codes are
+    # equal, checked first), so the chain compares as for any layer.
+    from dataclasses import replace as dc_replace
+
+    from _util import check_chain, host_inputs, oracle_layer, small_configs
+
+    cfg = small_configs()[name]
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + 1)
+    T, H, q = cfg.num_tokens, cfg.num_kv_heads, cfg.query_len
+
+    def bf16(*shape):
+        return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+
+    k_new, v_new, i_new = bf16(T, H, 128), bf16(T, H, 128), bf16(T, 128)
+    q_raw, qi_raw = bf16(T, cfg.num_q_heads, 128), bf16(T, cfg.num_idx_heads, 128)
+    npos = int(hi["seq_lens"].max())
+    cos, sin = _rope_tables(npos, 64)
+    wk, wi, wq, wqi = ((rng.standard_normal(128) * 0.2 + 1).astype(np.float32) for _ in range(4))
+    tfs = {n: dict(norm_weight=wt, eps=1e-6, cos=cos, sin=sin, rot_dim=64, neox=True)
+           for n, wt in (("k", wk), ("i", wi), ("q", wq), ("qi", wqi))}
+    dev = {n: torch.from_numpy(a).cuda() for n, a in (("wk", wk), ("wi", wi), ("wq", wq), ("wqi", wqi),
+                                                      ("cos", cos), ("sin", sin))}
+    nr = {n: isb.norm_rope(dev[wn], 1e-6, dev["cos"], dev["sin"], 64, True)
+          for n, wn in (("k", "wk"), ("i", "wi"), ("q", "wq"), ("qi", "wqi"))}
+    _say(f"fused decode step with norm + rope: {name}")
+    isb.write_cache(k_new.cuda(), v_new.cuda(), i_new.cuda(), w.block_table, w.seq_lens, q, w.k_pool, w.v_pool,
+                    cfg.kv_dtype, w.k_scale, w.v_scale, w.idx_pool, cfg.idx_dtype, w.idx_scale,
+                    k_norm_rope=nr["k"], idx_norm_rope=nr["i"])
+    qg = isb.prepare_query(q_raw.cuda(), w.seq_lens, q, nr["q"], cfg.q_dtype)
+    qig = isb.prepare_query(qi_raw.cuda(), w.seq_lens, q, nr["qi"], cfg.qidx_dtype)
+    w = dc_replace(w, q=qg.view(torch.uint8), q_idx=qig.view(torch.uint8))
+    layer = isb.DecodeLayer(w)
+    layer.run()
+    torch.cuda.synchronize()
+    # the oracle's side
+    writer.write_cache(_host(k_new), _host(v_new), _host(i_new), hi["block_table"], hi["seq_lens"], q,
+                       hi["k_pool"], hi["v_pool"], cfg.kv_dtype, hi["k_scale"], hi["v_scale"], hi["idx_pool"],
+                       cfg.idx_dtype, hi["idx_scale"], k_tf=tfs["k"], idx_tf=tfs["i"])
+    q_ref = writer.prepare_query(_host(q_raw), hi["seq_lens"], q, tfs["q"], cfg.q_dtype)
+    qi_ref = writer.prepare_query(_host(qi_raw), hi["seq_lens"], q, tfs["qi"], cfg.qidx_dtype)
+    assert np.array_equal(w.k_pool.cpu().numpy(), hi["k_pool"]) and np.array_equal(w.idx_pool.cpu().numpy(),
+                                                                                      hi["idx_pool"])
+    assert np.array_equal(w.q.cpu().numpy(), q_ref.view(np.uint8)) and \
+        np.array_equal(w.q_idx.cpu().numpy(), qi_ref.view(np.uint8))
+    hi = dict(hi, q=formats.decode_query(q_ref.view(np.uint8), cfg.q_dtype),
+              q_idx=formats.decode_query(qi_ref.view(np.uint8), cfg.qidx_dtype))
+    ref = oracle_layer(hi)
+    check_chain(hi, layer.scores.cpu().numpy().astype(np.float64), layer.topk.cpu().numpy(),
+                layer.sparse_bt.cpu().numpy(), layer.sparse_ctx.cpu().numpy(), layer.out.float().cpu().numpy(),
+                ref, hi["block_table"])
