@@ -395,3 +395,35 @@ def test_attention_mxfp4_pages_match_dense_on_decoded_values():
             torch.from_numpy(K).expand(1, 16, L, 128), torch.from_numpy(V).expand(1, 16, L, 128),
             scale=w.sm_scale)
         np.testing.assert_allclose(out[t], o.reshape(16, 128).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_shard_selections_merged_give_the_whole_row_selection():
+    # The context-parallel reading: each shard of a row's blocks selects as if
+    # it were a whole row; the top K - 1 of the union of the shards' picks
+    # (excluding the row's tail), plus the tail, is the whole row's selection.
+    import math
+
+    def order(sc, b):                       # larger first, NaN last, -0 == +0, then lower index
+        s = float(sc)
+        return (1, 0.0, b) if math.isnan(s) else (0, -(s + 0.0), b)
+
+    rng = np.random.default_rng(12)
+    for trial in range(300):
+        n = int(rng.integers(2, 90))
+        K = int(rng.integers(1, 12))
+        row = rng.choice([-1.0, -0.0, 0.0, 0.5, 1.0, np.nan, np.inf, -np.inf], size=n) if trial % 3 == 0 \
+            else np.round(rng.standard_normal(n), 1)
+        row = row.astype(np.float32)
+        whole = od.topk_select(row[None, None, :], np.array([n * 128]), 1, K)[0, 0]
+        G = int(rng.integers(1, min(n, 6) + 1))
+        cuts = np.sort(rng.choice(np.arange(1, n), size=G - 1, replace=False)) if G > 1 else np.array([], int)
+        bounds = np.concatenate([[0], cuts, [n]])
+        cands = set()
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            sel = od.topk_select(row[None, None, a:b], np.array([(b - a) * 128]), 1, K)[0, 0]
+            cands |= {a + int(x) for x in sel if x >= 0}
+        tail = n - 1
+        pool = sorted((c for c in cands if c != tail), key=lambda c: order(row[c], c))
+        merged = sorted(pool[:K - 1] + [tail])
+        want = [int(x) for x in whole if x >= 0]
+        assert merged == want, (trial, n, K, G, merged, want)
