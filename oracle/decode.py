@@ -107,6 +107,40 @@ def topk_select(scores, seq_lens, q_len, top_k):
     return out
 
 
+def merge_candidates(cand_scores, cand_ids, seq_lens, q_len, top_k, max_blocks):
+    """Selections [H_kv, T, top_k] from per-row candidates: cand_ids [H_kv, T, C]
+    block ids (distinct in a row; -1 = empty) with their scores.
+
+    The merge step of context parallelism (PR 2962 names the candidate exchange
+    among the users of the emit helper; the reading: shards of a row's blocks
+    each select as if they were the whole row, and the union of their picks,
+    with scores, is merged).  Per row: the tail block n_t - 1 plus the best
+    top_k - 1 candidates with ids in [0, n_t - 1), in topk_select's order; a
+    row with n_t - 1 <= top_k - 1 takes all its blocks, as topk_select does.
+    """
+    cs = np.asarray(cand_scores)
+    ci = np.asarray(cand_ids)
+    H_kv, T, _ = ci.shape
+    out = np.full((H_kv, T, top_k), -1, dtype=np.int32)
+    for t in range(T):
+        r, i = divmod(t, q_len)
+        nt = min(num_blocks(causal_length(seq_lens[r], q_len, i)), max_blocks)
+        if nt == 0:
+            continue
+        tail = nt - 1
+        for g in range(H_kv):
+            if tail <= top_k - 1:
+                sel = np.arange(nt)
+            else:
+                ok = (ci[g, t] >= 0) & (ci[g, t] < tail)
+                ids, sc = ci[g, t][ok], cs[g, t][ok]
+                nan = np.isnan(sc)
+                order = np.lexsort((ids, -np.where(nan, 0.0, sc), nan))
+                sel = np.sort(np.append(ids[order[: top_k - 1]], tail))
+            out[g, t, : sel.size] = sel
+    return out
+
+
 def emit_sparse_block_table(topk, block_table, seq_lens, q_len, num_kv_heads, top_k,
                             pages_per_block):
     """Sparse page table int32 [T H_kv, top_k ppb] and sparse lengths int32 [T H_kv].
