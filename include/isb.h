@@ -14,7 +14,10 @@
  *   isb_sparse_pa_decode         paged attention over the selected pages only
  *                                (split-K flash decode; the last split of a
  *                                row merges it, in the same launch);
- *   isb_select_attend            top-k, emit and attention in one launch.
+ *   isb_select_attend            top-k, emit and attention in one launch;
+ *   isb_topk_merge               a row's selection from the (score, block id)
+ *                                picks of shards of its blocks (the merge
+ *                                step of context parallelism).
  *
  * In front of them, the cache writer of the same decode step:
  *
@@ -210,6 +213,33 @@ ISB_API int isb_topk_select_emit(isb_stream_t stream, const float* scores,
                                  int block_table_stride, int pages_per_block,
                                  int32_t* topk_idx, int32_t* sparse_bt,
                                  int32_t* sparse_ctx);
+
+/*
+ * isb_topk_merge - the selection of each (KV head, token) row from candidates.
+ *
+ * The merge step of context parallelism (ROCm/ATOM PR 2962 lists a candidate
+ * exchange among the users of the emit helper).  When each shard of a row's
+ * blocks (a contiguous range) is selected by isb_topk_select as if it were the
+ * whole row, the shards' picks, gathered with their scores, hold the row's
+ * true winners, and this call returns exactly what isb_topk_select returns on
+ * the whole row: the tail n_t - 1 plus the best top_k - 1 candidates with ids
+ * in [0, n_t - 1) (score descending, NaN below every number, -0.0 == +0.0,
+ * ties to the lower block index), ascending, -1 padded; a row with
+ * n_t - 1 <= top_k - 1 takes all its blocks.  n_t as in isb_topk_select,
+ * clamped to max_blocks.
+ *
+ *   cand_scores  [num_kv_heads][T][num_cands] fp32
+ *   cand_ids     [num_kv_heads][T][num_cands] int32 block ids, distinct within
+ *                a row; -1 (or any id outside [0, n_t - 1)) = no candidate
+ *   seq_lens     [num_reqs] int32
+ *   topk_idx     out, [num_kv_heads][T][top_k] int32
+ * Shape errors: num_cands > 1024, top_k < 1 or > max_blocks,
+ * num_reqs * decode_query_len * num_kv_heads > 2^31 - 1.
+ */
+ISB_API int isb_topk_merge(isb_stream_t stream, const float* cand_scores,
+                           const int32_t* cand_ids, int num_cands, const int32_t* seq_lens,
+                           int num_reqs, int decode_query_len, int num_kv_heads,
+                           int max_blocks, int top_k, int32_t* topk_idx);
 
 /*
  * Bytes of workspace isb_sparse_pa_decode needs for these arguments: one

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     sparse_pa_workspace_bytes,
     strerror,
     topk_select,
+    topk_merge,
     topk_select_emit,
     version,
     write_cache,

@@ -99,6 +99,7 @@ _SIGNATURES = {
     "isb_write_cache": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _F, _F, _I64, _P, _I, _F, _I64,
                          _NR, _NR], _I),
     "isb_prepare_query": ([_P, _P, _I, _P, _I, _I, _NR, _I, _P], _I),
+    "isb_topk_merge": ([_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
     "isb_quantize_e4m3": ([_P, _P, _I64, _P], _I),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -214,6 +215,24 @@ def topk_select_emit(scores, seq_lens, decode_query_len, top_k, block_table, pag
           decode_query_len, H_kv, MB, top_k, block_table.data_ptr(), block_table.shape[1],
           pages_per_block, topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr())
     return topk_idx, sparse_bt, sparse_ctx
+
+
+def topk_merge(cand_scores, cand_ids, seq_lens, decode_query_len, top_k, max_blocks, topk_idx=None):
+    """Selections [H_kv, T, top_k] int32 from candidates [H_kv, T, C] (see isb_topk_merge)."""
+    dev = _dev(cand_scores, cand_ids, seq_lens)
+    if cand_scores.shape != cand_ids.shape or cand_scores.dim() != 3:
+        raise ValueError("cand_scores and cand_ids are [H_kv, T, C]")
+    if cand_scores.dtype != torch.float32 or cand_ids.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("cand_scores fp32, cand_ids and seq_lens int32")
+    H_kv, T, C = cand_ids.shape
+    if T != seq_lens.shape[0] * decode_query_len:
+        raise ValueError("T must be num_reqs * query_len")
+    if topk_idx is None:
+        topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
+    _dev(topk_idx)
+    _call("topk_merge", _stream(dev), cand_scores.data_ptr(), cand_ids.data_ptr(), C, seq_lens.data_ptr(),
+          seq_lens.shape[0], decode_query_len, H_kv, max_blocks, top_k, topk_idx.data_ptr())
+    return topk_idx
 
 
 def sparse_pa_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, sparse_bt_stride, kv_dtype) -> int:

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libisb.so")
 
-SOURCES = ["capi.hip", "index_score.hip", "topk_select.hip", "emit.hip", "sparse_pa.hip", "writer.hip"]
+SOURCES = ["capi.hip", "index_score.hip", "topk_select.hip", "emit.hip", "sparse_pa.hip", "writer.hip", "merge.hip"]
 
 # gfx950 only.  Packed fp32 VALU ops are disabled (-packed-fp32-ops): the
 # compiler must not form v_pk_{add,mul,fma}_f32 on its own.

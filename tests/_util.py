@@ -188,3 +188,28 @@ def oracle_layer(hi):
                            hi["k_pool"], hi["v_pool"], cfg.kv_dtype, hi["k_scale"], hi["v_scale"],
                            hi["block_table"], hi["seq_lens"], cfg.query_len, cfg.num_kv_heads,
                            cfg.max_blocks, cfg.top_k, cfg.pages_per_block, hi["sm_scale"])
+
+
+def shard_candidates(scores, lens, G, K, rng):
+    """Candidates of each decode row (q = 1) from G contiguous shards of its
+    blocks, each selected by topk_select as a whole row: ids [H, T, G K] with
+    their scores, -1 padded, shuffled."""
+    H, T, MB = scores.shape
+    ids = np.full((H, T, G * K), -1, dtype=np.int32)
+    sc = np.zeros((H, T, G * K), dtype=scores.dtype)
+    for t in range(T):
+        n = min(od.num_blocks(int(lens[t])), MB)
+        if n == 0:
+            continue
+        cuts = np.sort(rng.choice(np.arange(1, n), size=min(G, n) - 1, replace=False)) if n > 1 else []
+        bounds = np.concatenate([[0], cuts, [n]]).astype(int)
+        for g in range(H):
+            picks = []
+            for a, b in zip(bounds[:-1], bounds[1:]):
+                sel = od.topk_select(scores[g:g + 1, t:t + 1, a:b], np.array([(b - a) * 128]), 1, K)[0, 0]
+                picks += [a + int(x) for x in sel if x >= 0]
+            picks = rng.permutation(picks)
+            ids[g, t, :len(picks)] = picks
+            sc[g, t, :len(picks)] = scores[g, t, picks]
+    return sc, ids
+

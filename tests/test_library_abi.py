@@ -30,7 +30,7 @@ def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("isb_index_score", "isb_topk_select", "isb_emit_sparse_block_table",
               "isb_sparse_pa_decode", "isb_sparse_pa_workspace_bytes", "isb_strerror", "isb_version",
-              "isb_write_cache", "isb_quantize_e4m3", "isb_prepare_query"):
+              "isb_write_cache", "isb_quantize_e4m3", "isb_prepare_query", "isb_topk_merge"):
         assert n in names
 
 
@@ -114,6 +114,11 @@ def test_argument_checks_return_before_any_launch(lib):
     assert pq(dt=2) == -2
     assert pq(H=70000) == -3
     assert pq(nr=binding.NormRope(rope_cos=16, rope_sin=32, rope_positions=8, rot_dim=2)) == -3
+    # the candidate merge
+    assert lib.isb_topk_merge(NULL, NULL, p, 8, p, 1, 1, 1, 16, 4, p) == -1
+    assert lib.isb_topk_merge(NULL, p, p, 0, p, 1, 1, 1, 16, 4, p) == -1
+    assert lib.isb_topk_merge(NULL, p, p, 1025, p, 1, 1, 1, 16, 4, p) == -3     # too many candidates
+    assert lib.isb_topk_merge(NULL, p, p, 8, p, 1, 1, 1, 16, 17, p) == -3       # top_k > max_blocks
     assert lib.isb_quantize_e4m3(NULL, NULL, 4, p) == -1
     assert lib.isb_quantize_e4m3(NULL, p, 0, p) == -1
     # workspace

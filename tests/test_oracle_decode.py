@@ -429,30 +429,6 @@ def test_shard_selections_merged_give_the_whole_row_selection():
         assert merged == want, (trial, n, K, G, merged, want)
 
 
-def shard_candidates(scores, lens, G, K, rng):
-    """Candidates of each decode row (q = 1) from G contiguous shards of its
-    blocks, each selected by topk_select as a whole row: ids [H, T, G K] with
-    their scores, -1 padded, shuffled."""
-    H, T, MB = scores.shape
-    ids = np.full((H, T, G * K), -1, dtype=np.int32)
-    sc = np.zeros((H, T, G * K), dtype=scores.dtype)
-    for t in range(T):
-        n = min(od.num_blocks(int(lens[t])), MB)
-        if n == 0:
-            continue
-        cuts = np.sort(rng.choice(np.arange(1, n), size=min(G, n) - 1, replace=False)) if n > 1 else []
-        bounds = np.concatenate([[0], cuts, [n]]).astype(int)
-        for g in range(H):
-            picks = []
-            for a, b in zip(bounds[:-1], bounds[1:]):
-                sel = od.topk_select(scores[g:g + 1, t:t + 1, a:b], np.array([(b - a) * 128]), 1, K)[0, 0]
-                picks += [a + int(x) for x in sel if x >= 0]
-            picks = rng.permutation(picks)
-            ids[g, t, :len(picks)] = picks
-            sc[g, t, :len(picks)] = scores[g, t, picks]
-    return sc, ids
-
-
 def test_merge_candidates_of_shards_equals_the_whole_row_selection():
     rng = np.random.default_rng(13)
     for trial in range(40):
@@ -465,6 +441,7 @@ def test_merge_candidates_of_shards_equals_the_whole_row_selection():
         lens = rng.integers(0, MB * 128 + 1, T)
         lens[0] = 0
         G = int(rng.integers(1, 7))
+        from _util import shard_candidates
         sc, ids = shard_candidates(scores, lens, G, K, rng)
         merged = od.merge_candidates(sc, ids, lens, 1, K, MB)
         assert np.array_equal(merged, od.topk_select(scores, lens, 1, K)), trial
