@@ -497,8 +497,10 @@ def time_writer(isb, w, stream, steps):
     return {"kernel": "write_cache", "avg_ms": round(ms, 5), "tokens": live, "algorithmic_bytes": nbytes,
             "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "avg_ms_with_norm_rope": round(ms_nr, 5),
-            "note": "cache write in front of the step, outside value; back-to-back launches, median of 3; "
-                    "with_norm_rope: QK-norm and a 64-dim NeoX rope on K and the index keys"}
+            "note": "cache write in front of the step, outside value; back-to-back calls timed with HIP "
+                    "events, median of 3 (at a decode step's size the host's call rate, ~4-5 us a call, "
+                    "bounds this; the kernel trace gives the kernel alone); with_norm_rope: QK-norm and a "
+                    "64-dim NeoX rope on K and the index keys"}
 
 
 if __name__ == "__main__":
