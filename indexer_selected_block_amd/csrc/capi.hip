@@ -1,7 +1,7 @@
 // Library-wide entry points of the C ABI: version and status text.
 #include "isb_host.h"
 
-extern "C" int isb_version(void) { return 100; }  // 0.1.0
+extern "C" int isb_version(void) { return 200; }  // 0.2.0: the cache writer, query step and candidate merge
 
 extern "C" const char* isb_strerror(int status) {
   switch (status) {
