@@ -555,3 +555,71 @@ def test_fused_decode_step_with_norm_and_rope(name):
     check_chain(hi, layer.scores.cpu().numpy().astype(np.float64), layer.topk.cpu().numpy(),
                 layer.sparse_bt.cpu().numpy(), layer.sparse_ctx.cpu().numpy(), layer.out.float().cpu().numpy(),
                 ref, hi["block_table"])
+
+
+@pytest.mark.parametrize("name", ["fp8_decode", "mxfp4"])
+def test_write_and_layer_replay_from_a_hip_graph(name):
+    # A serving loop captures the whole step: the cache write (with QK-norm and
+    # rope), the query preparation and the layer.  Between replays the pools go
+    # back to their state before the write and every output is overwritten;
+    # each replay must give the eager step's pools and outputs bit for bit.
+    from dataclasses import replace as dc_replace
+
+    from _util import small_configs
+
+    cfg = small_configs()[name]
+    w = wl.make_workload(cfg, device="cuda")
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + 2)
+    T, H, q = cfg.num_tokens, cfg.num_kv_heads, cfg.query_len
+
+    def bf16(*shape):
+        return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16).cuda()
+
+    k_new, v_new, i_new = bf16(T, H, 128), bf16(T, H, 128), bf16(T, 128)
+    q_raw = bf16(T, cfg.num_q_heads, 128)
+    cos, sin = (torch.from_numpy(a).cuda() for a in _rope_tables(int(w.seq_lens.max().item()), 64))
+    wn = torch.from_numpy((rng.standard_normal(128) * 0.2 + 1).astype(np.float32)).cuda()
+    nr = isb.norm_rope(wn, 1e-6, cos, sin, 64, True)
+    q_out = torch.empty((T, cfg.num_q_heads, 128), dtype=torch.bfloat16 if cfg.q_dtype == "bf16" else torch.uint8,
+                        device="cuda")
+    w = dc_replace(w, q=q_out.view(torch.uint8))
+    layer = isb.DecodeLayer(w)
+    pools0 = [t.clone() for t in (w.k_pool, w.v_pool, w.idx_pool)]
+
+    def step():
+        isb.write_cache(k_new, v_new, i_new, w.block_table, w.seq_lens, q, w.k_pool, w.v_pool, cfg.kv_dtype,
+                        w.k_scale, w.v_scale, w.idx_pool, cfg.idx_dtype, w.idx_scale, k_norm_rope=nr,
+                        idx_norm_rope=nr)
+        isb.prepare_query(q_raw, w.seq_lens, q, nr, cfg.q_dtype, out=q_out)
+        layer.run()
+
+    _say(f"graph of write + layer: {name}")
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (w.k_pool, w.v_pool, w.idx_pool, q_out, layer.topk, layer.out)]
+    for t, t0 in zip((w.k_pool, w.v_pool, w.idx_pool), pools0):
+        t.copy_(t0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capturing stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t, t0 in zip((w.k_pool, w.v_pool, w.idx_pool), pools0):
+            t.copy_(t0)                    # eager work between replays
+        q_out.zero_()
+        layer.out.fill_(float("nan"))
+        layer.topk.fill_(-9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (w.k_pool, w.v_pool, w.idx_pool, q_out, layer.topk, layer.out)
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                               b.view(torch.uint8) if b.dtype != torch.int32 else b), f"replay {rep}"
+    del graph
+    torch.cuda.synchronize()
