@@ -209,3 +209,24 @@ def test_bench_counts_each_attended_position_once():
                 for pos in range(128 * b, min(128 * b + 128, Lt)):
                     seen.add((g, r, pos))
     assert bench.distinct_attended_tokens(w, torch.from_numpy(topk)) == len(seen)
+
+
+def test_norm_rope_struct_checks_its_tensors():
+    # Host logic only: the isb_norm_rope the binding builds, and what it refuses.
+    import torch
+    w = torch.ones(128)
+    cos, sin = torch.zeros(10, 32), torch.zeros(10, 32)
+    nr = binding.norm_rope(w, 1e-6, cos, sin, 64, neox=False)
+    assert nr.norm_weight == w.data_ptr() and abs(nr.eps - 1e-6) < 1e-12
+    assert nr.rope_cos == cos.data_ptr() and nr.rope_sin == sin.data_ptr()
+    assert (nr.rope_positions, nr.rot_dim, nr.neox) == (10, 64, 0)
+    empty = binding.norm_rope()
+    assert not empty.norm_weight and not empty.rope_cos
+    with pytest.raises(ValueError):
+        binding.norm_rope(torch.ones(64))                      # weight of the wrong width
+    with pytest.raises(ValueError):
+        binding.norm_rope(w, 1e-6, cos, None, 64)              # cos without sin
+    with pytest.raises(ValueError):
+        binding.norm_rope(w, 1e-6, cos, sin, 128)              # tables narrower than rot_dim / 2
+    with pytest.raises(ValueError):
+        binding.norm_rope(w.double())                          # not fp32
