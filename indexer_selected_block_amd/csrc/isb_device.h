@@ -58,6 +58,15 @@ __device__ __forceinline__ u32x4 bl16_nt(__amdgpu_buffer_rsrc_t r, int voff, int
 __device__ __forceinline__ uint32_t bl4_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 2);
 }
+// The same with the default cache policy: pages that several rows of one
+// request read (their selections share blocks) stay in L2 and the last-level
+// cache between those reads.
+__device__ __forceinline__ u32x4 bl16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bl4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
 
 // ----------------------------------------------------------------- conversions
 // All exact: e4m3 and e2m1 * 2^k values are representable in bf16 (the
