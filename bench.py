@@ -49,10 +49,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="fp8_decode")
-    ap.add_argument("--layers", type=int, default=4,
+    ap.add_argument("--layers", type=int, default=8,
                     help="independent copies of the layer's inputs, used round-robin, so a "
-                         "step does not find the previous step's pages in the 256 MB "
-                         "last-level cache")
+                         "step does not find the pages it reads in the 256 MB last-level "
+                         "cache (a step's pages were last read 8 steps, over 500 MB of "
+                         "attended pages and 5 GB of index keys, earlier)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -210,51 +211,130 @@ def stored_traffic(config, kernel, sha):
     return None
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle, as it is, on whole requests of the same workload until the
-    budget is spent; tokens/s over the requests it finished."""
+def _oracle_worker(folder, fields, wid, nworkers, budget_s, barrier, results):
+    """One CPU process of the oracle baseline: requests wid, wid + nworkers, ...
+    of the saved sample, cycling, until its budget is spent; reports (query
+    tokens, requests, seconds)."""
     import numpy as np
-    import torch
-    from threadpoolctl import threadpool_limits
 
     from oracle import decode as od
     from oracle import formats
 
+    d = {k: np.load(os.path.join(folder, k + ".npy"), mmap_mode="r")
+         for k in ("idx", "k", "v", "off", "lens", "q", "q_idx")}
+    ql, ppb = fields["query_len"], fields["ppb"]
+    off, lens = np.array(d["off"]), np.array(d["lens"])
+    live = [r for r in range(len(lens)) if lens[r] > 0]
+    mine = live[wid::nworkers] or live[:1]
+    barrier.wait(timeout=600)
+    t0 = time.perf_counter()
+    tokens = nreq = 0
+    i = 0
+    while True:
+        r = mine[i % len(mine)]
+        i += 1
+        L, b0, b1 = int(lens[r]), int(off[r]), int(off[r + 1])
+        nb = b1 - b0
+        q = formats.decode_query(np.array(d["q"][r * ql:(r + 1) * ql]), fields["q_dtype"])
+        q_idx = formats.decode_query(np.array(d["q_idx"][r * ql:(r + 1) * ql]), fields["qidx_dtype"])
+        od.decode_layer(q, q_idx, d["idx"][b0:b1], fields["idx_dtype"], fields["idx_scale"],
+                        d["k"][b0 * ppb:b1 * ppb], d["v"][b0 * ppb:b1 * ppb], fields["kv_dtype"],
+                        fields["k_scale"], fields["v_scale"], np.arange(nb, dtype=np.int64)[None, :], [L], ql,
+                        fields["num_kv_heads"], nb, fields["top_k"], ppb, fields["sm_scale"])
+        tokens += ql
+        nreq += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    results.put((tokens, nreq, time.perf_counter() - t0))
+
+
+def cpu_baseline(w, budget_s, max_sample_bytes=3 << 30):
+    """The oracle, as it is, on whole requests of the same workload, in
+    parallel processes over this host's cores (one numpy / BLAS thread each),
+    until each has spent the budget; tokens/s of all of them together.  The
+    sample is the batch's requests in order, as many as fit in
+    max_sample_bytes of host copies of their pages."""
+    import multiprocessing as mp
+    import tempfile
+
+    import numpy as np
+
     cfg = w.cfg
     ppb = cfg.pages_per_block
-    done_tokens, elapsed, nreq = 0, 0.0, 0
-    # whole requests in order, cycling over the batch until the budget is spent
-    order = [r for _ in range(1000) for r in range(cfg.total_reqs)]
-    with threadpool_limits(limits=1):
-        for r in order:
-            if elapsed >= budget_s and nreq >= 2:
-                break
-            L = int(w.seq_lens[r])
-            nb = -(-L // 128)
-            if nb == 0:
-                continue
-            ids = w.block_table[r, :nb].long()
-            # copy this request's pages to the host (not timed), renumbered 0..nb-1
-            idx_pool = w.idx_pool[ids].cpu().numpy()
-            kv = lambda p: p.view(p.shape[0] // ppb, -1)[ids].cpu().reshape(nb * ppb, -1).numpy()  # noqa: E731
-            k_pool, v_pool = kv(w.k_pool), kv(w.v_pool)
-            toks = torch.arange(r * cfg.query_len, (r + 1) * cfg.query_len, device=w.q.device)
-            qb = w.q[toks].cpu().numpy()
-            qib = w.q_idx[toks].cpu().numpy()
-            bt = np.arange(nb, dtype=np.int64)[None, :]
-            t0 = time.perf_counter()
-            q = formats.decode_query(qb, cfg.q_dtype)
-            q_idx = formats.decode_query(qib, cfg.qidx_dtype)
-            od.decode_layer(q, q_idx, idx_pool, cfg.idx_dtype, w.idx_scale, k_pool, v_pool,
-                            cfg.kv_dtype, w.k_scale, w.v_scale, bt, [L], cfg.query_len,
-                            cfg.num_kv_heads, nb, cfg.top_k, ppb, w.sm_scale)
-            elapsed += time.perf_counter() - t0
-            done_tokens += cfg.query_len
-            nreq += 1
-    return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nreq} whole requests of the same workload, taken in order and cycling "
-                      f"({done_tokens} query tokens), {elapsed:.1f} s of CPU, numpy float64 with "
-                      f"BLAS limited to 1 thread"}
+    affinity = len(os.sched_getaffinity(0))
+    # one process a core, at most 16: the CPU share of one GPU on the boxes
+    # this runs on
+    nproc = max(1, min(affinity, 16))
+    lens_all = w.seq_lens.cpu().numpy()
+    per_block = w.idx_pool.shape[1] + 2 * ppb * w.k_pool.shape[1]
+    reqs, nbytes = [], 0
+    for r, L in enumerate(lens_all):
+        nb = -(-int(L) // 128)
+        if reqs and nbytes + nb * per_block > max_sample_bytes:
+            break
+        reqs.append(r)
+        nbytes += nb * per_block
+    # each sampled request's pages copied to the host (not timed), renumbered
+    lens = lens_all[reqs]
+    nblk = [-(-int(L) // 128) for L in lens]
+    off = np.concatenate([[0], np.cumsum(nblk)]).astype(np.int64)
+    ids = torch_cat_blocks(w, reqs, nblk)
+    kv = lambda p: p.view(p.shape[0] // ppb, -1)[ids].cpu().reshape(len(ids) * ppb, -1).numpy()  # noqa: E731
+    ql = cfg.query_len
+    toks = [r * ql + i for r in reqs for i in range(ql)]
+    fields = dict(query_len=ql, ppb=ppb, q_dtype=cfg.q_dtype, qidx_dtype=cfg.qidx_dtype,
+                  idx_dtype=cfg.idx_dtype, kv_dtype=cfg.kv_dtype, num_kv_heads=cfg.num_kv_heads, top_k=cfg.top_k,
+                  idx_scale=w.idx_scale, k_scale=w.k_scale, v_scale=w.v_scale, sm_scale=w.sm_scale)
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    with tempfile.TemporaryDirectory() as tmp:
+        for name, arr in (("idx", w.idx_pool[ids].cpu().numpy()), ("k", kv(w.k_pool)), ("v", kv(w.v_pool)),
+                          ("off", off), ("lens", lens), ("q", w.q[toks].cpu().numpy()),
+                          ("q_idx", w.q_idx[toks].cpu().numpy())):
+            np.save(os.path.join(tmp, name + ".npy"), arr)
+            del arr
+        for k in env:
+            os.environ[k] = "1"
+        try:
+            ctx = mp.get_context("spawn")    # fresh interpreters: no GPU state is inherited
+            barrier, results = ctx.Barrier(nproc), ctx.Queue()
+            procs = [ctx.Process(target=_oracle_worker, args=(tmp, fields, i, nproc, budget_s, barrier, results))
+                     for i in range(nproc)]
+            for p in procs:
+                p.start()
+            got = []
+            deadline = time.time() + budget_s + 900
+            while len(got) < nproc:
+                try:
+                    got.append(results.get(timeout=5))
+                except Exception:  # queue.Empty: check that every worker is still alive
+                    dead = [p.exitcode for p in procs if p.exitcode not in (None, 0)]
+                    if dead or time.time() > deadline:
+                        for p in procs:
+                            p.kill()
+                        raise RuntimeError(f"CPU oracle workers failed (exit codes {dead})")
+            for p in procs:
+                p.join()
+        finally:
+            for k, v in env.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    tokens = sum(g[0] for g in got)
+    nreq = sum(g[1] for g in got)
+    rate = sum(g[0] / g[2] for g in got)    # the processes run side by side
+    return {"value": rate, "unit": "tokens/s", "cores": nproc, "kind": "oracle",
+            "sample": f"the first {len(reqs)} of {len(lens_all)} requests of the same workload, whole; "
+                      f"{nproc} processes, one a core ({affinity} cores in this process's affinity), each "
+                      f"cycling over its share for ~{budget_s:.0f} s: {nreq} requests ({tokens} query tokens) "
+                      f"in all; numpy float64 with BLAS limited to 1 thread a process"}
+
+
+def torch_cat_blocks(w, reqs, nblk):
+    """Device block ids of the given requests' blocks, request after request."""
+    import torch
+    parts = [w.block_table[r, :n].long() for r, n in zip(reqs, nblk) if n]
+    return torch.cat(parts) if parts else torch.zeros(0, dtype=torch.long, device=w.block_table.device)
 
 
 def main():

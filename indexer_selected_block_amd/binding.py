@@ -148,6 +148,64 @@ def _code(dtype) -> int:
     return DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
 
 
+# Bytes of one page: a K or V page of one KV head (16 tokens bf16 / fp8, 128
+# tokens MXFP4) and an index page (128 tokens).
+KV_PAGE_BYTES = {BF16: 4096, FP8_E4M3: 2048, MXFP4: 8704}
+IDX_PAGE_BYTES = {BF16: 32768, FP8_E4M3: 16384, MXFP4: 8704}
+
+
+def _check_kv_pools(k_pool, v_pool, kv_dtype, num_kv_heads) -> int:
+    """K and V pools: uint8 [pages, num_kv_heads * page bytes], the same shape
+    (one page id addresses both, so the kernels bound V by K's page count);
+    returns the page count."""
+    code = _code(kv_dtype)
+    if code not in KV_PAGE_BYTES:
+        raise NotImplementedError(f"K/V dtype {kv_dtype!r} is not bf16, fp8 or mxfp4")
+    row = num_kv_heads * KV_PAGE_BYTES[code]
+    for name, pool in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if pool.dtype != torch.uint8 or pool.dim() != 2 or pool.shape[1] != row:
+            raise ValueError(f"{name} must be uint8 [pages, {row}] (num_kv_heads x page bytes), "
+                             f"got {pool.dtype} {tuple(pool.shape)}")
+    if v_pool.shape != k_pool.shape:
+        raise ValueError(f"k_pool {tuple(k_pool.shape)} and v_pool {tuple(v_pool.shape)} must have the same "
+                         f"pages: one page id addresses both")
+    return k_pool.shape[0]
+
+
+def _check_idx_pool(idx_pool, idx_dtype) -> int:
+    """Index pool: uint8 [blocks, index page bytes]; returns the block count."""
+    code = _code(idx_dtype)
+    if code not in IDX_PAGE_BYTES:
+        raise NotImplementedError(f"index dtype {idx_dtype!r} is not bf16, fp8 or mxfp4")
+    row = IDX_PAGE_BYTES[code]
+    if idx_pool.dtype != torch.uint8 or idx_pool.dim() != 2 or idx_pool.shape[1] != row:
+        raise ValueError(f"idx_pool must be uint8 [blocks, {row}], got {idx_pool.dtype} {tuple(idx_pool.shape)}")
+    return idx_pool.shape[0]
+
+
+def _check_int32(**tensors) -> None:
+    for name, t in tensors.items():
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32, got {t.dtype}")
+
+
+def _check_query(name, q, q_dtype, tokens, heads) -> None:
+    """A query [tokens, heads, 128] stored as bf16 (2 bytes an element) or e4m3
+    (1 byte): any torch dtype whose storage has exactly that many bytes."""
+    code = _code(q_dtype)
+    if code not in (BF16, FP8_E4M3):
+        raise NotImplementedError(f"{name} dtype {q_dtype!r} is not bf16 or e4m3")
+    want = tokens * heads * 128 * (2 if code == BF16 else 1)
+    if q.dim() < 2 or q.shape[0] != tokens or q.shape[1] != heads or q.numel() * q.element_size() != want:
+        raise ValueError(f"{name} must hold [{tokens}, {heads}, 128] {'bf16' if code == BF16 else 'e4m3'} "
+                         f"elements, got {q.dtype} {tuple(q.shape)}")
+
+
+def _check_shape(name, t, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def version() -> int:
     return int(load_library().isb_version())
 
@@ -159,11 +217,22 @@ def strerror(status: int) -> str:
 def index_score(q_idx, q_idx_dtype, idx_pool, idx_dtype, idx_scale, block_table, seq_lens,
                 decode_query_len, num_kv_heads, max_blocks, scores=None):
     """Block scores [num_kv_heads, T, max_blocks] fp32 (see isb_index_score)."""
-    dev = _dev(q_idx, idx_pool, block_table, seq_lens)
     T, H_idx = q_idx.shape[0], q_idx.shape[1]
+    _check_idx_pool(idx_pool, idx_dtype)
+    _check_int32(block_table=block_table, seq_lens=seq_lens)
+    R = seq_lens.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != R or seq_lens.dim() != 1:
+        raise ValueError("block_table is [num_reqs, stride] and seq_lens [num_reqs]")
+    if T != R * decode_query_len:
+        raise ValueError(f"q_idx has {T} tokens, expected num_reqs * decode_query_len = {R * decode_query_len}")
+    _check_query("q_idx", q_idx, q_idx_dtype, T, H_idx)
+    dev = _dev(q_idx, idx_pool, block_table, seq_lens)
     if scores is None:
         scores = torch.empty((num_kv_heads, T, max_blocks), dtype=torch.float32, device=dev)
     _dev(scores)
+    if scores.dtype != torch.float32:
+        raise ValueError("scores must be float32")
+    _check_shape("scores", scores, (num_kv_heads, T, max_blocks))
     _call("index_score", _stream(dev), q_idx.data_ptr(), _code(q_idx_dtype), H_idx,
           idx_pool.data_ptr(), _code(idx_dtype), float(idx_scale), idx_pool.shape[0],
           block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(), seq_lens.shape[0],
@@ -171,13 +240,31 @@ def index_score(q_idx, q_idx_dtype, idx_pool, idx_dtype, idx_scale, block_table,
     return scores
 
 
+def _check_scores(scores, seq_lens, decode_query_len):
+    """scores fp32 [H_kv, T, max_blocks] with T = num_reqs * decode_query_len; seq_lens int32."""
+    _check_int32(seq_lens=seq_lens)
+    if scores.dtype != torch.float32 or scores.dim() != 3:
+        raise ValueError("scores must be float32 [num_kv_heads, T, max_blocks]")
+    if scores.shape[1] != seq_lens.shape[0] * decode_query_len:
+        raise ValueError("scores has T != num_reqs * decode_query_len rows")
+    return scores.shape
+
+
+def _check_table(block_table, seq_lens):
+    _check_int32(block_table=block_table)
+    if block_table.dim() != 2 or block_table.shape[0] != seq_lens.shape[0]:
+        raise ValueError("block_table must be int32 [num_reqs, stride]")
+
+
 def topk_select(scores, seq_lens, decode_query_len, top_k, topk_idx=None):
     """Selected blocks [num_kv_heads, T, top_k] int32 (see isb_topk_select)."""
+    H_kv, T, MB = _check_scores(scores, seq_lens, decode_query_len)
     dev = _dev(scores, seq_lens)
-    H_kv, T, MB = scores.shape
     if topk_idx is None:
         topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
     _dev(topk_idx)
+    _check_int32(topk_idx=topk_idx)
+    _check_shape("topk_idx", topk_idx, (H_kv, T, top_k))
     _call("topk_select", _stream(dev), scores.data_ptr(), seq_lens.data_ptr(), seq_lens.shape[0],
           decode_query_len, H_kv, MB, top_k, topk_idx.data_ptr())
     return topk_idx
@@ -186,13 +273,20 @@ def topk_select(scores, seq_lens, decode_query_len, top_k, topk_idx=None):
 def emit_sparse_block_table(topk_idx, block_table, seq_lens, decode_query_len, pages_per_block,
                             sparse_bt=None, sparse_ctx=None):
     """(sparse_bt [T*H_kv, K*ppb], sparse_ctx [T*H_kv]) int32 (see isb_emit_sparse_block_table)."""
-    dev = _dev(topk_idx, block_table, seq_lens)
+    _check_int32(topk_idx=topk_idx, seq_lens=seq_lens)
+    _check_table(block_table, seq_lens)
     H_kv, T, K = topk_idx.shape
+    if T != seq_lens.shape[0] * decode_query_len:
+        raise ValueError("topk_idx has T != num_reqs * decode_query_len rows")
+    dev = _dev(topk_idx, block_table, seq_lens)
     if sparse_bt is None:
         sparse_bt = torch.empty((T * H_kv, K * pages_per_block), dtype=torch.int32, device=dev)
     if sparse_ctx is None:
         sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
     _dev(sparse_bt, sparse_ctx)
+    _check_int32(sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    _check_shape("sparse_bt", sparse_bt, (T * H_kv, K * pages_per_block))
+    _check_shape("sparse_ctx", sparse_ctx, (T * H_kv,))
     _call("emit_sparse_block_table", _stream(dev), topk_idx.data_ptr(), block_table.data_ptr(),
           block_table.shape[1], seq_lens.data_ptr(), seq_lens.shape[0], decode_query_len, H_kv, K,
           pages_per_block, sparse_bt.data_ptr(), sparse_ctx.data_ptr())
@@ -202,8 +296,9 @@ def emit_sparse_block_table(topk_idx, block_table, seq_lens, decode_query_len, p
 def topk_select_emit(scores, seq_lens, decode_query_len, top_k, block_table, pages_per_block,
                      topk_idx=None, sparse_bt=None, sparse_ctx=None):
     """(topk_idx, sparse_bt, sparse_ctx) in one launch (see isb_topk_select_emit)."""
+    H_kv, T, MB = _check_scores(scores, seq_lens, decode_query_len)
+    _check_table(block_table, seq_lens)
     dev = _dev(scores, seq_lens, block_table)
-    H_kv, T, MB = scores.shape
     if topk_idx is None:
         topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
     if sparse_bt is None:
@@ -211,6 +306,10 @@ def topk_select_emit(scores, seq_lens, decode_query_len, top_k, block_table, pag
     if sparse_ctx is None:
         sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
     _dev(topk_idx, sparse_bt, sparse_ctx)
+    _check_int32(topk_idx=topk_idx, sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    _check_shape("topk_idx", topk_idx, (H_kv, T, top_k))
+    _check_shape("sparse_bt", sparse_bt, (T * H_kv, top_k * pages_per_block))
+    _check_shape("sparse_ctx", sparse_ctx, (T * H_kv,))
     _call("topk_select_emit", _stream(dev), scores.data_ptr(), seq_lens.data_ptr(), seq_lens.shape[0],
           decode_query_len, H_kv, MB, top_k, block_table.data_ptr(), block_table.shape[1],
           pages_per_block, topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr())
@@ -219,7 +318,6 @@ def topk_select_emit(scores, seq_lens, decode_query_len, top_k, block_table, pag
 
 def topk_merge(cand_scores, cand_ids, seq_lens, decode_query_len, top_k, max_blocks, topk_idx=None):
     """Selections [H_kv, T, top_k] int32 from candidates [H_kv, T, C] (see isb_topk_merge)."""
-    dev = _dev(cand_scores, cand_ids, seq_lens)
     if cand_scores.shape != cand_ids.shape or cand_scores.dim() != 3:
         raise ValueError("cand_scores and cand_ids are [H_kv, T, C]")
     if cand_scores.dtype != torch.float32 or cand_ids.dtype != torch.int32 or seq_lens.dtype != torch.int32:
@@ -227,6 +325,7 @@ def topk_merge(cand_scores, cand_ids, seq_lens, decode_query_len, top_k, max_blo
     H_kv, T, C = cand_ids.shape
     if T != seq_lens.shape[0] * decode_query_len:
         raise ValueError("T must be num_reqs * query_len")
+    dev = _dev(cand_scores, cand_ids, seq_lens)
     if topk_idx is None:
         topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
     _dev(topk_idx)
@@ -240,11 +339,23 @@ def sparse_pa_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, sparse_bt_s
         num_tokens, num_q_heads, num_kv_heads, sparse_bt_stride, _code(kv_dtype)))
 
 
+def _check_out(out, T, num_q_heads):
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    _check_shape("out", out, (T, num_q_heads, 128))
+
+
 def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, sparse_bt, sparse_ctx,
                      num_q_heads, num_kv_heads, sm_scale, out=None, workspace=None):
     """Attention output [T, num_q_heads, 128] bf16 (see isb_sparse_pa_decode)."""
-    dev = _dev(q, k_pool, v_pool, sparse_bt, sparse_ctx)
     T = q.shape[0]
+    num_pages = _check_kv_pools(k_pool, v_pool, kv_dtype, num_kv_heads)
+    _check_query("q", q, q_dtype, T, num_q_heads)
+    _check_int32(sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    if sparse_bt.dim() != 2 or sparse_bt.shape[0] != T * num_kv_heads:
+        raise ValueError(f"sparse_bt must be int32 [{T * num_kv_heads}, stride]")
+    _check_shape("sparse_ctx", sparse_ctx, (T * num_kv_heads,))
+    dev = _dev(q, k_pool, v_pool, sparse_bt, sparse_ctx)
     stride = sparse_bt.shape[1]
     need = sparse_pa_workspace_bytes(T, num_q_heads, num_kv_heads, stride, kv_dtype)
     if workspace is None:  # zero-filled: the arrival counters start at zero
@@ -252,8 +363,9 @@ def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, spa
     if out is None:
         out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
     _dev(out, workspace)
+    _check_out(out, T, num_q_heads)
     _call("sparse_pa_decode", _stream(dev), q.data_ptr(), _code(q_dtype), k_pool.data_ptr(),
-          v_pool.data_ptr(), _code(kv_dtype), k_pool.shape[0], float(k_scale), float(v_scale),
+          v_pool.data_ptr(), _code(kv_dtype), num_pages, float(k_scale), float(v_scale),
           sparse_bt.data_ptr(), stride, sparse_ctx.data_ptr(), T, num_q_heads, num_kv_heads, 128,
           float(sm_scale), workspace.data_ptr(), workspace.numel(), out.data_ptr())
     return out
@@ -263,8 +375,11 @@ def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_d
                   kv_dtype, k_scale, v_scale, num_q_heads, sm_scale, topk_idx=None, sparse_bt=None,
                   sparse_ctx=None, out=None, workspace=None):
     """(topk_idx, sparse_bt, sparse_ctx, out): top-k, emit and attention (see isb_select_attend)."""
+    H_kv, T, MB = _check_scores(scores, seq_lens, decode_query_len)
+    _check_table(block_table, seq_lens)
+    num_pages = _check_kv_pools(k_pool, v_pool, kv_dtype, H_kv)
+    _check_query("q", q, q_dtype, T, num_q_heads)
     dev = _dev(scores, seq_lens, block_table, q, k_pool, v_pool)
-    H_kv, T, MB = scores.shape
     ppb = 1 if _code(kv_dtype) == DTYPE_CODES["mxfp4"] else 8
     if topk_idx is None:
         topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
@@ -278,9 +393,14 @@ def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_d
     if workspace is None:  # zero-filled: the arrival counters start at zero
         workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
     _dev(topk_idx, sparse_bt, sparse_ctx, out, workspace)
+    _check_int32(topk_idx=topk_idx, sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    _check_shape("topk_idx", topk_idx, (H_kv, T, top_k))
+    _check_shape("sparse_bt", sparse_bt, (T * H_kv, top_k * ppb))
+    _check_shape("sparse_ctx", sparse_ctx, (T * H_kv,))
+    _check_out(out, T, num_q_heads)
     _call("select_attend", _stream(dev), scores.data_ptr(), seq_lens.data_ptr(), seq_lens.shape[0],
           decode_query_len, H_kv, MB, top_k, block_table.data_ptr(), block_table.shape[1], q.data_ptr(),
-          _code(q_dtype), k_pool.data_ptr(), v_pool.data_ptr(), _code(kv_dtype), k_pool.shape[0],
+          _code(q_dtype), k_pool.data_ptr(), v_pool.data_ptr(), _code(kv_dtype), num_pages,
           float(k_scale), float(v_scale), num_q_heads, float(sm_scale), workspace.data_ptr(),
           workspace.numel(), topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr(), out.data_ptr())
     return topk_idx, sparse_bt, sparse_ctx, out
@@ -313,8 +433,6 @@ def _write_cache_args(k_new, v_new, idx_new, block_table, seq_lens, decode_query
                       idx_norm_rope=None):
     if (idx_new is None) != (idx_pool is None):
         raise ValueError("idx_new and idx_pool go together")
-    dev = _dev(k_new, v_new, block_table, seq_lens, k_pool, v_pool,
-               *(() if idx_new is None else (idx_new, idx_pool)))
     R, H_kv = seq_lens.shape[0], k_new.shape[1]
     T = R * decode_query_len
     if k_new.shape != (T, H_kv, 128) or v_new.shape != (T, H_kv, 128) or \
@@ -325,12 +443,11 @@ def _write_cache_args(k_new, v_new, idx_new, block_table, seq_lens, decode_query
             raise ValueError("new keys and values are bf16")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_table.shape[0] != R:
         raise ValueError("block_table [num_reqs, stride] and seq_lens [num_reqs] are int32")
-    kv_page = {BF16: 4096, FP8_E4M3: 2048, MXFP4: 8704}.get(_code(kv_dtype))
-    idx_page = {BF16: 32768, FP8_E4M3: 16384, MXFP4: 8704}.get(_code(idx_dtype))
-    for pool, row in ((k_pool, kv_page and H_kv * kv_page), (v_pool, kv_page and H_kv * kv_page)) + \
-            (() if idx_pool is None else ((idx_pool, idx_page),)):
-        if row and (pool.dtype != torch.uint8 or pool.numel() != pool.shape[0] * row):
-            raise ValueError("pools are uint8 [pages, page bytes (times H_kv for K / V)]")
+    _check_kv_pools(k_pool, v_pool, kv_dtype, H_kv)
+    if idx_pool is not None:
+        _check_idx_pool(idx_pool, idx_dtype)
+    dev = _dev(k_new, v_new, block_table, seq_lens, k_pool, v_pool,
+               *(() if idx_new is None else (idx_new, idx_pool)))
     return (_stream(dev), k_new.data_ptr(), v_new.data_ptr(),
             None if idx_new is None else idx_new.data_ptr(), block_table.data_ptr(), block_table.shape[1],
             seq_lens.data_ptr(), R, decode_query_len, H_kv, k_pool.data_ptr(),

@@ -5,8 +5,8 @@ Test infrastructure only (see the package docstring).
 Pool layout read here (its own code; it shares nothing with the GPU path):
 
 * index cache - one page per 128-token block, page id = block id
-  (ROCm/ATOM PR 2962, the commit that declares the MXFP4 caches: "a single
-  8704 B field per block for the index key"):
+  (ROCm/ATOM PR 2962, the commit that declares the MXFP4 caches: the index
+  cache holds one 8704 B page for each 128-token block):
     bf16  eight 16-token tiles, each in the element order of a 16-token K
           page (below);
     fp8   the same with e4m3 elements, times the per-tensor ``idx_scale``
@@ -27,10 +27,10 @@ Pool layout read here (its own code; it shares nothing with the GPU path):
   page id addresses a K page and a V page (vLLM PR 61889, Details).
 * K/V cache, mxfp4 - one 8704 B page per block for K and one for V
   (PR 2962, Summary: K and V use the same MXFP4 page format).
-* A K/V page id holds one page per KV head ([num_pages][H_kv][page]): the
-  MXFP4 cache declares one field per (page, KV head) for K and for V, and a
-  single field per block for the index key (PR 2962, the commit that
-  declares the MXFP4 caches).
+* A K/V page id holds one page per KV head ([num_pages][H_kv][page]): in the
+  MXFP4 caches K and V each get a page for every pair of page id and KV head,
+  while the index key gets one page for each block, whatever the head count
+  (PR 2962, the commit that declares the MXFP4 caches).
 """
 from __future__ import annotations
 

@@ -10,10 +10,19 @@ scale 1, clamped at the format's maximum).  Readings where the sources are silen
 * placement - token i of request r's q new tokens sits at absolute position
   seq_lens[r] - q + i (the lengths include the new tokens); a position below
   zero (a pad request) is not written;
-* e4m3fn encoding - of x / scale formed in fp32 (the precision the kernel
-  decides in): round to nearest, ties to the even code, magnitudes above 448
-  saturate to 448, NaN becomes 0x7F; the sign is kept (a negative value that
-  rounds to zero is -0), as in every encoding here;
+* e4m3fn encoding with a per-tensor scale - the library's quantiser is
+  defined on its own interface: the scale is an fp32 argument and the value an
+  fp32 number (bf16 inputs, or the fp32 result of the optional norm / rope), so
+  the quotient is the fp32 division fl32(x / scale), and the code is that
+  quotient rounded to the nearest e4m3fn value, ties to the even code -
+  exactly what the plain tensor expression (x / scale).to(float8_e4m3fn)
+  computes on fp32 tensors.  Magnitudes above 448 saturate to 448 (the
+  saturating cast of ROCm/ATOM PR 2962, Follow-ups), NaN becomes 0x7F and the
+  sign is kept (a negative value that rounds to zero is -0), as in every
+  encoding here.  Rounding the fp32 quotient can differ from rounding the exact
+  quotient where the two lie on either side of a midpoint between two codes;
+  this definition takes the fp32 quotient.  With a unit scale (the query
+  cast) the quotient is exact and the two agree;
 * MXFP4 encoding (OCP MX v1.0) - per 32 consecutive dims the shared exponent
   is floor(log2 amax) - 2 (2 is the largest e2m1 exponent), clamped to the
   e8m0 range [-127, 127] (-127 for an all-zero group); each element's e2m1
@@ -150,14 +159,19 @@ def transform(x, pos: int, tf) -> np.ndarray:
     return y.astype(np.float32).astype(np.float64)
 
 
+def quantize_e4m3_scaled(x, scale: float) -> np.ndarray:
+    """e4m3fn bytes of the fp32 quotient fl32(x / scale): x and scale are fp32
+    numbers (x rounded to fp32 first), the division is IEEE fp32 division,
+    then encode_e4m3 rounds that quotient (see the module docstring)."""
+    y = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    return encode_e4m3(y.astype(np.float64))
+
+
 def _element_bytes(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
     """[..., 128] values -> [..., 128, e] stored bytes for bf16 / fp8."""
     if dtype == "bf16":
         return _bf16_bytes(x)
-    # the quotient is rounded to fp32 before the e4m3 rounding, as the kernel
-    # forms it: both sides take the rounding decision on the same number
-    y = np.asarray(x, dtype=np.float32) / np.float32(scale)
-    return encode_e4m3(y.astype(np.float64))[..., None]
+    return quantize_e4m3_scaled(x, scale)[..., None]
 
 
 def write_cache(k_new, v_new, idx_new, block_table, seq_lens, q_len: int,

@@ -5,10 +5,11 @@
   tables bit-exact when both sides get the same fp32 scores / the same
   selection; attention within 1e-2 max|V| + 1e-3 (fp8, MXFP4) or
   4e-3 max|V| (bf16).
-* The chained layer: the GPU's own selection must be a valid top-k of the
-  oracle's fp64 scores (exactly the oracle's wherever no two candidates are
-  closer than the GPU's score error), and rows that agree must agree on the
-  table and the output.
+* The chained layer, every row: the oracle's top-k of the GPU's own fp32
+  scores equals the GPU's selection bit for bit, the oracle's emit of it
+  equals the GPU's table, and the oracle's attention over the GPU's table
+  matches the GPU's output; the GPU's selection is also a valid top-k of the
+  oracle's fp64 scores within the GPU's score error.
 * Full-size workloads in the launch configuration the benchmark times, on
   sampled requests the oracle recomputes from their own pages.
 """
@@ -481,7 +482,7 @@ def test_full_size_sampled(name):
         lens = w.seq_lens.cpu().numpy()
         reqs = [int(np.nonzero(lens > 0)[0][0]), int(np.nonzero(lens > 0)[0][-1]), int(np.nonzero(lens == 0)[0][0])]
     _say(f"[full] {name}: oracle on requests {reqs}")
-    hi, toks = sample_requests(w, reqs)
+    hi, toks, remap = sample_requests(w, reqs)
     ref = oracle_layer(hi)
     H_kv = cfg.num_kv_heads
     rows = [t * H_kv + g for t in toks for g in range(H_kv)]
@@ -489,6 +490,6 @@ def test_full_size_sampled(name):
     check_chain(hi, layer.scores[:, toks, :].cpu().numpy().astype(np.float64),
                  layer.topk[:, toks, :].cpu().numpy(), layer.sparse_bt[rows].cpu().numpy(),
                  layer.sparse_ctx[rows].cpu().numpy(), layer.out[toks].float().cpu().numpy(), ref,
-                 bt_global)
+                 bt_global, remap)
     del w, layer
     torch.cuda.empty_cache()

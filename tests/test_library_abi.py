@@ -147,6 +147,72 @@ def test_binding_refuses_cpu_tensors(lib):
         binding.topk_select(torch.zeros(1, 1, 4), torch.ones(1, dtype=torch.int32), 1, 2)
 
 
+def _fp8_pools(pages, heads=1):
+    import torch
+    return (torch.zeros(pages, heads * 2048, dtype=torch.uint8), torch.zeros(pages, heads * 2048, dtype=torch.uint8))
+
+
+def test_binding_refuses_pools_that_do_not_match_before_any_launch(lib):
+    # The kernels bound page ids by the K pool's page count and address V with
+    # the same id: a V pool shorter than K (the K/V length mismatch vLLM PR
+    # 61889 trims), a flat pool or the wrong row size is refused on the host.
+    # CPU tensors: every refusal below comes before the device check.
+    import torch
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)  # noqa: E731
+    q = torch.zeros(2, 16, 128, dtype=torch.bfloat16)
+    k, v = _fp8_pools(64)
+    for kp, vp in ((k, v[:60]), (k.reshape(-1), v.reshape(-1)), (k[:, :1024], v[:, :1024]),
+                   (k.view(torch.int8), v.view(torch.int8))):
+        with pytest.raises(ValueError, match="pool"):
+            binding.sparse_pa_decode(q, "bf16", kp, vp, "fp8", 1.0, 1.0, i32(2, 128), i32(2), 16, 1, 0.1)
+        with pytest.raises(ValueError, match="pool"):
+            binding.select_attend(torch.zeros(1, 2, 16), i32(2), 1, 4, i32(2, 16), q, "bf16", kp, vp, "fp8",
+                                  1.0, 1.0, 16, 0.1)
+        with pytest.raises(ValueError, match="pool"):
+            binding.write_cache(torch.zeros(2, 1, 128, dtype=torch.bfloat16),
+                                torch.zeros(2, 1, 128, dtype=torch.bfloat16), None, i32(2, 16), i32(2), 1,
+                                kp, vp, "fp8", 1.0, 1.0)
+    with pytest.raises(ValueError, match="idx_pool"):
+        binding.index_score(torch.zeros(2, 1, 128, dtype=torch.bfloat16), "bf16",
+                            torch.zeros(8, 8704, dtype=torch.uint8), "fp8", 1.0, i32(2, 8), i32(2), 1, 1, 8)
+
+
+def test_binding_refuses_wrong_index_and_query_types(lib):
+    import torch
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)  # noqa: E731
+    k, v = _fp8_pools(64)
+    q = torch.zeros(2, 16, 128, dtype=torch.bfloat16)
+    # int64 tables and lengths
+    with pytest.raises(ValueError, match="int32"):
+        binding.sparse_pa_decode(q, "bf16", k, v, "fp8", 1.0, 1.0, torch.zeros(2, 128, dtype=torch.int64),
+                                 i32(2), 16, 1, 0.1)
+    with pytest.raises(ValueError, match="int32"):
+        binding.topk_select(torch.zeros(1, 2, 16), torch.zeros(2, dtype=torch.int64), 1, 4)
+    with pytest.raises(ValueError, match="int32"):
+        binding.index_score(torch.zeros(2, 1, 128, dtype=torch.bfloat16), "bf16",
+                            torch.zeros(8, 16384, dtype=torch.uint8), "fp8", 1.0,
+                            torch.zeros(2, 8, dtype=torch.int64), i32(2), 1, 1, 8)
+    # a query whose storage does not hold [T, H, 128] elements of its dtype
+    with pytest.raises(ValueError, match="q"):
+        binding.sparse_pa_decode(torch.zeros(2, 16, 128, dtype=torch.uint8), "bf16", k, v, "fp8", 1.0, 1.0,
+                                 i32(2, 128), i32(2), 16, 1, 0.1)
+    with pytest.raises(ValueError, match="q_idx"):
+        binding.index_score(torch.zeros(2, 1, 64, dtype=torch.bfloat16), "bf16",
+                            torch.zeros(8, 16384, dtype=torch.uint8), "fp8", 1.0, i32(2, 8), i32(2), 1, 1, 8)
+    with pytest.raises(NotImplementedError):
+        binding.sparse_pa_decode(q, "mxfp4", k, v, "fp8", 1.0, 1.0, i32(2, 128), i32(2), 16, 1, 0.1)
+    # sparse table rows and lengths must match the query's rows
+    with pytest.raises(ValueError, match="sparse_bt"):
+        binding.sparse_pa_decode(q, "bf16", k, v, "fp8", 1.0, 1.0, i32(3, 128), i32(2), 16, 1, 0.1)
+    with pytest.raises(ValueError, match="sparse_ctx"):
+        binding.sparse_pa_decode(q, "bf16", k, v, "fp8", 1.0, 1.0, i32(2, 128), i32(3), 16, 1, 0.1)
+    # scores must be fp32 [H_kv, num_reqs * q, MB]
+    with pytest.raises(ValueError, match="scores"):
+        binding.topk_select(torch.zeros(1, 3, 16), i32(2), 1, 4)
+    with pytest.raises(ValueError, match="scores"):
+        binding.topk_select(torch.zeros(1, 2, 16, dtype=torch.float64), i32(2), 1, 4)
+
+
 def test_mfma_overlap_check_reads_register_ranges():
     # The build's assembly check: a destination over a source is caught, an
     # accumulator identical to the destination is not.

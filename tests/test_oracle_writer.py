@@ -25,6 +25,62 @@ def test_e4m3_encode_matches_torch_including_ties():
     assert np.array_equal(got, ref)
 
 
+def _double_rounding_cases():
+    """(x, scale) pairs, x a bf16 value and scale an fp32 number, whose fp32
+    quotient fl32(x / scale) lands exactly on the midpoint between two
+    adjacent e4m3 values while the exact quotient lies off it, so that rounding
+    the exact quotient and rounding the fp32 quotient give different codes.
+    Built from the midpoints of torch's own e4m3 value table, independent of
+    the oracle's tables."""
+    from fractions import Fraction
+    vals = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    out = []
+    for c in range(8, 0x7E):
+        mid = Fraction(vals[c]) / 2 + Fraction(vals[c + 1]) / 2
+        for x in (0.1171875, 0.75, 1.0, 1.5, 3.25, 7.0, 13.5, 100.0):
+            base = np.float32(float(Fraction(x) / mid))
+            for step in range(-3, 4):
+                s = np.nextafter(base, np.float32(np.inf if step > 0 else 0), dtype=np.float32)
+                for _ in range(abs(step) - 1):
+                    s = np.nextafter(s, np.float32(np.inf if step > 0 else 0), dtype=np.float32)
+                s = base if step == 0 else s
+                q32 = np.float32(np.float32(x) / s)
+                exact = Fraction(x) / Fraction(float(s))
+                if Fraction(float(q32)) != mid or exact == mid:
+                    continue
+                out.append((x, float(s), c, exact > mid))
+    return out
+
+
+def test_scaled_e4m3_is_the_rounding_of_the_fp32_quotient():
+    # The library's quantiser with a per-tensor scale: the code of fl32(x / scale),
+    # rounded to nearest with ties to even.  Where that differs from rounding the
+    # exact quotient (double-rounding cases), the oracle must follow the stated
+    # definition, and so must torch's own fp32 division followed by its e4m3 cast.
+    cases = _double_rounding_cases()
+    differ = 0
+    for x, s, c, above in cases:
+        got = int(writer.quantize_e4m3_scaled(np.float64(x), s))
+        ties_even = c if c % 2 == 0 else c + 1                 # the tie at the midpoint: even code
+        exact = c + 1 if above else c                           # nearest to the exact quotient
+        lib = int((torch.tensor([x], dtype=torch.float32) / torch.tensor([s], dtype=torch.float32))
+                  .to(torch.float8_e4m3fn).view(torch.uint8)[0])
+        assert got == ties_even == lib, (x, s, c)
+        differ += exact != got
+    assert differ >= 100, f"only {differ} cases separate the two roundings"
+    # and the cache writer stores exactly these codes (one fp8 key per case)
+    for x, s, c, _ in cases[:64]:
+        k_pool = np.zeros((8, 2048), dtype=np.uint8)
+        v_pool = np.zeros((8, 2048), dtype=np.uint8)
+        idx_pool = np.zeros((1, 16384), dtype=np.uint8)
+        k = np.full((1, 1, 128), x)
+        writer.write_cache(k, k, None, np.array([[0]]), np.array([1]), 1, k_pool, v_pool, "fp8", s, s,
+                           idx_pool, "fp8", 1.0)
+        K, _ = pools.kv_page_tokens(k_pool, v_pool, "fp8", [0], 1.0, 1.0)
+        code = int(writer.encode_e4m3(K[0, 0, 0]))
+        assert code == (c if c % 2 == 0 else c + 1)
+
+
 def test_e4m3_encode_saturates_keeps_sign_and_nan():
     got = writer.encode_e4m3([448.0, 460.0, 1e6, -1e6, np.inf, -np.inf, np.nan, -0.0, -1e-12])
     assert list(got) == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE, 0x7F, 0x80, 0x80]
