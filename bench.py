@@ -16,10 +16,13 @@ Prints one JSON line: decode tokens/s of the whole step (value), the
 attended-KV HBM rate of the attention, per-call durations (the step's two
 calls, and the path's separate calls index_score, topk_select_emit and
 sparse_pa_decode) taken as differences between back-to-back passes of K steps
-timed with HIP events on the launch stream, a roofline entry for the dominant
-kernel (and one for the attention alone), a device copy's measured rate at the
+timed with HIP events on the launch stream (with a 512 MB scrub between the
+steps of every pass, so no step finds its inputs in the last-level cache), a
+roofline entry for the dominant kernel (and one for the attention alone), the
+measured ceilings of the two large launches (their page reads with no
+arithmetic, in their own grids), a device copy's measured rate at the
 attention's transfer size and at 1 GiB next to the nominal peak, and the CPU
-oracle timed on a bounded sample of the same workload on this host.
+oracle timed on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -54,6 +57,8 @@ def parse():
                          "step does not find the pages it reads in the 256 MB last-level "
                          "cache (a step's pages were last read 8 steps, over 500 MB of "
                          "attended pages and 5 GB of index keys, earlier)")
+    ap.add_argument("--scrub-mb", type=int, default=512,
+                    help="MB a copy moves between the steps of the per-call timing passes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -185,7 +190,7 @@ def kernel_sources_sha():
     files = {"index_score": "index_score.hip", "topk_select_emit": "topk_select.hip",
              "sparse_pa_decode": "sparse_pa.hip", "select_attend": "sparse_pa.hip"}
     common = b"".join(open(os.path.join(csrc, f), "rb").read()
-                      for f in ("isb_device.h", "isb_host.h", "select_device.h"))
+                      for f in ("isb_device.h", "isb_host.h", "select_device.h", "grid_maps.h"))
     return {k: hashlib.sha256(common + open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
             for k, f in files.items()}
 
@@ -401,7 +406,7 @@ def main():
         w, c = L.w, L.w.cfg
         isb.sparse_pa_decode(w.q, c.q_dtype, w.k_pool, w.v_pool, c.kv_dtype, w.k_scale, w.v_scale,
                              L.sparse_bt, L.sparse_ctx, c.num_q_heads, c.num_kv_heads, w.sm_scale,
-                             out=L.out, workspace=L.workspace)
+                             out=L.out, workspace=L.workspace, decode_query_len=c.query_len)
 
     def call_select_attend(L):
         w, c = L.w, L.w.cfg
@@ -423,17 +428,30 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    # the four passes in turn, three times; each pass's median, so that one
-    # noisy pass does not move a difference
-    reps = {"i": [], "it": [], "ita": [], "step": []}
+    # A scrub between steps of these passes (a copy that moves --scrub-mb MB
+    # through the memory system, in every pass alike, so that it cancels in
+    # the differences) leaves nothing of a step's inputs in the 256 MB
+    # last-level cache for the next step, whatever the workload's size.
+    scrub_half = max(1, args.scrub_mb // 2) << 20
+    scrub_src = torch.ones(scrub_half, dtype=torch.uint8, device=dev)
+    scrub_dst = torch.empty_like(scrub_src)
+
+    def scrub(L):
+        scrub_dst.copy_(scrub_src)
+
+    # the passes in turn, three times; each pass's median, so that one noisy
+    # pass does not move a difference
+    reps = {"s": [], "i": [], "it": [], "ita": [], "step": []}
     for _ in range(3):
-        reps["i"].append(pass_ms([call_index]))
-        reps["it"].append(pass_ms([call_index, call_topk]))
-        reps["ita"].append(pass_ms([call_index, call_topk, call_attend]))
-        reps["step"].append(pass_ms([call_index, call_select_attend]))
-    t_i, t_it, t_ita, t_step = (sorted(reps[k])[1] for k in ("i", "it", "ita", "step"))
-    dur_ms = {"index_score": t_i, "topk_select_emit": t_it - t_i, "sparse_pa_decode": t_ita - t_it,
+        reps["s"].append(pass_ms([scrub]))
+        reps["i"].append(pass_ms([call_index, scrub]))
+        reps["it"].append(pass_ms([call_index, call_topk, scrub]))
+        reps["ita"].append(pass_ms([call_index, call_topk, call_attend, scrub]))
+        reps["step"].append(pass_ms([call_index, call_select_attend, scrub]))
+    t_s, t_i, t_it, t_ita, t_step = (sorted(reps[k])[1] for k in ("s", "i", "it", "ita", "step"))
+    dur_ms = {"index_score": t_i - t_s, "topk_select_emit": t_it - t_i, "sparse_pa_decode": t_ita - t_it,
               "select_attend": t_step - t_i}
+    ceilings = time_ceilings(layers, pass_ms, scrub, t_s, stream)
     # the same with one input copy: the attention's pages can stay in the
     # last-level cache from the step before (reported apart, never as value)
     all_layers = layers
@@ -503,6 +521,13 @@ def main():
     }
     if dominant != "index_score":
         result["roofline_index_score"] = roof("index_score")
+    for k, c in ceilings.items():
+        kernel = {"index_gather": "index_score", "attention_gather": "sparse_pa_decode"}[k]
+        gbps = alg[kernel] / (c["avg_ms"] * 1e-3) / 1e9
+        c.update({"GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                  "kernel_over_ceiling": round(dur_ms[kernel] / c["avg_ms"], 3),
+                  "bytes": int(round(alg[kernel]))})
+    result["ceilings"] = ceilings
     result["measured_copy"] = {"at_attention_size": measured_copy(int(alg["sparse_pa_decode"])),
                                "at_1GiB": measured_copy(1 << 30)}
     if args.cpu_seconds > 0:
@@ -512,6 +537,63 @@ def main():
         result["cpu_baseline"] = None
     result["write_cache"] = time_writer(isb, w0, stream, args.steps)
     print(json.dumps(result))
+
+
+def time_ceilings(layers, pass_ms, scrub, t_scrub, stream):
+    """The measurement kernels of libisb_ceiling on the same inputs and
+    passes as the layer's calls: the index scan's and the attention's page
+    reads with no arithmetic, in their grids.  Per launch, as the passes'
+    difference to the scrub alone."""
+    import ctypes
+
+    import torch
+
+    from indexer_selected_block_amd import binding as bd
+    from indexer_selected_block_amd.build import CEILING_LIB_PATH
+
+    lib = ctypes.CDLL(CEILING_LIB_PATH)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.isb_ceiling_index_gather.argtypes = [P, P, I, I64, P, I, P, I, I, I, I, P]
+    lib.isb_ceiling_attention_gather.argtypes = [P, P, P, I, I64, P, I, P, I, I, I, P, ctypes.c_size_t]
+    lib.isb_ceiling_attention_words.argtypes = [I, I, I, I]
+    lib.isb_ceiling_attention_words.restype = ctypes.c_size_t
+    cfg = layers[0].w.cfg
+    st = ctypes.c_void_p(stream.cuda_stream)
+    dev = layers[0].w.q.device
+    idx_out = torch.empty((cfg.total_reqs, cfg.max_blocks), dtype=torch.float32, device=dev)
+    words = lib.isb_ceiling_attention_words(cfg.num_tokens, cfg.num_kv_heads, layers[0].sparse_bt.shape[1],
+                                            bd._code(cfg.kv_dtype))
+    att_out = torch.empty((max(int(words), 1),), dtype=torch.int32, device=dev)
+
+    def index_gather(L):
+        w = L.w
+        rc = lib.isb_ceiling_index_gather(st, w.idx_pool.data_ptr(), bd._code(cfg.idx_dtype), w.idx_pool.shape[0],
+                                          w.block_table.data_ptr(), w.block_table.shape[1], w.seq_lens.data_ptr(),
+                                          w.seq_lens.shape[0], cfg.query_len, cfg.num_idx_heads, cfg.max_blocks,
+                                          idx_out.data_ptr())
+        if rc:
+            raise RuntimeError(f"isb_ceiling_index_gather: status {rc}")
+
+    def attention_gather(L):
+        w = L.w
+        rc = lib.isb_ceiling_attention_gather(st, w.k_pool.data_ptr(), w.v_pool.data_ptr(), bd._code(cfg.kv_dtype),
+                                              w.k_pool.shape[0], L.sparse_bt.data_ptr(), L.sparse_bt.shape[1],
+                                              L.sparse_ctx.data_ptr(), cfg.num_tokens, cfg.query_len,
+                                              cfg.num_kv_heads, att_out.data_ptr(), att_out.numel())
+        if rc:
+            raise RuntimeError(f"isb_ceiling_attention_gather: status {rc}")
+
+    out = {}
+    kinds = [("attention_gather", attention_gather)]
+    if not scorer_is_wide(cfg):
+        kinds.insert(0, ("index_gather", index_gather))
+    for name, f in kinds:
+        t = sorted(pass_ms([f, scrub]) for _ in range(3))[1] - t_scrub
+        out[name] = {"avg_ms": round(t, 5)}
+    out["index_gather" if "index_gather" in out else "attention_gather"]["method"] = (
+        "the same page reads, grid and cache policy as the call, no arithmetic (libisb_ceiling); "
+        "per launch over the input copies, with the scrub between steps, like the calls")
+    return out
 
 
 def writer_bytes(cfg, live_tokens):

@@ -262,6 +262,11 @@ ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, in
  * multiplied by k_scale / v_scale.  Rows with sparse_ctx = 0 output zeros.
  *
  *   q           [num_tokens][num_q_heads][128], q_dtype ISB_BF16 or ISB_FP8_E4M3
+ *   decode_query_len  query tokens per request (the decode call's own
+ *               argument): num_tokens is a multiple of it, and the rows of
+ *               one request's tokens may select the same pages.  It changes
+ *               only how pages are read (with 1, no page is read twice in a
+ *               call and pages are streamed past the caches), never a result.
  *   k_pool, v_pool  [num_pages][num_kv_heads] pages of kv_dtype (layout above)
  *   sparse_bt   [num_tokens * num_kv_heads][sparse_bt_stride] int32 page ids
  *   sparse_ctx  [num_tokens * num_kv_heads] int32, <= sparse_bt_stride * P
@@ -272,7 +277,8 @@ ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, in
  *               of it may hold anything.  Calls that share a workspace must
  *               not overlap in time.
  *   out         out, [num_tokens][num_q_heads][128] bf16
- * Shape errors: head_dim != 128, num_q_heads % num_kv_heads, G > 16.
+ * Shape errors: head_dim != 128, num_q_heads % num_kv_heads, G > 16,
+ * num_tokens % decode_query_len.
  */
 ISB_API int isb_sparse_pa_decode(isb_stream_t stream,
                          const void* q, int q_dtype,
@@ -280,9 +286,9 @@ ISB_API int isb_sparse_pa_decode(isb_stream_t stream,
                          int64_t num_pages, float k_scale, float v_scale,
                          const int32_t* sparse_bt, int sparse_bt_stride,
                          const int32_t* sparse_ctx, int num_tokens,
-                         int num_q_heads, int num_kv_heads, int head_dim,
-                         float sm_scale, void* workspace, size_t workspace_bytes,
-                         void* out);
+                         int decode_query_len, int num_q_heads, int num_kv_heads,
+                         int head_dim, float sm_scale, void* workspace,
+                         size_t workspace_bytes, void* out);
 
 /*
  * isb_select_attend - isb_topk_select_emit followed by isb_sparse_pa_decode,

@@ -94,7 +94,7 @@ _SIGNATURES = {
     "isb_select_attend": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _I, _I64, _F, _F, _I, _F,
                            _P, _SZ, _P, _P, _P, _P], _I),
     "isb_sparse_pa_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
-    "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I,
+    "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I, _I,
                               _F, _P, _SZ, _P], _I),
     "isb_write_cache": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _F, _F, _I64, _P, _I, _F, _I64,
                          _NR, _NR], _I),
@@ -346,8 +346,10 @@ def _check_out(out, T, num_q_heads):
 
 
 def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, sparse_bt, sparse_ctx,
-                     num_q_heads, num_kv_heads, sm_scale, out=None, workspace=None):
-    """Attention output [T, num_q_heads, 128] bf16 (see isb_sparse_pa_decode)."""
+                     num_q_heads, num_kv_heads, sm_scale, out=None, workspace=None, decode_query_len=1):
+    """Attention output [T, num_q_heads, 128] bf16 (see isb_sparse_pa_decode;
+    decode_query_len: query tokens per request, which only decides how pages
+    are read)."""
     T = q.shape[0]
     num_pages = _check_kv_pools(k_pool, v_pool, kv_dtype, num_kv_heads)
     _check_query("q", q, q_dtype, T, num_q_heads)
@@ -366,7 +368,8 @@ def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, spa
     _check_out(out, T, num_q_heads)
     _call("sparse_pa_decode", _stream(dev), q.data_ptr(), _code(q_dtype), k_pool.data_ptr(),
           v_pool.data_ptr(), _code(kv_dtype), num_pages, float(k_scale), float(v_scale),
-          sparse_bt.data_ptr(), stride, sparse_ctx.data_ptr(), T, num_q_heads, num_kv_heads, 128,
+          sparse_bt.data_ptr(), stride, sparse_ctx.data_ptr(), T, int(decode_query_len), num_q_heads,
+          num_kv_heads, 128,
           float(sm_scale), workspace.data_ptr(), workspace.numel(), out.data_ptr())
     return out
 

@@ -12,8 +12,11 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libisb.so")
+# measurement kernels for the benchmark (include/isb_ceiling.h): not part of the layer
+CEILING_LIB_PATH = os.path.join(PKG_DIR, "libisb_ceiling.so")
 
 SOURCES = ["capi.hip", "index_score.hip", "topk_select.hip", "emit.hip", "sparse_pa.hip", "writer.hip", "merge.hip"]
+CEILING_SOURCES = ["ceiling.hip"]
 
 # gfx950 only.  Packed fp32 VALU ops are disabled (-packed-fp32-ops): the
 # compiler must not form v_pk_{add,mul,fma}_f32 on its own.
@@ -31,10 +34,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every kernel source into libisb.so next to this file; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+def _compile(sources, out_path, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out_path + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines()
@@ -43,8 +45,18 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every kernel source into libisb.so next to this file; returns its path."""
+    return _compile(SOURCES, LIB_PATH, verbose)
+
+
+def build_ceiling_library(verbose: bool = False) -> str:
+    """Compile the benchmark's measurement kernels into libisb_ceiling.so."""
+    return _compile(CEILING_SOURCES, CEILING_LIB_PATH, verbose)
 
 
 _MFMA = re.compile(r"^\s*(v_mfma\S*)\s+(.*)$")
@@ -104,4 +116,5 @@ def check_mfma_operands() -> int:
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_ceiling_library(verbose=True))
     print(f"checked {check_mfma_operands()} MFMA instructions: no operand overlap")

@@ -33,6 +33,7 @@
 // key m's dims 32 g + (16 / esize) h ...), so each load instruction reads one
 // contiguous KiB; MXFP4 pages keep their token-major format (64 B a key: one
 // 16-key tile is also one contiguous KiB a load).
+#include "grid_maps.h"
 #include "isb_device.h"
 #include "isb_host.h"
 
@@ -49,27 +50,8 @@ struct ScoreArgs {
   int H_idx, bt_stride, R, q_len, H_kv, MB;
 };
 
-constexpr int kScoreWaves = 4;        // waves (blocks) per workgroup
 
-// Column group of request r taken by workgroup column p of gx, for workgroups
-// of BPW blocks.  Workgroups are dealt round-robin to the eight dies (XCDs),
-// each with its own L2.  This mapping hands each die whole 32-block spans (one
-// 128-byte line of a score row), so the workgroups that write a line share an
-// L2, which merges their 4- and 8-byte writes before the line goes to HBM
-// (spread over eight L2s, each partial line was written back on its own).
-// The spans rotate over the dies from request to request: the spans past a
-// short request's end hold no keys, and a fixed span-to-die map would leave
-// the dies that own the last spans idle.  Any mapping is correct; this one
-// only places the work.
-template <int BPW>
-__device__ __forceinline__ int score_column(int p, int gx, int r) {
-  constexpr int LW = 32 / BPW;  // workgroups per span
-  const int full = gx / (8 * LW) * (8 * LW);
-  if (p >= full) return p;
-  const int k = p & 7, q = p >> 3;
-  const int j = q / LW, w = q % LW;
-  return LW * (8 * j + ((k + r) & 7)) + w;
-}
+
 constexpr int kMaxQueryRows = 64;     // q_len * H_idx of the tile / stream variants
 constexpr long long kMaxWideRows = 1 << 20;  // q_len * H_idx of the wide variant
 

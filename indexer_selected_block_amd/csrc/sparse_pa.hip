@@ -51,9 +51,13 @@
 // dim 8 r + dt.
 //
 // Page loads are raw buffer loads from a wave-uniform descriptor of the page
-// (one offset register a wave) with the default cache policy: the rows of one
-// request share most of their pages (a prefill chunk, speculative tokens), and
-// even rows that share none ran slightly faster than with nontemporal loads.
+// (one offset register a wave).  When a request has several query tokens (a
+// prefill chunk, speculative tokens) its rows share most of their pages, and
+// the loads keep the default cache policy so that the rows after the first
+// find those pages in L2; with one token a request no page is read twice in a
+// launch, and 16-token pages are streamed past the caches (nontemporal
+// loads), which raises the rate the memory system delivers them at.
+#include "grid_maps.h"
 #include "isb_device.h"
 #include "isb_host.h"
 #include "select_device.h"
@@ -78,17 +82,6 @@ struct PaArgs {
 
 constexpr int kPaWaves = 4;
 constexpr int kMergeGroup = 8;  // splits whose partials the merging workgroup loads at once
-
-// Row of grid column x.  Workgroups are dealt round-robin to the eight dies
-// (XCDs), each with its own L2; consecutive rows (the tokens of one request,
-// whose selections share blocks) are given to one die, die d taking rows
-// [d R / 8, (d + 1) R / 8), so a block several of them attend is fetched into
-// that die's L2 once.  A permutation of the rows: any mapping gives the same
-// results.  Rows past the last multiple of eight keep their column.
-__device__ __forceinline__ int grid_row(int x, int rows) {
-  const int per = rows >> 3;
-  return x < 8 * per ? (x & 7) * per + (x >> 3) : x;
-}
 
 template <int Q_DT>
 __device__ __forceinline__ bf16x8 load_q8_t(const uint8_t* row, int dim0) {
@@ -269,15 +262,17 @@ struct PageRegs {
   u32x4 v[NC];
 };
 
-template <int KV_DT>
+template <int KV_DT, bool NT>
 __device__ __forceinline__ void load_k16(PageRegs<KV_DT>& pr, __amdgpu_buffer_rsrc_t kpage, int lane) {
 #pragma unroll
-  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.k[h] = bl16(kpage, 1024 * h + 16 * lane, 0);
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h)
+    pr.k[h] = NT ? bl16_nt(kpage, 1024 * h + 16 * lane, 0) : bl16(kpage, 1024 * h + 16 * lane, 0);
 }
-template <int KV_DT>
+template <int KV_DT, bool NT>
 __device__ __forceinline__ void load_v16(PageRegs<KV_DT>& pr, __amdgpu_buffer_rsrc_t vpage, int lane) {
 #pragma unroll
-  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h) pr.v[h] = bl16(vpage, 1024 * h + 16 * lane, 0);
+  for (int h = 0; h < PageRegs<KV_DT>::NC; ++h)
+    pr.v[h] = NT ? bl16_nt(vpage, 1024 * h + 16 * lane, 0) : bl16(vpage, 1024 * h + 16 * lane, 0);
 }
 
 // Keys at or past nvalid in a page may hold anything (0 x NaN would poison
@@ -339,7 +334,7 @@ __device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const
 // A split is walked one round (four runs, one per wave) at a time; each
 // round's loads are issued together and its logits give one exact max per
 // head, folded into the wave's running max between rounds.
-template <int KV_DT, int Q_DT, int RUN, typename IdFn>
+template <int KV_DT, int Q_DT, int RUN, bool NT, typename IdFn>
 __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, int row, int split, int kvh,
                                                int n_tok, bf16x8 (&qb)[4], int my_ids, IdFn ids,
                                                __bf16* out_row) {
@@ -387,12 +382,12 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, i
       const int64_t id = __builtin_amdgcn_readlane(my_ids, ibase + (j < cnt ? j : 0));
       ok[j] = page_ok(id, a.num_pages);
       use[j] = (ok[j] ? id : 0) * hstride + hoff;
-      load_k16<KV_DT>(pr[j], page_rsrc(a.kp + use[j], PB), lane);
+      load_k16<KV_DT, NT>(pr[j], page_rsrc(a.kp + use[j], PB), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 0; j < RUN; ++j) {
-      load_v16<KV_DT>(pr[j], page_rsrc(a.vp + use[j], PB), lane);
+      load_v16<KV_DT, NT>(pr[j], page_rsrc(a.vp + use[j], PB), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Pass 1: every logit of the run, then one exact max per head.
@@ -461,9 +456,10 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, i
   finish_split(a, wp, row, split, live, out_row);
 }
 
-// RUN: pages of one wave's run (a power of two).  grid (rows, splits), four
-// waves a workgroup; page ids come from the sparse page table.
-template <int KV_DT, int Q_DT, int RUN>
+// RUN: pages of one wave's run (a power of two); NT: nontemporal page loads.
+// grid (rows, splits), four waves a workgroup; page ids come from the sparse
+// page table.
+template <int KV_DT, int Q_DT, int RUN, bool NT>
 __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   constexpr int ROUND = 4 * RUN;
@@ -492,7 +488,7 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
     for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
   }
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  attend_split16<KV_DT, Q_DT, RUN>(a, wp, row, split, kvh, n_tok, qb, my_ids, load_ids, out_row);
+  attend_split16<KV_DT, Q_DT, RUN, NT>(a, wp, row, split, kvh, n_tok, qb, my_ids, load_ids, out_row);
 }
 
 // ----------------------------------------------------------------- select + attend
@@ -515,7 +511,7 @@ struct SelArgs {
 
 constexpr int kSelMaxBlocks = 2048;
 
-template <int KV_DT, int Q_DT, int RUN, int E>
+template <int KV_DT, int Q_DT, int RUN, bool NT, int E>
 __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   constexpr int ROUND = 4 * RUN;
@@ -570,7 +566,7 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   };
   const int my_ids = ids(0);
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  attend_split16<KV_DT, Q_DT, RUN>(a, wp, row, split, kvh, n_tok, qb, my_ids, ids, out_row);
+  attend_split16<KV_DT, Q_DT, RUN, NT>(a, wp, row, split, kvh, n_tok, qb, my_ids, ids, out_row);
 }
 
 // ----------------------------------------------------------------- MXFP4 pages
@@ -750,14 +746,16 @@ __global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
   attend_split_mx<Q_DT>(a, wp, row, split, t, kvh, n_tok, id_raw, out_row);
 }
 
+// nt: one query token a request, so no page is read twice in the launch.
 template <int KV_DT, int Q_DT>
-static void launch_decode(const PaArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (KV_DT == ISB_MXFP4)
+static void launch_decode(const PaArgs& a, dim3 grid, bool nt, hipStream_t st) {
+  if constexpr (KV_DT == ISB_MXFP4) {
     hipLaunchKernelGGL((pamx_kernel<Q_DT>), grid, dim3(256), 0, st, a);
-  else if constexpr (KV_DT == ISB_BF16)
-    hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, 4>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, 8>), grid, dim3(256), 0, st, a);
+  } else {
+    constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
+    if (nt) hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, false>), grid, dim3(256), 0, st, a);
+  }
 }
 
 }  // namespace isb
@@ -816,21 +814,22 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
 }
 
 template <int KV_DT, int Q_DT, int E>
-static void launch_select_attend_e(const PaArgs& a, const SelArgs& sa, dim3 grid, hipStream_t st) {
+static void launch_select_attend_e(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
   if constexpr (KV_DT == ISB_MXFP4) {
     hipLaunchKernelGGL((pamxsel_kernel<Q_DT, E>), grid, dim3(256), 0, st, a, sa);
   } else {
     constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
-    hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, E>), grid, dim3(256), 0, st, a, sa);
+    if (nt) hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, true, E>), grid, dim3(256), 0, st, a, sa);
+    else hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, false, E>), grid, dim3(256), 0, st, a, sa);
   }
 }
 
 template <int KV_DT, int Q_DT>
-static void launch_select_attend(const PaArgs& a, const SelArgs& sa, dim3 grid, hipStream_t st) {
-  if (sa.MB <= 256) launch_select_attend_e<KV_DT, Q_DT, 1>(a, sa, grid, st);
-  else if (sa.MB <= 512) launch_select_attend_e<KV_DT, Q_DT, 2>(a, sa, grid, st);
-  else if (sa.MB <= 1024) launch_select_attend_e<KV_DT, Q_DT, 4>(a, sa, grid, st);
-  else launch_select_attend_e<KV_DT, Q_DT, 8>(a, sa, grid, st);
+static void launch_select_attend(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
+  if (sa.MB <= 256) launch_select_attend_e<KV_DT, Q_DT, 1>(a, sa, grid, nt, st);
+  else if (sa.MB <= 512) launch_select_attend_e<KV_DT, Q_DT, 2>(a, sa, grid, nt, st);
+  else if (sa.MB <= 1024) launch_select_attend_e<KV_DT, Q_DT, 4>(a, sa, grid, nt, st);
+  else launch_select_attend_e<KV_DT, Q_DT, 8>(a, sa, grid, nt, st);
 }
 
 }  // namespace isb
@@ -839,11 +838,13 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
                                     const void* k_pool, const void* v_pool, int kv_dtype,
                                     int64_t num_pages, float k_scale, float v_scale,
                                     const int32_t* sparse_bt, int sparse_bt_stride,
-                                    const int32_t* sparse_ctx, int num_tokens, int num_q_heads,
-                                    int num_kv_heads, int head_dim, float sm_scale,
+                                    const int32_t* sparse_ctx, int num_tokens, int decode_query_len,
+                                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale,
                                     void* workspace, size_t workspace_bytes, void* out) {
   using namespace isb;
   if (!sparse_bt || !sparse_ctx) return ISB_E_INVALID_ARG;
+  if (decode_query_len <= 0) return ISB_E_INVALID_ARG;
+  if (num_tokens > 0 && num_tokens % decode_query_len != 0) return ISB_E_SHAPE;
   PaArgs a;
   PaPlan plan;
   const int err = pa_setup(q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale,
@@ -855,15 +856,16 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   hipStream_t st = as_hip(stream);
   const dim3 grid((unsigned)plan.rows, plan.splits);
   const bool qb = q_dtype == ISB_BF16;
+  const bool nt = decode_query_len == 1;
   if (kv_dtype == ISB_BF16) {
-    if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, st);
-    else launch_decode<ISB_BF16, ISB_FP8_E4M3>(a, grid, st);
+    if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, nt, st);
+    else launch_decode<ISB_BF16, ISB_FP8_E4M3>(a, grid, nt, st);
   } else if (kv_dtype == ISB_FP8_E4M3) {
-    if (qb) launch_decode<ISB_FP8_E4M3, ISB_BF16>(a, grid, st);
-    else launch_decode<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, grid, st);
+    if (qb) launch_decode<ISB_FP8_E4M3, ISB_BF16>(a, grid, nt, st);
+    else launch_decode<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, grid, nt, st);
   } else {
-    if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, st);
-    else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, st);
+    if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, nt, st);
+    else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, nt, st);
   }
   return launch_status();
 }
@@ -904,22 +906,23 @@ extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const
                                  sparse_bt, sparse_ctx);
     if (e) return e;
     return isb_sparse_pa_decode(stream, q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale,
-                                sparse_bt, top_k * ppb, sparse_ctx, (int)T, num_q_heads, num_kv_heads,
-                                kHeadDim, sm_scale, workspace, workspace_bytes, out);
+                                sparse_bt, top_k * ppb, sparse_ctx, (int)T, decode_query_len, num_q_heads,
+                                num_kv_heads, kHeadDim, sm_scale, workspace, workspace_bytes, out);
   }
   SelArgs sa{scores, seq_lens, block_table, topk_idx, sparse_bt, sparse_ctx, decode_query_len, (int)T,
              max_blocks, top_k, block_table_stride};
   const dim3 grid((unsigned)plan.rows, plan.splits);
   const bool qb = q_dtype == ISB_BF16;
+  const bool nt = decode_query_len == 1;
   if (kv_dtype == ISB_BF16) {
-    if (qb) launch_select_attend<ISB_BF16, ISB_BF16>(a, sa, grid, st);
-    else launch_select_attend<ISB_BF16, ISB_FP8_E4M3>(a, sa, grid, st);
+    if (qb) launch_select_attend<ISB_BF16, ISB_BF16>(a, sa, grid, nt, st);
+    else launch_select_attend<ISB_BF16, ISB_FP8_E4M3>(a, sa, grid, nt, st);
   } else if (kv_dtype == ISB_FP8_E4M3) {
-    if (qb) launch_select_attend<ISB_FP8_E4M3, ISB_BF16>(a, sa, grid, st);
-    else launch_select_attend<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, sa, grid, st);
+    if (qb) launch_select_attend<ISB_FP8_E4M3, ISB_BF16>(a, sa, grid, nt, st);
+    else launch_select_attend<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, sa, grid, nt, st);
   } else {
-    if (qb) launch_select_attend<ISB_MXFP4, ISB_BF16>(a, sa, grid, st);
-    else launch_select_attend<ISB_MXFP4, ISB_FP8_E4M3>(a, sa, grid, st);
+    if (qb) launch_select_attend<ISB_MXFP4, ISB_BF16>(a, sa, grid, nt, st);
+    else launch_select_attend<ISB_MXFP4, ISB_FP8_E4M3>(a, sa, grid, nt, st);
   }
   return launch_status();
 }

@@ -241,7 +241,8 @@ def test_select_attend_matches_the_two_calls(case):
     topk, sbt, sctx = isb.topk_select_emit(scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table,
                                            cfg.pages_per_block)
     out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
-                               sbt, sctx, cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+                               sbt, sctx, cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale,
+                               decode_query_len=cfg.query_len)
     T, H_kv = cfg.num_tokens, cfg.num_kv_heads
     f_topk = torch.full_like(topk, 777)
     f_sbt = torch.full_like(sbt, -5)
@@ -276,7 +277,8 @@ def test_sparse_pa_parity(name):
     ref = oracle_attention(hi, sbt, sctx)
     out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
                                torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
-                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale,
+                               decode_query_len=cfg.query_len)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     assert np.isfinite(got).all(), "NaN in attention output (poison read?)"
@@ -317,7 +319,8 @@ def test_sparse_pa_one_split_several_rounds(base):
     ref = oracle_attention(hi, sbt, sctx)
     out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
                                torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
-                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale,
+                               decode_query_len=cfg.query_len)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     assert np.isfinite(got).all()
@@ -339,7 +342,8 @@ def test_sparse_pa_variants(variant):
     ref = oracle_attention(hi, sbt, sctx)
     out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
                                torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
-                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale,
+                               decode_query_len=cfg.query_len)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     assert np.isfinite(got).all(), "NaN in attention output (poison read?)"
@@ -362,7 +366,8 @@ def test_sparse_pa_row_counts(reqs):
     ref = oracle_attention(hi, sbt, sctx)
     out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
                                torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
-                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale)
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale,
+                               decode_query_len=cfg.query_len)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     assert np.isfinite(got).all(), "NaN in attention output (poison read?)"
@@ -382,7 +387,8 @@ def test_sparse_pa_every_block_is_dense_attention():
     assert list(sctx) == list(hi["seq_lens"])
     ref = oracle_attention(hi, sbt, sctx)
     out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
-                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(), 16, 1, w.sm_scale)
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(), 16, 1, w.sm_scale,
+                               decode_query_len=cfg.query_len)
     torch.cuda.synchronize()
     tol = attn_tol("fp8", attended_vmax(hi, sbt, sctx))
     assert np.abs(out.float().cpu().numpy() - ref).max() <= tol

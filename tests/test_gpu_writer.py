@@ -259,7 +259,7 @@ def test_reusing_layer_writes_kv_only_and_attends_with_the_source_selection():
                     cfg.kv_dtype, w.k_scale, w.v_scale)
     qB = torch.from_numpy(rng.standard_normal((T, cfg.num_q_heads, 128)).astype(np.float32)).to(torch.bfloat16)
     out = isb.sparse_pa_decode(qB.cuda(), "bf16", k_pool, v_pool, cfg.kv_dtype, w.k_scale, w.v_scale, sbt, sctx,
-                               cfg.num_q_heads, H, w.sm_scale)
+                               cfg.num_q_heads, H, w.sm_scale, decode_query_len=q)
     torch.cuda.synchronize()
     hB = dict(hi, q=_host(qB), k_pool=hi["k_pool"].copy(), v_pool=hi["v_pool"].copy())
     writer.write_cache(_host(news[0]), _host(news[1]), None, hi["block_table"], hi["seq_lens"], q, hB["k_pool"],

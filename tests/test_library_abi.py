@@ -40,6 +40,33 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(_declared()) == set(binding.EXPORTED)
 
 
+def test_measurement_library_exports_its_header(lib):
+    # libisb_ceiling: the benchmark's page-read ceilings, declared in
+    # include/isb_ceiling.h, built beside libisb; argument checks on the CPU
+    from indexer_selected_block_amd.build import CEILING_LIB_PATH, build_ceiling_library
+    if not os.path.exists(CEILING_LIB_PATH):
+        build_ceiling_library()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "isb_ceiling.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(isb_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["isb_ceiling_attention_gather", "isb_ceiling_attention_words", "isb_ceiling_index_gather"]
+    ceil = ctypes.CDLL(CEILING_LIB_PATH)
+    for n in names:
+        assert hasattr(ceil, n)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    ceil.isb_ceiling_index_gather.argtypes = [P, P, I, I64, P, I, P, I, I, I, I, P]
+    ceil.isb_ceiling_attention_gather.argtypes = [P, P, P, I, I64, P, I, P, I, I, I, P, ctypes.c_size_t]
+    ceil.isb_ceiling_attention_words.argtypes = [I, I, I, I]
+    ceil.isb_ceiling_attention_words.restype = ctypes.c_size_t
+    assert ceil.isb_ceiling_attention_words(128, 1, 128, 1) == 128 * 4 * 4     # 4 splits, 4 waves
+    assert ceil.isb_ceiling_attention_words(0, 1, 128, 1) == 0
+    p = ctypes.c_void_p(16)
+    assert ceil.isb_ceiling_index_gather(None, None, 1, 8, p, 4, p, 1, 1, 1, 4, p) == -1
+    assert ceil.isb_ceiling_index_gather(None, p, 5, 8, p, 4, p, 1, 1, 1, 4, p) == -2
+    assert ceil.isb_ceiling_index_gather(None, p, 1, 8, p, 4, p, 1, 17, 1, 4, p) == -3     # prefill chunk
+    assert ceil.isb_ceiling_attention_gather(None, p, p, 1, 8, p, 128, p, 3, 2, 1, p, 1 << 20) == -3
+    assert ceil.isb_ceiling_attention_gather(None, p, p, 1, 8, p, 128, p, 128, 1, 1, p, 100) == -4
+
+
 def test_version_and_strerror(lib):
     assert lib.isb_version() >= 100
     for s in (0, -1, -2, -3, -4, -5):
@@ -58,13 +85,13 @@ def test_argument_checks_return_before_any_launch(lib):
     assert lib.isb_topk_select_emit(NULL, NULL, NULL, 1, 1, 1, 4, 2, NULL, 4, 8, NULL, NULL, NULL) == -1
     assert lib.isb_select_attend(NULL, NULL, NULL, 1, 1, 1, 4, 2, NULL, 4, NULL, 0, NULL, NULL, 1, 8, 1.0, 1.0,
                                  16, 0.1, NULL, 0, NULL, NULL, NULL, NULL) == -1
-    assert lib.isb_sparse_pa_decode(NULL, NULL, 0, NULL, NULL, 1, 1, 1.0, 1.0, NULL, 1, NULL, 1, 16, 1,
+    assert lib.isb_sparse_pa_decode(NULL, NULL, 0, NULL, NULL, 1, 1, 1.0, 1.0, NULL, 1, NULL, 1, 1, 16, 1,
                                     128, 0.1, NULL, 0, NULL) == -1
     p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
     # dtypes
     assert lib.isb_index_score(NULL, p, 7, 1, p, 0, 1.0, 1, p, 1, p, 1, 1, 1, 1, p) == -2
     assert lib.isb_index_score(NULL, p, 2, 1, p, 0, 1.0, 1, p, 1, p, 1, 1, 1, 1, p) == -2   # MXFP4 query
-    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 9, 1, 1.0, 1.0, p, 1, p, 1, 16, 1, 128, 0.1,
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 9, 1, 1.0, 1.0, p, 1, p, 1, 1, 16, 1, 128, 0.1,
                                     p, 1 << 20, p) == -2
     # shapes
     assert lib.isb_index_score(NULL, p, 0, 3, p, 0, 1.0, 1, p, 4, p, 1, 1, 2, 4, p) == -3       # 3 % 2
@@ -87,9 +114,9 @@ def test_argument_checks_return_before_any_launch(lib):
                                  32, 0.1, p, 1 << 20, p, p, p, p) == -3                          # G = 32
     assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 4, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,
                                  16, 0.1, p, 16, p, p, p, p) == -4                               # workspace
-    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 16, 1, 64, 0.1,
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 1, 16, 1, 64, 0.1,
                                     p, 1 << 20, p) == -3                                         # head_dim
-    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 32, 1, 128, 0.1,
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 1, 32, 1, 128, 0.1,
                                     p, 1 << 20, p) == -3                                         # G = 32
     # the cache writer and the query cast
     w = lambda k=p, idx=p, ipool=p, H=1, kvdt=1, ks=1.0, idt=1, xs=1.0, q=1, ktf=None: lib.isb_write_cache(  # noqa
@@ -124,7 +151,7 @@ def test_argument_checks_return_before_any_launch(lib):
     # workspace
     need = lib.isb_sparse_pa_workspace_bytes(4, 16, 1, 128, 1)
     assert need > 0
-    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 4, 16, 1, 128, 0.1,
+    assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 4, 1, 16, 1, 128, 0.1,
                                     p, need - 1, p) == -4
 
 
