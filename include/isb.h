@@ -242,9 +242,9 @@ ISB_API int isb_topk_merge(isb_stream_t stream, const float* cand_scores,
                            int max_blocks, int top_k, int32_t* topk_idx);
 
 /*
- * Bytes of workspace isb_sparse_pa_decode needs for these arguments: one
- * arrival counter per row (the first 4 * rows bytes, padded to 256) and the
- * split-K partial results.  Returns 0 for invalid arguments.
+ * Bytes of workspace isb_sparse_pa_decode needs for these arguments: the
+ * split-K partial results of every (row, split), 16 heads x (128 + 2) fp32
+ * each.  Returns 0 for invalid arguments.
  */
 ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv_heads,
                                      int sparse_bt_stride, int kv_dtype);
@@ -255,9 +255,11 @@ ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, in
  * For row (t, g) and query head h of KV group g (vLLM API page, the decode
  * call): z_u = sm_scale * dot(q[t][h], K_u) over sparse positions
  * u < sparse_ctx[row]; out[t][h] = sum_u softmax(z)_u V_u, in fp32, written as
- * bf16.  A row's pages are split across workgroups; the workgroup that
- * finishes a row last merges its partial results (log-sum-exp weights, in
- * split order, so results do not depend on timing).  One launch.  Position u is slot u mod P of page sparse_bt[row][u div P], with
+ * bf16.  A row's pages are split across workgroups; each publishes its
+ * partial result, and a workgroup that finds every other split of its row
+ * published merges the row (log-sum-exp weights, in split order, so results
+ * do not depend on timing).  One launch.  Position u is slot u mod P of page
+ * sparse_bt[row][u div P], with
  * P = 16 tokens per page (bf16 / fp8 K/V) or 128 (MXFP4 K/V).  fp8 K/V are
  * multiplied by k_scale / v_scale.  Rows with sparse_ctx = 0 output zeros.
  *
@@ -271,11 +273,11 @@ ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, in
  *   sparse_bt   [num_tokens * num_kv_heads][sparse_bt_stride] int32 page ids
  *   sparse_ctx  [num_tokens * num_kv_heads] int32, <= sparse_bt_stride * P
  *   workspace   >= isb_sparse_pa_workspace_bytes(...) bytes, 16-byte aligned,
- *               zero-filled before its first use (e.g. one hipMemsetAsync).
- *               The arrival counters at its start must be zero when a call
- *               begins, and every completed call leaves them zero; the rest
- *               of it may hold anything.  Calls that share a workspace must
- *               not overlap in time.
+ *               filled with 0xFF bytes before its first use (one fill of the
+ *               buffer): a slot of split partials is free when all its words
+ *               are 0xFFFFFFFF, a value no published word takes.  Every
+ *               completed call leaves the workspace so; calls that share a
+ *               workspace must not overlap in time.
  *   out         out, [num_tokens][num_q_heads][128] bf16
  * Shape errors: head_dim != 128, num_q_heads % num_kv_heads, G > 16,
  * num_tokens % decode_query_len.

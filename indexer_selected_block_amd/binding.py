@@ -339,6 +339,12 @@ def sparse_pa_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, sparse_bt_s
         num_tokens, num_q_heads, num_kv_heads, sparse_bt_stride, _code(kv_dtype)))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """An attention workspace in its initial state: every byte 0xFF (all split
+    partial slots free).  Every completed call leaves it so."""
+    return torch.full((max(int(nbytes), 16),), 0xFF, dtype=torch.uint8, device=device)
+
+
 def _check_out(out, T, num_q_heads):
     if out.dtype != torch.bfloat16:
         raise ValueError("out must be bfloat16")
@@ -360,8 +366,8 @@ def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, spa
     dev = _dev(q, k_pool, v_pool, sparse_bt, sparse_ctx)
     stride = sparse_bt.shape[1]
     need = sparse_pa_workspace_bytes(T, num_q_heads, num_kv_heads, stride, kv_dtype)
-    if workspace is None:  # zero-filled: the arrival counters start at zero
-        workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = new_workspace(need, dev)
     if out is None:
         out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
     _dev(out, workspace)
@@ -393,8 +399,8 @@ def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_d
     if out is None:
         out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
     need = sparse_pa_workspace_bytes(T, num_q_heads, H_kv, top_k * ppb, kv_dtype)
-    if workspace is None:  # zero-filled: the arrival counters start at zero
-        workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = new_workspace(need, dev)
     _dev(topk_idx, sparse_bt, sparse_ctx, out, workspace)
     _check_int32(topk_idx=topk_idx, sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
     _check_shape("topk_idx", topk_idx, (H_kv, T, top_k))
@@ -515,7 +521,7 @@ class DecodeLayer:
         self.sparse_ctx = torch.empty((T * cfg.num_kv_heads,), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, cfg.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
         need = sparse_pa_workspace_bytes(T, cfg.num_q_heads, cfg.num_kv_heads, cfg.top_k * ppb, cfg.kv_dtype)
-        self.workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
+        self.workspace = new_workspace(need, dev)
 
     def run(self):
         w, cfg = self.w, self.w.cfg

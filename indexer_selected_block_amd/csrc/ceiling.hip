@@ -109,13 +109,13 @@ struct AttArgs {
   int sbt_stride, H_kv, pps;
 };
 
-// 16-token pages: grid (rows, splits), four waves; a round is four runs of
-// RUN pages, one a wave, every K page of the run then every V page issued at
-// once (the attention kernel's order); page ids fetched for 64 / RUN rounds
-// at a time as the attention kernel does.
-template <int PB, int RUN, bool NT>
-__global__ __launch_bounds__(256) void attention_gather16_kernel(AttArgs a) {
-  constexpr int ROUND = 4 * RUN, IDS = 64 / RUN;
+// 16-token pages: grid (rows, splits), NW waves; a round is NW runs of RUN
+// pages, one a wave, every K page of the run then every V page issued at once
+// (the attention kernel's order); page ids fetched for 64 / RUN rounds at a
+// time as the attention kernel does.
+template <int PB, int RUN, bool NT, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_gather16_kernel(AttArgs a) {
+  constexpr int ROUND = NW * RUN, IDS = 64 / RUN;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int kvh = row % a.H_kv;
@@ -158,7 +158,13 @@ __global__ __launch_bounds__(256) void attention_gather16_kernel(AttArgs a) {
       if (j < cnt) acc ^= fold_page<PB>(k[j]) ^ fold_page<PB>(v[j]);
   }
   acc ^= __shfl_xor(acc, 1);
-  if (lane == 0) a.out[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave] = acc;
+  if (lane == 0) a.out[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * NW + wave] = acc;
+}
+
+template <int PB, int RUN, bool NT>
+void launch_gather16(const AttArgs& a, dim3 grid, int nw, hipStream_t st) {
+  if (nw == 8) hipLaunchKernelGGL((attention_gather16_kernel<PB, RUN, NT, 8>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((attention_gather16_kernel<PB, RUN, NT, 4>), grid, dim3(256), 0, st, a);
 }
 
 // MXFP4 pages: one 8704 B page of K and one of V a wave, page p0 + wave of
@@ -219,7 +225,7 @@ extern "C" size_t isb_ceiling_attention_words(int num_tokens, int num_kv_heads, 
   using namespace isb;
   if (num_tokens <= 0 || num_kv_heads <= 0 || sparse_bt_stride <= 0 || !is_pool_dtype(kv_dtype)) return 0;
   const PaPlan p = pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype);
-  return (size_t)p.rows * p.splits * 4;
+  return (size_t)p.rows * p.splits * p.waves;
 }
 
 extern "C" int isb_ceiling_attention_gather(isb_stream_t stream, const void* k_pool, const void* v_pool,
@@ -235,7 +241,7 @@ extern "C" int isb_ceiling_attention_gather(isb_stream_t stream, const void* k_p
   if (num_tokens % decode_query_len != 0 || (long long)num_tokens * num_kv_heads > 0x7FFFFFFFLL) return ISB_E_SHAPE;
   const PaPlan p = pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype);
   if (p.splits > 65535) return ISB_E_SHAPE;
-  if (out_words < (size_t)p.rows * p.splits * 4) return ISB_E_WORKSPACE;
+  if (out_words < (size_t)p.rows * p.splits * p.waves) return ISB_E_WORKSPACE;
   AttArgs a{(const uint8_t*)k_pool, (const uint8_t*)v_pool, sparse_bt, sparse_ctx, out, num_pages, sparse_bt_stride,
             num_kv_heads, p.pages_per_split};
   hipStream_t st = as_hip(stream);
@@ -244,11 +250,11 @@ extern "C" int isb_ceiling_attention_gather(isb_stream_t stream, const void* k_p
   if (kv_dtype == ISB_MXFP4) {
     hipLaunchKernelGGL(attention_gather_mx_kernel, grid, dim3(256), 0, st, a);
   } else if (kv_dtype == ISB_FP8_E4M3) {
-    if (nt) hipLaunchKernelGGL((attention_gather16_kernel<2048, 8, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attention_gather16_kernel<2048, 8, false>), grid, dim3(256), 0, st, a);
+    if (nt) launch_gather16<2048, 8, true>(a, grid, p.waves, st);
+    else launch_gather16<2048, 8, false>(a, grid, p.waves, st);
   } else {
-    if (nt) hipLaunchKernelGGL((attention_gather16_kernel<4096, 4, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attention_gather16_kernel<4096, 4, false>), grid, dim3(256), 0, st, a);
+    if (nt) launch_gather16<4096, 4, true>(a, grid, p.waves, st);
+    else launch_gather16<4096, 4, false>(a, grid, p.waves, st);
   }
   return launch_status();
 }

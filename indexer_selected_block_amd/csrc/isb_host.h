@@ -27,20 +27,25 @@ inline int64_t idx_page_bytes(int dt) {
 // Split-K plan of isb_sparse_pa_decode; shared by the workspace query so the
 // two always agree.  A wave attends a run of `pages_per_wave` consecutive
 // pages whose loads it issues at once: 8 fp8 / 4 bf16 16-token pages (32 KiB
-// of K and V), or one 128-token MXFP4 page; a workgroup (four waves) covers
-// four runs a round.  Rows are cut into just enough splits to give the chip
-// about kPaResidentWorkgroups workgroups (two per CU of an MI355X); a split
-// longer than one round is walked round by round.  Batches that fill the chip
-// by themselves thus take one split per row, with nothing to merge between
-// workgroups, and small batches spread a row over several workgroups that
-// each read everything they attend in one round.
-constexpr int kPaResidentWorkgroups = 512;
+// of K and V), or one 128-token MXFP4 page; a workgroup of `waves` waves
+// covers one run a wave a round.  The chip holds kPaResidentWaves such waves
+// at once (two a SIMD).  When every run of the batch fits in that at once and
+// eight-wave workgroups still give every CU one, a workgroup of fp8 pages has
+// eight waves (a row needs half as many splits, so half as many partials are
+// merged); otherwise four.  Rows are cut into just enough splits to fill the chip; a
+// split longer than one round is walked round by round.  Batches that fill
+// the chip by themselves thus take one split a row, with nothing to merge
+// between workgroups, and small batches spread a row over several
+// workgroups that each read everything they attend in one round.
+constexpr int kPaResidentWaves = 2048;  // 256 CUs x 4 SIMDs x 2 waves
+constexpr int kPaCUs = 256;
 
 struct PaPlan {
   int rows;             // num_tokens * num_kv_heads
   int max_pages;        // sparse_bt_stride
   int pages_per_wave;   // run of one wave
-  int pages_per_round;  // 4 runs: what a workgroup reads at once
+  int waves;            // waves a workgroup: 4 or 8
+  int pages_per_round;  // one run a wave: what a workgroup reads at once
   int pages_per_split;  // a whole number of rounds
   int splits;           // workgroups per row
 };
@@ -50,9 +55,15 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   p.rows = num_tokens * num_kv_heads;
   p.max_pages = sparse_bt_stride;
   p.pages_per_wave = kv_dtype == ISB_MXFP4 ? 1 : kv_dtype == ISB_BF16 ? 4 : 8;
-  p.pages_per_round = 4 * p.pages_per_wave;
+  p.waves = 4;
+  const long long runs = (p.max_pages + p.pages_per_wave - 1) / p.pages_per_wave;  // of a whole row
+  if (kv_dtype == ISB_FP8_E4M3 && (long long)p.rows * runs <= kPaResidentWaves &&
+      (long long)p.rows * ((runs + 7) / 8) >= kPaCUs)
+    p.waves = 8;
+  p.pages_per_round = p.waves * p.pages_per_wave;
   const int rounds = (p.max_pages + p.pages_per_round - 1) / p.pages_per_round;  // of a whole row
-  int want = (kPaResidentWorkgroups + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
+  const int resident = kPaResidentWaves / p.waves;  // workgroups the chip holds at once
+  int want = (resident + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
   if (kv_dtype == ISB_MXFP4) want = rounds;  // MXFP4 rows are short: one round a split
   if (want > rounds) want = rounds;
   if (want < 1) want = 1;
@@ -63,15 +74,15 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   return p;
 }
 
-// Workspace: one arrival counter per row (padded to 256 B), then the partial
-// results per (row, split): 16 heads x 128 dims fp32, then 16 x (m, l).
+// Workspace: the partial results per (row, split): 16 heads x 128 dims fp32,
+// then 16 x (m, l).  A slot is free when every word of it is 0xFFFFFFFF; the
+// workspace starts that way (filled with 0xFF bytes), and every completed
+// call leaves it that way.
 constexpr size_t kPartialO = 16 * 128;
 constexpr size_t kPartialML = 16 * 2;
 
-inline size_t pa_arrival_bytes(const PaPlan& p) { return ((size_t)p.rows * 4 + 255) / 256 * 256; }
-
 inline size_t pa_workspace_bytes(const PaPlan& p) {
-  return pa_arrival_bytes(p) + (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float);
+  return (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float);
 }
 
 // The standalone emit launch (emit.hip); the fused top-k entry point falls

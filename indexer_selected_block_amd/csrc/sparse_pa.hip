@@ -72,7 +72,6 @@ struct PaArgs {
   const int32_t* sctx;
   float* part_o;
   float* part_ml;
-  uint32_t* arrivals;  // per row: splits that have published (zero between calls)
   __bf16* out;
   int64_t num_pages;
   float qk_scale;  // sm_scale * k_scale * log2(e)
@@ -80,7 +79,6 @@ struct PaArgs {
   int sbt_stride, H_q, H_kv, G, splits, pps;
 };
 
-constexpr int kPaWaves = 4;
 constexpr int kMergeGroup = 8;  // splits whose partials the merging workgroup loads at once
 
 template <int Q_DT>
@@ -97,69 +95,86 @@ __device__ __forceinline__ bool page_ok(int64_t id, int64_t n) { return id >= 0 
 
 // Per-workgroup LDS of the merge: each wave's per-head max and sum, and its
 // unnormalised output O[head][dim].
+template <int NW>
 struct alignas(16) WaveParts {
-  float m[kPaWaves][16];
-  float l[kPaWaves][16];
-  float o[kPaWaves][16][kHeadDim + 4];
+  float m[NW][16];
+  float l[NW][16];
+  float o[NW][16][kHeadDim + 4];
 };
 
+// Split partials in the workspace.  A free slot holds kFreeSlot in every
+// word; a published word never does (NaNs are published as the canonical
+// quiet NaN, and no finite value has these bits), so every word tells by
+// itself whether it has landed.
+constexpr uint32_t kFreeSlot = 0xFFFFFFFFu;
+__device__ __forceinline__ float publishable(float x) { return x != x ? qnan() : x; }
+__device__ __forceinline__ bool published(float x) { return __float_as_uint(x) != kFreeSlot; }
+__device__ __forceinline__ void store_agent(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The workgroup's share of a row, once every wave has written its part: merge
-// the waves; a row of one split is finished here, otherwise the split is
-// published and the last split to arrive merges the row (log-sum-exp weights,
-// in split order) and writes it.  Thread (h, d0) = (tid / 16, 8 (tid % 16))
-// owns dims d0 .. d0 + 7 of head h.
-__device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts& wp, int row, int split, int live,
+// the waves; a row of one split is finished here.  Otherwise the split
+// publishes its partial (agent-coherent stores, thread-interleaved: element x
+// of thread i at 256 x + i, so each store covers 256 contiguous bytes), waits
+// until its stores are complete, then reads the partials of the row's other
+// splits.  A workgroup that finds every word of them published merges the
+// row (log-sum-exp weights, in split order, so the result does not depend on
+// which workgroup merges), writes it and frees the row's slots for the next
+// call.  The split whose stores complete last always finds the others
+// published, so every row is merged; two workgroups that both find them
+// write the same bytes.  Nothing waits for another workgroup, and only
+// coherent (agent-scope) accesses touch the partials, so no cache writeback
+// or invalidation is needed between workgroups on different dies.  Thread
+// (h, d0) = (tid / 16, 8 (tid % 16)) of the first 256 owns dims d0 .. d0 + 7
+// of head h.
+template <int NW>
+__device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts<NW>& wp, int row, int split, int live,
                                              __bf16* out_row) {
-  __shared__ int s_last;
-  const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
+  const int tid = threadIdx.x;
+  const int h = (tid >> 4) & 15, d0 = 8 * (tid & 15);
+  const bool mine = tid < 256 && h < a.G;
   __syncthreads();
-  float M = neg_inf();
+  float M = neg_inf(), L = 0.f, O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (tid < 256) {
 #pragma unroll
-  for (int w = 0; w < kPaWaves; ++w) M = fmaxf(M, wp.m[w][h]);
-  float L = 0.f, O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wp.m[w][h]);
 #pragma unroll
-  for (int w = 0; w < kPaWaves; ++w) {
-    const float mw = wp.m[w][h];
-    const float wt = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    L += wp.l[w][h] * wt;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(&wp.o[w][h][d0]);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(&wp.o[w][h][d0 + 4]);
+    for (int w = 0; w < NW; ++w) {
+      const float mw = wp.m[w][h];
+      const float wt = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += wp.l[w][h] * wt;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&wp.o[w][h][d0]);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(&wp.o[w][h][d0 + 4]);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      O[x] += lo[x] * wt;
-      O[4 + x] += hi[x] * wt;
+      for (int x = 0; x < 4; ++x) {
+        O[x] += lo[x] * wt;
+        O[4 + x] += hi[x] * wt;
+      }
     }
   }
 
   if (live > 1) {
-    // Publish this split's partial with agent-coherent stores, wait until
-    // they are complete, then count the arrival.  The workgroup that arrives
-    // last merges the row and clears the count for the next call.  Only
-    // coherent (agent-scope) accesses touch the partials and the counter, so
-    // no cache writeback or invalidation is needed between workgroups on
-    // different dies.  A split's 16 x 128 outputs are stored
-    // thread-interleaved (element x of thread i at 256 x + i), so each store
-    // and load instruction covers 256 contiguous bytes.
-    const size_t base = (size_t)row * a.splits + split;
-    float* po = a.part_o + base * kPartialO + threadIdx.x;
+    const size_t rbase = (size_t)row * a.splits;
+    if (mine) {
+      float* po = a.part_o + (rbase + split) * kPartialO + tid;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) __hip_atomic_store(po + 256 * x, O[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((threadIdx.x & 15) == 0) {
-      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.part_ml + (base * 16 + h) * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int x = 0; x < 8; ++x) store_agent(po + 256 * x, publishable(O[x]));
+      if ((tid & 15) == 0) {
+        store_agent(a.part_ml + ((rbase + split) * 16 + h) * 2 + 0, publishable(M));
+        store_agent(a.part_ml + ((rbase + split) * 16 + h) * 2 + 1, publishable(L));
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
-    __syncthreads();
-    if (threadIdx.x == 0)
-      s_last = __hip_atomic_fetch_add(a.arrivals + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(live - 1);
-    __syncthreads();
-    if (!s_last) return;
-    if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (h >= a.G) return;
-    // Merge in split order, so the result does not depend on which workgroup
-    // came last: this split's values are in registers, the others are read
-    // back kMergeGroup splits at a time, every load of a group issued first.
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete
+    __syncthreads();                // ... and every thread's, before any reads back
+    // The other live splits, kMergeGroup at a time (every load of a group
+    // issued first), merged in split order as they come; whether they were
+    // all published is known only at the end, and decides whether this
+    // workgroup writes the row.
+    bool valid = true;
     const float Mo = M, Lo = L;
     float Oo[8];
 #pragma unroll
@@ -168,41 +183,60 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts& wp, int
     L = 0.f;
 #pragma unroll
     for (int x = 0; x < 8; ++x) O[x] = 0.f;
-    for (int s0 = 0; s0 < live; s0 += kMergeGroup) {
-      float ms[kMergeGroup], ls[kMergeGroup], os[kMergeGroup][8];
+    if (mine) {
+      for (int s0 = 0; s0 < live; s0 += kMergeGroup) {
+        float ms[kMergeGroup], ls[kMergeGroup], os[kMergeGroup][8];
 #pragma unroll
-      for (int k = 0; k < kMergeGroup; ++k) {
-        const int sp = s0 + k;
-        if (sp < live && sp != split) {  // a wave-uniform branch
-          const size_t b = ((size_t)row * a.splits + sp) * 16 + h;
-          ms[k] = __hip_atomic_load(a.part_ml + b * 2 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ls[k] = __hip_atomic_load(a.part_ml + b * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const float* pk = a.part_o + ((size_t)row * a.splits + sp) * kPartialO + threadIdx.x;
+        for (int k = 0; k < kMergeGroup; ++k) {
+          const int sp = s0 + k;
+          if (sp < live && sp != split) {  // a wave-uniform branch
+            const size_t b = (rbase + sp) * 16 + h;
+            ms[k] = load_agent(a.part_ml + b * 2 + 0);
+            ls[k] = load_agent(a.part_ml + b * 2 + 1);
+            const float* pk = a.part_o + (rbase + sp) * kPartialO + tid;
 #pragma unroll
-          for (int x = 0; x < 8; ++x)
-            os[k][x] = __hip_atomic_load(pk + 256 * x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int x = 0; x < 8; ++x) os[k][x] = load_agent(pk + 256 * x);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeGroup; ++k) {
+          const int sp = s0 + k;
+          if (sp >= live) break;
+          const bool own = sp == split;
+          if (!own) {
+            bool ok = published(ms[k]) && published(ls[k]);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) ok = ok && published(os[k][x]);
+            valid = valid && ok;
+          }
+          const float mk = own ? Mo : ms[k];
+          if (mk == neg_inf()) continue;
+          const float Mn = fmaxf(M, mk);
+          const float wa = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+          const float wb = __builtin_amdgcn_exp2f(mk - Mn);
+          L = L * wa + (own ? Lo : ls[k]) * wb;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : os[k][x]) * wb;
+          M = Mn;
         }
       }
+    }
+    if (!__syncthreads_and(valid)) return;  // another split is still to publish: it merges the row
+    if (mine) {  // free the row's slots for the next call
+      for (int sp = 0; sp < live; ++sp) {
+        float* po = a.part_o + (rbase + sp) * kPartialO + tid;
 #pragma unroll
-      for (int k = 0; k < kMergeGroup; ++k) {
-        const int sp = s0 + k;
-        if (sp >= live) break;
-        const bool own = sp == split;
-        const float mk = own ? Mo : ms[k];
-        if (mk == neg_inf()) continue;
-        const float Mn = fmaxf(M, mk);
-        const float wa = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float wb = __builtin_amdgcn_exp2f(mk - Mn);
-        L = L * wa + (own ? Lo : ls[k]) * wb;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : os[k][x]) * wb;
-        M = Mn;
+        for (int x = 0; x < 8; ++x) store_agent(po + 256 * x, __uint_as_float(kFreeSlot));
+        if ((tid & 15) == 0) {
+          store_agent(a.part_ml + ((rbase + sp) * 16 + h) * 2 + 0, __uint_as_float(kFreeSlot));
+          store_agent(a.part_ml + ((rbase + sp) * 16 + h) * 2 + 1, __uint_as_float(kFreeSlot));
+        }
       }
     }
   }
   // Finished row: normalise and write bf16 (nontemporal: nothing here reads
   // it back).
-  if (h < a.G) {
+  if (mine) {
     const float inv = a.v_scale / L;
     bf16x8 ob;
 #pragma unroll
@@ -215,7 +249,7 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts& wp, int
 // A row with nothing to attend outputs zeros (split 0 writes them).
 __device__ __forceinline__ void write_empty_row(const PaArgs& a, int split, __bf16* out_row) {
   const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
-  if (split == 0 && h < a.G) {
+  if (split == 0 && threadIdx.x < 256 && h < a.G) {
     bf16x8 z;
 #pragma unroll
     for (int x = 0; x < 8; ++x) z[x] = (__bf16)0.f;
@@ -224,8 +258,8 @@ __device__ __forceinline__ void write_empty_row(const PaArgs& a, int split, __bf
 }
 
 // A wave's result in LDS; row r of V^T tile dt is dim DIM_MUL r + DT_MUL dt.
-template <int DIM_MUL, int DT_MUL>
-__device__ __forceinline__ void wave_to_lds(WaveParts& wp, int wave, int lane, float m, float l,
+template <int DIM_MUL, int DT_MUL, int NW>
+__device__ __forceinline__ void wave_to_lds(WaveParts<NW>& wp, int wave, int lane, float m, float l,
                                             const f32x4 (&o)[8]) {
   const int c = lane & 15, g = lane >> 4;
   const float l_tot = sum_over_groups(l);
@@ -334,13 +368,13 @@ __device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const
 // A split is walked one round (four runs, one per wave) at a time; each
 // round's loads are issued together and its logits give one exact max per
 // head, folded into the wave's running max between rounds.
-template <int KV_DT, int Q_DT, int RUN, bool NT, typename IdFn>
-__device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, int row, int split, int kvh,
+template <int KV_DT, int Q_DT, int RUN, bool NT, int NW, typename IdFn>
+__device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts<NW>& wp, int row, int split, int kvh,
                                                int n_tok, bf16x8 (&qb)[4], int my_ids, IdFn ids,
                                                __bf16* out_row) {
   static_assert(RUN % 2 == 0, "P.V takes the pages of a run in pairs");
   constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
-  constexpr int ROUND = 4 * RUN;    // pages of a round
+  constexpr int ROUND = NW * RUN;   // pages of a round
   constexpr int IDS = 64 / RUN;     // rounds whose page ids one id fetch holds
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -400,7 +434,7 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, i
         k_operand<KV_DT>(pr[j], kb);
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16(kb[x], qb[x], sacc);
+        for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16_k<NW == 8>(kb[x], qb[x], sacc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
         const int nv = min(16, n_tok - (wb + j) * 16);
@@ -448,22 +482,22 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts& wp, i
         if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          o[dt] = mfma_16x16x32_bf16(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
+          o[dt] = mfma_16x16x32_bf16_k<NW == 8>(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
       }
     }
   }
-  wave_to_lds<1, 16>(wp, wave, lane, M, lsum, o);  // row r of tile dt: dim 16 dt + r
-  finish_split(a, wp, row, split, live, out_row);
+  wave_to_lds<1, 16, NW>(wp, wave, lane, M, lsum, o);  // row r of tile dt: dim 16 dt + r
+  finish_split<NW>(a, wp, row, split, live, out_row);
 }
 
-// RUN: pages of one wave's run (a power of two); NT: nontemporal page loads.
-// grid (rows, splits), four waves a workgroup; page ids come from the sparse
+// RUN: pages of one wave's run (a power of two); NT: nontemporal page loads;
+// NW: waves a workgroup.  grid (rows, splits); page ids come from the sparse
 // page table.
-template <int KV_DT, int Q_DT, int RUN, bool NT>
-__global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
+template <int KV_DT, int Q_DT, int RUN, bool NT, int NW>
+__global__ __launch_bounds__(64 * NW) void pa16_kernel(PaArgs a) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
-  constexpr int ROUND = 4 * RUN;
-  __shared__ WaveParts wp;
+  constexpr int ROUND = NW * RUN;
+  __shared__ WaveParts<NW> wp;
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -488,7 +522,7 @@ __global__ __launch_bounds__(256) void pa16_kernel(PaArgs a) {
     for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
   }
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  attend_split16<KV_DT, Q_DT, RUN, NT>(a, wp, row, split, kvh, n_tok, qb, my_ids, load_ids, out_row);
+  attend_split16<KV_DT, Q_DT, RUN, NT, NW>(a, wp, row, split, kvh, n_tok, qb, my_ids, load_ids, out_row);
 }
 
 // ----------------------------------------------------------------- select + attend
@@ -511,12 +545,13 @@ struct SelArgs {
 
 constexpr int kSelMaxBlocks = 2048;
 
-template <int KV_DT, int Q_DT, int RUN, bool NT, int E>
-__global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
+template <int KV_DT, int Q_DT, int RUN, bool NT, int NW, int E>
+__global__ __launch_bounds__(64 * NW) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
-  constexpr int ROUND = 4 * RUN;
-  __shared__ WaveParts wp;
-  __shared__ SelectLds<256> sl;
+  constexpr int NT_ = 64 * NW;      // threads a workgroup
+  constexpr int ROUND = NW * RUN;
+  __shared__ WaveParts<NW> wp;
+  __shared__ SelectLds<NT_> sl;
   __shared__ int32_t s_bt[kSelMaxBlocks];
   __shared__ int32_t s_sel[kSelMaxBlocks];
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
@@ -545,7 +580,7 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   for (int x = 0; x < E; ++x)
     if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
   int32_t* o = sa.topk + (size_t)trow * sa.K;
-  const int m = select_row<256, E>(sc, nt, sa.K, sl, [&](int k, int b) {
+  const int m = select_row<NT_, E>(sc, nt, sa.K, sl, [&](int k, int b) {
     s_sel[k] = b;
     if (split == 0) o[k] = b;
   });
@@ -554,7 +589,7 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   if (split == 0) {
     const int slots = sa.K * 8;
     int32_t* so = sa.sbt + (size_t)row * slots;
-    for (int x = tid; x < slots; x += 256) so[x] = (x >> 3) < m ? s_bt[s_sel[x >> 3]] * 8 + (x & 7) : -1;
+    for (int x = tid; x < slots; x += NT_) so[x] = (x >> 3) < m ? s_bt[s_sel[x >> 3]] * 8 + (x & 7) : -1;
     if (tid == 0) sa.sctx[row] = n_tok;
   }
   const int p0 = split * a.pps;
@@ -566,14 +601,14 @@ __global__ __launch_bounds__(256) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   };
   const int my_ids = ids(0);
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  attend_split16<KV_DT, Q_DT, RUN, NT>(a, wp, row, split, kvh, n_tok, qb, my_ids, ids, out_row);
+  attend_split16<KV_DT, Q_DT, RUN, NT, NW>(a, wp, row, split, kvh, n_tok, qb, my_ids, ids, out_row);
 }
 
 // ----------------------------------------------------------------- MXFP4 pages
 // One 128-token page a wave (eight 16-key tiles): page p0 + wave of the
 // row's split, whose id is id_raw (-1 past the row's pages).
 template <int Q_DT>
-__device__ __forceinline__ void attend_split_mx(const PaArgs& a, WaveParts& wp, int row, int split, int t,
+__device__ __forceinline__ void attend_split_mx(const PaArgs& a, WaveParts<4>& wp, int row, int split, int t,
                                                 int kvh, int n_tok, int32_t id_raw, __bf16* out_row) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -685,14 +720,14 @@ __device__ __forceinline__ void attend_split_mx(const PaArgs& a, WaveParts& wp, 
       }
     }
   }
-  wave_to_lds<8, 1>(wp, wave, lane, mx, lsum, o);  // row r of tile dt: dim 8 r + dt
-  finish_split(a, wp, row, split, live, out_row);
+  wave_to_lds<8, 1, 4>(wp, wave, lane, mx, lsum, o);  // row r of tile dt: dim 8 r + dt
+  finish_split<4>(a, wp, row, split, live, out_row);
 }
 
 // grid (rows, splits); page ids come from the sparse page table.
 template <int Q_DT>
 __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
-  __shared__ WaveParts wp;
+  __shared__ WaveParts<4> wp;
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int p = split * a.pps + wave_id();
@@ -709,7 +744,7 @@ __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
 // table and the sparse length.
 template <int Q_DT, int E>
 __global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
-  __shared__ WaveParts wp;
+  __shared__ WaveParts<4> wp;
   __shared__ SelectLds<256> sl;
   __shared__ int32_t s_bt[kSelMaxBlocks];
   __shared__ int32_t s_sel[kSelMaxBlocks];
@@ -746,15 +781,24 @@ __global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
   attend_split_mx<Q_DT>(a, wp, row, split, t, kvh, n_tok, id_raw, out_row);
 }
 
-// nt: one query token a request, so no page is read twice in the launch.
+// nt: one query token a request, so no page is read twice in the launch;
+// the plan gives the waves a workgroup.
 template <int KV_DT, int Q_DT>
-static void launch_decode(const PaArgs& a, dim3 grid, bool nt, hipStream_t st) {
+static void launch_decode(const PaArgs& a, dim3 grid, bool nt, const PaPlan& plan, hipStream_t st) {
+  const int nw = plan.waves;
   if constexpr (KV_DT == ISB_MXFP4) {
     hipLaunchKernelGGL((pamx_kernel<Q_DT>), grid, dim3(256), 0, st, a);
   } else {
     constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
-    if (nt) hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, false>), grid, dim3(256), 0, st, a);
+    if constexpr (KV_DT == ISB_FP8_E4M3) {  // the plan takes eight waves for fp8 pages only
+      if (nw == 8) {
+        if (nt) hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, true, 8>), grid, dim3(512), 0, st, a);
+        else hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, false, 8>), grid, dim3(512), 0, st, a);
+        return;
+      }
+    }
+    if (nt) hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, true, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, false, 4>), grid, dim3(256), 0, st, a);
   }
 }
 
@@ -797,8 +841,7 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
   a.vp = (const uint8_t*)v_pool;
   a.sbt = nullptr;
   a.sctx = nullptr;
-  a.arrivals = (uint32_t*)workspace;
-  a.part_o = (float*)((uint8_t*)workspace + pa_arrival_bytes(plan));
+  a.part_o = (float*)workspace;
   a.part_ml = a.part_o + (size_t)plan.rows * plan.splits * kPartialO;
   a.out = (__bf16*)out;
   a.num_pages = num_pages;
@@ -813,23 +856,38 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
   return ISB_OK;
 }
 
-template <int KV_DT, int Q_DT, int E>
+// E: scores a thread holds, E x (64 NW) >= max_blocks.
+template <int KV_DT, int Q_DT, int NW, int E>
 static void launch_select_attend_e(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
   if constexpr (KV_DT == ISB_MXFP4) {
     hipLaunchKernelGGL((pamxsel_kernel<Q_DT, E>), grid, dim3(256), 0, st, a, sa);
   } else {
     constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
-    if (nt) hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, true, E>), grid, dim3(256), 0, st, a, sa);
-    else hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, false, E>), grid, dim3(256), 0, st, a, sa);
+    const dim3 b(64 * NW);
+    if (nt) hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, true, NW, E>), grid, b, 0, st, a, sa);
+    else hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, false, NW, E>), grid, b, 0, st, a, sa);
   }
 }
 
+template <int KV_DT, int Q_DT, int NW>
+static void launch_select_attend_nw(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
+  constexpr int NT = 64 * NW;
+  if (sa.MB <= NT) launch_select_attend_e<KV_DT, Q_DT, NW, 1>(a, sa, grid, nt, st);
+  else if (sa.MB <= 2 * NT) launch_select_attend_e<KV_DT, Q_DT, NW, 2>(a, sa, grid, nt, st);
+  else if (sa.MB <= 4 * NT) launch_select_attend_e<KV_DT, Q_DT, NW, 4>(a, sa, grid, nt, st);
+  else launch_select_attend_e<KV_DT, Q_DT, NW, 8 * 4 / NW>(a, sa, grid, nt, st);
+}
+
 template <int KV_DT, int Q_DT>
-static void launch_select_attend(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
-  if (sa.MB <= 256) launch_select_attend_e<KV_DT, Q_DT, 1>(a, sa, grid, nt, st);
-  else if (sa.MB <= 512) launch_select_attend_e<KV_DT, Q_DT, 2>(a, sa, grid, nt, st);
-  else if (sa.MB <= 1024) launch_select_attend_e<KV_DT, Q_DT, 4>(a, sa, grid, nt, st);
-  else launch_select_attend_e<KV_DT, Q_DT, 8>(a, sa, grid, nt, st);
+static void launch_select_attend(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, const PaPlan& plan,
+                                 hipStream_t st) {
+  if constexpr (KV_DT == ISB_FP8_E4M3) {  // the plan takes eight waves for fp8 pages only
+    if (plan.waves == 8) {
+      launch_select_attend_nw<KV_DT, Q_DT, 8>(a, sa, grid, nt, st);
+      return;
+    }
+  }
+  launch_select_attend_nw<KV_DT, Q_DT, 4>(a, sa, grid, nt, st);
 }
 
 }  // namespace isb
@@ -858,14 +916,14 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   const bool qb = q_dtype == ISB_BF16;
   const bool nt = decode_query_len == 1;
   if (kv_dtype == ISB_BF16) {
-    if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, nt, st);
-    else launch_decode<ISB_BF16, ISB_FP8_E4M3>(a, grid, nt, st);
+    if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, nt, plan, st);
+    else launch_decode<ISB_BF16, ISB_FP8_E4M3>(a, grid, nt, plan, st);
   } else if (kv_dtype == ISB_FP8_E4M3) {
-    if (qb) launch_decode<ISB_FP8_E4M3, ISB_BF16>(a, grid, nt, st);
-    else launch_decode<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, grid, nt, st);
+    if (qb) launch_decode<ISB_FP8_E4M3, ISB_BF16>(a, grid, nt, plan, st);
+    else launch_decode<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, grid, nt, plan, st);
   } else {
-    if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, nt, st);
-    else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, nt, st);
+    if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, nt, plan, st);
+    else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, nt, plan, st);
   }
   return launch_status();
 }
@@ -915,14 +973,14 @@ extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const
   const bool qb = q_dtype == ISB_BF16;
   const bool nt = decode_query_len == 1;
   if (kv_dtype == ISB_BF16) {
-    if (qb) launch_select_attend<ISB_BF16, ISB_BF16>(a, sa, grid, nt, st);
-    else launch_select_attend<ISB_BF16, ISB_FP8_E4M3>(a, sa, grid, nt, st);
+    if (qb) launch_select_attend<ISB_BF16, ISB_BF16>(a, sa, grid, nt, plan, st);
+    else launch_select_attend<ISB_BF16, ISB_FP8_E4M3>(a, sa, grid, nt, plan, st);
   } else if (kv_dtype == ISB_FP8_E4M3) {
-    if (qb) launch_select_attend<ISB_FP8_E4M3, ISB_BF16>(a, sa, grid, nt, st);
-    else launch_select_attend<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, sa, grid, nt, st);
+    if (qb) launch_select_attend<ISB_FP8_E4M3, ISB_BF16>(a, sa, grid, nt, plan, st);
+    else launch_select_attend<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, sa, grid, nt, plan, st);
   } else {
-    if (qb) launch_select_attend<ISB_MXFP4, ISB_BF16>(a, sa, grid, nt, st);
-    else launch_select_attend<ISB_MXFP4, ISB_FP8_E4M3>(a, sa, grid, nt, st);
+    if (qb) launch_select_attend<ISB_MXFP4, ISB_BF16>(a, sa, grid, nt, plan, st);
+    else launch_select_attend<ISB_MXFP4, ISB_FP8_E4M3>(a, sa, grid, nt, plan, st);
   }
   return launch_status();
 }

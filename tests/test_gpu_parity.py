@@ -225,6 +225,8 @@ _SEL_CASES = {
     "mxfp4_two_kv_heads": ("mxfp4", dict(num_kv_heads=2, num_q_heads=16)),
     "mxfp4_bf16_query": ("mxfp4", dict(q_dtype="bf16")),
     "prefill_mxfp4": ("prefill_mxfp4", {}),              # 37 tokens a request, 74 rows
+    # 128 one-token rows of 16 blocks: two splits of eight-wave workgroups
+    "fp8_decode_eight_waves": ("fp8_decode", dict(num_reqs=128, ctx_lo=1500, ctx_hi=4000, pool_blocks=128 * 32 + 64)),
 }
 
 
@@ -354,12 +356,15 @@ def test_sparse_pa_variants(variant):
 
 # Any row count: the split plan gives small batches many splits a row (every
 # page in flight at once) and large ones a single split; the counts cross the
-# plan's steps (512 resident workgroups) and leave ragged final rounds.
-@pytest.mark.parametrize("reqs", [1, 2, 5, 33, 129, 257, 511, 700])
-def test_sparse_pa_row_counts(reqs):
+# plan's steps (512 resident four-wave workgroups) and leave ragged final
+# rounds.  (128, 16) and (150, 12) take two splits of eight-wave workgroups,
+# (256, 8) one split of eight waves.
+@pytest.mark.parametrize("reqs,top_k", [(1, 8), (2, 8), (5, 8), (33, 8), (129, 8), (257, 8), (511, 8), (700, 8),
+                                        (128, 16), (150, 12), (256, 8)])
+def test_sparse_pa_row_counts(reqs, top_k):
     cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=reqs, ctx_lo=200, ctx_hi=5000,
-                    pool_blocks=reqs * 40 + 64, top_k=8)
-    _say(f"[sparse_pa rows] {reqs} rows")
+                    pool_blocks=reqs * 40 + 64, top_k=top_k)
+    _say(f"[sparse_pa rows] {reqs} rows, top-k {top_k}")
     w = wl.make_workload(cfg, device="cuda")
     hi = host_inputs(w)
     sbt, sctx = _synthetic_table(hi, 31 + reqs)
@@ -394,29 +399,23 @@ def test_sparse_pa_every_block_is_dense_attention():
     assert np.abs(out.float().cpu().numpy() - ref).max() <= tol
 
 
-def _arrival_bytes(rows):
-    return (4 * rows + 255) // 256 * 256
-
-
 def test_sparse_pa_repeat_calls_and_output_contents():
-    # Neither the output's prior contents nor those of the workspace past its
-    # arrival counters matter: three calls with differently filled buffers give
-    # bit-identical results, and each call leaves the counters zero.
+    # The output's prior contents do not matter: three calls with differently
+    # filled outputs give bit-identical results, and each call leaves the
+    # workspace as it found it (every byte 0xFF: every split slot free).
     for name in ("long_context", "fp8_decode", "mxfp4"):
         w, layer, hi = _run_small(name)
         cfg = w.cfg
         outs = []
-        for fill, wfill in ((float("nan"), 0xFF), (0.0, 0), (float("inf"), 0x7F)):
-            ws = torch.full_like(layer.workspace, wfill)
-            ws[:_arrival_bytes(cfg.num_tokens * cfg.num_kv_heads)] = 0
+        ws = isb.binding.new_workspace(layer.workspace.numel(), "cuda")
+        for fill in (float("nan"), 0.0, float("inf")):
             out = torch.full((cfg.num_tokens, cfg.num_q_heads, 128), fill, dtype=torch.bfloat16, device="cuda")
             isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
                                  layer.sparse_bt, layer.sparse_ctx, cfg.num_q_heads, cfg.num_kv_heads,
-                                 w.sm_scale, out=out, workspace=ws)
+                                 w.sm_scale, out=out, workspace=ws, decode_query_len=cfg.query_len)
             outs.append(out)
             torch.cuda.synchronize()
-            assert not ws[:_arrival_bytes(cfg.num_tokens * cfg.num_kv_heads)].any()
-        torch.cuda.synchronize()
+            assert bool((ws == 0xFF).all()), "a split slot was left occupied"
         for o in outs[1:]:
             assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
         assert torch.equal(outs[0].view(torch.int16), layer.out.view(torch.int16))
@@ -438,8 +437,8 @@ def test_layer_chain(name):
 def test_layer_replays_from_a_hip_graph(name):
     # The calls allocate nothing and never synchronise, so a layer step can be
     # captured; every replay (with eager work and syncs in between) must give
-    # the eager step's outputs bit for bit, and leave the workspace counters
-    # zero for the next call.
+    # the eager step's outputs bit for bit, and leave every workspace slot
+    # free for the next call.
     _say(f"[graph] {name}")
     w = wl.make_workload(SMALL[name], device="cuda")
     layer = isb.DecodeLayer(w)
@@ -467,7 +466,7 @@ def test_layer_replays_from_a_hip_graph(name):
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
                                b.view(torch.uint8) if b.dtype != torch.int32 else b), f"replay {rep}"
-        assert not layer.workspace[:(4 * rows + 255) // 256 * 256].any()
+        assert bool((layer.workspace == 0xFF).all()), f"replay {rep}: a split slot was left occupied"
 
 
 # ------------------------------------------------------------------ full size, sampled

@@ -57,7 +57,7 @@ def test_measurement_library_exports_its_header(lib):
     ceil.isb_ceiling_attention_gather.argtypes = [P, P, P, I, I64, P, I, P, I, I, I, P, ctypes.c_size_t]
     ceil.isb_ceiling_attention_words.argtypes = [I, I, I, I]
     ceil.isb_ceiling_attention_words.restype = ctypes.c_size_t
-    assert ceil.isb_ceiling_attention_words(128, 1, 128, 1) == 128 * 4 * 4     # 4 splits, 4 waves
+    assert ceil.isb_ceiling_attention_words(128, 1, 128, 1) == 128 * 2 * 8     # 2 splits of 8 waves
     assert ceil.isb_ceiling_attention_words(0, 1, 128, 1) == 0
     p = ctypes.c_void_p(16)
     assert ceil.isb_ceiling_index_gather(None, None, 1, 8, p, 4, p, 1, 1, 1, 4, p) == -1
@@ -156,14 +156,12 @@ def test_argument_checks_return_before_any_launch(lib):
 
 
 def test_workspace_query(lib):
-    # one u32 arrival counter per row (padded to 256 B), then the split-K
-    # partials: rows x splits x 16 heads x (128 + 2) floats
-    for T, stride, dt in [(128, 128, 1), (4300, 128, 1), (64, 16, 2), (16, 256, 1), (4, 32, 0)]:
+    # the split-K partials: rows x splits x 16 heads x (128 + 2) floats; the
+    # plan's split counts for the five workloads' shapes
+    for T, stride, dt, splits in [(128, 128, 1, 2), (4300, 128, 1, 1), (64, 16, 2, 4), (16, 256, 1, 8),
+                                  (4, 32, 0, 2)]:
         n = lib.isb_sparse_pa_workspace_bytes(T, 16, 1, stride, dt)
-        n -= (4 * T + 255) // 256 * 256
-        assert n > 0 and n % (16 * 130 * 4) == 0
-        splits = n // (16 * 130 * 4) // T
-        assert 1 <= splits <= stride
+        assert n == T * splits * 16 * 130 * 4, (T, stride, dt)
     assert lib.isb_sparse_pa_workspace_bytes(0, 16, 1, 128, 1) == 0
     assert lib.isb_sparse_pa_workspace_bytes(4, 16, 1, 128, 5) == 0
 
