@@ -244,7 +244,8 @@ ISB_API int isb_topk_merge(isb_stream_t stream, const float* cand_scores,
 /*
  * Bytes of workspace isb_sparse_pa_decode needs for these arguments: the
  * split-K partial results of every (row, split), 16 heads x (128 + 2) fp32
- * each.  Returns 0 for invalid arguments.
+ * each.  0 when every row takes one split (nothing is published), or for
+ * invalid arguments.
  */
 ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, int num_kv_heads,
                                      int sparse_bt_stride, int kv_dtype);
@@ -273,11 +274,11 @@ ISB_API size_t isb_sparse_pa_workspace_bytes(int num_tokens, int num_q_heads, in
  *   sparse_bt   [num_tokens * num_kv_heads][sparse_bt_stride] int32 page ids
  *   sparse_ctx  [num_tokens * num_kv_heads] int32, <= sparse_bt_stride * P
  *   workspace   >= isb_sparse_pa_workspace_bytes(...) bytes, 16-byte aligned,
- *               filled with 0xFF bytes before its first use (one fill of the
- *               buffer): a slot of split partials is free when all its words
- *               are 0xFFFFFFFF, a value no published word takes.  Every
- *               completed call leaves the workspace so; calls that share a
- *               workspace must not overlap in time.
+ *               zero-filled before its first use (one fill of the buffer): a
+ *               slot of split partials is free when all its words are zero,
+ *               and a published word never is.  Every completed call leaves
+ *               the workspace zero; calls that share a workspace must not
+ *               overlap in time.  May be NULL when the size query gives 0.
  *   out         out, [num_tokens][num_q_heads][128] bf16
  * Shape errors: head_dim != 128, num_q_heads % num_kv_heads, G > 16,
  * num_tokens % decode_query_len.

@@ -340,9 +340,9 @@ def sparse_pa_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, sparse_bt_s
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """An attention workspace in its initial state: every byte 0xFF (all split
-    partial slots free).  Every completed call leaves it so."""
-    return torch.full((max(int(nbytes), 16),), 0xFF, dtype=torch.uint8, device=device)
+    """An attention workspace in its initial state: zero-filled (every split
+    partial slot free).  Every completed call leaves it so."""
+    return torch.zeros((max(int(nbytes), 16),), dtype=torch.uint8, device=device)
 
 
 def _check_out(out, T, num_q_heads):

@@ -75,14 +75,15 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
 }
 
 // Workspace: the partial results per (row, split): 16 heads x 128 dims fp32,
-// then 16 x (m, l).  A slot is free when every word of it is 0xFFFFFFFF; the
-// workspace starts that way (filled with 0xFF bytes), and every completed
-// call leaves it that way.
+// then 16 x (m, l).  A slot is free when every word of it is zero; the
+// workspace starts that way (zero-filled), and every completed call leaves it
+// that way.  Rows of one split publish nothing, so a plan of one split a row
+// needs none.
 constexpr size_t kPartialO = 16 * 128;
 constexpr size_t kPartialML = 16 * 2;
 
 inline size_t pa_workspace_bytes(const PaPlan& p) {
-  return (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float);
+  return p.splits > 1 ? (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float) : 0;
 }
 
 // The standalone emit launch (emit.hip); the fused top-k entry point falls

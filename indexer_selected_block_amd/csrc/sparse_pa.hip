@@ -102,19 +102,22 @@ struct alignas(16) WaveParts {
   float o[NW][16][kHeadDim + 4];
 };
 
-// Split partials in the workspace.  A free slot holds kFreeSlot in every
-// word; a published word never does (NaNs are published as the canonical
-// quiet NaN, and no finite value has these bits), so every word tells by
-// itself whether it has landed.
-constexpr uint32_t kFreeSlot = 0xFFFFFFFFu;
-__device__ __forceinline__ float publishable(float x) { return x != x ? qnan() : x; }
-__device__ __forceinline__ bool published(float x) { return __float_as_uint(x) != kFreeSlot; }
-__device__ __forceinline__ void store_agent(float* p, float x) {
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Split partials in the workspace.  A free slot holds zero in every word; a
+// published word holds the bitwise complement of its value, which is never
+// zero (NaNs are published as the canonical quiet NaN, and no value has all
+// 32 bits set), so every word tells by itself whether it has landed.
+__device__ __forceinline__ void publish_word(float* p, float x) {
+  const uint32_t bits = x != x ? __float_as_uint(qnan()) : __float_as_uint(x);
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), ~bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void free_word(float* p) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t read_word(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool published(uint32_t w) { return w != 0u; }
+__device__ __forceinline__ float word_value(uint32_t w) { return __uint_as_float(~w); }
 
 // The workgroup's share of a row, once every wave has written its part: merge
 // the waves; a row of one split is finished here.  Otherwise the split
@@ -162,10 +165,10 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts<NW>& wp,
     if (mine) {
       float* po = a.part_o + (rbase + split) * kPartialO + tid;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) store_agent(po + 256 * x, publishable(O[x]));
+      for (int x = 0; x < 8; ++x) publish_word(po + 256 * x, O[x]);
       if ((tid & 15) == 0) {
-        store_agent(a.part_ml + ((rbase + split) * 16 + h) * 2 + 0, publishable(M));
-        store_agent(a.part_ml + ((rbase + split) * 16 + h) * 2 + 1, publishable(L));
+        publish_word(a.part_ml + ((rbase + split) * 16 + h) * 2 + 0, M);
+        publish_word(a.part_ml + ((rbase + split) * 16 + h) * 2 + 1, L);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete
@@ -185,17 +188,17 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts<NW>& wp,
     for (int x = 0; x < 8; ++x) O[x] = 0.f;
     if (mine) {
       for (int s0 = 0; s0 < live; s0 += kMergeGroup) {
-        float ms[kMergeGroup], ls[kMergeGroup], os[kMergeGroup][8];
+        uint32_t ms[kMergeGroup], ls[kMergeGroup], os[kMergeGroup][8];
 #pragma unroll
         for (int k = 0; k < kMergeGroup; ++k) {
           const int sp = s0 + k;
           if (sp < live && sp != split) {  // a wave-uniform branch
             const size_t b = (rbase + sp) * 16 + h;
-            ms[k] = load_agent(a.part_ml + b * 2 + 0);
-            ls[k] = load_agent(a.part_ml + b * 2 + 1);
+            ms[k] = read_word(a.part_ml + b * 2 + 0);
+            ls[k] = read_word(a.part_ml + b * 2 + 1);
             const float* pk = a.part_o + (rbase + sp) * kPartialO + tid;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) os[k][x] = load_agent(pk + 256 * x);
+            for (int x = 0; x < 8; ++x) os[k][x] = read_word(pk + 256 * x);
           }
         }
 #pragma unroll
@@ -209,14 +212,14 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts<NW>& wp,
             for (int x = 0; x < 8; ++x) ok = ok && published(os[k][x]);
             valid = valid && ok;
           }
-          const float mk = own ? Mo : ms[k];
+          const float mk = own ? Mo : word_value(ms[k]);
           if (mk == neg_inf()) continue;
           const float Mn = fmaxf(M, mk);
           const float wa = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
           const float wb = __builtin_amdgcn_exp2f(mk - Mn);
-          L = L * wa + (own ? Lo : ls[k]) * wb;
+          L = L * wa + (own ? Lo : word_value(ls[k])) * wb;
 #pragma unroll
-          for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : os[k][x]) * wb;
+          for (int x = 0; x < 8; ++x) O[x] = O[x] * wa + (own ? Oo[x] : word_value(os[k][x])) * wb;
           M = Mn;
         }
       }
@@ -226,10 +229,10 @@ __device__ __forceinline__ void finish_split(const PaArgs& a, WaveParts<NW>& wp,
       for (int sp = 0; sp < live; ++sp) {
         float* po = a.part_o + (rbase + sp) * kPartialO + tid;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) store_agent(po + 256 * x, __uint_as_float(kFreeSlot));
+        for (int x = 0; x < 8; ++x) free_word(po + 256 * x);
         if ((tid & 15) == 0) {
-          store_agent(a.part_ml + ((rbase + sp) * 16 + h) * 2 + 0, __uint_as_float(kFreeSlot));
-          store_agent(a.part_ml + ((rbase + sp) * 16 + h) * 2 + 1, __uint_as_float(kFreeSlot));
+          free_word(a.part_ml + ((rbase + sp) * 16 + h) * 2 + 0);
+          free_word(a.part_ml + ((rbase + sp) * 16 + h) * 2 + 1);
         }
       }
     }
@@ -821,7 +824,7 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
                     int64_t num_pages, float k_scale, float v_scale, int sparse_bt_stride,
                     int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, float sm_scale,
                     void* workspace, size_t workspace_bytes, void* out, PaArgs& a, PaPlan& plan) {
-  if (!q || !k_pool || !v_pool || !workspace || !out) return ISB_E_INVALID_ARG;
+  if (!q || !k_pool || !v_pool || !out) return ISB_E_INVALID_ARG;
   if (num_pages <= 0 || sparse_bt_stride <= 0 || num_tokens <= 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0)
     return ISB_E_INVALID_ARG;
@@ -834,7 +837,9 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
   if (rows > 0x7FFFFFFFLL) return ISB_E_SHAPE;
   plan = pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype);
   if (plan.splits > 65535) return ISB_E_SHAPE;
-  if (workspace_bytes < pa_workspace_bytes(plan)) return ISB_E_WORKSPACE;
+  const size_t need = pa_workspace_bytes(plan);  // 0: every row one split, nothing published
+  if (need > 0 && !workspace) return ISB_E_INVALID_ARG;
+  if (workspace_bytes < need) return ISB_E_WORKSPACE;
   const bool fp8 = kv_dtype == ISB_FP8_E4M3;
   a.q = (const uint8_t*)q;
   a.kp = (const uint8_t*)k_pool;

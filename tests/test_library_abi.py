@@ -112,7 +112,7 @@ def test_argument_checks_return_before_any_launch(lib):
                                  16, 0.1, p, 1 << 20, p, p, p, p) == -3                          # MB > stride
     assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 4, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,
                                  32, 0.1, p, 1 << 20, p, p, p, p) == -3                          # G = 32
-    assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 4, 2, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0,
+    assert lib.isb_select_attend(NULL, p, p, 1, 1, 1, 8, 8, p, 8, p, 0, p, p, 1, 8, 1.0, 1.0,
                                  16, 0.1, p, 16, p, p, p, p) == -4                               # workspace
     assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 1, 1, 16, 1, 64, 0.1,
                                     p, 1 << 20, p) == -3                                         # head_dim
@@ -158,10 +158,11 @@ def test_argument_checks_return_before_any_launch(lib):
 def test_workspace_query(lib):
     # the split-K partials: rows x splits x 16 heads x (128 + 2) floats; the
     # plan's split counts for the five workloads' shapes
+    # (none when every row is one split: nothing is published)
     for T, stride, dt, splits in [(128, 128, 1, 2), (4300, 128, 1, 1), (64, 16, 2, 4), (16, 256, 1, 8),
                                   (4, 32, 0, 2)]:
         n = lib.isb_sparse_pa_workspace_bytes(T, 16, 1, stride, dt)
-        assert n == T * splits * 16 * 130 * 4, (T, stride, dt)
+        assert n == (T * splits * 16 * 130 * 4 if splits > 1 else 0), (T, stride, dt)
     assert lib.isb_sparse_pa_workspace_bytes(0, 16, 1, 128, 1) == 0
     assert lib.isb_sparse_pa_workspace_bytes(4, 16, 1, 128, 5) == 0
 
