@@ -294,6 +294,27 @@ ISB_API int isb_sparse_pa_decode(isb_stream_t stream,
                          size_t workspace_bytes, void* out);
 
 /*
+ * isb_sparse_pa_decode_noalloc - isb_sparse_pa_decode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, hosts that forbid allocation).  The
+ * split partials go to the library's own zero-initialised device array
+ * (8 MiB, one per device, held until the process ends; every completed call
+ * leaves it zero).  Arguments, results and errors as isb_sparse_pa_decode;
+ * ISB_E_WORKSPACE when the partials these arguments need
+ * (isb_sparse_pa_workspace_bytes) exceed 8 MiB.  The stream must belong to
+ * the current device.  Calls that overlap in time on one device share the
+ * array and race.
+ */
+ISB_API int isb_sparse_pa_decode_noalloc(isb_stream_t stream,
+                         const void* q, int q_dtype,
+                         const void* k_pool, const void* v_pool, int kv_dtype,
+                         int64_t num_pages, float k_scale, float v_scale,
+                         const int32_t* sparse_bt, int sparse_bt_stride,
+                         const int32_t* sparse_ctx, int num_tokens,
+                         int decode_query_len, int num_q_heads, int num_kv_heads,
+                         int head_dim, float sm_scale, void* out);
+
+/*
  * isb_select_attend - isb_topk_select_emit followed by isb_sparse_pa_decode,
  * in one launch where it can: each attention workgroup selects its row's
  * blocks itself (from the row's scores and block-table row) and takes its

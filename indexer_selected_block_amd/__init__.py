@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     quantize_e4m3,
     select_attend,
     sparse_pa_decode,
+    sparse_pa_decode_noalloc,
     sparse_pa_workspace_bytes,
     strerror,
     topk_select,

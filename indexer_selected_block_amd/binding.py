@@ -96,6 +96,8 @@ _SIGNATURES = {
     "isb_sparse_pa_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
     "isb_sparse_pa_decode": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I, _I,
                               _F, _P, _SZ, _P], _I),
+    "isb_sparse_pa_decode_noalloc": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I, _I,
+                                      _F, _P], _I),
     "isb_write_cache": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _F, _F, _I64, _P, _I, _F, _I64,
                          _NR, _NR], _I),
     "isb_prepare_query": ([_P, _P, _I, _P, _I, _I, _NR, _I, _P], _I),
@@ -380,6 +382,27 @@ def sparse_pa_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, spa
     return out
 
 
+def sparse_pa_decode_noalloc(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, sparse_bt, sparse_ctx,
+                             num_q_heads, num_kv_heads, sm_scale, out, decode_query_len=1):
+    """sparse_pa_decode into a caller-owned ``out`` with no workspace: the
+    split partials go to the library's own device array (see
+    isb_sparse_pa_decode_noalloc).  Allocates nothing."""
+    T = q.shape[0]
+    num_pages = _check_kv_pools(k_pool, v_pool, kv_dtype, num_kv_heads)
+    _check_query("q", q, q_dtype, T, num_q_heads)
+    _check_int32(sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    if sparse_bt.dim() != 2 or sparse_bt.shape[0] != T * num_kv_heads:
+        raise ValueError(f"sparse_bt must be int32 [{T * num_kv_heads}, stride]")
+    _check_shape("sparse_ctx", sparse_ctx, (T * num_kv_heads,))
+    _check_out(out, T, num_q_heads)
+    dev = _dev(q, k_pool, v_pool, sparse_bt, sparse_ctx, out)
+    _call("sparse_pa_decode_noalloc", _stream(dev), q.data_ptr(), _code(q_dtype), k_pool.data_ptr(),
+          v_pool.data_ptr(), _code(kv_dtype), num_pages, float(k_scale), float(v_scale), sparse_bt.data_ptr(),
+          sparse_bt.shape[1], sparse_ctx.data_ptr(), T, int(decode_query_len), num_q_heads, num_kv_heads, 128,
+          float(sm_scale), out.data_ptr())
+    return out
+
+
 def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_dtype, k_pool, v_pool,
                   kv_dtype, k_scale, v_scale, num_q_heads, sm_scale, topk_idx=None, sparse_bt=None,
                   sparse_ctx=None, out=None, workspace=None):
@@ -541,4 +564,5 @@ isb_emit_sparse_block_table = emit_sparse_block_table
 isb_topk_select_emit = topk_select_emit
 isb_select_attend = select_attend
 isb_sparse_pa_decode = sparse_pa_decode
+isb_sparse_pa_decode_noalloc = sparse_pa_decode_noalloc
 isb_sparse_pa_workspace_bytes = sparse_pa_workspace_bytes

@@ -57,6 +57,8 @@
 // find those pages in L2; with one token a request no page is read twice in a
 // launch, and 16-token pages are streamed past the caches (nontemporal
 // loads), which raises the rate the memory system delivers them at.
+#include <mutex>
+
 #include "grid_maps.h"
 #include "isb_device.h"
 #include "isb_host.h"
@@ -931,6 +933,66 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
     else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, nt, plan, st);
   }
   return launch_status();
+}
+
+// ----------------------------------------------------------------- no allocation
+// isb_sparse_pa_decode_noalloc: the same call with the split partials in this
+// library's own device memory, for callers that cannot allocate (code under
+// HIP graph capture, serving loops, hosts that forbid allocation).  The array
+// is zero-initialised when the library's code is loaded on a device, which is
+// the free state of every slot, and every completed call leaves it so; each
+// device holds its own copy until the process ends.  Calls that overlap in
+// time on one device share it and race.
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // per device: the device address of `scratch`
+
+// The device address of the current device's scratch, looked up once per
+// device (with that device current); nullptr if the lookup fails.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int isb_sparse_pa_decode_noalloc(isb_stream_t stream, const void* q, int q_dtype,
+                                            const void* k_pool, const void* v_pool, int kv_dtype,
+                                            int64_t num_pages, float k_scale, float v_scale,
+                                            const int32_t* sparse_bt, int sparse_bt_stride,
+                                            const int32_t* sparse_ctx, int num_tokens, int decode_query_len,
+                                            int num_q_heads, int num_kv_heads, int head_dim, float sm_scale,
+                                            void* out) {
+  using namespace isb;
+  // every argument check of isb_sparse_pa_decode first, the scratch standing
+  // in as a workspace of its size (nothing is read or written here): errors
+  // come back before any device call, and partials beyond the scratch are
+  // ISB_E_WORKSPACE
+  if (!sparse_bt || !sparse_ctx || decode_query_len <= 0) return ISB_E_INVALID_ARG;
+  if (num_tokens > 0 && num_tokens % decode_query_len != 0) return ISB_E_SHAPE;
+  {
+    PaArgs a;
+    PaPlan plan;
+    const int err = pa_setup(q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale, sparse_bt_stride,
+                             num_tokens, num_q_heads, num_kv_heads, head_dim, sm_scale,
+                             reinterpret_cast<void*>(uintptr_t(256)), kNoallocScratchBytes, out, a, plan);
+    if (err) return err;
+  }
+  void* ws = device_scratch();
+  if (!ws) return ISB_E_LAUNCH;
+  return isb_sparse_pa_decode(stream, q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale, sparse_bt,
+                              sparse_bt_stride, sparse_ctx, num_tokens, decode_query_len, num_q_heads, num_kv_heads,
+                              head_dim, sm_scale, ws, kNoallocScratchBytes, out);
 }
 
 extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const int32_t* seq_lens,

@@ -30,6 +30,7 @@ def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("isb_index_score", "isb_topk_select", "isb_emit_sparse_block_table",
               "isb_sparse_pa_decode", "isb_sparse_pa_workspace_bytes", "isb_strerror", "isb_version",
+              "isb_sparse_pa_decode_noalloc",
               "isb_write_cache", "isb_quantize_e4m3", "isb_prepare_query", "isb_topk_merge"):
         assert n in names
 
@@ -153,6 +154,13 @@ def test_argument_checks_return_before_any_launch(lib):
     assert need > 0
     assert lib.isb_sparse_pa_decode(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 4, 1, 16, 1, 128, 0.1,
                                     p, need - 1, p) == -4
+    # the allocation-free call refuses partials beyond its 8 MiB array before touching a device:
+    # 511 rows of two splits need 511 x 2 x 8320 B
+    assert lib.isb_sparse_pa_workspace_bytes(511, 16, 1, 128, 1) == 511 * 2 * 8320 > 8 << 20
+    assert lib.isb_sparse_pa_decode_noalloc(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 511, 1, 16, 1, 128, 0.1,
+                                            p) == -4
+    assert lib.isb_sparse_pa_decode_noalloc(NULL, NULL, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 4, 1, 16, 1, 128, 0.1,
+                                            p) == -1
 
 
 def test_workspace_query(lib):
