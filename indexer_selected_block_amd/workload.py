@@ -152,6 +152,71 @@ CONFIGS: dict[str, Config] = {
 }
 
 
+# Ragged prefill batches: each request contributes the last chunk_lens[r]
+# positions of its context as query tokens, each token carrying its own
+# request id and absolute position (the prefill call's query_req_id /
+# query_abs_pos).  The setup is the prefill workload's (fp8 K/V and index,
+# contexts U{16384..65536}, top-k 16 per token) with six requests whose chunks
+# run from a single token to 1024 tokens.
+RAGGED_CHUNKS: dict[str, tuple[int, ...]] = {
+    "prefill_ragged": (512, 1, 300, 77, 1024, 133),
+}
+
+
+def ragged_config(name: str) -> Config:
+    """The request-level setup of a ragged prefill batch (query_len unused: 1)."""
+    chunks = RAGGED_CHUNKS[name]
+    base = CONFIGS["prefill"]
+    return replace(base, name=name, num_reqs=len(chunks), query_len=1,
+                   pool_blocks=len(chunks) * base.max_blocks + 64, seed=7,
+                   description=f"{len(chunks)} requests with prefill chunks of "
+                               f"{'/'.join(map(str, chunks))} tokens ({sum(chunks)} in all), contexts "
+                               "U{16384..65536}, fp8 K/V and index, top-k 16 per token")
+
+
+@dataclass
+class RaggedBatch:
+    query_req_id: torch.Tensor   # int32 [T]: the token's row of the block table
+    query_abs_pos: torch.Tensor  # int32 [T]: its 0-based position in the request
+    q: torch.Tensor              # uint8 [T, H_q, 128 * qbytes]
+    q_idx: torch.Tensor          # uint8 [T, H_idx, 128 * qbytes]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_req_id.shape[0])
+
+    def to(self, device) -> "RaggedBatch":
+        return RaggedBatch(*(t.to(device) for t in (self.query_req_id, self.query_abs_pos, self.q,
+                                                      self.q_idx)))
+
+
+def ragged_batch(w: "Workload", chunk_lens, order: str = "grouped", seed: int = 0) -> RaggedBatch:
+    """Query tokens of a ragged prefill over the requests of ``w``: request r
+    gives its last chunk_lens[r] positions (0 = none).  ``order``: "grouped"
+    (request by request, positions ascending: a prefill batch as a scheduler
+    lays it out) or "shuffled" (a seeded permutation of the same tokens).
+    Fresh seeded queries of the workload's query dtypes."""
+    cfg = w.cfg
+    lens = w.seq_lens.cpu().to(torch.int64)
+    chunks = torch.as_tensor(list(chunk_lens), dtype=torch.int64)
+    if chunks.shape[0] != lens.shape[0] or bool((chunks < 0).any()) or bool((chunks > lens).any()):
+        raise ValueError("one chunk length a request, each within the request's length")
+    req = torch.repeat_interleave(torch.arange(lens.shape[0]), chunks)
+    first = torch.cumsum(chunks, 0) - chunks
+    pos = lens[req] - chunks[req] + (torch.arange(req.shape[0]) - first[req])
+    if order == "shuffled":
+        perm = torch.randperm(req.shape[0], generator=torch.Generator().manual_seed(seed * 31 + 5))
+        req, pos = req[perm], pos[perm]
+    elif order != "grouped":
+        raise ValueError(order)
+    T = int(req.shape[0])
+    streams = _Streams(cfg.seed * 1009 + seed, torch.device("cpu"))
+    q = _query(cfg, streams, _T_Q, (T, cfg.num_q_heads, cfg.head_dim), cfg.q_dtype)
+    q_idx = _query(cfg, streams, _T_QIDX, (T, cfg.num_idx_heads, cfg.head_dim), cfg.qidx_dtype)
+    dev = w.seq_lens.device
+    return RaggedBatch(req.to(torch.int32).to(dev), pos.to(torch.int32).to(dev), q.to(dev), q_idx.to(dev))
+
+
 def shrink(cfg: Config, num_reqs: int, ctx_lo: int, ctx_hi: int, num_pad_reqs: int | None = None,
            pool_blocks: int | None = None, top_k: int | None = None) -> Config:
     """A smaller workload with the same dtypes, heads and query length."""

@@ -12,7 +12,9 @@ in each docstring:
 * ``formats``  - exact decoding of bf16, e4m3fn, e2m1, e8m0 and the MXFP4 page;
 * ``pools``    - reading tokens out of the paged index and K/V caches;
 * ``decode``   - index score, top-k selection, sparse block-table emission and
-                 sparse attention, and the four chained as one decode layer.
+                 sparse attention, and the four chained as one decode layer;
+* ``prefill``  - the same steps for a ragged prefill batch, each query token
+                 with its own request id and absolute position.
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 library routines on special cases, brute force on tiny inputs, invariants),
@@ -21,4 +23,4 @@ maximum over the block's tokens, and index heads of one KV group being summed -
 whose arithmetic is pinned but whose choice of definition is a reading.
 """
 
-from . import formats, pools, decode  # noqa: F401
+from . import formats, pools, decode, prefill  # noqa: F401
