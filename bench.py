@@ -106,54 +106,63 @@ def measured_copy(nbytes_moved):
     return {"bytes_moved": 2 * half, "avg_us": round(us, 2), "GBps": round(2 * half / (us * 1e-6) / 1e9, 1)}
 
 
-def distinct_attended_tokens(w, topk):
+def token_geometry(L):
+    """Per query token of a layer's batch: (request, causal length).  Decode
+    batches: token r q + i of request r, L_t = max(0, L_r - (q - 1 - i));
+    ragged prefill batches: each token's own request id and position + 1."""
+    b = getattr(L, "b", None)
+    if b is not None:
+        return list(zip(b.query_req_id.cpu().tolist(), [p + 1 for p in b.query_abs_pos.cpu().tolist()]))
+    ql = L.w.cfg.query_len
+    return [(r, max(0, Lr - (ql - 1 - i))) for r, Lr in enumerate(L.w.seq_lens.cpu().tolist()) for i in range(ql)]
+
+
+def distinct_attended_tokens(L, topk):
     """K/V positions the attention must read at least once: per request and KV
     head, the union over the request's query tokens of their selected blocks,
     each block up to the longest causal reach of a token that selects it (the
     tokens of one request can select the same blocks)."""
-    cfg = w.cfg
-    ql = cfg.query_len
-    lens = w.seq_lens.cpu().tolist()
+    geo = token_geometry(L)
     tk = topk.cpu().tolist()  # [H_kv][T][K]
     total = 0
-    for g in range(cfg.num_kv_heads):
-        for r, L in enumerate(lens):
-            reach = {}
-            for i in range(ql):
-                Lt = max(0, L - (ql - 1 - i))
-                for b in tk[g][r * ql + i]:
-                    if b >= 0:
-                        reach[b] = max(reach.get(b, 0), min(128, Lt - 128 * b))
-            total += sum(reach.values())
+    for g in range(L.w.cfg.num_kv_heads):
+        reach = {}
+        for t, (r, Lt) in enumerate(geo):
+            for b in tk[g][t]:
+                if b >= 0:
+                    reach[(r, b)] = max(reach.get((r, b), 0), min(128, Lt - 128 * b))
+        total += sum(reach.values())
     return total
 
 
-def algorithmic_bytes(w, sparse_ctx, topk):
+def algorithmic_bytes(L, sparse_ctx, topk):
     """Bytes each kernel must move for this batch: the index keys of every
-    request once, the queries, the table entries and lengths read, the scores,
+    request once (up to the farthest position one of its tokens sees), the
+    queries, the table entries and token positions read, the scores,
     selection, page table and outputs written; for the attention the K and V
     bytes of the positions attended, each distinct position once (rows of one
     request that select the same block need its bytes once).  Split partials
     and re-reads are not counted."""
-    cfg = w.cfg
-    lens = w.seq_lens.cpu().tolist()
-    ql, T = cfg.query_len, cfg.num_tokens
-    n_req_blocks = sum(-(-L // 128) for L in lens)
-    n_tok_blocks = 0
-    for r, L in enumerate(lens):
-        for i in range(ql):
-            n_tok_blocks += -(-max(0, L - (ql - 1 - i)) // 128)
+    cfg = L.w.cfg
+    geo = token_geometry(L)
+    T = len(geo)
+    reach = {}
+    for r, Lt in geo:
+        reach[r] = max(reach.get(r, 0), Lt)
+    n_req_blocks = sum(-(-x // 128) for x in reach.values())
+    n_tok_blocks = sum(-(-Lt // 128) for _, Lt in geo)
+    per_token_in = 8 * T if getattr(L, "b", None) is not None else 4 * len(reach)   # positions / lengths
     qidx = T * cfg.num_idx_heads * 128 * Q_BYTES[cfg.qidx_dtype]
-    score = (sum(lens) * IDX_BYTES[cfg.idx_dtype] + qidx + 4 * n_req_blocks + 4 * len(lens)
+    score = (sum(reach.values()) * IDX_BYTES[cfg.idx_dtype] + qidx + 4 * n_req_blocks + per_token_in
              + 4 * cfg.num_kv_heads * n_tok_blocks)
     rows = T * cfg.num_kv_heads
     slots = cfg.top_k * cfg.pages_per_block
     # top-k + emit: scores and lengths in, the table entries the selection names
     # in, the selection, the page table and the lengths out
-    topk_emit = (4 * cfg.num_kv_heads * n_tok_blocks + 4 * len(lens) + 4 * rows * cfg.top_k
+    topk_emit = (4 * cfg.num_kv_heads * n_tok_blocks + per_token_in + 4 * rows * cfg.top_k
                  + 4 * rows * cfg.top_k + 4 * rows * (slots + 1))
     ctx = sparse_ctx.cpu().long()
-    attended = distinct_attended_tokens(w, topk) * 2 * KV_BYTES[cfg.kv_dtype]
+    attended = distinct_attended_tokens(L, topk) * 2 * KV_BYTES[cfg.kv_dtype]
     ptok = 128 // cfg.pages_per_block
     pages = int(((ctx + ptok - 1) // ptok).sum())
     attn = (attended + T * cfg.num_q_heads * 128 * (Q_BYTES[cfg.q_dtype] + 2) + 4 * pages + 4 * rows)
@@ -161,20 +170,18 @@ def algorithmic_bytes(w, sparse_ctx, topk):
     return {"index_score": score, "topk_select_emit": topk_emit, "sparse_pa_decode": attn}, attended, per_row
 
 
-def index_flops(w):
+def index_flops(L):
     """Multiply-adds (x2) the scorer must do: each index query row against each
     of its token's causally valid keys, 128 dims."""
-    cfg = w.cfg
-    ql = cfg.query_len
-    tok_keys = sum(max(0, L - (ql - 1 - i)) for L in w.seq_lens.cpu().tolist() for i in range(ql))
-    return 2 * 128 * cfg.num_idx_heads * tok_keys
+    return 2 * 128 * L.w.cfg.num_idx_heads * sum(Lt for _, Lt in token_geometry(L))
 
 
-def scorer_is_wide(cfg):
-    """More than 16 tokens or 64 index query rows a request: the scorer that
-    holds a block's keys in registers and runs them against 16-row query tiles
-    on MFMA (prefill chunks); its bound is the MFMA rate, not HBM."""
-    return cfg.query_len > 16 or cfg.query_len * cfg.num_idx_heads > 64
+def scorer_is_wide(cfg, ragged=False):
+    """More than 16 tokens or 64 index query rows a request, or a ragged
+    prefill batch: the scorer that holds a block's keys in registers and runs
+    them against 16-row query tiles on MFMA; its bound is the MFMA rate, not
+    HBM."""
+    return ragged or cfg.query_len > 16 or cfg.query_len * cfg.num_idx_heads > 64
 
 
 # dense MFMA peaks of MI355X (TFLOP/s) for the scorer's operand types: bf16
@@ -361,14 +368,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
-    cfg = wl.CONFIGS[args.config]
+    ragged = args.config in wl.RAGGED_CHUNKS
+    cfg = wl.ragged_config(args.config) if ragged else wl.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     print(f"[bench] building {args.config} x{args.layers} on {torch.cuda.get_device_name(0)}",
           file=sys.stderr, flush=True)
     layers = []
     for li in range(args.layers):
         c = cfg if li == 0 else dataclasses.replace(cfg, seed=cfg.seed + 1000 * li)
-        layers.append(isb.DecodeLayer(wl.make_workload(c, device=dev)))
+        w = wl.make_workload(c, device=dev)
+        if ragged:  # a prefill batch: the requests' chunks, each token with its own request and position
+            layers.append(isb.PrefillLayer(w, wl.ragged_batch(w, wl.RAGGED_CHUNKS[args.config], seed=li)))
+        else:
+            layers.append(isb.DecodeLayer(w))
     torch.cuda.synchronize()
 
     for s in range(args.warmup):
@@ -382,7 +394,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     # live query tokens: pad requests (length 0) compute nothing and are not counted
-    T = int((layers[0].w.seq_lens > 0).sum()) * cfg.query_len
+    T = (layers[0].b.num_tokens if ragged else int((layers[0].w.seq_lens > 0).sum()) * cfg.query_len)
     ms_per_step = 1000.0 * elapsed / args.steps
 
     # ---- per-kernel durations, each in its place in the step: passes of K
@@ -394,22 +406,43 @@ def main():
 
     def call_index(L):
         w, c = L.w, L.w.cfg
+        if ragged:
+            isb.index_score_prefill(L.b.q_idx, c.qidx_dtype, w.idx_pool, c.idx_dtype, w.idx_scale, w.block_table,
+                                    L.b.query_req_id, L.b.query_abs_pos, c.num_kv_heads, c.max_blocks,
+                                    scores=L.scores)
+            return
         isb.index_score(w.q_idx, c.qidx_dtype, w.idx_pool, c.idx_dtype, w.idx_scale, w.block_table,
                         w.seq_lens, c.query_len, c.num_kv_heads, c.max_blocks, scores=L.scores)
 
     def call_topk(L):
         w, c = L.w, L.w.cfg
+        if ragged:
+            isb.topk_select_emit_prefill(L.scores, L.b.query_req_id, L.b.query_abs_pos, c.top_k, w.block_table,
+                                         c.pages_per_block, topk_idx=L.topk, sparse_bt=L.sparse_bt,
+                                         sparse_ctx=L.sparse_ctx)
+            return
         isb.topk_select_emit(L.scores, w.seq_lens, c.query_len, c.top_k, w.block_table, c.pages_per_block,
                              topk_idx=L.topk, sparse_bt=L.sparse_bt, sparse_ctx=L.sparse_ctx)
 
     def call_attend(L):
         w, c = L.w, L.w.cfg
+        if ragged:
+            isb.sparse_pa_prefill(L.b.q, c.q_dtype, w.k_pool, w.v_pool, c.kv_dtype, w.k_scale, w.v_scale,
+                                  L.sparse_bt, L.sparse_ctx, c.num_q_heads, c.num_kv_heads, w.sm_scale,
+                                  out=L.out, workspace=L.workspace)
+            return
         isb.sparse_pa_decode(w.q, c.q_dtype, w.k_pool, w.v_pool, c.kv_dtype, w.k_scale, w.v_scale,
                              L.sparse_bt, L.sparse_ctx, c.num_q_heads, c.num_kv_heads, w.sm_scale,
                              out=L.out, workspace=L.workspace, decode_query_len=c.query_len)
 
     def call_select_attend(L):
         w, c = L.w, L.w.cfg
+        if ragged:
+            isb.select_attend_prefill(L.scores, L.b.query_req_id, L.b.query_abs_pos, c.top_k, w.block_table, L.b.q,
+                                      c.q_dtype, w.k_pool, w.v_pool, c.kv_dtype, w.k_scale, w.v_scale,
+                                      c.num_q_heads, w.sm_scale, topk_idx=L.topk, sparse_bt=L.sparse_bt,
+                                      sparse_ctx=L.sparse_ctx, out=L.out, workspace=L.workspace)
+            return
         isb.select_attend(L.scores, w.seq_lens, c.query_len, c.top_k, w.block_table, w.q, c.q_dtype, w.k_pool,
                           w.v_pool, c.kv_dtype, w.k_scale, w.v_scale, c.num_q_heads, w.sm_scale, topk_idx=L.topk,
                           sparse_bt=L.sparse_bt, sparse_ctx=L.sparse_ctx, out=L.out, workspace=L.workspace)
@@ -451,7 +484,7 @@ def main():
     t_s, t_i, t_it, t_ita, t_step = (sorted(reps[k])[1] for k in ("s", "i", "it", "ita", "step"))
     dur_ms = {"index_score": t_i - t_s, "topk_select_emit": t_it - t_i, "sparse_pa_decode": t_ita - t_it,
               "select_attend": t_step - t_i}
-    ceilings = time_ceilings(layers, pass_ms, scrub, t_s, stream)
+    ceilings = time_ceilings(layers, pass_ms, scrub, t_s, stream, ragged)
     # the same with one input copy: the attention's pages can stay in the
     # last-level cache from the step before (reported apart, never as value)
     all_layers = layers
@@ -464,16 +497,16 @@ def main():
     w0 = layers[0].w
     # the copies differ in lengths and selections: bytes are averaged over the
     # copies the timed steps cycle through, like the durations
-    per_copy = [algorithmic_bytes(L.w, L.sparse_ctx, L.topk) for L in layers]
+    per_copy = [algorithmic_bytes(L, L.sparse_ctx, L.topk) for L in layers]
     alg = {k: sum(a[k] for a, _, _ in per_copy) / len(per_copy) for k in per_copy[0][0]}
     attended = sum(x for _, x, _ in per_copy) / len(per_copy)
     attended_rows = sum(x for _, _, x in per_copy) / len(per_copy)
     shas = kernel_sources_sha()
 
-    flops = sum(index_flops(L.w) for L in layers) / len(layers)
+    flops = sum(index_flops(L) for L in layers) / len(layers)
 
     def roof(kernel):
-        if kernel == "index_score" and scorer_is_wide(cfg):
+        if kernel == "index_score" and scorer_is_wide(cfg, ragged):
             tflops = flops / (dur_ms[kernel] * 1e-3) / 1e12
             peak = mfma_peak_tflops(cfg)
             return {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
@@ -504,7 +537,8 @@ def main():
         "dtype": "e4m3->bf16 mfma, f32 accumulate" if cfg.kv_dtype == "fp8" else f"{cfg.kv_dtype} in, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "requests": cfg.total_reqs,
-                   "query_len": cfg.query_len, "tokens_per_step": T, "token_rows": cfg.num_tokens,
+                   "query_len": "ragged" if ragged else cfg.query_len, "tokens_per_step": T,
+                   "token_rows": T if ragged else cfg.num_tokens,
                    "top_k": cfg.top_k,
                    "q_heads_per_kv": cfg.num_q_heads // cfg.num_kv_heads,
                    "index_heads": cfg.num_idx_heads, "kv_cache": cfg.kv_dtype,
@@ -512,7 +546,8 @@ def main():
         "attended_kv_GBps": round(attn_gbps, 1),
         "attended_kv_pct_hbm_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 2),
         "attended_kv_bytes": {"distinct": int(round(attended)), "summed_over_rows": int(round(attended_rows))},
-        "step_launches": ["index_score", "select_attend"],
+        "step_launches": (["index_score_prefill", "select_attend_prefill"] if ragged
+                          else ["index_score", "select_attend"]),
         "kernel_ms": {k: round(v, 5) for k, v in dur_ms.items()},
         "kernel_ms_method": "differences of back-to-back passes of K steps ending after each call (HIP events; median of 3 rounds)",
         "sparse_pa_decode_ms_one_input_copy": round(warm_attend, 5),
@@ -530,16 +565,16 @@ def main():
     result["ceilings"] = ceilings
     result["measured_copy"] = {"at_attention_size": measured_copy(int(alg["sparse_pa_decode"])),
                                "at_1GiB": measured_copy(1 << 30)}
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not ragged:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
-    else:
+    else:  # the oracle baseline is taken on decode batches
         result["cpu_baseline"] = None
-    result["write_cache"] = time_writer(isb, w0, stream, args.steps)
+    result["write_cache"] = None if ragged else time_writer(isb, w0, stream, args.steps)
     print(json.dumps(result))
 
 
-def time_ceilings(layers, pass_ms, scrub, t_scrub, stream):
+def time_ceilings(layers, pass_ms, scrub, t_scrub, stream, ragged=False):
     """The measurement kernels of libisb_ceiling on the same inputs and
     passes as the layer's calls: the index scan's and the attention's page
     reads with no arithmetic, in their grids.  Per launch, as the passes'
@@ -561,7 +596,8 @@ def time_ceilings(layers, pass_ms, scrub, t_scrub, stream):
     st = ctypes.c_void_p(stream.cuda_stream)
     dev = layers[0].w.q.device
     idx_out = torch.empty((cfg.total_reqs, cfg.max_blocks), dtype=torch.float32, device=dev)
-    words = lib.isb_ceiling_attention_words(cfg.num_tokens, cfg.num_kv_heads, layers[0].sparse_bt.shape[1],
+    T = layers[0].sparse_ctx.shape[0] // cfg.num_kv_heads
+    words = lib.isb_ceiling_attention_words(T, cfg.num_kv_heads, layers[0].sparse_bt.shape[1],
                                             bd._code(cfg.kv_dtype))
     att_out = torch.empty((max(int(words), 1),), dtype=torch.int32, device=dev)
 
@@ -576,16 +612,18 @@ def time_ceilings(layers, pass_ms, scrub, t_scrub, stream):
 
     def attention_gather(L):
         w = L.w
+        # a prefill batch's rows share pages: read through the caches, as a
+        # decode_query_len above 1 asks for
         rc = lib.isb_ceiling_attention_gather(st, w.k_pool.data_ptr(), w.v_pool.data_ptr(), bd._code(cfg.kv_dtype),
                                               w.k_pool.shape[0], L.sparse_bt.data_ptr(), L.sparse_bt.shape[1],
-                                              L.sparse_ctx.data_ptr(), cfg.num_tokens, cfg.query_len,
+                                              L.sparse_ctx.data_ptr(), T, T if ragged else cfg.query_len,
                                               cfg.num_kv_heads, att_out.data_ptr(), att_out.numel())
         if rc:
             raise RuntimeError(f"isb_ceiling_attention_gather: status {rc}")
 
     out = {}
     kinds = [("attention_gather", attention_gather)]
-    if not scorer_is_wide(cfg):
+    if not scorer_is_wide(cfg, ragged):
         kinds.insert(0, ("index_gather", index_gather))
     for name, f in kinds:
         t = sorted(pass_ms([f, scrub]) for _ in range(3))[1] - t_scrub

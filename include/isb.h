@@ -342,6 +342,93 @@ ISB_API int isb_select_attend(isb_stream_t stream, const float* scores,
                               int32_t* sparse_bt, int32_t* sparse_ctx, void* out);
 
 /*
+ * Prefill batches
+ * ---------------
+ * The prefill call of the vLLM API page for sparse_attention_msa
+ * (MiniMaxM3SparseAiterPAImpl.forward, prefill branch) gives every query
+ * token its own request and position instead of a uniform chunk:
+ *   query_req_id   [num_tokens] int32: the token's row of block_table;
+ *   query_abs_pos  [num_tokens] int32: its 0-based position in the request.
+ * Token t attends to positions 0 .. query_abs_pos[t] of its request: causal
+ * length L_t = query_abs_pos[t] + 1 (the token's own key is already in the
+ * cache) and n_t = ceil(L_t / 128) blocks.  Tokens may come in any order, of
+ * any requests; a scheduler's order (each request's tokens together,
+ * positions ascending) lets the scorer read a block once for many tokens.
+ * Every other rule, layout and output is the decode call's with T =
+ * num_tokens: scores [num_kv_heads][T][max_blocks], topk_idx
+ * [num_kv_heads][T][top_k], sparse_bt / sparse_ctx rows t * num_kv_heads + g,
+ * out [T][num_q_heads][128].  A token whose request id is outside
+ * [0, num_reqs) or whose position is outside [0, 128 * max_blocks) (the
+ * block-table width for the emit call) is an empty row: -inf scores, no
+ * selection, sparse length 0, zero output; nothing is read through it.
+ */
+
+/*
+ * isb_index_score_prefill - isb_index_score for a prefill batch.  Takes the
+ * wide variant whatever the batch (query tiles of 128 rows of consecutive
+ * tokens; each run of one request's tokens in a tile reads its blocks once).
+ * Shape errors: those of isb_index_score, 16 % num_idx_heads != 0,
+ * num_tokens * num_idx_heads > 2^31 - 1 or more than 65535 tiles of 128 rows.
+ */
+ISB_API int isb_index_score_prefill(isb_stream_t stream, const void* q_idx, int q_idx_dtype,
+                                    int num_idx_heads, const void* idx_pool, int idx_dtype,
+                                    float idx_scale, int64_t idx_pool_blocks,
+                                    const int32_t* block_table, int block_table_stride, int num_reqs,
+                                    const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                    int num_tokens, int num_kv_heads, int max_blocks, float* scores);
+
+/* isb_topk_select_prefill - isb_topk_select for a prefill batch. */
+ISB_API int isb_topk_select_prefill(isb_stream_t stream, const float* scores, int num_reqs,
+                                    const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                    int num_tokens, int num_kv_heads, int max_blocks, int top_k,
+                                    int32_t* topk_idx);
+
+/*
+ * isb_emit_sparse_block_table_prefill - isb_emit_sparse_block_table for a
+ * prefill batch; positions are valid below 128 * block_table_stride.
+ */
+ISB_API int isb_emit_sparse_block_table_prefill(isb_stream_t stream, const int32_t* topk_idx,
+                                                const int32_t* block_table, int block_table_stride,
+                                                int num_reqs, const int32_t* query_req_id,
+                                                const int32_t* query_abs_pos, int num_tokens,
+                                                int num_kv_heads, int top_k, int pages_per_block,
+                                                int32_t* sparse_bt, int32_t* sparse_ctx);
+
+/* isb_topk_select_emit_prefill - isb_topk_select_emit for a prefill batch. */
+ISB_API int isb_topk_select_emit_prefill(isb_stream_t stream, const float* scores, int num_reqs,
+                                         const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                         int num_tokens, int num_kv_heads, int max_blocks, int top_k,
+                                         const int32_t* block_table, int block_table_stride,
+                                         int pages_per_block, int32_t* topk_idx, int32_t* sparse_bt,
+                                         int32_t* sparse_ctx);
+
+/*
+ * isb_sparse_pa_prefill - isb_sparse_pa_decode for the rows of a prefill
+ * batch (the prefill call's sparse_bt / sparse_ctx): the same results; the
+ * rows of one request share many pages, which are read through the caches.
+ * Workspace as isb_sparse_pa_workspace_bytes(num_tokens, ...) gives, with the
+ * same contract.
+ */
+ISB_API int isb_sparse_pa_prefill(isb_stream_t stream, const void* q, int q_dtype,
+                                  const void* k_pool, const void* v_pool, int kv_dtype,
+                                  int64_t num_pages, float k_scale, float v_scale,
+                                  const int32_t* sparse_bt, int sparse_bt_stride,
+                                  const int32_t* sparse_ctx, int num_tokens, int num_q_heads,
+                                  int num_kv_heads, int head_dim, float sm_scale, void* workspace,
+                                  size_t workspace_bytes, void* out);
+
+/* isb_select_attend_prefill - isb_select_attend for a prefill batch. */
+ISB_API int isb_select_attend_prefill(isb_stream_t stream, const float* scores, int num_reqs,
+                                      const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                      int num_tokens, int num_kv_heads, int max_blocks, int top_k,
+                                      const int32_t* block_table, int block_table_stride,
+                                      const void* q, int q_dtype, const void* k_pool,
+                                      const void* v_pool, int kv_dtype, int64_t num_pages,
+                                      float k_scale, float v_scale, int num_q_heads, float sm_scale,
+                                      void* workspace, size_t workspace_bytes, int32_t* topk_idx,
+                                      int32_t* sparse_bt, int32_t* sparse_ctx, void* out);
+
+/*
  * The optional QK-norm and rope of the fused cache writer (ROCm/ATOM PR 2962,
  * Follow-ups: the fused QK-norm / rope / cache writer; the pages give none of
  * the step's parameters, so the caller does).  For one 128-dim head vector x

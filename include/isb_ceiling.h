@@ -44,8 +44,9 @@ ISB_API int isb_ceiling_index_gather(isb_stream_t stream, const void* idx_pool, 
 
 /*
  * The K and V pages isb_sparse_pa_decode reads for these arguments, in its
- * grid (rows, splits) and split plan, each wave's pages of a round issued at
- * once, with the cache policy the call takes for decode_query_len.
+ * grid and plan (rows x splits workgroups, or one wave a row for batches of
+ * many rows of 16-token pages), each wave's pages of a round issued at once,
+ * with the cache policy the call takes for decode_query_len.
  *   out  >= isb_ceiling_attention_words(...) uint32 words, one per wave.
  */
 ISB_API int isb_ceiling_attention_gather(isb_stream_t stream, const void* k_pool, const void* v_pool,

@@ -103,6 +103,14 @@ _SIGNATURES = {
     "isb_prepare_query": ([_P, _P, _I, _P, _I, _I, _NR, _I, _P], _I),
     "isb_topk_merge": ([_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
     "isb_quantize_e4m3": ([_P, _P, _I64, _P], _I),
+    "isb_index_score_prefill": ([_P, _P, _I, _I, _P, _I, _F, _I64, _P, _I, _I, _P, _P, _I, _I, _I, _P], _I),
+    "isb_topk_select_prefill": ([_P, _P, _I, _P, _P, _I, _I, _I, _I, _P], _I),
+    "isb_emit_sparse_block_table_prefill": ([_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "isb_topk_select_emit_prefill": ([_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P], _I),
+    "isb_sparse_pa_prefill": ([_P, _P, _I, _P, _P, _I, _I64, _F, _F, _P, _I, _P, _I, _I, _I, _I, _F, _P, _SZ,
+                               _P], _I),
+    "isb_select_attend_prefill": ([_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _I, _I64, _F, _F,
+                                   _I, _F, _P, _SZ, _P, _P, _P, _P], _I),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -438,6 +446,174 @@ def select_attend(scores, seq_lens, decode_query_len, top_k, block_table, q, q_d
     return topk_idx, sparse_bt, sparse_ctx, out
 
 
+# ---------------------------------------------------------------- prefill batches
+def _check_tokens(query_req_id, query_abs_pos, block_table) -> int:
+    """Per-token request ids and positions, int32 [T]; block_table int32
+    [num_reqs, stride].  Returns T."""
+    _check_int32(query_req_id=query_req_id, query_abs_pos=query_abs_pos, block_table=block_table)
+    if query_req_id.dim() != 1 or query_abs_pos.shape != query_req_id.shape:
+        raise ValueError("query_req_id and query_abs_pos must be int32 [num_tokens]")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [num_reqs, stride]")
+    return int(query_req_id.shape[0])
+
+
+def _check_prefill_scores(scores, T):
+    if scores.dtype != torch.float32 or scores.dim() != 3 or scores.shape[1] != T:
+        raise ValueError(f"scores must be float32 [num_kv_heads, {T}, max_blocks]")
+    return scores.shape
+
+
+def index_score_prefill(q_idx, q_idx_dtype, idx_pool, idx_dtype, idx_scale, block_table, query_req_id,
+                        query_abs_pos, num_kv_heads, max_blocks, scores=None):
+    """Block scores [num_kv_heads, T, max_blocks] fp32 of a prefill batch (see
+    isb_index_score_prefill)."""
+    T = _check_tokens(query_req_id, query_abs_pos, block_table)
+    H_idx = q_idx.shape[1]
+    _check_idx_pool(idx_pool, idx_dtype)
+    _check_query("q_idx", q_idx, q_idx_dtype, T, H_idx)
+    dev = _dev(q_idx, idx_pool, block_table, query_req_id, query_abs_pos)
+    if scores is None:
+        scores = torch.empty((num_kv_heads, T, max_blocks), dtype=torch.float32, device=dev)
+    _dev(scores)
+    if scores.dtype != torch.float32:
+        raise ValueError("scores must be float32")
+    _check_shape("scores", scores, (num_kv_heads, T, max_blocks))
+    _call("index_score_prefill", _stream(dev), q_idx.data_ptr(), _code(q_idx_dtype), H_idx,
+          idx_pool.data_ptr(), _code(idx_dtype), float(idx_scale), idx_pool.shape[0], block_table.data_ptr(),
+          block_table.shape[1], block_table.shape[0], query_req_id.data_ptr(), query_abs_pos.data_ptr(), T,
+          num_kv_heads, max_blocks, scores.data_ptr())
+    return scores
+
+
+def topk_select_prefill(scores, num_reqs, query_req_id, query_abs_pos, top_k, topk_idx=None):
+    """Selections [num_kv_heads, T, top_k] int32 of a prefill batch (see
+    isb_topk_select_prefill)."""
+    _check_int32(query_req_id=query_req_id, query_abs_pos=query_abs_pos)
+    T = int(query_req_id.shape[0])
+    H_kv, _, MB = _check_prefill_scores(scores, T)
+    dev = _dev(scores, query_req_id, query_abs_pos)
+    if topk_idx is None:
+        topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
+    _dev(topk_idx)
+    _check_int32(topk_idx=topk_idx)
+    _check_shape("topk_idx", topk_idx, (H_kv, T, top_k))
+    _call("topk_select_prefill", _stream(dev), scores.data_ptr(), int(num_reqs), query_req_id.data_ptr(),
+          query_abs_pos.data_ptr(), T, H_kv, MB, top_k, topk_idx.data_ptr())
+    return topk_idx
+
+
+def emit_sparse_block_table_prefill(topk_idx, block_table, query_req_id, query_abs_pos, pages_per_block,
+                                    sparse_bt=None, sparse_ctx=None):
+    """(sparse_bt [T*H_kv, K*ppb], sparse_ctx [T*H_kv]) int32 of a prefill batch
+    (see isb_emit_sparse_block_table_prefill)."""
+    T = _check_tokens(query_req_id, query_abs_pos, block_table)
+    _check_int32(topk_idx=topk_idx)
+    H_kv, Tk, K = topk_idx.shape
+    if Tk != T:
+        raise ValueError("topk_idx must have one row per token")
+    dev = _dev(topk_idx, block_table, query_req_id, query_abs_pos)
+    if sparse_bt is None:
+        sparse_bt = torch.empty((T * H_kv, K * pages_per_block), dtype=torch.int32, device=dev)
+    if sparse_ctx is None:
+        sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
+    _dev(sparse_bt, sparse_ctx)
+    _check_int32(sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    _check_shape("sparse_bt", sparse_bt, (T * H_kv, K * pages_per_block))
+    _check_shape("sparse_ctx", sparse_ctx, (T * H_kv,))
+    _call("emit_sparse_block_table_prefill", _stream(dev), topk_idx.data_ptr(), block_table.data_ptr(),
+          block_table.shape[1], block_table.shape[0], query_req_id.data_ptr(), query_abs_pos.data_ptr(), T,
+          H_kv, K, pages_per_block, sparse_bt.data_ptr(), sparse_ctx.data_ptr())
+    return sparse_bt, sparse_ctx
+
+
+def topk_select_emit_prefill(scores, query_req_id, query_abs_pos, top_k, block_table, pages_per_block,
+                             topk_idx=None, sparse_bt=None, sparse_ctx=None):
+    """(topk_idx, sparse_bt, sparse_ctx) of a prefill batch in one launch (see
+    isb_topk_select_emit_prefill)."""
+    T = _check_tokens(query_req_id, query_abs_pos, block_table)
+    H_kv, _, MB = _check_prefill_scores(scores, T)
+    dev = _dev(scores, block_table, query_req_id, query_abs_pos)
+    if topk_idx is None:
+        topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
+    if sparse_bt is None:
+        sparse_bt = torch.empty((T * H_kv, top_k * pages_per_block), dtype=torch.int32, device=dev)
+    if sparse_ctx is None:
+        sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
+    _dev(topk_idx, sparse_bt, sparse_ctx)
+    _check_int32(topk_idx=topk_idx, sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    _check_shape("topk_idx", topk_idx, (H_kv, T, top_k))
+    _check_shape("sparse_bt", sparse_bt, (T * H_kv, top_k * pages_per_block))
+    _check_shape("sparse_ctx", sparse_ctx, (T * H_kv,))
+    _call("topk_select_emit_prefill", _stream(dev), scores.data_ptr(), block_table.shape[0],
+          query_req_id.data_ptr(), query_abs_pos.data_ptr(), T, H_kv, MB, top_k, block_table.data_ptr(),
+          block_table.shape[1], pages_per_block, topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr())
+    return topk_idx, sparse_bt, sparse_ctx
+
+
+def sparse_pa_prefill(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, sparse_bt, sparse_ctx,
+                      num_q_heads, num_kv_heads, sm_scale, out=None, workspace=None):
+    """Attention output [T, num_q_heads, 128] bf16 for the rows of a prefill
+    batch (see isb_sparse_pa_prefill)."""
+    T = q.shape[0]
+    num_pages = _check_kv_pools(k_pool, v_pool, kv_dtype, num_kv_heads)
+    _check_query("q", q, q_dtype, T, num_q_heads)
+    _check_int32(sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    if sparse_bt.dim() != 2 or sparse_bt.shape[0] != T * num_kv_heads:
+        raise ValueError(f"sparse_bt must be int32 [{T * num_kv_heads}, stride]")
+    _check_shape("sparse_ctx", sparse_ctx, (T * num_kv_heads,))
+    dev = _dev(q, k_pool, v_pool, sparse_bt, sparse_ctx)
+    stride = sparse_bt.shape[1]
+    need = sparse_pa_workspace_bytes(T, num_q_heads, num_kv_heads, stride, kv_dtype)
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    if out is None:
+        out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    _dev(out, workspace)
+    _check_out(out, T, num_q_heads)
+    _call("sparse_pa_prefill", _stream(dev), q.data_ptr(), _code(q_dtype), k_pool.data_ptr(),
+          v_pool.data_ptr(), _code(kv_dtype), num_pages, float(k_scale), float(v_scale), sparse_bt.data_ptr(),
+          stride, sparse_ctx.data_ptr(), T, num_q_heads, num_kv_heads, 128, float(sm_scale),
+          workspace.data_ptr(), workspace.numel(), out.data_ptr())
+    return out
+
+
+def select_attend_prefill(scores, query_req_id, query_abs_pos, top_k, block_table, q, q_dtype, k_pool, v_pool,
+                          kv_dtype, k_scale, v_scale, num_q_heads, sm_scale, topk_idx=None, sparse_bt=None,
+                          sparse_ctx=None, out=None, workspace=None):
+    """(topk_idx, sparse_bt, sparse_ctx, out) of a prefill batch (see
+    isb_select_attend_prefill)."""
+    T = _check_tokens(query_req_id, query_abs_pos, block_table)
+    H_kv, _, MB = _check_prefill_scores(scores, T)
+    num_pages = _check_kv_pools(k_pool, v_pool, kv_dtype, H_kv)
+    _check_query("q", q, q_dtype, T, num_q_heads)
+    dev = _dev(scores, block_table, query_req_id, query_abs_pos, q, k_pool, v_pool)
+    ppb = 1 if _code(kv_dtype) == DTYPE_CODES["mxfp4"] else 8
+    if topk_idx is None:
+        topk_idx = torch.empty((H_kv, T, top_k), dtype=torch.int32, device=dev)
+    if sparse_bt is None:
+        sparse_bt = torch.empty((T * H_kv, top_k * ppb), dtype=torch.int32, device=dev)
+    if sparse_ctx is None:
+        sparse_ctx = torch.empty((T * H_kv,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((T, num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    need = sparse_pa_workspace_bytes(T, num_q_heads, H_kv, top_k * ppb, kv_dtype)
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    _dev(topk_idx, sparse_bt, sparse_ctx, out, workspace)
+    _check_int32(topk_idx=topk_idx, sparse_bt=sparse_bt, sparse_ctx=sparse_ctx)
+    _check_shape("topk_idx", topk_idx, (H_kv, T, top_k))
+    _check_shape("sparse_bt", sparse_bt, (T * H_kv, top_k * ppb))
+    _check_shape("sparse_ctx", sparse_ctx, (T * H_kv,))
+    _check_out(out, T, num_q_heads)
+    _call("select_attend_prefill", _stream(dev), scores.data_ptr(), block_table.shape[0], query_req_id.data_ptr(),
+          query_abs_pos.data_ptr(), T, H_kv, MB, top_k, block_table.data_ptr(), block_table.shape[1], q.data_ptr(),
+          _code(q_dtype), k_pool.data_ptr(), v_pool.data_ptr(), _code(kv_dtype), num_pages, float(k_scale),
+          float(v_scale), num_q_heads, float(sm_scale), workspace.data_ptr(), workspace.numel(),
+          topk_idx.data_ptr(), sparse_bt.data_ptr(), sparse_ctx.data_ptr(), out.data_ptr())
+    return topk_idx, sparse_bt, sparse_ctx, out
+
+
 def write_cache(k_new, v_new, idx_new, block_table, seq_lens, decode_query_len, k_pool, v_pool, kv_dtype,
                 k_scale, v_scale, idx_pool=None, idx_dtype="bf16", idx_scale=1.0, k_norm_rope=None,
                 idx_norm_rope=None):
@@ -557,6 +733,36 @@ class DecodeLayer:
         return self.out
 
 
+class PrefillLayer:
+    """One sparse prefill layer over a ragged batch (per-token request ids and
+    positions) of a workload's requests: index_score_prefill, then
+    select_attend_prefill, with persistent outputs, as DecodeLayer."""
+
+    def __init__(self, w, batch):
+        cfg = w.cfg
+        self.w, self.b = w, batch
+        dev = w.q.device
+        T = batch.num_tokens
+        self.scores = torch.empty((cfg.num_kv_heads, T, cfg.max_blocks), dtype=torch.float32, device=dev)
+        self.topk = torch.empty((cfg.num_kv_heads, T, cfg.top_k), dtype=torch.int32, device=dev)
+        ppb = cfg.pages_per_block
+        self.sparse_bt = torch.empty((T * cfg.num_kv_heads, cfg.top_k * ppb), dtype=torch.int32, device=dev)
+        self.sparse_ctx = torch.empty((T * cfg.num_kv_heads,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, cfg.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+        need = sparse_pa_workspace_bytes(T, cfg.num_q_heads, cfg.num_kv_heads, cfg.top_k * ppb, cfg.kv_dtype)
+        self.workspace = new_workspace(need, dev)
+
+    def run(self):
+        w, b, cfg = self.w, self.b, self.w.cfg
+        index_score_prefill(b.q_idx, cfg.qidx_dtype, w.idx_pool, cfg.idx_dtype, w.idx_scale, w.block_table,
+                            b.query_req_id, b.query_abs_pos, cfg.num_kv_heads, cfg.max_blocks, scores=self.scores)
+        select_attend_prefill(self.scores, b.query_req_id, b.query_abs_pos, cfg.top_k, w.block_table, b.q,
+                              cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale, cfg.num_q_heads,
+                              w.sm_scale, topk_idx=self.topk, sparse_bt=self.sparse_bt, sparse_ctx=self.sparse_ctx,
+                              out=self.out, workspace=self.workspace)
+        return self.out
+
+
 # C names, for callers that prefer them.
 isb_index_score = index_score
 isb_topk_select = topk_select
@@ -566,3 +772,9 @@ isb_select_attend = select_attend
 isb_sparse_pa_decode = sparse_pa_decode
 isb_sparse_pa_decode_noalloc = sparse_pa_decode_noalloc
 isb_sparse_pa_workspace_bytes = sparse_pa_workspace_bytes
+isb_index_score_prefill = index_score_prefill
+isb_topk_select_prefill = topk_select_prefill
+isb_emit_sparse_block_table_prefill = emit_sparse_block_table_prefill
+isb_topk_select_emit_prefill = topk_select_emit_prefill
+isb_sparse_pa_prefill = sparse_pa_prefill
+isb_select_attend_prefill = select_attend_prefill

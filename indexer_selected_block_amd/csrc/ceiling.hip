@@ -167,6 +167,59 @@ void launch_gather16(const AttArgs& a, dim3 grid, int nw, hipStream_t st) {
   else hipLaunchKernelGGL((attention_gather16_kernel<PB, RUN, NT, 4>), grid, dim3(256), 0, st, a);
 }
 
+// The row_wave plan: grid (ceil(rows / 4)), wave w of workgroup x takes row
+// 4 grid_row(x) + w alone and walks its runs in order, each run's loads
+// issued at once as in the attention kernel.
+template <int PB, int RUN, bool NT>
+__global__ __launch_bounds__(256) void attention_gather16_row_kernel(AttArgs a, int rows) {
+  constexpr int IDS = 64 / RUN;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int row = 4 * grid_row(blockIdx.x, gridDim.x) + wave;
+  if (row >= rows) return;
+  const int kvh = row % a.H_kv;
+  const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
+  auto ids = [&](int r0) {
+    const int pidx = r0 * RUN + lane;
+    return pidx < a.sbt_stride ? pages[pidx] : -1;
+  };
+  int my_ids = ids(0);
+  const int n_tok = a.sctx[row];
+  uint32_t acc = 0;
+  const int npages = min((n_tok + 15) / 16, a.sbt_stride);
+  const int nruns = (npages + RUN - 1) / RUN;
+  const int64_t hstride = (int64_t)a.H_kv * PB, hoff = (int64_t)kvh * PB;
+  for (int r = 0; r < nruns; ++r) {
+    if (r > 0 && r % IDS == 0) my_ids = ids(r);
+    const int cnt = min(RUN, npages - r * RUN);
+    const int ibase = (r % IDS) * RUN;
+    PageData<PB> k[RUN], v[RUN];
+    int64_t use[RUN];
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      const int64_t id = __builtin_amdgcn_readlane(my_ids, ibase + (j < cnt ? j : 0));
+      use[j] = (id >= 0 && id < a.num_pages ? id : 0) * hstride + hoff;
+      load_page<PB, NT>(k[j], page_rsrc(a.kp + use[j], PB), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      load_page<PB, NT>(v[j], page_rsrc(a.vp + use[j], PB), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < RUN; ++j)
+      if (j < cnt) acc ^= fold_page<PB>(k[j]) ^ fold_page<PB>(v[j]);
+  }
+  acc ^= __shfl_xor(acc, 1);
+  if (lane == 0) a.out[row] = acc;
+}
+
+template <int PB, int RUN, bool NT>
+void launch_gather16_rows(const AttArgs& a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL((attention_gather16_row_kernel<PB, RUN, NT>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     st, a, rows);
+}
+
 // MXFP4 pages: one 8704 B page of K and one of V a wave, page p0 + wave of
 // the split.
 __global__ __launch_bounds__(256) void attention_gather_mx_kernel(AttArgs a) {
@@ -225,7 +278,7 @@ extern "C" size_t isb_ceiling_attention_words(int num_tokens, int num_kv_heads, 
   using namespace isb;
   if (num_tokens <= 0 || num_kv_heads <= 0 || sparse_bt_stride <= 0 || !is_pool_dtype(kv_dtype)) return 0;
   const PaPlan p = pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype);
-  return (size_t)p.rows * p.splits * p.waves;
+  return p.row_wave ? (size_t)p.rows : (size_t)p.rows * p.splits * p.waves;
 }
 
 extern "C" int isb_ceiling_attention_gather(isb_stream_t stream, const void* k_pool, const void* v_pool,
@@ -241,12 +294,22 @@ extern "C" int isb_ceiling_attention_gather(isb_stream_t stream, const void* k_p
   if (num_tokens % decode_query_len != 0 || (long long)num_tokens * num_kv_heads > 0x7FFFFFFFLL) return ISB_E_SHAPE;
   const PaPlan p = pa_plan(num_tokens, num_kv_heads, sparse_bt_stride, kv_dtype);
   if (p.splits > 65535) return ISB_E_SHAPE;
-  if (out_words < (size_t)p.rows * p.splits * p.waves) return ISB_E_WORKSPACE;
+  if (out_words < (p.row_wave ? (size_t)p.rows : (size_t)p.rows * p.splits * p.waves)) return ISB_E_WORKSPACE;
   AttArgs a{(const uint8_t*)k_pool, (const uint8_t*)v_pool, sparse_bt, sparse_ctx, out, num_pages, sparse_bt_stride,
             num_kv_heads, p.pages_per_split};
   hipStream_t st = as_hip(stream);
   const dim3 grid((unsigned)p.rows, p.splits);
   const bool nt = decode_query_len == 1;
+  if (p.row_wave) {  // 16-token pages only
+    if (kv_dtype == ISB_FP8_E4M3) {
+      if (nt) launch_gather16_rows<2048, 8, true>(a, p.rows, st);
+      else launch_gather16_rows<2048, 8, false>(a, p.rows, st);
+    } else {
+      if (nt) launch_gather16_rows<4096, 4, true>(a, p.rows, st);
+      else launch_gather16_rows<4096, 4, false>(a, p.rows, st);
+    }
+    return launch_status();
+  }
   if (kv_dtype == ISB_MXFP4) {
     hipLaunchKernelGGL(attention_gather_mx_kernel, grid, dim3(256), 0, st, a);
   } else if (kv_dtype == ISB_FP8_E4M3) {

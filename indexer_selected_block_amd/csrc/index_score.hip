@@ -43,14 +43,14 @@ struct ScoreArgs {
   const uint8_t* q_idx;
   const uint8_t* pool;
   const int32_t* bt;
-  const int32_t* seq_lens;
+  const int32_t* seq_lens;  // decode batches
   float* scores;
   int64_t pool_blocks;
   float idx_scale;
   int H_idx, bt_stride, R, q_len, H_kv, MB;
+  TokenMap tm;  // wide variant: each token's request and causal length (both batch forms)
+  int T;        // query tokens
 };
-
-
 
 constexpr int kMaxQueryRows = 64;     // q_len * H_idx of the tile / stream variants
 constexpr long long kMaxWideRows = 1 << 20;  // q_len * H_idx of the wide variant
@@ -471,77 +471,169 @@ __device__ __forceinline__ void wide_part_max(const PartOps<KEY_DT, Q_DT>& k, in
   }
 }
 
-// grid (ceil(MB / 4), R, ceil(QR / (16 kWideTiles))), 4 waves a workgroup:
-// wave w scores block 4 x + w of request y for query rows
-// [16 kWideTiles z, 16 kWideTiles (z + 1)), which the workgroup stages in
-// LDS.  Needs 16 % H_idx == 0, so a 16-row tile holds whole tokens (row n =
-// token n / H_idx, head n % H_idx) and each KV group's index heads sit on
-// adjacent lanes.
+// Tiles that hold tokens of several requests: the rows of 16-row tile
+// [16 q, 16 q + 16) (this lane's row is token `tok`, -1 past the tile) against
+// block b of every run of the tile's tokens [k_begin, ntok) after the first,
+// folded into `best`.  Each run reads its block again for every 16-row tile
+// it has rows in.  Kept out of line (few registers), so that the kernel's
+// single-run path keeps four waves a SIMD.
+template <int KEY_DT, int Q_DT>
+__device__ __attribute__((noinline)) float wide_other_runs(const uint8_t* pool, int64_t pool_blocks,
+                                                           const int32_t* bt, int bt_stride, const int* s_req,
+                                                           const int* s_len, const uint8_t* qrow, int b, int k_begin,
+                                                           int ntok, int tok, int tlo, int thi, float best) {
+  constexpr int NT = wide_part_tiles<KEY_DT>();
+  constexpr int PARTS = 8 / NT;
+  constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
+  const int lane = threadIdx.x & 63;
+  for (int k0 = k_begin, k1 = 0; k0 < ntok; k0 = k1) {
+    const int rr = __builtin_amdgcn_readfirstlane(s_req[k0]);
+    k1 = ntok;
+    for (int base = k0 + 1; base < ntok; base += kWave) {
+      const int k = base + lane;
+      const uint64_t diff = __ballot(k < ntok && s_req[k] != rr);
+      if (diff) {
+        k1 = base + __builtin_ctzll(diff);
+        break;
+      }
+    }
+    if (k1 <= tlo || k0 > thi) continue;  // no row of this 16-row tile in the run
+    const bool in = tok >= k0 && tok < k1;
+    const int v = in ? s_len[tok] - b * kBlockTokens : 0;
+    const int nv = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
+    if (!__ballot(nv > 0)) continue;  // none of its rows reaches block b
+    const int64_t blk = __builtin_amdgcn_readfirstlane(bt[(size_t)rr * bt_stride + b]);
+    if (blk < 0 || blk >= pool_blocks) {  // poison block id: nothing is read through it
+      if (nv > 0) best = qnan();
+      continue;
+    }
+    const __amdgpu_buffer_rsrc_t page = page_rsrc(pool + blk * PB, (int)PB);
+#pragma unroll 1
+    for (int part = 0; part < PARTS; ++part) {
+      PartRaw<KEY_DT> raw;
+      load_part_raw<KEY_DT>(raw, page, part, lane);
+      PartOps<KEY_DT, Q_DT> ops;
+      part_operands<KEY_DT, Q_DT>(raw, lane, ops);
+      wide_part_max<KEY_DT, Q_DT>(ops, part, qrow, false, nv, lane, best);
+    }
+  }
+  return best;
+}
+
+// Wave-uniform maximum of an int over the wave.
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off, kWave));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// grid (ceil(MB / 4), tiles[, tiles a request]), 4 waves a workgroup: wave w
+// scores block 4 x + w (x from score_column) for the query rows [n0, n1) of
+// the workgroup's tile, which it stages in LDS.  Global query row n = t H_idx
+// + h (token t, index head h).  Tiles of a decode batch (grid (., R, z)):
+// rows [r QR + 128 z, ..) of request r, QR = q H_idx; of a prefill batch
+// (grid (., tiles)): rows [128 y, 128 y + 128) of the whole batch.  The tile's
+// tokens are taken in runs of consecutive tokens of one request (one run
+// whenever a tile holds one request's tokens); each run scores its request's
+// block b against its own rows.  Needs 16 % H_idx == 0, so a 16-row tile
+// holds whole tokens and each KV group's index heads sit on adjacent lanes.
 template <int KEY_DT, int Q_DT>
 __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   constexpr int NT = wide_part_tiles<KEY_DT>();
   constexpr int PARTS = 8 / NT;
   constexpr int QROW = Q_DT == ISB_BF16 ? 2 * kHeadDim : kHeadDim;  // bytes of a query row
+  constexpr int TROWS = 16 * kWideTiles;                            // rows of a tile
   // LDS pitch of a staged row: 16 bytes past a multiple of 256 puts the 16
   // rows a 16-byte read of a tile touches on distinct banks
   constexpr int QPITCH = QROW + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[16 * kWideTiles * QPITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[TROWS * QPITCH];
+  __shared__ int s_req[TROWS];  // per token of the tile: request and causal length
+  __shared__ int s_len[TROWS];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int m = lane & 15;
-  const int r = blockIdx.y;
-  const int QR = a.q_len * a.H_idx;
-  const int n0 = 16 * kWideTiles * blockIdx.z;   // first query row of this workgroup
-  const int n1 = min(QR, n0 + 16 * kWideTiles);  // one past the last
+  const bool prefill = a.tm.req_id != nullptr;
+  int n0, n1, rot;
+  if (prefill) {
+    n0 = TROWS * blockIdx.y;
+    n1 = min(a.T * a.H_idx, n0 + TROWS);
+    rot = blockIdx.y;
+  } else {
+    const int QR = a.q_len * a.H_idx;
+    n0 = blockIdx.y * QR + TROWS * blockIdx.z;
+    n1 = min((int)blockIdx.y * QR + QR, n0 + TROWS);
+    rot = blockIdx.y;
+  }
   const int per = a.H_idx / a.H_kv;  // index heads of a KV group
   // H_idx divides 16 and per divides H_idx: both are powers of two, so the
   // row -> (token, head) and head -> group splits are shifts and masks
   const int hsh = __builtin_ctz(a.H_idx), psh = __builtin_ctz(per);
-  const int T = a.R * a.q_len;
-  const int L = a.seq_lens[r];
-  const int nr = (L + kBlockTokens - 1) / kBlockTokens;
-  const int col = score_column<kScoreWaves>(blockIdx.x, gridDim.x, blockIdx.y);
+  const int t0 = n0 >> hsh;                  // first token of the tile
+  const int ntok = ((n1 - 1) >> hsh) - t0 + 1;  // its tokens
+  const int col = score_column<kScoreWaves>(blockIdx.x, gridDim.x, rot);
   const int b = col * kScoreWaves + wave;
-  // -inf for every token of this workgroup's rows at block b (no token of the
-  // request reaches it)
+  // -inf for every token of the tile at block b (none of them reaches it)
   auto write_unreached = [&]() {
-    const int i0 = n0 >> hsh, i1 = n1 >> hsh;
-    for (int x = lane; x < (i1 - i0) * a.H_kv; x += kWave) {
-      const int i = i0 + x / a.H_kv, gg = x % a.H_kv;
-      a.scores[((size_t)gg * T + (size_t)r * a.q_len + i) * a.MB + b] = neg_inf();
+    for (int x = lane; x < ntok * a.H_kv; x += kWave) {
+      const int k = x / a.H_kv, gg = x % a.H_kv;
+      a.scores[((size_t)gg * a.T + t0 + k) * a.MB + b] = neg_inf();
     }
   };
-  if (col * kScoreWaves >= nr) {  // all four blocks past the request's end (uniform over the workgroup)
-    if (b < a.MB) write_unreached();
-    return;
-  }
-  const bool live = b < nr && b < a.MB;
-  int64_t blk = 0;
-  if (live) blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r * a.bt_stride + b]);
+  // The first token's block is requested before anything else, so that one
+  // round trip covers its keys, the tile's token data and the query rows.
+  const TokenPos tp0 = token_pos(a.tm, t0);
+  const bool pre = b < a.MB && b * kBlockTokens < tp0.L;
+  int64_t blk0 = 0;
+  if (pre) blk0 = __builtin_amdgcn_readfirstlane(a.bt[(size_t)tp0.r * a.bt_stride + b]);
+  constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
   // an out-of-range block id is poison: NaN where the block is causally
   // visible, -inf elsewhere; nothing is read through it
-  const bool bad = blk < 0 || blk >= a.pool_blocks;
-  constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
-  const __amdgpu_buffer_rsrc_t page = page_rsrc(a.pool + (bad ? 0 : blk) * PB, (int)PB);
-  // the first part of the keys is requested before the query rows, so one
-  // round trip covers both
+  const bool bad0 = blk0 < 0 || blk0 >= a.pool_blocks;
   PartRaw<KEY_DT> raw;
-  if (live) load_part_raw<KEY_DT>(raw, page, 0, lane);
-  // The four waves score four blocks against the same query rows: the rows
-  // (contiguous in q_idx: row n of request r is row r QR + n) are staged in
-  // LDS once, as stored.
+  if (pre) load_part_raw<KEY_DT>(raw, page_rsrc(a.pool + (bad0 ? 0 : blk0) * PB, (int)PB), 0, lane);
   {
-    const uint8_t* src = a.q_idx + ((size_t)r * QR + n0) * QROW;
+    const uint8_t* src = a.q_idx + (size_t)n0 * QROW;
     constexpr int CPR = QROW / 16;  // 16-byte chunks a row
     for (int c = threadIdx.x; c < (n1 - n0) * CPR; c += 256)
       *reinterpret_cast<u32x4*>(s_q + (c / CPR) * QPITCH + (c % CPR) * 16) = ld16(src + (size_t)c * 16);
+    for (int k = threadIdx.x; k < ntok; k += 256) {
+      const TokenPos tp = token_pos(a.tm, t0 + k);
+      s_req[k] = tp.r;
+      s_len[k] = tp.L;
+    }
   }
   __syncthreads();
+  // blocks the tile's tokens reach (the same in every wave)
+  int nb = 0;
+  for (int k = lane; k < ntok; k += kWave) nb = max(nb, (s_len[k] + kBlockTokens - 1) / kBlockTokens);
+  const int nmax = wave_max_int(nb);
   if (b >= a.MB) return;
-  if (b >= nr) {
+  if (b >= nmax) {
     write_unreached();
     return;
   }
-  // row n = n0 + 16 q + m of each tile q: its causally valid keys in this block
+  // The first run of the tile: its tokens [0, k1) (all of them when the tile
+  // holds one request's tokens).
+  int k1 = ntok;
+  for (int base = 1; base < ntok; base += kWave) {
+    const int k = base + lane;
+    const uint64_t diff = __ballot(k < ntok && s_req[k] != tp0.r);
+    if (diff) {
+      k1 = base + __builtin_ctzll(diff);
+      break;
+    }
+  }
+  int nr = 0;  // blocks the first run's tokens reach
+  for (int k = lane; k < k1; k += kWave) nr = max(nr, (s_len[k] + kBlockTokens - 1) / kBlockTokens);
+  nr = wave_max_int(nr);
+  int64_t blk = blk0;
+  bool bad = bad0;
+  if (!pre && b < nr) {  // a later token of the first run reaches block b
+    blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)tp0.r * a.bt_stride + b]);
+    bad = blk < 0 || blk >= a.pool_blocks;
+    if (!bad) load_part_raw<KEY_DT>(raw, page_rsrc(a.pool + blk * PB, (int)PB), 0, lane);
+  }
+  // row n = n0 + 16 q + m of each tile q: its causally valid keys in this
+  // block if its token is in the first run (0 otherwise)
   float best[kWideTiles];
   int nv[kWideTiles];
   const uint8_t* qrow[kWideTiles];  // this lane's staged query row of tile q
@@ -549,23 +641,44 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
     const int n = n0 + 16 * q + m;
-    const int v = n < n1 ? causal_len(L, a.q_len, n >> hsh) - b * kBlockTokens : 0;
+    const int k = (n >> hsh) - t0;
+    const int v = n < n1 && k < k1 ? s_len[k] - b * kBlockTokens : 0;
     nv[q] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
     best[q] = neg_inf();
     qrow[q] = s_q + ((n < n1 ? n : n0) - n0) * QPITCH;
-    // rows grow in causal length down the tile: its first row (lane 0) sees
-    // the fewest keys
-    if (__builtin_amdgcn_readfirstlane(nv[q]) == kBlockTokens) full |= 1u << q;
+    if (__ballot(nv[q] == kBlockTokens) == ~0ull) full |= 1u << q;
   }
+  if (b < nr) {
+    if (bad) {
 #pragma unroll
-  for (int part = 0; part < PARTS; ++part) {
-    PartOps<KEY_DT, Q_DT> ops;
-    part_operands<KEY_DT, Q_DT>(raw, lane, ops);
-    if (part + 1 < PARTS) load_part_raw<KEY_DT>(raw, page, part + 1, lane);  // in flight during this part
+      for (int q = 0; q < kWideTiles; ++q)
+        if (nv[q] > 0) best[q] = qnan();
+    } else {
+      const __amdgpu_buffer_rsrc_t page = page_rsrc(a.pool + blk * PB, (int)PB);
 #pragma unroll
-    for (int q = 0; q < kWideTiles; ++q)
-      if (n0 + 16 * q < n1)  // wave-uniform: the tile has rows
-        wide_part_max<KEY_DT, Q_DT>(ops, part, qrow[q], (full >> q) & 1u, nv[q], lane, best[q]);
+      for (int part = 0; part < PARTS; ++part) {
+        PartOps<KEY_DT, Q_DT> ops;
+        part_operands<KEY_DT, Q_DT>(raw, lane, ops);
+        if (part + 1 < PARTS) load_part_raw<KEY_DT>(raw, page, part + 1, lane);  // in flight during this part
+#pragma unroll
+        for (int q = 0; q < kWideTiles; ++q)
+          if (n0 + 16 * q < n1 && ((n0 + 16 * q) >> hsh) - t0 < k1)  // wave-uniform: the tile has rows in the run
+            wide_part_max<KEY_DT, Q_DT>(ops, part, qrow[q], (full >> q) & 1u, nv[q], lane, best[q]);
+      }
+    }
+  }
+  if (k1 < ntok) {  // tokens of other requests in the tile (wave-uniform)
+#pragma unroll
+    for (int q = 0; q < kWideTiles; ++q) {
+      const int lo = n0 + 16 * q;
+      if (lo >= n1) continue;
+      const int thi = (min(lo + 16, n1) - 1 - n0) >> hsh;  // last token of the 16-row tile
+      if (thi < k1) continue;
+      const int n = lo + m;
+      best[q] = wide_other_runs<KEY_DT, Q_DT>(a.pool, a.pool_blocks, a.bt, a.bt_stride, s_req, s_len, qrow[q], b,
+                                              k1, ntok, n < n1 ? (n >> hsh) - t0 : -1, (lo - n0) >> hsh, thi,
+                                              best[q]);
+    }
   }
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
@@ -573,14 +686,13 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
     if (n0 + 16 * q >= n1) continue;  // wave-uniform
     float s = nan_max(best[q], shfl_xor_f32(best[q], 16));  // over the four lane groups
     s = nan_max(s, shfl_xor_f32(s, 32));
-    if (bad) s = nv[q] > 0 ? qnan() : neg_inf();
     // sum the group's heads: rows n .. n + per - 1 sit on adjacent lanes
     for (int off = 1; off < per; off <<= 1) s += shfl_xor_f32(s, off);
     if (KEY_DT == ISB_FP8_E4M3) s *= a.idx_scale;
     const int h = n & (a.H_idx - 1);
     if (lane < 16 && n < n1 && (h & (per - 1)) == 0) {
-      const int i = n >> hsh, gg = h >> psh;
-      a.scores[((size_t)gg * T + (size_t)r * a.q_len + i) * a.MB + b] = s;
+      const int gg = h >> psh;
+      a.scores[((size_t)gg * a.T + (n >> hsh)) * a.MB + b] = s;
     }
   }
 }
@@ -644,8 +756,15 @@ static void launch(const ScoreArgs& a, hipStream_t st) {
 
 template <int KEY_DT, int Q_DT>
 static void launch_wide(const ScoreArgs& a, hipStream_t st) {
-  const int QR = a.q_len * a.H_idx;
-  const dim3 grid((a.MB + kScoreWaves - 1) / kScoreWaves, a.R, (QR + 16 * kWideTiles - 1) / (16 * kWideTiles));
+  constexpr int TROWS = 16 * kWideTiles;
+  const unsigned cols = (a.MB + kScoreWaves - 1) / kScoreWaves;
+  dim3 grid;
+  if (a.tm.req_id) {
+    grid = dim3(cols, (unsigned)(((long long)a.T * a.H_idx + TROWS - 1) / TROWS));
+  } else {
+    const int QR = a.q_len * a.H_idx;
+    grid = dim3(cols, a.R, (QR + TROWS - 1) / TROWS);
+  }
   hipLaunchKernelGGL((index_wide_kernel<KEY_DT, Q_DT>), grid, dim3(256), 0, st, a);
 }
 
@@ -666,33 +785,11 @@ static void launch_key(const ScoreArgs& a, bool one_row, bool wide, hipStream_t 
 
 }  // namespace isb
 
-extern "C" int isb_index_score(isb_stream_t stream, const void* q_idx, int q_idx_dtype,
-                               int num_idx_heads, const void* idx_pool, int idx_dtype,
-                               float idx_scale, int64_t idx_pool_blocks,
-                               const int32_t* block_table, int block_table_stride,
-                               const int32_t* seq_lens, int num_reqs, int decode_query_len,
-                               int num_kv_heads, int max_blocks, float* scores) {
-  using namespace isb;
-  if (!q_idx || !idx_pool || !block_table || !seq_lens || !scores) return ISB_E_INVALID_ARG;
-  if (num_idx_heads <= 0 || num_reqs <= 0 || decode_query_len <= 0 || num_kv_heads <= 0 ||
-      max_blocks <= 0 || block_table_stride <= 0 || idx_pool_blocks <= 0)
-    return ISB_E_INVALID_ARG;
-  if (!is_query_dtype(q_idx_dtype) || !is_pool_dtype(idx_dtype)) return ISB_E_UNSUPPORTED_DTYPE;
-  if (num_idx_heads % num_kv_heads != 0 || max_blocks > block_table_stride) return ISB_E_SHAPE;
-  // up to 16 tokens and 64 query rows a request: the tile / stream variants;
-  // more (a prefill chunk): the wide variant, whose 16-row tiles must hold
-  // whole tokens
-  const long long QR = (long long)decode_query_len * num_idx_heads;
-  const bool wide = decode_query_len > 16 || QR > kMaxQueryRows;
-  if (wide && (16 % num_idx_heads != 0 || QR > kMaxWideRows)) return ISB_E_SHAPE;
-  if ((long long)num_reqs * decode_query_len > 0x7FFFFFFFLL) return ISB_E_SHAPE;
-  if (num_reqs > 65535) return ISB_E_SHAPE;
-  if (!(idx_scale > 0.f) && idx_dtype == ISB_FP8_E4M3) return ISB_E_INVALID_ARG;
-  ScoreArgs a{(const uint8_t*)q_idx, (const uint8_t*)idx_pool, block_table, seq_lens, scores,
-              idx_pool_blocks, idx_scale, num_idx_heads, block_table_stride, num_reqs,
-              decode_query_len, num_kv_heads, max_blocks};
-  hipStream_t st = as_hip(stream);
-  const bool one_row = decode_query_len * num_idx_heads == 1;
+namespace isb {
+
+// Dispatch on the key and index-query types.
+static void launch_types(const ScoreArgs& a, int q_idx_dtype, int idx_dtype, bool one_row, bool wide,
+                         hipStream_t st) {
   const bool qb = q_idx_dtype == ISB_BF16;
   if (idx_dtype == ISB_MXFP4) {
     if (qb) launch_key<ISB_MXFP4, ISB_BF16>(a, one_row, wide, st);
@@ -704,5 +801,70 @@ extern "C" int isb_index_score(isb_stream_t stream, const void* q_idx, int q_idx
     if (qb) launch_key<ISB_BF16, ISB_BF16>(a, one_row, wide, st);
     else launch_key<ISB_BF16, ISB_FP8_E4M3>(a, one_row, wide, st);
   }
+}
+
+// Checks shared by the two entry points; 0 or an ISB_E_* code.
+static int check_score(const void* q_idx, int q_idx_dtype, int num_idx_heads, const void* idx_pool, int idx_dtype,
+                       float idx_scale, int64_t idx_pool_blocks, const int32_t* block_table,
+                       int block_table_stride, int num_reqs, int num_kv_heads, int max_blocks, float* scores) {
+  if (!q_idx || !idx_pool || !block_table || !scores) return ISB_E_INVALID_ARG;
+  if (num_idx_heads <= 0 || num_reqs <= 0 || num_kv_heads <= 0 || max_blocks <= 0 || block_table_stride <= 0 ||
+      idx_pool_blocks <= 0)
+    return ISB_E_INVALID_ARG;
+  if (!is_query_dtype(q_idx_dtype) || !is_pool_dtype(idx_dtype)) return ISB_E_UNSUPPORTED_DTYPE;
+  if (num_idx_heads % num_kv_heads != 0 || max_blocks > block_table_stride) return ISB_E_SHAPE;
+  if (!(idx_scale > 0.f) && idx_dtype == ISB_FP8_E4M3) return ISB_E_INVALID_ARG;
+  return ISB_OK;
+}
+
+}  // namespace isb
+
+extern "C" int isb_index_score(isb_stream_t stream, const void* q_idx, int q_idx_dtype,
+                               int num_idx_heads, const void* idx_pool, int idx_dtype,
+                               float idx_scale, int64_t idx_pool_blocks,
+                               const int32_t* block_table, int block_table_stride,
+                               const int32_t* seq_lens, int num_reqs, int decode_query_len,
+                               int num_kv_heads, int max_blocks, float* scores) {
+  using namespace isb;
+  if (!seq_lens || decode_query_len <= 0) return ISB_E_INVALID_ARG;
+  const int err = check_score(q_idx, q_idx_dtype, num_idx_heads, idx_pool, idx_dtype, idx_scale, idx_pool_blocks,
+                              block_table, block_table_stride, num_reqs, num_kv_heads, max_blocks, scores);
+  if (err) return err;
+  // up to 16 tokens and 64 query rows a request: the tile / stream variants;
+  // more (a prefill chunk): the wide variant, whose 16-row tiles must hold
+  // whole tokens
+  const long long QR = (long long)decode_query_len * num_idx_heads;
+  const bool wide = decode_query_len > 16 || QR > kMaxQueryRows;
+  if (wide && (16 % num_idx_heads != 0 || QR > kMaxWideRows)) return ISB_E_SHAPE;
+  if ((long long)num_reqs * decode_query_len > 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  if (wide && (long long)num_reqs * QR > 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  if (num_reqs > 65535) return ISB_E_SHAPE;
+  ScoreArgs a{(const uint8_t*)q_idx, (const uint8_t*)idx_pool, block_table, seq_lens, scores,
+              idx_pool_blocks, idx_scale, num_idx_heads, block_table_stride, num_reqs,
+              decode_query_len, num_kv_heads, max_blocks, decode_map(seq_lens, decode_query_len),
+              num_reqs * decode_query_len};
+  launch_types(a, q_idx_dtype, idx_dtype, decode_query_len * num_idx_heads == 1, wide, as_hip(stream));
+  return launch_status();
+}
+
+extern "C" int isb_index_score_prefill(isb_stream_t stream, const void* q_idx, int q_idx_dtype,
+                                       int num_idx_heads, const void* idx_pool, int idx_dtype,
+                                       float idx_scale, int64_t idx_pool_blocks,
+                                       const int32_t* block_table, int block_table_stride, int num_reqs,
+                                       const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                       int num_tokens, int num_kv_heads, int max_blocks, float* scores) {
+  using namespace isb;
+  if (!query_req_id || !query_abs_pos || num_tokens <= 0) return ISB_E_INVALID_ARG;
+  const int err = check_score(q_idx, q_idx_dtype, num_idx_heads, idx_pool, idx_dtype, idx_scale, idx_pool_blocks,
+                              block_table, block_table_stride, num_reqs, num_kv_heads, max_blocks, scores);
+  if (err) return err;
+  if (16 % num_idx_heads != 0) return ISB_E_SHAPE;
+  const long long rows = (long long)num_tokens * num_idx_heads;
+  if (rows > 0x7FFFFFFFLL || (rows + 16 * kWideTiles - 1) / (16 * kWideTiles) > 65535) return ISB_E_SHAPE;
+  ScoreArgs a{(const uint8_t*)q_idx, (const uint8_t*)idx_pool, block_table, nullptr, scores,
+              idx_pool_blocks, idx_scale, num_idx_heads, block_table_stride, num_reqs,
+              1, num_kv_heads, max_blocks, prefill_map(query_req_id, query_abs_pos, num_reqs, max_blocks),
+              num_tokens};
+  launch_types(a, q_idx_dtype, idx_dtype, false, true, as_hip(stream));
   return launch_status();
 }

@@ -25,6 +25,39 @@ constexpr int kMxPageBytes = kMxDataBytes + 128 * 4;  // 8704
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWave = 64;
 
+// Where query token t stands: the request it belongs to and its causal
+// length L_t (positions 0 .. L_t - 1 of that request are visible to it).
+//  - decode batches (req_id null): token t = r q + i is one of the last q
+//    tokens of request r, L_t = max(0, seq_lens[r] - (q - 1 - i));
+//  - prefill batches (the prefill call of the vLLM API page for
+//    sparse_attention_msa, MiniMaxM3SparseAiterPAImpl.forward): per-token
+//    request ids and 0-based absolute positions, L_t = abs_pos + 1.  A token
+//    whose request id is outside [0, num_reqs) or whose position is outside
+//    [0, max_len) is an empty row (L_t = 0): nothing is read through it.
+struct TokenMap {
+  const int32_t* seq_lens;  // decode: [R]
+  const int32_t* req_id;    // prefill: [T]; null for a decode batch
+  const int32_t* abs_pos;   // prefill: [T]
+  int q_len;                // decode
+  int num_reqs;             // prefill
+  int max_len;              // prefill
+};
+
+struct TokenPos {
+  int r, L;
+};
+
+__device__ __forceinline__ TokenPos token_pos(const TokenMap& m, int t) {
+  if (m.req_id) {
+    const int r = m.req_id[t], p = m.abs_pos[t];
+    const bool ok = r >= 0 && r < m.num_reqs && p >= 0 && p < m.max_len;
+    return TokenPos{ok ? r : 0, ok ? p + 1 : 0};
+  }
+  const int r = t / m.q_len, i = t - r * m.q_len;
+  const int L = m.seq_lens[r] - (m.q_len - 1 - i);
+  return TokenPos{r, L > 0 ? L : 0};
+}
+
 // Index of this thread's wave in the workgroup, as a wave-uniform (scalar)
 // value, so that addresses derived from it live in scalar registers.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

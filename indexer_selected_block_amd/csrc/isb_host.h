@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "isb.h"
+#include "isb_device.h"
 
 namespace isb {
 
@@ -39,6 +40,14 @@ inline int64_t idx_page_bytes(int dt) {
 // workgroups that each read everything they attend in one round.
 constexpr int kPaResidentWaves = 2048;  // 256 CUs x 4 SIMDs x 2 waves
 constexpr int kPaCUs = 256;
+// 16-token-page batches whose rows fill every round of resident waves (at
+// least kPaRowWaveRows of each kPaResidentWaves) give each row one wave of its
+// own (row_wave): the rows of a round are resident together, one wave walks a
+// row's runs in order, and rows of one request, dealt to one die, read the
+// blocks they share through its L2 while they are there.  A last round that
+// is only partly full would leave most of the chip idle for a whole row's
+// runs: such batches keep four waves a row.
+constexpr int kPaRowWaveRows = 2048 - 64;
 
 struct PaPlan {
   int rows;             // num_tokens * num_kv_heads
@@ -48,6 +57,7 @@ struct PaPlan {
   int pages_per_round;  // one run a wave: what a workgroup reads at once
   int pages_per_split;  // a whole number of rounds
   int splits;           // workgroups per row
+  bool row_wave;        // one wave a row, four rows a workgroup, runs in turn
 };
 
 inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, int kv_dtype) {
@@ -56,6 +66,14 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   p.max_pages = sparse_bt_stride;
   p.pages_per_wave = kv_dtype == ISB_MXFP4 ? 1 : kv_dtype == ISB_BF16 ? 4 : 8;
   p.waves = 4;
+  const int last = p.rows % kPaResidentWaves;  // rows of the last round
+  p.row_wave = kv_dtype != ISB_MXFP4 && p.rows >= kPaRowWaveRows && (last == 0 || last >= kPaRowWaveRows);
+  if (p.row_wave) {
+    p.pages_per_round = p.pages_per_wave;
+    p.pages_per_split = p.max_pages;
+    p.splits = 1;
+    return p;
+  }
   const long long runs = (p.max_pages + p.pages_per_wave - 1) / p.pages_per_wave;  // of a whole row
   if (kv_dtype == ISB_FP8_E4M3 && (long long)p.rows * runs <= kPaResidentWaves &&
       (long long)p.rows * ((runs + 7) / 8) >= kPaCUs)
@@ -86,11 +104,29 @@ inline size_t pa_workspace_bytes(const PaPlan& p) {
   return p.splits > 1 ? (size_t)p.rows * p.splits * (kPartialO + kPartialML) * sizeof(float) : 0;
 }
 
-// The standalone emit launch (emit.hip); the fused top-k entry point falls
+// Token maps (isb_device.h) of the two batch forms.  A prefill position is
+// valid below 128 max_blocks (the table width the call reads), and at most
+// 2^31 - 2 so that its causal length fits an int.
+inline TokenMap decode_map(const int32_t* seq_lens, int q_len) {
+  return TokenMap{seq_lens, nullptr, nullptr, q_len, 0, 0};
+}
+inline TokenMap prefill_map(const int32_t* req_id, const int32_t* abs_pos, int num_reqs, int max_blocks) {
+  const long long len = 128LL * max_blocks;
+  return TokenMap{nullptr, req_id, abs_pos, 1, num_reqs, len < 0x7FFFFFFFLL ? (int)len : 0x7FFFFFFF};
+}
+
+// The standalone emit launch (emit.hip); the fused top-k entry points fall
 // back to it for rows too wide for LDS.
 int emit_launch(hipStream_t st, const int32_t* topk_idx, const int32_t* block_table,
-                int block_table_stride, const int32_t* seq_lens, int num_reqs, int decode_query_len,
-                int num_kv_heads, int top_k, int pages_per_block, int32_t* sparse_bt,
-                int32_t* sparse_ctx);
+                int block_table_stride, const TokenMap& tm, int num_tokens, int num_kv_heads,
+                int top_k, int pages_per_block, int32_t* sparse_bt, int32_t* sparse_ctx);
+
+// Top-k and emit in one launch for either batch form (topk_select.hip);
+// the select + attend entry points fall back to it for rows they cannot
+// take in one launch.  Checks the emit arguments; the top-k ones are the
+// caller's.
+int topk_select_emit_run(hipStream_t st, const float* scores, const TokenMap& tm, int T, int num_kv_heads,
+                         int max_blocks, int top_k, const int32_t* block_table, int block_table_stride,
+                         int pages_per_block, int32_t* topk_idx, int32_t* sparse_bt, int32_t* sparse_ctx);
 
 }  // namespace isb

@@ -366,13 +366,107 @@ __device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const
   }
 }
 
+// One run of a wave: pages wb .. wb + cnt - 1 of its row (cnt >= 1, at most
+// RUN), whose ids sit in lanes ibase .. ibase + cnt - 1 of my_ids, folded into
+// the wave's running max M (per head), sum share lsum and output o.  Every
+// load of the run is issued before any math; its logits give one exact max
+// per head, which rescales what earlier runs accumulated if it grew.
+// KEEP: pin MFMA operands live (see mfma_16x16x32_bf16_k).
+template <int KV_DT, int Q_DT, int RUN, bool NT, bool KEEP>
+__device__ __forceinline__ void attend_run16(const PaArgs& a, int lane, int n_tok, int wb, int cnt, int my_ids,
+                                             int ibase, int64_t hstride, int64_t hoff, const bf16x8 (&qb)[4],
+                                             bool first, float& M, float& lsum, f32x4 (&o)[8]) {
+  constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
+  const int g = lane >> 4;
+  // Every load of the run, unconditionally: slots past the run re-read its
+  // first page, an out-of-range id reads page 0 and poisons its tile.  All
+  // K chunks are issued before all V chunks, page by page, and kept in that
+  // order, so the logits of page j wait only for K of pages <= j and P.V of
+  // page j only for V of pages <= j.
+  PageRegs<KV_DT> pr[RUN];
+  bool ok[RUN];
+  int64_t use[RUN];
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    const int64_t id = __builtin_amdgcn_readlane(my_ids, ibase + (j < cnt ? j : 0));
+    ok[j] = page_ok(id, a.num_pages);
+    use[j] = (ok[j] ? id : 0) * hstride + hoff;
+    load_k16<KV_DT, NT>(pr[j], page_rsrc(a.kp + use[j], PB), lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    load_v16<KV_DT, NT>(pr[j], page_rsrc(a.vp + use[j], PB), lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Pass 1: every logit of the run, then one exact max per head.
+  float z[RUN][4];
+  float mx = neg_inf();
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    if (j < cnt) {
+      bf16x8 kb[4];
+      k_operand<KV_DT>(pr[j], kb);
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16_k<KEEP>(kb[x], qb[x], sacc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
+      const int nv = min(16, n_tok - (wb + j) * 16);
+      if (nv < 16) {  // the row's last page: keys past its length do not count
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
+        clear_tail_keys<KV_DT>(pr[j], nv, g);
+      }
+      if (!ok[j]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[j][e] = qnan();
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, z[j][e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[j][e] = neg_inf();
+    }
+  }
+  mx = max_over_groups(mx);
+  // Fold the run's max into the running one (rescaling what earlier runs
+  // accumulated).
+  const float m_new = fmaxf(M, mx);
+  if (!first) {
+    const float alpha = M == m_new ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+  }
+  M = m_new;
+  // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
+  // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
+#pragma unroll
+  for (int j = 0; j < RUN; j += 2) {
+    if (j < cnt) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
+        const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
+        lsum += p0v + p1v;
+        pb[e] = (__bf16)p0v;
+        pb[4 + e] = (__bf16)p1v;
+      }
+      if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = mfma_16x16x32_bf16_k<KEEP>(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
+    }
+  }
+}
+
 // The attention of one split of row `row` (token t = row / H_kv, KV head kvh),
 // given its sparse length, its query operand qb, this lane's page id for the
 // first rounds (my_ids = ids(0)) and `ids(r0)`: this lane's page id for round
 // r0 + lane / RUN, slot lane % RUN of this wave's run (-1 past the split).
-// A split is walked one round (four runs, one per wave) at a time; each
-// round's loads are issued together and its logits give one exact max per
-// head, folded into the wave's running max between rounds.
+// A split is walked one round (one run a wave) at a time.
 template <int KV_DT, int Q_DT, int RUN, bool NT, int NW, typename IdFn>
 __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts<NW>& wp, int row, int split, int kvh,
                                                int n_tok, bf16x8 (&qb)[4], int my_ids, IdFn ids,
@@ -382,7 +476,7 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts<NW>& w
   constexpr int ROUND = NW * RUN;   // pages of a round
   constexpr int IDS = 64 / RUN;     // rounds whose page ids one id fetch holds
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int c = lane & 15, g = lane >> 4;
+  const int c = lane & 15;
   const int p0 = split * a.pps;
   if (n_tok <= 0) {
     write_empty_row(a, split, out_row);
@@ -402,97 +496,66 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts<NW>& w
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t hstride = (int64_t)a.H_kv * PB;  // bytes per page id (all heads)
   const int64_t hoff = (int64_t)kvh * PB;
+  bool first = true;
   for (int r = 0; r < nrounds; ++r) {
     if (r > 0 && r % IDS == 0) my_ids = ids(r);
     const int wb = p0 + r * ROUND + wave * RUN;
     const int cnt = max(0, min(RUN, p1 - wb));
     if (cnt == 0) continue;  // wave-uniform: this wave has nothing left in the split
-    const int ibase = (r % IDS) * RUN;
-    // Every load of the run, unconditionally: slots past the run re-read its
-    // first page, an out-of-range id reads page 0 and poisons its tile.  All
-    // K chunks are issued before all V chunks, page by page, and kept in that
-    // order, so the logits of page j wait only for K of pages <= j and P.V of
-    // page j only for V of pages <= j.
-    PageRegs<KV_DT> pr[RUN];
-    bool ok[RUN];
-    int64_t use[RUN];
-#pragma unroll
-    for (int j = 0; j < RUN; ++j) {
-      const int64_t id = __builtin_amdgcn_readlane(my_ids, ibase + (j < cnt ? j : 0));
-      ok[j] = page_ok(id, a.num_pages);
-      use[j] = (ok[j] ? id : 0) * hstride + hoff;
-      load_k16<KV_DT, NT>(pr[j], page_rsrc(a.kp + use[j], PB), lane);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < RUN; ++j) {
-      load_v16<KV_DT, NT>(pr[j], page_rsrc(a.vp + use[j], PB), lane);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Pass 1: every logit of the run, then one exact max per head.
-    float z[RUN][4];
-    float mx = neg_inf();
-#pragma unroll
-    for (int j = 0; j < RUN; ++j) {
-      if (j < cnt) {
-        bf16x8 kb[4];
-        k_operand<KV_DT>(pr[j], kb);
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16_k<NW == 8>(kb[x], qb[x], sacc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
-        const int nv = min(16, n_tok - (wb + j) * 16);
-        if (nv < 16) {  // the row's last page: keys past its length do not count
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
-          clear_tail_keys<KV_DT>(pr[j], nv, g);
-        }
-        if (!ok[j]) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[j][e] = qnan();
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, z[j][e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[j][e] = neg_inf();
-      }
-    }
-    mx = max_over_groups(mx);
-    // Fold the round's max into the running one (rescaling what earlier
-    // rounds accumulated).
-    const float m_new = fmaxf(M, mx);
-    if (r > 0) {
-      const float alpha = M == m_new ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    }
-    M = m_new;
-    // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
-    // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
-#pragma unroll
-    for (int j = 0; j < RUN; j += 2) {
-      if (j < cnt) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
-          const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
-          lsum += p0v + p1v;
-          pb[e] = (__bf16)p0v;
-          pb[4 + e] = (__bf16)p1v;
-        }
-        if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          o[dt] = mfma_16x16x32_bf16_k<NW == 8>(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
-      }
-    }
+    attend_run16<KV_DT, Q_DT, RUN, NT, NW == 8>(a, lane, n_tok, wb, cnt, my_ids, (r % IDS) * RUN, hstride, hoff,
+                                                qb, first, M, lsum, o);
+    first = false;
   }
   wave_to_lds<1, 16, NW>(wp, wave, lane, M, lsum, o);  // row r of tile dt: dim 16 dt + r
   finish_split<NW>(a, wp, row, split, live, out_row);
+}
+
+// The whole of row `row` by one wave, its runs one after another (rows that
+// fill the chip by themselves: no split, no merge); writes the row's output
+// straight from the wave's registers.  my_ids, ids(r0): this lane's page id
+// for run r0 + lane / RUN, slot lane % RUN.
+template <int KV_DT, int Q_DT, int RUN, bool NT, typename IdFn>
+__device__ __forceinline__ void attend_row_wave16(const PaArgs& a, int kvh, int n_tok, bf16x8 (&qb)[4],
+                                                  int my_ids, IdFn ids, __bf16* out_row) {
+  constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
+  constexpr int IDS = 64 / RUN;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const bool mine = c < a.G;
+  if (n_tok <= 0) {
+    if (mine) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<bf16x4*>(out_row + c * kHeadDim + 16 * dt + 4 * g) = bf16x4{0, 0, 0, 0};
+    }
+    return;
+  }
+  const int npages = min((n_tok + 15) / 16, a.sbt_stride);
+  const int nruns = (npages + RUN - 1) / RUN;
+  zero_missing_heads(qb, c, a.G);
+  float M = neg_inf(), lsum = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t hstride = (int64_t)a.H_kv * PB;
+  const int64_t hoff = (int64_t)kvh * PB;
+  for (int r = 0; r < nruns; ++r) {
+    if (r > 0 && r % IDS == 0) my_ids = ids(r);
+    const int wb = r * RUN;
+    attend_run16<KV_DT, Q_DT, RUN, NT, false>(a, lane, n_tok, wb, min(RUN, npages - wb), my_ids, (r % IDS) * RUN,
+                                              hstride, hoff, qb, r == 0, M, lsum, o);
+  }
+  // lane (g, c): dims 16 dt + 4 g + e of head c
+  const float inv = a.v_scale / sum_over_groups(lsum);
+  if (mine) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x4 ob = {(__bf16)(o[dt][0] * inv), (__bf16)(o[dt][1] * inv), (__bf16)(o[dt][2] * inv),
+                         (__bf16)(o[dt][3] * inv)};
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2, ob),
+                                  reinterpret_cast<u32x2*>(out_row + c * kHeadDim + 16 * dt + 4 * g));
+    }
+  }
 }
 
 // RUN: pages of one wave's run (a power of two); NT: nontemporal page loads;
@@ -530,6 +593,35 @@ __global__ __launch_bounds__(64 * NW) void pa16_kernel(PaArgs a) {
   attend_split16<KV_DT, Q_DT, RUN, NT, NW>(a, wp, row, split, kvh, n_tok, qb, my_ids, load_ids, out_row);
 }
 
+// One wave a row (the row_wave plan): grid (ceil(rows / 4)), wave w of
+// workgroup x attends row 4 grid_row(x) + w alone, its runs in order.
+template <int KV_DT, int Q_DT, int RUN, bool NT>
+__global__ __launch_bounds__(256) void pa16row_kernel(PaArgs a, int rows) {
+  constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int row = 4 * grid_row(blockIdx.x, gridDim.x) + wave;
+  if (row >= rows) return;
+  const int c = lane & 15, g = lane >> 4;
+  const int t = row / a.H_kv, kvh = row % a.H_kv;
+  const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
+  // lane l holds the id of page r0 RUN + l: runs r0 .. r0 + 64 / RUN - 1
+  auto load_ids = [&](int r0) {
+    const int pidx = r0 * RUN + lane;
+    return pidx < a.sbt_stride ? pages[pidx] : -1;
+  };
+  const int my_ids = load_ids(0);
+  const int n_tok = a.sctx[row];
+  bf16x8 qb[4];
+  {
+    const int hc = c < a.G ? c : 0;
+    const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * QB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
+  }
+  __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
+  attend_row_wave16<KV_DT, Q_DT, RUN, NT>(a, kvh, n_tok, qb, my_ids, load_ids, out_row);
+}
+
 // ----------------------------------------------------------------- select + attend
 // Top-k selection and the attention of a row in one launch, for 16-token
 // pages and rows of up to kSelMaxBlocks blocks.  Every workgroup of a row
@@ -540,38 +632,41 @@ __global__ __launch_bounds__(64 * NW) void pa16_kernel(PaArgs a) {
 // sparse length, as isb_topk_select_emit would.
 struct SelArgs {
   const float* scores;      // [H_kv][T][MB]
-  const int32_t* seq_lens;  // [R]
+  TokenMap tm;              // each token's request and causal length
   const int32_t* bt;        // [R][bt_stride]
   int32_t* topk;            // out [H_kv][T][K]
   int32_t* sbt;             // out [T * H_kv][K * ppb]
   int32_t* sctx;            // out [T * H_kv]
-  int q_len, T, MB, K, bt_stride;
+  int T, MB, K, bt_stride;
 };
 
-constexpr int kSelMaxBlocks = 2048;
+constexpr int kSelMaxBlocks = 2048;      // rows whose block-table row is staged in LDS
+constexpr int kSelWideMaxBlocks = 8192;  // widest rows selected in the attention launch
 
-template <int KV_DT, int Q_DT, int RUN, bool NT, int NW, int E>
+// BTL: the request's block-table row is read whole with the scores and kept
+// in LDS (rows of up to kSelMaxBlocks blocks); otherwise (wider rows) only the
+// selected blocks' entries are read, after the selection.
+template <int KV_DT, int Q_DT, int RUN, bool NT, int NW, int E, bool BTL>
 __global__ __launch_bounds__(64 * NW) void pa16sel_kernel(PaArgs a, SelArgs sa) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
   constexpr int NT_ = 64 * NW;      // threads a workgroup
   constexpr int ROUND = NW * RUN;
   __shared__ WaveParts<NW> wp;
   __shared__ SelectLds<NT_> sl;
-  __shared__ int32_t s_bt[kSelMaxBlocks];
+  __shared__ int32_t s_bt[BTL ? kSelMaxBlocks : 1];
   __shared__ int32_t s_sel[kSelMaxBlocks];
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
-  const int r = t / sa.q_len, i = t % sa.q_len;
   const int trow = kvh * sa.T + t;  // the row's index in the score and selection buffers
-  // Every global load first: the request's length, the row's scores, the
-  // request's block-table row and the query.
-  const int Lr = sa.seq_lens[r];
+  // Every global load first: the token's request and length, the row's
+  // scores, the request's block-table row and the query.
+  const TokenPos tp = token_pos(sa.tm, t);
   float sc[E];
-  int32_t btv[E];
+  int32_t btv[BTL ? E : 1];
   load_run<E, true>(sa.scores + (size_t)trow * sa.MB, E * tid, sa.MB, sc);
-  load_run<E, true>(sa.bt + (size_t)r * sa.bt_stride, E * tid, sa.MB, btv);
+  if constexpr (BTL) load_run<E, true>(sa.bt + (size_t)tp.r * sa.bt_stride, E * tid, sa.MB, btv);
   bf16x8 qb[4];
   {
     const int hc = c < a.G ? c : 0;
@@ -579,22 +674,30 @@ __global__ __launch_bounds__(64 * NW) void pa16sel_kernel(PaArgs a, SelArgs sa) 
 #pragma unroll
     for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
   }
-  const int Lt = max(0, Lr - (sa.q_len - 1 - i));
+  const int Lt = tp.L;
   const int nt = min((Lt + kBlockTokens - 1) / kBlockTokens, sa.MB);
+  if constexpr (BTL) {
 #pragma unroll
-  for (int x = 0; x < E; ++x)
-    if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
+    for (int x = 0; x < E; ++x)
+      if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
+  }
   int32_t* o = sa.topk + (size_t)trow * sa.K;
   const int m = select_row<NT_, E>(sc, nt, sa.K, sl, [&](int k, int b) {
     s_sel[k] = b;
     if (split == 0) o[k] = b;
   });
-  __syncthreads();  // the selection and the block-table row are in LDS
+  __syncthreads();  // the selection (and the block-table row) are in LDS
+  if constexpr (!BTL) {  // the selected blocks' ids, in place of their indices
+    for (int k = tid; k < m; k += NT_) s_sel[k] = sa.bt[(size_t)tp.r * sa.bt_stride + s_sel[k]];
+    __syncthreads();
+  }
+  // block id of the k-th selected block
+  auto blk = [&](int k) { return BTL ? s_bt[s_sel[k]] : s_sel[k]; };
   const int n_tok = m > 0 ? (m - 1) * kBlockTokens + (Lt - kBlockTokens * (nt - 1)) : 0;
   if (split == 0) {
     const int slots = sa.K * 8;
     int32_t* so = sa.sbt + (size_t)row * slots;
-    for (int x = tid; x < slots; x += NT_) so[x] = (x >> 3) < m ? s_bt[s_sel[x >> 3]] * 8 + (x & 7) : -1;
+    for (int x = tid; x < slots; x += NT_) so[x] = (x >> 3) < m ? blk(x >> 3) * 8 + (x & 7) : -1;
     if (tid == 0) sa.sctx[row] = n_tok;
   }
   const int p0 = split * a.pps;
@@ -602,7 +705,7 @@ __global__ __launch_bounds__(64 * NW) void pa16sel_kernel(PaArgs a, SelArgs sa) 
   const int mpages = 8 * m;
   auto ids = [&](int r0) {
     const int pidx = p0 + (r0 + lane / RUN) * ROUND + wave * RUN + lane % RUN;
-    return pidx < pend && pidx < mpages ? s_bt[s_sel[pidx >> 3]] * 8 + (pidx & 7) : -1;
+    return pidx < pend && pidx < mpages ? blk(pidx >> 3) * 8 + (pidx & 7) : -1;
   };
   const int my_ids = ids(0);
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
@@ -747,41 +850,47 @@ __global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
 // 16-token pages: every workgroup of a row selects the row's blocks from its
 // scores and block-table row, split 0 also writes the selection, the page
 // table and the sparse length.
-template <int Q_DT, int E>
+template <int Q_DT, int E, bool BTL>
 __global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
   __shared__ WaveParts<4> wp;
   __shared__ SelectLds<256> sl;
-  __shared__ int32_t s_bt[kSelMaxBlocks];
+  __shared__ int32_t s_bt[BTL ? kSelMaxBlocks : 1];
   __shared__ int32_t s_sel[kSelMaxBlocks];
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int tid = threadIdx.x;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
-  const int r = t / sa.q_len, i = t % sa.q_len;
   const int trow = kvh * sa.T + t;  // the row's index in the score and selection buffers
-  const int Lr = sa.seq_lens[r];
+  const TokenPos tp = token_pos(sa.tm, t);
   float sc[E];
-  int32_t btv[E];
+  int32_t btv[BTL ? E : 1];
   load_run<E, true>(sa.scores + (size_t)trow * sa.MB, E * tid, sa.MB, sc);
-  load_run<E, true>(sa.bt + (size_t)r * sa.bt_stride, E * tid, sa.MB, btv);
-  const int Lt = max(0, Lr - (sa.q_len - 1 - i));
+  if constexpr (BTL) load_run<E, true>(sa.bt + (size_t)tp.r * sa.bt_stride, E * tid, sa.MB, btv);
+  const int Lt = tp.L;
   const int nt = min((Lt + kBlockTokens - 1) / kBlockTokens, sa.MB);
+  if constexpr (BTL) {
 #pragma unroll
-  for (int x = 0; x < E; ++x)
-    if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
+    for (int x = 0; x < E; ++x)
+      if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
+  }
   int32_t* o = sa.topk + (size_t)trow * sa.K;
   const int m = select_row<256, E>(sc, nt, sa.K, sl, [&](int k, int b) {
     s_sel[k] = b;
     if (split == 0) o[k] = b;
   });
-  __syncthreads();  // the selection and the block-table row are in LDS
+  __syncthreads();  // the selection (and the block-table row) are in LDS
+  if constexpr (!BTL) {  // the selected blocks' ids, in place of their indices
+    for (int k = tid; k < m; k += 256) s_sel[k] = sa.bt[(size_t)tp.r * sa.bt_stride + s_sel[k]];
+    __syncthreads();
+  }
+  auto blk = [&](int k) { return BTL ? s_bt[s_sel[k]] : s_sel[k]; };
   const int n_tok = m > 0 ? (m - 1) * kBlockTokens + (Lt - kBlockTokens * (nt - 1)) : 0;
   if (split == 0) {  // one page a block: the row's k-th page is its k-th selected block
     int32_t* so = sa.sbt + (size_t)row * sa.K;
-    for (int x = tid; x < sa.K; x += 256) so[x] = x < m ? s_bt[s_sel[x]] : -1;
+    for (int x = tid; x < sa.K; x += 256) so[x] = x < m ? blk(x) : -1;
     if (tid == 0) sa.sctx[row] = n_tok;
   }
   const int p = split * a.pps + wave_id();
-  const int32_t id_raw = p < m ? s_bt[s_sel[p]] : -1;
+  const int32_t id_raw = p < m ? blk(p) : -1;
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
   attend_split_mx<Q_DT>(a, wp, row, split, t, kvh, n_tok, id_raw, out_row);
 }
@@ -795,6 +904,12 @@ static void launch_decode(const PaArgs& a, dim3 grid, bool nt, const PaPlan& pla
     hipLaunchKernelGGL((pamx_kernel<Q_DT>), grid, dim3(256), 0, st, a);
   } else {
     constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
+    if (plan.row_wave) {
+      const dim3 g((unsigned)((plan.rows + 3) / 4));
+      if (nt) hipLaunchKernelGGL((pa16row_kernel<KV_DT, Q_DT, RUN, true>), g, dim3(256), 0, st, a, plan.rows);
+      else hipLaunchKernelGGL((pa16row_kernel<KV_DT, Q_DT, RUN, false>), g, dim3(256), 0, st, a, plan.rows);
+      return;
+    }
     if constexpr (KV_DT == ISB_FP8_E4M3) {  // the plan takes eight waves for fp8 pages only
       if (nw == 8) {
         if (nt) hipLaunchKernelGGL((pa16_kernel<KV_DT, Q_DT, RUN, true, 8>), grid, dim3(512), 0, st, a);
@@ -863,26 +978,29 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
   return ISB_OK;
 }
 
-// E: scores a thread holds, E x (64 NW) >= max_blocks.
-template <int KV_DT, int Q_DT, int NW, int E>
+// E: scores a thread holds, E x (64 NW) >= max_blocks; BTL: the block-table
+// row goes to LDS with the scores (max_blocks <= kSelMaxBlocks).
+template <int KV_DT, int Q_DT, int NW, int E, bool BTL>
 static void launch_select_attend_e(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
   if constexpr (KV_DT == ISB_MXFP4) {
-    hipLaunchKernelGGL((pamxsel_kernel<Q_DT, E>), grid, dim3(256), 0, st, a, sa);
+    hipLaunchKernelGGL((pamxsel_kernel<Q_DT, E, BTL>), grid, dim3(256), 0, st, a, sa);
   } else {
     constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
     const dim3 b(64 * NW);
-    if (nt) hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, true, NW, E>), grid, b, 0, st, a, sa);
-    else hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, false, NW, E>), grid, b, 0, st, a, sa);
+    if (nt) hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, true, NW, E, BTL>), grid, b, 0, st, a, sa);
+    else hipLaunchKernelGGL((pa16sel_kernel<KV_DT, Q_DT, RUN, false, NW, E, BTL>), grid, b, 0, st, a, sa);
   }
 }
 
 template <int KV_DT, int Q_DT, int NW>
 static void launch_select_attend_nw(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
   constexpr int NT = 64 * NW;
-  if (sa.MB <= NT) launch_select_attend_e<KV_DT, Q_DT, NW, 1>(a, sa, grid, nt, st);
-  else if (sa.MB <= 2 * NT) launch_select_attend_e<KV_DT, Q_DT, NW, 2>(a, sa, grid, nt, st);
-  else if (sa.MB <= 4 * NT) launch_select_attend_e<KV_DT, Q_DT, NW, 4>(a, sa, grid, nt, st);
-  else launch_select_attend_e<KV_DT, Q_DT, NW, 8 * 4 / NW>(a, sa, grid, nt, st);
+  if (sa.MB <= NT) launch_select_attend_e<KV_DT, Q_DT, NW, 1, true>(a, sa, grid, nt, st);
+  else if (sa.MB <= 2 * NT) launch_select_attend_e<KV_DT, Q_DT, NW, 2, true>(a, sa, grid, nt, st);
+  else if (sa.MB <= 4 * NT) launch_select_attend_e<KV_DT, Q_DT, NW, 4, true>(a, sa, grid, nt, st);
+  else if (sa.MB <= kSelMaxBlocks) launch_select_attend_e<KV_DT, Q_DT, NW, 8 * 4 / NW, true>(a, sa, grid, nt, st);
+  else if (sa.MB <= 4096) launch_select_attend_e<KV_DT, Q_DT, NW, 16 * 4 / NW, false>(a, sa, grid, nt, st);
+  else launch_select_attend_e<KV_DT, Q_DT, NW, 32 * 4 / NW, false>(a, sa, grid, nt, st);
 }
 
 template <int KV_DT, int Q_DT>
@@ -895,6 +1013,28 @@ static void launch_select_attend(const PaArgs& a, const SelArgs& sa, dim3 grid, 
     }
   }
   launch_select_attend_nw<KV_DT, Q_DT, 4>(a, sa, grid, nt, st);
+}
+
+}  // namespace isb
+
+namespace isb {
+
+// The attention launch for a plan set up by pa_setup; nt: nontemporal page
+// loads (one query token a request, so no page is read twice).
+static int pa_run(hipStream_t st, const PaArgs& a, const PaPlan& plan, int q_dtype, int kv_dtype, bool nt) {
+  const dim3 grid((unsigned)plan.rows, plan.splits);
+  const bool qb = q_dtype == ISB_BF16;
+  if (kv_dtype == ISB_BF16) {
+    if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, nt, plan, st);
+    else launch_decode<ISB_BF16, ISB_FP8_E4M3>(a, grid, nt, plan, st);
+  } else if (kv_dtype == ISB_FP8_E4M3) {
+    if (qb) launch_decode<ISB_FP8_E4M3, ISB_BF16>(a, grid, nt, plan, st);
+    else launch_decode<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, grid, nt, plan, st);
+  } else {
+    if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, nt, plan, st);
+    else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, nt, plan, st);
+  }
+  return launch_status();
 }
 
 }  // namespace isb
@@ -918,21 +1058,27 @@ extern "C" int isb_sparse_pa_decode(isb_stream_t stream, const void* q, int q_dt
   if (err) return err;
   a.sbt = sparse_bt;
   a.sctx = sparse_ctx;
-  hipStream_t st = as_hip(stream);
-  const dim3 grid((unsigned)plan.rows, plan.splits);
-  const bool qb = q_dtype == ISB_BF16;
-  const bool nt = decode_query_len == 1;
-  if (kv_dtype == ISB_BF16) {
-    if (qb) launch_decode<ISB_BF16, ISB_BF16>(a, grid, nt, plan, st);
-    else launch_decode<ISB_BF16, ISB_FP8_E4M3>(a, grid, nt, plan, st);
-  } else if (kv_dtype == ISB_FP8_E4M3) {
-    if (qb) launch_decode<ISB_FP8_E4M3, ISB_BF16>(a, grid, nt, plan, st);
-    else launch_decode<ISB_FP8_E4M3, ISB_FP8_E4M3>(a, grid, nt, plan, st);
-  } else {
-    if (qb) launch_decode<ISB_MXFP4, ISB_BF16>(a, grid, nt, plan, st);
-    else launch_decode<ISB_MXFP4, ISB_FP8_E4M3>(a, grid, nt, plan, st);
-  }
-  return launch_status();
+  return pa_run(as_hip(stream), a, plan, q_dtype, kv_dtype, decode_query_len == 1);
+}
+
+extern "C" int isb_sparse_pa_prefill(isb_stream_t stream, const void* q, int q_dtype,
+                                     const void* k_pool, const void* v_pool, int kv_dtype,
+                                     int64_t num_pages, float k_scale, float v_scale,
+                                     const int32_t* sparse_bt, int sparse_bt_stride,
+                                     const int32_t* sparse_ctx, int num_tokens, int num_q_heads,
+                                     int num_kv_heads, int head_dim, float sm_scale, void* workspace,
+                                     size_t workspace_bytes, void* out) {
+  using namespace isb;
+  if (!sparse_bt || !sparse_ctx) return ISB_E_INVALID_ARG;
+  PaArgs a;
+  PaPlan plan;
+  const int err = pa_setup(q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale,
+                           sparse_bt_stride, num_tokens, num_q_heads, num_kv_heads, head_dim, sm_scale,
+                           workspace, workspace_bytes, out, a, plan);
+  if (err) return err;
+  a.sbt = sparse_bt;
+  a.sctx = sparse_ctx;
+  return pa_run(as_hip(stream), a, plan, q_dtype, kv_dtype, false);
 }
 
 // ----------------------------------------------------------------- no allocation
@@ -995,24 +1141,20 @@ extern "C" int isb_sparse_pa_decode_noalloc(isb_stream_t stream, const void* q, 
                               head_dim, sm_scale, ws, kNoallocScratchBytes, out);
 }
 
-extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const int32_t* seq_lens,
-                                 int num_reqs, int decode_query_len, int num_kv_heads, int max_blocks,
-                                 int top_k, const int32_t* block_table, int block_table_stride,
-                                 const void* q, int q_dtype, const void* k_pool, const void* v_pool,
-                                 int kv_dtype, int64_t num_pages, float k_scale, float v_scale,
-                                 int num_q_heads, float sm_scale, void* workspace,
-                                 size_t workspace_bytes, int32_t* topk_idx, int32_t* sparse_bt,
-                                 int32_t* sparse_ctx, void* out) {
-  using namespace isb;
-  if (!scores || !seq_lens || !block_table || !topk_idx || !sparse_bt || !sparse_ctx)
-    return ISB_E_INVALID_ARG;
-  if (num_reqs <= 0 || decode_query_len <= 0 || num_kv_heads <= 0 || max_blocks <= 0 ||
-      block_table_stride <= 0)
-    return ISB_E_INVALID_ARG;
+namespace isb {
+
+// isb_select_attend for either batch form; nt as for pa_run.
+static int select_attend_run(hipStream_t st, const float* scores, const TokenMap& tm, long long T,
+                             int num_kv_heads, int max_blocks, int top_k, const int32_t* block_table,
+                             int block_table_stride, const void* q, int q_dtype, const void* k_pool,
+                             const void* v_pool, int kv_dtype, int64_t num_pages, float k_scale, float v_scale,
+                             int num_q_heads, float sm_scale, void* workspace, size_t workspace_bytes,
+                             int32_t* topk_idx, int32_t* sparse_bt, int32_t* sparse_ctx, void* out, bool nt) {
+  if (!scores || !block_table || !topk_idx || !sparse_bt || !sparse_ctx) return ISB_E_INVALID_ARG;
+  if (T <= 0 || num_kv_heads <= 0 || max_blocks <= 0 || block_table_stride <= 0) return ISB_E_INVALID_ARG;
   if (top_k < 1 || top_k > max_blocks || max_blocks > (1 << 20) || max_blocks > block_table_stride)
     return ISB_E_SHAPE;
   const int ppb = kv_dtype == ISB_MXFP4 ? 1 : 8;
-  const long long T = (long long)num_reqs * decode_query_len;
   if (T * num_kv_heads * top_k * ppb > 0x7FFFFFFFLL) return ISB_E_SHAPE;
   PaArgs a;
   PaPlan plan;
@@ -1020,25 +1162,25 @@ extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const
                            (int)T, num_q_heads, num_kv_heads, kHeadDim, sm_scale, workspace, workspace_bytes,
                            out, a, plan);
   if (err) return err;
-  hipStream_t st = as_hip(stream);
-  const bool one_launch = max_blocks <= kSelMaxBlocks && max_blocks % 4 == 0 && block_table_stride % 4 == 0 &&
-                          reinterpret_cast<uintptr_t>(scores) % 16 == 0 &&
+  // rows wider than kSelMaxBlocks keep only their selection in LDS, which
+  // holds up to kSelMaxBlocks blocks
+  const bool one_launch = max_blocks <= kSelWideMaxBlocks && top_k <= kSelMaxBlocks && max_blocks % 4 == 0 &&
+                          block_table_stride % 4 == 0 && reinterpret_cast<uintptr_t>(scores) % 16 == 0 &&
                           reinterpret_cast<uintptr_t>(block_table) % 16 == 0;
-  if (!one_launch) {
-    // wide or unaligned rows: the two steps as two launches.
-    int e = isb_topk_select_emit(stream, scores, seq_lens, num_reqs, decode_query_len, num_kv_heads,
-                                 max_blocks, top_k, block_table, block_table_stride, ppb, topk_idx,
-                                 sparse_bt, sparse_ctx);
+  if (!one_launch || plan.row_wave) {
+    // wide or unaligned rows, or one wave a row (whose workgroups attend four
+    // rows and could not select them together): the two steps as two launches.
+    const int e = topk_select_emit_run(st, scores, tm, (int)T, num_kv_heads, max_blocks, top_k, block_table,
+                                       block_table_stride, ppb, topk_idx, sparse_bt, sparse_ctx);
     if (e) return e;
-    return isb_sparse_pa_decode(stream, q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale,
-                                sparse_bt, top_k * ppb, sparse_ctx, (int)T, decode_query_len, num_q_heads,
-                                num_kv_heads, kHeadDim, sm_scale, workspace, workspace_bytes, out);
+    a.sbt = sparse_bt;
+    a.sctx = sparse_ctx;
+    return pa_run(st, a, plan, q_dtype, kv_dtype, nt);
   }
-  SelArgs sa{scores, seq_lens, block_table, topk_idx, sparse_bt, sparse_ctx, decode_query_len, (int)T,
-             max_blocks, top_k, block_table_stride};
+  SelArgs sa{scores, tm, block_table, topk_idx, sparse_bt, sparse_ctx, (int)T, max_blocks, top_k,
+             block_table_stride};
   const dim3 grid((unsigned)plan.rows, plan.splits);
   const bool qb = q_dtype == ISB_BF16;
-  const bool nt = decode_query_len == 1;
   if (kv_dtype == ISB_BF16) {
     if (qb) launch_select_attend<ISB_BF16, ISB_BF16>(a, sa, grid, nt, plan, st);
     else launch_select_attend<ISB_BF16, ISB_FP8_E4M3>(a, sa, grid, nt, plan, st);
@@ -1050,4 +1192,40 @@ extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const
     else launch_select_attend<ISB_MXFP4, ISB_FP8_E4M3>(a, sa, grid, nt, plan, st);
   }
   return launch_status();
+}
+
+}  // namespace isb
+
+extern "C" int isb_select_attend(isb_stream_t stream, const float* scores, const int32_t* seq_lens,
+                                 int num_reqs, int decode_query_len, int num_kv_heads, int max_blocks,
+                                 int top_k, const int32_t* block_table, int block_table_stride,
+                                 const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                                 int kv_dtype, int64_t num_pages, float k_scale, float v_scale,
+                                 int num_q_heads, float sm_scale, void* workspace,
+                                 size_t workspace_bytes, int32_t* topk_idx, int32_t* sparse_bt,
+                                 int32_t* sparse_ctx, void* out) {
+  using namespace isb;
+  if (!seq_lens || num_reqs <= 0 || decode_query_len <= 0) return ISB_E_INVALID_ARG;
+  return select_attend_run(as_hip(stream), scores, decode_map(seq_lens, decode_query_len),
+                           (long long)num_reqs * decode_query_len, num_kv_heads, max_blocks, top_k, block_table,
+                           block_table_stride, q, q_dtype, k_pool, v_pool, kv_dtype, num_pages, k_scale, v_scale,
+                           num_q_heads, sm_scale, workspace, workspace_bytes, topk_idx, sparse_bt, sparse_ctx, out,
+                           decode_query_len == 1);
+}
+
+extern "C" int isb_select_attend_prefill(isb_stream_t stream, const float* scores, int num_reqs,
+                                         const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                         int num_tokens, int num_kv_heads, int max_blocks, int top_k,
+                                         const int32_t* block_table, int block_table_stride, const void* q,
+                                         int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                                         int64_t num_pages, float k_scale, float v_scale, int num_q_heads,
+                                         float sm_scale, void* workspace, size_t workspace_bytes,
+                                         int32_t* topk_idx, int32_t* sparse_bt, int32_t* sparse_ctx, void* out) {
+  using namespace isb;
+  if (!query_req_id || !query_abs_pos || num_reqs <= 0) return ISB_E_INVALID_ARG;
+  return select_attend_run(as_hip(stream), scores,
+                           prefill_map(query_req_id, query_abs_pos, num_reqs, max_blocks), num_tokens,
+                           num_kv_heads, max_blocks, top_k, block_table, block_table_stride, q, q_dtype, k_pool,
+                           v_pool, kv_dtype, num_pages, k_scale, v_scale, num_q_heads, sm_scale, workspace,
+                           workspace_bytes, topk_idx, sparse_bt, sparse_ctx, out, false);
 }

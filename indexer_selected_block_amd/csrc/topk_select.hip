@@ -29,27 +29,27 @@ namespace isb {
 
 struct TopkArgs {
   const float* scores;
-  const int32_t* seq_lens;
+  TokenMap tm;
   const int32_t* bt;  // fused emit only
   int32_t* topk;
   int32_t* sbt;       // fused emit only
   int32_t* sctx;      // fused emit only
-  int q_len, T, MB, K, H_kv, bt_stride, ppb;
+  int T, MB, K, H_kv, bt_stride, ppb;
 };
 
 // Causal geometry of topk row `row` (= g * T + t).
 struct RowGeom {
   int g, t, r, Lt, nt;
 };
-__device__ __forceinline__ RowGeom row_geom(const TopkArgs& a, int row, int Lr) {
+__device__ __forceinline__ RowGeom row_geom(const TopkArgs& a, int row) {
   RowGeom q;
   q.g = row / a.T;
   q.t = row % a.T;
-  q.r = q.t / a.q_len;
-  const int i = q.t % a.q_len;
-  const int Lt = Lr - (a.q_len - 1 - i);
-  q.Lt = Lt > 0 ? Lt : 0;
-  // n_t never exceeds the score row (callers keep seq_lens <= 128 max_blocks)
+  const TokenPos tp = token_pos(a.tm, q.t);
+  q.r = tp.r;
+  q.Lt = tp.L;
+  // n_t never exceeds the score row (decode callers keep seq_lens <= 128
+  // max_blocks; prefill positions past it are empty rows)
   q.nt = min((q.Lt + kBlockTokens - 1) / kBlockTokens, a.MB);
   return q;
 }
@@ -123,9 +123,8 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
   const int row = blockIdx.x;
   // Every global load first: length, scores and (fused, narrow rows) the
   // block-table row, so the workgroup waits for one round trip.
-  const int Lr = a.seq_lens[(row % a.T) / a.q_len];
+  const RowGeom q = row_geom(a, row);
   const float* s = a.scores + (size_t)row * a.MB;
-  const RowGeom q = row_geom(a, row, Lr);
   float sc[E];
   int32_t btv[E];
   load_run<E, VEC>(s, E * tid, a.MB, sc);
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(256) void topk_global_kernel(TopkArgs a) {
   __shared__ int s_wave[4];
   __shared__ int s_pick[2];
   const int row = blockIdx.x;
-  const RowGeom q = row_geom(a, row, a.seq_lens[(row % a.T) / a.q_len]);
+  const RowGeom q = row_geom(a, row);
   int32_t* o = a.topk + (size_t)row * a.K;
   const float* s = a.scores + (size_t)row * a.MB;
   const int W = q.nt - 1;
@@ -216,31 +215,20 @@ static void launch_reg(const TopkArgs& a, unsigned rows, size_t lds, hipStream_t
     launch_reg_v<EMIT, BT_LDS, false>(a, rows, lds, st);
 }
 
-// Shared argument checks of the two entry points; 0 or an ISB_E_* code.
-static int check_topk(const float* scores, const int32_t* seq_lens, int32_t* topk_idx, int num_reqs,
-                      int decode_query_len, int num_kv_heads, int max_blocks, int top_k) {
-  if (!scores || !seq_lens || !topk_idx) return ISB_E_INVALID_ARG;
-  if (num_reqs <= 0 || decode_query_len <= 0 || num_kv_heads <= 0 || max_blocks <= 0)
-    return ISB_E_INVALID_ARG;
+// Shared argument checks of the entry points; 0 or an ISB_E_* code.
+static int check_topk(const float* scores, int32_t* topk_idx, long long num_tokens, int num_kv_heads,
+                      int max_blocks, int top_k) {
+  if (!scores || !topk_idx) return ISB_E_INVALID_ARG;
+  if (num_tokens <= 0 || num_kv_heads <= 0 || max_blocks <= 0) return ISB_E_INVALID_ARG;
   if (top_k < 1 || top_k > max_blocks || max_blocks > (1 << 20)) return ISB_E_SHAPE;
-  const long long rows = (long long)num_reqs * decode_query_len * num_kv_heads;
-  if (rows > 0x7FFFFFFFLL) return ISB_E_SHAPE;
+  if (num_tokens * num_kv_heads > 0x7FFFFFFFLL) return ISB_E_SHAPE;
   return ISB_OK;
 }
 
-}  // namespace isb
-
-extern "C" int isb_topk_select(isb_stream_t stream, const float* scores, const int32_t* seq_lens,
-                               int num_reqs, int decode_query_len, int num_kv_heads,
-                               int max_blocks, int top_k, int32_t* topk_idx) {
-  using namespace isb;
-  const int err = check_topk(scores, seq_lens, topk_idx, num_reqs, decode_query_len, num_kv_heads,
-                             max_blocks, top_k);
-  if (err) return err;
-  TopkArgs a{scores, seq_lens, nullptr, topk_idx, nullptr, nullptr, decode_query_len,
-             num_reqs * decode_query_len, max_blocks, top_k, num_kv_heads, 0, 0};
-  const unsigned rows = (unsigned)((long long)a.T * num_kv_heads);
-  hipStream_t st = as_hip(stream);
+static int topk_select_run(hipStream_t st, const float* scores, const TokenMap& tm, int T, int num_kv_heads,
+                           int max_blocks, int top_k, int32_t* topk_idx) {
+  TopkArgs a{scores, tm, nullptr, topk_idx, nullptr, nullptr, T, max_blocks, top_k, num_kv_heads, 0, 0};
+  const unsigned rows = (unsigned)((long long)T * num_kv_heads);
   const size_t lds = topk_lds_bytes(max_blocks, top_k, false, false);
   if (lds)
     launch_reg<false, false>(a, rows, lds, st);
@@ -249,27 +237,19 @@ extern "C" int isb_topk_select(isb_stream_t stream, const float* scores, const i
   return launch_status();
 }
 
-extern "C" int isb_topk_select_emit(isb_stream_t stream, const float* scores,
-                                    const int32_t* seq_lens, int num_reqs, int decode_query_len,
-                                    int num_kv_heads, int max_blocks, int top_k,
-                                    const int32_t* block_table, int block_table_stride,
-                                    int pages_per_block, int32_t* topk_idx, int32_t* sparse_bt,
-                                    int32_t* sparse_ctx) {
-  using namespace isb;
-  const int err = check_topk(scores, seq_lens, topk_idx, num_reqs, decode_query_len, num_kv_heads,
-                             max_blocks, top_k);
-  if (err) return err;
+int topk_select_emit_run(hipStream_t st, const float* scores, const TokenMap& tm, int T,
+                                int num_kv_heads, int max_blocks, int top_k, const int32_t* block_table,
+                                int block_table_stride, int pages_per_block, int32_t* topk_idx,
+                                int32_t* sparse_bt, int32_t* sparse_ctx) {
   if (!block_table || !sparse_bt || !sparse_ctx) return ISB_E_INVALID_ARG;
   if (block_table_stride <= 0) return ISB_E_INVALID_ARG;
   if (pages_per_block != 1 && pages_per_block != 8) return ISB_E_SHAPE;
   if (max_blocks > block_table_stride) return ISB_E_SHAPE;
-  const long long slots = (long long)num_reqs * decode_query_len * num_kv_heads * top_k * pages_per_block;
+  const long long slots = (long long)T * num_kv_heads * top_k * pages_per_block;
   if (slots > 0x7FFFFFFFLL) return ISB_E_SHAPE;
-  TopkArgs a{scores, seq_lens, block_table, topk_idx, sparse_bt, sparse_ctx, decode_query_len,
-             num_reqs * decode_query_len, max_blocks, top_k, num_kv_heads, block_table_stride,
-             pages_per_block};
-  const unsigned rows = (unsigned)((long long)a.T * num_kv_heads);
-  hipStream_t st = as_hip(stream);
+  TopkArgs a{scores, tm, block_table, topk_idx, sparse_bt, sparse_ctx, T, max_blocks, top_k, num_kv_heads,
+             block_table_stride, pages_per_block};
+  const unsigned rows = (unsigned)((long long)T * num_kv_heads);
   // The block-table row rides along with the scores when it is small; a wide
   // row's table would double what each workgroup reads before it can select,
   // so there only the selected blocks' entries are read, after the selection.
@@ -282,9 +262,66 @@ extern "C" int isb_topk_select_emit(isb_stream_t stream, const float* scores,
     hipLaunchKernelGGL(topk_global_kernel, dim3(rows), dim3(256), 0, st, a);
     const int e = launch_status();
     if (e) return e;
-    return emit_launch(st, topk_idx, block_table, block_table_stride, seq_lens, num_reqs,
-                           decode_query_len, num_kv_heads, top_k, pages_per_block, sparse_bt,
-                           sparse_ctx);
+    return emit_launch(st, topk_idx, block_table, block_table_stride, tm, T, num_kv_heads, top_k,
+                       pages_per_block, sparse_bt, sparse_ctx);
   }
   return launch_status();
+}
+
+}  // namespace isb
+
+extern "C" int isb_topk_select(isb_stream_t stream, const float* scores, const int32_t* seq_lens,
+                               int num_reqs, int decode_query_len, int num_kv_heads,
+                               int max_blocks, int top_k, int32_t* topk_idx) {
+  using namespace isb;
+  if (!seq_lens || num_reqs <= 0 || decode_query_len <= 0) return ISB_E_INVALID_ARG;
+  const long long T = (long long)num_reqs * decode_query_len;
+  const int err = check_topk(scores, topk_idx, T, num_kv_heads, max_blocks, top_k);
+  if (err) return err;
+  return topk_select_run(as_hip(stream), scores, decode_map(seq_lens, decode_query_len), (int)T, num_kv_heads,
+                         max_blocks, top_k, topk_idx);
+}
+
+extern "C" int isb_topk_select_prefill(isb_stream_t stream, const float* scores, int num_reqs,
+                                       const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                       int num_tokens, int num_kv_heads, int max_blocks, int top_k,
+                                       int32_t* topk_idx) {
+  using namespace isb;
+  if (!query_req_id || !query_abs_pos || num_reqs <= 0) return ISB_E_INVALID_ARG;
+  const int err = check_topk(scores, topk_idx, num_tokens, num_kv_heads, max_blocks, top_k);
+  if (err) return err;
+  return topk_select_run(as_hip(stream), scores, prefill_map(query_req_id, query_abs_pos, num_reqs, max_blocks),
+                         num_tokens, num_kv_heads, max_blocks, top_k, topk_idx);
+}
+
+extern "C" int isb_topk_select_emit(isb_stream_t stream, const float* scores,
+                                    const int32_t* seq_lens, int num_reqs, int decode_query_len,
+                                    int num_kv_heads, int max_blocks, int top_k,
+                                    const int32_t* block_table, int block_table_stride,
+                                    int pages_per_block, int32_t* topk_idx, int32_t* sparse_bt,
+                                    int32_t* sparse_ctx) {
+  using namespace isb;
+  if (!seq_lens || num_reqs <= 0 || decode_query_len <= 0) return ISB_E_INVALID_ARG;
+  const long long T = (long long)num_reqs * decode_query_len;
+  const int err = check_topk(scores, topk_idx, T, num_kv_heads, max_blocks, top_k);
+  if (err) return err;
+  return topk_select_emit_run(as_hip(stream), scores, decode_map(seq_lens, decode_query_len), (int)T,
+                              num_kv_heads, max_blocks, top_k, block_table, block_table_stride, pages_per_block,
+                              topk_idx, sparse_bt, sparse_ctx);
+}
+
+extern "C" int isb_topk_select_emit_prefill(isb_stream_t stream, const float* scores, int num_reqs,
+                                            const int32_t* query_req_id, const int32_t* query_abs_pos,
+                                            int num_tokens, int num_kv_heads, int max_blocks, int top_k,
+                                            const int32_t* block_table, int block_table_stride,
+                                            int pages_per_block, int32_t* topk_idx, int32_t* sparse_bt,
+                                            int32_t* sparse_ctx) {
+  using namespace isb;
+  if (!query_req_id || !query_abs_pos || num_reqs <= 0) return ISB_E_INVALID_ARG;
+  const int err = check_topk(scores, topk_idx, num_tokens, num_kv_heads, max_blocks, top_k);
+  if (err) return err;
+  return topk_select_emit_run(as_hip(stream), scores,
+                              prefill_map(query_req_id, query_abs_pos, num_reqs, max_blocks), num_tokens,
+                              num_kv_heads, max_blocks, top_k, block_table, block_table_stride, pages_per_block,
+                              topk_idx, sparse_bt, sparse_ctx);
 }

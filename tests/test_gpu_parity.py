@@ -227,6 +227,13 @@ _SEL_CASES = {
     "prefill_mxfp4": ("prefill_mxfp4", {}),              # 37 tokens a request, 74 rows
     # 128 one-token rows of 16 blocks: two splits of eight-wave workgroups
     "fp8_decode_eight_waves": ("fp8_decode", dict(num_reqs=128, ctx_lo=1500, ctx_hi=4000, pool_blocks=128 * 32 + 64)),
+    # rows wider than 2048 blocks: one launch that reads only the selected
+    # blocks' table entries (4096 and 8192 blocks; MXFP4 at 3904)
+    "long_context_4096_blocks": ("long_context", dict(num_reqs=2, ctx_lo=400000, ctx_hi=524288,
+                                                      pool_blocks=2 * 4096 + 64)),
+    "long_context_8192_blocks": ("long_context", dict(num_reqs=2, ctx_lo=900000, ctx_hi=1048576,
+                                                      pool_blocks=2 * 8192 + 64)),
+    "mxfp4_3904_blocks": ("mxfp4", dict(num_reqs=3, ctx_lo=300000, ctx_hi=499712, pool_blocks=3 * 3904 + 64)),
 }
 
 
@@ -360,7 +367,8 @@ def test_sparse_pa_variants(variant):
 # rounds.  (128, 16) and (150, 12) take two splits of eight-wave workgroups,
 # (256, 8) one split of eight waves.
 @pytest.mark.parametrize("reqs,top_k", [(1, 8), (2, 8), (5, 8), (33, 8), (129, 8), (257, 8), (511, 8), (700, 8),
-                                        (128, 16), (150, 12), (256, 8)])
+                                        (128, 16), (150, 12), (256, 8),
+                                        (1984, 8), (2049, 4)])   # one wave a row from 1984 rows
 def test_sparse_pa_row_counts(reqs, top_k):
     cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=reqs, ctx_lo=200, ctx_hi=5000,
                     pool_blocks=reqs * 40 + 64, top_k=top_k)
@@ -379,6 +387,31 @@ def test_sparse_pa_row_counts(reqs, top_k):
     tol = attn_tol(cfg.kv_dtype, attended_vmax(hi, sbt, sctx))
     err = np.abs(got - ref).max()
     assert err <= tol, f"max |err| {err:.4g} > {tol:.4g}"
+
+
+@pytest.mark.parametrize("base,kw", [("tiny_bf16", dict(num_q_heads=16)),
+                                     ("fp8_decode", dict(num_kv_heads=2, num_q_heads=16, num_idx_heads=2)),
+                                     ("fp8_decode", dict(q_dtype="e4m3"))])
+def test_sparse_pa_one_wave_a_row(base, kw):
+    # batches of at least 1984 rows of 16-token pages give every row a wave of
+    # its own: bf16 pages, two KV heads (row = token, head), an e4m3 query
+    reqs = 1000 if kw.get("num_kv_heads") == 2 else 2000
+    cfg = wl.shrink(dataclasses.replace(wl.CONFIGS[base], **kw), num_reqs=reqs, ctx_lo=100, ctx_hi=1500,
+                    pool_blocks=reqs * 13 + 64, top_k=6)
+    _say(f"[sparse_pa one wave a row] {base} {kw}")
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    sbt, sctx = _synthetic_table(hi, 77)
+    ref = oracle_attention(hi, sbt, sctx)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale, decode_query_len=cfg.query_len)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    tol = attn_tol(cfg.kv_dtype, attended_vmax(hi, sbt, sctx))
+    err = np.abs(got - ref).max(axis=(1, 2))
+    assert (err <= tol).all(), f"max |err| {err.max():.4g} > {tol:.4g}"
 
 
 def test_sparse_pa_every_block_is_dense_attention():

@@ -31,7 +31,9 @@ def test_header_declares_the_four_calls():
     for n in ("isb_index_score", "isb_topk_select", "isb_emit_sparse_block_table",
               "isb_sparse_pa_decode", "isb_sparse_pa_workspace_bytes", "isb_strerror", "isb_version",
               "isb_sparse_pa_decode_noalloc",
-              "isb_write_cache", "isb_quantize_e4m3", "isb_prepare_query", "isb_topk_merge"):
+              "isb_write_cache", "isb_quantize_e4m3", "isb_prepare_query", "isb_topk_merge",
+              "isb_index_score_prefill", "isb_topk_select_prefill", "isb_emit_sparse_block_table_prefill",
+              "isb_topk_select_emit_prefill", "isb_sparse_pa_prefill", "isb_select_attend_prefill"):
         assert n in names
 
 
@@ -161,6 +163,48 @@ def test_argument_checks_return_before_any_launch(lib):
                                             p) == -4
     assert lib.isb_sparse_pa_decode_noalloc(NULL, NULL, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 4, 1, 16, 1, 128, 0.1,
                                             p) == -1
+
+
+def test_prefill_argument_checks_return_before_any_launch(lib):
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
+    # isb_index_score_prefill(stream, q_idx, qdt, H_idx, pool, idt, scale, blocks, bt, stride, R, req, pos, T,
+    #                         H_kv, MB, scores)
+    sc = lambda q=p, req=p, pos=p, T=8, H=1, R=1, MB=4, stride=4, qdt=0, idt=0: lib.isb_index_score_prefill(  # noqa
+        NULL, q, qdt, H, p, idt, 1.0, 8, p, stride, R, req, pos, T, 1, MB, p)
+    assert sc(q=NULL) == -1 and sc(req=NULL) == -1 and sc(pos=NULL) == -1
+    assert sc(T=0) == -1 and sc(R=0) == -1
+    assert sc(qdt=2) == -2 and sc(idt=5) == -2
+    assert sc(H=3) == -3                                  # 16 % H_idx
+    assert sc(MB=8) == -3                                 # MB > stride
+    assert sc(T=65535 * 128 + 1) == -3                    # more than 65535 tiles of 128 rows
+    assert sc(T=1 << 28, H=16) == -3                      # rows > 2^31 - 1
+    # isb_topk_select_prefill(stream, scores, R, req, pos, T, H_kv, MB, K, topk)
+    assert lib.isb_topk_select_prefill(NULL, p, 1, NULL, p, 4, 1, 4, 2, p) == -1
+    assert lib.isb_topk_select_prefill(NULL, p, 0, p, p, 4, 1, 4, 2, p) == -1
+    assert lib.isb_topk_select_prefill(NULL, p, 1, p, p, 0, 1, 4, 2, p) == -1
+    assert lib.isb_topk_select_prefill(NULL, p, 1, p, p, 4, 1, 4, 5, p) == -3    # K > MB
+    # isb_emit_sparse_block_table_prefill(stream, topk, bt, stride, R, req, pos, T, H_kv, K, ppb, sbt, sctx)
+    assert lib.isb_emit_sparse_block_table_prefill(NULL, p, p, 4, 1, NULL, p, 4, 1, 2, 8, p, p) == -1
+    assert lib.isb_emit_sparse_block_table_prefill(NULL, p, p, 4, 1, p, p, 4, 1, 2, 4, p, p) == -3   # ppb 4
+    # isb_topk_select_emit_prefill(stream, scores, R, req, pos, T, H_kv, MB, K, bt, stride, ppb, topk, sbt, sctx)
+    assert lib.isb_topk_select_emit_prefill(NULL, p, 1, p, NULL, 4, 1, 4, 2, p, 4, 8, p, p, p) == -1
+    assert lib.isb_topk_select_emit_prefill(NULL, p, 1, p, p, 4, 1, 8, 2, p, 4, 8, p, p, p) == -3   # MB > stride
+    assert lib.isb_topk_select_emit_prefill(NULL, p, 1, p, p, 4, 1, 4, 2, p, 4, 2, p, p, p) == -3   # ppb 2
+    # isb_sparse_pa_prefill(stream, q, qdt, kp, vp, kvdt, pages, ks, vs, sbt, stride, sctx, T, Hq, Hkv, hd, sm,
+    #                       ws, ws_bytes, out)
+    assert lib.isb_sparse_pa_prefill(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, NULL, 8, p, 4, 16, 1, 128, 0.1,
+                                     p, 1 << 20, p) == -1
+    assert lib.isb_sparse_pa_prefill(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 8, p, 4, 16, 1, 64, 0.1,
+                                     p, 1 << 20, p) == -3                                         # head_dim
+    need = lib.isb_sparse_pa_workspace_bytes(4, 16, 1, 128, 1)
+    assert lib.isb_sparse_pa_prefill(NULL, p, 0, p, p, 1, 8, 1.0, 1.0, p, 128, p, 4, 16, 1, 128, 0.1,
+                                     p, need - 1, p) == -4
+    # isb_select_attend_prefill(stream, scores, R, req, pos, T, H_kv, MB, K, bt, stride, q, qdt, kp, vp, kvdt,
+    #                           pages, ks, vs, Hq, sm, ws, ws_bytes, topk, sbt, sctx, out)
+    sa = lambda req=p, R=1, MB=4, K=2, Hq=16: lib.isb_select_attend_prefill(  # noqa: E731
+        NULL, p, R, req, p, 4, 1, MB, K, p, 4, p, 0, p, p, 1, 8, 1.0, 1.0, Hq, 0.1, p, 1 << 20, p, p, p, p)
+    assert sa(req=NULL) == -1 and sa(R=0) == -1
+    assert sa(MB=8) == -3 and sa(K=5) == -3 and sa(Hq=32) == -3
 
 
 def test_workspace_query(lib):
@@ -308,7 +352,25 @@ def test_bench_counts_each_attended_position_once():
             for b in blocks:
                 for pos in range(128 * b, min(128 * b + 128, Lt)):
                     seen.add((g, r, pos))
-    assert bench.distinct_attended_tokens(w, torch.from_numpy(topk)) == len(seen)
+    import types
+    assert bench.distinct_attended_tokens(types.SimpleNamespace(w=w), torch.from_numpy(topk)) == len(seen)
+    # a ragged prefill batch, tokens shuffled: the same count from per-token
+    # request ids and positions
+    b = wl.ragged_batch(w, [min(c, L) for c, L in zip([3, 1, 5, 2, 4], lens)], order="shuffled", seed=4)
+    req, pos = b.query_req_id.tolist(), b.query_abs_pos.tolist()
+    topk = np.full((cfg.num_kv_heads, b.num_tokens, K), -1, dtype=np.int32)
+    seen = set()
+    for g in range(cfg.num_kv_heads):
+        for t in range(b.num_tokens):
+            Lt = pos[t] + 1
+            nt = -(-Lt // 128)
+            blocks = sorted(set(rng.choice(nt, size=min(K, nt), replace=False).tolist()) | {nt - 1})[:K]
+            topk[g, t, :len(blocks)] = blocks
+            for bb in blocks:
+                for p in range(128 * bb, min(128 * bb + 128, Lt)):
+                    seen.add((g, req[t], p))
+    L = types.SimpleNamespace(w=w, b=b)
+    assert bench.distinct_attended_tokens(L, torch.from_numpy(topk)) == len(seen)
 
 
 def test_norm_rope_struct_checks_its_tensors():
