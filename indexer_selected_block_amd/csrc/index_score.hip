@@ -394,6 +394,12 @@ struct PartOps<ISB_MXFP4, ISB_FP8_E4M3> {
   u32x4 data[4];  // e2m1, as loaded
   int sa[4];      // this lane's e8m0 scale byte of each tile
 };
+// e4m3 keys against an e4m3 query: the keys as loaded (lane (g, m) of a tile
+// holds key m's dims 32 g .. 32 g + 31), multiplied on the fp8 MFMA
+template <>
+struct PartOps<ISB_FP8_E4M3, ISB_FP8_E4M3> {
+  i32x8 k8[2];
+};
 
 template <int KEY_DT, int Q_DT>
 __device__ __forceinline__ void part_operands(const PartRaw<KEY_DT>& k, int lane, PartOps<KEY_DT, Q_DT>& o) {
@@ -404,6 +410,12 @@ __device__ __forceinline__ void part_operands(const PartRaw<KEY_DT>& k, int lane
     for (int tt = 0; tt < NT; ++tt) {
       o.data[tt] = k.data[tt];
       o.sa[tt] = (int)((k.scl[tt] >> (8 * g)) & 0xFFu);
+    }
+  } else if constexpr (KEY_DT == ISB_FP8_E4M3 && Q_DT == ISB_FP8_E4M3) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const u32x4 c0 = k.t[tt].c[0], c1 = k.t[tt].c[1];
+      o.k8[tt] = i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
     }
   } else if constexpr (KEY_DT == ISB_MXFP4) {
 #pragma unroll
@@ -444,6 +456,13 @@ __device__ __forceinline__ void wide_part_max(const PartOps<KEY_DT, Q_DT>& k, in
       const i32x8 ka = {(int)k.data[tt][0], (int)k.data[tt][1], (int)k.data[tt][2], (int)k.data[tt][3], 0, 0, 0, 0};
       acc[tt] = mfma_scale_fp4_e4m3(ka, qb, f32x4{0.f, 0.f, 0.f, 0.f}, k.sa[tt]);
     }
+  } else if constexpr (KEY_DT == ISB_FP8_E4M3 && Q_DT == ISB_FP8_E4M3) {
+    // the query row's dims 32 g .. 32 g + 31, the bytes the keys hold
+    const u32x4 lo = ld16(qrow + 32 * g);
+    const u32x4 hi = ld16(qrow + 32 * g + 16);
+    const i32x8 qb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_scale_e4m3(k.k8[tt], qb, f32x4{0.f, 0.f, 0.f, 0.f});
   } else {
     bf16x8 qb[4];
 #pragma unroll
@@ -471,24 +490,26 @@ __device__ __forceinline__ void wide_part_max(const PartOps<KEY_DT, Q_DT>& k, in
   }
 }
 
-// Tiles that hold tokens of several requests: the rows of 16-row tile
-// [16 q, 16 q + 16) (this lane's row is token `tok`, -1 past the tile) against
-// block b of every run of the tile's tokens [k_begin, ntok) after the first,
-// folded into `best`.  Each run reads its block again for every 16-row tile
-// it has rows in.  Kept out of line (few registers), so that the kernel's
-// single-run path keeps four waves a SIMD.
-template <int KEY_DT, int Q_DT>
-__device__ __attribute__((noinline)) float wide_other_runs(const uint8_t* pool, int64_t pool_blocks,
-                                                           const int32_t* bt, int bt_stride, const int* s_req,
-                                                           const int* s_len, const uint8_t* qrow, int b, int k_begin,
-                                                           int ntok, int tok, int tlo, int thi, float best) {
+// Tiles that hold tokens of several requests: the tile's 16-row tiles
+// against block b of every run of its tokens [k_begin, ntok) after the first,
+// folded into best[q] (lane row m of tile q: token tok[q], -1 past the tile;
+// staged query row qrow[q]).  A slow path with little state, so that the
+// single-run path keeps its register budget: each run reads its block's keys
+// again for every 16-row tile it has rows in, a part at a time.
+template <int KEY_DT, int Q_DT, int NQ>
+__device__ __forceinline__ void wide_other_runs(const uint8_t* pool, int64_t pool_blocks, const int32_t* bt,
+                                                int bt_stride, const int* s_req, const int* s_len,
+                                                const uint8_t* const (&qrow)[NQ], const int (&tok)[NQ], int b,
+                                                int k_begin, int ntok, float (&best)[NQ]) {
   constexpr int NT = wide_part_tiles<KEY_DT>();
   constexpr int PARTS = 8 / NT;
   constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
   const int lane = threadIdx.x & 63;
+#pragma unroll 1
   for (int k0 = k_begin, k1 = 0; k0 < ntok; k0 = k1) {
     const int rr = __builtin_amdgcn_readfirstlane(s_req[k0]);
     k1 = ntok;
+#pragma unroll 1
     for (int base = k0 + 1; base < ntok; base += kWave) {
       const int k = base + lane;
       const uint64_t diff = __ballot(k < ntok && s_req[k] != rr);
@@ -497,27 +518,29 @@ __device__ __attribute__((noinline)) float wide_other_runs(const uint8_t* pool, 
         break;
       }
     }
-    if (k1 <= tlo || k0 > thi) continue;  // no row of this 16-row tile in the run
-    const bool in = tok >= k0 && tok < k1;
-    const int v = in ? s_len[tok] - b * kBlockTokens : 0;
-    const int nv = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
-    if (!__ballot(nv > 0)) continue;  // none of its rows reaches block b
-    const int64_t blk = __builtin_amdgcn_readfirstlane(bt[(size_t)rr * bt_stride + b]);
-    if (blk < 0 || blk >= pool_blocks) {  // poison block id: nothing is read through it
-      if (nv > 0) best = qnan();
-      continue;
-    }
-    const __amdgpu_buffer_rsrc_t page = page_rsrc(pool + blk * PB, (int)PB);
+    int64_t blk = -1;  // fetched when a row of the run first needs it
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const bool in = tok[q] >= k0 && tok[q] < k1;
+      const int v = in ? s_len[tok[q]] - b * kBlockTokens : 0;
+      const int nv = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
+      if (!__ballot(nv > 0)) continue;  // no row of tile q in the run reaches block b (wave-uniform)
+      if (blk < 0) blk = __builtin_amdgcn_readfirstlane(bt[(size_t)rr * bt_stride + b]);
+      if (blk < 0 || blk >= pool_blocks) {  // poison block id: nothing is read through it
+        if (nv > 0) best[q] = qnan();
+        continue;
+      }
+      const __amdgpu_buffer_rsrc_t page = page_rsrc(pool + blk * PB, (int)PB);
 #pragma unroll 1
-    for (int part = 0; part < PARTS; ++part) {
-      PartRaw<KEY_DT> raw;
-      load_part_raw<KEY_DT>(raw, page, part, lane);
-      PartOps<KEY_DT, Q_DT> ops;
-      part_operands<KEY_DT, Q_DT>(raw, lane, ops);
-      wide_part_max<KEY_DT, Q_DT>(ops, part, qrow, false, nv, lane, best);
+      for (int part = 0; part < PARTS; ++part) {
+        PartRaw<KEY_DT> raw;
+        load_part_raw<KEY_DT>(raw, page, part, lane);
+        PartOps<KEY_DT, Q_DT> ops;
+        part_operands<KEY_DT, Q_DT>(raw, lane, ops);
+        wide_part_max<KEY_DT, Q_DT>(ops, part, qrow[q], false, nv, lane, best[q]);
+      }
     }
   }
-  return best;
 }
 
 // Wave-uniform maximum of an int over the wave.
@@ -527,49 +550,49 @@ __device__ __forceinline__ int wave_max_int(int x) {
   return __builtin_amdgcn_readfirstlane(x);
 }
 
-// grid (ceil(MB / 4), tiles[, tiles a request]), 4 waves a workgroup: wave w
+// grid (ceil(MB / 4), R, tiles a request) for a decode batch (RAGGED false)
+// or (ceil(MB / 4), tiles) for a prefill batch, 4 waves a workgroup: wave w
 // scores block 4 x + w (x from score_column) for the query rows [n0, n1) of
 // the workgroup's tile, which it stages in LDS.  Global query row n = t H_idx
-// + h (token t, index head h).  Tiles of a decode batch (grid (., R, z)):
-// rows [r QR + 128 z, ..) of request r, QR = q H_idx; of a prefill batch
-// (grid (., tiles)): rows [128 y, 128 y + 128) of the whole batch.  The tile's
-// tokens are taken in runs of consecutive tokens of one request (one run
-// whenever a tile holds one request's tokens); each run scores its request's
-// block b against its own rows.  Needs 16 % H_idx == 0, so a 16-row tile
-// holds whole tokens and each KV group's index heads sit on adjacent lanes.
-template <int KEY_DT, int Q_DT>
+// + h (token t, index head h).  A decode tile is rows [r QR + 128 z, ..) of
+// request r (QR = q H_idx): one request, causal lengths from seq_lens.  A
+// prefill tile is rows [128 y, 128 y + 128) of the batch, its tokens taken in
+// runs of consecutive tokens of one request (one run whenever the tile holds
+// one request's tokens); each run scores its request's block b against its
+// own rows.  Needs 16 % H_idx == 0, so a 16-row tile holds whole tokens and
+// each KV group's index heads sit on adjacent lanes.
+template <int KEY_DT, int Q_DT, bool RAGGED>
 __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   constexpr int NT = wide_part_tiles<KEY_DT>();
   constexpr int PARTS = 8 / NT;
   constexpr int QROW = Q_DT == ISB_BF16 ? 2 * kHeadDim : kHeadDim;  // bytes of a query row
   constexpr int TROWS = 16 * kWideTiles;                            // rows of a tile
+  constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
   // LDS pitch of a staged row: 16 bytes past a multiple of 256 puts the 16
   // rows a 16-byte read of a tile touches on distinct banks
   constexpr int QPITCH = QROW + 16;
   __shared__ __attribute__((aligned(16))) uint8_t s_q[TROWS * QPITCH];
-  __shared__ int s_req[TROWS];  // per token of the tile: request and causal length
-  __shared__ int s_len[TROWS];
+  __shared__ int s_req[RAGGED ? TROWS : 1];  // per token of a prefill tile: request and causal length
+  __shared__ int s_len[RAGGED ? TROWS : 1];
+  __shared__ int s_nb[kScoreWaves];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int m = lane & 15;
-  const bool prefill = a.tm.req_id != nullptr;
-  int n0, n1, rot;
-  if (prefill) {
+  int n0, n1;
+  if constexpr (RAGGED) {
     n0 = TROWS * blockIdx.y;
     n1 = min(a.T * a.H_idx, n0 + TROWS);
-    rot = blockIdx.y;
   } else {
     const int QR = a.q_len * a.H_idx;
     n0 = blockIdx.y * QR + TROWS * blockIdx.z;
     n1 = min((int)blockIdx.y * QR + QR, n0 + TROWS);
-    rot = blockIdx.y;
   }
   const int per = a.H_idx / a.H_kv;  // index heads of a KV group
   // H_idx divides 16 and per divides H_idx: both are powers of two, so the
   // row -> (token, head) and head -> group splits are shifts and masks
   const int hsh = __builtin_ctz(a.H_idx), psh = __builtin_ctz(per);
-  const int t0 = n0 >> hsh;                  // first token of the tile
+  const int t0 = n0 >> hsh;                     // first token of the tile
   const int ntok = ((n1 - 1) >> hsh) - t0 + 1;  // its tokens
-  const int col = score_column<kScoreWaves>(blockIdx.x, gridDim.x, rot);
+  const int col = score_column<kScoreWaves>(blockIdx.x, gridDim.x, blockIdx.y);
   const int b = col * kScoreWaves + wave;
   // -inf for every token of the tile at block b (none of them reaches it)
   auto write_unreached = [&]() {
@@ -578,59 +601,79 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
       a.scores[((size_t)gg * a.T + t0 + k) * a.MB + b] = neg_inf();
     }
   };
-  // The first token's block is requested before anything else, so that one
-  // round trip covers its keys, the tile's token data and the query rows.
-  const TokenPos tp0 = token_pos(a.tm, t0);
-  const bool pre = b < a.MB && b * kBlockTokens < tp0.L;
-  int64_t blk0 = 0;
-  if (pre) blk0 = __builtin_amdgcn_readfirstlane(a.bt[(size_t)tp0.r * a.bt_stride + b]);
-  constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
+  // The tile's first request and the blocks it has (decode: the request's
+  // length bounds every token of the tile, and workgroups past its blocks
+  // stop before reading anything else).
+  int r0, nreq;
+  if constexpr (RAGGED) {
+    const TokenPos tp0 = token_pos(a.tm, t0);
+    r0 = tp0.r;
+    nreq = (tp0.L + kBlockTokens - 1) / kBlockTokens;  // the first token's: a lower bound
+  } else {
+    r0 = blockIdx.y;
+    nreq = (a.seq_lens[r0] + kBlockTokens - 1) / kBlockTokens;
+    if (col * kScoreWaves >= nreq) {  // uniform over the workgroup
+      if (b < a.MB) write_unreached();
+      return;
+    }
+  }
+  // The first request's block is requested before anything else, so that
+  // one round trip covers its keys, the tile's token data and the query rows.
+  const bool pre = b < a.MB && b < nreq;
+  int64_t blk = 0;
+  if (pre) blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r0 * a.bt_stride + b]);
   // an out-of-range block id is poison: NaN where the block is causally
   // visible, -inf elsewhere; nothing is read through it
-  const bool bad0 = blk0 < 0 || blk0 >= a.pool_blocks;
+  bool bad = blk < 0 || blk >= a.pool_blocks;
   PartRaw<KEY_DT> raw;
-  if (pre) load_part_raw<KEY_DT>(raw, page_rsrc(a.pool + (bad0 ? 0 : blk0) * PB, (int)PB), 0, lane);
+  if (pre) load_part_raw<KEY_DT>(raw, page_rsrc(a.pool + (bad ? 0 : blk) * PB, (int)PB), 0, lane);
+  // The tile's query rows, as stored (and a prefill tile's tokens: request,
+  // causal length, and the blocks they reach).
   {
     const uint8_t* src = a.q_idx + (size_t)n0 * QROW;
     constexpr int CPR = QROW / 16;  // 16-byte chunks a row
     for (int c = threadIdx.x; c < (n1 - n0) * CPR; c += 256)
       *reinterpret_cast<u32x4*>(s_q + (c / CPR) * QPITCH + (c % CPR) * 16) = ld16(src + (size_t)c * 16);
-    for (int k = threadIdx.x; k < ntok; k += 256) {
-      const TokenPos tp = token_pos(a.tm, t0 + k);
-      s_req[k] = tp.r;
-      s_len[k] = tp.L;
+    if constexpr (RAGGED) {
+      int nb = 0;
+      for (int k = threadIdx.x; k < ntok; k += 256) {
+        const TokenPos tp = token_pos(a.tm, t0 + k);
+        s_req[k] = tp.r;
+        s_len[k] = tp.L;
+        nb = max(nb, (tp.L + kBlockTokens - 1) / kBlockTokens);
+      }
+      nb = wave_max_int(nb);
+      if (lane == 0) s_nb[wave] = nb;
     }
   }
   __syncthreads();
-  // blocks the tile's tokens reach (the same in every wave)
-  int nb = 0;
-  for (int k = lane; k < ntok; k += kWave) nb = max(nb, (s_len[k] + kBlockTokens - 1) / kBlockTokens);
-  const int nmax = wave_max_int(nb);
+  const int nmax = RAGGED ? max(max(s_nb[0], s_nb[1]), max(s_nb[2], s_nb[3])) : nreq;
   if (b >= a.MB) return;
   if (b >= nmax) {
     write_unreached();
     return;
   }
-  // The first run of the tile: its tokens [0, k1) (all of them when the tile
-  // holds one request's tokens).
-  int k1 = ntok;
-  for (int base = 1; base < ntok; base += kWave) {
-    const int k = base + lane;
-    const uint64_t diff = __ballot(k < ntok && s_req[k] != tp0.r);
-    if (diff) {
-      k1 = base + __builtin_ctzll(diff);
-      break;
+  // The first run of the tile: its tokens [0, k1) (all of them in a decode
+  // tile, and in a prefill tile that holds one request's tokens), which reach
+  // nr blocks.
+  int k1 = ntok, nr = nreq;
+  if constexpr (RAGGED) {
+    for (int base = 1; base < ntok; base += kWave) {
+      const int k = base + lane;
+      const uint64_t diff = __ballot(k < ntok && s_req[k] != r0);
+      if (diff) {
+        k1 = base + __builtin_ctzll(diff);
+        break;
+      }
     }
-  }
-  int nr = 0;  // blocks the first run's tokens reach
-  for (int k = lane; k < k1; k += kWave) nr = max(nr, (s_len[k] + kBlockTokens - 1) / kBlockTokens);
-  nr = wave_max_int(nr);
-  int64_t blk = blk0;
-  bool bad = bad0;
-  if (!pre && b < nr) {  // a later token of the first run reaches block b
-    blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)tp0.r * a.bt_stride + b]);
-    bad = blk < 0 || blk >= a.pool_blocks;
-    if (!bad) load_part_raw<KEY_DT>(raw, page_rsrc(a.pool + blk * PB, (int)PB), 0, lane);
+    nr = 0;
+    for (int k = lane; k < k1; k += kWave) nr = max(nr, (s_len[k] + kBlockTokens - 1) / kBlockTokens);
+    nr = wave_max_int(nr);
+    if (!pre && b < nr) {  // a later token of the first run reaches block b
+      blk = __builtin_amdgcn_readfirstlane(a.bt[(size_t)r0 * a.bt_stride + b]);
+      bad = blk < 0 || blk >= a.pool_blocks;
+      if (!bad) load_part_raw<KEY_DT>(raw, page_rsrc(a.pool + blk * PB, (int)PB), 0, lane);
+    }
   }
   // row n = n0 + 16 q + m of each tile q: its causally valid keys in this
   // block if its token is in the first run (0 otherwise)
@@ -638,15 +681,23 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   int nv[kWideTiles];
   const uint8_t* qrow[kWideTiles];  // this lane's staged query row of tile q
   uint32_t full = 0;                // bit q: every row of tile q sees the whole block
+  uint32_t act = 0;                 // bit q: tile q has rows in the first run
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
     const int n = n0 + 16 * q + m;
     const int k = (n >> hsh) - t0;
-    const int v = n < n1 && k < k1 ? s_len[k] - b * kBlockTokens : 0;
+    int v = 0;
+    if constexpr (RAGGED) {
+      v = n < n1 && k < k1 ? s_len[k] - b * kBlockTokens : 0;
+    } else {  // token t = r q + i: length seq_lens[r] - (q - 1 - i)
+      const int i = (n >> hsh) - r0 * a.q_len;
+      v = n < n1 ? a.seq_lens[r0] - (a.q_len - 1 - i) - b * kBlockTokens : 0;
+    }
     nv[q] = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
     best[q] = neg_inf();
     qrow[q] = s_q + ((n < n1 ? n : n0) - n0) * QPITCH;
     if (__ballot(nv[q] == kBlockTokens) == ~0ull) full |= 1u << q;
+    if (n0 + 16 * q < n1 && ((n0 + 16 * q) >> hsh) - t0 < k1) act |= 1u << q;
   }
   if (b < nr) {
     if (bad) {
@@ -662,22 +713,21 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
         if (part + 1 < PARTS) load_part_raw<KEY_DT>(raw, page, part + 1, lane);  // in flight during this part
 #pragma unroll
         for (int q = 0; q < kWideTiles; ++q)
-          if (n0 + 16 * q < n1 && ((n0 + 16 * q) >> hsh) - t0 < k1)  // wave-uniform: the tile has rows in the run
+          if ((act >> q) & 1u)  // wave-uniform
             wide_part_max<KEY_DT, Q_DT>(ops, part, qrow[q], (full >> q) & 1u, nv[q], lane, best[q]);
       }
     }
   }
-  if (k1 < ntok) {  // tokens of other requests in the tile (wave-uniform)
+  if constexpr (RAGGED) {
+    if (k1 < ntok) {  // tokens of other requests in the tile (wave-uniform)
+      int tok[kWideTiles];
 #pragma unroll
-    for (int q = 0; q < kWideTiles; ++q) {
-      const int lo = n0 + 16 * q;
-      if (lo >= n1) continue;
-      const int thi = (min(lo + 16, n1) - 1 - n0) >> hsh;  // last token of the 16-row tile
-      if (thi < k1) continue;
-      const int n = lo + m;
-      best[q] = wide_other_runs<KEY_DT, Q_DT>(a.pool, a.pool_blocks, a.bt, a.bt_stride, s_req, s_len, qrow[q], b,
-                                              k1, ntok, n < n1 ? (n >> hsh) - t0 : -1, (lo - n0) >> hsh, thi,
-                                              best[q]);
+      for (int q = 0; q < kWideTiles; ++q) {
+        const int n = n0 + 16 * q + m;
+        tok[q] = n < n1 ? (n >> hsh) - t0 : -1;
+      }
+      wide_other_runs<KEY_DT, Q_DT, kWideTiles>(a.pool, a.pool_blocks, a.bt, a.bt_stride, s_req, s_len, qrow, tok,
+                                                b, k1, ntok, best);
     }
   }
 #pragma unroll
@@ -761,11 +811,12 @@ static void launch_wide(const ScoreArgs& a, hipStream_t st) {
   dim3 grid;
   if (a.tm.req_id) {
     grid = dim3(cols, (unsigned)(((long long)a.T * a.H_idx + TROWS - 1) / TROWS));
+    hipLaunchKernelGGL((index_wide_kernel<KEY_DT, Q_DT, true>), grid, dim3(256), 0, st, a);
   } else {
     const int QR = a.q_len * a.H_idx;
     grid = dim3(cols, a.R, (QR + TROWS - 1) / TROWS);
+    hipLaunchKernelGGL((index_wide_kernel<KEY_DT, Q_DT, false>), grid, dim3(256), 0, st, a);
   }
-  hipLaunchKernelGGL((index_wide_kernel<KEY_DT, Q_DT>), grid, dim3(256), 0, st, a);
 }
 
 template <int KEY_DT, int Q_DT>

@@ -181,6 +181,18 @@ __device__ __forceinline__ f32x4 mfma_scale_fp4_e4m3(i32x8 a, i32x8 b, f32x4 c, 
   return d;
 }
 
+// The same instruction with A and B both in e4m3, unit scales: lane
+// l = 16 g + r supplies 32 bytes of row r of A and of column r of B, and byte
+// j of a lane group's A lanes meets byte j of the same group's B lanes in
+// the sum (the 8-bit layout above is the same for A and B), so any placement
+// of the 128 k values over a group's 32 bytes that A and B share gives the
+// whole dot product.
+__device__ __forceinline__ f32x4 mfma_scale_e4m3(i32x8 a, i32x8 b, f32x4 c) {
+  f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  asm volatile("" ::"v"(a), "v"(b));
+  return d;
+}
+
 // ----------------------------------------------------------------- cross-lane
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
