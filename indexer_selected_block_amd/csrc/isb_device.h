@@ -152,19 +152,26 @@ __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c)
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 // The same product with both sources kept live past the instruction (an
-// empty asm reads them), for kernels whose register budget is tight enough
-// that the allocator would otherwise place the destination over a source
-// register; see mfma_scale_fp4_e4m3.
+// empty asm that takes the result reads them, so it cannot be placed before
+// the product), for kernels whose register budget is tight enough that the
+// allocator would otherwise place the destination over a source register;
+// see mfma_scale_fp4_e4m3.
 template <bool KEEP>
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16_k(bf16x8 a, bf16x8 b, f32x4 c) {
   f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  if constexpr (KEEP) asm volatile("" ::"v"(a), "v"(b));
+  if constexpr (KEEP) asm volatile("" : "+v"(d) : "v"(a), "v"(b));
   return d;
 }
 // v_mfma_f32_16x16x16_bf16: lane l = 16 g + r supplies A[r][4 g + i] and
 // B[4 g + i][r] (i < 4); result as above.
 __device__ __forceinline__ f32x4 mfma_16x16x16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+template <bool KEEP>
+__device__ __forceinline__ f32x4 mfma_16x16x16_bf16_k(bf16x4 a, bf16x4 b, f32x4 c) {
+  f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  if constexpr (KEEP) asm volatile("" : "+v"(d) : "v"(a), "v"(b));
+  return d;
 }
 // v_mfma_scale_f32_16x16x128_f8f6f4 with A in e2m1 and B in e4m3:
 //   A lane l = 16 g + r: row r, k = 32 g .. 32 g + 31 as 32 nibbles in the

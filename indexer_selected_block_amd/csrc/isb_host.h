@@ -82,7 +82,6 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   const int rounds = (p.max_pages + p.pages_per_round - 1) / p.pages_per_round;  // of a whole row
   const int resident = kPaResidentWaves / p.waves;  // workgroups the chip holds at once
   int want = (resident + p.rows - 1) / (p.rows > 0 ? p.rows : 1);
-  if (kv_dtype == ISB_MXFP4) want = rounds;  // MXFP4 rows are short: one round a split
   if (want > rounds) want = rounds;
   if (want < 1) want = 1;
   const int rounds_per_split = (rounds + want - 1) / want;

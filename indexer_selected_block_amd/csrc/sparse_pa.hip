@@ -713,151 +713,191 @@ __global__ __launch_bounds__(64 * NW) void pa16sel_kernel(PaArgs a, SelArgs sa) 
 }
 
 // ----------------------------------------------------------------- MXFP4 pages
-// One 128-token page a wave (eight 16-key tiles): page p0 + wave of the
-// row's split, whose id is id_raw (-1 past the row's pages).
+// The query operand of an MXFP4 row: e4m3 bytes as the scaled MFMA's B
+// operand (dims 16 g .. and 64 + 16 g ..), or bf16 operands; zero past the
+// group's G heads.
 template <int Q_DT>
-__device__ __forceinline__ void attend_split_mx(const PaArgs& a, WaveParts<4>& wp, int row, int split, int t,
-                                                int kvh, int n_tok, int32_t id_raw, __bf16* out_row) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
+struct MxQuery {
+  i32x8 q8;
+  bf16x8 qb[4];
+};
+
+template <int Q_DT>
+__device__ __forceinline__ MxQuery<Q_DT> load_mx_query(const PaArgs& a, int t, int kvh, int lane) {
   const int c = lane & 15, g = lane >> 4;
+  const int hc = c < a.G ? c : 0;
+  const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * (Q_DT == ISB_BF16 ? 2 : 1);
+  MxQuery<Q_DT> mq;
+  if constexpr (Q_DT == ISB_FP8_E4M3) {
+    const u32x4 lo = ld16(qrow + 16 * g), hi = ld16(qrow + 64 + 16 * g);
+    mq.q8 = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    if (c >= a.G) mq.q8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mq.qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
+    zero_missing_heads(mq.qb, c, a.G);
+  }
+  return mq;
+}
+
+// Page p of a row (one 128-token MXFP4 page: eight 16-key tiles) whose id is
+// id (wave-uniform), folded into the wave's running max M (per head), sum
+// share lsum and output o.  KEEP: pin MFMA operands live (see
+// mfma_16x16x32_bf16_k).
+template <int Q_DT, bool KEEP>
+__device__ __forceinline__ void attend_page_mx(const PaArgs& a, int lane, int kvh, int n_tok, int p, int64_t id,
+                                               const MxQuery<Q_DT>& mq, bool first, float& M, float& lsum,
+                                               f32x4 (&o)[8]) {
+  const int c = lane & 15, g = lane >> 4;
+  const bool ok = page_ok(id, a.num_pages);
+  const int64_t pg = ((ok ? id : 0) * a.H_kv + kvh) * kMxPageBytes;
+  const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kp + pg, kMxPageBytes);
+  const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vp + pg, kMxPageBytes);
+  u32x4 kd[8];
+  uint32_t ks[8];
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    kd[tt] = bl16(rk, 64 * c + 16 * g, 1024 * tt);
+    ks[tt] = bl4(rk, 4 * c, kMxDataBytes + 64 * tt);
+  }
+  // V: keys 16 tt + 4 g + e of tile tt, the word of dims 8 c .. 8 c + 7,
+  // and the four keys' scale words (one 16-byte load a tile)
+  uint32_t vw[8][4];
+  u32x4 vs[8];
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vw[tt][e] = bl4(rv, 64 * (4 * g + e) + 4 * c, 1024 * tt);
+    vs[tt] = bl16(rv, 16 * g, kMxDataBytes + 64 * tt);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int nvp = min(kBlockTokens, n_tok - p * kBlockTokens);  // keys of the page that count
+  // Pass 1: the page's logits and one exact max per head.
+  float z[8][4];
+  float mx = neg_inf();
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t sbyte = (ks[tt] >> (8 * g)) & 0xFFu;
+    if constexpr (Q_DT == ISB_FP8_E4M3) {
+      const i32x8 ka = {(int)kd[tt][0], (int)kd[tt][1], (int)kd[tt][2], (int)kd[tt][3], 0, 0, 0, 0};
+      s = mfma_scale_fp4_e4m3(ka, mq.q8, s, (int)sbyte);
+    } else {
+      const float sc = e8m0_to_f32(sbyte);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = mfma_16x16x32_bf16_k<KEEP>(e2m1x8_to_bf16x8(kd[tt][j], sc), mq.qb[j], s);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = ok ? s[e] * a.qk_scale : qnan();
+      z[tt][e] = 16 * tt + 4 * g + e < nvp ? v : neg_inf();
+      mx = fmaxf(mx, z[tt][e]);
+    }
+  }
+  mx = max_over_groups(mx);
+  const float m_new = fmaxf(M, mx);
+  if (!first) {
+    const float alpha = M == m_new ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+  }
+  M = m_new;
+  // Pass 2: probabilities and P.V.  Lane (g, c) takes keys 4 g + e of the
+  // tile and dims 8 c .. 8 c + 7 (one data word, one scale byte per key);
+  // MFMA dt gets dim 8 c + dt.
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pr[e] = __builtin_amdgcn_exp2f(z[tt][e] - M);
+      lsum += pr[e];
+    }
+    const bf16x4 pb = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
+    bf16x8 vv[4];  // key e: dims 8 c .. 8 c + 7
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = 16 * tt + 4 * g + e;
+      const bool on = tok < nvp;  // keys past the length may be poison: zero, unit scale
+      const uint32_t w = on ? vw[tt][e] : 0u;
+      const uint32_t sw = vs[tt][e];
+      const float sc = on ? e8m0_to_f32((sw >> (8 * (c >> 2))) & 0xFFu) : 1.f;
+      vv[e] = e2m1x8_to_bf16x8(w, sc);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x4 vt = {vv[0][dt], vv[1][dt], vv[2][dt], vv[3][dt]};
+      o[dt] = mfma_16x16x16_bf16_k<KEEP>(vt, pb, o[dt]);
+    }
+  }
+}
+
+// The attention of one split of an MXFP4 row: page p0 + NW r + wave in round
+// r.  ids(r0): this lane's page id for round r0 + lane of this wave (-1 past
+// the split), fetched 64 rounds at a time and read out a round at a time.
+template <int Q_DT, int NW, typename IdFn>
+__device__ __forceinline__ void attend_split_mx(const PaArgs& a, WaveParts<NW>& wp, int row, int split, int t,
+                                                int kvh, int n_tok, IdFn ids, __bf16* out_row) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int p0 = split * a.pps;
-  const int p = p0 + wave;
   if (n_tok <= 0) {
     write_empty_row(a, split, out_row);
     return;
   }
   const int npages = min((n_tok + kBlockTokens - 1) / kBlockTokens, a.sbt_stride);
   if (p0 >= npages) return;
+  const int p1 = min(npages, p0 + a.pps);
   const int live = (npages + a.pps - 1) / a.pps;
-
-  float mx = neg_inf(), lsum = 0.f;
+  float M = neg_inf(), lsum = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (p < npages) {
-    const int hc = c < a.G ? c : 0;
-    const uint8_t* qrow = a.q + ((size_t)t * a.H_q + kvh * a.G + hc) * kHeadDim * (Q_DT == ISB_BF16 ? 2 : 1);
-    // query first (the load counter is in order): e4m3 bytes as the scaled
-    // MFMA's B operand (dims 16 g .. and 64 + 16 g ..), or bf16 operands
-    i32x8 q8;
-    bf16x8 qb[4];
-    if constexpr (Q_DT == ISB_FP8_E4M3) {
-      const u32x4 lo = ld16(qrow + 16 * g), hi = ld16(qrow + 64 + 16 * g);
-      q8 = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
-    }
-    const int64_t id = __builtin_amdgcn_readfirstlane(id_raw);
-    const bool ok = page_ok(id, a.num_pages);
-    const int64_t pg = ((ok ? id : 0) * a.H_kv + kvh) * kMxPageBytes;
-    const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kp + pg, kMxPageBytes);
-    const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vp + pg, kMxPageBytes);
-    u32x4 kd[8];
-    uint32_t ks[8];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      kd[tt] = bl16(rk, 64 * c + 16 * g, 1024 * tt);
-      ks[tt] = bl4(rk, 4 * c, kMxDataBytes + 64 * tt);
-    }
-    // V: keys 16 tt + 4 g + e of tile tt, the word of dims 8 c .. 8 c + 7,
-    // and the four keys' scale words (one 16-byte load a tile)
-    uint32_t vw[8][4];
-    u32x4 vs[8];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vw[tt][e] = bl4(rv, 64 * (4 * g + e) + 4 * c, 1024 * tt);
-      vs[tt] = bl16(rv, 16 * g, kMxDataBytes + 64 * tt);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (Q_DT == ISB_FP8_E4M3) {
-      if (c >= a.G) q8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    } else {
-      zero_missing_heads(qb, c, a.G);
-    }
-    const int nvp = min(kBlockTokens, n_tok - p * kBlockTokens);  // keys of the page that count
-    // Pass 1: the page's logits and one exact max per head.
-    float z[8][4];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      const uint32_t sbyte = (ks[tt] >> (8 * g)) & 0xFFu;
-      if constexpr (Q_DT == ISB_FP8_E4M3) {
-        const i32x8 ka = {(int)kd[tt][0], (int)kd[tt][1], (int)kd[tt][2], (int)kd[tt][3], 0, 0, 0, 0};
-        s = mfma_scale_fp4_e4m3(ka, q8, s, (int)sbyte);
-      } else {
-        const float sc = e8m0_to_f32(sbyte);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s = mfma_16x16x32_bf16(e2m1x8_to_bf16x8(kd[tt][j], sc), qb[j], s);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = ok ? s[e] * a.qk_scale : qnan();
-        z[tt][e] = 16 * tt + 4 * g + e < nvp ? v : neg_inf();
-        mx = fmaxf(mx, z[tt][e]);
-      }
-    }
-    mx = max_over_groups(mx);
-    // Pass 2: probabilities and P.V.  Lane (g, c) takes keys 4 g + e of the
-    // tile and dims 8 c .. 8 c + 7 (one data word, one scale byte per key);
-    // MFMA dt gets dim 8 c + dt.
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      float pr[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(z[tt][e] - mx);
-        lsum += pr[e];
-      }
-      const bf16x4 pb = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
-      bf16x8 vv[4];  // key e: dims 8 c .. 8 c + 7
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 16 * tt + 4 * g + e;
-        const bool on = tok < nvp;  // keys past the length may be poison: zero, unit scale
-        const uint32_t w = on ? vw[tt][e] : 0u;
-        const uint32_t sw = vs[tt][e];
-        const float sc = on ? e8m0_to_f32((sw >> (8 * (c >> 2))) & 0xFFu) : 1.f;
-        vv[e] = e2m1x8_to_bf16x8(w, sc);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16x4 vt = {vv[0][dt], vv[1][dt], vv[2][dt], vv[3][dt]};
-        o[dt] = mfma_16x16x16_bf16(vt, pb, o[dt]);
-      }
+  if (p0 + wave < p1) {  // wave-uniform: this wave has pages in the split
+    int32_t my_ids = ids(0);
+    const MxQuery<Q_DT> mq = load_mx_query<Q_DT>(a, t, kvh, lane);
+    for (int r = 0, p = p0 + wave; p < p1; ++r, p += NW) {
+      if (r > 0 && r % kWave == 0) my_ids = ids(r);
+      const int64_t id = __builtin_amdgcn_readlane(my_ids, r % kWave);
+      attend_page_mx<Q_DT, NW == 8>(a, lane, kvh, n_tok, p, id, mq, r == 0, M, lsum, o);
     }
   }
-  wave_to_lds<8, 1, 4>(wp, wave, lane, mx, lsum, o);  // row r of tile dt: dim 8 r + dt
-  finish_split<4>(a, wp, row, split, live, out_row);
+  wave_to_lds<8, 1, NW>(wp, wave, lane, M, lsum, o);  // row r of tile dt: dim 8 r + dt
+  finish_split<NW>(a, wp, row, split, live, out_row);
 }
 
-// grid (rows, splits); page ids come from the sparse page table.
-template <int Q_DT>
-__global__ __launch_bounds__(256) void pamx_kernel(PaArgs a) {
-  __shared__ WaveParts<4> wp;
+// grid (rows, splits), NW waves a workgroup; page ids come from the sparse
+// page table.
+template <int Q_DT, int NW>
+__global__ __launch_bounds__(64 * NW) void pamx_kernel(PaArgs a) {
+  __shared__ WaveParts<NW> wp;
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
-  const int p = split * a.pps + wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int n_tok = a.sctx[row];
-  const int32_t id_raw = p < a.sbt_stride ? a.sbt[(size_t)row * a.sbt_stride + p] : -1;
+  const int pend = min(a.sbt_stride, (split + 1) * a.pps);
+  const int32_t* pages = a.sbt + (size_t)row * a.sbt_stride;
+  auto ids = [&](int r0) {  // this wave's page of round r0 + lane
+    const int p = split * a.pps + NW * (r0 + lane) + wave;
+    return p < pend ? pages[p] : -1;
+  };
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  attend_split_mx<Q_DT>(a, wp, row, split, t, kvh, n_tok, id_raw, out_row);
+  attend_split_mx<Q_DT, NW>(a, wp, row, split, t, kvh, n_tok, ids, out_row);
 }
 
 // Selection and attention of a row in one launch for MXFP4 pages (one page a
-// block) and rows of up to kSelMaxBlocks blocks, as pa16sel_kernel does for
-// 16-token pages: every workgroup of a row selects the row's blocks from its
-// scores and block-table row, split 0 also writes the selection, the page
-// table and the sparse length.
-template <int Q_DT, int E, bool BTL>
-__global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
-  __shared__ WaveParts<4> wp;
-  __shared__ SelectLds<256> sl;
+// block), as pa16sel_kernel does for 16-token pages: every workgroup of a row
+// selects the row's blocks from its scores and block-table row, split 0 also
+// writes the selection, the page table and the sparse length.
+template <int Q_DT, int NW, int E, bool BTL>
+__global__ __launch_bounds__(64 * NW) void pamxsel_kernel(PaArgs a, SelArgs sa) {
+  constexpr int NT_ = 64 * NW;
+  __shared__ WaveParts<NW> wp;
+  __shared__ SelectLds<NT_> sl;
   __shared__ int32_t s_bt[BTL ? kSelMaxBlocks : 1];
   __shared__ int32_t s_sel[kSelMaxBlocks];
   const int row = grid_row(blockIdx.x, gridDim.x), split = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int t = row / a.H_kv, kvh = row % a.H_kv;
   const int trow = kvh * sa.T + t;  // the row's index in the score and selection buffers
   const TokenPos tp = token_pos(sa.tm, t);
@@ -873,26 +913,30 @@ __global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
       if (E * tid + x < sa.MB) s_bt[E * tid + x] = btv[x];
   }
   int32_t* o = sa.topk + (size_t)trow * sa.K;
-  const int m = select_row<256, E>(sc, nt, sa.K, sl, [&](int k, int b) {
+  const int m = select_row<NT_, E>(sc, nt, sa.K, sl, [&](int k, int b) {
     s_sel[k] = b;
     if (split == 0) o[k] = b;
   });
   __syncthreads();  // the selection (and the block-table row) are in LDS
   if constexpr (!BTL) {  // the selected blocks' ids, in place of their indices
-    for (int k = tid; k < m; k += 256) s_sel[k] = sa.bt[(size_t)tp.r * sa.bt_stride + s_sel[k]];
+    for (int k = tid; k < m; k += NT_) s_sel[k] = sa.bt[(size_t)tp.r * sa.bt_stride + s_sel[k]];
     __syncthreads();
   }
   auto blk = [&](int k) { return BTL ? s_bt[s_sel[k]] : s_sel[k]; };
   const int n_tok = m > 0 ? (m - 1) * kBlockTokens + (Lt - kBlockTokens * (nt - 1)) : 0;
   if (split == 0) {  // one page a block: the row's k-th page is its k-th selected block
     int32_t* so = sa.sbt + (size_t)row * sa.K;
-    for (int x = tid; x < sa.K; x += 256) so[x] = x < m ? blk(x) : -1;
+    for (int x = tid; x < sa.K; x += NT_) so[x] = x < m ? blk(x) : -1;
     if (tid == 0) sa.sctx[row] = n_tok;
   }
-  const int p = split * a.pps + wave_id();
-  const int32_t id_raw = p < m ? blk(p) : -1;
+  const int wave = wave_id();
+  const int pend = min(m, (split + 1) * a.pps);
+  auto ids = [&](int r0) {  // this wave's page of round r0 + lane
+    const int p = split * a.pps + NW * (r0 + lane) + wave;
+    return p < pend ? blk(p) : -1;
+  };
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  attend_split_mx<Q_DT>(a, wp, row, split, t, kvh, n_tok, id_raw, out_row);
+  attend_split_mx<Q_DT, NW>(a, wp, row, split, t, kvh, n_tok, ids, out_row);
 }
 
 // nt: one query token a request, so no page is read twice in the launch;
@@ -900,8 +944,8 @@ __global__ __launch_bounds__(256) void pamxsel_kernel(PaArgs a, SelArgs sa) {
 template <int KV_DT, int Q_DT>
 static void launch_decode(const PaArgs& a, dim3 grid, bool nt, const PaPlan& plan, hipStream_t st) {
   const int nw = plan.waves;
-  if constexpr (KV_DT == ISB_MXFP4) {
-    hipLaunchKernelGGL((pamx_kernel<Q_DT>), grid, dim3(256), 0, st, a);
+  if constexpr (KV_DT == ISB_MXFP4) {  // the plan gives MXFP4 rows four waves a workgroup
+    hipLaunchKernelGGL((pamx_kernel<Q_DT, 4>), grid, dim3(256), 0, st, a);
   } else {
     constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
     if (plan.row_wave) {
@@ -983,7 +1027,7 @@ static int pa_setup(const void* q, int q_dtype, const void* k_pool, const void* 
 template <int KV_DT, int Q_DT, int NW, int E, bool BTL>
 static void launch_select_attend_e(const PaArgs& a, const SelArgs& sa, dim3 grid, bool nt, hipStream_t st) {
   if constexpr (KV_DT == ISB_MXFP4) {
-    hipLaunchKernelGGL((pamxsel_kernel<Q_DT, E, BTL>), grid, dim3(256), 0, st, a, sa);
+    hipLaunchKernelGGL((pamxsel_kernel<Q_DT, NW, E, BTL>), grid, dim3(64 * NW), 0, st, a, sa);
   } else {
     constexpr int RUN = KV_DT == ISB_BF16 ? 4 : 8;
     const dim3 b(64 * NW);
