@@ -492,19 +492,31 @@ __device__ __forceinline__ void wide_part_max(const PartOps<KEY_DT, Q_DT>& k, in
 
 // Tiles that hold tokens of several requests: the tile's 16-row tiles
 // against block b of every run of its tokens [k_begin, ntok) after the first,
-// folded into best[q] (lane row m of tile q: token tok[q], -1 past the tile;
-// staged query row qrow[q]).  A slow path with little state, so that the
-// single-run path keeps its register budget: each run reads its block's keys
-// again for every 16-row tile it has rows in, a part at a time.
+// folded into best[q] (lane row m of tile q: row n0 + 16 q + m of the tile
+// [n0, n1), staged at s_q + (16 q + m) qpitch).  Each run reads its block once,
+// a part at a time, and runs it against every 16-row tile with rows in the
+// run; the rows' running maxima wait in this wave's LDS slice s_best
+// [NQ][64] meanwhile, so the loops stay rolled and the path holds few
+// registers (the single-run path keeps its budget).
 template <int KEY_DT, int Q_DT, int NQ>
 __device__ __forceinline__ void wide_other_runs(const uint8_t* pool, int64_t pool_blocks, const int32_t* bt,
                                                 int bt_stride, const int* s_req, const int* s_len,
-                                                const uint8_t* const (&qrow)[NQ], const int (&tok)[NQ], int b,
-                                                int k_begin, int ntok, float (&best)[NQ]) {
+                                                const uint8_t* s_q, int qpitch, int n0, int n1, int t0, int hsh,
+                                                float* s_best, int b, int k_begin, int ntok, float (&best)[NQ]) {
   constexpr int NT = wide_part_tiles<KEY_DT>();
   constexpr int PARTS = 8 / NT;
   constexpr int64_t PB = KEY_DT == ISB_BF16 ? 32768 : KEY_DT == ISB_FP8_E4M3 ? 16384 : kMxPageBytes;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, m = lane & 15;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) s_best[64 * q + lane] = best[q];
+  // row n0 + 16 q + m: its token's causally valid keys in block b if the
+  // token is in tokens [k0, k1), else 0
+  auto row_nv = [&](int q, int k0, int k1) {
+    const int n = n0 + 16 * q + m;
+    const int k = (n >> hsh) - t0;
+    const int v = n < n1 && k >= k0 && k < k1 ? s_len[k] - b * kBlockTokens : 0;
+    return v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
+  };
 #pragma unroll 1
   for (int k0 = k_begin, k1 = 0; k0 < ntok; k0 = k1) {
     const int rr = __builtin_amdgcn_readfirstlane(s_req[k0]);
@@ -518,29 +530,38 @@ __device__ __forceinline__ void wide_other_runs(const uint8_t* pool, int64_t poo
         break;
       }
     }
-    int64_t blk = -1;  // fetched when a row of the run first needs it
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const bool in = tok[q] >= k0 && tok[q] < k1;
-      const int v = in ? s_len[tok[q]] - b * kBlockTokens : 0;
-      const int nv = v < 0 ? 0 : (v > kBlockTokens ? kBlockTokens : v);
-      if (!__ballot(nv > 0)) continue;  // no row of tile q in the run reaches block b (wave-uniform)
-      if (blk < 0) blk = __builtin_amdgcn_readfirstlane(bt[(size_t)rr * bt_stride + b]);
-      if (blk < 0 || blk >= pool_blocks) {  // poison block id: nothing is read through it
-        if (nv > 0) best[q] = qnan();
-        continue;
-      }
-      const __amdgpu_buffer_rsrc_t page = page_rsrc(pool + blk * PB, (int)PB);
+    uint32_t has = 0;  // bit q: a row of tile q is in the run and reaches block b
 #pragma unroll 1
-      for (int part = 0; part < PARTS; ++part) {
-        PartRaw<KEY_DT> raw;
-        load_part_raw<KEY_DT>(raw, page, part, lane);
-        PartOps<KEY_DT, Q_DT> ops;
-        part_operands<KEY_DT, Q_DT>(raw, lane, ops);
-        wide_part_max<KEY_DT, Q_DT>(ops, part, qrow[q], false, nv, lane, best[q]);
+    for (int q = 0; q < NQ; ++q)
+      if (__ballot(row_nv(q, k0, k1) > 0)) has |= 1u << q;
+    if (!has) continue;  // wave-uniform
+    const int64_t blk = __builtin_amdgcn_readfirstlane(bt[(size_t)rr * bt_stride + b]);
+    if (blk < 0 || blk >= pool_blocks) {  // poison block id: nothing is read through it
+#pragma unroll 1
+      for (int q = 0; q < NQ; ++q)
+        if (row_nv(q, k0, k1) > 0) s_best[64 * q + lane] = qnan();
+      continue;
+    }
+    const __amdgpu_buffer_rsrc_t page = page_rsrc(pool + blk * PB, (int)PB);
+#pragma unroll 1
+    for (int part = 0; part < PARTS; ++part) {
+      PartRaw<KEY_DT> raw;
+      load_part_raw<KEY_DT>(raw, page, part, lane);
+      PartOps<KEY_DT, Q_DT> ops;
+      part_operands<KEY_DT, Q_DT>(raw, lane, ops);
+#pragma unroll 1
+      for (int q = 0; q < NQ; ++q) {
+        if (!((has >> q) & 1u)) continue;  // wave-uniform
+        const int n = n0 + 16 * q + m;
+        const uint8_t* qrow = s_q + ((n < n1 ? n : n0) - n0) * qpitch;
+        float bq = s_best[64 * q + lane];
+        wide_part_max<KEY_DT, Q_DT>(ops, part, qrow, false, row_nv(q, k0, k1), lane, bq);
+        s_best[64 * q + lane] = bq;
       }
     }
   }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) best[q] = s_best[64 * q + lane];
 }
 
 // Wave-uniform maximum of an int over the wave.
@@ -575,6 +596,7 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   __shared__ int s_req[RAGGED ? TROWS : 1];  // per token of a prefill tile: request and causal length
   __shared__ int s_len[RAGGED ? TROWS : 1];
   __shared__ int s_nb[kScoreWaves];
+  __shared__ float s_best[RAGGED ? kScoreWaves * kWideTiles * kWave : 1];  // the later runs' row maxima
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int m = lane & 15;
   int n0, n1;
@@ -592,7 +614,13 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   const int hsh = __builtin_ctz(a.H_idx), psh = __builtin_ctz(per);
   const int t0 = n0 >> hsh;                     // first token of the tile
   const int ntok = ((n1 - 1) >> hsh) - t0 + 1;  // its tokens
-  const int col = score_column<kScoreWaves>(blockIdx.x, gridDim.x, blockIdx.y);
+  // The tile's first request (decode: the tile's request).  Its index also
+  // rotates the column -> die map, so that the tiles of one request (and a
+  // ragged tile's first run) fetch a block on the same die, where the tiles
+  // after the first find it in L2.
+  TokenPos tp0{(int)blockIdx.y, 0};
+  if constexpr (RAGGED) tp0 = token_pos(a.tm, t0);
+  const int col = score_column<kScoreWaves>(blockIdx.x, gridDim.x, tp0.r);
   const int b = col * kScoreWaves + wave;
   // -inf for every token of the tile at block b (none of them reaches it)
   auto write_unreached = [&]() {
@@ -606,7 +634,6 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
   // stop before reading anything else).
   int r0, nreq;
   if constexpr (RAGGED) {
-    const TokenPos tp0 = token_pos(a.tm, t0);
     r0 = tp0.r;
     nreq = (tp0.L + kBlockTokens - 1) / kBlockTokens;  // the first token's: a lower bound
   } else {
@@ -719,16 +746,10 @@ __global__ __launch_bounds__(256) void index_wide_kernel(ScoreArgs a) {
     }
   }
   if constexpr (RAGGED) {
-    if (k1 < ntok) {  // tokens of other requests in the tile (wave-uniform)
-      int tok[kWideTiles];
-#pragma unroll
-      for (int q = 0; q < kWideTiles; ++q) {
-        const int n = n0 + 16 * q + m;
-        tok[q] = n < n1 ? (n >> hsh) - t0 : -1;
-      }
-      wide_other_runs<KEY_DT, Q_DT, kWideTiles>(a.pool, a.pool_blocks, a.bt, a.bt_stride, s_req, s_len, qrow, tok,
-                                                b, k1, ntok, best);
-    }
+    if (k1 < ntok)  // tokens of other requests in the tile (wave-uniform)
+      wide_other_runs<KEY_DT, Q_DT, kWideTiles>(a.pool, a.pool_blocks, a.bt, a.bt_stride, s_req, s_len, s_q, QPITCH,
+                                                n0, n1, t0, hsh, s_best + wave * kWideTiles * kWave, b, k1, ntok,
+                                                best);
   }
 #pragma unroll
   for (int q = 0; q < kWideTiles; ++q) {
