@@ -186,9 +186,10 @@ def scorer_is_wide(cfg, ragged=False):
 
 # dense MFMA peaks of MI355X (TFLOP/s) for the scorer's operand types: bf16
 # operands (bf16 / fp8 keys converted to bf16, or MXFP4 keys with a bf16 query),
-# or MXFP4 keys with an e4m3 query on the scaled fp8/fp4 instruction (fp8 rate)
+# or fp8 / MXFP4 keys with an e4m3 query on the scaled fp8/fp4 instruction
+# (fp8 rate)
 def mfma_peak_tflops(cfg):
-    return 5000.0 if (cfg.idx_dtype == "mxfp4" and cfg.qidx_dtype == "e4m3") else 2500.0
+    return 5000.0 if (cfg.idx_dtype in ("fp8", "mxfp4") and cfg.qidx_dtype == "e4m3") else 2500.0
 
 
 def kernel_sources_sha():

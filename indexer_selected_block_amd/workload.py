@@ -149,6 +149,16 @@ CONFIGS: dict[str, Config] = {
         pool_blocks=4 * 512 + 64, key_dist="normal", seed=6,
         description="4 requests x 512-token prefill chunks, contexts U{16384..65536}, fp8 K/V and index, "
                     "top-k 16 per token"),
+    # The same chunks with the index query cast to unit-scale e4m3 (the index
+    # query form of the MXFP4 path, here against fp8 keys): the scorer then
+    # multiplies keys as stored on the fp8 MFMA.
+    "prefill_e4m3q": Config(
+        "prefill_e4m3q", num_reqs=4, query_len=512, ctx_lo=16384, ctx_hi=65536, num_pad_reqs=0,
+        num_kv_heads=1, num_q_heads=16, num_idx_heads=1, top_k=16,
+        idx_dtype="fp8", kv_dtype="fp8", q_dtype="bf16", qidx_dtype="e4m3",
+        pool_blocks=4 * 512 + 64, key_dist="normal", seed=6,
+        description="4 requests x 512-token prefill chunks, contexts U{16384..65536}, fp8 K/V and index, "
+                    "e4m3 index query, top-k 16 per token"),
 }
 
 

@@ -504,7 +504,7 @@ def test_layer_replays_from_a_hip_graph(name):
 
 # ------------------------------------------------------------------ full size, sampled
 FULL_SAMPLES = {"tiny_bf16": [0, 1, 2, 3], "fp8_decode": [3, 77], "spec_decode": None,
-                "mxfp4": [5, 60], "long_context": [6], "prefill": [2]}
+                "mxfp4": [5, 60], "long_context": [6], "prefill": [2], "prefill_e4m3q": [1]}
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLES))
