@@ -8,19 +8,21 @@
 // [0, n_t - 1), ties to the lower block index; NaN ranks below every number
 // and -0.0 equals +0.0.  The selection is written ascending and padded with -1.
 //
-// Method: radix select on order-preserving 32-bit keys.  Four 8-bit passes
-// each count, per wave, the keys that match the prefix found so far into a
-// 256-bin LDS histogram (no contention between waves); the waves' bins are
-// summed and the digit where the count of larger keys reaches top_k - 1 is
-// found with a wave-wide prefix sum.  With four waves every wave finds the
-// digit itself from histograms that alternate between two buffers, so a pass
-// has one barrier; with more waves wave 0 finds it and hands it over in LDS
-// (two barriers).  The passes stop early once the keys under the prefix
-// found so far are exactly the ones still needed.  Keys above the threshold
-// (compared under the prefix's mask) are taken, and keys equal to it are taken
-// in block order until the count is met.  One scan of packed (greater, equal)
-// counts gives each thread its output position, so the output is ascending
-// without a sort.
+// Method: radix select on order-preserving 32-bit keys.  On rows of four or
+// more keys a thread, the bits every candidate key shares are found first
+// (AND and OR over the row).  Passes of up to 8 bits below them each count,
+// per wave, the keys that match the prefix found so far into a 256-bin LDS
+// histogram (no contention between waves); the waves' bins are summed and the
+// digit where the count of larger keys reaches top_k - 1 is found with a
+// wave-wide prefix sum.  With four waves every wave finds the digit itself
+// from histograms that alternate between two buffers, so a pass has one
+// barrier; with more waves wave 0 finds it and hands it over in LDS (two
+// barriers).  The passes stop early once the keys under the prefix found so
+// far are exactly the ones still needed.  Keys above the threshold (compared
+// under the prefix's mask) are taken, and keys equal to it are taken in block
+// order until the count is met.  One scan of packed (greater, equal) counts
+// gives each thread its output position, so the output is ascending without
+// a sort.
 #pragma once
 
 #include "isb_device.h"
@@ -108,6 +110,7 @@ struct alignas(16) SelectLds {
   static constexpr int NB = NT <= 256 ? 2 : 1;
   int hist[NB][NT / 64][256];
   int wave_tot[NT / 64];
+  uint32_t wave_and[NT / 64], wave_or[NT / 64];
   int pick[3];
 };
 
@@ -130,11 +133,48 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
   const int jlim = W - E * tid;  // my keys i < jlim are candidates
   const int keep = K - 1;        // candidates to select (0 when top_k = 1)
   int need = keep;
-  uint32_t prefix = 0u, pmask = 0u;
+  // Rows of four or more keys a thread start below the candidates' common
+  // leading bits (AND and OR of every key agree there).  Scores of one row
+  // mostly share their sign and leading exponent bits, and a pass over such
+  // bits puts nearly every key in one or two bins, whose atomic counts
+  // serialize; for narrower rows the extra exchange costs more than it saves.
+  uint32_t kand = 0u, kor = ~0u;
+  if constexpr (E >= 4) {
+    kand = ~0u;
+    kor = 0u;
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (i < jlim) {
+        kand &= key[i];
+        kor |= key[i];
+      }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      kand &= (uint32_t)__shfl_xor((int)kand, off, kWave);
+      kor |= (uint32_t)__shfl_xor((int)kor, off, kWave);
+    }
+    if (lane == 0) {
+      sl.wave_and[wave] = kand;
+      sl.wave_or[wave] = kor;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      kand &= sl.wave_and[w];
+      kor |= sl.wave_or[w];
+    }
+  }
+  // bits [0, hi) differ between candidates (all 32 may, for narrow rows); the
+  // bits above are the prefix
+  int hi = kand == kor ? 0 : 32 - __builtin_clz(kand ^ kor);
+  uint32_t pmask = hi == 32 ? 0u : ~((1u << hi) - 1u);
+  uint32_t prefix = kand & pmask;
   // With need >= 1 every pass finds its digit (need never exceeds the keys
   // that match the prefix); with top_k = 1 only the tail is selected.
   constexpr int NB = SelectLds<NT>::NB;
-  for (int shift = 24, pass = 0; shift >= 0 && keep > 0; shift -= 8, ++pass) {
+  for (int pass = 0; hi > 0 && keep > 0; ++pass) {
+    const int lo = hi > 8 ? hi - 8 : 0;  // this pass's digit: bits [lo, hi)
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
     int(&hist)[NW][256] = sl.hist[NB == 2 ? (pass & 1) : 0];
     // this wave's histogram: cleared, then filled (LDS operations of a wave
     // complete in order; no wave still reads it: with two buffers its last
@@ -144,7 +184,7 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
     for (int x = 0; x < 4; ++x) hist[wave][lane + 64 * x] = 0;
 #pragma unroll
     for (int i = 0; i < E; ++i)
-      if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&hist[wave][(key[i] >> shift) & 0xFF], 1);
+      if (i < jlim && (key[i] & pmask) == prefix) atomicAdd(&hist[wave][(key[i] >> lo) & dmask], 1);
     __syncthreads();
     int digit = 0, above = 0, inside = 0;
     if (NB == 2 || wave == 0) {
@@ -187,9 +227,10 @@ __device__ __forceinline__ int select_row(const float (&sc)[E], int nt, int K, S
       above = sl.pick[1];
       inside = sl.pick[2];
     }
-    prefix |= (uint32_t)digit << shift;
-    pmask |= 0xFFu << shift;
+    prefix |= (uint32_t)digit << lo;
+    pmask |= dmask << lo;
     need -= above;
+    hi = lo;
     // Every key under the prefix is taken: the lower digits cannot change
     // the selection, so the passes stop (the keys compare under the mask).
     if (inside == need) break;

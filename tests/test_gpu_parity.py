@@ -167,6 +167,76 @@ def test_topk_full_size_shapes(MB, R, q_len, K):
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
+def _shared_prefix_rows(rng, rows, MB):
+    """Score rows whose candidates share long runs of leading key bits (the
+    selection starts below them on wide rows): all equal; equal but for the
+    lowest three mantissa bits; two exponents; equal with NaNs and a few one
+    ulp above; mostly -inf; standard normal (signs differ: no shared bits)."""
+    s = np.empty((rows, MB), np.float32)
+    for r in range(rows):
+        kind = r % 6
+        if kind == 0:
+            s[r] = 2.5
+        elif kind == 1:
+            s[r] = (np.uint32(0x3F800000) + rng.integers(0, 8, MB).astype(np.uint32)).view(np.float32)
+        elif kind == 2:
+            s[r] = rng.choice(np.array([3.0, 3.5, 5.0, 6.0], np.float32), MB)
+        elif kind == 3:
+            s[r] = 7.0
+            s[r, rng.integers(0, MB, 5)] = np.nan
+            s[r, rng.integers(0, MB, 3)] = np.nextafter(np.float32(7.0), np.float32(8.0))
+        elif kind == 4:
+            s[r] = -np.inf
+            s[r, rng.integers(0, MB, 40)] = -1.0
+        else:
+            s[r] = rng.standard_normal(MB)
+    return s
+
+
+@pytest.mark.parametrize("MB,K", [(1024, 16), (2048, 16), (4096, 32), (8192, 32)])
+def test_topk_rows_sharing_leading_bits(MB, K):
+    rng = np.random.default_rng(MB + K)
+    R = 12
+    lens = np.full(R, 128 * MB, np.int32)
+    lens[6:] = rng.integers(128 * (MB // 2), 128 * MB + 1, R - 6)
+    s = _shared_prefix_rows(rng, R, MB)[None]
+    ref = od.topk_select(s, lens, 1, K)
+    got = isb.topk_select(torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), 1, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("case", ["mxfp4_3904_blocks", "long_context_4096_blocks", "long_context_8192_blocks"])
+def test_select_attend_rows_sharing_leading_bits(case):
+    # The selection inside the attention launch on the same rows, against the
+    # oracle's selection (and the two-call path's page table and output).
+    base, kw = _SEL_CASES[case]
+    cfg = dataclasses.replace(SMALL[base], **kw)
+    w = wl.make_workload(cfg, device="cuda")
+    T, H_kv, MB = cfg.num_tokens, cfg.num_kv_heads, cfg.max_blocks
+    rng = np.random.default_rng(MB)
+    s = _shared_prefix_rows(rng, H_kv * T, MB).reshape(H_kv, T, MB)
+    scores = torch.from_numpy(s).cuda()
+    ref = od.topk_select(s, w.seq_lens.cpu().numpy(), cfg.query_len, cfg.top_k)
+    topk, sbt, sctx = isb.topk_select_emit(scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table,
+                                           cfg.pages_per_block)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               sbt, sctx, cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale,
+                               decode_query_len=cfg.query_len)
+    f_topk = torch.full_like(topk, 777)
+    f_sbt = torch.full_like(sbt, -5)
+    f_sctx = torch.full_like(sctx, 3)
+    f_out = torch.full_like(out, float("nan"))
+    isb.select_attend(scores, w.seq_lens, cfg.query_len, cfg.top_k, w.block_table, w.q, cfg.q_dtype, w.k_pool,
+                      w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale, cfg.num_q_heads, w.sm_scale,
+                      topk_idx=f_topk, sparse_bt=f_sbt, sparse_ctx=f_sctx, out=f_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(topk.cpu().numpy(), ref)
+    assert np.array_equal(f_topk.cpu().numpy(), ref)
+    assert torch.equal(f_sbt, sbt) and torch.equal(f_sctx, sctx)
+    assert torch.equal(f_out.view(torch.int16), out.view(torch.int16))
+
+
 # ------------------------------------------------------------------ emit
 @pytest.mark.parametrize("ppb", [8, 1])
 @pytest.mark.parametrize("H_kv,q_len", [(1, 1), (1, 4), (2, 3)])
