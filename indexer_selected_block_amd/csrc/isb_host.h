@@ -31,13 +31,14 @@ inline int64_t idx_page_bytes(int dt) {
 // of K and V), or one 128-token MXFP4 page; a workgroup of `waves` waves
 // covers one run a wave a round.  The chip holds kPaResidentWaves such waves
 // at once (two a SIMD).  When every run of the batch fits in that at once and
-// eight-wave workgroups still give every CU one, a workgroup of fp8 pages has
-// eight waves (a row needs half as many splits, so half as many partials are
-// merged); otherwise four.  Rows are cut into just enough splits to fill the chip; a
-// split longer than one round is walked round by round.  Batches that fill
-// the chip by themselves thus take one split a row, with nothing to merge
-// between workgroups, and small batches spread a row over several
-// workgroups that each read everything they attend in one round.
+// eight-wave workgroups still reach a quarter of the CUs, a workgroup of fp8
+// pages has eight waves (a row needs half as many splits, so half as many
+// partials are merged, and the rows of a small batch, which are latency-bound,
+// wait on fewer hand-offs); otherwise four.  Rows are cut into just enough
+// splits to fill the chip; a split longer than one round is walked round by
+// round.  Batches that fill the chip by themselves thus take one split a row,
+// with nothing to merge between workgroups, and small batches spread a row
+// over several workgroups that each read everything they attend in one round.
 constexpr int kPaResidentWaves = 2048;  // 256 CUs x 4 SIMDs x 2 waves
 constexpr int kPaCUs = 256;
 // 16-token-page batches whose rows fill every round of resident waves (at
@@ -76,7 +77,7 @@ inline PaPlan pa_plan(int num_tokens, int num_kv_heads, int sparse_bt_stride, in
   }
   const long long runs = (p.max_pages + p.pages_per_wave - 1) / p.pages_per_wave;  // of a whole row
   if (kv_dtype == ISB_FP8_E4M3 && (long long)p.rows * runs <= kPaResidentWaves &&
-      (long long)p.rows * ((runs + 7) / 8) >= kPaCUs)
+      (long long)p.rows * ((runs + 7) / 8) >= kPaCUs / 4)
     p.waves = 8;
   p.pages_per_round = p.waves * p.pages_per_wave;
   const int rounds = (p.max_pages + p.pages_per_round - 1) / p.pages_per_round;  // of a whole row
