@@ -366,6 +366,137 @@ __device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const
   }
 }
 
+// The pieces of a run for the one-wave-a-row pipeline (attend_row_wave16),
+// which issues the next run's loads between this run's passes.  A run of a
+// wave: up to RUN consecutive pages of its row, their raw bytes and where they
+// come from.
+template <int KV_DT, int RUN>
+struct RunRegs {
+  PageRegs<KV_DT> pr[RUN];
+  bool ok[RUN];      // the page id is in range (else page 0 is read and the tile poisoned)
+  int64_t use[RUN];  // byte offset of the page's K (and V) in its pool
+};
+
+// The run's page ids: lanes ibase .. ibase + cnt - 1 of my_ids (cnt >= 1);
+// slots past the run re-read its first page.
+template <int KV_DT, int RUN>
+__device__ __forceinline__ void run_pages(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int cnt, int my_ids, int ibase,
+                                          int64_t hstride, int64_t hoff) {
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    const int64_t id = __builtin_amdgcn_readlane(my_ids, ibase + (j < cnt ? j : 0));
+    rr.ok[j] = page_ok(id, a.num_pages);
+    rr.use[j] = (rr.ok[j] ? id : 0) * hstride + hoff;
+  }
+}
+
+// Every K load of the run, then (separately) every V load, page by page and
+// kept in that order, so the logits of page j wait only for K of pages <= j
+// and P.V of page j only for V of pages <= j.
+template <int KV_DT, int RUN, bool NT>
+__device__ __forceinline__ void issue_k_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane) {
+  constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
+  __builtin_amdgcn_sched_barrier(0);  // no load of the run moves above what comes before
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    load_k16<KV_DT, NT>(rr.pr[j], page_rsrc(a.kp + rr.use[j], PB), lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+template <int KV_DT, int RUN, bool NT>
+__device__ __forceinline__ void issue_v_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane) {
+  constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
+  __builtin_amdgcn_sched_barrier(0);  // no load of the run moves above what comes before
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    load_v16<KV_DT, NT>(rr.pr[j], page_rsrc(a.vp + rr.use[j], PB), lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Pass 1 of a run (pages wb .. wb + cnt - 1 of the row): every logit z of the
+// run, then one exact max per head, folded into the running max M (rescaling
+// what earlier runs accumulated if it grew).  Uses the run's K registers (and
+// clears the V bytes of keys past the row's length on its last page).
+// KEEP: pin MFMA operands live (see mfma_16x16x32_bf16_k).
+template <int KV_DT, int Q_DT, int RUN, bool KEEP>
+__device__ __forceinline__ void logits_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane, int n_tok, int wb,
+                                           int cnt, const bf16x8 (&qb)[4], bool first, float& M, float& lsum,
+                                           f32x4 (&o)[8], bf16x8 (&pb)[RUN / 2]) {
+  const int g = lane >> 4;
+  float z[RUN][4];
+  float mx = neg_inf();
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    if (j < cnt) {
+      bf16x8 kb[4];
+      k_operand<KV_DT>(rr.pr[j], kb);
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16_k<KEEP>(kb[x], qb[x], sacc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
+      const int nv = min(16, n_tok - (wb + j) * 16);
+      if (nv < 16) {  // the row's last page: keys past its length do not count
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
+        clear_tail_keys<KV_DT>(rr.pr[j], nv, g);
+      }
+      if (!rr.ok[j]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[j][e] = qnan();
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, z[j][e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[j][e] = neg_inf();
+    }
+  }
+  mx = max_over_groups(mx);
+  const float m_new = fmaxf(M, mx);
+  if (!first) {
+    const float alpha = M == m_new ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+  }
+  M = m_new;
+  // The probabilities, as the P.V MFMA takes them: keys 4 g + e of pages j
+  // and j + 1 in pb[j / 2] (bf16), their fp32 sum into lsum.
+#pragma unroll
+  for (int j = 0; j < RUN; j += 2) {
+    if (j < cnt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
+        const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
+        lsum += p0v + p1v;
+        pb[j / 2][e] = (__bf16)p0v;
+        pb[j / 2][4 + e] = (__bf16)p1v;
+      }
+    }
+  }
+}
+
+// Pass 2 of a run: P.V, two pages per MFMA (keys 4 g + e of the first page,
+// then of the second, on v_mfma_f32_16x16x32_bf16).  Uses the run's V
+// registers.
+template <int KV_DT, int RUN, bool KEEP>
+__device__ __forceinline__ void pv_run(RunRegs<KV_DT, RUN>& rr, int lane, int cnt, const bf16x8 (&pb)[RUN / 2],
+                                       f32x4 (&o)[8]) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < RUN; j += 2) {
+    if (j < cnt) {
+      if (j + 1 >= cnt) clear_tail_keys<KV_DT>(rr.pr[j + 1], 0, g);  // a run's odd last slot
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = mfma_16x16x32_bf16_k<KEEP>(v_pair_operand<KV_DT>(rr.pr[j], rr.pr[j + 1], dt), pb[j / 2], o[dt]);
+    }
+  }
+}
+
 // One run of a wave: pages wb .. wb + cnt - 1 of its row (cnt >= 1, at most
 // RUN), whose ids sit in lanes ibase .. ibase + cnt - 1 of my_ids, folded into
 // the wave's running max M (per head), sum share lsum and output o.  Every
@@ -516,7 +647,7 @@ __device__ __forceinline__ void attend_split16(const PaArgs& a, WaveParts<NW>& w
 // for run r0 + lane / RUN, slot lane % RUN.
 template <int KV_DT, int Q_DT, int RUN, bool NT, typename IdFn>
 __device__ __forceinline__ void attend_row_wave16(const PaArgs& a, int kvh, int n_tok, bf16x8 (&qb)[4],
-                                                  int my_ids, IdFn ids, __bf16* out_row) {
+                                                  int my_ids, IdFn ids, __bf16* out_row, bf16x8* s_qb) {
   constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
   constexpr int IDS = 64 / RUN;
   const int lane = threadIdx.x & 63;
@@ -539,11 +670,33 @@ __device__ __forceinline__ void attend_row_wave16(const PaArgs& a, int kvh, int 
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t hstride = (int64_t)a.H_kv * PB;
   const int64_t hoff = (int64_t)kvh * PB;
+  // The runs in a pipeline: the next run's K loads are issued once this
+  // run's logits have consumed its K registers, and its V loads once this
+  // run's P.V has consumed its V registers, so they are in flight during this
+  // run's math without registers of their own.  The query operand waits in
+  // this wave's LDS slice s_qb and is read back for each run's logits.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s_qb[4 * lane + j] = qb[j];
+  RunRegs<KV_DT, RUN> rr;
+  run_pages<KV_DT, RUN>(a, rr, min(RUN, npages), my_ids, 0, hstride, hoff);
+  issue_k_run<KV_DT, RUN, NT>(a, rr, lane);
+  issue_v_run<KV_DT, RUN, NT>(a, rr, lane);
   for (int r = 0; r < nruns; ++r) {
-    if (r > 0 && r % IDS == 0) my_ids = ids(r);
-    const int wb = r * RUN;
-    attend_run16<KV_DT, Q_DT, RUN, NT, false>(a, lane, n_tok, wb, min(RUN, npages - wb), my_ids, (r % IDS) * RUN,
-                                              hstride, hoff, qb, r == 0, M, lsum, o);
+    const int wb = r * RUN, cnt = min(RUN, npages - wb);
+    bf16x8 pb[RUN / 2];
+    bf16x8 qr[4];
+    asm volatile("" ::: "memory");  // read the query back each run, not kept in registers
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qr[j] = s_qb[4 * lane + j];
+    logits_run<KV_DT, Q_DT, RUN, false>(a, rr, lane, n_tok, wb, cnt, qr, r == 0, M, lsum, o, pb);
+    // the next run (after the last one: this run's pages again, unused)
+    const bool more = r + 1 < nruns;
+    if (more && (r + 1) % IDS == 0) my_ids = ids(r + 1);
+    const int nx = more ? r + 1 : r;
+    run_pages<KV_DT, RUN>(a, rr, min(RUN, npages - nx * RUN), my_ids, (nx % IDS) * RUN, hstride, hoff);
+    issue_k_run<KV_DT, RUN, NT>(a, rr, lane);
+    pv_run<KV_DT, RUN, false>(rr, lane, cnt, pb, o);
+    issue_v_run<KV_DT, RUN, NT>(a, rr, lane);
   }
   // lane (g, c): dims 16 dt + 4 g + e of head c
   const float inv = a.v_scale / sum_over_groups(lsum);
@@ -598,6 +751,7 @@ __global__ __launch_bounds__(64 * NW) void pa16_kernel(PaArgs a) {
 template <int KV_DT, int Q_DT, int RUN, bool NT>
 __global__ __launch_bounds__(256) void pa16row_kernel(PaArgs a, int rows) {
   constexpr int QB = Q_DT == ISB_BF16 ? 2 : 1;
+  __shared__ bf16x8 s_qb[4][4 * kWave];  // each wave's query operand
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int row = 4 * grid_row(blockIdx.x, gridDim.x) + wave;
   if (row >= rows) return;
@@ -619,7 +773,7 @@ __global__ __launch_bounds__(256) void pa16row_kernel(PaArgs a, int rows) {
     for (int j = 0; j < 4; ++j) qb[j] = load_q8_t<Q_DT>(qrow, 32 * g + 8 * j);
   }
   __bf16* out_row = a.out + ((size_t)t * a.H_q + kvh * a.G) * kHeadDim;
-  attend_row_wave16<KV_DT, Q_DT, RUN, NT>(a, kvh, n_tok, qb, my_ids, load_ids, out_row);
+  attend_row_wave16<KV_DT, Q_DT, RUN, NT>(a, kvh, n_tok, qb, my_ids, load_ids, out_row, s_qb[wave]);
 }
 
 // ----------------------------------------------------------------- select + attend
