@@ -392,24 +392,27 @@ __device__ __forceinline__ void run_pages(const PaArgs& a, RunRegs<KV_DT, RUN>& 
 
 // Every K load of the run, then (separately) every V load, page by page and
 // kept in that order, so the logits of page j wait only for K of pages <= j
-// and P.V of page j only for V of pages <= j.
+// and P.V of page j only for V of pages <= j.  live false: the loads are
+// issued against an empty range (they return zeros and read no memory).
 template <int KV_DT, int RUN, bool NT>
-__device__ __forceinline__ void issue_k_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane) {
+__device__ __forceinline__ void issue_k_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane,
+                                            bool live = true) {
   constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
   __builtin_amdgcn_sched_barrier(0);  // no load of the run moves above what comes before
 #pragma unroll
   for (int j = 0; j < RUN; ++j) {
-    load_k16<KV_DT, NT>(rr.pr[j], page_rsrc(a.kp + rr.use[j], PB), lane);
+    load_k16<KV_DT, NT>(rr.pr[j], page_rsrc(a.kp + rr.use[j], live ? PB : 0), lane);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 template <int KV_DT, int RUN, bool NT>
-__device__ __forceinline__ void issue_v_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane) {
+__device__ __forceinline__ void issue_v_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane,
+                                            bool live = true) {
   constexpr int PB = KV_DT == ISB_BF16 ? 4096 : 2048;
   __builtin_amdgcn_sched_barrier(0);  // no load of the run moves above what comes before
 #pragma unroll
   for (int j = 0; j < RUN; ++j) {
-    load_v16<KV_DT, NT>(rr.pr[j], page_rsrc(a.vp + rr.use[j], PB), lane);
+    load_v16<KV_DT, NT>(rr.pr[j], page_rsrc(a.vp + rr.use[j], live ? PB : 0), lane);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -689,14 +692,15 @@ __device__ __forceinline__ void attend_row_wave16(const PaArgs& a, int kvh, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) qr[j] = s_qb[4 * lane + j];
     logits_run<KV_DT, Q_DT, RUN, false>(a, rr, lane, n_tok, wb, cnt, qr, r == 0, M, lsum, o, pb);
-    // the next run (after the last one: this run's pages again, unused)
+    // the next run (after the last one: loads of an empty range, so the
+    // loop needs no branch around them)
     const bool more = r + 1 < nruns;
     if (more && (r + 1) % IDS == 0) my_ids = ids(r + 1);
     const int nx = more ? r + 1 : r;
     run_pages<KV_DT, RUN>(a, rr, min(RUN, npages - nx * RUN), my_ids, (nx % IDS) * RUN, hstride, hoff);
-    issue_k_run<KV_DT, RUN, NT>(a, rr, lane);
+    issue_k_run<KV_DT, RUN, NT>(a, rr, lane, more);
     pv_run<KV_DT, RUN, false>(rr, lane, cnt, pb, o);
-    issue_v_run<KV_DT, RUN, NT>(a, rr, lane);
+    issue_v_run<KV_DT, RUN, NT>(a, rr, lane, more);
   }
   // lane (g, c): dims 16 dt + 4 g + e of head c
   const float inv = a.v_scale / sum_over_groups(lsum);
