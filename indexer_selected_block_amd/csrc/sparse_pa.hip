@@ -417,23 +417,23 @@ __device__ __forceinline__ void issue_v_run(const PaArgs& a, RunRegs<KV_DT, RUN>
   }
 }
 
-// Pass 1 of a run (pages wb .. wb + cnt - 1 of the row): every logit z of the
-// run, then one exact max per head, folded into the running max M (rescaling
-// what earlier runs accumulated if it grew).  Uses the run's K registers (and
-// clears the V bytes of keys past the row's length on its last page).
-// KEEP: pin MFMA operands live (see mfma_16x16x32_bf16_k).
+// Pass 1 of a run (pages wb .. wb + cnt - 1 of the row, raw bytes in pr,
+// ok[j]: page j's id was in range): every logit z of the run, then one exact
+// max per head, folded into the running max M (rescaling what earlier runs
+// accumulated if it grew).  Uses the run's K registers (and clears the V
+// bytes of keys past the row's length on its last page).  KEEP: pin MFMA
+// operands live (see mfma_16x16x32_bf16_k).
 template <int KV_DT, int Q_DT, int RUN, bool KEEP>
-__device__ __forceinline__ void logits_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane, int n_tok, int wb,
-                                           int cnt, const bf16x8 (&qb)[4], bool first, float& M, float& lsum,
-                                           f32x4 (&o)[8], bf16x8 (&pb)[RUN / 2]) {
+__device__ __forceinline__ void run_logits(const PaArgs& a, PageRegs<KV_DT> (&pr)[RUN], const bool (&ok)[RUN],
+                                           int lane, int n_tok, int wb, int cnt, const bf16x8 (&qb)[4], bool first,
+                                           float& M, float& lsum, f32x4 (&o)[8], float (&z)[RUN][4]) {
   const int g = lane >> 4;
-  float z[RUN][4];
   float mx = neg_inf();
 #pragma unroll
   for (int j = 0; j < RUN; ++j) {
     if (j < cnt) {
       bf16x8 kb[4];
-      k_operand<KV_DT>(rr.pr[j], kb);
+      k_operand<KV_DT>(pr[j], kb);
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16_k<KEEP>(kb[x], qb[x], sacc);
@@ -443,9 +443,9 @@ __device__ __forceinline__ void logits_run(const PaArgs& a, RunRegs<KV_DT, RUN>&
       if (nv < 16) {  // the row's last page: keys past its length do not count
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
-        clear_tail_keys<KV_DT>(rr.pr[j], nv, g);
+        clear_tail_keys<KV_DT>(pr[j], nv, g);
       }
-      if (!rr.ok[j]) {
+      if (!ok[j]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[j][e] = qnan();
       }
@@ -465,8 +465,18 @@ __device__ __forceinline__ void logits_run(const PaArgs& a, RunRegs<KV_DT, RUN>&
     for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
   }
   M = m_new;
-  // The probabilities, as the P.V MFMA takes them: keys 4 g + e of pages j
-  // and j + 1 in pb[j / 2] (bf16), their fp32 sum into lsum.
+}
+
+// Pass 1 for the pipeline, which then holds the run's probabilities rather
+// than its logits while the next run's K loads are in flight: keys 4 g + e of
+// pages j and j + 1 in pb[j / 2] (bf16, as the P.V MFMA takes them), their
+// fp32 sum into lsum.
+template <int KV_DT, int Q_DT, int RUN, bool KEEP>
+__device__ __forceinline__ void logits_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane, int n_tok, int wb,
+                                           int cnt, const bf16x8 (&qb)[4], bool first, float& M, float& lsum,
+                                           f32x4 (&o)[8], bf16x8 (&pb)[RUN / 2]) {
+  float z[RUN][4];
+  run_logits<KV_DT, Q_DT, RUN, KEEP>(a, rr.pr, rr.ok, lane, n_tok, wb, cnt, qb, first, M, lsum, o, z);
 #pragma unroll
   for (int j = 0; j < RUN; j += 2) {
     if (j < cnt) {
@@ -535,45 +545,7 @@ __device__ __forceinline__ void attend_run16(const PaArgs& a, int lane, int n_to
   }
   // Pass 1: every logit of the run, then one exact max per head.
   float z[RUN][4];
-  float mx = neg_inf();
-#pragma unroll
-  for (int j = 0; j < RUN; ++j) {
-    if (j < cnt) {
-      bf16x8 kb[4];
-      k_operand<KV_DT>(pr[j], kb);
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) sacc = mfma_16x16x32_bf16_k<KEEP>(kb[x], qb[x], sacc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) z[j][e] = sacc[e] * a.qk_scale;
-      const int nv = min(16, n_tok - (wb + j) * 16);
-      if (nv < 16) {  // the row's last page: keys past its length do not count
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[j][e] = 4 * g + e < nv ? z[j][e] : neg_inf();
-        clear_tail_keys<KV_DT>(pr[j], nv, g);
-      }
-      if (!ok[j]) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[j][e] = qnan();
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, z[j][e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) z[j][e] = neg_inf();
-    }
-  }
-  mx = max_over_groups(mx);
-  // Fold the run's max into the running one (rescaling what earlier runs
-  // accumulated).
-  const float m_new = fmaxf(M, mx);
-  if (!first) {
-    const float alpha = M == m_new ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
-    lsum *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-  }
-  M = m_new;
+  run_logits<KV_DT, Q_DT, RUN, KEEP>(a, pr, ok, lane, n_tok, wb, cnt, qb, first, M, lsum, o, z);
   // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
   // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
 #pragma unroll
