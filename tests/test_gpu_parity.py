@@ -484,6 +484,29 @@ def test_sparse_pa_one_wave_a_row(base, kw):
     assert (err <= tol).all(), f"max |err| {err.max():.4g} > {tol:.4g}"
 
 
+def test_sparse_pa_one_wave_a_row_long_rows_and_empty_rows():
+    # one wave a row with sixteen runs a row (the page ids of runs 8.. are
+    # fetched mid-walk) and rows of length 0 among them
+    cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=2000, ctx_lo=100, ctx_hi=2500, num_pad_reqs=40,
+                    pool_blocks=2040 * 20 + 64, top_k=16)
+    _say("[sparse_pa one wave a row] sixteen runs, empty rows")
+    w = wl.make_workload(cfg, device="cuda")
+    hi = host_inputs(w)
+    sbt, sctx = _synthetic_table(hi, 78)
+    assert (sctx == 0).sum() >= 40 and sbt.shape[1] == 128
+    ref = oracle_attention(hi, sbt, sctx)
+    out = isb.sparse_pa_decode(w.q, cfg.q_dtype, w.k_pool, w.v_pool, cfg.kv_dtype, w.k_scale, w.v_scale,
+                               torch.from_numpy(sbt).cuda(), torch.from_numpy(sctx).cuda(),
+                               cfg.num_q_heads, cfg.num_kv_heads, w.sm_scale, decode_query_len=cfg.query_len)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert (got[sctx == 0] == 0).all()
+    tol = attn_tol(cfg.kv_dtype, attended_vmax(hi, sbt, sctx))
+    err = np.abs(got - ref).max(axis=(1, 2))
+    assert (err <= tol).all(), f"max |err| {err.max():.4g} > {tol:.4g}"
+
+
 def test_sparse_pa_every_block_is_dense_attention():
     # top-k >= every row's block count: the sparse decode is dense causal attention.
     cfg = wl.shrink(wl.CONFIGS["fp8_decode"], num_reqs=4, ctx_lo=100, ctx_hi=2000, top_k=16)
