@@ -12,6 +12,8 @@ namespace isb {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -122,6 +124,17 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
                                           __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)});
 }
 
+// The same eight e4m3 bytes -> f16 (exact as well: f16 holds every e4m3
+// value, subnormals included).
+__device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return __builtin_bit_cast(f16x8, u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                         __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)});
+}
+
 // Eight e2m1 nibbles of one dword (low nibble of byte 0 first) -> eight bf16,
 // each multiplied by `scale` (a power of two from an e8m0 byte).
 __device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t w, float scale) {
@@ -159,6 +172,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c)
 template <bool KEEP>
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16_k(bf16x8 a, bf16x8 b, f32x4 c) {
   f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  if constexpr (KEEP) asm volatile("" : "+v"(d) : "v"(a), "v"(b));
+  return d;
+}
+// v_mfma_f32_16x16x32_f16: the same lane layout with f16 operands; KEEP as
+// for mfma_16x16x32_bf16_k.
+template <bool KEEP>
+__device__ __forceinline__ f32x4 mfma_16x16x32_f16_k(f16x8 a, f16x8 b, f32x4 c) {
+  f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   if constexpr (KEEP) asm volatile("" : "+v"(d) : "v"(a), "v"(b));
   return d;
 }

@@ -353,16 +353,40 @@ __device__ __forceinline__ void k_operand(const PageRegs<KV_DT>& pr, bf16x8 (&kb
   }
 }
 
-// V^T operand of dim tile dt for a pair of pages (keys 4 g + e of the first
-// page, then of the second), as v_mfma_f32_16x16x32_bf16 wants it.
+// Operand type of P.V: bf16 for bf16 V; f16 for fp8 V, whose e4m3 values
+// convert to f16 exactly as well, so the probabilities keep 11 significant
+// bits instead of bf16's 8 (a quarter of the rounding error in the output).
 template <int KV_DT>
-__device__ __forceinline__ bf16x8 v_pair_operand(const PageRegs<KV_DT>& a, const PageRegs<KV_DT>& b, int dt) {
+struct PvType {
+  using vec = bf16x8;
+  using elem = __bf16;
+};
+template <>
+struct PvType<ISB_FP8_E4M3> {
+  using vec = f16x8;
+  using elem = _Float16;
+};
+template <int KV_DT>
+using pv_vec = typename PvType<KV_DT>::vec;
+
+// v_mfma_f32_16x16x32 of P.V in the operand type of the pages.
+template <int KV_DT, bool KEEP>
+__device__ __forceinline__ f32x4 pv_mfma(pv_vec<KV_DT> v, pv_vec<KV_DT> p, f32x4 o) {
+  if constexpr (KV_DT == ISB_FP8_E4M3) return mfma_16x16x32_f16_k<KEEP>(v, p, o);
+  else return mfma_16x16x32_bf16_k<KEEP>(v, p, o);
+}
+
+// V^T operand of dim tile dt for a pair of pages (keys 4 g + e of the first
+// page, then of the second), as the P.V MFMA wants it.
+template <int KV_DT>
+__device__ __forceinline__ pv_vec<KV_DT> v_pair_operand(const PageRegs<KV_DT>& a, const PageRegs<KV_DT>& b,
+                                                        int dt) {
   if constexpr (KV_DT == ISB_BF16) {
     const int h = dt >> 1, q = dt & 1;
     return __builtin_bit_cast(bf16x8, u32x4{a.v[h][2 * q], a.v[h][2 * q + 1], b.v[h][2 * q], b.v[h][2 * q + 1]});
   } else {
     const int h = dt >> 2, q = dt & 3;
-    return e4m3x8_to_bf16x8(a.v[h][q], b.v[h][q]);
+    return e4m3x8_to_f16x8(a.v[h][q], b.v[h][q]);
   }
 }
 
@@ -469,12 +493,12 @@ __device__ __forceinline__ void run_logits(const PaArgs& a, PageRegs<KV_DT> (&pr
 
 // Pass 1 for the pipeline, which then holds the run's probabilities rather
 // than its logits while the next run's K loads are in flight: keys 4 g + e of
-// pages j and j + 1 in pb[j / 2] (bf16, as the P.V MFMA takes them), their
+// pages j and j + 1 in pb[j / 2] (in the P.V operand type), their
 // fp32 sum into lsum.
 template <int KV_DT, int Q_DT, int RUN, bool KEEP>
 __device__ __forceinline__ void logits_run(const PaArgs& a, RunRegs<KV_DT, RUN>& rr, int lane, int n_tok, int wb,
                                            int cnt, const bf16x8 (&qb)[4], bool first, float& M, float& lsum,
-                                           f32x4 (&o)[8], bf16x8 (&pb)[RUN / 2]) {
+                                           f32x4 (&o)[8], pv_vec<KV_DT> (&pb)[RUN / 2]) {
   float z[RUN][4];
   run_logits<KV_DT, Q_DT, RUN, KEEP>(a, rr.pr, rr.ok, lane, n_tok, wb, cnt, qb, first, M, lsum, o, z);
 #pragma unroll
@@ -485,18 +509,17 @@ __device__ __forceinline__ void logits_run(const PaArgs& a, RunRegs<KV_DT, RUN>&
         const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
         const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
         lsum += p0v + p1v;
-        pb[j / 2][e] = (__bf16)p0v;
-        pb[j / 2][4 + e] = (__bf16)p1v;
+        pb[j / 2][e] = (typename PvType<KV_DT>::elem)p0v;
+        pb[j / 2][4 + e] = (typename PvType<KV_DT>::elem)p1v;
       }
     }
   }
 }
 
 // Pass 2 of a run: P.V, two pages per MFMA (keys 4 g + e of the first page,
-// then of the second, on v_mfma_f32_16x16x32_bf16).  Uses the run's V
-// registers.
+// then of the second, on pv_mfma).  Uses the run's V registers.
 template <int KV_DT, int RUN, bool KEEP>
-__device__ __forceinline__ void pv_run(RunRegs<KV_DT, RUN>& rr, int lane, int cnt, const bf16x8 (&pb)[RUN / 2],
+__device__ __forceinline__ void pv_run(RunRegs<KV_DT, RUN>& rr, int lane, int cnt, const pv_vec<KV_DT> (&pb)[RUN / 2],
                                        f32x4 (&o)[8]) {
   const int g = lane >> 4;
 #pragma unroll
@@ -505,7 +528,7 @@ __device__ __forceinline__ void pv_run(RunRegs<KV_DT, RUN>& rr, int lane, int cn
       if (j + 1 >= cnt) clear_tail_keys<KV_DT>(rr.pr[j + 1], 0, g);  // a run's odd last slot
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        o[dt] = mfma_16x16x32_bf16_k<KEEP>(v_pair_operand<KV_DT>(rr.pr[j], rr.pr[j + 1], dt), pb[j / 2], o[dt]);
+        o[dt] = pv_mfma<KV_DT, KEEP>(v_pair_operand<KV_DT>(rr.pr[j], rr.pr[j + 1], dt), pb[j / 2], o[dt]);
     }
   }
 }
@@ -547,23 +570,23 @@ __device__ __forceinline__ void attend_run16(const PaArgs& a, int lane, int n_to
   float z[RUN][4];
   run_logits<KV_DT, Q_DT, RUN, KEEP>(a, pr, ok, lane, n_tok, wb, cnt, qb, first, M, lsum, o, z);
   // Pass 2: probabilities and P.V, two pages per MFMA (keys 4 g + e of the
-  // first page, then of the second, on v_mfma_f32_16x16x32_bf16).
+  // first page, then of the second, on pv_mfma).
 #pragma unroll
   for (int j = 0; j < RUN; j += 2) {
     if (j < cnt) {
-      bf16x8 pb;
+      pv_vec<KV_DT> pb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float p0v = __builtin_amdgcn_exp2f(z[j][e] - M);
         const float p1v = __builtin_amdgcn_exp2f(z[j + 1][e] - M);
         lsum += p0v + p1v;
-        pb[e] = (__bf16)p0v;
-        pb[4 + e] = (__bf16)p1v;
+        pb[e] = (typename PvType<KV_DT>::elem)p0v;
+        pb[4 + e] = (typename PvType<KV_DT>::elem)p1v;
       }
       if (j + 1 >= cnt) clear_tail_keys<KV_DT>(pr[j + 1], 0, g);  // a run's odd last slot
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        o[dt] = mfma_16x16x32_bf16_k<KEEP>(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
+        o[dt] = pv_mfma<KV_DT, KEEP>(v_pair_operand<KV_DT>(pr[j], pr[j + 1], dt), pb, o[dt]);
     }
   }
 }
@@ -658,7 +681,7 @@ __device__ __forceinline__ void attend_row_wave16(const PaArgs& a, int kvh, int 
   issue_v_run<KV_DT, RUN, NT>(a, rr, lane);
   for (int r = 0; r < nruns; ++r) {
     const int wb = r * RUN, cnt = min(RUN, npages - wb);
-    bf16x8 pb[RUN / 2];
+    pv_vec<KV_DT> pb[RUN / 2];
     bf16x8 qr[4];
     asm volatile("" ::: "memory");  // read the query back each run, not kept in registers
 #pragma unroll
