@@ -535,7 +535,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3->bf16 mfma, f32 accumulate" if cfg.kv_dtype == "fp8" else f"{cfg.kv_dtype} in, f32 accumulate",
+        "dtype": ("e4m3 K->bf16 and V->f16 mfma, f32 accumulate" if cfg.kv_dtype == "fp8"
+                  else f"{cfg.kv_dtype} in, f32 accumulate"),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "requests": cfg.total_reqs,
                    "query_len": "ragged" if ragged else cfg.query_len, "tokens_per_step": T,
