@@ -304,6 +304,9 @@ _SEL_CASES = {
     "long_context_8192_blocks": ("long_context", dict(num_reqs=2, ctx_lo=900000, ctx_hi=1048576,
                                                       pool_blocks=2 * 8192 + 64)),
     "mxfp4_3904_blocks": ("mxfp4", dict(num_reqs=3, ctx_lo=300000, ctx_hi=499712, pool_blocks=3 * 3904 + 64)),
+    # rows wider than 8192 blocks: the two calls (selection over global memory)
+    "long_context_10000_blocks": ("long_context", dict(num_reqs=1, ctx_lo=1200000, ctx_hi=1280000,
+                                                       pool_blocks=10000 + 64)),
 }
 
 
