@@ -14,7 +14,9 @@ in each docstring:
 * ``decode``   - index score, top-k selection, sparse block-table emission and
                  sparse attention, and the four chained as one decode layer;
 * ``prefill``  - the same steps for a ragged prefill batch, each query token
-                 with its own request id and absolute position.
+                 with its own request id and absolute position;
+* ``writer``   - writing a step's new tokens into the caches (optional QK-norm
+                 and rope, the fp8 / MXFP4 encodings) and the e4m3 query cast.
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 library routines on special cases, brute force on tiny inputs, invariants),
@@ -23,4 +25,4 @@ maximum over the block's tokens, and index heads of one KV group being summed -
 whose arithmetic is pinned but whose choice of definition is a reading.
 """
 
-from . import formats, pools, decode, prefill  # noqa: F401
+from . import formats, pools, decode, prefill, writer  # noqa: F401
